@@ -1,0 +1,194 @@
+// C-ABI entry points of libmoe.so: host-side argument checks, then the
+// kernel launches.  No allocation, no host<->device copies, no sync.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+
+#include "moe.h"
+
+// launchers (one per kernel family)
+extern "C" {
+moe_status_t moe_route_topk_launch(const float*, int64_t, int32_t, int32_t, int32_t, int32_t*, float*, uint32_t*,
+                                   hipStream_t);
+size_t moe_permute_ws_bytes_impl(int64_t, int32_t, int32_t);
+moe_status_t moe_permute_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
+                                int32_t*, int32_t*, int32_t*, uint16_t*, void*, uint32_t*, hipStream_t);
+moe_status_t moe_unpermute_combine_launch(const uint16_t*, const float*, const int32_t*, int64_t, int32_t, int32_t,
+                                          uint16_t*, hipStream_t);
+moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const float*, const int32_t*, int64_t,
+                                         int32_t, int32_t, uint16_t*, float*, hipStream_t);
+moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*, int32_t,
+                                        uint16_t*, hipStream_t);
+moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
+                                         uint8_t*, uint8_t*, uint32_t*, hipStream_t);
+moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
+                                 const int32_t*, void*, void*, uint32_t*, hipStream_t);
+}
+
+namespace moe_host {
+
+// CU count per device, read once per device (the only global state).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace moe_host
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, dtype or layout";
+    case MOE_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+moe_status_t moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                            int32_t* topk_ids, float* topk_w, uint32_t* err_flag, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > E || K > 32) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  return moe_route_topk_launch(logits, T, E, K, renormalize, topk_ids, topk_w, err_flag, S(stream));
+}
+
+size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t K) {
+  if (T < 0 || E < 1 || K < 1) return 0;
+  return moe_permute_ws_bytes_impl(T, E, K);
+}
+
+moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E, int32_t K,
+                         int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
+                         uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    if (d < 8 || d % 8) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGNMENT;
+  }
+  const size_t need = moe_permute_ws_bytes_impl(T, E, K);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
+  return moe_permute_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_perm, ws,
+                            err_flag, S(stream));
+}
+
+size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
+  (void)desc;
+  return 0;
+}
+
+moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_scale, const void* B,
+                          const uint8_t* B_scale, const int32_t* group_sizes, void* C, void* C_aux, void* ws,
+                          size_t ws_bytes, uint32_t* err_flag, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->G < 1 || d->G > 1024 || d->N < 1 || d->m_cap < 0) return MOE_ERR_INVALID_ARG;
+  if (d->m_cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!A || !B || !C || !group_sizes) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_aux && !aligned16(C_aux))) return MOE_ERR_ALIGNMENT;
+  if (d->dtype != MOE_DTYPE_BF16 && d->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (d->out_dtype != MOE_OUT_BF16 && d->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
+  if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (d->N % 8) return MOE_ERR_UNSUPPORTED;
+  if (d->ragged == MOE_RAGGED_M) {
+    if (d->K < 1) return MOE_ERR_INVALID_ARG;
+    if (d->b_layout != MOE_B_NK && d->b_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
+    if (d->epilogue == MOE_EPI_SWIGLU) {
+      if (d->b_layout != MOE_B_NK || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
+    } else if (C_aux) {
+      return MOE_ERR_INVALID_ARG;
+    }
+    if (d->dtype == MOE_DTYPE_MXFP8) {
+      if (d->K % 128 || d->b_layout != MOE_B_NK || d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
+      if (!A_scale || !B_scale) return MOE_ERR_INVALID_ARG;
+      if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (reinterpret_cast<uintptr_t>(B_scale) & 3u))
+        return MOE_ERR_ALIGNMENT;
+    } else {
+      if (d->K % 64) return MOE_ERR_UNSUPPORTED;
+      if (d->b_layout == MOE_B_KN && d->N < 8) return MOE_ERR_UNSUPPORTED;
+    }
+    if (d->m_cap == 0) return MOE_OK;
+  } else if (d->ragged == MOE_RAGGED_K) {
+    if (d->dtype != MOE_DTYPE_BF16 || d->epilogue != MOE_EPI_NONE || C_aux) return MOE_ERR_UNSUPPORTED;
+    if (d->M < 8 || d->M % 8) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, err_flag, S(stream));
+}
+
+moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, const int32_t* perm_dst, int64_t T,
+                                   int32_t d, int32_t K, uint16_t* y, void* stream) {
+  if (T < 0 || K < 1 || K > 32 || d < 8 || d % 8) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!y_perm || !perm_dst || !y)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(y_perm) || !aligned16(y))) return MOE_ERR_ALIGNMENT;
+  return moe_unpermute_combine_launch(y_perm, topk_w, perm_dst, T, d, K, y, S(stream));
+}
+
+moe_status_t moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
+                                  const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint16_t* dy_perm,
+                                  float* d_topk_w, void* stream) {
+  if (T < 0 || K < 1 || K > 32 || d < 8 || d % 8) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || !y_perm || !topk_w || !perm_dst || !dy_perm || !d_topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(dy) || !aligned16(y_perm) || !aligned16(dy_perm))) return MOE_ERR_ALIGNMENT;
+  return moe_combine_backward_launch(dy, y_perm, topk_w, perm_dst, T, d, K, dy_perm, d_topk_w, S(stream));
+}
+
+moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
+                                 const int32_t* group_sizes, int32_t G, uint16_t* dgu, void* stream) {
+  if (m_cap < 0 || f < 8 || f % 8) return MOE_ERR_INVALID_ARG;
+  if (group_sizes && (G < 1 || G > 1024)) return MOE_ERR_INVALID_ARG;
+  if (m_cap > 0 && (!gu || !dh || !dgu)) return MOE_ERR_INVALID_ARG;
+  if (m_cap > 0 && (!aligned16(gu) || !aligned16(dh) || !aligned16(dgu))) return MOE_ERR_ALIGNMENT;
+  return moe_swiglu_backward_launch(gu, dh, m_cap, f, group_sizes, G, dgu, S(stream));
+}
+
+moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols, int32_t axis,
+                                  const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,
+                                  uint32_t* err_flag, void* stream) {
+  if (rows < 0 || cols < 8) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !q || !scale)) return MOE_ERR_INVALID_ARG;
+  if (axis == 0) {
+    if (cols % 32) return MOE_ERR_UNSUPPORTED;
+    if (group_sizes && (G < 1 || G > 1024)) return MOE_ERR_INVALID_ARG;
+    if (rows > 0 && (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u))) return MOE_ERR_ALIGNMENT;
+  } else if (axis == 1) {
+    if (!group_sizes || G < 1 || G > 1024) return MOE_ERR_INVALID_ARG;
+    if (cols % 8) return MOE_ERR_UNSUPPORTED;
+    if (rows > 0 && (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u) ||
+                     (reinterpret_cast<uintptr_t>(scale) & 7u)))
+      return MOE_ERR_ALIGNMENT;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return mxfp8_group_quantize_launch(x, rows, cols, axis, group_sizes, G, q, scale, err_flag, S(stream));
+}
+
+}  // extern "C"

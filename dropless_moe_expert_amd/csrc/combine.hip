@@ -1,0 +1,176 @@
+// Unpermute-and-combine, its backward, and the SwiGLU backward.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine", Figure 3 and section "Optimization 2": combine brings expert
+// outputs back to the original token order and accumulates them;
+// "AI Systems Performance Engineering" ch. 1, §2.3.2 dispatch/combine table:
+// the accumulation is a weighted sum by the routing weights.
+//
+// All three are HBM-bound: one wavefront per token (or row), 16-byte vector
+// loads/stores, fp32 arithmetic, bf16 storage.
+#include "common.h"
+
+namespace moe {
+
+// y[t] = bf16(sum_k w[t,k] * y_perm[perm_dst[t*K+k]]), k ascending.
+__global__ __launch_bounds__(256) void unpermute_combine_kernel(const uint16_t* __restrict__ y_perm,
+                                                                const float* __restrict__ w,
+                                                                const int32_t* __restrict__ perm_dst, int64_t T,
+                                                                int d, int K, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int32_t my_row = 0;
+  float my_w = 1.f;
+  if (lane < K) {
+    my_row = perm_dst[t * K + lane];
+    if (w) my_w = w[t * K + lane];
+  }
+  // broadcast the K rows and weights while every lane is active
+  int32_t rows[32];
+  float ws[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
+    ws[k] = (k < K) ? __shfl(my_w, k, 64) : 0.f;
+  }
+  const int nvec = d / 8;
+  for (int v = lane; v < nvec; v += 64) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k >= K) break;
+      const int32_t r = rows[k];
+      const float wk = ws[k];
+      float f[8];
+      unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d)[v], f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wk, f[j], acc[j]);
+    }
+    reinterpret_cast<uint4*>(y + t * d)[v] = pack8(acc);
+  }
+}
+
+// dy_perm[perm_dst[t,k]] = bf16(w[t,k] * dy[t]);  dw[t,k] = <dy[t], y_perm[perm_dst[t,k]]>
+__global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* __restrict__ dy,
+                                                               const uint16_t* __restrict__ y_perm,
+                                                               const float* __restrict__ w,
+                                                               const int32_t* __restrict__ perm_dst, int64_t T,
+                                                               int d, int K, uint16_t* __restrict__ dy_perm,
+                                                               float* __restrict__ dw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int32_t my_row = 0;
+  float my_w = 0.f;
+  if (lane < K) {
+    my_row = perm_dst[t * K + lane];
+    my_w = w[t * K + lane];
+  }
+  float dot[32];
+  int32_t rows[32];
+  float ws[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    dot[k] = 0.f;
+    rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
+    ws[k] = (k < K) ? __shfl(my_w, k, 64) : 0.f;
+  }
+  const int nvec = d / 8;
+  for (int v = lane; v < nvec; v += 64) {
+    float g[8];
+    unpack8(reinterpret_cast<const uint4*>(dy + t * d)[v], g);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      if (k < K) {
+        const int32_t r = rows[k];
+        const float wk = ws[k];
+        float yv[8], o[8];
+        unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d)[v], yv);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          s = fmaf(g[j], yv[j], s);
+          o[j] = wk * g[j];
+        }
+        dot[k] += s;
+        reinterpret_cast<uint4*>(dy_perm + (int64_t)r * d)[v] = pack8(o);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    if (k < K) {
+      const float s = wave_sum(dot[k]);
+      if (lane == 0) dw[t * K + k] = s;
+    }
+  }
+}
+
+// dgu = [dg | du] from gu = [g | u], dh; rows < sum(group_sizes) (or all rows)
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(const uint16_t* __restrict__ gu,
+                                                              const uint16_t* __restrict__ dh, int64_t m_cap, int f,
+                                                              const int32_t* __restrict__ group_sizes, int G,
+                                                              uint16_t* __restrict__ dgu) {
+  __shared__ int64_t s_rows;
+  if (threadIdx.x == 0) {
+    int64_t tot = m_cap;
+    if (group_sizes) {
+      tot = 0;
+      for (int g = 0; g < G; ++g) tot += max(group_sizes[g], 0);
+      tot = min(tot, m_cap);
+    }
+    s_rows = tot;
+  }
+  __syncthreads();
+  const int64_t rows = s_rows;
+  const int nvec = f / 8;
+  const int64_t total = rows * nvec;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / nvec;
+    const int v = (int)(idx - r * nvec);
+    float g[8], u[8], d[8], dg[8], du[8];
+    unpack8(reinterpret_cast<const uint4*>(gu + r * 2 * f)[v], g);
+    unpack8(reinterpret_cast<const uint4*>(gu + r * 2 * f + f)[v], u);
+    unpack8(reinterpret_cast<const uint4*>(dh + r * f)[v], d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float s = 1.0f / (1.0f + __expf(-g[j]));
+      dg[j] = d[j] * u[j] * s * (1.0f + g[j] * (1.0f - s));
+      du[j] = d[j] * g[j] * s;
+    }
+    reinterpret_cast<uint4*>(dgu + r * 2 * f)[v] = pack8(dg);
+    reinterpret_cast<uint4*>(dgu + r * 2 * f + f)[v] = pack8(du);
+  }
+}
+
+}  // namespace moe
+
+extern "C" moe_status_t moe_unpermute_combine_launch(const uint16_t* y_perm, const float* w, const int32_t* perm_dst,
+                                                     int64_t T, int32_t d, int32_t K, uint16_t* y, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  hipLaunchKernelGGL(moe::unpermute_combine_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, y_perm, w,
+                     perm_dst, T, d, K, y);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" moe_status_t moe_combine_backward_launch(const uint16_t* dy, const uint16_t* y_perm, const float* w,
+                                                    const int32_t* perm_dst, int64_t T, int32_t d, int32_t K,
+                                                    uint16_t* dy_perm, float* dw, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  hipLaunchKernelGGL(moe::combine_backward_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, dy, y_perm, w,
+                     perm_dst, T, d, K, dy_perm, dw);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" moe_status_t moe_swiglu_backward_launch(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
+                                                   const int32_t* group_sizes, int32_t G, uint16_t* dgu,
+                                                   hipStream_t s) {
+  if (m_cap == 0) return MOE_OK;
+  const int64_t work = m_cap * (f / 8);
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, (int64_t)moe_host::device_cu_count() * 16);
+  hipLaunchKernelGGL(moe::swiglu_backward_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, s, gu,
+                     dh, m_cap, f, group_sizes, G, dgu);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -1,0 +1,584 @@
+// Grouped GEMM over ragged expert groups (bf16 and MXFP8), persistent, with
+// a device-side tile scheduler.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine", section "Optimization 1: Grouped GEMM": every expert's matmul in
+// one kernel call, each with its true token count, computing only the
+// regions with valid tokens, with no device-to-host copy of the counts
+// (which would break graph capture); MXFP8 block scaling for the expert
+// matmuls.  Section "What specialized optimizations are required for
+// dropless MoE?": the counts may be invisible to the CPU.
+//
+// Design (gfx950):
+//  * The grid is a function of host arguments only (CU count, m_cap, G,
+//    N, K).  Each workgroup reads group_sizes once, builds the row prefix and
+//    the m-tile prefix of the groups in LDS, and walks the flat tile index
+//    space [0, m_tiles * n_tiles) with a grid stride, so only tiles holding
+//    valid rows are ever computed; the last tile of a group masks its tail.
+//  * 256 x 256 output tile, 4 wavefronts (2 x 2), 128 x 128 per wavefront as
+//    8 x 8 MFMA 16x16x32 bf16 (or 16x16x128 scaled fp8) accumulators.
+//  * Operands are staged through LDS in 2 stages of 64 bf16 (128 fp8) along
+//    K: 128-byte rows, 16-byte slots XOR-swizzled by (row >> 1) & 7.
+//    K-contiguous sources go straight from HBM/L2 to LDS with
+//    global_load_lds_dwordx4; K-outer sources (the data-gradient weight, both
+//    weight-gradient operands) are loaded as 8x8 blocks, transposed in
+//    registers and written as 16-byte rows.
+//  * The MFMA computes D[n][m] (weights as the first operand), so each lane
+//    holds 4 consecutive output columns of one row: 8-byte bf16 stores; for
+//    SwiGLU a wavefront owns matching gate and up columns and applies
+//    silu(g) * u in registers.
+//  * Workgroup ids are remapped so that consecutive tiles run on the same XCD
+//    (the hardware deals workgroups round-robin over the 8 XCDs), keeping the
+//    A and B panels that neighbouring tiles share in one L2.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxGroups = 1024;
+constexpr int kBM = 256, kBN = 256;     // output tile (rows m, columns n)
+constexpr int kWM = 2, kWN = 2;         // wavefront grid
+constexpr int kThreads = kWM * kWN * 64;
+constexpr int kRowBytes = 128;          // one LDS row of a stage: 64 bf16 / 128 fp8
+constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;  // wavefront tile
+constexpr int kTM = kWTM / 16, kTN = kWTN / 16;    // MFMA subtiles per wavefront
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
+
+enum { MODE_M_NK = 0, MODE_M_KN = 1, MODE_K = 2 };
+
+struct GGArgs {
+  const uint8_t* A;        // activations (bytes)
+  const uint8_t* B;        // weights / second operand (bytes)
+  const uint8_t* As;       // MXFP8 scales of A
+  const uint8_t* Bs;       // MXFP8 scales of B
+  const int32_t* sizes;    // device group sizes
+  uint8_t* C;
+  uint8_t* Caux;
+  uint32_t* flag;
+  int64_t m_cap;
+  int G, M, N, K;
+  int n_tiles;             // tiles along n (ragged-M) / q (ragged-K)
+  int p_tiles;             // ragged-K: tiles along p (rows of C[g])
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// ----------------------------------------------------------------- group prefix
+struct GroupInfo {
+  int32_t roff[kMaxGroups + 1];   // clamped row offsets
+  int32_t tpre[kMaxGroups + 1];   // m-tile prefix (ragged-M) / rank order (ragged-K)
+  int32_t scan[kThreads];
+};
+
+// exclusive scan of v over the workgroup (kThreads values), returns exclusive, total in *tot
+__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* buf, int32_t* tot) {
+  const int t = threadIdx.x;
+  buf[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    int32_t add = (t >= o) ? buf[t - o] : 0;
+    __syncthreads();
+    buf[t] += add;
+    __syncthreads();
+  }
+  int32_t incl = buf[t];
+  *tot = buf[kThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Builds roff (row offsets, sizes clamped to >= 0 and to m_cap) and, for
+// ragged-M, tpre = prefix of ceil(size / kBM).  Raises flags from block 0.
+template <bool TILES>
+__device__ void build_groups(const GGArgs& a, GroupInfo& gi) {
+  const int t = threadIdx.x;
+  constexpr int per = kMaxGroups / kThreads;  // 4 groups per thread
+  int32_t s[per];
+  int32_t local = 0;
+  bool neg = false;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    int g = t * per + i;
+    int32_t v = (g < a.G) ? a.sizes[g] : 0;
+    if (v < 0) { neg = true; v = 0; }
+    s[i] = v;
+    local += v;
+  }
+  int32_t tot;
+  int32_t base = block_scan(local, gi.scan, &tot);
+  const int64_t cap = a.m_cap;
+  int64_t o = base;
+#pragma unroll
+  for (int i = 0; i < per; ++i) {
+    int g = t * per + i;
+    if (g <= a.G) gi.roff[g] = (int32_t)min<int64_t>(o, cap);
+    o += s[i];
+  }
+  if (t == kThreads - 1 && a.G == kMaxGroups) gi.roff[kMaxGroups] = (int32_t)min<int64_t>(o, cap);
+  if (blockIdx.x == 0 && t == 0) {
+    if ((int64_t)tot > cap) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
+  }
+  if (blockIdx.x == 0 && __any(neg) && (t & 63) == 0) raise_flag(a.flag, MOE_FLAG_NEGATIVE_SIZE);
+  __syncthreads();
+  if (TILES) {
+    int32_t lt = 0;
+    int32_t nt[per];
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      int g = t * per + i;
+      int32_t rows = (g < a.G) ? gi.roff[g + 1] - gi.roff[g] : 0;
+      nt[i] = (rows + kBM - 1) / kBM;
+      lt += nt[i];
+    }
+    int32_t tt;
+    int32_t b = block_scan(lt, gi.scan, &tt);
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      int g = t * per + i;
+      if (g <= a.G) gi.tpre[g] = b;
+      b += nt[i];
+    }
+    if (t == kThreads - 1 && a.G == kMaxGroups) gi.tpre[kMaxGroups] = b;
+    __syncthreads();
+  } else {
+    // ragged-K: order groups by size, largest first (ties: lower index first),
+    // so the longest contractions start earliest.  tpre[rank] = group.
+    for (int g = t; g < a.G; g += kThreads) {
+      const int32_t sg = gi.roff[g + 1] - gi.roff[g];
+      int rank = 0;
+      for (int h = 0; h < a.G; ++h) {
+        const int32_t sh = gi.roff[h + 1] - gi.roff[h];
+        rank += (sh > sg) || (sh == sg && h < g);
+      }
+      gi.tpre[rank] = g;
+    }
+    __syncthreads();
+  }
+}
+
+// last g in [0, G) with tpre[g] <= mt
+__device__ __forceinline__ int find_group(const int32_t* tpre, int G, int mt) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (tpre[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ----------------------------------------------------------------- loaders
+// K-contiguous rows straight into LDS.  Tile row r of the stage comes from
+// global row grow(r); 16-byte slot (r, s) holds chunk swz(r, s) of that row.
+template <int R, typename RowFn>
+__device__ __forceinline__ void load_rows_direct(uint8_t* lds, const uint8_t* g, int64_t ld_bytes, int64_t k0_bytes,
+                                                 RowFn grow) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NW = kThreads / 64;
+#pragma unroll
+  for (int i = 0; i < R / 8 / NW; ++i) {
+    const int blk = i * NW + wave;
+    const int row = blk * 8 + (lane >> 3);
+    // swz(row, lane & 7): (row >> 1) & 7 = ((blk & 1) << 2) | (lane >> 4), and blk & 1 = wave & 1
+    static_assert(NW % 2 == 0, "swizzle shortcut needs an even wavefront count");
+    const int chunk = (lane & 7) ^ (((wave & 1) << 2) | (lane >> 4));
+    const uint8_t* src = g + grow(row) * ld_bytes + k0_bytes + chunk * 16;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(lds + blk * 1024), 16, 0, 0);
+  }
+}
+
+// Per-row 4-byte scale words (MXFP8: 4 blocks of 32 for a 128-wide stage).
+template <int R, typename RowFn>
+__device__ __forceinline__ void load_scales_direct(uint8_t* lds, const uint8_t* s, int64_t ld, int64_t kb0,
+                                                   RowFn grow) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NW = kThreads / 64;
+#pragma unroll
+  for (int i = 0; i < R / 64 / NW; ++i) {
+    const int blk = i * NW + wave;
+    const int row = blk * 64 + lane;
+    const uint8_t* src = s + grow(row) * ld + kb0;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(lds + blk * 256), 4, 0, 0);
+  }
+}
+
+// K-outer source: element (k, c) at g[k * ld + c] (bf16).  Tile row r = column
+// c0 + r; stage k-range [k0, k0 + 64) with rows k >= k_end read as zero and
+// columns clamped to [0, ncols).  Each thread moves R / 256 blocks of 8 x 8.
+template <int R>
+struct KOuterLoad {
+  uint4 v[R / kThreads][8];
+  __device__ __forceinline__ void issue(const uint16_t* g, int64_t ld, int64_t k0, int64_t k_end, int c0, int ncols) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < R / kThreads; ++i) {
+      const int b = t + i * kThreads;
+      const int nb = b % (R / 8), kb = b / (R / 8);
+      int c = c0 + nb * 8;
+      if (c > ncols - 8) c = ncols - 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int64_t k = k0 + kb * 8 + q;
+        v[i][q] = (k < k_end) ? *reinterpret_cast<const uint4*>(g + k * ld + c) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < R / kThreads; ++i) {
+      const int b = t + i * kThreads;
+      const int nb = b % (R / 8), kb = b / (R / 8);
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(v[i]);  // w[q*4 + p]: row k=q, cols 2p, 2p+1
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t lo = w[(2 * p) * 4 + (j >> 1)], hi = w[(2 * p + 1) * 4 + (j >> 1)];
+          o[p] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+        const int row = nb * 8 + j;
+        *reinterpret_cast<uint4*>(lds + row * kRowBytes + swz(row, kb) * 16) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+};
+
+// ----------------------------------------------------------------- compute
+template <bool MX>
+struct Frag;
+
+template <>
+struct Frag<false> {
+  typedef bf16x8_t T;
+};
+template <>
+struct Frag<true> {
+  typedef i32x8_t T;
+};
+
+// A fragment row of a stage: tile rows base + 16*i share the swizzle of
+// base (16*i only moves (row >> 1) & 7 by multiples of 8), so a lane's slot is
+// fixed for a whole stage: slot = chunk ^ ((r16 >> 1) & 7) for wavefront
+// tiles aligned to 16 rows.
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* lds, int row, int slot) {
+  return *reinterpret_cast<const uint4*>(lds + row * kRowBytes + slot * 16);
+}
+
+// One stage: W tile rows [0, kBN) at lw, X tile rows [0, kBM) at lx.
+template <bool MX>
+__device__ __forceinline__ void compute_stage(const uint8_t* lw, const uint8_t* lx, const uint8_t* sw,
+                                              const uint8_t* sx, f32x4_t (&acc)[kTN][kTM]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave / kWM, wm = wave % kWM;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int slot0 = g4 ^ ((r16 >> 1) & 7);  // chunk g4 (bf16 k-step 0 / fp8 low half)
+  const int wrow0 = wn * kWTN + r16, xrow0 = wm * kWTM + r16;
+  if constexpr (!MX) {
+#pragma unroll 1
+    for (int s = 0; s < 2; ++s) {
+      const int slot = slot0 ^ (s << 2);  // chunk s*4 + g4
+      bf16x8_t wf[kTN], xf[kTM];
+#pragma unroll
+      for (int i = 0; i < kTN; ++i) wf[i] = __builtin_bit_cast(bf16x8_t, lds_read16(lw, wrow0 + i * 16, slot));
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) xf[j] = __builtin_bit_cast(bf16x8_t, lds_read16(lx, xrow0 + j * 16, slot));
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
+#pragma unroll
+        for (int j = 0; j < kTM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    }
+  } else {
+    i32x8_t wf[kTN], xf[kTM];
+    int wsc[kTN], xsc[kTM];
+#pragma unroll
+    for (int i = 0; i < kTN; ++i) {
+      const int row = wrow0 + i * 16;
+      const uint4 lo = lds_read16(lw, row, slot0), hi = lds_read16(lw, row, slot0 ^ 4);
+      wf[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      wsc[i] = sw[row * 4 + g4];
+    }
+#pragma unroll
+    for (int j = 0; j < kTM; ++j) {
+      const int row = xrow0 + j * 16;
+      const uint4 lo = lds_read16(lx, row, slot0), hi = lds_read16(lx, row, slot0 ^ 4);
+      xf[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      xsc[j] = sx[row * 4 + g4];
+    }
+#pragma unroll
+    for (int i = 0; i < kTN; ++i)
+#pragma unroll
+      for (int j = 0; j < kTM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xf[j], acc[i][j], 0, 0, 0, wsc[i], 0, xsc[j]);
+  }
+}
+
+// ----------------------------------------------------------------- epilogue
+template <int OUT>
+__device__ __forceinline__ void store_sub(uint8_t* C, int64_t ldc, int64_t m, int n, const f32x4_t& v) {
+  if constexpr (OUT == MOE_OUT_F32) {
+    *reinterpret_cast<float4*>(C + (m * ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    *reinterpret_cast<uint2*>(C + (m * ldc + n) * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
+// Writes the wavefront's accumulators.  Plain: column n0 + wn*kWTN + 16i + 4*g4.
+// SwiGLU: subtiles i < kTN/2 are gate columns j = n0 + wn*kWTN/2 + 16i + 4*g4
+// and subtiles i + kTN/2 the up columns of the same j; the pre-activations go
+// to Caux first, then h = silu(g) * u is formed in place and stored.
+template <int EPI, int OUT>
+__device__ __forceinline__ void store_tile(const GGArgs& a, f32x4_t (&acc)[kTN][kTM], int64_t m0, int rows, int n0,
+                                           int ncols, int64_t ldc, uint8_t* C, int f) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave / kWM, wm = wave % kWM;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  if constexpr (EPI == MOE_EPI_SWIGLU) {
+    const int jbase = n0 + wn * (kWTN / 2) + g4 * 4;
+    if (a.Caux) {
+      uint8_t* aux = a.Caux;
+      const int64_t lda = 2 * (int64_t)f;
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) {
+        const int mr = wm * kWTM + j * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < kTN / 2; ++i) {
+          const int jc = jbase + i * 16;
+          if (mr < rows && jc < f) {
+            store_sub<MOE_OUT_BF16>(aux, lda, m0 + mr, jc, acc[i][j]);
+            store_sub<MOE_OUT_BF16>(aux, lda, m0 + mr, f + jc, acc[i + kTN / 2][j]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTN / 2; ++i)
+#pragma unroll
+      for (int j = 0; j < kTM; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][q] = silu_f32(acc[i][j][q]) * acc[i + kTN / 2][j][q];
+#pragma unroll
+    for (int j = 0; j < kTM; ++j) {
+      const int mr = wm * kWTM + j * 16 + r16;
+#pragma unroll
+      for (int i = 0; i < kTN / 2; ++i) {
+        const int jc = jbase + i * 16;
+        if (mr < rows && jc < f) store_sub<MOE_OUT_BF16>(C, ldc, m0 + mr, jc, acc[i][j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kTM; ++j) {
+      const int mr = wm * kWTM + j * 16 + r16;
+#pragma unroll
+      for (int i = 0; i < kTN; ++i) {
+        const int n = n0 + wn * kWTN + i * 16 + g4 * 4;
+        if (mr < rows && n < ncols) store_sub<OUT>(C, ldc, m0 + mr, n, acc[i][j]);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int worker_id() {
+  // consecutive worker ids share an XCD (blocks are dealt round-robin to 8 XCDs)
+  const int nb = gridDim.x;
+  if (nb % 8) return blockIdx.x;
+  return (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+}
+
+// ----------------------------------------------------------------- kernel
+template <int MODE, bool MX, int EPI, int OUT>
+__global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
+  extern __shared__ __align__(1024) uint8_t smem[];
+  // two operand stages, then (MXFP8) per stage W scales [kBN][4] and X scales [kBM][4]
+  auto stage = [&](int i) -> uint8_t* { return smem + i * kStageBytes; };
+  auto sstage = [&](int i) -> uint8_t* { return smem + 2 * kStageBytes + i * (kBN + kBM) * 4; };
+  GroupInfo& gi = *reinterpret_cast<GroupInfo*>(smem + 2 * kStageBytes + (MX ? 2 * (kBN + kBM) * 4 : 0));
+
+  build_groups<MODE != MODE_K>(a, gi);
+
+  const int wid = worker_id();
+  const int f = a.N / 2;  // SwiGLU width
+
+  if constexpr (MODE != MODE_K) {
+    const int64_t total = (int64_t)gi.tpre[a.G] * a.n_tiles;
+    const int elt = MX ? 1 : 2;
+    const int64_t lda_b = (int64_t)a.K * elt;
+    const int nk = a.K / (MX ? 128 : 64);
+    for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+      const int mt = (int)(tile / a.n_tiles), nt = (int)(tile % a.n_tiles);
+      const int g = find_group(gi.tpre, a.G, mt);
+      const int64_t m0 = gi.roff[g] + (int64_t)(mt - gi.tpre[g]) * kBM;
+      const int rows = (int)min<int64_t>(kBM, gi.roff[g + 1] - m0);
+      const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (kBN / 2) : nt * kBN;
+      const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
+
+      auto xrow = [&](int r) -> int64_t { return m0 + min(r, rows - 1); };
+      auto wrow = [&](int r) -> int64_t {
+        if constexpr (EPI == MOE_EPI_SWIGLU) {
+          const int wn = r / kWTN, q = r % kWTN;
+          int jj = n0 + wn * (kWTN / 2) + (q % (kWTN / 2));
+          jj = min(jj, f - 1);
+          return (int64_t)g * nrows_b + (q < kWTN / 2 ? jj : f + jj);
+        } else {
+          return (int64_t)g * nrows_b + min(n0 + r, a.N - 1);
+        }
+      };
+      const uint16_t* Bkn = reinterpret_cast<const uint16_t*>(a.B) + (int64_t)g * a.K * a.N;
+      KOuterLoad<kBN> wl;
+
+      f32x4_t acc[kTN][kTM];
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
+#pragma unroll
+        for (int j = 0; j < kTM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      __syncthreads();  // the previous tile's last stage has been read by everyone
+      // prologue: stage 0
+      load_rows_direct<kBM>(stage(0) + kBN * kRowBytes, a.A, lda_b, 0, xrow);
+      if constexpr (MODE == MODE_M_NK) {
+        load_rows_direct<kBN>(stage(0), a.B, lda_b, 0, wrow);
+      } else {
+        wl.issue(Bkn, a.N, 0, a.K, n0, a.N);
+        wl.store(stage(0));
+      }
+      if constexpr (MX) {
+        load_scales_direct<kBM>(sstage(0) + kBN * 4, a.As, a.K / 32, 0, xrow);
+        load_scales_direct<kBN>(sstage(0), a.Bs, a.K / 32, 0, wrow);
+      }
+      for (int kt = 0; kt < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int cur = kt & 1, nxt = cur ^ 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+          const int64_t kb = (int64_t)(kt + 1) * kRowBytes;
+          load_rows_direct<kBM>(stage(nxt) + kBN * kRowBytes, a.A, lda_b, kb, xrow);
+          if constexpr (MODE == MODE_M_NK) {
+            load_rows_direct<kBN>(stage(nxt), a.B, lda_b, kb, wrow);
+          } else {
+            wl.issue(Bkn, a.N, (int64_t)(kt + 1) * 64, a.K, n0, a.N);
+          }
+          if constexpr (MX) {
+            load_scales_direct<kBM>(sstage(nxt) + kBN * 4, a.As, a.K / 32, (kt + 1) * 4, xrow);
+            load_scales_direct<kBN>(sstage(nxt), a.Bs, a.K / 32, (kt + 1) * 4, wrow);
+          }
+        }
+        compute_stage<MX>(stage(cur), stage(cur) + kBN * kRowBytes, sstage(cur), sstage(cur) + kBN * 4, acc);
+        if constexpr (MODE == MODE_M_KN) {
+          if (more) wl.store(stage(nxt));
+        }
+      }
+      store_tile<EPI, OUT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N,
+                           EPI == MOE_EPI_SWIGLU ? f : a.N, a.C, f);
+    }
+  } else {
+    // ragged-K: C[g] [M, N] = sum over the group's rows r of A[r, p] * B[r, q]
+    const int per_group = a.p_tiles * a.n_tiles;
+    const int64_t total = (int64_t)a.G * per_group;
+    const uint16_t* A16 = reinterpret_cast<const uint16_t*>(a.A);
+    const uint16_t* B16 = reinterpret_cast<const uint16_t*>(a.B);
+    for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+      const int rank = (int)(tile / per_group), rem = (int)(tile % per_group);
+      const int g = gi.tpre[rank];
+      const int pt = rem / a.n_tiles, qt = rem % a.n_tiles;
+      const int p0 = pt * kBM, q0 = qt * kBN;
+      const int64_t r0 = gi.roff[g], r1 = gi.roff[g + 1];
+      const int nk = (int)((r1 - r0 + 63) / 64);
+      KOuterLoad<kBM> xl;
+      KOuterLoad<kBN> wl;
+      f32x4_t acc[kTN][kTM];
+#pragma unroll
+      for (int i = 0; i < kTN; ++i)
+#pragma unroll
+        for (int j = 0; j < kTM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      if (nk > 0) {
+        xl.issue(A16, a.M, r0, r1, p0, a.M);
+        wl.issue(B16, a.N, r0, r1, q0, a.N);
+        xl.store(stage(0) + kBN * kRowBytes);
+        wl.store(stage(0));
+      }
+      for (int kt = 0; kt < nk; ++kt) {
+        __syncthreads();
+        const int cur = kt & 1, nxt = cur ^ 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+          xl.issue(A16, a.M, r0 + (int64_t)(kt + 1) * 64, r1, p0, a.M);
+          wl.issue(B16, a.N, r0 + (int64_t)(kt + 1) * 64, r1, q0, a.N);
+        }
+        compute_stage<false>(stage(cur), stage(cur) + kBN * kRowBytes, nullptr, nullptr, acc);
+        if (more) {
+          xl.store(stage(nxt) + kBN * kRowBytes);
+          wl.store(stage(nxt));
+        }
+      }
+      uint8_t* Cg = a.C + (int64_t)g * a.M * a.N * (OUT == MOE_OUT_F32 ? 4 : 2);
+      store_tile<MOE_EPI_NONE, OUT>(a, acc, p0, min(kBM, a.M - p0), q0, a.N, a.N, Cg, 0);
+    }
+  }
+}
+
+template <int MODE, bool MX, int EPI, int OUT>
+static moe_status_t launch(const GGArgs& a, hipStream_t s, int64_t max_tiles) {
+  const size_t smem = 2 * (size_t)kStageBytes + (MX ? 2 * (kBN + kBM) * 4 : 0) + sizeof(GroupInfo);
+  auto kern = grouped_gemm_kernel<MODE, MX, EPI, OUT>;
+  static bool attr_set = false;  // per process; the attribute is per function
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+      return MOE_ERR_HIP;
+    attr_set = true;
+  }
+  int64_t grid = moe_host::device_cu_count();
+  if (max_tiles < grid) grid = max_tiles;
+  if (grid <= 0) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), smem, s, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe
+
+extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A, const uint8_t* As, const void* B,
+                                            const uint8_t* Bs, const int32_t* sizes, void* C, void* Caux,
+                                            uint32_t* flag, hipStream_t s) {
+  using namespace moe;
+  GGArgs a;
+  a.A = reinterpret_cast<const uint8_t*>(A);
+  a.B = reinterpret_cast<const uint8_t*>(B);
+  a.As = As;
+  a.Bs = Bs;
+  a.sizes = sizes;
+  a.C = reinterpret_cast<uint8_t*>(C);
+  a.Caux = reinterpret_cast<uint8_t*>(Caux);
+  a.flag = flag;
+  a.m_cap = d->m_cap;
+  a.G = d->G;
+  a.M = d->M;
+  a.N = d->N;
+  a.K = d->K;
+  if (d->ragged == MOE_RAGGED_M) {
+    const int ncols = d->epilogue == MOE_EPI_SWIGLU ? d->N / 2 : d->N;
+    const int bn = d->epilogue == MOE_EPI_SWIGLU ? kBN / 2 : kBN;
+    a.n_tiles = (ncols + bn - 1) / bn;
+    a.p_tiles = 0;
+    const int64_t max_m_tiles = (d->m_cap + kBM - 1) / kBM + d->G;
+    const int64_t max_tiles = max_m_tiles * a.n_tiles;
+    if (d->dtype == MOE_DTYPE_MXFP8) {
+      if (d->epilogue == MOE_EPI_SWIGLU) return launch<MODE_M_NK, true, MOE_EPI_SWIGLU, MOE_OUT_BF16>(a, s, max_tiles);
+      return launch<MODE_M_NK, true, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
+    }
+    if (d->b_layout == MOE_B_NK) {
+      if (d->epilogue == MOE_EPI_SWIGLU) return launch<MODE_M_NK, false, MOE_EPI_SWIGLU, MOE_OUT_BF16>(a, s, max_tiles);
+      if (d->out_dtype == MOE_OUT_F32) return launch<MODE_M_NK, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
+      return launch<MODE_M_NK, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
+    }
+    if (d->out_dtype == MOE_OUT_F32) return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
+    return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
+  }
+  a.n_tiles = (d->N + kBN - 1) / kBN;
+  a.p_tiles = (d->M + kBM - 1) / kBM;
+  const int64_t max_tiles = (int64_t)d->G * a.n_tiles * a.p_tiles;
+  if (d->out_dtype == MOE_OUT_F32) return launch<MODE_K, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
+  return launch<MODE_K, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
+}

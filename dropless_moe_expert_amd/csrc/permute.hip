@@ -1,0 +1,166 @@
+// Permute = dispatch, local part: a stable counting sort of (token, expert)
+// pairs into expert-contiguous rows, then the row copy of x.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine", section "Optimization 2": dispatch reorders tokens locally by
+// expert before the exchange; Figure 3: combine restores the original order.
+//
+// Three launches, no atomics deciding any order:
+//   1. rank:    one wavefront per chunk of kChunk pairs.  Pairs are taken 64 at
+//               a time in pair order; a lane's rank among equal experts in
+//               the chunk = running count + lanes below it with the same
+//               expert (found with 8 ballots over the id bits).  Writes the
+//               local rank of every pair and the chunk's per-expert counts.
+//   2. scan:    one workgroup: per expert, an exclusive scan over chunks; the
+//               totals are group_sizes; their exclusive scan is group_offsets;
+//               chunk bases become absolute row offsets.
+//   3. scatter: one wavefront per token: row r = base[chunk][e] + local rank
+//               for each of its K pairs; writes perm_dst / perm_src and copies
+//               the token's row once from HBM to its K destinations (16-byte
+//               vector loads and stores).
+#include "common.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;  // pairs per rank wavefront
+
+__global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
+                                                          int32_t* __restrict__ local_rank,
+                                                          int32_t* __restrict__ chunk_counts, uint32_t* flag) {
+  __shared__ int32_t running[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) running[e] = 0;
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t c1 = min(M, c0 + kChunk);
+  bool bad = false;
+  for (int64_t base = c0; base < c1; base += 64) {
+    const int64_t i = base + lane;
+    const bool valid = i < c1;
+    int e = valid ? ids[i] : 0;
+    if (valid && (e < 0 || e >= E)) { bad = true; e = E - 1; }
+    // lanes with the same expert: AND over the 8 id bits of (ballot or its complement)
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      same &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int before = __popcll(same & below);
+    const int total = __popcll(same);
+    int r = 0;
+    if (valid) r = running[e] + before;
+    __syncthreads();  // all lanes read running[] before the update
+    if (valid) {
+      local_rank[i] = r;
+      if (before == total - 1) running[e] += total;  // highest lane of the class updates
+    }
+    __syncthreads();
+  }
+  if (__any(bad) && lane == 0) raise_flag(flag, MOE_FLAG_BAD_EXPERT_ID);
+  for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)blockIdx.x * E + e] = running[e];
+}
+
+__global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
+                                                           int32_t* __restrict__ group_sizes,
+                                                           int32_t* __restrict__ group_offsets) {
+  __shared__ int32_t tot[256];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunk; ++c) {
+      int32_t v = chunk_counts[(int64_t)c * E + e];
+      chunk_counts[(int64_t)c * E + e] = run;  // exclusive within the expert
+      run += v;
+    }
+  }
+  tot[e] = (e < E) ? run : 0;
+  __syncthreads();
+  // exclusive scan over experts (E <= 256; a plain serial scan by one thread
+  // would do, a Hillis-Steele scan keeps it short)
+  int32_t incl = tot[e];
+  for (int o = 1; o < 256; o <<= 1) {
+    int32_t add = (e >= o) ? tot[e - o] : 0;
+    __syncthreads();
+    incl += add;
+    tot[e] = incl;
+    __syncthreads();
+  }
+  const int32_t excl = incl - run;
+  if (e < E) {
+    group_sizes[e] = run;
+    group_offsets[e] = excl;
+    for (int c = 0; c < nchunk; ++c) chunk_counts[(int64_t)c * E + e] += excl;
+  }
+  if (e == E - 1) group_offsets[E] = incl;
+}
+
+// one wavefront per token
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __restrict__ x,
+                                                              const int32_t* __restrict__ ids,
+                                                              const int32_t* __restrict__ local_rank,
+                                                              const int32_t* __restrict__ chunk_base, int64_t T,
+                                                              int d, int E, int K, int32_t* __restrict__ perm_src,
+                                                              int32_t* __restrict__ perm_dst,
+                                                              uint16_t* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  // lane k < K resolves pair k
+  int32_t my_row = 0;
+  if (lane < K) {
+    const int64_t i = t * K + lane;
+    int e = ids[i];
+    if (e < 0 || e >= E) e = E - 1;
+    my_row = chunk_base[(i / kChunk) * E + e] + local_rank[i];
+    perm_dst[i] = my_row;
+    perm_src[my_row] = (int32_t)i;
+  }
+  if (x == nullptr) return;
+  // broadcast the K destination rows while every lane is active
+  int32_t rows[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  const int nvec = d / 8;
+  for (int v = lane; v < nvec; v += 64) {
+    const uint4 val = src[v];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (k < K) reinterpret_cast<uint4*>(x_perm + (int64_t)rows[k] * d)[v] = val;
+  }
+}
+
+}  // namespace moe
+
+extern "C" size_t moe_permute_ws_bytes_impl(int64_t T, int32_t E, int32_t K) {
+  const int64_t M = T * K;
+  const int64_t nchunk = (M + moe::kChunk - 1) / moe::kChunk;
+  size_t a = (size_t)M * 4;
+  a = (a + 255) & ~(size_t)255;
+  size_t b = (size_t)nchunk * E * 4;
+  return a + ((b + 255) & ~(size_t)255);
+}
+
+extern "C" moe_status_t moe_permute_launch(const uint16_t* x, const int32_t* ids, int64_t T, int32_t d, int32_t E,
+                                           int32_t K, int32_t* group_sizes, int32_t* group_offsets,
+                                           int32_t* perm_src, int32_t* perm_dst, uint16_t* x_perm, void* ws,
+                                           uint32_t* flag, hipStream_t s) {
+  const int64_t M = T * K;
+  const int64_t nchunk = (M + moe::kChunk - 1) / moe::kChunk;
+  int32_t* local_rank = reinterpret_cast<int32_t*>(ws);
+  size_t a = ((size_t)M * 4 + 255) & ~(size_t)255;
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + a);
+  if (M > 0) {
+    hipLaunchKernelGGL(moe::permute_rank_kernel, dim3((unsigned)nchunk), dim3(64), 0, s, ids, M, E, local_rank,
+                       chunk_counts, flag);
+  }
+  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+                     group_offsets);
+  if (T > 0) {
+    hipLaunchKernelGGL(moe::permute_scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, ids,
+                       local_rank, chunk_counts, T, d, E, K, perm_src, perm_dst, x_perm);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

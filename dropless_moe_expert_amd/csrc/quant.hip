@@ -1,0 +1,179 @@
+// Group-aware MXFP8 quantisation: bf16 -> E4M3 codes + one E8M0 scale per
+// block of 32.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine": group-aware MXFP8 quantisation is one of the building blocks
+// (section "What specialized optimizations are required for dropless MoE?")
+// and feeds MXFP8 block scaling of the expert matmuls (section "Optimization
+// 1").  "AI Systems Performance Engineering" ch. 1, §1.1 low-precision
+// scaling figure: each group of (usually) 32 values gets its own scale.
+// Scale rule (OCP MX v1.0): e = floor(log2 amax) - 8 (8 = largest E4M3
+// exponent) clamped to [-127, 127], byte = e + 127; codes are the E4M3FN
+// round-to-nearest-even of v * 2^-e clamped to +-448.
+//
+// v * 2^-e is exact in fp32 (bf16 input times a power of two that keeps the
+// result below 512); v_cvt_pk_fp8_f32 rounds to nearest even and keeps the
+// sign of zero, so clamping first reproduces the rule exactly.
+#include "common.h"
+
+namespace moe {
+
+// floor(log2(amax)) - 8 from the fp32 bits of a bf16 amax; clamped
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;  // zero or subnormal amax: floor(log2) <= -127
+  return max(-127, min(127, ef - 127 - 8));
+}
+
+__device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+  return (uint32_t)hi;
+}
+
+// multiply by 2^-e with e in [-127, 127]: 2^127 is one step outside the
+// normal-exponent helper, so scale in two exact steps
+__device__ __forceinline__ float scale_pow2(float v, int e) {
+  const int ne = -e;  // in [-127, 127]
+  if (ne >= -126) return v * pow2i(ne);
+  return (v * pow2i(-63)) * pow2i(-64);
+}
+
+// axis 0: 4 lanes per block of 32 (8 values each); rows < rows_valid
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                                            const int32_t* __restrict__ group_sizes, int G,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  __shared__ int64_t s_rows;
+  if (threadIdx.x == 0) {
+    int64_t tot = rows;
+    if (group_sizes) {
+      tot = 0;
+      for (int g = 0; g < G; ++g) tot += max(group_sizes[g], 0);
+      tot = min(tot, rows);
+    }
+    s_rows = tot;
+  }
+  __syncthreads();
+  const int64_t nrows = s_rows;
+  const int nvec = cols / 8;  // 8-element pieces per row
+  const int64_t total = nrows * nvec;
+  // the grid-stride step is a multiple of 4, so the 4 lanes of one block
+  // always move together and the shuffles stay within a block
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx - (threadIdx.x & 3) < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const bool live = idx < total;
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) unpack8(reinterpret_cast<const uint4*>(x)[idx], f);
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int e = mx_exponent(amax);
+    if (live) {
+      uint2 out;
+      out.x = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
+      out.y = cvt4_e4m3(scale_pow2(f[4], e), scale_pow2(f[5], e), scale_pow2(f[6], e), scale_pow2(f[7], e));
+      reinterpret_cast<uint2*>(q)[idx] = out;
+      if ((idx & 3) == 0) scale[idx >> 2] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// axis 1: one thread per (block row p, 8-column piece); blocks restart at groups
+__global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                                            const int32_t* __restrict__ group_sizes, int G,
+                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ scale,
+                                                            uint32_t* flag) {
+  extern __shared__ int64_t sh[];  // [0,G]: group row offsets; [G+1, 2G+2): block prefix
+  int64_t* roff = sh;
+  int64_t* boff = sh + G + 1;
+  if (threadIdx.x == 0) {
+    int64_t o = 0, p = 0;
+    bool neg = false, over = false;
+    for (int g = 0; g < G; ++g) {
+      int64_t s = group_sizes[g];
+      if (s < 0) { neg = true; s = 0; }
+      if (o + s > rows) { over = true; s = rows - o; }
+      roff[g] = o;
+      boff[g] = p;
+      o += s;
+      p += (s + 31) / 32;
+    }
+    roff[G] = o;
+    boff[G] = p;
+    if (neg) raise_flag(flag, MOE_FLAG_NEGATIVE_SIZE);
+    if (over) raise_flag(flag, MOE_FLAG_ROWS_OVER_CAP);
+  }
+  __syncthreads();
+  const int64_t nblk = boff[G];
+  const int npc = cols / 8;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * npc;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = idx / npc;
+    const int c8 = (int)(idx - p * npc) * 8;
+    // group of block p: last g with boff[g] <= p
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (boff[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int64_t r0 = roff[g] + (p - boff[g]) * 32;
+    const int n = (int)min((int64_t)32, roff[g + 1] - r0);
+    float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < n; ++i) {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], fabsf(f[j]));
+    }
+    int e[8];
+    uint2 sc;
+    uint8_t* scb = reinterpret_cast<uint8_t*>(&sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = mx_exponent(amax[j]);
+      scb[j] = (uint8_t)(e[j] + 127);
+    }
+    *reinterpret_cast<uint2*>(scale + p * cols + c8) = sc;
+    for (int i = 0; i < n; ++i) {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
+      uint2 out;
+      out.x = cvt4_e4m3(scale_pow2(f[0], e[0]), scale_pow2(f[1], e[1]), scale_pow2(f[2], e[2]), scale_pow2(f[3], e[3]));
+      out.y = cvt4_e4m3(scale_pow2(f[4], e[4]), scale_pow2(f[5], e[5]), scale_pow2(f[6], e[6]), scale_pow2(f[7], e[7]));
+      *reinterpret_cast<uint2*>(q + (r0 + i) * cols + c8) = out;
+    }
+  }
+}
+
+}  // namespace moe
+
+extern "C" moe_status_t mxfp8_group_quantize_launch(const uint16_t* x, int64_t rows, int32_t cols, int32_t axis,
+                                                    const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,
+                                                    uint32_t* flag, hipStream_t s) {
+  if (rows == 0) return MOE_OK;
+  const int64_t cap = (int64_t)moe_host::device_cu_count() * 16;
+  if (axis == 0) {
+    const int64_t work = rows * (cols / 8);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
+    hipLaunchKernelGGL(moe::mx_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, cols, group_sizes,
+                       G, q, scale);
+  } else {
+    const int64_t work = (rows / 32 + G) * (cols / 8);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
+    const size_t shmem = sizeof(int64_t) * (size_t)(2 * G + 2);
+    hipLaunchKernelGGL(moe::mx_quant_cols_kernel, dim3((unsigned)blocks), dim3(256), shmem, s, x, rows, cols,
+                       group_sizes, G, q, scale, flag);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

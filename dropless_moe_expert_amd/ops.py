@@ -1,0 +1,340 @@
+"""Python binding of libmoe.so: argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels.  torch supplies
+device memory and the current HIP stream; this module allocates outputs,
+checks dtypes and shapes, passes raw pointers through ``ctypes`` and turns a
+non-zero status into an exception.  There is no CPU fallback: without the
+built library (or without a GPU) every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
+
+MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1
+MOE_RAGGED_M, MOE_RAGGED_K = 0, 1
+MOE_B_NK, MOE_B_KN = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
+
+FLAG_BAD_EXPERT_ID = 0x1
+FLAG_ROWS_OVER_CAP = 0x2
+FLAG_NEGATIVE_SIZE = 0x4
+FLAG_NAN_LOGIT = 0x8
+
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
+    "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine", "moe_combine_backward",
+    "moe_swiglu_backward", "mxfp8_group_quantize",
+)
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class GGDesc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("ragged", ctypes.c_int32), ("b_layout", ctypes.c_int32),
+                ("epilogue", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("G", ctypes.c_int32),
+                ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32), ("m_cap", ctypes.c_int64)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIB_PATH, require_gpu: bool = True):
+    """dlopen libmoe.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise MoeError(f"{path} is not built; run dropless_moe_expert_amd.build.build()")
+        if require_gpu and not torch.cuda.is_available():
+            raise MoeError("no GPU visible: the dropless MoE kernels run only on an MI355X (gfx950)")
+        L = ctypes.CDLL(path, mode=ctypes.RTLD_GLOBAL)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        sig = {
+            "moe_abi_version": (ctypes.c_int, []),
+            "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_route_topk": (ctypes.c_int, [P, i64, i32, i32, i32, P, P, P, P]),
+            "moe_permute_workspace_bytes": (sz, [i64, i32, i32]),
+            "moe_permute": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P, P]),
+            "grouped_gemm_workspace_bytes": (sz, [ctypes.POINTER(GGDesc)]),
+            "grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GGDesc), P, P, P, P, P, P, P, P, sz, P, P]),
+            "moe_unpermute_combine": (ctypes.c_int, [P, P, P, i64, i32, i32, P, P]),
+            "moe_combine_backward": (ctypes.c_int, [P, P, P, P, i64, i32, i32, P, P, P]),
+            "moe_swiglu_backward": (ctypes.c_int, [P, P, i64, i32, P, i32, P, P]),
+            "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+        if require_gpu:
+            _check_single_hip_runtime()
+        return _lib
+
+
+def _check_single_hip_runtime() -> None:
+    """libmoe.so must bind to the HIP runtime torch already loaded."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:  # pragma: no cover
+        return
+    if len(paths) > 1:
+        raise MoeError(f"two HIP runtimes are mapped ({sorted(paths)}); streams and pointers would not be shared")
+
+
+def lib():
+    return _lib if _lib is not None else load_library()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib().moe_status_string(status).decode()
+        raise MoeError(f"{what}: status {status} ({msg})")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise MoeError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise MoeError("tensors must be contiguous")
+    return ts[0].device
+
+
+def new_flag(device) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+# ------------------------------------------------------------------ steps
+
+def route_topk(logits: torch.Tensor, K: int, renormalize: bool = True, flag: Optional[torch.Tensor] = None):
+    """-> (topk_ids int32 [T,K], topk_w fp32 [T,K])."""
+    assert logits.dtype == torch.float32 and logits.dim() == 2
+    dev = _dev(logits)
+    T, E = logits.shape
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _check(lib().moe_route_topk(_ptr(logits), T, E, K, int(renormalize), _ptr(ids), _ptr(w), _ptr(flag),
+                                _stream(dev)), "moe_route_topk")
+    return ids, w
+
+
+def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None):
+    """-> dict(group_sizes, group_offsets, perm_src, perm_dst, x_perm)."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2
+    dev = _dev(topk_ids, x)
+    T, K = topk_ids.shape
+    d = 0 if x is None else x.shape[1]
+    if x is not None:
+        assert x.dtype == torch.bfloat16 and x.shape[0] == T
+    M = T * K
+    out = dict(
+        group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
+        group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm_src=torch.empty(M, dtype=torch.int32, device=dev),
+        perm_dst=torch.empty(M, dtype=torch.int32, device=dev),
+        x_perm=None if x is None else torch.empty((M, d), dtype=torch.bfloat16, device=dev),
+    )
+    need = lib().moe_permute_workspace_bytes(T, E, K)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute(_ptr(x), _ptr(topk_ids), T, d, E, K, _ptr(out["group_sizes"]),
+                             _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
+                             _ptr(out["x_perm"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _ptr(flag), _stream(dev)), "moe_permute")
+    return out
+
+
+def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_sizes: torch.Tensor, *, b_layout: int = MOE_B_NK,
+                 epilogue: int = MOE_EPI_NONE, out_dtype: torch.dtype = torch.bfloat16, keep_aux: bool = False,
+                 out: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
+                 flag: Optional[torch.Tensor] = None):
+    """Ragged-M grouped GEMM, bf16.  A [m_cap, K]; B [G, N, K] (NK) or [G, K, N] (KN).
+    Returns C [m_cap, N] (or [m_cap, N/2] with SwiGLU) and, with keep_aux, the
+    pre-activations [m_cap, N].  Rows past sum(group_sizes) are left untouched."""
+    dev = _dev(A, B, group_sizes)
+    assert A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16 and group_sizes.dtype == torch.int32
+    m_cap, Kd = A.shape
+    G = B.shape[0]
+    N = B.shape[1] if b_layout == MOE_B_NK else B.shape[2]
+    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
+    if out is None:
+        out = torch.empty((m_cap, ncols), dtype=out_dtype, device=dev)
+    if keep_aux and aux is None:
+        aux = torch.empty((m_cap, N), dtype=torch.bfloat16, device=dev)
+    d = GGDesc(MOE_DTYPE_BF16, MOE_RAGGED_M, b_layout, epilogue,
+               MOE_OUT_F32 if out_dtype == torch.float32 else MOE_OUT_BF16, G, 0, N, Kd, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(A), None, _ptr(B), None, _ptr(group_sizes), _ptr(out),
+                              _ptr(aux), None, 0, _ptr(flag), _stream(dev)), "grouped_gemm")
+    return (out, aux) if keep_aux else out
+
+
+def grouped_gemm_wgrad(X: torch.Tensor, Y: torch.Tensor, group_sizes: torch.Tensor, *,
+                       out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                       flag: Optional[torch.Tensor] = None):
+    """Ragged-K grouped GEMM: C[g] = sum over group g's rows r of X[r]^T Y[r] -> [G, P, Q]."""
+    dev = _dev(X, Y, group_sizes)
+    m_cap, P = X.shape
+    Q = Y.shape[1]
+    G = group_sizes.numel()
+    if out is None:
+        out = torch.empty((G, P, Q), dtype=out_dtype, device=dev)
+    d = GGDesc(MOE_DTYPE_BF16, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE,
+               MOE_OUT_F32 if out_dtype == torch.float32 else MOE_OUT_BF16, G, P, Q, 0, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(X), None, _ptr(Y), None, _ptr(group_sizes), _ptr(out), None,
+                              None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (ragged K)")
+    return out
+
+
+def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq: torch.Tensor, Bs: torch.Tensor,
+                       group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
+                       out: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None):
+    """MXFP8 ragged-M grouped GEMM.  Aq uint8 [m_cap, K], As uint8 [m_cap, K/32],
+    Bq uint8 [G, N, K], Bs uint8 [G, N, K/32] -> bf16 [m_cap, N] (or N/2 with SwiGLU)."""
+    dev = _dev(Aq, As, Bq, Bs, group_sizes)
+    m_cap, Kd = Aq.shape
+    G, N = Bq.shape[0], Bq.shape[1]
+    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
+    if out is None:
+        out = torch.empty((m_cap, ncols), dtype=torch.bfloat16, device=dev)
+    d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, MOE_B_NK, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bq), _ptr(Bs), _ptr(group_sizes),
+                              _ptr(out), None, None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (mxfp8)")
+    return out
+
+
+def unpermute_combine(y_perm: torch.Tensor, topk_w: Optional[torch.Tensor], perm_dst: torch.Tensor, T: int, K: int,
+                      out: Optional[torch.Tensor] = None):
+    dev = _dev(y_perm, perm_dst, topk_w)
+    d = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    _check(lib().moe_unpermute_combine(_ptr(y_perm), _ptr(topk_w), _ptr(perm_dst), T, d, K, _ptr(out),
+                                       _stream(dev)), "moe_unpermute_combine")
+    return out
+
+
+def combine_backward(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor, perm_dst: torch.Tensor, K: int):
+    """-> (dy_perm bf16 [T*K, d], d_topk_w fp32 [T, K])."""
+    dev = _dev(dy, y_perm, topk_w, perm_dst)
+    T, d = dy.shape
+    dyp = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _check(lib().moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(topk_w), _ptr(perm_dst), T, d, K, _ptr(dyp),
+                                      _ptr(dw), _stream(dev)), "moe_combine_backward")
+    return dyp, dw
+
+
+def swiglu_backward(gu: torch.Tensor, dh: torch.Tensor, group_sizes: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None):
+    dev = _dev(gu, dh, group_sizes)
+    m_cap, f = dh.shape
+    if out is None:
+        out = torch.empty((m_cap, 2 * f), dtype=torch.bfloat16, device=dev)
+    G = 0 if group_sizes is None else group_sizes.numel()
+    _check(lib().moe_swiglu_backward(_ptr(gu), _ptr(dh), m_cap, f, _ptr(group_sizes), G, _ptr(out),
+                                     _stream(dev)), "moe_swiglu_backward")
+    return out
+
+
+def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_sizes: Optional[torch.Tensor] = None,
+                   flag: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """-> (codes uint8 [rows, cols], scales uint8): axis 0 [rows, cols/32]; axis 1 [rows/32 + G, cols]."""
+    dev = _dev(x, group_sizes)
+    assert x.dtype == torch.bfloat16
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if axis == 0:
+        s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    else:
+        s = torch.empty((rows // 32 + group_sizes.numel(), cols), dtype=torch.uint8, device=dev)
+    G = 0 if group_sizes is None else group_sizes.numel()
+    _check(lib().mxfp8_group_quantize(_ptr(x), rows, cols, axis, _ptr(group_sizes), G, _ptr(q), _ptr(s), _ptr(flag),
+                                      _stream(dev)), "mxfp8_group_quantize")
+    return q, s
+
+
+# ------------------------------------------------------------------ the layer
+
+def moe_forward(logits: torch.Tensor, x: torch.Tensor, w1p: torch.Tensor, w2: torch.Tensor, K: int,
+                keep: bool = False, flag: Optional[torch.Tensor] = None):
+    """Router top-K -> permute -> GEMM + SwiGLU -> GEMM -> combine.  Returns y
+    [T, d] and, if keep, the intermediates the backward needs."""
+    E = w1p.shape[0]
+    T = x.shape[0]
+    ids, w = route_topk(logits, K, flag=flag)
+    p = permute(x, ids, E, flag=flag)
+    if keep:
+        h, gu = grouped_gemm(p["x_perm"], w1p, p["group_sizes"], epilogue=MOE_EPI_SWIGLU, keep_aux=True, flag=flag)
+    else:
+        h, gu = grouped_gemm(p["x_perm"], w1p, p["group_sizes"], epilogue=MOE_EPI_SWIGLU, flag=flag), None
+    y_perm = grouped_gemm(h, w2, p["group_sizes"], flag=flag)
+    y = unpermute_combine(y_perm, w, p["perm_dst"], T, K)
+    if not keep:
+        return y, None
+    return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, **p)
+
+
+def moe_backward(dy: torch.Tensor, saved: dict, w1p: torch.Tensor, w2: torch.Tensor, K: int,
+                 flag: Optional[torch.Tensor] = None):
+    """Backward of moe_forward (routing weights' gradient included, router logits' not)."""
+    sizes, dst = saved["group_sizes"], saved["perm_dst"]
+    T = dy.shape[0]
+    dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
+    dh = grouped_gemm(dyp, w2, sizes, b_layout=MOE_B_KN, flag=flag)           # dY_perm [M,d] x W2_e [d,f]
+    dw2 = grouped_gemm_wgrad(dyp, saved["h"], sizes, flag=flag)                # [E, d, f]
+    dgu = swiglu_backward(saved["gu"], dh, sizes)
+    dxp = grouped_gemm(dgu, w1p, sizes, b_layout=MOE_B_KN, flag=flag)          # dGU [M,2f] x W1p_e [2f,d]
+    dw1p = grouped_gemm_wgrad(dgu, saved["x_perm"], sizes, flag=flag)          # [E, 2f, d]
+    dx = unpermute_combine(dxp, None, dst, T, K)
+    return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)
+
+
+def expert_mlp(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1p: torch.Tensor, w2: torch.Tensor,
+               flag: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
+               y: Optional[torch.Tensor] = None):
+    """The expert share alone (rows already permuted): GEMM + SwiGLU, then GEMM."""
+    h = grouped_gemm(x_perm, w1p, group_sizes, epilogue=MOE_EPI_SWIGLU, out=h, flag=flag)
+    return grouped_gemm(h, w2, group_sizes, out=y, flag=flag), h
+
+
+def expert_mlp_mxfp8(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1q, w1s, w2q, w2s,
+                     flag: Optional[torch.Tensor] = None):
+    """MXFP8 expert share: quantise X, GEMM + SwiGLU, quantise H, GEMM.  Weights
+    come pre-quantised ([G, N, K] codes with [G, N, K/32] scales)."""
+    xq, xs = mxfp8_quantize(x_perm, 0, group_sizes, flag=flag)
+    h = grouped_gemm_mxfp8(xq, xs, w1q, w1s, group_sizes, epilogue=MOE_EPI_SWIGLU, flag=flag)
+    hq, hs = mxfp8_quantize(h, 0, group_sizes, flag=flag)
+    y = grouped_gemm_mxfp8(hq, hs, w2q, w2s, group_sizes, flag=flag)
+    return y, dict(xq=xq, xs=xs, h=h, hq=hq, hs=hs)
+
+
+def quantize_weights(w: torch.Tensor):
+    """[G, N, K] bf16 -> (codes [G, N, K], scales [G, N, K/32]) along K."""
+    G, N, Kd = w.shape
+    q, s = mxfp8_quantize(w.reshape(G * N, Kd), 0)
+    return q.view(G, N, Kd), s.view(G, N, Kd // 32)

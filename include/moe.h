@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the dropless mixture-of-experts expert layer for MI355X
+ * (gfx950), library libmoe.so.
+ *
+ * The layer (page "NVIDIA Accelerates Dropless MoE Training in JAX Using
+ * Transformer Engine", sections "What specialized optimizations are required
+ * for dropless MoE?" with Figure 3, "Optimization 1: Grouped GEMM" and
+ * "Optimization 2: Expert parallelism to integrate Dispatch and Combine"):
+ *
+ *   router top-K  ->  permute tokens into expert-contiguous rows (dispatch,
+ *   local part)  ->  grouped GEMM of every expert's rows with its own gate/up
+ *   weight, SwiGLU  ->  grouped GEMM with the down weight  ->  unpermute and
+ *   combine by the routing weights.  Optionally the grouped GEMMs run on
+ *   MXFP8 operands (E4M3 values, one E8M0 scale per 32 along K) produced by a
+ *   group-aware quantiser.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers (HBM) unless stated otherwise; the caller
+ *    owns every buffer.  The library never allocates, frees, copies to the
+ *    host or synchronises inside a call: each call only enqueues kernels on
+ *    `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *  - Per-expert token counts (`group_sizes`) stay on the device; no entry
+ *    point reads them on the host, and every launch grid depends only on host
+ *    arguments, so each call may be captured in a hipGraph and replayed with
+ *    new data (the page's requirement that kernels work when the shapes are
+ *    not visible to the CPU, section "What specialized optimizations are
+ *    required for dropless MoE?").
+ *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *  - Errors that the host can see (NULL required pointers, bad sizes,
+ *    misalignment, too small workspace, unsupported combinations) return a
+ *    status synchronously and enqueue nothing.  A launch failure returns
+ *    MOE_ERR_HIP.  Errors in the DATA (an expert id outside [0,E), a
+ *    negative group size, group sizes summing past the buffer) cannot be
+ *    seen without a sync: kernels OR a MOE_FLAG_* bit into *err_flag (a
+ *    device uint32; may be NULL) and clamp so that every access stays in
+ *    bounds.  The caller polls the flag when it chooses.
+ *  - Calls are thread-safe; calls on different streams may overlap.
+ */
+#ifndef DROPLESS_MOE_H
+#define DROPLESS_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* NULL pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* shape / dtype / layout combination not implemented */
+  MOE_ERR_ALIGNMENT = 3,   /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  MOE_ERR_HIP = 5          /* the HIP runtime refused a launch */
+} moe_status_t;
+
+/* bits OR-ed into *err_flag by kernels */
+#define MOE_FLAG_BAD_EXPERT_ID 0x1u  /* id outside [0,E): treated as E-1 */
+#define MOE_FLAG_ROWS_OVER_CAP 0x2u  /* sum of group sizes > m_cap: rows past m_cap ignored */
+#define MOE_FLAG_NEGATIVE_SIZE 0x4u  /* a group size < 0: treated as 0 */
+#define MOE_FLAG_NAN_LOGIT     0x8u  /* NaN router logit: treated as -inf */
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+/* Static text of a status code. */
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Router top-K.  Blog intro: a learned router activates each token's Top-K
+ * experts; ch. 1 of "AI Systems Performance Engineering", §4.1 worked
+ * example: softmax = exponentials of (score - row max) over their sum.
+ *
+ * logits    fp32 [T, E]   router scores (bias already added)
+ * topk_ids  int32 [T, K]  out: the K highest-scoring experts, in descending
+ *                         score order; equal scores go to the lower index
+ * topk_w    fp32 [T, K]   out: renormalize != 0: exp(l_k - max) / sum over
+ *                         the K picks (they sum to 1); renormalize == 0: the
+ *                         softmax over all E experts at the picks
+ * Limits: 1 <= K <= min(E, 32), E <= 256, T >= 0.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renormalize,
+                            int32_t* topk_ids, float* topk_w, uint32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Permute (dispatch, local part; blog section "Optimization 2": tokens are
+ * reordered by expert).  A stable counting sort of the T*K (token, expert)
+ * pairs, pair i = t*K + k:
+ *   group_sizes[e]    = number of pairs routed to e                int32 [E]
+ *   group_offsets[e]  = exclusive prefix sum; [E] = T*K            int32 [E+1]
+ *   perm_dst[i]       = row of pair i in expert-contiguous order    int32 [T*K]
+ *   perm_src[r]       = pair held by row r (inverse of perm_dst)    int32 [T*K]
+ *   x_perm[r, :]      = x[perm_src[r] / K, :]                       bf16 [T*K, d]
+ * Rows of one expert keep ascending token order.  The result does not
+ * depend on thread timing (no atomics decide an order).  x / x_perm may both
+ * be NULL to build the maps only.  ws: moe_permute_workspace_bytes(T,E,K)
+ * bytes, 256-byte aligned, contents need not be initialised.
+ * Limits: E <= 256, K <= 32, d % 8 == 0 when x is given.
+ * ------------------------------------------------------------------------ */
+size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t K);
+moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E, int32_t K,
+                         int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
+                         uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped GEMM (blog section "Optimization 1: Grouped GEMM": all experts in
+ * one call, each with its true token count, only rows with valid tokens
+ * computed; counts on the device).  Group g owns rows [o_g, o_g + s_g) of the
+ * ragged operand, o_g = s_0 + ... + s_{g-1}, s_g = group_sizes[g].
+ *
+ * ragged = MOE_RAGGED_M (forward and data gradient):
+ *   C[r, n] = sum_k A[r, k] * Bop_g[k, n]   for rows r of group g
+ *   A  [m_cap, K] (K contiguous);  B_NK: B [G, N, K] (Bop_g = B[g]^T);
+ *   B_KN: B [G, K, N] (Bop_g = B[g]).  Output C [m_cap, N] (out_dtype).
+ *   epilogue MOE_EPI_SWIGLU (B_NK, bf16 only): N = 2f; with acc = A*Bop,
+ *   C [m_cap, f] = bf16(silu(acc[:, j]) * acc[:, f + j]) (rows [0,f) of B[g]
+ *   are the gate projection, rows [f,2f) the up projection: the prefused
+ *   weight of the blog's MaxText config) and, if C_aux is not NULL,
+ *   C_aux [m_cap, 2f] = bf16(acc) (the pre-activations, for the backward).
+ *   Rows r >= sum(s_g) are not written.
+ * ragged = MOE_RAGGED_K (weight gradient; contraction over a group's rows):
+ *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
+ *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
+ * dtype = MOE_DTYPE_MXFP8 (RAGGED_M, B_NK only): A, B are E4M3 codes with
+ *   E8M0 scales A_scale [m_cap, K/32], B_scale [G, N, K/32] (value =
+ *   code * 2^(scale - 127)); accumulation fp32, output bf16.
+ * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
+ * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
+ *   MXFP8: K % 128 == 0.  A, B, C 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_MXFP8 1
+#define MOE_RAGGED_M 0
+#define MOE_RAGGED_K 1
+#define MOE_B_NK 0
+#define MOE_B_KN 1
+#define MOE_EPI_NONE 0
+#define MOE_EPI_SWIGLU 1
+#define MOE_OUT_BF16 0
+#define MOE_OUT_F32 1
+
+typedef struct moe_gg_desc {
+  int32_t dtype;     /* MOE_DTYPE_* */
+  int32_t ragged;    /* MOE_RAGGED_M | MOE_RAGGED_K */
+  int32_t b_layout;  /* MOE_B_NK | MOE_B_KN (RAGGED_M) */
+  int32_t epilogue;  /* MOE_EPI_NONE | MOE_EPI_SWIGLU */
+  int32_t out_dtype; /* MOE_OUT_BF16 | MOE_OUT_F32 */
+  int32_t G;         /* number of groups */
+  int32_t M;         /* RAGGED_K: rows of each C[g]; ignored for RAGGED_M */
+  int32_t N;         /* output columns (before the SwiGLU epilogue halves them) */
+  int32_t K;         /* RAGGED_M: contraction length; ignored for RAGGED_K */
+  int64_t m_cap;     /* rows of the ragged operand(s); sum(group_sizes) <= m_cap */
+} moe_gg_desc;
+
+size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc);
+moe_status_t grouped_gemm(const moe_gg_desc* desc, const void* A, const uint8_t* A_scale, const void* B,
+                          const uint8_t* B_scale, const int32_t* group_sizes, void* C, void* C_aux, void* ws,
+                          size_t ws_bytes, uint32_t* err_flag, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Unpermute and combine (blog Figure 3: restore the original token order;
+ * ch. 1 §2.3.2 dispatch/combine table: the expert outputs of a token are
+ * merged by a weighted sum):
+ *   y[t, :] = bf16( sum_{k ascending} w[t,k] * y_perm[perm_dst[t*K+k], :] )
+ * accumulated in fp32.  topk_w == NULL means every weight is 1 (the plain
+ * sum used to fold the data gradient back to tokens).
+ * y_perm bf16 [>= T*K, d], perm_dst int32 [T*K], y bf16 [T, d]; d % 8 == 0.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, const int32_t* perm_dst,
+                                   int64_t T, int32_t d, int32_t K, uint16_t* y, void* stream);
+
+/* Backward of the combine: dy_perm[perm_dst[t*K+k], :] = bf16(w[t,k] * dy[t, :])
+ * and d_topk_w[t,k] = sum_j dy[t,j] * y_perm[perm_dst[t*K+k], j] (fp32).
+ * dy bf16 [T,d], y_perm bf16 [T*K,d], dy_perm bf16 [T*K,d], d_topk_w fp32 [T,K]. */
+moe_status_t moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
+                                  const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint16_t* dy_perm,
+                                  float* d_topk_w, void* stream);
+
+/* Backward of SwiGLU from the stored pre-activations gu = [g | u] bf16
+ * [m_cap, 2f] and dh bf16 [m_cap, f]: with s = sigmoid(g),
+ * dgu[:, j] = bf16(dh*u*s*(1 + g*(1-s))), dgu[:, f+j] = bf16(dh*g*s).
+ * Rows >= sum(group_sizes) are skipped (group_sizes may be NULL: all m_cap
+ * rows).  f % 8 == 0. */
+moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
+                                 const int32_t* group_sizes, int32_t G, uint16_t* dgu, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Group-aware MXFP8 quantisation (blog: "group-aware MXFP8 quantization" and
+ * MXFP8 block scaling for expert matmuls, section "Optimization 1"; ch. 1
+ * §1.1 low-precision scaling: one scale per block of 32).  Scale rule (OCP
+ * MX v1.0): per block, e = floor(log2(amax)) - 8 clamped to [-127, 127],
+ * scale byte = e + 127 (amax == 0 gives byte 0); codes = E4M3FN
+ * round-to-nearest-even of clamp(v * 2^-e, -448, 448), sign kept on zero.
+ *
+ * axis 0: blocks of 32 along each row. x bf16 [rows, cols] -> q [rows, cols],
+ *   scale [rows, cols/32].  If group_sizes != NULL only rows < sum(sizes)
+ *   are written.  cols % 32 == 0.
+ * axis 1: blocks of 32 down each column, restarting at every group's first
+ *   row (a group's last block may be short).  The block starting at row
+ *   o_g + 32*b has scale row P_g + b, P_g = sum_{h<g} ceil(s_h/32); scale is
+ *   [rows/32 + G, cols] (rows past the used ones are not written).
+ *   group_sizes required.  cols % 8 == 0.
+ * ------------------------------------------------------------------------ */
+moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols, int32_t axis,
+                                  const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,
+                                  uint32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DROPLESS_MOE_H */

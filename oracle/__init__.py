@@ -150,7 +150,7 @@ def permute(ids, E: int):
     """-> group_sizes [E], group_offsets [E+1], perm_src [M], perm_dst [T*K] (int32)."""
     ids = _np(ids, np.int32)
     T, K = ids.shape
-    assert ids.min() >= 0 and ids.max() < E
+    assert ids.size == 0 or (ids.min() >= 0 and ids.max() < E)
     sizes = np.empty(E, np.int32)
     offs = np.empty(E + 1, np.int32)
     src = np.empty(T * K, np.int32)

@@ -1,0 +1,99 @@
+"""CPU checks of the C ABI: the library builds, loads and exports every
+function include/moe.h declares; host-checkable argument errors come back as
+status codes without any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _lib():
+    from dropless_moe_expert_amd import build, ops
+    if not os.path.exists(ops.LIB_PATH):
+        build.build()
+    return ops, ops.load_library(require_gpu=False)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\**\s+\**([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_route_topk", "moe_permute", "grouped_gemm", "moe_unpermute_combine", "mxfp8_group_quantize",
+              "moe_combine_backward", "moe_swiglu_backward", "moe_permute_workspace_bytes",
+              "grouped_gemm_workspace_bytes", "moe_abi_version", "moe_status_string"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    ops, L = _lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(ops.EXPORTS)
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_string(0) == b"ok"
+
+
+def test_host_checkable_errors_return_status():
+    ops, L = _lib()
+    INVALID, UNSUPPORTED, ALIGN, WS = 1, 2, 3, 4
+    # router: K > E, E > 256, T < 0
+    assert L.moe_route_topk(None, 10, 8, 9, 1, None, None, None, None) == INVALID
+    assert L.moe_route_topk(None, 10, 300, 2, 1, None, None, None, None) == INVALID
+    assert L.moe_route_topk(None, -1, 8, 2, 1, None, None, None, None) == INVALID
+    # permute: missing outputs, missing workspace, d not a multiple of 8
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.moe_permute(None, fake, 4, 0, 8, 2, None, None, None, None, None, None, 0, None, None) == INVALID
+    assert L.moe_permute(None, fake, 4, 0, 8, 2, fake, fake, fake, fake, None, None, 0, None, None) == WS
+    assert L.moe_permute(fake, fake, 4, 12, 8, 2, fake, fake, fake, fake, fake, fake, 1 << 20, None, None) == UNSUPPORTED
+    assert L.moe_permute(ctypes.c_void_p((1 << 20) + 2), fake, 4, 16, 8, 2, fake, fake, fake, fake, fake, fake,
+                         1 << 20, None, None) == ALIGN
+    assert L.moe_permute_workspace_bytes(16384, 128, 8) >= 16384 * 8 * 4
+    # grouped GEMM descriptor checks
+    d = ops.GGDesc(0, 0, 0, 0, 0, 4, 0, 64, 64, 100)
+    bd = ctypes.byref(d)
+    assert L.grouped_gemm(bd, None, None, fake, None, fake, fake, None, None, 0, None, None) == INVALID
+    d.K = 96  # bf16 needs K % 64 == 0
+    assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    d.K = 64
+    d.G = 2000
+    assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == INVALID
+    d.G = 4
+    d.dtype = 1  # MXFP8 without scales
+    d.K = 128
+    assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == INVALID
+    d.dtype, d.epilogue, d.b_layout = 0, 1, 1  # SwiGLU needs the NK layout
+    assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    d.epilogue, d.b_layout = 0, 0
+    assert L.grouped_gemm(bd, ctypes.c_void_p((1 << 20) + 8), None, fake, None, fake, fake, None, None, 0, None,
+                          None) == ALIGN
+    # combine / backward helpers / quantiser
+    assert L.moe_unpermute_combine(fake, None, fake, 4, 12, 2, fake, None) == INVALID
+    assert L.moe_combine_backward(fake, fake, None, fake, 4, 16, 2, fake, fake, None) == INVALID
+    assert L.moe_swiglu_backward(fake, fake, 4, 12, None, 0, fake, None) == INVALID
+    assert L.mxfp8_group_quantize(fake, 4, 48, 0, None, 0, fake, fake, None, None) == UNSUPPORTED
+    assert L.mxfp8_group_quantize(fake, 4, 64, 1, None, 0, fake, fake, None, None) == INVALID
+    assert L.mxfp8_group_quantize(fake, 4, 64, 2, None, 0, fake, fake, None, None) == INVALID
+
+
+def test_product_path_refuses_without_gpu():
+    """No CPU fallback: the binding raises when no GPU is visible."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    from dropless_moe_expert_amd import ops
+    saved = ops._lib
+    ops._lib = None
+    try:
+        with pytest.raises(ops.MoeError):
+            ops.load_library()
+    finally:
+        ops._lib = saved

@@ -1,0 +1,373 @@
+"""GPU parity of every step against the CPU oracle, through the C ABI.
+
+Integer results (routing ids, counts, offsets, permutation maps, MXFP8 codes
+and scales) must match bit for bit; bf16 outputs within a max relative error
+of 1e-2; MXFP8 GEMM outputs within 2e-2 relative L2 of the oracle fed the
+identical quantised operands.  Shapes are small enough for the oracle but
+span several 256-wide tiles with ragged tails and empty groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from dropless_moe_expert_amd import inputs
+from gpu_util import (BF16_TOL, MX_TOL, W_RTOL, bf16, dev, host_u16, max_rel_err, rel_l2, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from dropless_moe_expert_amd import ops as _ops
+    _ops.load_library()
+    return _ops
+
+
+# ------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,E,K,renorm", [(300, 8, 2, 1), (1000, 128, 8, 1), (77, 256, 8, 1), (64, 4, 1, 1),
+                                          (50, 32, 32, 1), (129, 60, 5, 0), (0, 8, 2, 1)])
+def test_route_topk(ops, T, E, K, renorm):
+    say("route", T, E, K, renorm)
+    rng = np.random.default_rng(T * 7 + E)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if T:
+        l[:, ::3] = np.round(l[:, ::3] * 2) / 2     # many exact ties
+    ids_ref, w_ref = orc.route_topk(l, K, renormalize=bool(renorm))
+    ids, w = ops.route_topk(dev(torch.from_numpy(l)), K, renormalize=bool(renorm))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=W_RTOL, atol=1e-30)
+
+
+# ------------------------------------------------------------------- permute
+
+@pytest.mark.parametrize("T,E,K,d", [(256, 8, 2, 128), (3000, 128, 8, 64), (1, 4, 2, 8), (2049, 256, 8, 24),
+                                     (700, 5, 1, 4096), (0, 8, 2, 16)])
+def test_permute(ops, T, E, K, d):
+    say("permute", T, E, K, d)
+    rng = np.random.default_rng(T + E * 3)
+    ids = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int32).reshape(T, K)
+    if T > 10:
+        ids[: T // 3] = np.sort(ids[: T // 3], axis=1)     # skew: low experts more popular
+    x = bf16(rng, T, d)
+    sizes, offs, src, dst = orc.permute(ids, E)
+    xp_ref = orc.gather_rows(x, src, K)
+    out = ops.permute(dev(x), dev(torch.from_numpy(ids)), E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["group_sizes"].cpu().numpy(), sizes)
+    np.testing.assert_array_equal(out["group_offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(out["perm_src"].cpu().numpy(), src)
+    np.testing.assert_array_equal(out["perm_dst"].cpu().numpy(), dst)
+    np.testing.assert_array_equal(host_u16(out["x_perm"]), xp_ref)
+
+
+def test_permute_maps_only_and_deterministic(ops):
+    rng = np.random.default_rng(5)
+    T, E, K = 5000, 64, 6
+    ids = dev(torch.from_numpy(np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)))
+    a = ops.permute(None, ids, E)
+    b = ops.permute(None, ids, E)
+    for k in ("group_sizes", "group_offsets", "perm_src", "perm_dst"):
+        assert torch.equal(a[k], b[k])
+
+
+# ------------------------------------------------------------------- grouped GEMM
+
+SIZES = [np.array([0, 300, 1, 0, 517], np.int32),            # empty first/middle, ragged tails
+         np.array([256, 255, 257, 0], np.int32),               # tile edges, empty last
+         np.array([5], np.int32),
+         np.array([0, 0, 0], np.int32)]                         # nothing to do
+
+
+@pytest.mark.parametrize("si", range(len(SIZES)))
+@pytest.mark.parametrize("N,Kd", [(512, 192), (264, 64)])
+def test_grouped_gemm_nk(ops, si, N, Kd):
+    sizes = SIZES[si]
+    say("gg nk", sizes.tolist(), N, Kd)
+    rng = np.random.default_rng(si * 10 + N)
+    G, M = sizes.size, int(sizes.sum())
+    m_cap = M + 37                                           # rows past the groups must stay untouched
+    A, B = bf16(rng, m_cap, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    ref = orc.grouped_gemm(A, B, sizes)
+    C = torch.full((m_cap + 64, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ops.grouped_gemm(dev(A), dev(B), dev(torch.from_numpy(sizes)), out=C[:m_cap])
+    torch.cuda.synchronize()
+    if M:
+        assert max_rel_err(C[:M], ref) <= BF16_TOL
+    assert torch.all(C[M:] == 7.0)
+    # fp32 output
+    C32 = ops.grouped_gemm(dev(A), dev(B), dev(torch.from_numpy(sizes)), out_dtype=torch.float32)
+    if M:
+        r = orc.bf16_to_f64(ref)
+        assert np.abs(C32[:M].cpu().double().numpy() - r).max() <= 1e-2 * np.abs(r).max()
+
+
+@pytest.mark.parametrize("f,Kd", [(384, 128), (200, 64), (128, 320)])
+def test_grouped_gemm_swiglu(ops, f, Kd):
+    sizes = np.array([3, 0, 400, 129, 0, 1], np.int32)
+    say("gg swiglu", f, Kd)
+    rng = np.random.default_rng(f + Kd)
+    G, M = sizes.size, int(sizes.sum())
+    A, W = bf16(rng, M, Kd), bf16(rng, G, 2 * f, Kd, scale=Kd ** -0.5)
+    h_ref, gu_ref = orc.gemm_swiglu(A, W, sizes, keep_gu=True)
+    h, gu = ops.grouped_gemm(dev(A), dev(W), dev(torch.from_numpy(sizes)), epilogue=ops.MOE_EPI_SWIGLU,
+                             keep_aux=True)
+    torch.cuda.synchronize()
+    assert max_rel_err(h, h_ref) <= BF16_TOL
+    assert max_rel_err(gu, gu_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("N,Kd", [(256, 128), (200, 320), (8, 64)])
+def test_grouped_gemm_kn_dgrad(ops, N, Kd):
+    sizes = np.array([0, 260, 7, 0, 300], np.int32)
+    say("gg kn", N, Kd)
+    rng = np.random.default_rng(N * Kd)
+    G, M = sizes.size, int(sizes.sum())
+    dC = bf16(rng, M, Kd)
+    B = bf16(rng, G, Kd, N, scale=Kd ** -0.5)                 # [G, K, N]: weight of a forward C = A B^T
+    # oracle: dA = dC @ W with W = B[g] as [Kd(=forward N), N(=forward K)]
+    ref = orc.grouped_dgrad(dC, B, sizes)
+    out = ops.grouped_gemm(dev(dC), dev(B), dev(torch.from_numpy(sizes)), b_layout=ops.MOE_B_KN)
+    torch.cuda.synchronize()
+    assert max_rel_err(out, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("P,Q", [(136, 264), (256, 64), (8, 8)])
+def test_grouped_gemm_wgrad(ops, P, Q):
+    sizes = np.array([0, 70, 300, 0, 5, 64], np.int32)
+    say("gg wgrad", P, Q)
+    rng = np.random.default_rng(P + Q)
+    G, M = sizes.size, int(sizes.sum())
+    X, Y = bf16(rng, M + 9, P), bf16(rng, M + 9, Q)
+    ref = orc.grouped_wgrad(X[:M], Y[:M], sizes)              # [G, P, Q]
+    out = ops.grouped_gemm_wgrad(dev(X), dev(Y), dev(torch.from_numpy(sizes)))
+    torch.cuda.synchronize()
+    assert max_rel_err(out, ref) <= BF16_TOL
+    for g in np.nonzero(sizes == 0)[0]:
+        assert torch.all(out[g] == 0)
+
+
+# ------------------------------------------------------------------- MXFP8
+
+@pytest.mark.parametrize("R,C", [(300, 256), (1, 32), (1000, 7168 // 4)])
+def test_mxfp8_quantize_axis0(ops, R, C):
+    say("mx q0", R, C)
+    rng = np.random.default_rng(R + C)
+    x32 = (rng.standard_normal((R, C)) * np.exp(rng.uniform(-30, 30, (R, 1)))).astype(np.float32)
+    x32[0, :32] = 0.0
+    if R > 2:
+        x32[1, :32] = -0.0
+        x32[2, :32] = np.float32(1e-39)     # subnormal block
+    x = inputs.to_bf16(x32)
+    q_ref, s_ref = orc.mxfp8_quantize(x, 0)
+    q, s = ops.mxfp8_quantize(dev(x), 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_mxfp8_quantize_axis0_valid_rows_only(ops):
+    rng = np.random.default_rng(9)
+    sizes = np.array([3, 0, 40], np.int32)
+    x = bf16(rng, 60, 64)
+    q_ref, s_ref = orc.mxfp8_quantize(x[:43], 0)
+    q = torch.full((60, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((60, 2), 0xCD, dtype=torch.uint8, device="cuda")
+    L = ops.lib()
+    xd, sd = dev(x), dev(torch.from_numpy(sizes))     # keep both alive until the kernel has run
+    st = L.mxfp8_group_quantize(ops._ptr(xd), 60, 64, 0, ops._ptr(sd), 3, ops._ptr(q), ops._ptr(s), None,
+                                ops._stream(q.device))
+    torch.cuda.synchronize()
+    assert st == 0
+    np.testing.assert_array_equal(q[:43].cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s[:43].cpu().numpy(), s_ref)
+    assert torch.all(q[43:] == 0xAB) and torch.all(s[43:] == 0xCD)
+
+
+def test_mxfp8_quantize_axis1_grouped(ops):
+    say("mx q1")
+    rng = np.random.default_rng(10)
+    sizes = np.array([0, 5, 32, 33, 0, 70, 1], np.int32)
+    M, C = int(sizes.sum()), 48
+    x = inputs.to_bf16((rng.standard_normal((M, C)) * 3).astype(np.float32))
+    q_ref, s_ref = orc.mxfp8_quantize(x, 1, sizes)
+    q, s = ops.mxfp8_quantize(dev(x), 1, dev(torch.from_numpy(sizes)))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s[: s_ref.shape[0]].cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_mxfp8(ops, swiglu):
+    sizes = np.array([0, 300, 1, 0, 260], np.int32)
+    say("gg mxfp8", swiglu)
+    rng = np.random.default_rng(11 + swiglu)
+    G, M, N, Kd = sizes.size, int(sizes.sum()), 512, 384
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    aq, as_ = orc.mxfp8_quantize(A, 0)
+    bq, bs = orc.mxfp8_quantize(orc.u16(B).reshape(-1, Kd), 0)
+    bq, bs = bq.reshape(G, N, Kd), bs.reshape(G, N, Kd // 32)
+    ref = orc.mx_grouped_gemm(aq, as_, bq, bs, sizes, swiglu=swiglu)
+    t = lambda a: dev(torch.from_numpy(np.ascontiguousarray(a)))
+    out = ops.grouped_gemm_mxfp8(t(aq), t(as_), t(bq), t(bs), t(sizes),
+                                 epilogue=ops.MOE_EPI_SWIGLU if swiglu else ops.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    assert rel_l2(out[:M], ref) <= MX_TOL
+    assert max_rel_err(out[:M], ref) <= 2 * BF16_TOL
+
+
+# ------------------------------------------------------------------- combine and backward helpers
+
+@pytest.mark.parametrize("T,K,d,weighted", [(300, 2, 128, True), (100, 8, 2048, True), (64, 4, 24, False)])
+def test_unpermute_combine(ops, T, K, d, weighted):
+    say("combine", T, K, d, weighted)
+    rng = np.random.default_rng(T + K + d)
+    E = 16
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    _, _, src, dst = orc.permute(ids, E)
+    yp = bf16(rng, T * K, d)
+    w = rng.dirichlet(np.ones(K), T).astype(np.float32) if weighted else None
+    ref = orc.unpermute_combine(yp, w, dst, T, K)
+    out = ops.unpermute_combine(dev(yp), None if w is None else dev(torch.from_numpy(w)),
+                                dev(torch.from_numpy(dst)), T, K)
+    torch.cuda.synchronize()
+    assert max_rel_err(out, ref) <= BF16_TOL
+
+
+def test_combine_backward_and_swiglu_backward(ops):
+    say("combine bwd")
+    rng = np.random.default_rng(21)
+    T, K, d, E, f = 200, 4, 256, 12, 96
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    sizes, _, src, dst = orc.permute(ids, E)
+    yp, dy = bf16(rng, T * K, d), bf16(rng, T, d)
+    w = rng.dirichlet(np.ones(K), T).astype(np.float32)
+    dyp_ref, dw_ref = orc.combine_backward(dy, yp, w, dst, K)
+    dyp, dw = ops.combine_backward(dev(dy), dev(yp), dev(torch.from_numpy(w)), dev(torch.from_numpy(dst)), K)
+    torch.cuda.synchronize()
+    assert max_rel_err(dyp, dyp_ref) <= BF16_TOL
+    np.testing.assert_allclose(dw.cpu().numpy(), dw_ref, rtol=1e-3, atol=1e-3 * np.abs(dw_ref).max())
+    M = T * K
+    gu, dh = bf16(rng, M, 2 * f, scale=2.0), bf16(rng, M, f)
+    dgu_ref = orc.swiglu_backward(gu, dh)
+    dgu = ops.swiglu_backward(dev(gu), dev(dh), dev(torch.from_numpy(sizes)))
+    torch.cuda.synchronize()
+    assert max_rel_err(dgu, dgu_ref) <= BF16_TOL
+
+
+# ------------------------------------------------------------------- the tiny layer end to end
+
+def test_tiny_layer_forward_backward(ops):
+    say("tiny layer")
+    L = inputs.workload("tiny")
+    y_ref, saved_ref = orc.layer_forward(L.logits, L.x, L.w1p, L.w2, L.K, keep=True)
+    g_ref = orc.layer_backward(L.dy, saved_ref, L.w1p, L.w2, L.K)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y, saved = ops.moe_forward(dev(L.logits), dev(L.x), dev(L.w1p), dev(L.w2), L.K, keep=True, flag=flag)
+    grads = ops.moe_backward(dev(L.dy), saved, dev(L.w1p), dev(L.w2), L.K, flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    np.testing.assert_array_equal(saved["ids"].cpu().numpy(), saved_ref["ids"])
+    np.testing.assert_array_equal(saved["group_sizes"].cpu().numpy(), saved_ref["sizes"])
+    assert saved_ref["sizes"][7] == 0
+    np.testing.assert_array_equal(saved["perm_dst"].cpu().numpy(), saved_ref["perm_dst"])
+    np.testing.assert_array_equal(host_u16(saved["x_perm"]), saved_ref["x_perm"])
+    assert max_rel_err(saved["h"], saved_ref["h"]) <= BF16_TOL
+    assert max_rel_err(saved["y_perm"], saved_ref["y_perm"]) <= BF16_TOL
+    assert max_rel_err(y, y_ref) <= BF16_TOL
+    for k in ("dy_perm", "dh", "dgu", "dx_perm", "dx", "dw2", "dw1p"):
+        assert max_rel_err(grads[k], g_ref[k]) <= BF16_TOL, k
+    dw = grads["dw"].cpu().numpy()
+    np.testing.assert_allclose(dw, g_ref["dw"], rtol=1e-2, atol=1e-2 * np.abs(g_ref["dw"]).max())
+    # expert 7 received nothing: its weight gradients are exact zeros
+    assert torch.all(grads["dw2"][7] == 0) and torch.all(grads["dw1p"][7] == 0)
+
+
+# ------------------------------------------------------------------- data errors: flags, bounds
+
+def test_flags_bad_ids_stay_in_bounds(ops):
+    say("flags ids")
+    T, E, K, d = 100, 8, 2, 16
+    rng = np.random.default_rng(31)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    ids[5, 0] = 9
+    ids[7, 1] = -3
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ops.permute(dev(bf16(rng, T, d)), dev(torch.from_numpy(ids)), E, flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & ops.FLAG_BAD_EXPERT_ID
+    dst = out["perm_dst"].cpu().numpy()
+    assert dst.min() >= 0 and dst.max() < T * K
+    assert int(out["group_sizes"].sum()) == T * K
+    np.testing.assert_array_equal(np.sort(dst), np.arange(T * K))
+
+
+def test_flags_bad_sizes(ops):
+    say("flags sizes")
+    rng = np.random.default_rng(32)
+    m_cap, Kd, N = 300, 64, 64
+    A, B = bf16(rng, m_cap, Kd), bf16(rng, 3, N, Kd)
+    buf = torch.full((m_cap + 40, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sizes = np.array([100, -5, 250], np.int32)        # negative, and 350 > m_cap
+    ops.grouped_gemm(dev(A), dev(B), dev(torch.from_numpy(sizes)), out=buf[:m_cap], flag=flag)
+    torch.cuda.synchronize()
+    f = int(flag.item())
+    assert f & ops.FLAG_NEGATIVE_SIZE and f & ops.FLAG_ROWS_OVER_CAP
+    assert torch.all(buf[m_cap:] == 3.0)
+    ref = orc.grouped_gemm(A, B, np.array([100, 0, 200], np.int32))   # the clamped reading
+    assert max_rel_err(buf[:m_cap], ref) <= BF16_TOL
+
+
+def test_flag_nan_logit(ops):
+    l = torch.randn(4, 8)
+    l[2, 3] = float("nan")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids, _ = ops.route_topk(dev(l), 2, flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & ops.FLAG_NAN_LOGIT
+    assert 3 not in ids[2].tolist()
+
+
+# ------------------------------------------------------------------- graph capture: sizes stay on the device
+
+def test_forward_graph_replay_follows_new_routing(ops):
+    say("graph replay")
+    T, d, E, K, f = 512, 128, 8, 2, 256
+    L = inputs.routed_layer("g", T, d, E, K, f, 51, bias_std=1.0)
+    logits, x, w1p, w2 = dev(L.logits), dev(L.x), dev(L.w1p), dev(L.w2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            ops.moe_forward(logits, x, w1p, w2, K)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y, _ = ops.moe_forward(logits, x, w1p, w2, K)
+    rng = np.random.default_rng(52)
+    for rep in range(3):
+        new = rng.standard_normal((T, E)).astype(np.float32) + np.array([3.0 * (rep == 1)] + [0] * (E - 1),
+                                                                          np.float32)
+        logits.copy_(torch.from_numpy(new))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_ref, _ = orc.layer_forward(new, L.x, L.w1p, L.w2, K)
+        assert max_rel_err(y, y_ref) <= BF16_TOL, rep
+        # an eager call between replays agrees bit for bit with the replay
+        y_eager, _ = ops.moe_forward(logits, x, w1p, w2, K)
+        torch.cuda.synchronize()
+        assert torch.equal(y_eager, y)
+
+
+def test_grouped_gemm_bitwise_deterministic(ops):
+    rng = np.random.default_rng(61)
+    sizes = dev(torch.from_numpy(np.array([100, 0, 700, 3], np.int32)))
+    A, B = dev(bf16(rng, 803, 256)), dev(bf16(rng, 4, 512, 256))
+    c1 = ops.grouped_gemm(A, B, sizes, epilogue=ops.MOE_EPI_SWIGLU)
+    c2 = ops.grouped_gemm(A, B, sizes, epilogue=ops.MOE_EPI_SWIGLU)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
