@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the dropless MoE expert path on one MI355X.
+
+Headline (one JSON line on stdout): valid-row grouped-GEMM TFLOP/s of the
+DeepSeek-V3-shaped one-GPU expert share (32 experts, 24,576 permuted rows
+with Zipf(1.2) group sizes, d=7168, SwiGLU ffn=2048, bf16 with fp32
+accumulation).  One step = the whole expert path of that workload: the
+gate/up grouped GEMM with the SwiGLU epilogue, then the down grouped GEMM.
+Valid-row FLOPs = 2 * rows * (2f * d + d * f); padding rows never count.
+
+Also reported in the same line:
+  * roofline of the dominant kernel (the gate/up GEMM), its average launch
+    time measured with HIP events on the stream it runs on;
+  * the MoE layer tokens/s of the Mixtral-shaped forward (T=4096, d=4096,
+    8 experts top-2, ffn=14336): route, permute, two grouped GEMMs, combine;
+  * the CPU oracle timed on a bounded sample of the same expert-share rows,
+    which also serves as a sampled parity check of those rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+MXFP8_PEAK_TFLOPS = 5000.0
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_swiglu_dsv3_share.json")
+GEMM_SOURCE = os.path.join(ROOT, "dropless_moe_expert_amd", "csrc", "grouped_gemm.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(flops_per_launch: float):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the Mixtral-shaped layer tokens/s")
+    ap.add_argument("--cpu-rows", type=int, default=2304, help="expert-share rows the oracle computes")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py measures one GPU only: this build has no multi-GPU path "
+                  "(the expert share of one GPU is the whole workload); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from dropless_moe_expert_amd import inputs, ops
+
+    ops.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ expert share (headline)
+    t0 = time.time()
+    L = inputs.workload("dsv3_share")
+    log(f"inputs generated in {time.time() - t0:.1f}s; group sizes {L.group_sizes.tolist()}")
+    M, d, f, E = L.M, L.d, L.f, L.E
+    x = L.x_perm.to(dev)
+    w1p = L.w1p.to(dev)
+    w2 = L.w2.to(dev)
+    sizes = L.group_sizes.to(dev)
+    h = torch.empty((M, f), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        ops.grouped_gemm(x, w1p, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h, flag=flag)
+        ops.grouped_gemm(h, w2, sizes, out=y, flag=flag)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)   # the stream the kernels are launched on
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        ops.grouped_gemm(x, w1p, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h, flag=flag)
+        ev[i][1].record(stream)
+        ops.grouped_gemm(h, w2, sizes, out=y, flag=flag)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gg1_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]))
+    gg2_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]))
+    ms_per_step = wall * 1e3 / args.steps
+    assert int(flag.item()) == 0, "device error flag raised"
+
+    flops_gg1 = 2.0 * M * (2 * f) * d
+    flops_gg2 = 2.0 * M * d * f
+    flops_step = flops_gg1 + flops_gg2
+    tflops = flops_step / (ms_per_step * 1e-3) / 1e12
+    gg1_tflops = flops_gg1 / (gg1_ms * 1e-3) / 1e12
+    gg2_tflops = flops_gg2 / (gg2_ms * 1e-3) / 1e12
+    log(f"expert share: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s; gate/up {gg1_ms:.3f} ms "
+        f"({gg1_tflops:.1f}), down {gg2_ms:.3f} ms ({gg2_tflops:.1f})")
+
+    traffic = measured_traffic(flops_gg1)
+    roofline = {
+        "kernel": "grouped_gemm gate/up + SwiGLU (dsv3 share)",
+        "bound": "mfma",
+        "achieved": round(gg1_tflops, 2),
+        "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(gg1_tflops / BF16_PEAK_TFLOPS, 4),
+        "traffic": traffic,
+        "algorithmic_flop_per_launch": flops_gg1,
+        "avg_launch_ms": round(gg1_ms, 4),
+    }
+
+    # ------------------------------------------------------------ MoE layer tokens/s (Mixtral-shaped)
+    layer = None
+    if not args.no_layer:
+        del w1p, w2
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        Lm = inputs.workload("mixtral")
+        log(f"layer inputs generated in {time.time() - t0:.1f}s")
+        lg, xm, w1m, w2m = (t.to(dev) for t in (Lm.logits, Lm.x, Lm.w1p, Lm.w2))
+        for _ in range(max(2, args.warmup // 2)):
+            ops.moe_forward(lg, xm, w1m, w2m, Lm.K, flag=flag)
+        torch.cuda.synchronize()
+        nl = max(5, args.steps // 2)
+        a = time.perf_counter()
+        for _ in range(nl):
+            ops.moe_forward(lg, xm, w1m, w2m, Lm.K, flag=flag)
+        torch.cuda.synchronize()
+        lms = (time.perf_counter() - a) * 1e3 / nl
+        assert int(flag.item()) == 0
+        lflops = 2.0 * Lm.T * Lm.K * (2 * Lm.f * Lm.d + Lm.d * Lm.f)
+        layer = {"workload": "mixtral-shaped forward T=4096 d=4096 E=8 top-2 ffn=14336 bf16",
+                 "tokens_per_s": round(Lm.T / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
+                 "valid_row_tflops": round(lflops / (lms * 1e-3) / 1e12, 2)}
+        log(f"mixtral layer: {lms:.3f} ms, {layer['tokens_per_s']:.0f} tokens/s")
+        del lg, xm, w1m, w2m
+        torch.cuda.empty_cache()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ------------------------------------------------------------ CPU baseline (oracle, bounded sample)
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle as orc
+        rng = np.random.default_rng(0)
+        offs = np.concatenate([[0], np.cumsum(L.group_sizes.numpy())])
+        # rows from every non-empty group, including each group's first and last row
+        cand = []
+        for g in range(E):
+            if offs[g + 1] > offs[g]:
+                cand += [offs[g], offs[g + 1] - 1]
+        extra = rng.choice(M, size=max(0, args.cpu_rows - len(cand)), replace=False)
+        rows = np.unique(np.concatenate([np.array(cand, np.int64), extra.astype(np.int64)]))[: args.cpu_rows]
+        try:
+            threads = len(os.sched_getaffinity(0))
+        except AttributeError:
+            threads = os.cpu_count() or 1
+        threads = int(os.environ.get("OMP_NUM_THREADS", threads))
+        a = time.perf_counter()
+        h_ref, _ = orc.gemm_swiglu(L.x_perm, L.w1p, L.group_sizes, rows=rows)
+        H = np.zeros((M, f), np.uint16)
+        H[rows] = h_ref
+        y_ref = orc.grouped_gemm(H, L.w2, L.group_sizes, rows=rows)
+        cpu_s = time.perf_counter() - a
+        cpu_flops = 2.0 * len(rows) * (2 * f * d + d * f)
+        cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(rows)} of {M} expert-share rows (gate/up+SwiGLU and down GEMM, fp64 accumulation), "
+                         f"{cpu_s:.1f}s"}
+        # sampled parity of the same rows (the oracle's inputs are the generator's, never the GPU's)
+        hg = h[torch.from_numpy(rows).to(dev)].cpu().view(torch.int16).numpy().view(np.uint16)
+        yg = y[torch.from_numpy(rows).to(dev)].cpu().view(torch.int16).numpy().view(np.uint16)
+
+        def mre(g, r):
+            g, r = orc.bf16_to_f64(g), orc.bf16_to_f64(r)
+            return float(np.abs(g - r).max() / np.abs(r).max())
+
+        parity = {"rows": int(len(rows)), "h_max_rel_err": mre(hg, h_ref), "y_max_rel_err": mre(yg, y_ref),
+                  "tol": 1e-2}
+        log(f"oracle: {cpu_s:.1f}s for {len(rows)} rows on {threads} threads; parity {parity}")
+
+    out = {
+        "metric": "grouped-GEMM valid-row TFLOPS (% of MFMA peak) + MoE-layer tokens/s, 1 MI355X",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws; no dataset)",
+        "config": {"workload": "deepseek-v3-shaped one-GPU expert share: 32 experts, 24576 rows, "
+                               "zipf(1.2) group sizes, d=7168, swiglu ffn=2048",
+                   "rows": M, "d": d, "ffn": f, "experts": E, "parallelism": "none (1 GPU)"},
+        "pct_of_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+        "kernels_ms": {"gate_up_swiglu": round(gg1_ms, 4), "down": round(gg2_ms, 4)},
+        "kernels_tflops": {"gate_up_swiglu": round(gg1_tflops, 2), "down": round(gg2_tflops, 2)},
+        "moe_layer": layer,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(out), flush=True)
+    if parity and (parity["h_max_rel_err"] > 1e-2 or parity["y_max_rel_err"] > 1e-2):
+        log("sampled parity FAILED")
+        return 1
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -56,36 +56,42 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def _normal_rows(seed: int, tag: int, rows: int, cols: int, std: float = 1.0) -> np.ndarray:
-    """[rows, cols] fp32 N(0, std), drawn in independent chunks of rows."""
-    out = np.empty((rows, cols), dtype=np.float32)
+def _normal_rows(seed: int, tag: int, rows: int, cols: int, std: float = 1.0) -> torch.Tensor:
+    """[rows, cols] bf16 (torch, CPU) of N(0, std) fp32 draws, in independent chunks of rows."""
+    out = torch.empty((rows, cols), dtype=torch.bfloat16)
     nchunk = (rows + _ROW_CHUNK - 1) // _ROW_CHUNK
 
     def fill(c: int) -> None:
         r0, r1 = c * _ROW_CHUNK, min(rows, (c + 1) * _ROW_CHUNK)
-        g = _rng(seed, tag, c)
-        out[r0:r1] = g.standard_normal((r1 - r0, cols), dtype=np.float32)
+        a = _rng(seed, tag, c).standard_normal((r1 - r0, cols), dtype=np.float32)
         if std != 1.0:
-            out[r0:r1] *= np.float32(std)
+            a *= np.float32(std)
+        out[r0:r1].copy_(torch.from_numpy(a))          # torch's cast: round to nearest even
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(fill, range(nchunk)))
     return out
 
 
-def _normal_experts(seed: int, tag: int, E: int, rows: int, cols: int, std: float,
-                    experts: Optional[list] = None) -> np.ndarray:
-    """[len(experts), rows, cols] fp32; expert e drawn from stream (seed, tag, e)."""
+def _normal_experts(parts, E: int, cols: int, experts: Optional[list] = None) -> torch.Tensor:
+    """bf16 [len(experts), sum(rows), cols]: for each expert e the row blocks
+    parts = [(seed, tag, rows, std), ...] stacked, block i drawn from stream
+    (seed, tag_i, e)."""
     ex_list = list(range(E)) if experts is None else list(experts)
-    out = np.empty((len(ex_list), rows, cols), dtype=np.float32)
+    total = sum(p[2] for p in parts)
+    out = torch.empty((len(ex_list), total, cols), dtype=torch.bfloat16)
+    jobs = [(i, j) for i in range(len(ex_list)) for j in range(len(parts))]
+    offs = np.concatenate([[0], np.cumsum([p[2] for p in parts])])
 
-    def fill(i: int) -> None:
-        g = _rng(seed, tag, ex_list[i])
-        out[i] = g.standard_normal((rows, cols), dtype=np.float32)
-        out[i] *= np.float32(std)
+    def fill(job) -> None:
+        i, j = job
+        seed, tag, rows, std = parts[j]
+        a = _rng(seed, tag, ex_list[i]).standard_normal((rows, cols), dtype=np.float32)
+        a *= np.float32(std)
+        out[i, offs[j]:offs[j + 1]].copy_(torch.from_numpy(a))
 
     with ThreadPoolExecutor(_threads()) as ex:
-        list(ex.map(fill, range(len(ex_list))))
+        list(ex.map(fill, jobs))
     return out
 
 
@@ -121,12 +127,10 @@ class Layer:
 
 
 def expert_weights(seed: int, E: int, d: int, f: int, experts: Optional[list] = None):
-    """(w1p [n,2f,d], w2 [n,d,f]) bf16 for the listed experts (default all)."""
-    g = _normal_experts(seed, _WGATE, E, f, d, 1.0 / np.sqrt(d), experts)
-    u = _normal_experts(seed, _WUP, E, f, d, 1.0 / np.sqrt(d), experts)
-    w1p = to_bf16(np.concatenate([g, u], axis=1))
-    del g, u
-    w2 = to_bf16(_normal_experts(seed, _WDOWN, E, d, f, 1.0 / np.sqrt(f), experts))
+    """(w1p [n,2f,d], w2 [n,d,f]) bf16 for the listed experts (default all).
+    w1p stacks the gate projection (rows [0,f)) over the up projection."""
+    w1p = _normal_experts([(seed, _WGATE, f, 1.0 / np.sqrt(d)), (seed, _WUP, f, 1.0 / np.sqrt(d))], E, d, experts)
+    w2 = _normal_experts([(seed, _WDOWN, d, 1.0 / np.sqrt(f))], E, f, experts)
     return w1p, w2
 
 
@@ -141,11 +145,11 @@ def routed_layer(name: str, T: int, d: int, E: int, K: int, f: int, seed: int,
     if bias is not None:
         logits = logits + np.asarray(bias, dtype=np.float32)[None, :]
     L.logits = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32))
-    L.x = to_bf16(_normal_rows(seed, _X, T, d))
+    L.x = _normal_rows(seed, _X, T, d)
     if weights:
         L.w1p, L.w2 = expert_weights(seed, E, d, f)
     if dy:
-        L.dy = to_bf16(_normal_rows(seed, _DY, T, d))
+        L.dy = _normal_rows(seed, _DY, T, d)
     return L
 
 
@@ -166,7 +170,7 @@ def expert_share(name: str, E: int, M: int, d: int, f: int, seed: int, weights: 
     if sizes is None:
         sizes = zipf_group_sizes(seed, E, M)
     L.group_sizes = torch.from_numpy(np.ascontiguousarray(sizes, dtype=np.int32))
-    L.x_perm = to_bf16(_normal_rows(seed, _X, int(sizes.sum()), d))
+    L.x_perm = _normal_rows(seed, _X, int(sizes.sum()), d)
     if weights:
         L.w1p, L.w2 = expert_weights(seed, E, d, f)
     return L
