@@ -168,39 +168,60 @@ __device__ __forceinline__ int find_group(const int32_t* tpre, int G, int mt) {
 }
 
 // ----------------------------------------------------------------- loaders
-// K-contiguous rows straight into LDS.  Tile row r of the stage comes from
-// global row grow(r); 16-byte slot (r, s) holds chunk swz(r, s) of that row.
-template <int R, typename RowFn>
-__device__ __forceinline__ void load_rows_direct(uint8_t* lds, const uint8_t* g, int64_t ld_bytes, int64_t k0_bytes,
-                                                 RowFn grow) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int NW = kThreads / 64;
-#pragma unroll
-  for (int i = 0; i < R / 8 / NW; ++i) {
-    const int blk = i * NW + wave;
-    const int row = blk * 8 + (lane >> 3);
-    // swz(row, lane & 7): (row >> 1) & 7 = ((blk & 1) << 2) | (lane >> 4), and blk & 1 = wave & 1
+// wavefront index as a scalar (uniform) value
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// K-contiguous rows straight into LDS.  Stage row r holds global row grow(r);
+// 16-byte slot (r, s) holds chunk swz(r, s) of it.  Each lane issues R/8/NW
+// loads; their 32-bit byte offsets (row * ld + chunk * 16) are computed once
+// per tile, and every stage adds only a uniform base pointer.
+template <int R>
+struct DirectRows {
+  static constexpr int NW = kThreads / 64;
+  static constexpr int N = R / 8 / NW;
+  uint32_t off[N];
+  template <typename RowFn>
+  __device__ __forceinline__ void init(int64_t ld_bytes, RowFn grow) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    // swz(row, lane & 7) with row = (i*NW + wave)*8 + lane/8: (row >> 1) & 7 =
+    // ((wave & 1) << 2) | (lane >> 4) for every i (NW even)
     static_assert(NW % 2 == 0, "swizzle shortcut needs an even wavefront count");
     const int chunk = (lane & 7) ^ (((wave & 1) << 2) | (lane >> 4));
-    const uint8_t* src = g + grow(row) * ld_bytes + k0_bytes + chunk * 16;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(lds + blk * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int row = (i * NW + wave) * 8 + (lane >> 3);
+      off[i] = (uint32_t)(grow(row) * ld_bytes + chunk * 16);
+    }
   }
-}
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base) const {
+    const int wave = wave_id();
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_ptr_t)(lds + (i * NW + wave) * 1024), 16,
+                                       0, 0);
+  }
+};
 
 // Per-row 4-byte scale words (MXFP8: 4 blocks of 32 for a 128-wide stage).
-template <int R, typename RowFn>
-__device__ __forceinline__ void load_scales_direct(uint8_t* lds, const uint8_t* s, int64_t ld, int64_t kb0,
-                                                   RowFn grow) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int NW = kThreads / 64;
+template <int R>
+struct DirectScales {
+  static constexpr int NW = kThreads / 64;
+  static constexpr int N = R / 64 / NW;
+  uint32_t off[N];
+  template <typename RowFn>
+  __device__ __forceinline__ void init(int64_t ld, RowFn grow) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < R / 64 / NW; ++i) {
-    const int blk = i * NW + wave;
-    const int row = blk * 64 + lane;
-    const uint8_t* src = s + grow(row) * ld + kb0;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(lds + blk * 256), 4, 0, 0);
+    for (int i = 0; i < N; ++i) off[i] = (uint32_t)(grow((i * NW + wave) * 64 + lane) * ld);
   }
-}
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base) const {
+    const int wave = wave_id();
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[i]), (lds_ptr_t)(lds + (i * NW + wave) * 256), 4, 0,
+                                       0);
+  }
+};
 
 // K-outer source: element (k, c) at g[k * ld + c] (bf16).  Tile row r = column
 // c0 + r; stage k-range [k0, k0 + 64) with rows k >= k_end read as zero and
@@ -270,7 +291,7 @@ __device__ __forceinline__ uint4 lds_read16(const uint8_t* lds, int row, int slo
 template <bool MX>
 __device__ __forceinline__ void compute_stage(const uint8_t* lw, const uint8_t* lx, const uint8_t* sw,
                                               const uint8_t* sx, f32x4_t (&acc)[kTN][kTM]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / kWM, wm = wave % kWM;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int slot0 = g4 ^ ((r16 >> 1) & 7);  // chunk g4 (bf16 k-step 0 / fp8 low half)
@@ -390,11 +411,15 @@ __device__ __forceinline__ int worker_id() {
 // ----------------------------------------------------------------- kernel
 template <int MODE, bool MX, int EPI, int OUT>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
-  extern __shared__ __align__(1024) uint8_t smem[];
-  // two operand stages, then (MXFP8) per stage W scales [kBN][4] and X scales [kBM][4]
-  auto stage = [&](int i) -> uint8_t* { return smem + i * kStageBytes; };
-  auto sstage = [&](int i) -> uint8_t* { return smem + 2 * kStageBytes + i * (kBN + kBM) * 4; };
-  GroupInfo& gi = *reinterpret_cast<GroupInfo*>(smem + 2 * kStageBytes + (MX ? 2 * (kBN + kBM) * 4 : 0));
+  // Two named stage buffers: a stage reads one while the direct-to-LDS loads
+  // of the next fill the other.  Distinct objects let the compiler see that
+  // the in-flight LDS-DMA writes cannot alias the fragment reads, so it does
+  // not wait for them before reading the current stage.
+  __shared__ __align__(1024) uint8_t buf0[kStageBytes];
+  __shared__ __align__(1024) uint8_t buf1[kStageBytes];
+  __shared__ __align__(16) uint8_t sc0[MX ? (kBN + kBM) * 4 : 16];   // MXFP8: W scales [kBN][4], X scales [kBM][4]
+  __shared__ __align__(16) uint8_t sc1[MX ? (kBN + kBM) * 4 : 16];
+  __shared__ GroupInfo gi;
 
   build_groups<MODE != MODE_K>(a, gi);
 
@@ -414,17 +439,32 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
       const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (kBN / 2) : nt * kBN;
       const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
 
-      auto xrow = [&](int r) -> int64_t { return m0 + min(r, rows - 1); };
+      // rows relative to per-tile uniform bases (offsets stay 32-bit)
+      auto xrow = [&](int r) -> int64_t { return min(r, rows - 1); };
       auto wrow = [&](int r) -> int64_t {
         if constexpr (EPI == MOE_EPI_SWIGLU) {
           const int wn = r / kWTN, q = r % kWTN;
           int jj = n0 + wn * (kWTN / 2) + (q % (kWTN / 2));
           jj = min(jj, f - 1);
-          return (int64_t)g * nrows_b + (q < kWTN / 2 ? jj : f + jj);
+          return q < kWTN / 2 ? jj : f + jj;
         } else {
-          return (int64_t)g * nrows_b + min(n0 + r, a.N - 1);
+          return min(n0 + r, a.N - 1);
         }
       };
+      const uint8_t* xbase = a.A + m0 * lda_b;
+      const uint8_t* wbase = a.B + (int64_t)g * nrows_b * lda_b;
+      const uint8_t* xsbase = MX ? a.As + m0 * (a.K / 32) : nullptr;
+      const uint8_t* wsbase = MX ? a.Bs + (int64_t)g * nrows_b * (a.K / 32) : nullptr;
+      DirectRows<kBM> xl;
+      DirectRows<kBN> wd;
+      DirectScales<kBM> xs;
+      DirectScales<kBN> ws;
+      xl.init(lda_b, xrow);
+      if constexpr (MODE == MODE_M_NK) wd.init(lda_b, wrow);
+      if constexpr (MX) {
+        xs.init(a.K / 32, xrow);
+        ws.init(a.K / 32, wrow);
+      }
       const uint16_t* Bkn = reinterpret_cast<const uint16_t*>(a.B) + (int64_t)g * a.K * a.N;
       KOuterLoad<kBN> wl;
 
@@ -434,41 +474,38 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
 #pragma unroll
         for (int j = 0; j < kTM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-      __syncthreads();  // the previous tile's last stage has been read by everyone
-      // prologue: stage 0
-      load_rows_direct<kBM>(stage(0) + kBN * kRowBytes, a.A, lda_b, 0, xrow);
-      if constexpr (MODE == MODE_M_NK) {
-        load_rows_direct<kBN>(stage(0), a.B, lda_b, 0, wrow);
-      } else {
-        wl.issue(Bkn, a.N, 0, a.K, n0, a.N);
-        wl.store(stage(0));
-      }
-      if constexpr (MX) {
-        load_scales_direct<kBM>(sstage(0) + kBN * 4, a.As, a.K / 32, 0, xrow);
-        load_scales_direct<kBN>(sstage(0), a.Bs, a.K / 32, 0, wrow);
-      }
-      for (int kt = 0; kt < nk; ++kt) {
+      // issue the loads of stage kt into (buf, sc); the K-outer weight goes to registers
+      auto load_stage = [&](uint8_t* buf, uint8_t* sc, int kt) {
+        const int kb = kt * kRowBytes;
+        xl.issue(buf + kBN * kRowBytes, xbase + kb);
+        if constexpr (MODE == MODE_M_NK) {
+          wd.issue(buf, wbase + kb);
+        } else {
+          wl.issue(Bkn, a.N, (int64_t)kt * 64, a.K, n0, a.N);
+        }
+        if constexpr (MX) {
+          xs.issue(sc + kBN * 4, xsbase + kt * 4);
+          ws.issue(sc, wsbase + kt * 4);
+        }
+      };
+      // one stage: wait for (cur) to land, start (nxt) = stage kt + 1, compute (cur)
+      auto body = [&](uint8_t* cur, uint8_t* sccur, uint8_t* nxt, uint8_t* scnxt, int kt) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const int cur = kt & 1, nxt = cur ^ 1;
         const bool more = kt + 1 < nk;
-        if (more) {
-          const int64_t kb = (int64_t)(kt + 1) * kRowBytes;
-          load_rows_direct<kBM>(stage(nxt) + kBN * kRowBytes, a.A, lda_b, kb, xrow);
-          if constexpr (MODE == MODE_M_NK) {
-            load_rows_direct<kBN>(stage(nxt), a.B, lda_b, kb, wrow);
-          } else {
-            wl.issue(Bkn, a.N, (int64_t)(kt + 1) * 64, a.K, n0, a.N);
-          }
-          if constexpr (MX) {
-            load_scales_direct<kBM>(sstage(nxt) + kBN * 4, a.As, a.K / 32, (kt + 1) * 4, xrow);
-            load_scales_direct<kBN>(sstage(nxt), a.Bs, a.K / 32, (kt + 1) * 4, wrow);
-          }
-        }
-        compute_stage<MX>(stage(cur), stage(cur) + kBN * kRowBytes, sstage(cur), sstage(cur) + kBN * 4, acc);
+        if (more) load_stage(nxt, scnxt, kt + 1);
+        compute_stage<MX>(cur, cur + kBN * kRowBytes, sccur, sccur + kBN * 4, acc);
         if constexpr (MODE == MODE_M_KN) {
-          if (more) wl.store(stage(nxt));
+          if (more) wl.store(nxt);
         }
+      };
+
+      __syncthreads();  // the previous tile's last stage has been read by everyone
+      load_stage(buf0, sc0, 0);
+      if constexpr (MODE == MODE_M_KN) wl.store(buf0);
+      for (int kt = 0; kt < nk; kt += 2) {
+        body(buf0, sc0, buf1, sc1, kt);
+        if (kt + 1 < nk) body(buf1, sc1, buf0, sc0, kt + 1);
       }
       store_tile<EPI, OUT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N,
                            EPI == MOE_EPI_SWIGLU ? f : a.N, a.C, f);
@@ -493,26 +530,29 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
       for (int i = 0; i < kTN; ++i)
 #pragma unroll
         for (int j = 0; j < kTM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();
-      if (nk > 0) {
-        xl.issue(A16, a.M, r0, r1, p0, a.M);
-        wl.issue(B16, a.N, r0, r1, q0, a.N);
-        xl.store(stage(0) + kBN * kRowBytes);
-        wl.store(stage(0));
-      }
-      for (int kt = 0; kt < nk; ++kt) {
+      auto body = [&](uint8_t* cur, uint8_t* nxt, int kt) {
         __syncthreads();
-        const int cur = kt & 1, nxt = cur ^ 1;
         const bool more = kt + 1 < nk;
         if (more) {
           xl.issue(A16, a.M, r0 + (int64_t)(kt + 1) * 64, r1, p0, a.M);
           wl.issue(B16, a.N, r0 + (int64_t)(kt + 1) * 64, r1, q0, a.N);
         }
-        compute_stage<false>(stage(cur), stage(cur) + kBN * kRowBytes, nullptr, nullptr, acc);
+        compute_stage<false>(cur, cur + kBN * kRowBytes, nullptr, nullptr, acc);
         if (more) {
-          xl.store(stage(nxt) + kBN * kRowBytes);
-          wl.store(stage(nxt));
+          xl.store(nxt + kBN * kRowBytes);
+          wl.store(nxt);
         }
+      };
+      __syncthreads();
+      if (nk > 0) {
+        xl.issue(A16, a.M, r0, r1, p0, a.M);
+        wl.issue(B16, a.N, r0, r1, q0, a.N);
+        xl.store(buf0 + kBN * kRowBytes);
+        wl.store(buf0);
+      }
+      for (int kt = 0; kt < nk; kt += 2) {
+        body(buf0, buf1, kt);
+        if (kt + 1 < nk) body(buf1, buf0, kt + 1);
       }
       uint8_t* Cg = a.C + (int64_t)g * a.M * a.N * (OUT == MOE_OUT_F32 ? 4 : 2);
       store_tile<MOE_EPI_NONE, OUT>(a, acc, p0, min(kBM, a.M - p0), q0, a.N, a.N, Cg, 0);
@@ -522,18 +562,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
 
 template <int MODE, bool MX, int EPI, int OUT>
 static moe_status_t launch(const GGArgs& a, hipStream_t s, int64_t max_tiles) {
-  const size_t smem = 2 * (size_t)kStageBytes + (MX ? 2 * (kBN + kBM) * 4 : 0) + sizeof(GroupInfo);
-  auto kern = grouped_gemm_kernel<MODE, MX, EPI, OUT>;
-  static bool attr_set = false;  // per process; the attribute is per function
-  if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
-      return MOE_ERR_HIP;
-    attr_set = true;
-  }
   int64_t grid = moe_host::device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), smem, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, MX, EPI, OUT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
