@@ -30,11 +30,10 @@
 //  * Workgroup ids are remapped so that consecutive tiles run on the same XCD
 //    (the hardware deals workgroups round-robin over the 8 XCDs), keeping the
 //    A and B panels that neighbouring tiles share in one L2.
-#include "common.h"
+#include "gg_common.h"
 
 namespace moe {
 
-constexpr int kMaxGroups = 1024;
 constexpr int kBM = 256, kBN = 256;     // output tile (rows m, columns n)
 constexpr int kWM = 2, kWN = 2;         // wavefront grid
 constexpr int kThreads = kWM * kWN * 64;
@@ -43,134 +42,9 @@ constexpr int kWTM = kBM / kWM, kWTN = kBN / kWN;  // wavefront tile
 constexpr int kTM = kWTM / 16, kTN = kWTN / 16;    // MFMA subtiles per wavefront
 constexpr int kStageBytes = (kBM + kBN) * kRowBytes;
 
-enum { MODE_M_NK = 0, MODE_M_KN = 1, MODE_K = 2 };
-
-struct GGArgs {
-  const uint8_t* A;        // activations (bytes)
-  const uint8_t* B;        // weights / second operand (bytes)
-  const uint8_t* As;       // MXFP8 scales of A
-  const uint8_t* Bs;       // MXFP8 scales of B
-  const int32_t* sizes;    // device group sizes
-  uint8_t* C;
-  uint8_t* Caux;
-  uint32_t* flag;
-  int64_t m_cap;
-  int G, M, N, K;
-  int n_tiles;             // tiles along n (ragged-M) / q (ragged-K)
-  int p_tiles;             // ragged-K: tiles along p (rows of C[g])
-};
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// ----------------------------------------------------------------- group prefix
-struct GroupInfo {
-  int32_t roff[kMaxGroups + 1];   // clamped row offsets
-  int32_t tpre[kMaxGroups + 1];   // m-tile prefix (ragged-M) / rank order (ragged-K)
-  int32_t scan[kThreads];
-};
-
-// exclusive scan of v over the workgroup (kThreads values), returns exclusive, total in *tot
-__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* buf, int32_t* tot) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int o = 1; o < kThreads; o <<= 1) {
-    int32_t add = (t >= o) ? buf[t - o] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
-  }
-  int32_t incl = buf[t];
-  *tot = buf[kThreads - 1];
-  __syncthreads();
-  return incl - v;
-}
-
-// Builds roff (row offsets, sizes clamped to >= 0 and to m_cap) and, for
-// ragged-M, tpre = prefix of ceil(size / kBM).  Raises flags from block 0.
-template <bool TILES>
-__device__ void build_groups(const GGArgs& a, GroupInfo& gi) {
-  const int t = threadIdx.x;
-  constexpr int per = kMaxGroups / kThreads;  // 4 groups per thread
-  int32_t s[per];
-  int32_t local = 0;
-  bool neg = false;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    int g = t * per + i;
-    int32_t v = (g < a.G) ? a.sizes[g] : 0;
-    if (v < 0) { neg = true; v = 0; }
-    s[i] = v;
-    local += v;
-  }
-  int32_t tot;
-  int32_t base = block_scan(local, gi.scan, &tot);
-  const int64_t cap = a.m_cap;
-  int64_t o = base;
-#pragma unroll
-  for (int i = 0; i < per; ++i) {
-    int g = t * per + i;
-    if (g <= a.G) gi.roff[g] = (int32_t)min<int64_t>(o, cap);
-    o += s[i];
-  }
-  if (t == kThreads - 1 && a.G == kMaxGroups) gi.roff[kMaxGroups] = (int32_t)min<int64_t>(o, cap);
-  if (blockIdx.x == 0 && t == 0) {
-    if ((int64_t)tot > cap) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
-  }
-  if (blockIdx.x == 0 && __any(neg) && (t & 63) == 0) raise_flag(a.flag, MOE_FLAG_NEGATIVE_SIZE);
-  __syncthreads();
-  if (TILES) {
-    int32_t lt = 0;
-    int32_t nt[per];
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      int g = t * per + i;
-      int32_t rows = (g < a.G) ? gi.roff[g + 1] - gi.roff[g] : 0;
-      nt[i] = (rows + kBM - 1) / kBM;
-      lt += nt[i];
-    }
-    int32_t tt;
-    int32_t b = block_scan(lt, gi.scan, &tt);
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      int g = t * per + i;
-      if (g <= a.G) gi.tpre[g] = b;
-      b += nt[i];
-    }
-    if (t == kThreads - 1 && a.G == kMaxGroups) gi.tpre[kMaxGroups] = b;
-    __syncthreads();
-  } else {
-    // ragged-K: order groups by size, largest first (ties: lower index first),
-    // so the longest contractions start earliest.  tpre[rank] = group.
-    for (int g = t; g < a.G; g += kThreads) {
-      const int32_t sg = gi.roff[g + 1] - gi.roff[g];
-      int rank = 0;
-      for (int h = 0; h < a.G; ++h) {
-        const int32_t sh = gi.roff[h + 1] - gi.roff[h];
-        rank += (sh > sg) || (sh == sg && h < g);
-      }
-      gi.tpre[rank] = g;
-    }
-    __syncthreads();
-  }
-}
-
-// last g in [0, G) with tpre[g] <= mt
-__device__ __forceinline__ int find_group(const int32_t* tpre, int G, int mt) {
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (tpre[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // ----------------------------------------------------------------- loaders
-// wavefront index as a scalar (uniform) value
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
 // K-contiguous rows straight into LDS.  Stage row r holds global row grow(r);
 // 16-byte slot (r, s) holds chunk swz(r, s) of it.  Each lane issues R/8/NW
 // loads; their 32-bit byte offsets (row * ld + chunk * 16) are computed once
@@ -336,15 +210,6 @@ __device__ __forceinline__ void compute_stage(const uint8_t* lw, const uint8_t* 
 }
 
 // ----------------------------------------------------------------- epilogue
-template <int OUT>
-__device__ __forceinline__ void store_sub(uint8_t* C, int64_t ldc, int64_t m, int n, const f32x4_t& v) {
-  if constexpr (OUT == MOE_OUT_F32) {
-    *reinterpret_cast<float4*>(C + (m * ldc + n) * 4) = make_float4(v[0], v[1], v[2], v[3]);
-  } else {
-    *reinterpret_cast<uint2*>(C + (m * ldc + n) * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  }
-}
-
 // Writes the wavefront's accumulators.  Plain: column n0 + wn*kWTN + 16i + 4*g4.
 // SwiGLU: subtiles i < kTN/2 are gate columns j = n0 + wn*kWTN/2 + 16i + 4*g4
 // and subtiles i + kTN/2 the up columns of the same j; the pre-activations go
@@ -401,14 +266,6 @@ __device__ __forceinline__ void store_tile(const GGArgs& a, f32x4_t (&acc)[kTN][
   }
 }
 
-__device__ __forceinline__ int worker_id() {
-  // consecutive worker ids share an XCD (blocks are dealt round-robin to 8 XCDs)
-  const int nb = gridDim.x;
-  if (nb % 8) return blockIdx.x;
-  return (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
-}
-
-// ----------------------------------------------------------------- kernel
 template <int MODE, bool MX, int EPI, int OUT>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
   // Two named stage buffers: a stage reads one while the direct-to-LDS loads
@@ -419,9 +276,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t buf1[kStageBytes];
   __shared__ __align__(16) uint8_t sc0[MX ? (kBN + kBM) * 4 : 16];   // MXFP8: W scales [kBN][4], X scales [kBM][4]
   __shared__ __align__(16) uint8_t sc1[MX ? (kBN + kBM) * 4 : 16];
-  __shared__ GroupInfo gi;
+  __shared__ GroupInfo<kThreads> gi;
 
-  build_groups<MODE != MODE_K>(a, gi);
+  build_groups<kThreads, kBM, MODE != MODE_K>(a, gi);
 
   const int wid = worker_id();
   const int f = a.N / 2;  // SwiGLU width
@@ -569,6 +426,8 @@ static moe_status_t launch(const GGArgs& a, hipStream_t s, int64_t max_tiles) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, hipStream_t s);  // gg_fwd.hip
+
 }  // namespace moe
 
 extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A, const uint8_t* As, const void* B,
@@ -600,11 +459,7 @@ extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A,
       if (d->epilogue == MOE_EPI_SWIGLU) return launch<MODE_M_NK, true, MOE_EPI_SWIGLU, MOE_OUT_BF16>(a, s, max_tiles);
       return launch<MODE_M_NK, true, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
     }
-    if (d->b_layout == MOE_B_NK) {
-      if (d->epilogue == MOE_EPI_SWIGLU) return launch<MODE_M_NK, false, MOE_EPI_SWIGLU, MOE_OUT_BF16>(a, s, max_tiles);
-      if (d->out_dtype == MOE_OUT_F32) return launch<MODE_M_NK, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
-      return launch<MODE_M_NK, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
-    }
+    if (d->b_layout == MOE_B_NK) return launch_fwd(a, d->epilogue, d->out_dtype == MOE_OUT_F32, s);
     if (d->out_dtype == MOE_OUT_F32) return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
     return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
   }
