@@ -14,8 +14,15 @@
 //    hide behind the other's MFMAs;
 //  * K is staged 32 at a time (64-byte LDS rows, 16-byte slots swizzled by
 //    (row >> 2) & 3 so a fragment read touches 16 distinct bank groups) in
-//    four named LDS buffers, filled by direct-to-LDS loads issued three
-//    stages ahead; each stage waits only for its own loads (vmcnt);
+//    five named LDS buffers (all 160 KB), filled by direct-to-LDS loads
+//    issued four stages ahead of the stage being read: loads from the
+//    L2 / MALL / HBM take microseconds under load, and LDS capacity is what
+//    bounds the bytes in flight; each stage waits only for its own loads;
+//  * the MFMA fragments of stage kt + 1 are read into registers while the
+//    MFMAs of stage kt run, so LDS latency and the per-stage barrier stay
+//    off the MFMA pipe;
+//  * the group of a tile is found by a wavefront scan over the device
+//    group sizes (no LDS table), which leaves all of LDS to the stages;
 //  * tiles are ordered in blocks of 4 m-tiles x all n-tiles and consecutive
 //    tiles run on one XCD, so the 32 tiles an XCD holds at a time share
 //    4 activation panels and 8 weight panels in its L2.
@@ -35,6 +42,14 @@ constexpr int STAGE = (BM + BN) * ROWB;       // 32 KB
 constexpr int GM = 4;                         // m-tiles per tile-order block
 constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
 
+// 16-byte slot swizzle of a 64-byte LDS row: slot = chunk ^ swz64(row).
+// (row >> 1) & 3 measured free of LDS bank conflicts for the fragment reads
+// on gfx950 (SQ_LDS_BANK_CONFLICT = 0), unlike (row >> 2) & 3 or no swizzle.
+#ifndef MOE_SWZ64
+#define MOE_SWZ64(row) (((row) >> 1) & 3)
+#endif
+__device__ __forceinline__ int swz64(int row) { return MOE_SWZ64(row); }
+
 // Direct-to-LDS rows: one wavefront instruction fills 16 rows (1 KB).  Lane l
 // writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ (l >> 4)
 // of that row (the swizzle (row >> 2) & 3 equals l >> 4 for these rows).
@@ -45,10 +60,10 @@ struct Rows {
   template <typename RowFn>
   __device__ __forceinline__ void init(int64_t ld_bytes, RowFn grow) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int chunk = (lane & 3) ^ (lane >> 4);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int row = (i * NWAVE + wave) * 16 + (lane >> 2);
+      const int chunk = (lane & 3) ^ swz64(row);
       off[i] = (uint32_t)(grow(row) * ld_bytes + chunk * 16);
     }
   }
@@ -73,22 +88,92 @@ struct Rows {
   }
 };
 
-__device__ __forceinline__ void compute(const uint8_t* buf, f32x4_t (&acc)[TN][TM]) {
+// MFMA fragments of one stage: 8 W (n) and 4 X (m) 16x32 slices per lane
+struct Frags {
+  bf16x8_t w[TN], x[TM];
+};
+
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int slot = g4 ^ ((r16 >> 2) & 3);
+  // rows base + 16 i + r16 with 16 | base: the swizzle depends on r16 only
+  // for the candidate swizzles (functions of row bits below 4)
+  const int slot = g4 ^ swz64(r16);
   const uint8_t* lw = buf + (wn * WTN + r16) * ROWB + slot * 16;
   const uint8_t* lx = buf + XOFF + (wm * WTM + r16) * ROWB + slot * 16;
-  bf16x8_t wf[TN], xf[TM];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) xf[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
+  for (int j = 0; j < TM; ++j) fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
 #pragma unroll
-  for (int i = 0; i < TN; ++i) wf[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+  for (int i = 0; i < TN; ++i) fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+}
+
+__device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], xf[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
+}
+
+// Group of m-tile mt from the device group sizes, one wavefront scan over
+// chunks of 64 groups (sizes clamped to >= 0 and the rows to m_cap, as the
+// other kernels do).  Returns g, the group's first row and its first m-tile.
+struct TileGroup {
+  int g;
+  int64_t row0, row1;
+  int64_t tile0;
+};
+
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int64_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// total m-tiles (mt < 0) or the group holding m-tile mt
+__device__ __forceinline__ TileGroup locate(const GGArgs& a, int64_t mt, int64_t* total) {
+  const int lane = threadIdx.x & 63;
+  int64_t rbase = 0, tbase = 0;
+  TileGroup r{a.G - 1, 0, 0, 0};
+  bool found = false;
+  for (int c = 0; c < a.G; c += 64) {
+    const int gi = c + lane;
+    const int64_t s = gi < a.G ? (int64_t)max(a.sizes[gi], 0) : 0;
+    const int64_t rincl = wave_incl_scan(s);
+    const int64_t r1 = min(rbase + rincl, a.m_cap), r0 = min(rbase + rincl - s, a.m_cap);
+    const int64_t nt = (r1 - r0 + BM - 1) / BM;
+    const int64_t tincl = wave_incl_scan(nt);
+    if (!found && mt >= 0) {
+      const uint64_t hit = __ballot(gi < a.G && nt > 0 && tbase + tincl > mt);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        r.g = c + l;
+        r.row0 = __shfl(r0, l, 64);
+        r.row1 = __shfl(r1, l, 64);
+        r.tile0 = tbase + __shfl(tincl - nt, l, 64);
+        found = true;
+      }
+    }
+    rbase += __shfl(rincl, 63, 64);
+    tbase += __shfl(tincl, 63, 64);
+  }
+  if (total) *total = tbase;
+  // the results are wavefront-uniform: keep them in scalar registers
+  auto u64 = [](int64_t v) -> int64_t {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  r.g = __builtin_amdgcn_readfirstlane(r.g);
+  r.row0 = u64(r.row0);
+  r.row1 = u64(r.row1);
+  r.tile0 = u64(r.tile0);
+  if (total) *total = u64(*total);
+  return r;
 }
 
 // Stores the wavefront's 128 x 64 block.  Plain: column n0 + wn*WTN + 16i + 4*g4.
@@ -144,17 +229,33 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
 
 template <int EPI, int OUT>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
+  // five named 32 KB stage buffers (the whole 160 KB LDS): stage kt lives in
+  // buffer kt % 5; loads run four stages ahead of the stage being read
   __shared__ __align__(1024) uint8_t b0[STAGE];
   __shared__ __align__(1024) uint8_t b1[STAGE];
   __shared__ __align__(1024) uint8_t b2[STAGE];
   __shared__ __align__(1024) uint8_t b3[STAGE];
-  __shared__ GroupInfo<THREADS> gi;
+  __shared__ __align__(1024) uint8_t b4[STAGE];
 
-  build_groups<THREADS, BM, true>(a, gi);
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    // data errors, reported once: negative sizes, rows past m_cap
+    bool neg = false;
+    int64_t tot = 0;
+    for (int c = 0; c < a.G; c += 64) {
+      const int gi = c + (int)threadIdx.x;
+      const int32_t v = gi < a.G ? a.sizes[gi] : 0;
+      neg |= v < 0;
+      tot += max(v, 0);
+    }
+    tot = wave_sum(tot);
+    if (__any(neg) && threadIdx.x == 0) raise_flag(a.flag, MOE_FLAG_NEGATIVE_SIZE);
+    if (tot > a.m_cap && threadIdx.x == 0) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
+  }
 
   const int wid = worker_id();
   const int f = a.N / 2;
-  const int64_t m_tiles = gi.tpre[a.G];
+  int64_t m_tiles = 0;
+  locate(a, -1, &m_tiles);
   const int64_t total = m_tiles * a.n_tiles;
   const int64_t lda_b = (int64_t)a.K * 2;
   const int nk = a.K / 32;
@@ -164,10 +265,12 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     const int64_t blk = tile / ((int64_t)GM * a.n_tiles);
     const int rem = (int)(tile - blk * GM * a.n_tiles);
     const int gm = (int)min<int64_t>(GM, m_tiles - blk * GM);
-    const int mt = (int)(blk * GM) + rem % gm, nt = rem / gm;
-    const int g = find_group(gi.tpre, a.G, mt);
-    const int64_t m0 = gi.roff[g] + (int64_t)(mt - gi.tpre[g]) * BM;
-    const int rows = (int)min<int64_t>(BM, gi.roff[g + 1] - m0);
+    const int64_t mt = blk * GM + rem % gm;
+    const int nt = rem / gm;
+    const TileGroup tg = locate(a, mt, nullptr);
+    const int g = tg.g;
+    const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
+    const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
     const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
     const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
 
@@ -196,33 +299,96 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       wl.issue(buf, wbase + kt * ROWB);
       xl.issue(buf + XOFF, xbase + kt * ROWB);
     };
-    // stage kt lives in cur; stage kt + 3 is loaded into nxt (the buffer of stage kt - 1)
-    auto step = [&](uint8_t* cur, uint8_t* nxt, int kt) {
-      const int after = min(2, nk - 1 - kt);   // stages issued after kt that may still be in flight
-      if (after >= 2) {
+    // wait until stage s has landed, given that stages up to s + 3 may have been issued
+    auto wait_stage = [&](int s) {
+      const int after = min(3, nk - 1 - s);
+      if (after >= 3) {
+        MOE_WAIT_VMCNT(3 * LPW);
+      } else if (after == 2) {
         MOE_WAIT_VMCNT(2 * LPW);
       } else if (after == 1) {
         MOE_WAIT_VMCNT(LPW);
       } else {
         MOE_WAIT_VMCNT(0);
       }
-      // a plain s_barrier: the loads were waited for above, and the memory
-      // clobber keeps the compiler from moving LDS reads across it
+      // every wavefront's fragment reads of the previous stage are done too
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt unconstrained
       asm volatile("s_barrier" ::: "memory");
-      if (kt + 3 < nk) issue(nxt, kt + 3);
-      compute(cur, acc);
+    };
+    Frags fa, fb;
+    // Step kt: the fragments of stage kt are in `cur`; stage kt + 1 (in nbuf)
+    // is waited for, published by the barrier and read into `nxt` while the
+    // MFMAs of stage kt run; stage kt's buffer (kbuf, now free) receives
+    // stage kt + 5.  The fast form has no guards: conditional code around
+    // the fragment reads makes the compiler wait for them (lgkmcnt(0)) at
+    // the join, which would serialise LDS latency into the MFMA stream.
+    auto step_fast = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
+      MOE_WAIT_VMCNT(3 * LPW);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): previous fragment reads done
+      asm volatile("s_barrier" ::: "memory");
+      issue(kbuf, kt + 5);
+      read_frags(nbuf, nxt);
+      mma(cur, acc);
+    };
+    auto step = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
+      if (kt + 1 < nk) wait_stage(kt + 1);
+      if (kt + 5 < nk) issue(kbuf, kt + 5);
+      if (kt + 1 < nk) read_frags(nbuf, nxt);
+      mma(cur, acc);
     };
 
     __syncthreads();  // every wavefront is done with the previous tile's buffers
     issue(b0, 0);
     if (nk > 1) issue(b1, 1);
     if (nk > 2) issue(b2, 2);
-    for (int kt = 0; kt < nk; kt += 4) {
-      step(b0, b3, kt);
-      if (kt + 1 < nk) step(b1, b0, kt + 1);
-      if (kt + 2 < nk) step(b2, b1, kt + 2);
-      if (kt + 3 < nk) step(b3, b2, kt + 3);
+    if (nk > 3) issue(b3, 3);
+    if (nk > 4) issue(b4, 4);
+    {
+      // stage 0 landed: stages 1..4 may still be in flight
+      const int after = min(4, nk - 1);
+      if (after >= 4) {
+        MOE_WAIT_VMCNT(4 * LPW);
+      } else if (after == 3) {
+        MOE_WAIT_VMCNT(3 * LPW);
+      } else if (after == 2) {
+        MOE_WAIT_VMCNT(2 * LPW);
+      } else if (after == 1) {
+        MOE_WAIT_VMCNT(LPW);
+      } else {
+        MOE_WAIT_VMCNT(0);
+      }
+      asm volatile("s_barrier" ::: "memory");
     }
+    read_frags(b0, fa);
+    int kt = 0;
+    // groups of ten steps while every step of the group still issues a stage (kt + 14 < nk)
+    for (; kt + 15 <= nk; kt += 10) {
+      step_fast(fa, fb, b0, b1, kt);
+      step_fast(fb, fa, b1, b2, kt + 1);
+      step_fast(fa, fb, b2, b3, kt + 2);
+      step_fast(fb, fa, b3, b4, kt + 3);
+      step_fast(fa, fb, b4, b0, kt + 4);
+      step_fast(fb, fa, b0, b1, kt + 5);
+      step_fast(fa, fb, b1, b2, kt + 6);
+      step_fast(fb, fa, b2, b3, kt + 7);
+      step_fast(fa, fb, b3, b4, kt + 8);
+      step_fast(fb, fa, b4, b0, kt + 9);
+    }
+    // the last (at most 14) steps, guarded; kt is a multiple of 10 here
+    if (kt < nk) step(fa, fb, b0, b1, kt);
+    if (kt + 1 < nk) step(fb, fa, b1, b2, kt + 1);
+    if (kt + 2 < nk) step(fa, fb, b2, b3, kt + 2);
+    if (kt + 3 < nk) step(fb, fa, b3, b4, kt + 3);
+    if (kt + 4 < nk) step(fa, fb, b4, b0, kt + 4);
+    if (kt + 5 < nk) step(fb, fa, b0, b1, kt + 5);
+    if (kt + 6 < nk) step(fa, fb, b1, b2, kt + 6);
+    if (kt + 7 < nk) step(fb, fa, b2, b3, kt + 7);
+    if (kt + 8 < nk) step(fa, fb, b3, b4, kt + 8);
+    if (kt + 9 < nk) step(fb, fa, b4, b0, kt + 9);
+    if (kt + 10 < nk) step(fa, fb, b0, b1, kt + 10);
+    if (kt + 11 < nk) step(fb, fa, b1, b2, kt + 11);
+    if (kt + 12 < nk) step(fa, fb, b2, b3, kt + 12);
+    if (kt + 13 < nk) step(fb, fa, b3, b4, kt + 13);
     store<EPI, OUT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f);
   }
 }
