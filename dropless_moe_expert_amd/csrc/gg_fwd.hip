@@ -26,67 +26,10 @@
 //  * tiles are ordered in blocks of 4 m-tiles x all n-tiles and consecutive
 //    tiles run on one XCD, so the 32 tiles an XCD holds at a time share
 //    4 activation panels and 8 weight panels in its L2.
-#include "gg_common.h"
+#include "gg_pipeline.h"
 
 namespace moe {
 namespace fwd {
-
-constexpr int BM = 256, BN = 256;   // tile rows (m) and columns (n)
-constexpr int ROWB = 64;            // LDS bytes per row and stage (32 bf16)
-constexpr int WM = 4, WN = 2;       // wavefront grid (m x n)
-constexpr int NWAVE = WM * WN, THREADS = NWAVE * 64;
-constexpr int WTM = BM / WM, WTN = BN / WN;   // 64 x 128 per wavefront
-constexpr int TM = WTM / 16, TN = WTN / 16;   // 4 x 8 MFMA subtiles
-constexpr int XOFF = BN * ROWB;               // X (activation) rows follow the W rows in a stage
-constexpr int STAGE = (BM + BN) * ROWB;       // 32 KB
-constexpr int GM = 4;                         // m-tiles per tile-order block
-constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
-
-// 16-byte slot swizzle of a 64-byte LDS row: slot = chunk ^ swz64(row).
-// (row >> 1) & 3 measured free of LDS bank conflicts for the fragment reads
-// on gfx950 (SQ_LDS_BANK_CONFLICT = 0), unlike (row >> 2) & 3 or no swizzle.
-#ifndef MOE_SWZ64
-#define MOE_SWZ64(row) (((row) >> 1) & 3)
-#endif
-__device__ __forceinline__ int swz64(int row) { return MOE_SWZ64(row); }
-
-// Direct-to-LDS rows: one wavefront instruction fills 16 rows (1 KB).  Lane l
-// writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ (l >> 4)
-// of that row (the swizzle (row >> 2) & 3 equals l >> 4 for these rows).
-template <int R>
-struct Rows {
-  static constexpr int N = R / 16 / NWAVE;
-  uint32_t off[N];
-  template <typename RowFn>
-  __device__ __forceinline__ void init(int64_t ld_bytes, RowFn grow) {
-    const int wave = wave_id(), lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int row = (i * NWAVE + wave) * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ swz64(row);
-      off[i] = (uint32_t)(grow(row) * ld_bytes + chunk * 16);
-    }
-  }
-  // The loads are written as inline asm: the compiler then does not track
-  // them as LDS writes and inserts no wait of its own before the fragment
-  // reads of other stage buffers; completion is enforced by the explicit
-  // vmcnt wait of each stage.  Its own vector-memory waits only grow more
-  // conservative (loads complete in order).
-  __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base) const {
-    const int wave = wave_id();
-    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds + wave * 1024;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %1, %2"
-          :
-          : "s"(l0 + i * NWAVE * 1024), "v"(off[i]), "s"(base)
-          : "memory", "m0");
-    }
-  }
-};
 
 // MFMA fragments of one stage: 8 W (n) and 4 X (m) 16x32 slices per lane
 struct Frags {
@@ -113,67 +56,6 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
   for (int i = 0; i < TN; ++i)
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
-}
-
-// Group of m-tile mt from the device group sizes, one wavefront scan over
-// chunks of 64 groups (sizes clamped to >= 0 and the rows to m_cap, as the
-// other kernels do).  Returns g, the group's first row and its first m-tile.
-struct TileGroup {
-  int g;
-  int64_t row0, row1;
-  int64_t tile0;
-};
-
-__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int64_t u = __shfl_up(v, o, 64);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-// total m-tiles (mt < 0) or the group holding m-tile mt
-__device__ __forceinline__ TileGroup locate(const GGArgs& a, int64_t mt, int64_t* total) {
-  const int lane = threadIdx.x & 63;
-  int64_t rbase = 0, tbase = 0;
-  TileGroup r{a.G - 1, 0, 0, 0};
-  bool found = false;
-  for (int c = 0; c < a.G; c += 64) {
-    const int gi = c + lane;
-    const int64_t s = gi < a.G ? (int64_t)max(a.sizes[gi], 0) : 0;
-    const int64_t rincl = wave_incl_scan(s);
-    const int64_t r1 = min(rbase + rincl, a.m_cap), r0 = min(rbase + rincl - s, a.m_cap);
-    const int64_t nt = (r1 - r0 + BM - 1) / BM;
-    const int64_t tincl = wave_incl_scan(nt);
-    if (!found && mt >= 0) {
-      const uint64_t hit = __ballot(gi < a.G && nt > 0 && tbase + tincl > mt);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        r.g = c + l;
-        r.row0 = __shfl(r0, l, 64);
-        r.row1 = __shfl(r1, l, 64);
-        r.tile0 = tbase + __shfl(tincl - nt, l, 64);
-        found = true;
-      }
-    }
-    rbase += __shfl(rincl, 63, 64);
-    tbase += __shfl(tincl, 63, 64);
-  }
-  if (total) *total = tbase;
-  // the results are wavefront-uniform: keep them in scalar registers
-  auto u64 = [](int64_t v) -> int64_t {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-  };
-  r.g = __builtin_amdgcn_readfirstlane(r.g);
-  r.row0 = u64(r.row0);
-  r.row1 = u64(r.row1);
-  r.tile0 = u64(r.tile0);
-  if (total) *total = u64(*total);
-  return r;
 }
 
 // Stores the wavefront's 128 x 64 block.  Plain: column n0 + wn*WTN + 16i + 4*g4.

@@ -1,0 +1,286 @@
+// Grouped GEMM, ragged along rows, MXFP8 operands (E4M3 codes, E8M0 scale
+// per 32 along K), bf16 output, optional SwiGLU epilogue.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine", section "Optimization 1: Grouped GEMM": MXFP8 block scaling for
+// the expert matmuls, fed by the group-aware quantisation kernels.
+//
+// Same pipeline as the bf16 forward kernel (persistent tiles from the device
+// group prefix, 256 x 256 tiles, 8 wavefronts, direct-to-LDS loads in 64-byte
+// rows, stages loaded three ahead), with K staged 64 codes at a time and
+// v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds row l % 32 and, for the
+// lane group g = l / 32, codes k = 16g..16g+15 and 32+16g..32+16g+15 of the
+// stage plus the scale of k-block g (layout verified on the hardware).
+// Each stage also carries its scales: every row's two scale bytes arrive by
+// a 2-byte direct load into one LDS word.  Four stages of 34 KB fit LDS.
+#include "gg_pipeline.h"
+
+namespace moe {
+namespace fwd {
+namespace mx {
+
+constexpr int SC_W = 2 * XOFF;                  // W scale words [BN], then X scale words [BM]
+constexpr int SC_X = SC_W + BN * 4;
+constexpr int MSTAGE = SC_X + BM * 4;           // 34 KB
+constexpr int LPW_MX = LPW + 1;                 // per wavefront and stage: 4 row loads + 1 scale load
+constexpr int MTN = WTN / 32, MTM = WTM / 32;   // 4 x 2 subtiles of 32 x 32
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// one scale word per row: lane l of wavefront w loads row 64 * (w % 4) + l of
+// W (w < 4) or X (w >= 4)
+struct ScaleRow {
+  uint32_t off;
+  bool is_w;
+  template <typename WRow, typename XRow>
+  __device__ __forceinline__ void init(int64_t ld, WRow wrow, XRow xrow) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    is_w = wave < 4;
+    const int r = (wave & 3) * 64 + lane;
+    off = (uint32_t)((is_w ? wrow(r) : xrow(r)) * ld);
+  }
+  __device__ __forceinline__ void issue(uint8_t* buf, const uint8_t* wsb, const uint8_t* xsb, int kt) const {
+    const int wave = wave_id();
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + (is_w ? SC_W : SC_X) + (wave & 3) * 256;
+    const uint8_t* base = (is_w ? wsb : xsb) + kt * 2;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_ushort %1, %2"
+        :
+        : "s"(l0), "v"(off), "s"(base)
+        : "memory", "m0");
+  }
+};
+
+struct Frags {
+  i32x8_t w[MTN], x[MTM];
+  int ws[MTN], xs[MTM];
+};
+
+__device__ __forceinline__ i32x8_t ld32(const uint8_t* rowp, int slot_lo, int slot_hi) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(rowp + slot_lo * 16);
+  const uint4 hi = *reinterpret_cast<const uint4*>(rowp + slot_hi * 16);
+  return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wn = wave / WM, wm = wave % WM;
+  const int r32 = lane & 31, g = lane >> 5;
+  const int sw = swz64(r32);                     // rows are 32-aligned bases + r32
+  const int s_lo = g ^ sw, s_hi = (2 + g) ^ sw;
+  const uint32_t* scw = reinterpret_cast<const uint32_t*>(buf + SC_W);
+  const uint32_t* scx = reinterpret_cast<const uint32_t*>(buf + SC_X);
+#pragma unroll
+  for (int i = 0; i < MTN; ++i) {
+    const int row = wn * WTN + i * 32 + r32;
+    fr.w[i] = ld32(buf + row * ROWB, s_lo, s_hi);
+    fr.ws[i] = (int)((scw[row] >> (8 * g)) & 0xFF);
+  }
+#pragma unroll
+  for (int j = 0; j < MTM; ++j) {
+    const int row = wm * WTM + j * 32 + r32;
+    fr.x[j] = ld32(buf + XOFF + row * ROWB, s_lo, s_hi);
+    fr.xs[j] = (int)((scx[row] >> (8 * g)) & 0xFF);
+  }
+}
+
+__device__ __forceinline__ void mma(const Frags& fr, f32x16_t (&acc)[MTN][MTM]) {
+#pragma unroll
+  for (int i = 0; i < MTN; ++i)
+#pragma unroll
+    for (int j = 0; j < MTM; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0, fr.ws[i], 0,
+                                                                   fr.xs[j]);
+}
+
+// 32x32 accumulator: element v of lane (r32, g) is n = 8*(v/4) + 4*g + v%4,
+// m = r32 within the subtile.  SwiGLU: subtiles i < MTN/2 hold gate columns,
+// i + MTN/2 the up columns of the same j.
+template <int EPI>
+__device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM], int64_t m0, int rows, int n0,
+                                      int ncols, int f) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wn = wave / WM, wm = wave % WM;
+  const int r32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < MTM; ++j) {
+    const int mr = wm * WTM + j * 32 + r32;
+    if constexpr (EPI == MOE_EPI_SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < MTN / 2; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jc = n0 + wn * (WTN / 2) + i * 32 + q * 8 + g * 4;
+          f32x4_t h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][j][q * 4 + e]) * acc[i + MTN / 2][j][q * 4 + e];
+          if (mr < rows && jc < f) store_sub<MOE_OUT_BF16>(a.C, f, m0 + mr, jc, h);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MTN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn * WTN + i * 32 + q * 8 + g * 4;
+          const f32x4_t v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+          if (mr < rows && n < ncols) store_sub<MOE_OUT_BF16>(a.C, ncols, m0 + mr, n, v);
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
+  __shared__ __align__(1024) uint8_t b0[MSTAGE];
+  __shared__ __align__(1024) uint8_t b1[MSTAGE];
+  __shared__ __align__(1024) uint8_t b2[MSTAGE];
+  __shared__ __align__(1024) uint8_t b3[MSTAGE];
+
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    bool neg = false;
+    int64_t tot = 0;
+    for (int c = 0; c < a.G; c += 64) {
+      const int gi = c + (int)threadIdx.x;
+      const int32_t v = gi < a.G ? a.sizes[gi] : 0;
+      neg |= v < 0;
+      tot += max(v, 0);
+    }
+    tot = wave_sum(tot);
+    if (__any(neg) && threadIdx.x == 0) raise_flag(a.flag, MOE_FLAG_NEGATIVE_SIZE);
+    if (tot > a.m_cap && threadIdx.x == 0) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
+  }
+
+  const int wid = worker_id();
+  const int f = a.N / 2;
+  int64_t m_tiles = 0;
+  locate(a, -1, &m_tiles);
+  const int64_t total = m_tiles * a.n_tiles;
+  const int64_t lda_b = a.K;            // one byte per code
+  const int64_t lds_b = a.K / 32;       // scale bytes per row
+  const int nk = a.K / 64;
+
+  for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+    const int64_t blk = tile / ((int64_t)GM * a.n_tiles);
+    const int rem = (int)(tile - blk * GM * a.n_tiles);
+    const int gm = (int)min<int64_t>(GM, m_tiles - blk * GM);
+    const int64_t mt = blk * GM + rem % gm;
+    const int nt = rem / gm;
+    const TileGroup tg = locate(a, mt, nullptr);
+    const int g = tg.g;
+    const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
+    const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
+    const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
+    const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
+
+    auto xrow = [&](int r) -> int64_t { return min(r, rows - 1); };
+    auto wrow = [&](int r) -> int64_t {
+      if constexpr (EPI == MOE_EPI_SWIGLU) {
+        const int wn = r / WTN, q = r % WTN;
+        const int jj = min(n0 + wn * (WTN / 2) + (q % (WTN / 2)), f - 1);
+        return q < WTN / 2 ? jj : f + jj;
+      } else {
+        return min(n0 + r, a.N - 1);
+      }
+    };
+    Rows<BM> xl;
+    Rows<BN> wl;
+    ScaleRow sl;
+    xl.init(lda_b, xrow);
+    wl.init(lda_b, wrow);
+    sl.init(lds_b, wrow, xrow);
+    const uint8_t* xbase = a.A + m0 * lda_b;
+    const uint8_t* wbase = a.B + (int64_t)g * nrows_b * lda_b;
+    const uint8_t* xsb = a.As + m0 * lds_b;
+    const uint8_t* wsb = a.Bs + (int64_t)g * nrows_b * lds_b;
+
+    f32x16_t acc[MTN][MTM];
+#pragma unroll
+    for (int i = 0; i < MTN; ++i)
+#pragma unroll
+      for (int j = 0; j < MTM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto issue = [&](uint8_t* buf, int kt) {
+      wl.issue(buf, wbase + kt * ROWB);
+      xl.issue(buf + XOFF, xbase + kt * ROWB);
+      sl.issue(buf, wsb, xsb, kt);
+    };
+    // Step kt: stage kt (in cur) has landed once at most the loads of stages
+    // kt + 1 and kt + 2 are outstanding; after the barrier its fragments are
+    // read and multiplied, and stage kt + 3 goes into the buffer of stage
+    // kt - 1.  No register prefetch of fragments here (32 x 32 accumulators
+    // leave no room at two wavefronts per SIMD); the other wavefront on the
+    // SIMD covers the LDS latency.
+    Frags fr;
+    auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+      MOE_WAIT_VMCNT(2 * LPW_MX);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      issue(lbuf, kt + 3);
+      read_frags(cur, fr);
+      mma(fr, acc);
+    };
+    auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+      const int after = min(2, nk - 1 - kt);
+      if (after >= 2) {
+        MOE_WAIT_VMCNT(2 * LPW_MX);
+      } else if (after == 1) {
+        MOE_WAIT_VMCNT(LPW_MX);
+      } else {
+        MOE_WAIT_VMCNT(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + 3 < nk) issue(lbuf, kt + 3);
+      read_frags(cur, fr);
+      mma(fr, acc);
+    };
+
+    __syncthreads();
+    issue(b0, 0);
+    if (nk > 1) issue(b1, 1);
+    if (nk > 2) issue(b2, 2);
+    int kt = 0;
+    for (; kt + 7 <= nk; kt += 4) {   // every step of the group issues a stage (kt + 6 < nk)
+      step_fast(b0, b3, kt);
+      step_fast(b1, b0, kt + 1);
+      step_fast(b2, b1, kt + 2);
+      step_fast(b3, b2, kt + 3);
+    }
+    if (kt < nk) step(b0, b3, kt);
+    if (kt + 1 < nk) step(b1, b0, kt + 1);
+    if (kt + 2 < nk) step(b2, b1, kt + 2);
+    if (kt + 3 < nk) step(b3, b2, kt + 3);
+    if (kt + 4 < nk) step(b0, b3, kt + 4);
+    if (kt + 5 < nk) step(b1, b0, kt + 5);
+    store<EPI>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f);
+  }
+}
+
+}  // namespace mx
+}  // namespace fwd
+
+moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, hipStream_t s) {
+  GGArgs b = a;
+  const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
+  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  b.n_tiles = (ncols + bn - 1) / bn;
+  const int64_t max_tiles = ((a.m_cap + fwd::BM - 1) / fwd::BM + a.G) * b.n_tiles;
+  int64_t grid = moe_host::device_cu_count();
+  if (max_tiles < grid) grid = max_tiles;
+  if (grid <= 0) grid = 1;
+  const dim3 g((unsigned)grid), t(fwd::THREADS);
+  if (epilogue == MOE_EPI_SWIGLU) {
+    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU>), g, t, 0, s, b);
+  } else {
+    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE>), g, t, 0, s, b);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace moe
