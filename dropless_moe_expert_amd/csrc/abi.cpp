@@ -27,6 +27,11 @@ moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*
                                  const int32_t*, void*, void*, uint32_t*, hipStream_t);
 }
 
+namespace moe {  // gg_fwd.hip
+size_t packed_weight_bytes(int G, int N, int K, int epilogue);
+moe_status_t launch_pack_weights(const uint16_t* w, int G, int N, int K, int epilogue, void* out, hipStream_t s);
+}  // namespace moe
+
 namespace moe_host {
 
 // CU count per device, read once per device (the only global state).
@@ -119,9 +124,10 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   if (d->N % 8) return MOE_ERR_UNSUPPORTED;
   if (d->ragged == MOE_RAGGED_M) {
     if (d->K < 1) return MOE_ERR_INVALID_ARG;
-    if (d->b_layout != MOE_B_NK && d->b_layout != MOE_B_KN) return MOE_ERR_UNSUPPORTED;
+    if (d->b_layout != MOE_B_NK && d->b_layout != MOE_B_KN && d->b_layout != MOE_B_PACKED) return MOE_ERR_UNSUPPORTED;
+    if (d->b_layout == MOE_B_PACKED && d->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->epilogue == MOE_EPI_SWIGLU) {
-      if (d->b_layout != MOE_B_NK || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
+      if (d->b_layout == MOE_B_KN || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
     } else if (C_aux) {
       return MOE_ERR_INVALID_ARG;
     }
@@ -142,6 +148,23 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
     return MOE_ERR_UNSUPPORTED;
   }
   return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, err_flag, S(stream));
+}
+
+size_t moe_pack_weights_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue) {
+  if (G < 1 || G > 1024 || N < 8 || N % 8 || K < 64 || K % 64) return 0;
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return 0;
+  if (epilogue == MOE_EPI_SWIGLU && (N / 2) % 8) return 0;
+  return moe::packed_weight_bytes(G, N, K, epilogue);
+}
+
+moe_status_t moe_pack_weights(const uint16_t* w, int32_t G, int32_t N, int32_t K, int32_t epilogue, void* out,
+                              size_t out_bytes, void* stream) {
+  const size_t need = moe_pack_weights_bytes(G, N, K, epilogue);
+  if (need == 0) return MOE_ERR_UNSUPPORTED;
+  if (!w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+  if (out_bytes < need) return MOE_ERR_WORKSPACE;
+  return moe::launch_pack_weights(w, G, N, K, epilogue, out, S(stream));
 }
 
 moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, const int32_t* perm_dst, int64_t T,

@@ -109,7 +109,11 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
   }
 }
 
-template <int EPI, int OUT>
+// Packed weights: for expert g, n-tile nt and K-stage kt the 256 weight rows
+// of the tile (in the order the tile uses them) are one contiguous 16 KB
+// block at ((g * n_tiles + nt) * nk + kt) * 16 KB, already in the LDS slot
+// order, so each direct load reads 1 KB of consecutive bytes.
+template <int EPI, int OUT, bool PACKED>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   // five named 32 KB stage buffers (the whole 160 KB LDS): stage kt lives in
   // buffer kt % 5; loads run four stages ahead of the stage being read
@@ -159,7 +163,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     Rows<BM> xl;
     Rows<BN> wl;
     xl.init(lda_b, [&](int r) -> int64_t { return min(r, rows - 1); });
-    wl.init(lda_b, [&](int r) -> int64_t {
+    if (!PACKED) wl.init(lda_b, [&](int r) -> int64_t {
       if constexpr (EPI == MOE_EPI_SWIGLU) {
         const int wn = r / WTN, q = r % WTN;
         const int jj = min(n0 + wn * (WTN / 2) + (q % (WTN / 2)), f - 1);
@@ -169,7 +173,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       }
     });
     const uint8_t* xbase = a.A + m0 * lda_b;
-    const uint8_t* wbase = a.B + (int64_t)g * nrows_b * lda_b;
+    const uint8_t* wbase = PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * (BN * ROWB)
+                                  : a.B + (int64_t)g * nrows_b * lda_b;
+    const int wstride = PACKED ? BN * ROWB : ROWB;   // bytes from one stage's weight block to the next
+    if constexpr (PACKED) {
+      const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < Rows<BN>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
+    }
 
     f32x4_t acc[TN][TM];
 #pragma unroll
@@ -178,7 +189,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto issue = [&](uint8_t* buf, int kt) {
-      wl.issue(buf, wbase + kt * ROWB);
+      wl.issue(buf, wbase + (int64_t)kt * wstride);
       xl.issue(buf + XOFF, xbase + kt * ROWB);
     };
     // wait until stage s has landed, given that stages up to s + 3 may have been issued
@@ -275,10 +286,67 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   }
 }
 
+// Packs W [G, rows_b, K] (rows_b = N, or 2f for SwiGLU) into the tile-stage
+// blocks the PACKED kernel reads; rows past the weight's end are zero.
+template <int EPI>
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int G, int N, int K,
+                                                           int n_tiles, uint4* __restrict__ out) {
+  const int nk = K / 32;
+  const int64_t chunks = (int64_t)G * n_tiles * nk * BN * 4;   // 16-byte chunks
+  const int f = N / 2;
+  const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : N;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += (int64_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(c & 3);
+    const int r = (int)((c >> 2) % BN);
+    const int64_t blk = (c >> 2) / BN;
+    const int kt = (int)(blk % nk);
+    const int64_t gn = blk / nk;
+    const int nt = (int)(gn % n_tiles), g = (int)(gn / n_tiles);
+    const int chunk = slot ^ swz64(r);
+    int row;
+    bool valid;
+    if constexpr (EPI == MOE_EPI_SWIGLU) {
+      const int n0 = nt * (BN / 2), wn = r / WTN, q = r % WTN;
+      const int jj = n0 + wn * (WTN / 2) + (q % (WTN / 2));
+      valid = jj < f;
+      row = q < WTN / 2 ? jj : f + jj;
+    } else {
+      row = nt * BN + r;
+      valid = row < N;
+    }
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (valid) v = *reinterpret_cast<const uint4*>(w + ((int64_t)g * nrows_b + row) * K + kt * 32 + chunk * 8);
+    out[c] = v;
+  }
+}
+
 }  // namespace fwd
 
+size_t packed_weight_bytes(int G, int N, int K, int epilogue) {
+  const int ncols = epilogue == MOE_EPI_SWIGLU ? N / 2 : N;
+  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  const int64_t n_tiles = (ncols + bn - 1) / bn;
+  return (size_t)G * n_tiles * (K / 32) * fwd::BN * fwd::ROWB;
+}
+
+moe_status_t launch_pack_weights(const uint16_t* w, int G, int N, int K, int epilogue, void* out, hipStream_t s) {
+  const int ncols = epilogue == MOE_EPI_SWIGLU ? N / 2 : N;
+  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  const int n_tiles = (ncols + bn - 1) / bn;
+  const int64_t chunks = (int64_t)G * n_tiles * (K / 32) * fwd::BN * 4;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((chunks + 255) / 256, (int64_t)moe_host::device_cu_count() * 16));
+  if (epilogue == MOE_EPI_SWIGLU) {
+    hipLaunchKernelGGL((fwd::pack_weights_kernel<MOE_EPI_SWIGLU>), dim3((unsigned)blocks), dim3(256), 0, s, w, G, N, K,
+                       n_tiles, reinterpret_cast<uint4*>(out));
+  } else {
+    hipLaunchKernelGGL((fwd::pack_weights_kernel<MOE_EPI_NONE>), dim3((unsigned)blocks), dim3(256), 0, s, w, G, N, K,
+                       n_tiles, reinterpret_cast<uint4*>(out));
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 // bf16, ragged-M, B [G, N, K]: the forward kernels
-moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, hipStream_t s) {
+moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int packed, hipStream_t s) {
   GGArgs b = a;
   const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
   const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
@@ -288,12 +356,20 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, hipStream_t 
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
-  if (epilogue == MOE_EPI_SWIGLU) {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16>), g, t, 0, s, b);
+  if (packed) {
+    if (epilogue == MOE_EPI_SWIGLU) {
+      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, true>), g, t, 0, s, b);
+    } else if (out_f32) {
+      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, true>), g, t, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, true>), g, t, 0, s, b);
+    }
+  } else if (epilogue == MOE_EPI_SWIGLU) {
+    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, false>), g, t, 0, s, b);
   } else if (out_f32) {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32>), g, t, 0, s, b);
+    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, false>), g, t, 0, s, b);
   } else {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16>), g, t, 0, s, b);
+    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, false>), g, t, 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -27,8 +27,8 @@ constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and 
 __device__ __forceinline__ int swz64(int row) { return MOE_SWZ64(row); }
 
 // Direct-to-LDS rows: one wavefront instruction fills 16 rows (1 KB).  Lane l
-// writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ (l >> 4)
-// of that row (the swizzle (row >> 2) & 3 equals l >> 4 for these rows).
+// writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ swz64(row)
+// of that row.
 template <int R>
 struct Rows {
   static constexpr int N = R / 16 / NWAVE;

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
 
 MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1
 MOE_RAGGED_M, MOE_RAGGED_K = 0, 1
-MOE_B_NK, MOE_B_KN = 0, 1
+MOE_B_NK, MOE_B_KN, MOE_B_PACKED = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 
@@ -32,7 +32,7 @@ FLAG_NAN_LOGIT = 0x8
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
     "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine", "moe_combine_backward",
-    "moe_swiglu_backward", "mxfp8_group_quantize",
+    "moe_swiglu_backward", "mxfp8_group_quantize", "moe_pack_weights_bytes", "moe_pack_weights",
 )
 
 
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_combine_backward": (ctypes.c_int, [P, P, P, P, i64, i32, i32, P, P, P]),
             "moe_swiglu_backward": (ctypes.c_int, [P, P, i64, i32, P, i32, P, P]),
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
+            "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
+            "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -169,18 +171,56 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Opt
     return out
 
 
-def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_sizes: torch.Tensor, *, b_layout: int = MOE_B_NK,
+class PackedWeights:
+    """bf16 expert weights [G, N, K] rewritten by moe_pack_weights for one
+    epilogue; usable only as B of the forward grouped GEMM with that epilogue."""
+
+    def __init__(self, data: torch.Tensor, G: int, N: int, K: int, epilogue: int):
+        self.data, self.G, self.N, self.K, self.epilogue = data, G, N, K, epilogue
+
+    @property
+    def shape(self):
+        return (self.G, self.N, self.K)
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def pack_weights(W: torch.Tensor, epilogue: int = MOE_EPI_NONE) -> PackedWeights:
+    """Pack W bf16 [G, N, K] (B_NK) for the forward GEMM with this epilogue."""
+    dev = _dev(W)
+    assert W.dtype == torch.bfloat16 and W.dim() == 3 and W.is_contiguous()
+    G, N, Kd = W.shape
+    need = lib().moe_pack_weights_bytes(G, N, Kd, epilogue)
+    if need == 0:
+        raise MoeError(f"moe_pack_weights: unsupported shape {tuple(W.shape)} / epilogue {epilogue}")
+    data = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_pack_weights(_ptr(W), G, N, Kd, epilogue, _ptr(data), need, _stream(dev)), "moe_pack_weights")
+    return PackedWeights(data, G, N, Kd, epilogue)
+
+
+def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int = MOE_B_NK,
                  epilogue: int = MOE_EPI_NONE, out_dtype: torch.dtype = torch.bfloat16, keep_aux: bool = False,
                  out: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
                  flag: Optional[torch.Tensor] = None):
-    """Ragged-M grouped GEMM, bf16.  A [m_cap, K]; B [G, N, K] (NK) or [G, K, N] (KN).
-    Returns C [m_cap, N] (or [m_cap, N/2] with SwiGLU) and, with keep_aux, the
-    pre-activations [m_cap, N].  Rows past sum(group_sizes) are left untouched."""
-    dev = _dev(A, B, group_sizes)
-    assert A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16 and group_sizes.dtype == torch.int32
+    """Ragged-M grouped GEMM, bf16.  A [m_cap, K]; B [G, N, K] (NK), [G, K, N]
+    (KN) or PackedWeights.  Returns C [m_cap, N] (or [m_cap, N/2] with SwiGLU)
+    and, with keep_aux, the pre-activations [m_cap, N].  Rows past
+    sum(group_sizes) are left untouched."""
+    packed = isinstance(B, PackedWeights)
+    Bt = B.data if packed else B
+    dev = _dev(A, Bt, group_sizes)
+    assert A.dtype == torch.bfloat16 and group_sizes.dtype == torch.int32
     m_cap, Kd = A.shape
+    if packed:
+        if B.epilogue != epilogue or B.K != Kd or b_layout != MOE_B_NK:
+            raise MoeError("packed weights used with another epilogue, K or layout than they were packed for")
+        b_layout = MOE_B_PACKED
+    else:
+        assert B.dtype == torch.bfloat16
     G = B.shape[0]
-    N = B.shape[1] if b_layout == MOE_B_NK else B.shape[2]
+    N = B.shape[2] if b_layout == MOE_B_KN else B.shape[1]
     ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
     if out is None:
         out = torch.empty((m_cap, ncols), dtype=out_dtype, device=dev)
@@ -188,7 +228,7 @@ def grouped_gemm(A: torch.Tensor, B: torch.Tensor, group_sizes: torch.Tensor, *,
         aux = torch.empty((m_cap, N), dtype=torch.bfloat16, device=dev)
     d = GGDesc(MOE_DTYPE_BF16, MOE_RAGGED_M, b_layout, epilogue,
                MOE_OUT_F32 if out_dtype == torch.float32 else MOE_OUT_BF16, G, 0, N, Kd, m_cap)
-    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(A), None, _ptr(B), None, _ptr(group_sizes), _ptr(out),
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(A), None, _ptr(Bt), None, _ptr(group_sizes), _ptr(out),
                               _ptr(aux), None, 0, _ptr(flag), _stream(dev)), "grouped_gemm")
     return (out, aux) if keep_aux else out
 

@@ -114,7 +114,9 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
  * ragged = MOE_RAGGED_M (forward and data gradient):
  *   C[r, n] = sum_k A[r, k] * Bop_g[k, n]   for rows r of group g
  *   A  [m_cap, K] (K contiguous);  B_NK: B [G, N, K] (Bop_g = B[g]^T);
- *   B_KN: B [G, K, N] (Bop_g = B[g]).  Output C [m_cap, N] (out_dtype).
+ *   B_KN: B [G, K, N] (Bop_g = B[g]);  B_PACKED (bf16 only): B[g]^T of
+ *   B_NK stored in the tile-stage layout written by moe_pack_weights for
+ *   the same G, N, K and epilogue.  Output C [m_cap, N] (out_dtype).
  *   epilogue MOE_EPI_SWIGLU (B_NK, bf16 only): N = 2f; with acc = A*Bop,
  *   C [m_cap, f] = bf16(silu(acc[:, j]) * acc[:, f + j]) (rows [0,f) of B[g]
  *   are the gate projection, rows [f,2f) the up projection: the prefused
@@ -137,6 +139,7 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
 #define MOE_RAGGED_K 1
 #define MOE_B_NK 0
 #define MOE_B_KN 1
+#define MOE_B_PACKED 2
 #define MOE_EPI_NONE 0
 #define MOE_EPI_SWIGLU 1
 #define MOE_OUT_BF16 0
@@ -145,7 +148,7 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
 typedef struct moe_gg_desc {
   int32_t dtype;     /* MOE_DTYPE_* */
   int32_t ragged;    /* MOE_RAGGED_M | MOE_RAGGED_K */
-  int32_t b_layout;  /* MOE_B_NK | MOE_B_KN (RAGGED_M) */
+  int32_t b_layout;  /* MOE_B_NK | MOE_B_KN | MOE_B_PACKED (RAGGED_M) */
   int32_t epilogue;  /* MOE_EPI_NONE | MOE_EPI_SWIGLU */
   int32_t out_dtype; /* MOE_OUT_BF16 | MOE_OUT_F32 */
   int32_t G;         /* number of groups */
@@ -159,6 +162,20 @@ size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc);
 moe_status_t grouped_gemm(const moe_gg_desc* desc, const void* A, const uint8_t* A_scale, const void* B,
                           const uint8_t* B_scale, const int32_t* group_sizes, void* C, void* C_aux, void* ws,
                           size_t ws_bytes, uint32_t* err_flag, void* stream);
+
+/* Weight packing for the bf16 forward GEMM (the expert weights of the blog's
+ * grouped GEMM, section "Optimization 1", are fixed between optimiser
+ * steps, so their storage order is free): W bf16 [G, N, K] (the B_NK
+ * operand; for epilogue MOE_EPI_SWIGLU the fused [gate; up] weight with
+ * N = 2f) is rewritten into out, moe_pack_weights_bytes(G, N, K, epilogue)
+ * bytes, 16-byte aligned, owned by the caller.  Every weight tile of every
+ * K-step becomes one contiguous block in the order the GEMM loads it;
+ * padding rows are zero.  The result is valid only as B of grouped_gemm with
+ * b_layout MOE_B_PACKED and the same G, N, K and epilogue.  Limits as for
+ * grouped_gemm (K % 64 == 0, N % 8 == 0, SwiGLU: (N/2) % 8 == 0). */
+size_t moe_pack_weights_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue);
+moe_status_t moe_pack_weights(const uint16_t* w, int32_t G, int32_t N, int32_t K, int32_t epilogue, void* out,
+                              size_t out_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Unpermute and combine (blog Figure 3: restore the original token order;

@@ -119,6 +119,46 @@ def test_grouped_gemm_swiglu(ops, f, Kd):
     assert max_rel_err(gu, gu_ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("N,Kd", [(512, 192), (264, 64), (8, 128)])
+def test_grouped_gemm_packed_weights(ops, N, Kd):
+    """Weights in the packed tile-stage layout give the oracle's result and the
+    very bits of the plain [G, N, K] layout (same products, same order)."""
+    sizes = np.array([0, 300, 1, 0, 517, 256], np.int32)
+    say("gg packed", N, Kd)
+    rng = np.random.default_rng(N + 3 * Kd)
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    ref = orc.grouped_gemm(A, B, sizes)
+    Bd, sz = dev(B), dev(torch.from_numpy(sizes))
+    P = ops.pack_weights(Bd)
+    C = ops.grouped_gemm(dev(A), P, sz)
+    C_plain = ops.grouped_gemm(dev(A), Bd, sz)
+    C32 = ops.grouped_gemm(dev(A), P, sz, out_dtype=torch.float32)
+    C32_plain = ops.grouped_gemm(dev(A), Bd, sz, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert max_rel_err(C, ref) <= BF16_TOL
+    assert torch.equal(C, C_plain) and torch.equal(C32, C32_plain)
+
+
+@pytest.mark.parametrize("f,Kd", [(384, 128), (200, 64), (8, 64)])
+def test_grouped_gemm_packed_weights_swiglu(ops, f, Kd):
+    sizes = np.array([3, 0, 400, 129, 0, 1], np.int32)
+    say("gg packed swiglu", f, Kd)
+    rng = np.random.default_rng(7 * f + Kd)
+    G, M = sizes.size, int(sizes.sum())
+    A, W = bf16(rng, M, Kd), bf16(rng, G, 2 * f, Kd, scale=Kd ** -0.5)
+    h_ref, gu_ref = orc.gemm_swiglu(A, W, sizes, keep_gu=True)
+    Wd, sz = dev(W), dev(torch.from_numpy(sizes))
+    P = ops.pack_weights(Wd, ops.MOE_EPI_SWIGLU)
+    h, gu = ops.grouped_gemm(dev(A), P, sz, epilogue=ops.MOE_EPI_SWIGLU, keep_aux=True)
+    h2, gu2 = ops.grouped_gemm(dev(A), Wd, sz, epilogue=ops.MOE_EPI_SWIGLU, keep_aux=True)
+    torch.cuda.synchronize()
+    assert max_rel_err(h, h_ref) <= BF16_TOL and max_rel_err(gu, gu_ref) <= BF16_TOL
+    assert torch.equal(h, h2) and torch.equal(gu, gu2)
+    with pytest.raises(ops.MoeError):          # packed for SwiGLU, used without it
+        ops.grouped_gemm(dev(A), P, sz)
+
+
 @pytest.mark.parametrize("N,Kd", [(256, 128), (200, 320), (8, 64)])
 def test_grouped_gemm_kn_dgrad(ops, N, Kd):
     sizes = np.array([0, 260, 7, 0, 300], np.int32)
