@@ -11,6 +11,7 @@ namespace moe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 

@@ -11,9 +11,12 @@
 //    group prefix; grid size depends on host arguments only;
 //  * 256 x 256 output tile, 8 wavefronts = 2 per SIMD (wavefront tile
 //    128 n x 64 m, 8 x 4 MFMA 16x16x32 bf16), so one wavefront's LDS waits
-//    hide behind the other's MFMAs;
+//    hide behind the other's MFMAs (measured alternatives, all slower: one
+//    wavefront per SIMD with 128 x 128 blocks and the accumulators in the
+//    accumulation registers; MFMA 32x32x16 instead of 16x16x32; issuing the
+//    next tile's first stages before storing the current one);
 //  * K is staged 32 at a time (64-byte LDS rows, 16-byte slots swizzled by
-//    (row >> 2) & 3 so a fragment read touches 16 distinct bank groups) in
+//    (row >> 1) & 3, free of bank conflicts for the fragment reads) in
 //    five named LDS buffers (all 160 KB), filled by direct-to-LDS loads
 //    issued four stages ahead of the stage being read: loads from the
 //    L2 / MALL / HBM take microseconds under load, and LDS capacity is what
@@ -26,36 +29,64 @@
 //  * tiles are ordered in blocks of 4 m-tiles x all n-tiles and consecutive
 //    tiles run on one XCD, so the 32 tiles an XCD holds at a time share
 //    4 activation panels and 8 weight panels in its L2.
+#include <type_traits>
+
 #include "gg_pipeline.h"
 
 namespace moe {
 namespace fwd {
+
+constexpr int WM = 4;                         // wavefront grid 4 (m) x 2 (n)
+constexpr int NWAVE = WM * WN, THREADS = NWAVE * 64;
+constexpr int WTM = BM / WM;                  // 64 x 128 per wavefront
+constexpr int TM = WTM / 16, TN = WTN / 16;   // 4 x 8 MFMA subtiles
+constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
 
 // MFMA fragments of one stage: 8 W (n) and 4 X (m) 16x32 slices per lane
 struct Frags {
   bf16x8_t w[TN], x[TM];
 };
 
-__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int wn = wave / WM, wm = wave % WM;
-  const int r16 = lane & 15, g4 = lane >> 4;
-  // rows base + 16 i + r16 with 16 | base: the swizzle depends on r16 only
-  // for the candidate swizzles (functions of row bits below 4)
-  const int slot = g4 ^ swz64(r16);
-  const uint8_t* lw = buf + (wn * WTN + r16) * ROWB + slot * 16;
-  const uint8_t* lx = buf + XOFF + (wm * WTM + r16) * ROWB + slot * 16;
-#pragma unroll
-  for (int j = 0; j < TM; ++j) fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
-#pragma unroll
-  for (int i = 0; i < TN; ++i) fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+// Wavefront position in the tile: wn = wave / WM, and the m-block wm is
+// rotated by 2 for wn = 1, so the two wavefronts of a SIMD (waves w and
+// w + 4 when wavefronts are dealt round-robin to the SIMDs) own m-blocks
+// two apart.  In a group's last, partial m-tile the wavefronts whose rows
+// are all past the group's end skip their MFMAs; with this placement every
+// SIMD then keeps about the same share of the remaining work.
+__device__ __forceinline__ void wave_pos(int& wn, int& wm) {
+  const int wave = wave_id();
+  wn = wave / WM;
+  wm = (wave % WM + 2 * wn) % WM;
 }
 
+// reads the W fragments and the first ACT X fragments (ACT = 0: nothing)
+template <int ACT>
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
+  if constexpr (ACT > 0) {
+    const int lane = threadIdx.x & 63;
+    int wn, wm;
+    wave_pos(wn, wm);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    // rows base + 16 i + r16 with 16 | base: the swizzle depends on r16 only
+    const int slot = g4 ^ swz64(r16);
+    const uint8_t* lw = buf + (wn * WTN + r16) * ROWB + slot * 16;
+    const uint8_t* lx = buf + XOFF + (wm * WTM + r16) * ROWB + slot * 16;
+#pragma unroll
+    for (int j = 0; j < ACT; ++j)
+      fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+  }
+}
+
+// MFMAs of the first ACT 16-row subtiles of the wavefront's 64 rows
+template <int ACT>
 __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < ACT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
 }
 
 // Stores the wavefront's 128 x 64 block.  Plain: column n0 + wn*WTN + 16i + 4*g4.
@@ -64,8 +95,9 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
 template <int EPI, int OUT>
 __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], int64_t m0, int rows, int n0,
                                       int ncols, int f) {
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int wn = wave / WM, wm = wave % WM;
+  const int lane = threadIdx.x & 63;
+  int wn, wm;
+  wave_pos(wn, wm);
   const int r16 = lane & 15, g4 = lane >> 4;
   if constexpr (EPI == MOE_EPI_SWIGLU) {
     const int jbase = n0 + wn * (WTN / 2) + g4 * 4;
@@ -160,8 +192,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
     const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
 
-    Rows<BM> xl;
-    Rows<BN> wl;
+    Rows<BM, NWAVE> xl;
+    Rows<BN, NWAVE> wl;
     xl.init(lda_b, [&](int r) -> int64_t { return min(r, rows - 1); });
     if (!PACKED) wl.init(lda_b, [&](int r) -> int64_t {
       if constexpr (EPI == MOE_EPI_SWIGLU) {
@@ -179,7 +211,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     if constexpr (PACKED) {
       const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
-      for (int i = 0; i < Rows<BN>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
+      for (int i = 0; i < Rows<BN, NWAVE>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
     }
 
     f32x4_t acc[TN][TM];
@@ -208,80 +240,99 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt unconstrained
       asm volatile("s_barrier" ::: "memory");
     };
-    Frags fa, fb;
-    // Step kt: the fragments of stage kt are in `cur`; stage kt + 1 (in nbuf)
-    // is waited for, published by the barrier and read into `nxt` while the
-    // MFMAs of stage kt run; stage kt's buffer (kbuf, now free) receives
-    // stage kt + 5.  The fast form has no guards: conditional code around
-    // the fragment reads makes the compiler wait for them (lgkmcnt(0)) at
-    // the join, which would serialise LDS latency into the MFMA stream.
-    auto step_fast = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
-      MOE_WAIT_VMCNT(3 * LPW);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): previous fragment reads done
-      asm volatile("s_barrier" ::: "memory");
-      issue(kbuf, kt + 5);
-      read_frags(nbuf, nxt);
-      mma(cur, acc);
-    };
-    auto step = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
-      if (kt + 1 < nk) wait_stage(kt + 1);
-      if (kt + 5 < nk) issue(kbuf, kt + 5);
-      if (kt + 1 < nk) read_frags(nbuf, nxt);
-      mma(cur, acc);
-    };
-
-    __syncthreads();  // every wavefront is done with the previous tile's buffers
-    issue(b0, 0);
-    if (nk > 1) issue(b1, 1);
-    if (nk > 2) issue(b2, 2);
-    if (nk > 3) issue(b3, 3);
-    if (nk > 4) issue(b4, 4);
-    {
-      // stage 0 landed: stages 1..4 may still be in flight
-      const int after = min(4, nk - 1);
-      if (after >= 4) {
-        MOE_WAIT_VMCNT(4 * LPW);
-      } else if (after == 3) {
+    // wavefronts whose 64 rows extend past the tile's valid rows skip the
+    // MFMAs (and fragment reads) of the missing 16-row subtiles
+    int wn_, wm_;
+    wave_pos(wn_, wm_);
+    const int act = min(TM, max(0, (rows - wm_ * WTM + 15) / 16));
+    auto run = [&](auto act_c) {
+      constexpr int ACT = decltype(act_c)::value;
+      Frags fa, fb;
+      // Step kt: the fragments of stage kt are in `cur`; stage kt + 1 (in nbuf)
+      // is waited for, published by the barrier and read into `nxt` while the
+      // MFMAs of stage kt run; stage kt's buffer (kbuf, now free) receives
+      // stage kt + 5.  The fast form has no guards: conditional code around
+      // the fragment reads makes the compiler wait for them (lgkmcnt(0)) at
+      // the join, which would serialise LDS latency into the MFMA stream.
+      auto step_fast = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
         MOE_WAIT_VMCNT(3 * LPW);
-      } else if (after == 2) {
-        MOE_WAIT_VMCNT(2 * LPW);
-      } else if (after == 1) {
-        MOE_WAIT_VMCNT(LPW);
-      } else {
-        MOE_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): previous fragment reads done
+        asm volatile("s_barrier" ::: "memory");
+        issue(kbuf, kt + 5);
+        read_frags<ACT>(nbuf, nxt);
+        mma<ACT>(cur, acc);
+      };
+      auto step = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
+        if (kt + 1 < nk) wait_stage(kt + 1);
+        if (kt + 5 < nk) issue(kbuf, kt + 5);
+        if (kt + 1 < nk) read_frags<ACT>(nbuf, nxt);
+        mma<ACT>(cur, acc);
+      };
+
+      __syncthreads();  // every wavefront is done with the previous tile's buffers
+      issue(b0, 0);
+      if (nk > 1) issue(b1, 1);
+      if (nk > 2) issue(b2, 2);
+      if (nk > 3) issue(b3, 3);
+      if (nk > 4) issue(b4, 4);
+      {
+        // stage 0 landed: stages 1..4 may still be in flight
+        const int after = min(4, nk - 1);
+        if (after >= 4) {
+          MOE_WAIT_VMCNT(4 * LPW);
+        } else if (after == 3) {
+          MOE_WAIT_VMCNT(3 * LPW);
+        } else if (after == 2) {
+          MOE_WAIT_VMCNT(2 * LPW);
+        } else if (after == 1) {
+          MOE_WAIT_VMCNT(LPW);
+        } else {
+          MOE_WAIT_VMCNT(0);
+        }
+        asm volatile("s_barrier" ::: "memory");
       }
-      asm volatile("s_barrier" ::: "memory");
+      read_frags<ACT>(b0, fa);
+      int kt = 0;
+      // groups of ten steps while every step of the group still issues a stage (kt + 14 < nk)
+      for (; kt + 15 <= nk; kt += 10) {
+        step_fast(fa, fb, b0, b1, kt);
+        step_fast(fb, fa, b1, b2, kt + 1);
+        step_fast(fa, fb, b2, b3, kt + 2);
+        step_fast(fb, fa, b3, b4, kt + 3);
+        step_fast(fa, fb, b4, b0, kt + 4);
+        step_fast(fb, fa, b0, b1, kt + 5);
+        step_fast(fa, fb, b1, b2, kt + 6);
+        step_fast(fb, fa, b2, b3, kt + 7);
+        step_fast(fa, fb, b3, b4, kt + 8);
+        step_fast(fb, fa, b4, b0, kt + 9);
+      }
+      // the last (at most 14) steps, guarded; kt is a multiple of 10 here
+      if (kt < nk) step(fa, fb, b0, b1, kt);
+      if (kt + 1 < nk) step(fb, fa, b1, b2, kt + 1);
+      if (kt + 2 < nk) step(fa, fb, b2, b3, kt + 2);
+      if (kt + 3 < nk) step(fb, fa, b3, b4, kt + 3);
+      if (kt + 4 < nk) step(fa, fb, b4, b0, kt + 4);
+      if (kt + 5 < nk) step(fb, fa, b0, b1, kt + 5);
+      if (kt + 6 < nk) step(fa, fb, b1, b2, kt + 6);
+      if (kt + 7 < nk) step(fb, fa, b2, b3, kt + 7);
+      if (kt + 8 < nk) step(fa, fb, b3, b4, kt + 8);
+      if (kt + 9 < nk) step(fb, fa, b4, b0, kt + 9);
+      if (kt + 10 < nk) step(fa, fb, b0, b1, kt + 10);
+      if (kt + 11 < nk) step(fb, fa, b1, b2, kt + 11);
+      if (kt + 12 < nk) step(fa, fb, b2, b3, kt + 12);
+      if (kt + 13 < nk) step(fb, fa, b3, b4, kt + 13);
+    };
+    if (act == TM) {
+      run(std::integral_constant<int, TM>());
+    } else if (act == 3) {
+      run(std::integral_constant<int, 3>());
+    } else if (act == 2) {
+      run(std::integral_constant<int, 2>());
+    } else if (act == 1) {
+      run(std::integral_constant<int, 1>());
+    } else {
+      run(std::integral_constant<int, 0>());
     }
-    read_frags(b0, fa);
-    int kt = 0;
-    // groups of ten steps while every step of the group still issues a stage (kt + 14 < nk)
-    for (; kt + 15 <= nk; kt += 10) {
-      step_fast(fa, fb, b0, b1, kt);
-      step_fast(fb, fa, b1, b2, kt + 1);
-      step_fast(fa, fb, b2, b3, kt + 2);
-      step_fast(fb, fa, b3, b4, kt + 3);
-      step_fast(fa, fb, b4, b0, kt + 4);
-      step_fast(fb, fa, b0, b1, kt + 5);
-      step_fast(fa, fb, b1, b2, kt + 6);
-      step_fast(fb, fa, b2, b3, kt + 7);
-      step_fast(fa, fb, b3, b4, kt + 8);
-      step_fast(fb, fa, b4, b0, kt + 9);
-    }
-    // the last (at most 14) steps, guarded; kt is a multiple of 10 here
-    if (kt < nk) step(fa, fb, b0, b1, kt);
-    if (kt + 1 < nk) step(fb, fa, b1, b2, kt + 1);
-    if (kt + 2 < nk) step(fa, fb, b2, b3, kt + 2);
-    if (kt + 3 < nk) step(fb, fa, b3, b4, kt + 3);
-    if (kt + 4 < nk) step(fa, fb, b4, b0, kt + 4);
-    if (kt + 5 < nk) step(fb, fa, b0, b1, kt + 5);
-    if (kt + 6 < nk) step(fa, fb, b1, b2, kt + 6);
-    if (kt + 7 < nk) step(fb, fa, b2, b3, kt + 7);
-    if (kt + 8 < nk) step(fa, fb, b3, b4, kt + 8);
-    if (kt + 9 < nk) step(fb, fa, b4, b0, kt + 9);
-    if (kt + 10 < nk) step(fa, fb, b0, b1, kt + 10);
-    if (kt + 11 < nk) step(fb, fa, b1, b2, kt + 11);
-    if (kt + 12 < nk) step(fa, fb, b2, b3, kt + 12);
-    if (kt + 13 < nk) step(fb, fa, b3, b4, kt + 13);
     store<EPI, OUT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f);
   }
 }

@@ -17,6 +17,11 @@
 
 namespace moe {
 namespace fwd {
+
+constexpr int WM = 4;                          // wavefront grid 4 (m) x 2 (n)
+constexpr int NWAVE = WM * WN, THREADS = NWAVE * 64;
+constexpr int WTM = BM / WM;                   // 64 x 128 per wavefront
+constexpr int LPW = (BM + BN) / 16 / NWAVE;    // direct row loads per wavefront and stage (4)
 namespace mx {
 
 constexpr int SC_W = 2 * XOFF;                  // W scale words [BN], then X scale words [BM]
@@ -25,7 +30,7 @@ constexpr int MSTAGE = SC_X + BM * 4;           // 34 KB
 constexpr int LPW_MX = LPW + 1;                 // per wavefront and stage: 4 row loads + 1 scale load
 constexpr int MTN = WTN / 32, MTM = WTM / 32;   // 4 x 2 subtiles of 32 x 32
 
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
 
 // one scale word per row: lane l of wavefront w loads row 64 * (w % 4) + l of
 // W (w < 4) or X (w >= 4)
@@ -186,8 +191,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
         return min(n0 + r, a.N - 1);
       }
     };
-    Rows<BM> xl;
-    Rows<BN> wl;
+    Rows<BM, NWAVE> xl;
+    Rows<BN, NWAVE> wl;
     ScaleRow sl;
     xl.init(lda_b, xrow);
     wl.init(lda_b, wrow);

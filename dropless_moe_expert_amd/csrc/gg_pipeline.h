@@ -9,14 +9,10 @@ namespace fwd {
 
 constexpr int BM = 256, BN = 256;   // tile rows (m) and columns (n)
 constexpr int ROWB = 64;            // LDS bytes per row and stage (32 bf16)
-constexpr int WM = 4, WN = 2;       // wavefront grid (m x n)
-constexpr int NWAVE = WM * WN, THREADS = NWAVE * 64;
-constexpr int WTM = BM / WM, WTN = BN / WN;   // 64 x 128 per wavefront
-constexpr int TM = WTM / 16, TN = WTN / 16;   // 4 x 8 MFMA subtiles
+constexpr int WN = 2, WTN = BN / WN;          // two wavefront columns of 128 n each
 constexpr int XOFF = BN * ROWB;               // X (activation) rows follow the W rows in a stage
 constexpr int STAGE = (BM + BN) * ROWB;       // 32 KB
 constexpr int GM = 4;                         // m-tiles per tile-order block
-constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
 
 // 16-byte slot swizzle of a 64-byte LDS row: slot = chunk ^ swz64(row).
 // (row >> 1) & 3 measured free of LDS bank conflicts for the fragment reads
@@ -29,16 +25,16 @@ __device__ __forceinline__ int swz64(int row) { return MOE_SWZ64(row); }
 // Direct-to-LDS rows: one wavefront instruction fills 16 rows (1 KB).  Lane l
 // writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ swz64(row)
 // of that row.
-template <int R>
+template <int R, int NW>
 struct Rows {
-  static constexpr int N = R / 16 / NWAVE;
+  static constexpr int N = R / 16 / NW;
   uint32_t off[N];
   template <typename RowFn>
   __device__ __forceinline__ void init(int64_t ld_bytes, RowFn grow) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int row = (i * NWAVE + wave) * 16 + (lane >> 2);
+      const int row = (i * NW + wave) * 16 + (lane >> 2);
       const int chunk = (lane & 3) ^ swz64(row);
       off[i] = (uint32_t)(grow(row) * ld_bytes + chunk * 16);
     }
@@ -58,7 +54,7 @@ struct Rows {
           "s_nop 0\n\t"
           "global_load_lds_dwordx4 %1, %2"
           :
-          : "s"(l0 + i * NWAVE * 1024), "v"(off[i]), "s"(base)
+          : "s"(l0 + i * NW * 1024), "v"(off[i]), "s"(base)
           : "memory", "m0");
     }
   }
