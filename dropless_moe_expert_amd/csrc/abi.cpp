@@ -30,6 +30,9 @@ moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*
 namespace moe {  // gg_fwd.hip
 size_t packed_weight_bytes(int G, int N, int K, int epilogue);
 moe_status_t launch_pack_weights(const uint16_t* w, int G, int N, int K, int epilogue, void* out, hipStream_t s);
+size_t packed_mx_weight_bytes(int G, int N, int K, int epilogue);   // gg_fwd_mx.hip
+moe_status_t launch_pack_mx_weights(const uint8_t* q, const uint8_t* sc, int G, int N, int K, int epilogue, void* out,
+                                    hipStream_t s);
 }  // namespace moe
 
 namespace moe_host {
@@ -125,16 +128,16 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   if (d->ragged == MOE_RAGGED_M) {
     if (d->K < 1) return MOE_ERR_INVALID_ARG;
     if (d->b_layout != MOE_B_NK && d->b_layout != MOE_B_KN && d->b_layout != MOE_B_PACKED) return MOE_ERR_UNSUPPORTED;
-    if (d->b_layout == MOE_B_PACKED && d->dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->epilogue == MOE_EPI_SWIGLU) {
       if (d->b_layout == MOE_B_KN || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
     } else if (C_aux) {
       return MOE_ERR_INVALID_ARG;
     }
     if (d->dtype == MOE_DTYPE_MXFP8) {
-      if (d->K % 128 || d->b_layout != MOE_B_NK || d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
-      if (!A_scale || !B_scale) return MOE_ERR_INVALID_ARG;
-      if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (reinterpret_cast<uintptr_t>(B_scale) & 3u))
+      if (d->K % 128 || d->b_layout == MOE_B_KN || d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
+      const bool packed = d->b_layout == MOE_B_PACKED;   // the weight scales travel inside the packed B
+      if (!A_scale || (!packed && !B_scale)) return MOE_ERR_INVALID_ARG;
+      if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (!packed && (reinterpret_cast<uintptr_t>(B_scale) & 3u)))
         return MOE_ERR_ALIGNMENT;
     } else {
       if (d->K % 64) return MOE_ERR_UNSUPPORTED;
@@ -165,6 +168,23 @@ moe_status_t moe_pack_weights(const uint16_t* w, int32_t G, int32_t N, int32_t K
   if (!aligned16(w) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
   if (out_bytes < need) return MOE_ERR_WORKSPACE;
   return moe::launch_pack_weights(w, G, N, K, epilogue, out, S(stream));
+}
+
+size_t moe_pack_weights_mxfp8_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue) {
+  if (G < 1 || G > 1024 || N < 8 || N % 8 || K < 128 || K % 128) return 0;
+  if (epilogue != MOE_EPI_NONE && epilogue != MOE_EPI_SWIGLU) return 0;
+  if (epilogue == MOE_EPI_SWIGLU && (N / 2) % 8) return 0;
+  return moe::packed_mx_weight_bytes(G, N, K, epilogue);
+}
+
+moe_status_t moe_pack_weights_mxfp8(const uint8_t* q, const uint8_t* scale, int32_t G, int32_t N, int32_t K,
+                                    int32_t epilogue, void* out, size_t out_bytes, void* stream) {
+  const size_t need = moe_pack_weights_mxfp8_bytes(G, N, K, epilogue);
+  if (need == 0) return MOE_ERR_UNSUPPORTED;
+  if (!q || !scale || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(scale) & 1u)) return MOE_ERR_ALIGNMENT;
+  if (out_bytes < need) return MOE_ERR_WORKSPACE;
+  return moe::launch_pack_mx_weights(q, scale, G, N, K, epilogue, out, S(stream));
 }
 
 moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, const int32_t* perm_dst, int64_t T,

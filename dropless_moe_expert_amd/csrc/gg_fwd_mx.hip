@@ -29,6 +29,11 @@ constexpr int SC_X = SC_W + BN * 4;
 constexpr int MSTAGE = SC_X + BM * 4;           // 34 KB
 constexpr int LPW_MX = LPW + 1;                 // per wavefront and stage: 4 row loads + 1 scale load
 constexpr int MTN = WTN / 32, MTM = WTM / 32;   // 4 x 2 subtiles of 32 x 32
+// packed weights: per (expert, n-tile, stage) 16 KB of codes in LDS slot
+// order, then the 256 rows' scale words (bytes 2kt, 2kt + 1 of each row's
+// scales, zero-extended to 4 bytes) in LDS order
+constexpr int PK_CODES = BN * ROWB;
+constexpr int PK_STAGE = PK_CODES + BN * 4;     // 17 KB
 
 
 
@@ -55,6 +60,20 @@ struct ScaleRow {
         :
         : "s"(l0), "v"(off), "s"(base)
         : "memory", "m0");
+  }  // packed weights: the W rows' scale words lie after the stage's codes; the
+  // X rows' scales are loaded as the aligned word holding the stage's bytes
+  // (row strides K/32 are multiples of 4), so both are plain dword loads
+  __device__ __forceinline__ void issue_packed(uint8_t* buf, const uint8_t* wstage, const uint8_t* xsb, int kt) const {
+    const int wave = wave_id();
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + (is_w ? SC_W : SC_X) + (wave & 3) * 256;
+    const uint8_t* base = is_w ? wstage : xsb + (kt >> 1) * 4;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2"
+        :
+        : "s"(l0), "v"(off), "s"(base)
+        : "memory", "m0");
   }
 };
 
@@ -69,7 +88,10 @@ __device__ __forceinline__ i32x8_t ld32(const uint8_t* rowp, int slot_lo, int sl
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
+// xsh: bit offset of the stage's two X scale bytes in their LDS word (16
+// when the packed path loaded the aligned word holding the previous stage's
+// bytes first)
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xsh = 0) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r32 = lane & 31, g = lane >> 5;
@@ -87,7 +109,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
   for (int j = 0; j < MTM; ++j) {
     const int row = wm * WTM + j * 32 + r32;
     fr.x[j] = ld32(buf + XOFF + row * ROWB, s_lo, s_hi);
-    fr.xs[j] = (int)((scx[row] >> (8 * g)) & 0xFF);
+    fr.xs[j] = (int)((scx[row] >> (xsh + 8 * g)) & 0xFF);
   }
 }
 
@@ -138,7 +160,7 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
   }
 }
 
-template <int EPI>
+template <int EPI, bool PACKED>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[MSTAGE];
   __shared__ __align__(1024) uint8_t b1[MSTAGE];
@@ -195,12 +217,21 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     Rows<BN, NWAVE> wl;
     ScaleRow sl;
     xl.init(lda_b, xrow);
-    wl.init(lda_b, wrow);
     sl.init(lds_b, wrow, xrow);
+    if constexpr (PACKED) {
+      const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < Rows<BN, NWAVE>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
+      if (sl.is_w) sl.off = (uint32_t)(PK_CODES + ((wave & 3) * 64 + lane) * 4);
+    } else {
+      wl.init(lda_b, wrow);
+    }
     const uint8_t* xbase = a.A + m0 * lda_b;
-    const uint8_t* wbase = a.B + (int64_t)g * nrows_b * lda_b;
+    const uint8_t* wbase = PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * PK_STAGE
+                                  : a.B + (int64_t)g * nrows_b * lda_b;
+    const int wstride = PACKED ? PK_STAGE : ROWB;
     const uint8_t* xsb = a.As + m0 * lds_b;
-    const uint8_t* wsb = a.Bs + (int64_t)g * nrows_b * lds_b;
+    const uint8_t* wsb = PACKED ? nullptr : a.Bs + (int64_t)g * nrows_b * lds_b;
 
     f32x16_t acc[MTN][MTM];
 #pragma unroll
@@ -211,9 +242,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     auto issue = [&](uint8_t* buf, int kt) {
-      wl.issue(buf, wbase + kt * ROWB);
+      const uint8_t* wstage = wbase + (int64_t)kt * wstride;
+      wl.issue(buf, wstage);
       xl.issue(buf + XOFF, xbase + kt * ROWB);
-      sl.issue(buf, wsb, xsb, kt);
+      if constexpr (PACKED) {
+        sl.issue_packed(buf, wstage, xsb, kt);
+      } else {
+        sl.issue(buf, wsb, xsb, kt);
+      }
     };
     // Step kt: stage kt (in cur) has landed once at most the loads of stages
     // kt + 1 and kt + 2 are outstanding; after the barrier its fragments are
@@ -227,7 +263,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       asm volatile("s_barrier" ::: "memory");
       issue(lbuf, kt + 3);
-      read_frags(cur, fr);
+      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
       mma(fr, acc);
     };
     auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
@@ -242,7 +278,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
       __builtin_amdgcn_s_waitcnt(0xC07F);
       asm volatile("s_barrier" ::: "memory");
       if (kt + 3 < nk) issue(lbuf, kt + 3);
-      read_frags(cur, fr);
+      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
       mma(fr, acc);
     };
 
@@ -267,10 +303,89 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   }
 }
 
+// Packs codes [G, rows_b, K] and scales [G, rows_b, K/32] (rows_b = N, or the
+// fused 2f of SwiGLU) into the (expert, n-tile, stage) blocks the PACKED
+// kernel reads: 1024 16-byte code chunks, then 64 chunks of 4 scale words.
+template <int EPI>
+__global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sc,
+                                                     int G, int N, int K, int n_tiles, uint4* __restrict__ out) {
+  const int nk = K / 64;
+  constexpr int UNITS = PK_STAGE / 16;   // 1088 per block
+  const int64_t total = (int64_t)G * n_tiles * nk * UNITS;
+  const int f = N / 2;
+  const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : N;
+  const int sld = K / 32;
+  auto src_row = [&](int nt, int r, bool& valid) -> int {
+    if constexpr (EPI == MOE_EPI_SWIGLU) {
+      const int n0 = nt * (BN / 2), wn = r / WTN, qq = r % WTN;
+      const int jj = n0 + wn * (WTN / 2) + (qq % (WTN / 2));
+      valid = jj < f;
+      return qq < WTN / 2 ? jj : f + jj;
+    } else {
+      const int row = nt * BN + r;
+      valid = row < N;
+      return row;
+    }
+  };
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
+    const int u = (int)(c % UNITS);
+    const int64_t blk = c / UNITS;
+    const int kt = (int)(blk % nk);
+    const int64_t gn = blk / nk;
+    const int nt = (int)(gn % n_tiles), g = (int)(gn / n_tiles);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (u < PK_CODES / 16) {
+      const int slot = u & 3, r = u >> 2;
+      const int chunk = slot ^ swz64(r);
+      bool valid;
+      const int row = src_row(nt, r, valid);
+      if (valid) v = *reinterpret_cast<const uint4*>(q + ((int64_t)g * nrows_b + row) * K + kt * 64 + chunk * 16);
+    } else {
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bool valid;
+        const int row = src_row(nt, (u - PK_CODES / 16) * 4 + e, valid);
+        wv[e] = 0;
+        if (valid) {
+          const uint8_t* p = sc + ((int64_t)g * nrows_b + row) * sld + 2 * kt;
+          wv[e] = (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+        }
+      }
+      v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    }
+    out[c] = v;
+  }
+}
+
 }  // namespace mx
 }  // namespace fwd
 
-moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, hipStream_t s) {
+size_t packed_mx_weight_bytes(int G, int N, int K, int epilogue) {
+  const int ncols = epilogue == MOE_EPI_SWIGLU ? N / 2 : N;
+  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  const int64_t n_tiles = (ncols + bn - 1) / bn;
+  return (size_t)G * n_tiles * (K / 64) * fwd::mx::PK_STAGE;
+}
+
+moe_status_t launch_pack_mx_weights(const uint8_t* q, const uint8_t* sc, int G, int N, int K, int epilogue, void* out,
+                                    hipStream_t s) {
+  const int ncols = epilogue == MOE_EPI_SWIGLU ? N / 2 : N;
+  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  const int n_tiles = (ncols + bn - 1) / bn;
+  const int64_t units = (int64_t)G * n_tiles * (K / 64) * (fwd::mx::PK_STAGE / 16);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((units + 255) / 256, (int64_t)moe_host::device_cu_count() * 16));
+  if (epilogue == MOE_EPI_SWIGLU) {
+    hipLaunchKernelGGL((fwd::mx::pack_mx_kernel<MOE_EPI_SWIGLU>), dim3((unsigned)blocks), dim3(256), 0, s, q, sc, G, N,
+                       K, n_tiles, reinterpret_cast<uint4*>(out));
+  } else {
+    hipLaunchKernelGGL((fwd::mx::pack_mx_kernel<MOE_EPI_NONE>), dim3((unsigned)blocks), dim3(256), 0, s, q, sc, G, N, K,
+                       n_tiles, reinterpret_cast<uint4*>(out));
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s) {
   GGArgs b = a;
   const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
   const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
@@ -280,10 +395,16 @@ moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, hipStream_t s) {
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
-  if (epilogue == MOE_EPI_SWIGLU) {
-    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU>), g, t, 0, s, b);
+  if (packed) {
+    if (epilogue == MOE_EPI_SWIGLU) {
+      hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU, true>), g, t, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE, true>), g, t, 0, s, b);
+    }
+  } else if (epilogue == MOE_EPI_SWIGLU) {
+    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU, false>), g, t, 0, s, b);
   } else {
-    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE>), g, t, 0, s, b);
+    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE, false>), g, t, 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -33,6 +33,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
     "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine", "moe_combine_backward",
     "moe_swiglu_backward", "mxfp8_group_quantize", "moe_pack_weights_bytes", "moe_pack_weights",
+    "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
 )
 
 
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
             "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
+            "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
+            "moe_pack_weights_mxfp8": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, sz, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -172,11 +175,12 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Opt
 
 
 class PackedWeights:
-    """bf16 expert weights [G, N, K] rewritten by moe_pack_weights for one
-    epilogue; usable only as B of the forward grouped GEMM with that epilogue."""
+    """Expert weights [G, N, K] rewritten by moe_pack_weights (bf16) or
+    moe_pack_weights_mxfp8 for one epilogue; usable only as B of the forward
+    grouped GEMM of that dtype with that epilogue."""
 
-    def __init__(self, data: torch.Tensor, G: int, N: int, K: int, epilogue: int):
-        self.data, self.G, self.N, self.K, self.epilogue = data, G, N, K, epilogue
+    def __init__(self, data: torch.Tensor, G: int, N: int, K: int, epilogue: int, mxfp8: bool = False):
+        self.data, self.G, self.N, self.K, self.epilogue, self.mxfp8 = data, G, N, K, epilogue, mxfp8
 
     @property
     def shape(self):
@@ -200,6 +204,21 @@ def pack_weights(W: torch.Tensor, epilogue: int = MOE_EPI_NONE) -> PackedWeights
     return PackedWeights(data, G, N, Kd, epilogue)
 
 
+def pack_weights_mxfp8(Bq: torch.Tensor, Bs: torch.Tensor, epilogue: int = MOE_EPI_NONE) -> PackedWeights:
+    """Pack MXFP8 weights (codes uint8 [G, N, K], scales uint8 [G, N, K/32])."""
+    dev = _dev(Bq, Bs)
+    assert Bq.dtype == torch.uint8 and Bs.dtype == torch.uint8 and Bq.dim() == 3
+    G, N, Kd = Bq.shape
+    assert tuple(Bs.shape) == (G, N, Kd // 32)
+    need = lib().moe_pack_weights_mxfp8_bytes(G, N, Kd, epilogue)
+    if need == 0:
+        raise MoeError(f"moe_pack_weights_mxfp8: unsupported shape {tuple(Bq.shape)} / epilogue {epilogue}")
+    data = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_pack_weights_mxfp8(_ptr(Bq), _ptr(Bs), G, N, Kd, epilogue, _ptr(data), need, _stream(dev)),
+           "moe_pack_weights_mxfp8")
+    return PackedWeights(data, G, N, Kd, epilogue, mxfp8=True)
+
+
 def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int = MOE_B_NK,
                  epilogue: int = MOE_EPI_NONE, out_dtype: torch.dtype = torch.bfloat16, keep_aux: bool = False,
                  out: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
@@ -214,7 +233,7 @@ def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int
     assert A.dtype == torch.bfloat16 and group_sizes.dtype == torch.int32
     m_cap, Kd = A.shape
     if packed:
-        if B.epilogue != epilogue or B.K != Kd or b_layout != MOE_B_NK:
+        if B.mxfp8 or B.epilogue != epilogue or B.K != Kd or b_layout != MOE_B_NK:
             raise MoeError("packed weights used with another epilogue, K or layout than they were packed for")
         b_layout = MOE_B_PACKED
     else:
@@ -250,20 +269,30 @@ def grouped_gemm_wgrad(X: torch.Tensor, Y: torch.Tensor, group_sizes: torch.Tens
     return out
 
 
-def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq: torch.Tensor, Bs: torch.Tensor,
+def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torch.Tensor],
                        group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
                        out: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None):
     """MXFP8 ragged-M grouped GEMM.  Aq uint8 [m_cap, K], As uint8 [m_cap, K/32],
-    Bq uint8 [G, N, K], Bs uint8 [G, N, K/32] -> bf16 [m_cap, N] (or N/2 with SwiGLU)."""
-    dev = _dev(Aq, As, Bq, Bs, group_sizes)
+    Bq uint8 [G, N, K] with Bs uint8 [G, N, K/32], or Bq = PackedWeights from
+    pack_weights_mxfp8 (Bs None) -> bf16 [m_cap, N] (or N/2 with SwiGLU)."""
+    packed = isinstance(Bq, PackedWeights)
     m_cap, Kd = Aq.shape
+    if packed:
+        if not Bq.mxfp8 or Bq.epilogue != epilogue or Bq.K != Kd:
+            raise MoeError("packed weights used with another dtype, epilogue or K than they were packed for")
+        dev = _dev(Aq, As, Bq.data, group_sizes)
+        Bt, layout = Bq.data, MOE_B_PACKED
+    else:
+        dev = _dev(Aq, As, Bq, Bs, group_sizes)
+        Bt, layout = Bq, MOE_B_NK
     G, N = Bq.shape[0], Bq.shape[1]
     ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
     if out is None:
         out = torch.empty((m_cap, ncols), dtype=torch.bfloat16, device=dev)
-    d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, MOE_B_NK, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
-    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bq), _ptr(Bs), _ptr(group_sizes),
-                              _ptr(out), None, None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (mxfp8)")
+    d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, layout, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bt), None if packed else _ptr(Bs),
+                              _ptr(group_sizes), _ptr(out), None, None, 0, _ptr(flag), _stream(dev)),
+           "grouped_gemm (mxfp8)")
     return out
 
 
@@ -365,7 +394,8 @@ def expert_mlp(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1p: torch.Tenso
 def expert_mlp_mxfp8(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1q, w1s, w2q, w2s,
                      flag: Optional[torch.Tensor] = None):
     """MXFP8 expert share: quantise X, GEMM + SwiGLU, quantise H, GEMM.  Weights
-    come pre-quantised ([G, N, K] codes with [G, N, K/32] scales)."""
+    come pre-quantised ([G, N, K] codes with [G, N, K/32] scales), or packed
+    (PackedWeights from pack_weights_mxfp8, with w1s = w2s = None)."""
     xq, xs = mxfp8_quantize(x_perm, 0, group_sizes, flag=flag)
     h = grouped_gemm_mxfp8(xq, xs, w1q, w1s, group_sizes, epilogue=MOE_EPI_SWIGLU, flag=flag)
     hq, hs = mxfp8_quantize(h, 0, group_sizes, flag=flag)

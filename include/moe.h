@@ -114,9 +114,10 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
  * ragged = MOE_RAGGED_M (forward and data gradient):
  *   C[r, n] = sum_k A[r, k] * Bop_g[k, n]   for rows r of group g
  *   A  [m_cap, K] (K contiguous);  B_NK: B [G, N, K] (Bop_g = B[g]^T);
- *   B_KN: B [G, K, N] (Bop_g = B[g]);  B_PACKED (bf16 only): B[g]^T of
- *   B_NK stored in the tile-stage layout written by moe_pack_weights for
- *   the same G, N, K and epilogue.  Output C [m_cap, N] (out_dtype).
+ *   B_KN: B [G, K, N] (Bop_g = B[g]);  B_PACKED: B[g]^T of B_NK stored in
+ *   the tile-stage layout written by moe_pack_weights (bf16) or
+ *   moe_pack_weights_mxfp8 for the same G, N, K and epilogue.  Output
+ *   C [m_cap, N] (out_dtype).
  *   epilogue MOE_EPI_SWIGLU (B_NK, bf16 only): N = 2f; with acc = A*Bop,
  *   C [m_cap, f] = bf16(silu(acc[:, j]) * acc[:, f + j]) (rows [0,f) of B[g]
  *   are the gate projection, rows [f,2f) the up projection: the prefused
@@ -126,9 +127,11 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
  * ragged = MOE_RAGGED_K (weight gradient; contraction over a group's rows):
  *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
  *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
- * dtype = MOE_DTYPE_MXFP8 (RAGGED_M, B_NK only): A, B are E4M3 codes with
- *   E8M0 scales A_scale [m_cap, K/32], B_scale [G, N, K/32] (value =
- *   code * 2^(scale - 127)); accumulation fp32, output bf16.
+ * dtype = MOE_DTYPE_MXFP8 (RAGGED_M, B_NK or B_PACKED): A, B are E4M3 codes
+ *   with E8M0 scales A_scale [m_cap, K/32], B_scale [G, N, K/32] (value =
+ *   code * 2^(scale - 127)); accumulation fp32, output bf16.  With
+ *   B_PACKED, B comes from moe_pack_weights_mxfp8 (codes and scales
+ *   together) and B_scale is ignored.
  * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
  * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
  *   MXFP8: K % 128 == 0.  A, B, C 16-byte aligned.
@@ -176,6 +179,19 @@ moe_status_t grouped_gemm(const moe_gg_desc* desc, const void* A, const uint8_t*
 size_t moe_pack_weights_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue);
 moe_status_t moe_pack_weights(const uint16_t* w, int32_t G, int32_t N, int32_t K, int32_t epilogue, void* out,
                               size_t out_bytes, void* stream);
+
+/* The same for MXFP8 weights (blog: MXFP8 expert matmuls, section
+ * "Optimization 1"; weights quantised once): codes q uint8 [G, N, K]
+ * (16-byte aligned) and E8M0 scales uint8 [G, N, K/32] (2-byte aligned), as
+ * written by mxfp8_group_quantize, are rewritten together into out
+ * (moe_pack_weights_mxfp8_bytes(G, N, K, epilogue) bytes, 16-byte aligned,
+ * caller-owned): per weight tile and 64-deep K-step the codes in load order,
+ * then the scale bytes of that step.  Valid only as B of an MXFP8
+ * grouped_gemm with b_layout MOE_B_PACKED and the same G, N, K, epilogue.
+ * K % 128 == 0, N % 8 == 0 (SwiGLU: (N/2) % 8 == 0); 0 bytes = unsupported. */
+size_t moe_pack_weights_mxfp8_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue);
+moe_status_t moe_pack_weights_mxfp8(const uint8_t* q, const uint8_t* scale, int32_t G, int32_t N, int32_t K,
+                                    int32_t epilogue, void* out, size_t out_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Unpermute and combine (blog Figure 3: restore the original token order;

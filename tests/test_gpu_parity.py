@@ -256,6 +256,31 @@ def test_grouped_gemm_mxfp8(ops, swiglu):
     torch.cuda.synchronize()
     assert rel_l2(out[:M], ref) <= MX_TOL
     assert max_rel_err(out[:M], ref) <= 2 * BF16_TOL
+    # the packed weight layout (codes and scales together) gives the same bits
+    epi = ops.MOE_EPI_SWIGLU if swiglu else ops.MOE_EPI_NONE
+    P = ops.pack_weights_mxfp8(t(bq), t(bs), epi)
+    out_p = ops.grouped_gemm_mxfp8(t(aq), t(as_), P, None, t(sizes), epilogue=epi)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p[:M], out[:M])
+
+
+@pytest.mark.parametrize("N,Kd", [(8, 128), (264, 256)])
+def test_grouped_gemm_mxfp8_packed_narrow(ops, N, Kd):
+    """Packed MXFP8 weights with a partial last n-tile (padding rows are zero)."""
+    sizes = np.array([3, 0, 257], np.int32)
+    say("gg mxfp8 packed", N, Kd)
+    rng = np.random.default_rng(N + Kd)
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    aq, as_ = orc.mxfp8_quantize(A, 0)
+    bq, bs = orc.mxfp8_quantize(orc.u16(B).reshape(-1, Kd), 0)
+    bq, bs = bq.reshape(G, N, Kd), bs.reshape(G, N, Kd // 32)
+    ref = orc.mx_grouped_gemm(aq, as_, bq, bs, sizes, swiglu=False)
+    t = lambda a: dev(torch.from_numpy(np.ascontiguousarray(a)))
+    P = ops.pack_weights_mxfp8(t(bq), t(bs))
+    out = ops.grouped_gemm_mxfp8(t(aq), t(as_), P, None, t(sizes))
+    torch.cuda.synchronize()
+    assert rel_l2(out[:M], ref) <= MX_TOL
 
 
 # ------------------------------------------------------------------- combine and backward helpers
