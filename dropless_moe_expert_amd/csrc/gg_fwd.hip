@@ -9,26 +9,34 @@
 // gfx950 design:
 //  * persistent workgroups (one per CU) walk the tiles of the device-side
 //    group prefix; grid size depends on host arguments only;
-//  * 256 x 256 output tile, 8 wavefronts = 2 per SIMD (wavefront tile
-//    128 n x 64 m, 8 x 4 MFMA 16x16x32 bf16), so one wavefront's LDS waits
-//    hide behind the other's MFMAs (measured alternatives, all slower: one
-//    wavefront per SIMD with 128 x 128 blocks and the accumulators in the
-//    accumulation registers; MFMA 32x32x16 instead of 16x16x32; issuing the
-//    next tile's first stages before storing the current one);
+//  * 256 x 256 output tile, 8 wavefronts = 2 per SIMD, each owning 128 n x
+//    64 m as 8 x 4 MFMA 16x16x32 bf16 accumulators; in a group's last,
+//    partial tile a wavefront reads and multiplies only its 16-row subtiles
+//    that hold valid rows (ACT of 4), and the two wavefronts of a SIMD own
+//    row blocks two apart to share what is left.  Measured: dealing the
+//    valid subtiles evenly to all wavefronts instead is 1.3 % slower, since
+//    every wavefront then also reads the weight fragments (on a
+//    power-limited chip, bytes moved cost as much as balance gains);
+//  * ping-pong schedule: each K-stage is a memory phase (issue the loads of a
+//    later stage, read this stage's fragments from LDS into registers) and a
+//    compute phase (the stage's MFMAs from registers), separated by
+//    workgroup barriers; the second wavefront of every SIMD runs one phase
+//    behind the first, so one of the two issues MFMAs while the other waits
+//    on LDS, and each needs a single set of fragment registers;
 //  * K is staged 32 at a time (64-byte LDS rows, 16-byte slots swizzled by
 //    (row >> 1) & 3, free of bank conflicts for the fragment reads) in
 //    five named LDS buffers (all 160 KB), filled by direct-to-LDS loads
 //    issued four stages ahead of the stage being read: loads from the
 //    L2 / MALL / HBM take microseconds under load, and LDS capacity is what
 //    bounds the bytes in flight; each stage waits only for its own loads;
-//  * the MFMA fragments of stage kt + 1 are read into registers while the
-//    MFMAs of stage kt run, so LDS latency and the per-stage barrier stay
-//    off the MFMA pipe;
 //  * the group of a tile is found by a wavefront scan over the device
 //    group sizes (no LDS table), which leaves all of LDS to the stages;
 //  * tiles are ordered in blocks of 4 m-tiles x all n-tiles and consecutive
 //    tiles run on one XCD, so the 32 tiles an XCD holds at a time share
 //    4 activation panels and 8 weight panels in its L2.
+// Measured on random operands, MI355X sustains about 70 % of its nominal
+// bf16 MFMA rate for this fragment pattern even with no memory traffic
+// (power-limited clocks); every byte moved lowers that further.
 #include <type_traits>
 
 #include "gg_pipeline.h"
@@ -42,45 +50,50 @@ constexpr int WTM = BM / WM;                  // 64 x 128 per wavefront
 constexpr int TM = WTM / 16, TN = WTN / 16;   // 4 x 8 MFMA subtiles
 constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
 
-// MFMA fragments of one stage: 8 W (n) and 4 X (m) 16x32 slices per lane
+// MFMA fragments of one stage: 8 W (n) and up to 4 X (m) 16x32 slices per lane
 struct Frags {
   bf16x8_t w[TN], x[TM];
 };
 
-// Wavefront position in the tile: wn = wave / WM, and the m-block wm is
-// rotated by 2 for wn = 1, so the two wavefronts of a SIMD (waves w and
-// w + 4 when wavefronts are dealt round-robin to the SIMDs) own m-blocks
-// two apart.  In a group's last, partial m-tile the wavefronts whose rows
-// are all past the group's end skip their MFMAs; with this placement every
-// SIMD then keeps about the same share of the remaining work.
+// Wavefront position in the tile: n-block wn = wave / WM (128 columns) and
+// row slot wm, rotated by 2 for wn = 1 so that the two wavefronts of a SIMD
+// (waves w and w + 4: wavefronts are dealt round-robin to the SIMDs) hold
+// slots two apart.
 __device__ __forceinline__ void wave_pos(int& wn, int& wm) {
   const int wave = wave_id();
   wn = wave / WM;
   wm = (wave % WM + 2 * wn) % WM;
 }
 
-// reads the W fragments and the first ACT X fragments (ACT = 0: nothing)
-template <int ACT>
-__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr) {
-  if constexpr (ACT > 0) {
-    const int lane = threadIdx.x & 63;
-    int wn, wm;
-    wave_pos(wn, wm);
-    const int r16 = lane & 15, g4 = lane >> 4;
-    // rows base + 16 i + r16 with 16 | base: the swizzle depends on r16 only
-    const int slot = g4 ^ swz64(r16);
-    const uint8_t* lw = buf + (wn * WTN + r16) * ROWB + slot * 16;
-    const uint8_t* lx = buf + XOFF + (wm * WTM + r16) * ROWB + slot * 16;
-#pragma unroll
-    for (int j = 0; j < ACT; ++j)
-      fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-      fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
-  }
+// Row slot wm owns tile rows xrow0 = 64 * wm + [0, 64), of which the first
+// act 16-row subtiles hold valid rows (0..4).
+__device__ __forceinline__ void slot_rows(int rows, int wm, int& act, int& xrow0) {
+  xrow0 = WTM * wm;
+  act = min(TM, max(0, (rows - xrow0 + 15) / 16));
 }
 
-// MFMAs of the first ACT 16-row subtiles of the wavefront's 64 rows
+// reads the stage's W fragments and the wavefront's ACT X fragments (rows
+// xrow0 + [0, 16 * ACT)); ACT = 0: nothing
+template <int ACT>
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xrow0) {
+  if constexpr (ACT == 0) return;
+  const int lane = threadIdx.x & 63;
+  int wn, wm;
+  wave_pos(wn, wm);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  // rows base + 16 i + r16 with 16 | base: the swizzle depends on r16 only
+  const int slot = g4 ^ swz64(r16);
+  const uint8_t* lw = buf + (wn * WTN + r16) * ROWB + slot * 16;
+  const uint8_t* lx = buf + XOFF + (xrow0 + r16) * ROWB + slot * 16;
+#pragma unroll
+  for (int j = 0; j < ACT; ++j)
+    fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+    fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+}
+
+// MFMAs of the wavefront's ACT 16-row subtiles
 template <int ACT>
 __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
 #pragma unroll
@@ -89,12 +102,12 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
     for (int j = 0; j < ACT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
 }
 
-// Stores the wavefront's 128 x 64 block.  Plain: column n0 + wn*WTN + 16i + 4*g4.
+// Stores the wavefront's 128 x (16 * ACT) block (rows xrow0 + ...).  Plain: column n0 + wn*WTN + 16i + 4*g4.
 // SwiGLU: subtiles i < TN/2 hold gate column j = n0 + wn*WTN/2 + 16i + 4*g4 and
 // subtile i + TN/2 the up column of the same j.
-template <int EPI, int OUT>
+template <int EPI, int OUT, int ACT>
 __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], int64_t m0, int rows, int n0,
-                                      int ncols, int f) {
+                                      int ncols, int f, int xrow0) {
   const int lane = threadIdx.x & 63;
   int wn, wm;
   wave_pos(wn, wm);
@@ -104,8 +117,8 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
     if (a.Caux) {
       const int64_t lda = 2 * (int64_t)f;
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int mr = wm * WTM + j * 16 + r16;
+      for (int j = 0; j < ACT; ++j) {
+        const int mr = xrow0 + j * 16 + r16;
 #pragma unroll
         for (int i = 0; i < TN / 2; ++i) {
           const int jc = jbase + i * 16;
@@ -117,8 +130,8 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
       }
     }
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int mr = wm * WTM + j * 16 + r16;
+    for (int j = 0; j < ACT; ++j) {
+      const int mr = xrow0 + j * 16 + r16;
 #pragma unroll
       for (int i = 0; i < TN / 2; ++i) {
         const int jc = jbase + i * 16;
@@ -130,8 +143,8 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int mr = wm * WTM + j * 16 + r16;
+    for (int j = 0; j < ACT; ++j) {
+      const int mr = xrow0 + j * 16 + r16;
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
         const int n = n0 + wn * WTN + i * 16 + g4 * 4;
@@ -214,19 +227,17 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       for (int i = 0; i < Rows<BN, NWAVE>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
     }
 
-    f32x4_t acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
     auto issue = [&](uint8_t* buf, int kt) {
       wl.issue(buf, wbase + (int64_t)kt * wstride);
       xl.issue(buf + XOFF, xbase + kt * ROWB);
     };
-    // wait until stage s has landed, given that stages up to s + 3 may have been issued
-    auto wait_stage = [&](int s) {
-      const int after = min(3, nk - 1 - s);
+    // Waits until this wavefront's loads of stage s + 1 have landed (stages
+    // up to min(s + 4, nk - 1) may have been issued) and its fragment reads
+    // are done, then the workgroup barrier.  The scheduling fences keep the
+    // compiler from moving MFMAs across the barrier.
+    auto sync = [&](int s) {
+      const int after = min(3, nk - 2 - s);
+      __builtin_amdgcn_sched_barrier(0);
       if (after >= 3) {
         MOE_WAIT_VMCNT(3 * LPW);
       } else if (after == 2) {
@@ -236,94 +247,59 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       } else {
         MOE_WAIT_VMCNT(0);
       }
-      // every wavefront's fragment reads of the previous stage are done too
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt/expcnt unconstrained
       asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // wavefronts whose 64 rows extend past the tile's valid rows skip the
-    // MFMAs (and fragment reads) of the missing 16-row subtiles
-    int wn_, wm_;
+    // the first wavefront of each SIMD is waves 0..3, the second 4..7
+    const bool second = wave_id() >= NWAVE / 2;
+    int wn_, wm_, act, xrow0;
     wave_pos(wn_, wm_);
-    const int act = min(TM, max(0, (rows - wm_ * WTM + 15) / 16));
+    slot_rows(rows, wm_, act, xrow0);
     auto run = [&](auto act_c) {
       constexpr int ACT = decltype(act_c)::value;
-      Frags fa, fb;
-      // Step kt: the fragments of stage kt are in `cur`; stage kt + 1 (in nbuf)
-      // is waited for, published by the barrier and read into `nxt` while the
-      // MFMAs of stage kt run; stage kt's buffer (kbuf, now free) receives
-      // stage kt + 5.  The fast form has no guards: conditional code around
-      // the fragment reads makes the compiler wait for them (lgkmcnt(0)) at
-      // the join, which would serialise LDS latency into the MFMA stream.
-      auto step_fast = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
-        MOE_WAIT_VMCNT(3 * LPW);
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): previous fragment reads done
-        asm volatile("s_barrier" ::: "memory");
-        issue(kbuf, kt + 5);
-        read_frags<ACT>(nbuf, nxt);
-        mma<ACT>(cur, acc);
+      f32x4_t acc[TN][TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      Frags fr;
+      // Iteration s: memory phase (issue stage s + 4 into the buffer of
+      // stage s - 1, which every wavefront finished reading before the last
+      // barrier; read the fragments of stage s), barrier, compute phase,
+      // barrier.  The second wavefronts start one barrier later, so their
+      // memory phase runs beside the first wavefronts' compute phase and
+      // the other way round; they skip the final barrier to even the count.
+      auto iter = [&](uint8_t* sbuf, uint8_t* lbuf, int s) {
+        if (s + 4 < nk) issue(lbuf, s + 4);
+        read_frags<ACT>(sbuf, fr, xrow0);
+        sync(s);
+        mma<ACT>(fr, acc);
+        if (!(second && s == nk - 1)) sync(s);
       };
-      auto step = [&](Frags& cur, Frags& nxt, uint8_t* kbuf, uint8_t* nbuf, int kt) {
-        if (kt + 1 < nk) wait_stage(kt + 1);
-        if (kt + 5 < nk) issue(kbuf, kt + 5);
-        if (kt + 1 < nk) read_frags<ACT>(nbuf, nxt);
-        mma<ACT>(cur, acc);
-      };
-
       __syncthreads();  // every wavefront is done with the previous tile's buffers
       issue(b0, 0);
       if (nk > 1) issue(b1, 1);
       if (nk > 2) issue(b2, 2);
       if (nk > 3) issue(b3, 3);
-      if (nk > 4) issue(b4, 4);
-      {
-        // stage 0 landed: stages 1..4 may still be in flight
-        const int after = min(4, nk - 1);
-        if (after >= 4) {
-          MOE_WAIT_VMCNT(4 * LPW);
-        } else if (after == 3) {
-          MOE_WAIT_VMCNT(3 * LPW);
-        } else if (after == 2) {
-          MOE_WAIT_VMCNT(2 * LPW);
-        } else if (after == 1) {
-          MOE_WAIT_VMCNT(LPW);
-        } else {
-          MOE_WAIT_VMCNT(0);
-        }
-        asm volatile("s_barrier" ::: "memory");
+      sync(-1);                 // stage 0 landed
+      if (second) sync(-1);     // the half-step offset
+      int s = 0;
+      for (; s + 5 <= nk; s += 5) {
+        iter(b0, b4, s);
+        iter(b1, b0, s + 1);
+        iter(b2, b1, s + 2);
+        iter(b3, b2, s + 3);
+        iter(b4, b3, s + 4);
       }
-      read_frags<ACT>(b0, fa);
-      int kt = 0;
-      // groups of ten steps while every step of the group still issues a stage (kt + 14 < nk)
-      for (; kt + 15 <= nk; kt += 10) {
-        step_fast(fa, fb, b0, b1, kt);
-        step_fast(fb, fa, b1, b2, kt + 1);
-        step_fast(fa, fb, b2, b3, kt + 2);
-        step_fast(fb, fa, b3, b4, kt + 3);
-        step_fast(fa, fb, b4, b0, kt + 4);
-        step_fast(fb, fa, b0, b1, kt + 5);
-        step_fast(fa, fb, b1, b2, kt + 6);
-        step_fast(fb, fa, b2, b3, kt + 7);
-        step_fast(fa, fb, b3, b4, kt + 8);
-        step_fast(fb, fa, b4, b0, kt + 9);
-      }
-      // the last (at most 14) steps, guarded; kt is a multiple of 10 here
-      if (kt < nk) step(fa, fb, b0, b1, kt);
-      if (kt + 1 < nk) step(fb, fa, b1, b2, kt + 1);
-      if (kt + 2 < nk) step(fa, fb, b2, b3, kt + 2);
-      if (kt + 3 < nk) step(fb, fa, b3, b4, kt + 3);
-      if (kt + 4 < nk) step(fa, fb, b4, b0, kt + 4);
-      if (kt + 5 < nk) step(fb, fa, b0, b1, kt + 5);
-      if (kt + 6 < nk) step(fa, fb, b1, b2, kt + 6);
-      if (kt + 7 < nk) step(fb, fa, b2, b3, kt + 7);
-      if (kt + 8 < nk) step(fa, fb, b3, b4, kt + 8);
-      if (kt + 9 < nk) step(fb, fa, b4, b0, kt + 9);
-      if (kt + 10 < nk) step(fa, fb, b0, b1, kt + 10);
-      if (kt + 11 < nk) step(fb, fa, b1, b2, kt + 11);
-      if (kt + 12 < nk) step(fa, fb, b2, b3, kt + 12);
-      if (kt + 13 < nk) step(fb, fa, b3, b4, kt + 13);
+      if (s < nk) iter(b0, b4, s);
+      if (s + 1 < nk) iter(b1, b0, s + 1);
+      if (s + 2 < nk) iter(b2, b1, s + 2);
+      if (s + 3 < nk) iter(b3, b2, s + 3);
+      store<EPI, OUT, ACT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f, xrow0);
     };
-    if (act == TM) {
-      run(std::integral_constant<int, TM>());
+    if (act == 4) {
+      run(std::integral_constant<int, 4>());
     } else if (act == 3) {
       run(std::integral_constant<int, 3>());
     } else if (act == 2) {
@@ -333,7 +309,6 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     } else {
       run(std::integral_constant<int, 0>());
     }
-    store<EPI, OUT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f);
   }
 }
 
