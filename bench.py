@@ -11,10 +11,17 @@ Valid-row FLOPs = 2 * rows * (2f * d + d * f); padding rows never count.
 Also reported in the same line:
   * roofline of the dominant kernel (the gate/up GEMM), its average launch
     time measured with HIP events on the stream it runs on;
-  * the MoE layer tokens/s of the Mixtral-shaped forward (T=4096, d=4096,
-    8 experts top-2, ffn=14336): route, permute, two grouped GEMMs, combine;
-  * the CPU oracle timed on a bounded sample of the same expert-share rows,
-    which also serves as a sampled parity check of those rows.
+  * every other step of the path on its own workload, each kernel timed with
+    HIP events on the launch stream and reported against its roofline
+    (TFLOP/s of valid rows vs the MFMA peak of its dtype, or GB/s of its
+    algorithmic bytes vs HBM):
+      - the same expert share in MXFP8 (quantise X, gate/up, quantise H, down);
+      - the Mixtral-shaped forward layer (route, permute, two GEMMs, combine),
+        as tokens/s;
+      - the fine-grained layer (T=16384, d=2048, 128 experts top-8, ffn=768)
+        forward and backward, as tokens/s;
+  * the CPU oracle timed on a bounded sample of the expert-share rows, which
+    also serves as a sampled parity check of those rows.
 """
 from __future__ import annotations
 
@@ -32,7 +39,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
-MXFP8_PEAK_TFLOPS = 5000.0
+MXFP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_swiglu_dsv3_share.json")
 GEMM_SOURCE = os.path.join(ROOT, "dropless_moe_expert_amd", "csrc", "gg_fwd.hip")
@@ -47,7 +54,7 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(flops_per_launch: float):
+def measured_traffic():
     """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
     try:
@@ -59,13 +66,188 @@ def measured_traffic(flops_per_launch: float):
     return t.get("hbm_bytes_per_launch")
 
 
+class Timer:
+    """Median HIP-event time of each named op, recorded on the stream the
+    library launches on (torch's current stream)."""
+
+    def __init__(self, torch, stream, reps: int):
+        self.torch, self.stream, self.reps = torch, stream, reps
+
+    def __call__(self, fn):
+        torch = self.torch
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.reps)]
+        for a, b in ev:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def flop_entry(ms: float, flops: float, peak: float) -> dict:
+    t = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(t, 2), "frac_of_mfma_peak": round(t / peak, 4)}
+
+
+def byte_entry(ms: float, nbytes: float) -> dict:
+    g = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "gbs": round(g, 1), "frac_of_hbm": round(g / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": int(nbytes)}
+
+
+def bench_mxfp8_share(torch, ops, L, dev, timer, flag) -> dict:
+    """The expert share in MXFP8: X and H quantised per 32 along K by
+    mxfp8_group_quantize, both GEMMs on MXFP8 operands (weights quantised and
+    packed once, outside the timed region)."""
+    M, d, f = L.M, L.d, L.f
+    x = L.x_perm.to(dev)
+    sizes = L.group_sizes.to(dev)
+    w1q, w1s = ops.quantize_weights(L.w1p.to(dev))
+    w2q, w2s = ops.quantize_weights(L.w2.to(dev))
+    w1k = ops.pack_weights_mxfp8(w1q, w1s, ops.MOE_EPI_SWIGLU)
+    w2k = ops.pack_weights_mxfp8(w2q, w2s)
+    del w1q, w1s, w2q, w2s
+    xq, xs = ops.mxfp8_quantize(x, 0, sizes, flag=flag)
+    h = ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU, flag=flag)
+    hq, hs = ops.mxfp8_quantize(h, 0, sizes, flag=flag)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    t_qx = timer(lambda: ops.mxfp8_quantize(x, 0, sizes, flag=flag))
+    t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h,
+                                                flag=flag))
+    t_qh = timer(lambda: ops.mxfp8_quantize(h, 0, sizes, flag=flag))
+    t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, w2k, None, sizes, out=y, flag=flag))
+    f1, f2 = 2.0 * M * 2 * f * d, 2.0 * M * d * f
+    step = t_qx + t_g1 + t_qh + t_g2
+    q = lambda R, C: R * C * 2 + R * C + R * C / 32   # read bf16, write codes and scales
+    return {
+        "workload": "deepseek-v3-shaped expert share in MXFP8 (same rows, sizes and weights; E4M3 + E8M0/32)",
+        "ms_per_step": round(step, 4),
+        "valid_row_tflops": round((f1 + f2) / (step * 1e-3) / 1e12, 2),
+        "frac_of_mxfp8_peak": round((f1 + f2) / (step * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
+        "kernels": {
+            "quantize_x": byte_entry(t_qx, q(M, d)),
+            "gate_up_swiglu_mxfp8": flop_entry(t_g1, f1, MXFP8_PEAK_TFLOPS),
+            "quantize_h": byte_entry(t_qh, q(M, f)),
+            "down_mxfp8": flop_entry(t_g2, f2, MXFP8_PEAK_TFLOPS),
+        },
+    }
+
+
+def routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep):
+    """Times route, permute, both GEMMs and combine of one routed layer."""
+    T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
+    M = T * K
+    ids, w = ops.route_topk(lg, K, flag=flag)
+    p = ops.permute(x, ids, E, flag=flag)
+    ws = None
+    t_route = timer(lambda: ops.route_topk(lg, K, flag=flag))
+    t_perm = timer(lambda: ops.permute(x, ids, E, flag=flag, workspace=ws))
+    if keep:
+        h, gu = ops.grouped_gemm(p["x_perm"], w1, p["group_sizes"], epilogue=ops.MOE_EPI_SWIGLU, keep_aux=True,
+                                 flag=flag)
+        t_g1 = timer(lambda: ops.grouped_gemm(p["x_perm"], w1, p["group_sizes"], epilogue=ops.MOE_EPI_SWIGLU,
+                                              out=h, aux=gu, keep_aux=True, flag=flag))
+    else:
+        h, gu = ops.grouped_gemm(p["x_perm"], w1, p["group_sizes"], epilogue=ops.MOE_EPI_SWIGLU, flag=flag), None
+        t_g1 = timer(lambda: ops.grouped_gemm(p["x_perm"], w1, p["group_sizes"], epilogue=ops.MOE_EPI_SWIGLU,
+                                              out=h, flag=flag))
+    y_perm = ops.grouped_gemm(h, w2, p["group_sizes"], flag=flag)
+    t_g2 = timer(lambda: ops.grouped_gemm(h, w2, p["group_sizes"], out=y_perm, flag=flag))
+    y = ops.unpermute_combine(y_perm, w, p["perm_dst"], T, K)
+    t_comb = timer(lambda: ops.unpermute_combine(y_perm, w, p["perm_dst"], T, K, out=y))
+    kern = {
+        "route": byte_entry(t_route, T * E * 4 + T * K * 8),
+        "permute": byte_entry(t_perm, T * d * 2 + T * K * 4 + M * d * 2 + M * 8),
+        "gate_up_swiglu": flop_entry(t_g1, 2.0 * M * 2 * f * d, BF16_PEAK_TFLOPS),
+        "down": flop_entry(t_g2, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
+        "combine": byte_entry(t_comb, M * d * 2 + M * 8 + T * d * 2),
+    }
+    saved = dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, **p)
+    return kern, t_route + t_perm + t_g1 + t_g2 + t_comb, saved
+
+
+def bench_mixtral(torch, ops, L, dev, timer, flag, steps) -> dict:
+    lg, x = L.logits.to(dev), L.x.to(dev)
+    w1 = ops.pack_weights(L.w1p.to(dev), ops.MOE_EPI_SWIGLU)
+    w2 = ops.pack_weights(L.w2.to(dev))
+    kern, ksum, _ = routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep=False)
+    # the whole layer back to back (host launch gaps included)
+    for _ in range(3):
+        ops.moe_forward(lg, x, w1, w2, L.K, flag=flag)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        ops.moe_forward(lg, x, w1, w2, L.K, flag=flag)
+    torch.cuda.synchronize()
+    lms = (time.perf_counter() - a) * 1e3 / steps
+    lflops = 2.0 * L.T * L.K * (2 * L.f * L.d + L.d * L.f)
+    return {"workload": "mixtral-shaped forward T=4096 d=4096 E=8 top-2 ffn=14336 bf16",
+            "tokens_per_s": round(L.T / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
+            "valid_row_tflops": round(lflops / (lms * 1e-3) / 1e12, 2),
+            "kernel_sum_ms": round(ksum, 4), "kernels": kern}
+
+
+def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
+    """Forward and backward of the fine-grained layer (weights unpacked: the
+    backward reads them as [K, N] too)."""
+    T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
+    M = T * K
+    lg, x, w1, w2, dy = (t.to(dev) for t in (L.logits, L.x, L.w1p, L.w2, L.dy))
+    kern, fsum, s = routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep=True)
+    sizes, dst = s["group_sizes"], s["perm_dst"]
+    dyp, dw = ops.combine_backward(dy, s["y_perm"], s["w"], dst, K)
+    t_cb = timer(lambda: ops.combine_backward(dy, s["y_perm"], s["w"], dst, K))
+    dh = ops.grouped_gemm(dyp, w2, sizes, b_layout=ops.MOE_B_KN, flag=flag)
+    t_dh = timer(lambda: ops.grouped_gemm(dyp, w2, sizes, b_layout=ops.MOE_B_KN, out=dh, flag=flag))
+    dw2 = ops.grouped_gemm_wgrad(dyp, s["h"], sizes, flag=flag)
+    t_dw2 = timer(lambda: ops.grouped_gemm_wgrad(dyp, s["h"], sizes, out=dw2, flag=flag))
+    dgu = ops.swiglu_backward(s["gu"], dh, sizes)
+    t_sb = timer(lambda: ops.swiglu_backward(s["gu"], dh, sizes, out=dgu))
+    dxp = ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, flag=flag)
+    t_dx = timer(lambda: ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, out=dxp, flag=flag))
+    dw1 = ops.grouped_gemm_wgrad(dgu, s["x_perm"], sizes, flag=flag)
+    t_dw1 = timer(lambda: ops.grouped_gemm_wgrad(dgu, s["x_perm"], sizes, out=dw1, flag=flag))
+    dx = ops.unpermute_combine(dxp, None, dst, T, K)
+    t_fold = timer(lambda: ops.unpermute_combine(dxp, None, dst, T, K, out=dx))
+    kern.update({
+        "combine_backward": byte_entry(t_cb, T * d * 2 + M * d * 2 * 2 + M * 8 + M * 4),
+        "dgrad_down": flop_entry(t_dh, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
+        "wgrad_down": flop_entry(t_dw2, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
+        "swiglu_backward": byte_entry(t_sb, M * 2 * f * 2 + M * f * 2 + M * 2 * f * 2),
+        "dgrad_gate_up": flop_entry(t_dx, 2.0 * M * 2 * f * d, BF16_PEAK_TFLOPS),
+        "wgrad_gate_up": flop_entry(t_dw1, 2.0 * M * 2 * f * d, BF16_PEAK_TFLOPS),
+        "fold_dx": byte_entry(t_fold, M * d * 2 + M * 4 + T * d * 2),
+    })
+    bsum = t_cb + t_dh + t_dw2 + t_sb + t_dx + t_dw1 + t_fold
+    # the whole forward + backward back to back
+    for _ in range(2):
+        y, sv = ops.moe_forward(lg, x, w1, w2, K, keep=True, flag=flag)
+        ops.moe_backward(dy, sv, w1, w2, K, flag=flag)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        y, sv = ops.moe_forward(lg, x, w1, w2, K, keep=True, flag=flag)
+        ops.moe_backward(dy, sv, w1, w2, K, flag=flag)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - a) * 1e3 / steps
+    fl = 3 * 2.0 * M * (2 * f * d + d * f)
+    return {"workload": "fine-grained forward+backward T=16384 d=2048 E=128 top-8 ffn=768 bf16, "
+                        "logit bias N(0,1.5) per expert",
+            "empty_experts": int((sizes == 0).sum().item()), "max_expert_rows": int(sizes.max().item()),
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "valid_row_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "forward_kernel_sum_ms": round(fsum, 4), "backward_kernel_sum_ms": round(bsum, 4), "kernels": kern}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-layer", action="store_true", help="skip the Mixtral-shaped layer tokens/s")
+    ap.add_argument("--no-layer", action="store_true", help="time only the headline expert share")
     ap.add_argument("--cpu-rows", type=int, default=2304, help="expert-share rows the oracle computes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling the HBM byte counters)")
@@ -101,6 +283,7 @@ def main() -> int:
     w2k = ops.pack_weights(w2)
     torch.cuda.synchronize()
     pack_ms = (time.perf_counter() - t0) * 1e3
+    del w1p, w2
     h = torch.empty((M, f), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -138,7 +321,6 @@ def main() -> int:
     log(f"expert share: {ms_per_step:.3f} ms/step, {tflops:.1f} TFLOP/s; gate/up {gg1_ms:.3f} ms "
         f"({gg1_tflops:.1f}), down {gg2_ms:.3f} ms ({gg2_tflops:.1f})")
 
-    traffic = measured_traffic(flops_gg1)
     roofline = {
         "kernel": "grouped_gemm gate/up + SwiGLU (dsv3 share)",
         "bound": "mfma",
@@ -146,38 +328,38 @@ def main() -> int:
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(gg1_tflops / BF16_PEAK_TFLOPS, 4),
-        "traffic": traffic,
+        "traffic": measured_traffic(),
         "algorithmic_flop_per_launch": flops_gg1,
         "avg_launch_ms": round(gg1_ms, 4),
     }
 
-    # ------------------------------------------------------------ MoE layer tokens/s (Mixtral-shaped)
-    layer = None
+    # ------------------------------------------------------------ the other workloads
+    workloads = {}
     if not args.no_layer:
-        del w1p, w2, w1k, w2k
+        timer = Timer(torch, stream, max(5, args.steps // 2))
+        del w1k, w2k
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        workloads["dsv3_mxfp8"] = bench_mxfp8_share(torch, ops, L, dev, timer, flag)
+        log(f"mxfp8 share: {workloads['dsv3_mxfp8']['ms_per_step']:.3f} ms/step "
+            f"({workloads['dsv3_mxfp8']['valid_row_tflops']} TFLOP/s) [{time.time() - t0:.1f}s]")
         torch.cuda.empty_cache()
         t0 = time.time()
         Lm = inputs.workload("mixtral")
-        log(f"layer inputs generated in {time.time() - t0:.1f}s")
-        lg, xm, w1m, w2m = (t.to(dev) for t in (Lm.logits, Lm.x, Lm.w1p, Lm.w2))
-        w1m, w2m = ops.pack_weights(w1m, ops.MOE_EPI_SWIGLU), ops.pack_weights(w2m)
-        for _ in range(max(2, args.warmup // 2)):
-            ops.moe_forward(lg, xm, w1m, w2m, Lm.K, flag=flag)
-        torch.cuda.synchronize()
-        nl = max(5, args.steps // 2)
-        a = time.perf_counter()
-        for _ in range(nl):
-            ops.moe_forward(lg, xm, w1m, w2m, Lm.K, flag=flag)
-        torch.cuda.synchronize()
-        lms = (time.perf_counter() - a) * 1e3 / nl
-        assert int(flag.item()) == 0
-        lflops = 2.0 * Lm.T * Lm.K * (2 * Lm.f * Lm.d + Lm.d * Lm.f)
-        layer = {"workload": "mixtral-shaped forward T=4096 d=4096 E=8 top-2 ffn=14336 bf16",
-                 "tokens_per_s": round(Lm.T / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
-                 "valid_row_tflops": round(lflops / (lms * 1e-3) / 1e12, 2)}
-        log(f"mixtral layer: {lms:.3f} ms, {layer['tokens_per_s']:.0f} tokens/s")
-        del lg, xm, w1m, w2m
+        workloads["mixtral"] = bench_mixtral(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
+        log(f"mixtral layer: {workloads['mixtral']['ms_per_step']:.3f} ms, "
+            f"{workloads['mixtral']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
+        del Lm
         torch.cuda.empty_cache()
+        t0 = time.time()
+        Lf = inputs.workload("finegrained")
+        workloads["finegrained"] = bench_finegrained(torch, ops, Lf, dev, timer, flag, max(5, args.steps // 5))
+        log(f"fine-grained fwd+bwd: {workloads['finegrained']['ms_per_step']:.3f} ms, "
+            f"{workloads['finegrained']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
+        del Lf
+        torch.cuda.empty_cache()
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0, "device error flag raised"
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
@@ -248,7 +430,8 @@ def main() -> int:
         "kernels_ms": {"gate_up_swiglu": round(gg1_ms, 4), "down": round(gg2_ms, 4)},
         "weights": f"packed once into the GEMM tile-stage layout before timing ({pack_ms:.1f} ms, both matrices)",
         "kernels_tflops": {"gate_up_swiglu": round(gg1_tflops, 2), "down": round(gg2_tflops, 2)},
-        "moe_layer": layer,
+        "moe_layer": workloads.get("mixtral"),
+        "workloads": workloads,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_sample": parity,
