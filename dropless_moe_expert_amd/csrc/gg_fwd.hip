@@ -49,6 +49,10 @@ constexpr int NWAVE = WM * WN, THREADS = NWAVE * 64;
 constexpr int WTM = BM / WM;                  // 64 x 128 per wavefront
 constexpr int TM = WTM / 16, TN = WTN / 16;   // 4 x 8 MFMA subtiles
 constexpr int LPW = (BM + BN) / 16 / NWAVE;   // direct loads per wavefront and stage (4)
+static_assert(KRows<NWAVE>::N == Rows<BN, NWAVE>::N, "a K-outer weight stage takes as many loads as a row stage");
+
+// weight (B) layouts of the kernel
+enum { BL_NK = 0, BL_PACKED = 1, BL_KN = 2 };
 
 // MFMA fragments of one stage: 8 W (n) and up to 4 X (m) 16x32 slices per lane
 struct Frags {
@@ -74,8 +78,8 @@ __device__ __forceinline__ void slot_rows(int rows, int wm, int& act, int& xrow0
 
 // reads the stage's W fragments and the wavefront's ACT X fragments (rows
 // xrow0 + [0, 16 * ACT)); ACT = 0: nothing
-template <int ACT>
-__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xrow0) {
+template <int ACT, int BL>
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xrow0, const uint32_t (&koff)[TN]) {
   if constexpr (ACT == 0) return;
   const int lane = threadIdx.x & 63;
   int wn, wm;
@@ -88,9 +92,14 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xr
 #pragma unroll
   for (int j = 0; j < ACT; ++j)
     fr.x[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lx + j * 16 * ROWB));
+  if constexpr (BL == BL_KN) {
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
-    fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+    for (int i = 0; i < TN; ++i) fr.w[i] = kfrag_read(buf, koff[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+      fr.w[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(lw + i * 16 * ROWB));
+  }
 }
 
 // MFMAs of the wavefront's ACT 16-row subtiles
@@ -154,11 +163,14 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
   }
 }
 
-// Packed weights: for expert g, n-tile nt and K-stage kt the 256 weight rows
-// of the tile (in the order the tile uses them) are one contiguous 16 KB
-// block at ((g * n_tiles + nt) * nk + kt) * 16 KB, already in the LDS slot
-// order, so each direct load reads 1 KB of consecutive bytes.
-template <int EPI, int OUT, bool PACKED>
+// Weight layouts (BL): BL_NK reads B [G, N, K] rows (K contiguous); BL_PACKED
+// reads the tile-stage blocks of moe_pack_weights: for expert g, n-tile nt
+// and K-stage kt the 256 weight rows of the tile (in the order the tile uses
+// them) are one contiguous 16 KB block at ((g * n_tiles + nt) * nk + kt) *
+// 16 KB, already in the LDS slot order, so each direct load reads 1 KB of
+// consecutive bytes; BL_KN reads B [G, K, N] (the data gradient's weight)
+// as K-outer stages, 32 rows of 256 columns, through LDS transpose reads.
+template <int EPI, int OUT, int BL>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   // five named 32 KB stage buffers (the whole 160 KB LDS): stage kt lives in
   // buffer kt % 5; loads run four stages ahead of the stage being read
@@ -190,6 +202,13 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   const int64_t total = m_tiles * a.n_tiles;
   const int64_t lda_b = (int64_t)a.K * 2;
   const int nk = a.K / 32;
+  uint32_t koff[TN];   // BL_KN: per-lane LDS offsets of the 8 weight fragments
+  {
+    int wn, wm;
+    wave_pos(wn, wm);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) koff[i] = BL == BL_KN ? kfrag_off(wn * WTN + 16 * i) : 0u;
+  }
 
   for (int64_t tile = wid; tile < total; tile += gridDim.x) {
     // tile order: blocks of GM m-tiles; inside a block m varies fastest
@@ -207,8 +226,10 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
 
     Rows<BM, NWAVE> xl;
     Rows<BN, NWAVE> wl;
+    KRows<NWAVE> kl;
     xl.init(lda_b, [&](int r) -> int64_t { return min(r, rows - 1); });
-    if (!PACKED) wl.init(lda_b, [&](int r) -> int64_t {
+    if constexpr (BL == BL_KN) kl.init((int64_t)a.N * 2, n0, a.N);
+    if constexpr (BL == BL_NK) wl.init(lda_b, [&](int r) -> int64_t {
       if constexpr (EPI == MOE_EPI_SWIGLU) {
         const int wn = r / WTN, q = r % WTN;
         const int jj = min(n0 + wn * (WTN / 2) + (q % (WTN / 2)), f - 1);
@@ -218,17 +239,23 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       }
     });
     const uint8_t* xbase = a.A + m0 * lda_b;
-    const uint8_t* wbase = PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * (BN * ROWB)
-                                  : a.B + (int64_t)g * nrows_b * lda_b;
-    const int wstride = PACKED ? BN * ROWB : ROWB;   // bytes from one stage's weight block to the next
-    if constexpr (PACKED) {
+    const uint8_t* wbase = BL == BL_PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * (BN * ROWB)
+                           : BL == BL_KN   ? a.B + (int64_t)g * a.K * a.N * 2
+                                           : a.B + (int64_t)g * nrows_b * lda_b;
+    // bytes from one stage's weight block to the next
+    const int wstride = BL == BL_PACKED ? BN * ROWB : BL == BL_KN ? 32 * a.N * 2 : ROWB;
+    if constexpr (BL == BL_PACKED) {
       const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
       for (int i = 0; i < Rows<BN, NWAVE>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
     }
 
     auto issue = [&](uint8_t* buf, int kt) {
-      wl.issue(buf, wbase + (int64_t)kt * wstride);
+      if constexpr (BL == BL_KN) {
+        kl.issue(buf, wbase + (int64_t)kt * wstride);
+      } else {
+        wl.issue(buf, wbase + (int64_t)kt * wstride);
+      }
       xl.issue(buf + XOFF, xbase + kt * ROWB);
     };
     // Waits until this wavefront's loads of stage s + 1 have landed (stages
@@ -272,7 +299,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       // the other way round; they skip the final barrier to even the count.
       auto iter = [&](uint8_t* sbuf, uint8_t* lbuf, int s) {
         if (s + 4 < nk) issue(lbuf, s + 4);
-        read_frags<ACT>(sbuf, fr, xrow0);
+        read_frags<ACT, BL>(sbuf, fr, xrow0, koff);
         sync(s);
         mma<ACT>(fr, acc);
         if (!(second && s == nk - 1)) sync(s);
@@ -371,8 +398,9 @@ moe_status_t launch_pack_weights(const uint16_t* w, int G, int N, int K, int epi
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-// bf16, ragged-M, B [G, N, K]: the forward kernels
-moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int packed, hipStream_t s) {
+// bf16, ragged-M: the forward kernels (B [G, N, K] rows or packed) and the
+// data gradient (B [G, K, N])
+moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout, hipStream_t s) {
   GGArgs b = a;
   const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
   const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
@@ -382,20 +410,28 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int packed, 
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
-  if (packed) {
-    if (epilogue == MOE_EPI_SWIGLU) {
-      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, true>), g, t, 0, s, b);
-    } else if (out_f32) {
-      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, true>), g, t, 0, s, b);
+  using namespace fwd;
+  if (b_layout == MOE_B_KN) {
+    if (epilogue == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+    if (out_f32) {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_KN>), g, t, 0, s, b);
     } else {
-      hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, true>), g, t, 0, s, b);
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_KN>), g, t, 0, s, b);
+    }
+  } else if (b_layout == MOE_B_PACKED) {
+    if (epilogue == MOE_EPI_SWIGLU) {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_PACKED>), g, t, 0, s, b);
+    } else if (out_f32) {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_PACKED>), g, t, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_PACKED>), g, t, 0, s, b);
     }
   } else if (epilogue == MOE_EPI_SWIGLU) {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, false>), g, t, 0, s, b);
+    hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_NK>), g, t, 0, s, b);
   } else if (out_f32) {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, false>), g, t, 0, s, b);
+    hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_NK>), g, t, 0, s, b);
   } else {
-    hipLaunchKernelGGL((fwd::gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, false>), g, t, 0, s, b);
+    hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_NK>), g, t, 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -67,6 +67,71 @@ struct Rows {
   }
 };
 
+// K-outer operands: element (k, n) at src[k * ld + n] (bf16), i.e. the
+// contraction runs down the rows (the data-gradient weight [K, N] and both
+// weight-gradient operands).  A stage holds 32 k-rows x 256 columns as
+// 512-byte LDS rows; 16-byte slot s of row k holds the 8 columns of chunk
+// s ^ kswz(k).  The swizzle gives the 8 rows that one half of a transpose
+// read touches (rows 8g + r and 8(g+1) + r, r < 4) distinct 32-byte bank
+// groups.  One direct load fills two rows (lane l: row l / 32, slot l % 32).
+constexpr int KROWB = 512;
+__device__ __forceinline__ int kswz(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+
+template <int NW>
+struct KRows {
+  static constexpr int N = 32 / 2 / NW;
+  uint32_t off[N];
+  // stage columns [n0, n0 + 256); chunks past the last column are clamped to
+  // it (their products land in output columns that are never stored)
+  __device__ __forceinline__ void init(int64_t ld_bytes, int n0, int ncols) {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = 2 * (i * NW + wave) + (lane >> 5);
+      const int c = (lane & 31) ^ kswz(k);
+      const int col = min(n0 + 8 * c, ncols - 8);
+      off[i] = (uint32_t)(k * ld_bytes + col * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* lds, const uint8_t* base) const {
+    const int wave = wave_id();
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(l0 + i * NW * 1024), "v"(off[i]), "s"(base)
+          : "memory", "m0");
+    }
+  }
+};
+
+// MFMA fragment (16 columns x 32 k) of a K-outer stage at tile column nb
+// (16 | nb): lane (g = l / 16, j = l % 16) receives k = 8g .. 8g + 7 of
+// column nb + j.  ds_read_b64_tr_b16 hands lane j of each 16-lane block
+// element (j % 4) of the 4-element rows addressed by lanes j / 4 + 4q,
+// q = 0..3 (measured on gfx950), so lane j addresses row 8g + j / 4 at
+// column nb + 4 (j % 4), and a second read covers rows + 4 (same swizzle).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_ptr;
+
+__device__ __forceinline__ uint32_t kfrag_off(int nb) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
+  const int k = 8 * g + (j >> 2);
+  const int n = nb + 4 * (j & 3);
+  return (uint32_t)(k * KROWB + (((n >> 3) ^ kswz(k)) << 4) + ((n >> 2) & 1) * 8);
+}
+
+__device__ __forceinline__ bf16x8_t kfrag_read(const uint8_t* buf, uint32_t off) {
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(buf + off));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(buf + off + 4 * KROWB));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Group of m-tile mt from the device group sizes, one wavefront scan over
 // chunks of 64 groups (sizes clamped to >= 0 and the rows to m_cap, as the
 // other kernels do).  Returns g, the group's first row and its first m-tile.

@@ -426,7 +426,7 @@ static moe_status_t launch(const GGArgs& a, hipStream_t s, int64_t max_tiles) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int packed, hipStream_t s);  // gg_fwd.hip
+moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout, hipStream_t s);  // gg_fwd.hip
 moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s);  // gg_fwd_mx.hip
 
 }  // namespace moe
@@ -457,10 +457,8 @@ extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A,
     const int64_t max_m_tiles = (d->m_cap + kBM - 1) / kBM + d->G;
     const int64_t max_tiles = max_m_tiles * a.n_tiles;
     if (d->dtype == MOE_DTYPE_MXFP8) return launch_fwd_mx(a, d->epilogue, d->b_layout == MOE_B_PACKED, s);
-    if (d->b_layout != MOE_B_KN)
-      return launch_fwd(a, d->epilogue, d->out_dtype == MOE_OUT_F32, d->b_layout == MOE_B_PACKED, s);
-    if (d->out_dtype == MOE_OUT_F32) return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_F32>(a, s, max_tiles);
-    return launch<MODE_M_KN, false, MOE_EPI_NONE, MOE_OUT_BF16>(a, s, max_tiles);
+    (void)max_tiles;
+    return launch_fwd(a, d->epilogue, d->out_dtype == MOE_OUT_F32, d->b_layout, s);
   }
   a.n_tiles = (d->N + kBN - 1) / kBN;
   a.p_tiles = (d->M + kBM - 1) / kBM;
