@@ -42,7 +42,7 @@ BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 MXFP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_swiglu_dsv3_share.json")
-GEMM_SOURCE = os.path.join(ROOT, "dropless_moe_expert_amd", "csrc", "gg_fwd.hip")
+GEMM_SOURCE = os.path.join(ROOT, "dropless_moe_expert_amd", "csrc", "gg_bf16.hip")
 
 
 def log(*a):

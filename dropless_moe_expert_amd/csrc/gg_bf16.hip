@@ -339,6 +339,155 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   }
 }
 
+// Weight gradient, ragged along the contraction: C[g] [P, Q] = sum over the
+// rows r of group g of A[r, p] * B[r, q] with A [m_cap, P], B [m_cap, Q]
+// (page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine", section "Optimization 1: Grouped GEMM": every expert's matmul in
+// one call, each over its true token count).  Both operands are K-outer
+// stages (32 rows of 256 columns, transpose reads) on the same ping-pong
+// schedule, in four 32 KB buffers (loads three stages ahead): the rest of LDS
+// holds each workgroup's copy of the group row offsets and of the group order,
+// largest group first, so the longest contractions start first.  A group's
+// last stage re-reads its last row into the missing rows and zeroes those
+// k-elements of the activation fragments.  Empty groups store zeros.
+constexpr int WG_STAGES = 4;
+
+template <int OUT>
+__global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
+  __shared__ __align__(1024) uint8_t b0[STAGE];
+  __shared__ __align__(1024) uint8_t b1[STAGE];
+  __shared__ __align__(1024) uint8_t b2[STAGE];
+  __shared__ __align__(1024) uint8_t b3[STAGE];
+  __shared__ GroupInfo<THREADS> gi;
+  build_groups<THREADS, BM, false>(a, gi);
+
+  const int P = a.M, Q = a.N;
+  const int per_group = a.p_tiles * a.n_tiles;
+  const int64_t total = (int64_t)a.G * per_group;
+  const int64_t lda = (int64_t)P * 2, ldb = (int64_t)Q * 2;
+  const int wid = worker_id();
+  const int lane = threadIdx.x & 63;
+  int wn, wm;
+  wave_pos(wn, wm);
+  uint32_t kw[TN], kx[TM];   // per-lane LDS offsets of the fragments
+#pragma unroll
+  for (int i = 0; i < TN; ++i) kw[i] = kfrag_off(wn * WTN + 16 * i);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) kx[j] = XOFF + kfrag_off(wm * WTM + 16 * j);
+  const bool second = wave_id() >= NWAVE / 2;
+
+  for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+    const int rank = (int)(tile / per_group), rem = (int)(tile - (int64_t)rank * per_group);
+    const int g = gi.tpre[rank];
+    const int pt = rem / a.n_tiles, qt = rem - pt * a.n_tiles;
+    const int p0 = pt * BM, q0 = qt * BN;
+    const int64_t r0 = gi.roff[g];
+    const int len = gi.roff[g + 1] - gi.roff[g];
+    const int nk = (len + 31) / 32;
+    const int rows = min(BM, P - p0);
+    int act, xrow0;
+    slot_rows(rows, wm, act, xrow0);
+
+    KRows<NWAVE> al, bl;
+    al.init(lda, p0, P);
+    bl.init(ldb, q0, Q);
+    const uint8_t* abase = a.A + r0 * lda;
+    const uint8_t* bbase = a.B + r0 * ldb;
+    auto issue = [&](uint8_t* buf, int kt) {
+      const int kv = len - 32 * kt;
+      if (kv >= 32) {
+        bl.issue(buf, bbase + (int64_t)kt * 32 * ldb);
+        al.issue(buf + XOFF, abase + (int64_t)kt * 32 * lda);
+      } else {
+        bl.issue_partial(buf, bbase + (int64_t)kt * 32 * ldb, kv, ldb);
+        al.issue_partial(buf + XOFF, abase + (int64_t)kt * 32 * lda, kv, lda);
+      }
+    };
+    auto sync = [&](int s) {
+      const int after = min(WG_STAGES - 2, nk - 2 - s);
+      __builtin_amdgcn_sched_barrier(0);
+      if (after >= 2) {
+        MOE_WAIT_VMCNT(2 * LPW);
+      } else if (after == 1) {
+        MOE_WAIT_VMCNT(LPW);
+      } else {
+        MOE_WAIT_VMCNT(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto run = [&](auto act_c) {
+      constexpr int ACT = decltype(act_c)::value;
+      f32x4_t acc[TN][TM];
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      Frags fr;
+      auto read = [&](const uint8_t* buf, int s) {
+        if constexpr (ACT > 0) {
+#pragma unroll
+          for (int i = 0; i < TN; ++i) fr.w[i] = kfrag_read(buf, kw[i]);
+#pragma unroll
+          for (int j = 0; j < ACT; ++j) fr.x[j] = kfrag_read(buf, kx[j]);
+          const int kv = len - 32 * s;
+          if (kv < 32) {
+            // k-elements past the group's rows: lane holds k = 8 (lane / 16) + e
+            const int k0 = 8 * (lane >> 4);
+#pragma unroll
+            for (int j = 0; j < ACT; ++j) {
+              s16x8_t v = __builtin_bit_cast(s16x8_t, fr.x[j]);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = (k0 + e < kv) ? v[e] : (short)0;
+              fr.x[j] = __builtin_bit_cast(bf16x8_t, v);
+            }
+          }
+        }
+      };
+      auto iter = [&](uint8_t* sbuf, uint8_t* lbuf, int s) {
+        if (s + WG_STAGES - 1 < nk) issue(lbuf, s + WG_STAGES - 1);
+        read(sbuf, s);
+        sync(s);
+        mma<ACT>(fr, acc);
+        if (!(second && s == nk - 1)) sync(s);
+      };
+      if (nk > 0) {
+        __syncthreads();  // every wavefront is done with the previous tile's buffers
+        issue(b0, 0);
+        if (nk > 1) issue(b1, 1);
+        if (nk > 2) issue(b2, 2);
+        sync(-1);
+        if (second) sync(-1);
+        int s = 0;
+        for (; s + 4 <= nk; s += 4) {
+          iter(b0, b3, s);
+          iter(b1, b0, s + 1);
+          iter(b2, b1, s + 2);
+          iter(b3, b2, s + 3);
+        }
+        if (s < nk) iter(b0, b3, s);
+        if (s + 1 < nk) iter(b1, b0, s + 1);
+        if (s + 2 < nk) iter(b2, b1, s + 2);
+      }
+      GGArgs ag = a;
+      ag.C = a.C + (int64_t)g * P * Q * (OUT == MOE_OUT_F32 ? 4 : 2);
+      store<MOE_EPI_NONE, OUT, ACT>(ag, acc, p0, rows, q0, Q, 0, xrow0);
+    };
+    if (act == 4) {
+      run(std::integral_constant<int, 4>());
+    } else if (act == 3) {
+      run(std::integral_constant<int, 3>());
+    } else if (act == 2) {
+      run(std::integral_constant<int, 2>());
+    } else if (act == 1) {
+      run(std::integral_constant<int, 1>());
+    } else {
+      run(std::integral_constant<int, 0>());
+    }
+  }
+}
+
 // Packs W [G, rows_b, K] (rows_b = N, or 2f for SwiGLU) into the tile-stage
 // blocks the PACKED kernel reads; rows past the weight's end are zero.
 template <int EPI>
@@ -432,6 +581,24 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
     hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_NK>), g, t, 0, s, b);
   } else {
     hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_NK>), g, t, 0, s, b);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// bf16, ragged-K: the weight gradients
+moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s) {
+  GGArgs b = a;
+  b.n_tiles = (a.N + fwd::BN - 1) / fwd::BN;
+  b.p_tiles = (a.M + fwd::BM - 1) / fwd::BM;
+  const int64_t max_tiles = (int64_t)a.G * b.n_tiles * b.p_tiles;
+  int64_t grid = moe_host::device_cu_count();
+  if (max_tiles < grid) grid = max_tiles;
+  if (grid <= 0) grid = 1;
+  const dim3 g((unsigned)grid), t(fwd::THREADS);
+  if (out_f32) {
+    hipLaunchKernelGGL((fwd::gg_wgrad_kernel<MOE_OUT_F32>), g, t, 0, s, b);
+  } else {
+    hipLaunchKernelGGL((fwd::gg_wgrad_kernel<MOE_OUT_BF16>), g, t, 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

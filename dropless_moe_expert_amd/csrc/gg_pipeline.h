@@ -107,6 +107,24 @@ struct KRows {
           : "memory", "m0");
     }
   }
+  // A stage with only kv < 32 valid rows: rows k >= kv re-read row kv - 1
+  // (ld_bytes = the row pitch given to init), so no load leaves the operand.
+  __device__ __forceinline__ void issue_partial(uint8_t* lds, const uint8_t* base, int kv, int64_t ld_bytes) const {
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int k = 2 * (i * NW + wave) + (lane >> 5);
+      const uint32_t o = off[i] - (uint32_t)((k - min(k, kv - 1)) * ld_bytes);
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(l0 + i * NW * 1024), "v"(o), "s"(base)
+          : "memory", "m0");
+    }
+  }
 };
 
 // MFMA fragment (16 columns x 32 k) of a K-outer stage at tile column nb
