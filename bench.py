@@ -20,6 +20,10 @@ Also reported in the same line:
         as tokens/s;
       - the fine-grained layer (T=16384, d=2048, 128 experts top-8, ffn=768)
         forward and backward, as tokens/s;
+  * measured ceilings: the GEMM inner loop's MFMA rate with random and with
+    constant operands (the library's measurement kernel, no memory traffic;
+    on random operands MI355X runs power-limited well below its nominal
+    peak) and the bandwidth of a plain 1 GiB device copy;
   * the CPU oracle timed on a bounded sample of the expert-share rows, which
     also serves as a sampled parity check of those rows.
 """
@@ -361,6 +365,30 @@ def main() -> int:
         torch.cuda.synchronize()
         assert int(flag.item()) == 0, "device error flag raised"
 
+    # ------------------------------------------------------------ measured ceilings
+    # the GEMM inner loop's MFMA rate with random and with constant operands
+    # (the library's measurement kernel, no global memory traffic), and a
+    # plain 1 GiB device copy for HBM
+    ctimer = Timer(torch, stream, 5)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ceil = {}
+    for name, rnd in (("mfma_bf16_random_operands_tflops", True), ("mfma_bf16_constant_operands_tflops", False)):
+        holder = {}
+
+        def run_ceiling():
+            holder["r"] = ops.bench_mfma_ceiling(rnd, 1000, 4 * cus, dev)
+
+        ms = ctimer(run_ceiling)
+        ceil[name] = round(holder["r"][1] / (ms * 1e-3) / 1e12, 1)
+    src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    ms = ctimer(lambda: dst.copy_(src))
+    ceil["hbm_copy_gbs"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del src, dst
+    roofline["measured_mfma_ceiling"] = ceil["mfma_bf16_random_operands_tflops"]
+    roofline["frac_of_measured_ceiling"] = round(gg1_tflops / ceil["mfma_bf16_random_operands_tflops"], 4)
+    log(f"ceilings: {ceil}")
+
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
@@ -433,6 +461,7 @@ def main() -> int:
         "moe_layer": workloads.get("mixtral"),
         "workloads": workloads,
         "roofline": roofline,
+        "measured_ceilings": ceil,
         "cpu_baseline": cpu,
         "parity_sample": parity,
     }

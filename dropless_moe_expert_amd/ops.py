@@ -34,6 +34,8 @@ EXPORTS = (
     "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine", "moe_combine_backward",
     "moe_swiglu_backward", "mxfp8_group_quantize", "moe_pack_weights_bytes", "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
+    # measurement only (include/moe_bench.h)
+    "moe_bench_mfma_flops", "moe_bench_mfma_ceiling",
 )
 
 
@@ -79,6 +81,8 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights_mxfp8": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, sz, P]),
+            "moe_bench_mfma_flops": (i64, [i64, i32]),
+            "moe_bench_mfma_ceiling": (ctypes.c_int, [i32, i32, P, i64, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -345,6 +349,17 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_sizes: Optional[torch.T
     _check(lib().mxfp8_group_quantize(_ptr(x), rows, cols, axis, _ptr(group_sizes), G, _ptr(q), _ptr(s), _ptr(flag),
                                       _stream(dev)), "mxfp8_group_quantize")
     return q, s
+
+
+# ------------------------------------------------------------------ measurement only
+
+def bench_mfma_ceiling(random_operands: bool, iters: int, blocks: int, device) -> Tuple[torch.Tensor, int]:
+    """Enqueues the MFMA ceiling kernel (include/moe_bench.h) on the current
+    stream; returns its sink tensor and the FLOPs of the call."""
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=device)
+    _check(lib().moe_bench_mfma_ceiling(int(bool(random_operands)), iters, _ptr(sink), blocks, _stream(sink.device)),
+           "moe_bench_mfma_ceiling")
+    return sink, int(lib().moe_bench_mfma_flops(blocks, iters))
 
 
 # ------------------------------------------------------------------ the layer
