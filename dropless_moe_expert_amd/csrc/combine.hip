@@ -13,13 +13,18 @@
 namespace moe {
 
 // y[t] = bf16(sum_k w[t,k] * y_perm[perm_dst[t*K+k]]), k ascending.
+// KT > 0: K known at compile time, so all KT row loads of a vector (and of
+// VB vectors) are issued before the first is used; KT = 0: any K <= 32.
+template <int KT, int VB>
 __global__ __launch_bounds__(256) void unpermute_combine_kernel(const uint16_t* __restrict__ y_perm,
                                                                 const float* __restrict__ w,
                                                                 const int32_t* __restrict__ perm_dst, int64_t T,
                                                                 int d, int K, uint16_t* __restrict__ y) {
+  constexpr int KM = KT > 0 ? KT : 32;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (KT > 0) K = KT;
   int32_t my_row = 0;
   float my_w = 1.f;
   if (lane < K) {
@@ -27,51 +32,78 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(const uint16_t* 
     if (w) my_w = w[t * K + lane];
   }
   // broadcast the K rows and weights while every lane is active
-  int32_t rows[32];
-  float ws[32];
+  int32_t rows[KM];
+  float ws[KM];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
+  for (int k = 0; k < KM; ++k) {
     rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
     ws[k] = (k < K) ? __shfl(my_w, k, 64) : 0.f;
   }
   const int nvec = d / 8;
-  for (int v = lane; v < nvec; v += 64) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (KT > 0) {
+    for (int v0 = lane; v0 < nvec; v0 += 64 * VB) {
+      uint4 in[VB][KT];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      if (k >= K) break;
-      const int32_t r = rows[k];
-      const float wk = ws[k];
-      float f[8];
-      unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d)[v], f);
+      for (int b = 0; b < VB; ++b) {
+        const int v = v0 + 64 * b;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wk, f[j], acc[j]);
+        for (int k = 0; k < KT; ++k)
+          in[b][k] = v < nvec ? reinterpret_cast<const uint4*>(y_perm + (int64_t)rows[k] * d)[v] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < VB; ++b) {
+        const int v = v0 + 64 * b;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+          float f[8];
+          unpack8(in[b][k], f);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[j] = fmaf(ws[k], f[j], acc[j]);
+        }
+        if (v < nvec) reinterpret_cast<uint4*>(y + t * d)[v] = pack8(acc);
+      }
     }
-    reinterpret_cast<uint4*>(y + t * d)[v] = pack8(acc);
+  } else {
+    for (int v = lane; v < nvec; v += 64) {
+      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        if (k >= K) break;
+        float f[8];
+        unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)rows[k] * d)[v], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(ws[k], f[j], acc[j]);
+      }
+      reinterpret_cast<uint4*>(y + t * d)[v] = pack8(acc);
+    }
   }
 }
 
 // dy_perm[perm_dst[t,k]] = bf16(w[t,k] * dy[t]);  dw[t,k] = <dy[t], y_perm[perm_dst[t,k]]>
+template <int KT>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* __restrict__ dy,
                                                                const uint16_t* __restrict__ y_perm,
                                                                const float* __restrict__ w,
                                                                const int32_t* __restrict__ perm_dst, int64_t T,
                                                                int d, int K, uint16_t* __restrict__ dy_perm,
                                                                float* __restrict__ dw) {
+  constexpr int KM = KT > 0 ? KT : 32;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (KT > 0) K = KT;
   int32_t my_row = 0;
   float my_w = 0.f;
   if (lane < K) {
     my_row = perm_dst[t * K + lane];
     my_w = w[t * K + lane];
   }
-  float dot[32];
-  int32_t rows[32];
-  float ws[32];
+  float dot[KM];
+  int32_t rows[KM];
+  float ws[KM];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
+  for (int k = 0; k < KM; ++k) {
     dot[k] = 0.f;
     rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
     ws[k] = (k < K) ? __shfl(my_w, k, 64) : 0.f;
@@ -80,29 +112,38 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* _
   for (int v = lane; v < nvec; v += 64) {
     float g[8];
     unpack8(reinterpret_cast<const uint4*>(dy + t * d)[v], g);
+    uint4 in[KM];
+    if constexpr (KT > 0) {
+      // every row load of this vector in flight before the first is used
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < KT; ++k) in[k] = reinterpret_cast<const uint4*>(y_perm + (int64_t)rows[k] * d)[v];
+    }
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
       if (k < K) {
         const int32_t r = rows[k];
-        const float wk = ws[k];
         float yv[8], o[8];
-        unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d)[v], yv);
-        float s = 0.f;
+        if constexpr (KT > 0) {
+          unpack8(in[k], yv);
+        } else {
+          unpack8(reinterpret_cast<const uint4*>(y_perm + (int64_t)r * d)[v], yv);
+        }
+        float sacc = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          s = fmaf(g[j], yv[j], s);
-          o[j] = wk * g[j];
+          sacc = fmaf(g[j], yv[j], sacc);
+          o[j] = ws[k] * g[j];
         }
-        dot[k] += s;
+        dot[k] += sacc;
         reinterpret_cast<uint4*>(dy_perm + (int64_t)r * d)[v] = pack8(o);
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
+  for (int k = 0; k < KM; ++k) {
     if (k < K) {
-      const float s = wave_sum(dot[k]);
-      if (lane == 0) dw[t * K + k] = s;
+      const float sum = wave_sum(dot[k]);
+      if (lane == 0) dw[t * K + k] = sum;
     }
   }
 }
@@ -150,8 +191,14 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const uint16_t* __
 extern "C" moe_status_t moe_unpermute_combine_launch(const uint16_t* y_perm, const float* w, const int32_t* perm_dst,
                                                      int64_t T, int32_t d, int32_t K, uint16_t* y, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  hipLaunchKernelGGL(moe::unpermute_combine_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, y_perm, w,
-                     perm_dst, T, d, K, y);
+  const dim3 g((unsigned)((T + 3) / 4)), b(256);
+  switch (K) {
+    case 1: hipLaunchKernelGGL((moe::unpermute_combine_kernel<1, 8>), g, b, 0, s, y_perm, w, perm_dst, T, d, K, y); break;
+    case 2: hipLaunchKernelGGL((moe::unpermute_combine_kernel<2, 4>), g, b, 0, s, y_perm, w, perm_dst, T, d, K, y); break;
+    case 4: hipLaunchKernelGGL((moe::unpermute_combine_kernel<4, 2>), g, b, 0, s, y_perm, w, perm_dst, T, d, K, y); break;
+    case 8: hipLaunchKernelGGL((moe::unpermute_combine_kernel<8, 2>), g, b, 0, s, y_perm, w, perm_dst, T, d, K, y); break;
+    default: hipLaunchKernelGGL((moe::unpermute_combine_kernel<0, 1>), g, b, 0, s, y_perm, w, perm_dst, T, d, K, y);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -159,8 +206,12 @@ extern "C" moe_status_t moe_combine_backward_launch(const uint16_t* dy, const ui
                                                     const int32_t* perm_dst, int64_t T, int32_t d, int32_t K,
                                                     uint16_t* dy_perm, float* dw, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  hipLaunchKernelGGL(moe::combine_backward_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, dy, y_perm, w,
-                     perm_dst, T, d, K, dy_perm, dw);
+  const dim3 g((unsigned)((T + 3) / 4)), b(256);
+  switch (K) {
+    case 2: hipLaunchKernelGGL((moe::combine_backward_kernel<2>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw); break;
+    case 8: hipLaunchKernelGGL((moe::combine_backward_kernel<8>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw); break;
+    default: hipLaunchKernelGGL((moe::combine_backward_kernel<0>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -11,18 +11,20 @@
 //               the chunk = running count + lanes below it with the same
 //               expert (found with 8 ballots over the id bits).  Writes the
 //               local rank of every pair and the chunk's per-expert counts.
-//   2. scan:    one workgroup: per expert, an exclusive scan over chunks; the
-//               totals are group_sizes; their exclusive scan is group_offsets;
-//               chunk bases become absolute row offsets.
+//   2. scan:    one workgroup: per expert, an exclusive scan over chunks
+//               (each expert's chunks split over 256 / E threads, loads
+//               batched); the totals are group_sizes; their exclusive scan is
+//               group_offsets; chunk bases become absolute row offsets.
 //   3. scatter: one wavefront per token: row r = base[chunk][e] + local rank
 //               for each of its K pairs; writes perm_dst / perm_src and copies
 //               the token's row once from HBM to its K destinations (16-byte
-//               vector loads and stores).
+//               vector loads and stores, all of a lane's loads of the row in
+//               flight before its stores when K is a compile-time value).
 #include "common.h"
 
 namespace moe {
 
-constexpr int kChunk = 1024;  // pairs per rank wavefront
+constexpr int kChunk = 256;  // pairs per rank wavefront
 
 __global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restrict__ ids, int64_t M, int E,
                                                           int32_t* __restrict__ local_rank,
@@ -65,38 +67,73 @@ __global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restr
 __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
                                                            int32_t* __restrict__ group_sizes,
                                                            int32_t* __restrict__ group_offsets) {
+  __shared__ int32_t part[256];
   __shared__ int32_t tot[256];
-  const int e = threadIdx.x;
-  int32_t run = 0;
-  if (e < E) {
-    for (int c = 0; c < nchunk; ++c) {
-      int32_t v = chunk_counts[(int64_t)c * E + e];
-      chunk_counts[(int64_t)c * E + e] = run;  // exclusive within the expert
-      run += v;
+  // thread (e, p): expert e = tid % E, part p = tid / E of P = 256 / E parts,
+  // each a contiguous range of chunks
+  const int tid = threadIdx.x;
+  const int P = 256 / E;
+  const int e = tid % E, p = tid / E;
+  const bool active = p < P;
+  const int per = (nchunk + P - 1) / P;
+  const int c0 = min(nchunk, p * per), c1 = min(nchunk, c0 + per);
+  constexpr int B = 8;   // loads in flight per thread
+  int32_t sum = 0;
+  if (active) {
+    for (int c = c0; c < c1; c += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) v[b] = (c + b < c1) ? chunk_counts[(int64_t)(c + b) * E + e] : 0;
+#pragma unroll
+      for (int b = 0; b < B; ++b) sum += v[b];
     }
   }
-  tot[e] = (e < E) ? run : 0;
+  part[tid] = active ? sum : 0;
   __syncthreads();
-  // exclusive scan over experts (E <= 256; a plain serial scan by one thread
-  // would do, a Hillis-Steele scan keeps it short)
-  int32_t incl = tot[e];
+  // exclusive prefix of this thread's part within its expert, and the expert total
+  int32_t before = 0, total = 0;
+  if (active) {
+    for (int q = 0; q < P; ++q) {
+      const int32_t v = part[q * E + e];
+      before += (q < p) ? v : 0;
+      total += v;
+    }
+  }
+  // exclusive scan over experts (E <= 256), Hillis-Steele in LDS
+  tot[tid] = (active && p == 0) ? total : 0;
+  __syncthreads();
+  int32_t incl = tot[tid];
   for (int o = 1; o < 256; o <<= 1) {
-    int32_t add = (e >= o) ? tot[e - o] : 0;
+    const int32_t add = (tid >= o) ? tot[tid - o] : 0;
     __syncthreads();
     incl += add;
-    tot[e] = incl;
+    tot[tid] = incl;
     __syncthreads();
   }
-  const int32_t excl = incl - run;
-  if (e < E) {
-    group_sizes[e] = run;
-    group_offsets[e] = excl;
-    for (int c = 0; c < nchunk; ++c) chunk_counts[(int64_t)c * E + e] += excl;
+  // tot[e] is now the inclusive prefix of the totals (threads e < E hold p == 0)
+  if (active) {
+    const int32_t goff = tot[e] - total;
+    if (p == 0) {
+      group_sizes[e] = total;
+      group_offsets[e] = goff;
+      if (e == E - 1) group_offsets[E] = tot[e];
+    }
+    int32_t run = goff + before;
+    for (int c = c0; c < c1; c += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) v[b] = (c + b < c1) ? chunk_counts[(int64_t)(c + b) * E + e] : 0;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        if (c + b < c1) chunk_counts[(int64_t)(c + b) * E + e] = run;   // absolute base of the chunk
+        run += v[b];
+      }
+    }
   }
-  if (e == E - 1) group_offsets[E] = incl;
 }
 
 // one wavefront per token
+template <int KT>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* __restrict__ ids,
                                                               const int32_t* __restrict__ local_rank,
@@ -104,9 +141,11 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __
                                                               int d, int E, int K, int32_t* __restrict__ perm_src,
                                                               int32_t* __restrict__ perm_dst,
                                                               uint16_t* __restrict__ x_perm) {
+  constexpr int KM = KT > 0 ? KT : 32;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (KT > 0) K = KT;
   // lane k < K resolves pair k
   int32_t my_row = 0;
   if (lane < K) {
@@ -119,16 +158,25 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __
   }
   if (x == nullptr) return;
   // broadcast the K destination rows while every lane is active
-  int32_t rows[32];
+  int32_t rows[KM];
 #pragma unroll
-  for (int k = 0; k < 32; ++k) rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
+  for (int k = 0; k < KM; ++k) rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
   const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
   const int nvec = d / 8;
-  for (int v = lane; v < nvec; v += 64) {
-    const uint4 val = src[v];
+  constexpr int VB = 4;   // vectors of the row a lane loads before storing them
+  for (int v0 = lane; v0 < nvec; v0 += 64 * VB) {
+    uint4 val[VB];
 #pragma unroll
-    for (int k = 0; k < 32; ++k)
-      if (k < K) reinterpret_cast<uint4*>(x_perm + (int64_t)rows[k] * d)[v] = val;
+    for (int b = 0; b < VB; ++b) val[b] = (v0 + 64 * b < nvec) ? src[v0 + 64 * b] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int b = 0; b < VB; ++b) {
+      const int v = v0 + 64 * b;
+      if (v < nvec) {
+#pragma unroll
+        for (int k = 0; k < KM; ++k)
+          if (k < K) reinterpret_cast<uint4*>(x_perm + (int64_t)rows[k] * d)[v] = val[b];
+      }
+    }
   }
 }
 
@@ -159,8 +207,19 @@ extern "C" moe_status_t moe_permute_launch(const uint16_t* x, const int32_t* ids
   hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
                      group_offsets);
   if (T > 0) {
-    hipLaunchKernelGGL(moe::permute_scatter_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x, ids,
-                       local_rank, chunk_counts, T, d, E, K, perm_src, perm_dst, x_perm);
+    const dim3 g((unsigned)((T + 3) / 4)), b(256);
+    switch (K) {
+      case 1: hipLaunchKernelGGL((moe::permute_scatter_kernel<1>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
+                                 E, K, perm_src, perm_dst, x_perm); break;
+      case 2: hipLaunchKernelGGL((moe::permute_scatter_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
+                                 E, K, perm_src, perm_dst, x_perm); break;
+      case 4: hipLaunchKernelGGL((moe::permute_scatter_kernel<4>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
+                                 E, K, perm_src, perm_dst, x_perm); break;
+      case 8: hipLaunchKernelGGL((moe::permute_scatter_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
+                                 E, K, perm_src, perm_dst, x_perm); break;
+      default: hipLaunchKernelGGL((moe::permute_scatter_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
+                                  d, E, K, perm_src, perm_dst, x_perm);
+    }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
