@@ -120,16 +120,22 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   if (d->G < 1 || d->G > 1024 || d->N < 1 || d->m_cap < 0) return MOE_ERR_INVALID_ARG;
   if (d->m_cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (!A || !B || !C || !group_sizes) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_aux && !aligned16(C_aux))) return MOE_ERR_ALIGNMENT;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MOE_ERR_ALIGNMENT;
+  if (C_aux && d->epilogue != MOE_EPI_SWIGLU_MXFP8 && !aligned16(C_aux)) return MOE_ERR_ALIGNMENT;
   if (d->dtype != MOE_DTYPE_BF16 && d->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
   if (d->out_dtype != MOE_OUT_BF16 && d->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
-  if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU && d->epilogue != MOE_EPI_SWIGLU_MXFP8)
+    return MOE_ERR_UNSUPPORTED;
   if (d->N % 8) return MOE_ERR_UNSUPPORTED;
   if (d->ragged == MOE_RAGGED_M) {
     if (d->K < 1) return MOE_ERR_INVALID_ARG;
     if (d->b_layout != MOE_B_NK && d->b_layout != MOE_B_KN && d->b_layout != MOE_B_PACKED) return MOE_ERR_UNSUPPORTED;
     if (d->epilogue == MOE_EPI_SWIGLU) {
       if (d->b_layout == MOE_B_KN || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
+    } else if (d->epilogue == MOE_EPI_SWIGLU_MXFP8) {
+      // codes to C, scales to C_aux (1-byte elements: 4-byte aligned rows of codes)
+      if (d->dtype != MOE_DTYPE_MXFP8 || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 32) return MOE_ERR_UNSUPPORTED;
+      if (!C_aux) return MOE_ERR_INVALID_ARG;
     } else if (C_aux) {
       return MOE_ERR_INVALID_ARG;
     }

@@ -65,6 +65,42 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// ---------------------------------------------------------------- MXFP8 rounding
+// Shared by the quantisation kernels and the GEMM epilogue that quantises its
+// output, so both apply the same rule bit for bit.  Scale rule (OCP MX v1.0):
+// e = floor(log2 amax) - 8 (8 = largest E4M3 exponent) clamped to
+// [-127, 127], byte = e + 127; codes are the E4M3FN round-to-nearest-even of
+// v * 2^-e clamped to +-448.  v * 2^-e is exact in fp32 for bf16 inputs;
+// v_cvt_pk_fp8_f32 rounds to nearest even and keeps the sign of zero.
+// floor(log2(amax)) - 8 from the fp32 bits of a bf16 amax; clamped
+__device__ __forceinline__ int mx_exponent(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;  // zero or subnormal amax: floor(log2) <= -127
+  return max(-127, min(127, ef - 127 - 8));
+}
+
+__device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+  return (uint32_t)hi;
+}
+
+// multiply by 2^-e with e in [-127, 127]: 2^127 is one step outside the
+// normal-exponent helper, so scale in two exact steps
+__device__ __forceinline__ float scale_pow2(float v, int e) {
+  const int ne = -e;  // in [-127, 127]
+  if (ne >= -126) return v * pow2i(ne);
+  return (v * pow2i(-63)) * pow2i(-64);
+}
+
 // silu(g) = g * sigmoid(g); hardware exp and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 

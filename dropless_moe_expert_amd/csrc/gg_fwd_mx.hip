@@ -125,12 +125,73 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x16_t (&acc)[MTN][MTM]) 
 // 32x32 accumulator: element v of lane (r32, g) is n = 8*(v/4) + 4*g + v%4,
 // m = r32 within the subtile.  SwiGLU: subtiles i < MTN/2 hold gate columns,
 // i + MTN/2 the up columns of the same j.
+// SwiGLU epilogues: EPI_SWIGLU stores h = bf16(silu(g) * u); EPI_SWIGLU_MXFP8
+// quantises that bf16 h per 32 columns as mxfp8_group_quantize (axis 0) does,
+// storing E4M3 codes to C and E8M0 scales to C_aux.  A 32-column block of a
+// row lies in lanes (r32, 0) and (r32, 1) of one subtile, 16 values each, so
+// its amax takes one exchange across the lane halves.  The quantised tile
+// (256 rows x 128 codes, 256 x 4 scales) is assembled in LDS (the stage
+// buffers, free once every wavefront has left the K loop) and written out by
+// the whole workgroup as 16-byte row pieces and 4-byte scale words.
 template <int EPI>
 __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM], int64_t m0, int rows, int n0,
-                                      int ncols, int f) {
+                                      int ncols, int f, uint8_t* lds_codes, uint8_t* lds_scales) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r32 = lane & 31, g = lane >> 5;
+  if constexpr (EPI == MOE_EPI_SWIGLU_MXFP8) {
+    constexpr int TC = BN / 2;   // codes per tile row
+    __syncthreads();             // every wavefront has read its last stage
+#pragma unroll
+    for (int j = 0; j < MTM; ++j) {
+      const int mr = wm * WTM + j * 32 + r32;
+#pragma unroll
+      for (int i = 0; i < MTN / 2; ++i) {
+        // h of this lane's 16 columns, rounded to bf16 exactly as the bf16 store does
+        float h[16];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t p = pack_bf16x2(silu_f32(acc[i][j][2 * q]) * acc[i + MTN / 2][j][2 * q],
+                                         silu_f32(acc[i][j][2 * q + 1]) * acc[i + MTN / 2][j][2 * q + 1]);
+          h[2 * q] = bf16_bits_to_f32(p & 0xFFFFu);
+          h[2 * q + 1] = bf16_bits_to_f32(p >> 16);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(h[v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int e = mx_exponent(amax);
+        const int cb = wn * (WTN / 2) + i * 32;   // the block's first column in the tile
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t codes = cvt4_e4m3(scale_pow2(h[4 * q], e), scale_pow2(h[4 * q + 1], e),
+                                           scale_pow2(h[4 * q + 2], e), scale_pow2(h[4 * q + 3], e));
+          *reinterpret_cast<uint32_t*>(lds_codes + mr * TC + cb + q * 8 + g * 4) = codes;
+        }
+        if (g == 0) lds_scales[mr * (TC / 32) + cb / 32] = (uint8_t)(e + 127);
+      }
+    }
+    __syncthreads();
+    // rows < rows, columns n0 + [0, 128) < f (f % 32 == 0: whole blocks)
+    const int ncb = min(TC, f - n0);   // valid codes in a tile row (multiple of 32)
+    for (int c = threadIdx.x; c < BM * (TC / 16); c += THREADS) {
+      const int row = c / (TC / 16), piece = c % (TC / 16);
+      if (row < rows && piece * 16 < ncb)
+        *reinterpret_cast<uint4*>(a.C + (m0 + row) * (int64_t)f + n0 + piece * 16) =
+            *reinterpret_cast<const uint4*>(lds_codes + row * TC + piece * 16);
+    }
+    const int64_t lds_row = f / 32;   // scale bytes per row
+    for (int row = threadIdx.x; row < rows; row += THREADS) {
+      uint8_t* dst = a.Caux + (m0 + row) * lds_row + n0 / 32;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(lds_scales + row * (TC / 32));
+      if (ncb == TC && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = w;
+      } else {
+        for (int b = 0; b < ncb / 32; ++b) dst[b] = (uint8_t)(w >> (8 * b));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < MTM; ++j) {
     const int mr = wm * WTM + j * 32 + r32;
@@ -200,12 +261,13 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     const int g = tg.g;
     const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
     const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
-    const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
-    const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
+    constexpr bool SWI = EPI != MOE_EPI_NONE;   // either SwiGLU epilogue: gate/up tile geometry
+    const int n0 = SWI ? nt * (BN / 2) : nt * BN;
+    const int nrows_b = SWI ? 2 * f : a.N;
 
     auto xrow = [&](int r) -> int64_t { return min(r, rows - 1); };
     auto wrow = [&](int r) -> int64_t {
-      if constexpr (EPI == MOE_EPI_SWIGLU) {
+      if constexpr (SWI) {
         const int wn = r / WTN, q = r % WTN;
         const int jj = min(n0 + wn * (WTN / 2) + (q % (WTN / 2)), f - 1);
         return q < WTN / 2 ? jj : f + jj;
@@ -299,7 +361,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     if (kt + 3 < nk) step(b3, b2, kt + 3);
     if (kt + 4 < nk) step(b0, b3, kt + 4);
     if (kt + 5 < nk) step(b1, b0, kt + 5);
-    store<EPI>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f);
+    store<EPI>(a, acc, m0, rows, n0, SWI ? f : a.N, f, b0, b1);
   }
 }
 
@@ -387,24 +449,30 @@ moe_status_t launch_pack_mx_weights(const uint8_t* q, const uint8_t* sc, int G, 
 
 moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s) {
   GGArgs b = a;
-  const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
-  const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
+  const bool swi = epilogue != MOE_EPI_NONE;
+  const int ncols = swi ? a.N / 2 : a.N;
+  const int bn = swi ? fwd::BN / 2 : fwd::BN;
   b.n_tiles = (ncols + bn - 1) / bn;
   const int64_t max_tiles = ((a.m_cap + fwd::BM - 1) / fwd::BM + a.G) * b.n_tiles;
   int64_t grid = moe_host::device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
+  using namespace fwd::mx;
   if (packed) {
-    if (epilogue == MOE_EPI_SWIGLU) {
-      hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU, true>), g, t, 0, s, b);
+    if (epilogue == MOE_EPI_SWIGLU_MXFP8) {
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU_MXFP8, true>), g, t, 0, s, b);
+    } else if (epilogue == MOE_EPI_SWIGLU) {
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU, true>), g, t, 0, s, b);
     } else {
-      hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE, true>), g, t, 0, s, b);
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_NONE, true>), g, t, 0, s, b);
     }
+  } else if (epilogue == MOE_EPI_SWIGLU_MXFP8) {
+    hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU_MXFP8, false>), g, t, 0, s, b);
   } else if (epilogue == MOE_EPI_SWIGLU) {
-    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_SWIGLU, false>), g, t, 0, s, b);
+    hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU, false>), g, t, 0, s, b);
   } else {
-    hipLaunchKernelGGL((fwd::mx::gg_fwd_mx_kernel<MOE_EPI_NONE, false>), g, t, 0, s, b);
+    hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_NONE, false>), g, t, 0, s, b);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -18,35 +18,6 @@
 
 namespace moe {
 
-// floor(log2(amax)) - 8 from the fp32 bits of a bf16 amax; clamped
-__device__ __forceinline__ int mx_exponent(float amax) {
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  if (ef == 0) return -127;  // zero or subnormal amax: floor(log2) <= -127
-  return max(-127, min(127, ef - 127 - 8));
-}
-
-__device__ __forceinline__ float pow2i(int e) {  // 2^e for e in [-126, 127]
-  return __uint_as_float((uint32_t)(e + 127) << 23);
-}
-
-__device__ __forceinline__ uint32_t cvt4_e4m3(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -448.f), 448.f);
-  b = fminf(fmaxf(b, -448.f), 448.f);
-  c = fminf(fmaxf(c, -448.f), 448.f);
-  d = fminf(fmaxf(d, -448.f), 448.f);
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-  return (uint32_t)hi;
-}
-
-// multiply by 2^-e with e in [-127, 127]: 2^127 is one step outside the
-// normal-exponent helper, so scale in two exact steps
-__device__ __forceinline__ float scale_pow2(float v, int e) {
-  const int ne = -e;  // in [-127, 127]
-  if (ne >= -126) return v * pow2i(ne);
-  return (v * pow2i(-63)) * pow2i(-64);
-}
-
 // axis 0: 4 lanes per block of 32 (8 values each); rows < rows_valid
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
                                                             const int32_t* __restrict__ group_sizes, int G,

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
 MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1
 MOE_RAGGED_M, MOE_RAGGED_K = 0, 1
 MOE_B_NK, MOE_B_KN, MOE_B_PACKED = 0, 1, 2
-MOE_EPI_NONE, MOE_EPI_SWIGLU = 0, 1
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_MXFP8 = 0, 1, 2
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 
 FLAG_BAD_EXPERT_ID = 0x1
@@ -275,14 +275,20 @@ def grouped_gemm_wgrad(X: torch.Tensor, Y: torch.Tensor, group_sizes: torch.Tens
 
 def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torch.Tensor],
                        group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
-                       out: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None):
+                       out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
+                       flag: Optional[torch.Tensor] = None):
     """MXFP8 ragged-M grouped GEMM.  Aq uint8 [m_cap, K], As uint8 [m_cap, K/32],
     Bq uint8 [G, N, K] with Bs uint8 [G, N, K/32], or Bq = PackedWeights from
-    pack_weights_mxfp8 (Bs None) -> bf16 [m_cap, N] (or N/2 with SwiGLU)."""
+    pack_weights_mxfp8 (Bs None) -> bf16 [m_cap, N] (or N/2 with SwiGLU).
+    With MOE_EPI_SWIGLU_MXFP8 (weights packed for MOE_EPI_SWIGLU, or
+    unpacked) -> (codes uint8 [m_cap, N/2], scales uint8 [m_cap, N/64]): the
+    SwiGLU output quantised as mxfp8_quantize(h, 0) would."""
     packed = isinstance(Bq, PackedWeights)
     m_cap, Kd = Aq.shape
+    fused = epilogue == MOE_EPI_SWIGLU_MXFP8
     if packed:
-        if not Bq.mxfp8 or Bq.epilogue != epilogue or Bq.K != Kd:
+        want = MOE_EPI_SWIGLU if fused else epilogue
+        if not Bq.mxfp8 or Bq.epilogue != want or Bq.K != Kd:
             raise MoeError("packed weights used with another dtype, epilogue or K than they were packed for")
         dev = _dev(Aq, As, Bq.data, group_sizes)
         Bt, layout = Bq.data, MOE_B_PACKED
@@ -290,14 +296,19 @@ def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torc
         dev = _dev(Aq, As, Bq, Bs, group_sizes)
         Bt, layout = Bq, MOE_B_NK
     G, N = Bq.shape[0], Bq.shape[1]
-    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
-    if out is None:
+    ncols = N // 2 if epilogue != MOE_EPI_NONE else N
+    if fused:
+        if out is None:
+            out = torch.empty((m_cap, ncols), dtype=torch.uint8, device=dev)
+        if out_scale is None:
+            out_scale = torch.empty((m_cap, ncols // 32), dtype=torch.uint8, device=dev)
+    elif out is None:
         out = torch.empty((m_cap, ncols), dtype=torch.bfloat16, device=dev)
     d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, layout, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
     _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bt), None if packed else _ptr(Bs),
-                              _ptr(group_sizes), _ptr(out), None, None, 0, _ptr(flag), _stream(dev)),
-           "grouped_gemm (mxfp8)")
-    return out
+                              _ptr(group_sizes), _ptr(out), _ptr(out_scale) if fused else None, None, 0, _ptr(flag),
+                              _stream(dev)), "grouped_gemm (mxfp8)")
+    return (out, out_scale) if fused else out
 
 
 def unpermute_combine(y_perm: torch.Tensor, topk_w: Optional[torch.Tensor], perm_dst: torch.Tensor, T: int, K: int,
@@ -407,13 +418,18 @@ def expert_mlp(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1p: torch.Tenso
 
 
 def expert_mlp_mxfp8(x_perm: torch.Tensor, group_sizes: torch.Tensor, w1q, w1s, w2q, w2s,
-                     flag: Optional[torch.Tensor] = None):
+                     flag: Optional[torch.Tensor] = None, fused: bool = False):
     """MXFP8 expert share: quantise X, GEMM + SwiGLU, quantise H, GEMM.  Weights
     come pre-quantised ([G, N, K] codes with [G, N, K/32] scales), or packed
-    (PackedWeights from pack_weights_mxfp8, with w1s = w2s = None)."""
+    (PackedWeights from pack_weights_mxfp8, with w1s = w2s = None).  fused:
+    the gate/up GEMM quantises H in its epilogue (no bf16 H)."""
     xq, xs = mxfp8_quantize(x_perm, 0, group_sizes, flag=flag)
-    h = grouped_gemm_mxfp8(xq, xs, w1q, w1s, group_sizes, epilogue=MOE_EPI_SWIGLU, flag=flag)
-    hq, hs = mxfp8_quantize(h, 0, group_sizes, flag=flag)
+    if fused:
+        hq, hs = grouped_gemm_mxfp8(xq, xs, w1q, w1s, group_sizes, epilogue=MOE_EPI_SWIGLU_MXFP8, flag=flag)
+        h = None
+    else:
+        h = grouped_gemm_mxfp8(xq, xs, w1q, w1s, group_sizes, epilogue=MOE_EPI_SWIGLU, flag=flag)
+        hq, hs = mxfp8_quantize(h, 0, group_sizes, flag=flag)
     y = grouped_gemm_mxfp8(hq, hs, w2q, w2s, group_sizes, flag=flag)
     return y, dict(xq=xq, xs=xs, h=h, hq=hq, hs=hs)
 

@@ -132,6 +132,13 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
  *   code * 2^(scale - 127)); accumulation fp32, output bf16.  With
  *   B_PACKED, B comes from moe_pack_weights_mxfp8 (codes and scales
  *   together) and B_scale is ignored.
+ *   epilogue MOE_EPI_SWIGLU_MXFP8 (MXFP8 only; the page's planned
+ *   quantisation fused with the GEMM, section "Optimization 1"): as
+ *   MOE_EPI_SWIGLU, and the bf16 h is then quantised exactly as
+ *   mxfp8_group_quantize (axis 0) would quantise it: C receives the E4M3
+ *   codes uint8 [m_cap, f], C_aux (required) the E8M0 scales uint8
+ *   [m_cap, f/32]; f % 32 == 0; packed weights are those packed for
+ *   MOE_EPI_SWIGLU.  Rows r >= sum(s_g) are not written.
  * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
  * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
  *   MXFP8: K % 128 == 0.  A, B, C 16-byte aligned.
@@ -145,6 +152,7 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
 #define MOE_B_PACKED 2
 #define MOE_EPI_NONE 0
 #define MOE_EPI_SWIGLU 1
+#define MOE_EPI_SWIGLU_MXFP8 2
 #define MOE_OUT_BF16 0
 #define MOE_OUT_F32 1
 

@@ -77,6 +77,13 @@ def test_host_checkable_errors_return_status():
     assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == INVALID
     d.dtype, d.epilogue, d.b_layout = 0, 1, 1  # SwiGLU needs the NK layout
     assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    d.epilogue, d.b_layout = 2, 0  # the quantising SwiGLU epilogue is MXFP8 only
+    assert L.grouped_gemm(bd, fake, None, fake, None, fake, fake, fake, None, 0, None, None) == UNSUPPORTED
+    d.dtype, d.N = 1, 64           # ... needs the scale output in C_aux
+    assert L.grouped_gemm(bd, fake, fake, fake, fake, fake, fake, None, None, 0, None, None) == INVALID
+    d.N = 96                       # ... and f % 32 == 0
+    assert L.grouped_gemm(bd, fake, fake, fake, fake, fake, fake, fake, None, 0, None, None) == UNSUPPORTED
+    d.dtype, d.N, d.K = 0, 64, 64
     d.epilogue, d.b_layout = 0, 0
     assert L.grouped_gemm(bd, ctypes.c_void_p((1 << 20) + 8), None, fake, None, fake, fake, None, None, 0, None,
                           None) == ALIGN

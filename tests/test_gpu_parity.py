@@ -264,6 +264,36 @@ def test_grouped_gemm_mxfp8(ops, swiglu):
     assert torch.equal(out_p[:M], out[:M])
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_grouped_gemm_mxfp8_fused_quant(ops, packed):
+    """SwiGLU + MXFP8 quantisation in the gate/up GEMM's epilogue: codes and
+    scales equal quantising the unfused bf16 h, bit for bit (several tiles,
+    ragged tails, empty groups); against the oracle within the MXFP8 bound."""
+    sizes = np.array([300, 0, 1, 517, 0, 33], np.int32)
+    say("gg mxfp8 fused quant", packed)
+    rng = np.random.default_rng(23 + packed)
+    G, M, f, Kd = sizes.size, int(sizes.sum()), 320, 256
+    A, B = bf16(rng, M, Kd), bf16(rng, G, 2 * f, Kd, scale=Kd ** -0.5)
+    aq, as_ = orc.mxfp8_quantize(A, 0)
+    bq, bs = orc.mxfp8_quantize(orc.u16(B).reshape(-1, Kd), 0)
+    bq, bs = bq.reshape(G, 2 * f, Kd), bs.reshape(G, 2 * f, Kd // 32)
+    t = lambda a: dev(torch.from_numpy(np.ascontiguousarray(a)))
+    W = ops.pack_weights_mxfp8(t(bq), t(bs), ops.MOE_EPI_SWIGLU) if packed else t(bq)
+    Ws = None if packed else t(bs)
+    h = ops.grouped_gemm_mxfp8(t(aq), t(as_), W, Ws, t(sizes), epilogue=ops.MOE_EPI_SWIGLU)
+    hq, hs = ops.mxfp8_quantize(h, 0, t(sizes))
+    fq, fs = ops.grouped_gemm_mxfp8(t(aq), t(as_), W, Ws, t(sizes), epilogue=ops.MOE_EPI_SWIGLU_MXFP8)
+    torch.cuda.synchronize()
+    assert torch.equal(fq[:M], hq[:M]) and torch.equal(fs[:M], hs[:M])
+    # oracle: its own h, quantised by its own rule; compare dequantised values
+    h_ref = orc.mx_grouped_gemm(aq, as_, bq, bs, sizes, swiglu=True)
+    q_ref, s_ref = orc.mxfp8_quantize(h_ref, 0)
+    deq = lambda q, sc: orc.e4m3_to_f64(q) * np.exp2(np.repeat(sc.astype(np.float64) - 127, 32, axis=1))
+    got = deq(fq[:M].cpu().numpy(), fs[:M].cpu().numpy())
+    ref = deq(q_ref, s_ref)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= MX_TOL
+
+
 @pytest.mark.parametrize("N,Kd", [(8, 128), (264, 256)])
 def test_grouped_gemm_mxfp8_packed_narrow(ops, N, Kd):
     """Packed MXFP8 weights with a partial last n-tile (padding rows are zero)."""
