@@ -53,6 +53,10 @@ static_assert(KRows<NWAVE>::N == Rows<BN, NWAVE>::N, "a K-outer weight stage tak
 
 // weight (B) layouts of the kernel
 enum { BL_NK = 0, BL_PACKED = 1, BL_KN = 2 };
+// kernel-internal epilogue: SwiGLU that also stores the pre-activations
+// (C_aux != NULL); its own instantiation keeps the h-only SwiGLU kernel lean
+constexpr int EPI_SWIGLU_AUX = 3;
+constexpr bool is_swiglu(int epi) { return epi == MOE_EPI_SWIGLU || epi == EPI_SWIGLU_AUX; }
 
 // MFMA fragments of one stage: 8 W (n) and up to 4 X (m) 16x32 slices per lane
 struct Frags {
@@ -121,9 +125,9 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
   int wn, wm;
   wave_pos(wn, wm);
   const int r16 = lane & 15, g4 = lane >> 4;
-  if constexpr (EPI == MOE_EPI_SWIGLU) {
+  if constexpr (is_swiglu(EPI)) {
     const int jbase = n0 + wn * (WTN / 2) + g4 * 4;
-    if (a.Caux) {
+    if (EPI == EPI_SWIGLU_AUX) {
       const int64_t lda = 2 * (int64_t)f;
 #pragma unroll
       for (int j = 0; j < ACT; ++j) {
@@ -159,6 +163,60 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
         const int n = n0 + wn * WTN + i * 16 + g4 * 4;
         if (mr < rows && n < ncols) store_sub<OUT>(a.C, ncols, m0 + mr, n, acc[i][j]);
       }
+    }
+  }
+}
+
+// Staged epilogue for bf16 outputs: every wavefront writes its rows
+// xrow0 + [0, 64) of the tile into the stage buffer of its row slot (free once
+// the K loop has waited for its last loads), 16-byte units XOR-swizzled by
+// row so that the 16 rows one store instruction touches fall on distinct
+// banks; after a barrier the workgroup copies whole tile rows out with
+// 16-byte stores (the direct epilogue writes 32-byte pieces of 16 rows per
+// instruction).  Plain: 256 columns per row (512 bytes); SwiGLU: h, 128
+// columns (256 bytes).
+template <int EPI, int ACT>
+__device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN][TM], int64_t m0, int rows, int n0,
+                                             int ncols, int xrow0, uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                             uint8_t* s3) {
+  auto buf = [&](int i) { return i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3; };
+  constexpr bool SWI = EPI == MOE_EPI_SWIGLU;
+  constexpr int RB = SWI ? 256 : 512;   // bytes per staged row
+  constexpr int UR = RB / 16;           // 16-byte units per row
+  const int lane = threadIdx.x & 63;
+  int wn, wm;
+  wave_pos(wn, wm);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  uint8_t* sb = buf(xrow0 / WTM);
+#pragma unroll
+  for (int j = 0; j < ACT; ++j) {
+    const int rl = j * 16 + r16;   // row within the slot
+#pragma unroll
+    for (int i = 0; i < (SWI ? TN / 2 : TN); ++i) {
+      uint2 w;
+      int col;
+      if constexpr (SWI) {
+        f32x4_t h;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = silu_f32(acc[i][j][q]) * acc[i + TN / 2][j][q];
+        w = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+        col = wn * (WTN / 2) + i * 16 + g4 * 4;
+      } else {
+        w = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
+        col = wn * WTN + i * 16 + g4 * 4;
+      }
+      const int u = col >> 3, half = (col >> 2) & 1;
+      *reinterpret_cast<uint2*>(sb + rl * RB + ((u ^ (rl % UR)) << 4) + half * 8) = w;
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < BM * UR; c += THREADS) {
+    const int row = c / UR, u = c - row * UR;
+    const int col = n0 + 8 * u;
+    if (row < rows && col < ncols) {
+      const int rl = row % WTM;
+      const uint4 v = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
+      *reinterpret_cast<uint4*>(a.C + ((m0 + row) * (int64_t)ncols + col) * 2) = v;
     }
   }
 }
@@ -221,8 +279,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     const int g = tg.g;
     const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
     const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
-    const int n0 = (EPI == MOE_EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
-    const int nrows_b = (EPI == MOE_EPI_SWIGLU) ? 2 * f : a.N;
+    const int n0 = is_swiglu(EPI) ? nt * (BN / 2) : nt * BN;
+    const int nrows_b = is_swiglu(EPI) ? 2 * f : a.N;
 
     Rows<BM, NWAVE> xl;
     Rows<BN, NWAVE> wl;
@@ -230,7 +288,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     xl.init(lda_b, [&](int r) -> int64_t { return min(r, rows - 1); });
     if constexpr (BL == BL_KN) kl.init((int64_t)a.N * 2, n0, a.N);
     if constexpr (BL == BL_NK) wl.init(lda_b, [&](int r) -> int64_t {
-      if constexpr (EPI == MOE_EPI_SWIGLU) {
+      if constexpr (is_swiglu(EPI)) {
         const int wn = r / WTN, q = r % WTN;
         const int jj = min(n0 + wn * (WTN / 2) + (q % (WTN / 2)), f - 1);
         return q < WTN / 2 ? jj : f + jj;
@@ -323,7 +381,11 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       if (s + 1 < nk) iter(b1, b0, s + 1);
       if (s + 2 < nk) iter(b2, b1, s + 2);
       if (s + 3 < nk) iter(b3, b2, s + 3);
-      store<EPI, OUT, ACT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, f, xrow0);
+      if constexpr (OUT == MOE_OUT_BF16 && EPI != EPI_SWIGLU_AUX) {
+        store_staged<EPI, ACT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, xrow0, b0, b1, b2, b3);
+      } else {
+        store<EPI, OUT, ACT>(a, acc, m0, rows, n0, is_swiglu(EPI) ? f : a.N, f, xrow0);
+      }
     };
     if (act == 4) {
       run(std::integral_constant<int, 4>());
@@ -568,13 +630,17 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_KN>), g, t, 0, s, b);
     }
   } else if (b_layout == MOE_B_PACKED) {
-    if (epilogue == MOE_EPI_SWIGLU) {
+    if (epilogue == MOE_EPI_SWIGLU && a.Caux) {
+      hipLaunchKernelGGL((gg_fwd_kernel<EPI_SWIGLU_AUX, MOE_OUT_BF16, BL_PACKED>), g, t, 0, s, b);
+    } else if (epilogue == MOE_EPI_SWIGLU) {
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_PACKED>), g, t, 0, s, b);
     } else if (out_f32) {
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_PACKED>), g, t, 0, s, b);
     } else {
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_PACKED>), g, t, 0, s, b);
     }
+  } else if (epilogue == MOE_EPI_SWIGLU && a.Caux) {
+    hipLaunchKernelGGL((gg_fwd_kernel<EPI_SWIGLU_AUX, MOE_OUT_BF16, BL_NK>), g, t, 0, s, b);
   } else if (epilogue == MOE_EPI_SWIGLU) {
     hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_NK>), g, t, 0, s, b);
   } else if (out_f32) {
