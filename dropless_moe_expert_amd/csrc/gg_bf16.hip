@@ -514,8 +514,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
         mma<ACT>(fr, acc);
         if (!(second && s == nk - 1)) sync(s);
       };
+      __syncthreads();  // every wavefront is done with the previous tile's buffers
       if (nk > 0) {
-        __syncthreads();  // every wavefront is done with the previous tile's buffers
         issue(b0, 0);
         if (nk > 1) issue(b1, 1);
         if (nk > 2) issue(b2, 2);
@@ -534,7 +534,11 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
       }
       GGArgs ag = a;
       ag.C = a.C + (int64_t)g * P * Q * (OUT == MOE_OUT_F32 ? 4 : 2);
-      store<MOE_EPI_NONE, OUT, ACT>(ag, acc, p0, rows, q0, Q, 0, xrow0);
+      if constexpr (OUT == MOE_OUT_BF16) {
+        store_staged<MOE_EPI_NONE, ACT>(ag, acc, p0, rows, q0, Q, xrow0, b0, b1, b2, b3);
+      } else {
+        store<MOE_EPI_NONE, OUT, ACT>(ag, acc, p0, rows, q0, Q, 0, xrow0);
+      }
     };
     if (act == 4) {
       run(std::integral_constant<int, 4>());
