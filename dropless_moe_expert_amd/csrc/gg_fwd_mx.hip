@@ -95,7 +95,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xs
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r32 = lane & 31, g = lane >> 5;
-  const int sw = swz64(r32);                     // rows are 32-aligned bases + r32
+  const int sw = swz_row<1>(r32);                // rows are 32-aligned bases + r32
   const int s_lo = g ^ sw, s_hi = (2 + g) ^ sw;
   const uint32_t* scw = reinterpret_cast<const uint32_t*>(buf + SC_W);
   const uint32_t* scx = reinterpret_cast<const uint32_t*>(buf + SC_X);
@@ -275,15 +275,15 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
         return min(n0 + r, a.N - 1);
       }
     };
-    Rows<BM, NWAVE> xl;
-    Rows<BN, NWAVE> wl;
+    Rows<BM, NWAVE, 1> xl;
+    Rows<BN, NWAVE, 1> wl;
     ScaleRow sl;
     xl.init(lda_b, xrow);
     sl.init(lds_b, wrow, xrow);
     if constexpr (PACKED) {
       const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
-      for (int i = 0; i < Rows<BN, NWAVE>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
+      for (int i = 0; i < Rows<BN, NWAVE, 1>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
       if (sl.is_w) sl.off = (uint32_t)(PK_CODES + ((wave & 3) * 64 + lane) * 4);
     } else {
       wl.init(lda_b, wrow);
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict_
     uint4 v = make_uint4(0, 0, 0, 0);
     if (u < PK_CODES / 16) {
       const int slot = u & 3, r = u >> 2;
-      const int chunk = slot ^ swz64(r);
+      const int chunk = slot ^ swz_row<1>(r);
       bool valid;
       const int row = src_row(nt, r, valid);
       if (valid) v = *reinterpret_cast<const uint4*>(q + ((int64_t)g * nrows_b + row) * K + kt * 64 + chunk * 16);

@@ -21,18 +21,23 @@ constexpr int XOFF = BN * ROWB;               // X (activation) rows follow the 
 constexpr int STAGE = (BM + BN) * ROWB;       // 32 KB
 constexpr int GM = 4;                         // m-tiles per tile-order block
 
-// 16-byte slot swizzle of a 64-byte LDS row: slot = chunk ^ swz64(row).
-// (row >> 1) & 3 measured free of LDS bank conflicts for the fragment reads
-// on gfx950 (SQ_LDS_BANK_CONFLICT = 0), unlike (row >> 2) & 3 or no swizzle.
-#ifndef MOE_SWZ64
-#define MOE_SWZ64(row) (((row) >> 1) & 3)
-#endif
-__device__ __forceinline__ int swz64(int row) { return MOE_SWZ64(row); }
+// 16-byte slot swizzles of a 64-byte LDS row: slot = chunk ^ swz_row<SW>(row),
+// chosen by measuring SQ_LDS_BANK_CONFLICT for each fragment read pattern:
+//  SW = 0, bf16 reads (lane l: row l % 16, chunk l / 16): (row >> 1) & 3 is
+//    free of conflicts on gfx950, (row >> 2) & 3 or no swizzle are not;
+//  SW = 1, MXFP8 reads (lane l: row l % 32, chunk l / 32 or 2 + l / 32):
+//    (row >> 2) & 3 is free of conflicts, (row >> 1) & 3 is 2-way.
+template <int SW>
+__device__ __forceinline__ int swz_row(int row) {
+  if constexpr (SW == 0) return (row >> 1) & 3;
+  return (row >> 2) & 3;
+}
+__device__ __forceinline__ int swz64(int row) { return swz_row<0>(row); }
 
 // Direct-to-LDS rows: one wavefront instruction fills 16 rows (1 KB).  Lane l
-// writes slot l & 3 of row 16*blk + l/4, which holds chunk (l & 3) ^ swz64(row)
-// of that row.
-template <int R, int NW>
+// writes slot l & 3 of row 16*blk + l/4, which holds chunk
+// (l & 3) ^ swz_row<SW>(row) of that row.
+template <int R, int NW, int SW = 0>
 struct Rows {
   static constexpr int N = R / 16 / NW;
   uint32_t off[N];
@@ -42,7 +47,7 @@ struct Rows {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int row = (i * NW + wave) * 16 + (lane >> 2);
-      const int chunk = (lane & 3) ^ swz64(row);
+      const int chunk = (lane & 3) ^ swz_row<SW>(row);
       off[i] = (uint32_t)(grow(row) * ld_bytes + chunk * 16);
     }
   }
