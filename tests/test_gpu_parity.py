@@ -466,3 +466,119 @@ def test_grouped_gemm_bitwise_deterministic(ops):
     c2 = ops.grouped_gemm(A, B, sizes, epilogue=ops.MOE_EPI_SWIGLU)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+# ------------------------------------------------------------------- guard bands
+
+def _guarded(shape, dtype, fill):
+    """A tensor of `shape` at the front of a buffer with a 4 KB tail; every
+    element starts at `fill` (checked as raw bits afterwards)."""
+    n = int(np.prod(shape))
+    tail = 4096 // torch.empty((), dtype=dtype).element_size()
+    buf = torch.full((n + tail,), fill, dtype=dtype, device="cuda")
+    return buf[:n].view(*shape), buf
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else (t.view(torch.int32) if t.element_size() == 4 else t)
+
+
+def _untouched(buf, start, fill):
+    ref = torch.full((1,), fill, dtype=buf.dtype, device=buf.device)
+    return bool(torch.all(_bits(buf[start:]) == _bits(ref)[0]).item())
+
+
+def test_guard_bands_every_output(ops):
+    """Rows past sum(group_sizes) and a 4 KB tail after every output keep their
+    sentinel, for every grouped GEMM variant and the bandwidth kernels (empty
+    groups first, in the middle and last; ragged group tails)."""
+    say("guard bands")
+    rng = np.random.default_rng(61)
+    sizes = np.array([0, 130, 0, 300, 1, 0], np.int32)
+    G, M = sizes.size, int(sizes.sum())
+    m_cap, Kd, N, f = M + 37, 128, 256, 128
+    S = dev(torch.from_numpy(sizes))
+    A = dev(bf16(rng, m_cap, Kd))
+    W = dev(bf16(rng, G, N, Kd, scale=Kd ** -0.5))
+    W1 = dev(bf16(rng, G, 2 * f, Kd, scale=Kd ** -0.5))
+    Wkn = dev(bf16(rng, G, Kd, N, scale=Kd ** -0.5))
+    nan16 = float("nan")
+    cases = []
+    out, buf = _guarded((m_cap, N), torch.bfloat16, nan16)
+    ops.grouped_gemm(A, W, S, out=out)
+    cases.append(("nk plain", out, buf, M * N))
+    out, buf = _guarded((m_cap, N), torch.float32, nan16)
+    ops.grouped_gemm(A, W, S, out=out, out_dtype=torch.float32)
+    cases.append(("nk f32", out, buf, M * N))
+    out, buf = _guarded((m_cap, N), torch.bfloat16, nan16)
+    ops.grouped_gemm(A, ops.pack_weights(W), S, out=out)
+    cases.append(("packed plain", out, buf, M * N))
+    out, buf = _guarded((m_cap, f), torch.bfloat16, nan16)
+    ops.grouped_gemm(A, ops.pack_weights(W1, ops.MOE_EPI_SWIGLU), S, epilogue=ops.MOE_EPI_SWIGLU, out=out)
+    cases.append(("packed swiglu", out, buf, M * f))
+    out, buf = _guarded((m_cap, f), torch.bfloat16, nan16)
+    aux, abuf = _guarded((m_cap, 2 * f), torch.bfloat16, nan16)
+    ops.grouped_gemm(A, W1, S, epilogue=ops.MOE_EPI_SWIGLU, out=out, aux=aux, keep_aux=True)
+    cases.append(("swiglu h", out, buf, M * f))
+    cases.append(("swiglu aux", aux, abuf, M * 2 * f))
+    out, buf = _guarded((m_cap, N), torch.bfloat16, nan16)
+    ops.grouped_gemm(A, Wkn, S, b_layout=ops.MOE_B_KN, out=out)
+    cases.append(("kn dgrad", out, buf, M * N))
+    # MXFP8: plain, SwiGLU, quantising SwiGLU (codes and scales)
+    aq, as_ = ops.mxfp8_quantize(A, 0)
+    wq, ws = ops.quantize_weights(W)
+    w1q, w1s = ops.quantize_weights(W1)
+    out, buf = _guarded((m_cap, N), torch.bfloat16, nan16)
+    ops.grouped_gemm_mxfp8(aq, as_, ops.pack_weights_mxfp8(wq, ws), None, S, out=out)
+    cases.append(("mxfp8 plain", out, buf, M * N))
+    P1 = ops.pack_weights_mxfp8(w1q, w1s, ops.MOE_EPI_SWIGLU)
+    out, buf = _guarded((m_cap, f), torch.bfloat16, nan16)
+    ops.grouped_gemm_mxfp8(aq, as_, P1, None, S, epilogue=ops.MOE_EPI_SWIGLU, out=out)
+    cases.append(("mxfp8 swiglu", out, buf, M * f))
+    q, qbuf = _guarded((m_cap, f), torch.uint8, 0xA5)
+    sc, sbuf = _guarded((m_cap, f // 32), torch.uint8, 0xA5)
+    ops.grouped_gemm_mxfp8(aq, as_, P1, None, S, epilogue=ops.MOE_EPI_SWIGLU_MXFP8, out=q, out_scale=sc)
+    cases.append(("mxfp8 fused codes", q, qbuf, M * f))
+    cases.append(("mxfp8 fused scales", sc, sbuf, M * (f // 32)))
+    # quantiser over the valid rows only
+    # (the binding allocates: call the library directly to quantise into the guarded buffers)
+    q, qbuf = _guarded((m_cap, Kd), torch.uint8, 0xA5)
+    sc, sbuf = _guarded((m_cap, Kd // 32), torch.uint8, 0xA5)
+    st = ops.lib().mxfp8_group_quantize(ops._ptr(A), m_cap, Kd, 0, ops._ptr(S), G, ops._ptr(q), ops._ptr(sc), None,
+                                        ops._stream(A.device))
+    assert st == 0
+    cases.append(("quantize codes", q, qbuf, M * Kd))
+    cases.append(("quantize scales", sc, sbuf, M * (Kd // 32)))
+    # weight gradient: every group written (empty ones as zeros), nothing past C
+    Y = dev(bf16(rng, m_cap, N))
+    out, buf = _guarded((G, Kd, N), torch.bfloat16, nan16)
+    ops.grouped_gemm_wgrad(A, Y, S, out=out)
+    cases.append(("wgrad", out, buf, G * Kd * N))
+    torch.cuda.synchronize()
+    for name, o, b, valid in cases:
+        assert _untouched(b, valid, 0xA5 if b.dtype == torch.uint8 else nan16), name
+    # the valid parts were written (no sentinel left in them)
+    for name, o, b, valid in cases:
+        if b.dtype in (torch.bfloat16, torch.float32):
+            assert not bool(torch.isnan(b[:valid]).any().item()), name
+    # wgrad of the empty groups: exact zeros
+    for g in np.nonzero(sizes == 0)[0]:
+        assert bool(torch.all(out[int(g)] == 0).item())
+    # permute and combine: exactly T*K rows / T rows, nothing past them
+    T, K, E, d = 97, 2, 5, 64
+    ids = dev(torch.from_numpy(rng.integers(0, E, size=(T, K)).astype(np.int32)))
+    ids[:, 1] = (ids[:, 0] + 1) % E
+    x = dev(bf16(rng, T, d))
+    p = ops.permute(x, ids, E)
+    xp, xbuf = _guarded((T * K, d), torch.bfloat16, nan16)
+    ws_bytes = ops.lib().moe_permute_workspace_bytes(T, E, K)
+    wsb = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    st = ops.lib().moe_permute(ops._ptr(x), ops._ptr(ids), T, d, E, K, ops._ptr(p["group_sizes"]),
+                               ops._ptr(p["group_offsets"]), ops._ptr(p["perm_src"]), ops._ptr(p["perm_dst"]),
+                               ops._ptr(xp), ops._ptr(wsb), ws_bytes, None, ops._stream(x.device))
+    assert st == 0
+    y, ybuf = _guarded((T, d), torch.bfloat16, nan16)
+    ops.unpermute_combine(xp, None, p["perm_dst"], T, K, out=y)
+    torch.cuda.synchronize()
+    assert _untouched(xbuf, T * K * d, nan16) and _untouched(ybuf, T * d, nan16)
+    assert not bool(torch.isnan(xbuf[: T * K * d]).any().item()) and not bool(torch.isnan(ybuf[: T * d]).any().item())
