@@ -19,7 +19,8 @@ Also reported in the same line:
         the quantisation of H fused in its epilogue, down; the unfused gate/up
         and quantisation of H are timed as well);
       - the Mixtral-shaped forward layer (route, permute, two GEMMs, combine),
-        as tokens/s;
+        as tokens/s, in bf16 and in MXFP8 (permute writing MXFP8 rows, gate/up
+        quantising its output);
       - the fine-grained layer (T=16384, d=2048, 128 experts top-8, ffn=768)
         forward and backward, as tokens/s;
   * measured ceilings: the GEMM inner loop's MFMA rate with random and with
@@ -202,6 +203,48 @@ def bench_mixtral(torch, ops, L, dev, timer, flag, steps) -> dict:
             "kernel_sum_ms": round(ksum, 4), "kernels": kern}
 
 
+def bench_mixtral_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
+    """The Mixtral-shaped layer on MXFP8 operands: route, permute writing MXFP8
+    rows, gate/up GEMM quantising its SwiGLU output, down GEMM, combine
+    (weights quantised and packed once, outside the timed region)."""
+    T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
+    M = T * K
+    lg, x = L.logits.to(dev), L.x.to(dev)
+    w1q, w1s = ops.quantize_weights(L.w1p.to(dev))
+    w1k = ops.pack_weights_mxfp8(w1q, w1s, ops.MOE_EPI_SWIGLU)
+    del w1q, w1s
+    w2q, w2s = ops.quantize_weights(L.w2.to(dev))
+    w2k = ops.pack_weights_mxfp8(w2q, w2s)
+    del w2q, w2s
+    ids, w = ops.route_topk(lg, K, flag=flag)
+    p = ops.permute_mxfp8(x, ids, E, flag=flag)
+    hq, hs = ops.grouped_gemm_mxfp8(p["xq"], p["xs"], w1k, None, p["group_sizes"],
+                                    epilogue=ops.MOE_EPI_SWIGLU_MXFP8, flag=flag)
+    y_perm = ops.grouped_gemm_mxfp8(hq, hs, w2k, None, p["group_sizes"], flag=flag)
+    t_perm = timer(lambda: ops.permute_mxfp8(x, ids, E, flag=flag))
+    t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(p["xq"], p["xs"], w1k, None, p["group_sizes"],
+                                                epilogue=ops.MOE_EPI_SWIGLU_MXFP8, out=hq, out_scale=hs, flag=flag))
+    t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, w2k, None, p["group_sizes"], out=y_perm, flag=flag))
+    for _ in range(3):
+        ops.moe_forward_mxfp8(lg, x, w1k, w2k, K, flag=flag)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        ops.moe_forward_mxfp8(lg, x, w1k, w2k, K, flag=flag)
+    torch.cuda.synchronize()
+    lms = (time.perf_counter() - a) * 1e3 / steps
+    lflops = 2.0 * M * (2 * f * d + d * f)
+    return {"workload": "mixtral-shaped forward T=4096 d=4096 E=8 top-2 ffn=14336 in MXFP8 (E4M3 + E8M0/32): "
+                        "route, permute writing MXFP8, gate/up + SwiGLU + quantise H, down, combine",
+            "tokens_per_s": round(T / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
+            "valid_row_tflops": round(lflops / (lms * 1e-3) / 1e12, 2),
+            "kernels": {
+                "permute_mxfp8": byte_entry(t_perm, T * d * 2 + T * K * 4 + M * d + M * d / 32 + M * 8),
+                "gate_up_swiglu_quantize_mxfp8": flop_entry(t_g1, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
+                "down_mxfp8": flop_entry(t_g2, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
+            }}
+
+
 def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
     """Forward and backward of the fine-grained layer (weights unpacked: the
     backward reads them as [K, N] too)."""
@@ -362,6 +405,10 @@ def main() -> int:
         workloads["mixtral"] = bench_mixtral(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
         log(f"mixtral layer: {workloads['mixtral']['ms_per_step']:.3f} ms, "
             f"{workloads['mixtral']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
+        torch.cuda.empty_cache()
+        workloads["mixtral_mxfp8"] = bench_mixtral_mxfp8(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
+        log(f"mixtral layer mxfp8: {workloads['mixtral_mxfp8']['ms_per_step']:.3f} ms, "
+            f"{workloads['mixtral_mxfp8']['tokens_per_s']:.0f} tokens/s")
         del Lm
         torch.cuda.empty_cache()
         t0 = time.time()

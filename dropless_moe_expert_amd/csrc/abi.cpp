@@ -15,6 +15,8 @@ moe_status_t moe_route_topk_launch(const float*, int64_t, int32_t, int32_t, int3
 size_t moe_permute_ws_bytes_impl(int64_t, int32_t, int32_t);
 moe_status_t moe_permute_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
                                 int32_t*, int32_t*, int32_t*, uint16_t*, void*, uint32_t*, hipStream_t);
+moe_status_t moe_permute_mxfp8_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
+                                      int32_t*, int32_t*, int32_t*, uint8_t*, uint8_t*, void*, uint32_t*, hipStream_t);
 moe_status_t moe_unpermute_combine_launch(const uint16_t*, const float*, const int32_t*, int64_t, int32_t, int32_t,
                                           uint16_t*, hipStream_t);
 moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const float*, const int32_t*, int64_t,
@@ -104,6 +106,23 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
   return moe_permute_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_perm, ws,
                             err_flag, S(stream));
+}
+
+moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                               int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                               int32_t* perm_dst, uint8_t* x_q, uint8_t* x_scale, void* ws, size_t ws_bytes,
+                               uint32_t* err_flag, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm_src || !perm_dst || !x || !x_q || !x_scale)) return MOE_ERR_INVALID_ARG;
+  if (d < 32 || d % 32) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!aligned16(x) || !aligned16(x_q))) return MOE_ERR_ALIGNMENT;
+  const size_t need = moe_permute_ws_bytes_impl(T, E, K);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
+  return moe_permute_mxfp8_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_q,
+                                  x_scale, ws, err_flag, S(stream));
 }
 
 size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {

@@ -180,6 +180,62 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __
   }
 }
 
+// The scatter writing MXFP8: each 32-element block of the token row (four
+// consecutive lanes' 16-byte vectors) gets one E8M0 scale and E4M3 codes by
+// the same rule and helpers as mxfp8_group_quantize (axis 0), then goes to
+// the token's K rows; equal to moe_permute followed by the quantiser.
+template <int KT>
+__global__ __launch_bounds__(256) void permute_scatter_mx_kernel(const uint16_t* __restrict__ x,
+                                                                 const int32_t* __restrict__ ids,
+                                                                 const int32_t* __restrict__ local_rank,
+                                                                 const int32_t* __restrict__ chunk_base, int64_t T,
+                                                                 int d, int E, int K, int32_t* __restrict__ perm_src,
+                                                                 int32_t* __restrict__ perm_dst,
+                                                                 uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
+  constexpr int KM = KT > 0 ? KT : 32;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  if (KT > 0) K = KT;
+  int32_t my_row = 0;
+  if (lane < K) {
+    const int64_t i = t * K + lane;
+    int e = ids[i];
+    if (e < 0 || e >= E) e = E - 1;
+    my_row = chunk_base[(i / kChunk) * E + e] + local_rank[i];
+    perm_dst[i] = my_row;
+    perm_src[my_row] = (int32_t)i;
+  }
+  int32_t rows[KM];
+#pragma unroll
+  for (int k = 0; k < KM; ++k) rows[k] = (k < K) ? __shfl(my_row, k, 64) : 0;
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  const int nvec = d / 8;   // a multiple of 4: blocks never straddle lanes of different iterations
+  for (int v = lane; v - (lane & 3) < nvec; v += 64) {
+    const bool live = v < nvec;
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) unpack8(src[v], f);
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int e = mx_exponent(amax);
+    if (live) {
+      uint2 q;
+      q.x = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
+      q.y = cvt4_e4m3(scale_pow2(f[4], e), scale_pow2(f[5], e), scale_pow2(f[6], e), scale_pow2(f[7], e));
+#pragma unroll
+      for (int k = 0; k < KM; ++k) {
+        if (k < K) {
+          reinterpret_cast<uint2*>(xq + (int64_t)rows[k] * d)[v] = q;
+          if ((lane & 3) == 0) xs[(int64_t)rows[k] * (d / 32) + (v >> 2)] = (uint8_t)(e + 127);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace moe
 
 extern "C" size_t moe_permute_ws_bytes_impl(int64_t T, int32_t E, int32_t K) {
@@ -219,6 +275,35 @@ extern "C" moe_status_t moe_permute_launch(const uint16_t* x, const int32_t* ids
                                  E, K, perm_src, perm_dst, x_perm); break;
       default: hipLaunchKernelGGL((moe::permute_scatter_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
                                   d, E, K, perm_src, perm_dst, x_perm);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" moe_status_t moe_permute_mxfp8_launch(const uint16_t* x, const int32_t* ids, int64_t T, int32_t d, int32_t E,
+                                                 int32_t K, int32_t* group_sizes, int32_t* group_offsets,
+                                                 int32_t* perm_src, int32_t* perm_dst, uint8_t* xq, uint8_t* xs,
+                                                 void* ws, uint32_t* flag, hipStream_t s) {
+  const int64_t M = T * K;
+  const int64_t nchunk = (M + moe::kChunk - 1) / moe::kChunk;
+  int32_t* local_rank = reinterpret_cast<int32_t*>(ws);
+  size_t a = ((size_t)M * 4 + 255) & ~(size_t)255;
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + a);
+  if (M > 0) {
+    hipLaunchKernelGGL(moe::permute_rank_kernel, dim3((unsigned)nchunk), dim3(64), 0, s, ids, M, E, local_rank,
+                       chunk_counts, flag);
+  }
+  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+                     group_offsets);
+  if (T > 0) {
+    const dim3 g((unsigned)((T + 3) / 4)), b(256);
+    switch (K) {
+      case 2: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
+                                 d, E, K, perm_src, perm_dst, xq, xs); break;
+      case 8: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
+                                 d, E, K, perm_src, perm_dst, xq, xs); break;
+      default: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                  T, d, E, K, perm_src, perm_dst, xq, xs);
     }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

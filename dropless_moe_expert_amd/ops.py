@@ -31,7 +31,8 @@ FLAG_NAN_LOGIT = 0x8
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
-    "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine", "moe_combine_backward",
+    "moe_permute_mxfp8", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
+    "moe_combine_backward",
     "moe_swiglu_backward", "mxfp8_group_quantize", "moe_pack_weights_bytes", "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
     # measurement only (include/moe_bench.h)
@@ -71,6 +72,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_route_topk": (ctypes.c_int, [P, i64, i32, i32, i32, P, P, P, P]),
             "moe_permute_workspace_bytes": (sz, [i64, i32, i32]),
             "moe_permute": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P, P]),
+            "moe_permute_mxfp8": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, sz, P, P]),
             "grouped_gemm_workspace_bytes": (sz, [ctypes.POINTER(GGDesc)]),
             "grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GGDesc), P, P, P, P, P, P, P, P, sz, P, P]),
             "moe_unpermute_combine": (ctypes.c_int, [P, P, P, i64, i32, i32, P, P]),
@@ -175,6 +177,34 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Opt
                              _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
                              _ptr(out["x_perm"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _ptr(flag), _stream(dev)), "moe_permute")
+    return out
+
+
+def permute_mxfp8(x: torch.Tensor, topk_ids: torch.Tensor, E: int, flag: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Permute with MXFP8 output -> dict(group_sizes, group_offsets, perm_src,
+    perm_dst, xq uint8 [T*K, d], xs uint8 [T*K, d/32])."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2 and x.dtype == torch.bfloat16
+    dev = _dev(topk_ids, x)
+    T, K = topk_ids.shape
+    d = x.shape[1]
+    M = T * K
+    out = dict(
+        group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
+        group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm_src=torch.empty(M, dtype=torch.int32, device=dev),
+        perm_dst=torch.empty(M, dtype=torch.int32, device=dev),
+        xq=torch.empty((M, d), dtype=torch.uint8, device=dev),
+        xs=torch.empty((M, d // 32), dtype=torch.uint8, device=dev),
+    )
+    need = lib().moe_permute_workspace_bytes(T, E, K)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().moe_permute_mxfp8(_ptr(x), _ptr(topk_ids), T, d, E, K, _ptr(out["group_sizes"]),
+                                   _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
+                                   _ptr(out["xq"]), _ptr(out["xs"]), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _ptr(flag), _stream(dev)),
+           "moe_permute_mxfp8")
     return out
 
 
@@ -392,6 +422,22 @@ def moe_forward(logits: torch.Tensor, x: torch.Tensor, w1p: torch.Tensor, w2: to
     if not keep:
         return y, None
     return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, **p)
+
+
+def moe_forward_mxfp8(logits: torch.Tensor, x: torch.Tensor, w1k, w2k, K: int,
+                      flag: Optional[torch.Tensor] = None):
+    """The routed layer on MXFP8 operands: router top-K -> permute writing
+    MXFP8 rows -> gate/up GEMM quantising its SwiGLU output -> down GEMM ->
+    combine.  w1k / w2k: PackedWeights from pack_weights_mxfp8 (gate/up packed
+    for MOE_EPI_SWIGLU).  Returns y [T, d] bf16 and the intermediates."""
+    T = x.shape[0]
+    ids, w = route_topk(logits, K, flag=flag)
+    p = permute_mxfp8(x, ids, w1k.G, flag=flag)
+    hq, hs = grouped_gemm_mxfp8(p["xq"], p["xs"], w1k, None, p["group_sizes"], epilogue=MOE_EPI_SWIGLU_MXFP8,
+                                flag=flag)
+    y_perm = grouped_gemm_mxfp8(hq, hs, w2k, None, p["group_sizes"], flag=flag)
+    y = unpermute_combine(y_perm, w, p["perm_dst"], T, K)
+    return y, dict(ids=ids, w=w, hq=hq, hs=hs, y_perm=y_perm, **p)
 
 
 def moe_backward(dy: torch.Tensor, saved: dict, w1p: torch.Tensor, w2: torch.Tensor, K: int,

@@ -105,6 +105,17 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
                          int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
                          uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream);
 
+/* Permute with MXFP8 output (the page's planned quantisation fused into the
+ * dispatch, section "Optimization 1"): the same maps as moe_permute, and
+ * instead of bf16 rows the E4M3 codes x_q uint8 [T*K, d] and E8M0 scales
+ * x_scale uint8 [T*K, d/32] that mxfp8_group_quantize (axis 0) would produce
+ * from moe_permute's x_perm, bit for bit; each token row is read and
+ * quantised once.  x, x_q 16-byte aligned; d % 32 == 0; ws as moe_permute. */
+moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                               int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                               int32_t* perm_dst, uint8_t* x_q, uint8_t* x_scale, void* ws, size_t ws_bytes,
+                               uint32_t* err_flag, void* stream);
+
 /* ------------------------------------------------------------------------
  * Grouped GEMM (blog section "Optimization 1: Grouped GEMM": all experts in
  * one call, each with its true token count, only rows with valid tokens

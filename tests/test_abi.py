@@ -62,6 +62,11 @@ def test_host_checkable_errors_return_status():
     assert L.moe_permute(ctypes.c_void_p((1 << 20) + 2), fake, 4, 16, 8, 2, fake, fake, fake, fake, fake, fake,
                          1 << 20, None, None) == ALIGN
     assert L.moe_permute_workspace_bytes(16384, 128, 8) >= 16384 * 8 * 4
+    # permute with MXFP8 output: d % 32 == 0, outputs required
+    assert L.moe_permute_mxfp8(fake, fake, 4, 48, 8, 2, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None,
+                               None) == UNSUPPORTED
+    assert L.moe_permute_mxfp8(fake, fake, 4, 64, 8, 2, fake, fake, fake, fake, None, fake, fake, 1 << 20, None,
+                               None) == INVALID
     # grouped GEMM descriptor checks
     d = ops.GGDesc(0, 0, 0, 0, 0, 4, 0, 64, 64, 100)
     bd = ctypes.byref(d)

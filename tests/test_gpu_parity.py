@@ -63,6 +63,55 @@ def test_permute(ops, T, E, K, d):
     np.testing.assert_array_equal(host_u16(out["x_perm"]), xp_ref)
 
 
+@pytest.mark.parametrize("T,E,K,d", [(256, 8, 2, 128), (3000, 128, 8, 64), (1, 4, 2, 32), (513, 6, 3, 96),
+                                     (0, 8, 2, 32)])
+def test_permute_mxfp8(ops, T, E, K, d):
+    """Permute writing MXFP8 rows: maps as moe_permute, codes and scales bit
+    for bit those of quantising the oracle's permuted bf16 rows."""
+    say("permute mxfp8", T, E, K, d)
+    rng = np.random.default_rng(T + 7 * E)
+    ids = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int32).reshape(T, K)
+    x = bf16(rng, T, d, scale=3.0)
+    sizes, offs, src, dst = orc.permute(ids, E)
+    xq_ref, xs_ref = orc.mxfp8_quantize(orc.gather_rows(x, src, K), 0)
+    out = ops.permute_mxfp8(dev(x), dev(torch.from_numpy(ids)), E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["group_sizes"].cpu().numpy(), sizes)
+    np.testing.assert_array_equal(out["group_offsets"].cpu().numpy(), offs)
+    np.testing.assert_array_equal(out["perm_src"].cpu().numpy(), src)
+    np.testing.assert_array_equal(out["perm_dst"].cpu().numpy(), dst)
+    np.testing.assert_array_equal(out["xq"].cpu().numpy(), xq_ref.reshape(T * K, d))
+    np.testing.assert_array_equal(out["xs"].cpu().numpy(), xs_ref.reshape(T * K, d // 32))
+
+
+def test_routed_layer_mxfp8(ops):
+    """The routed MXFP8 forward (permute writing MXFP8, gate/up quantising its
+    output, down, combine) against the oracle applying the same quantisation
+    at the same points."""
+    say("routed mxfp8 layer")
+    T, d, E, K, f = 600, 256, 8, 2, 256
+    L = inputs.routed_layer("mx", T, d, E, K, f, 71, bias_std=1.0)
+    lg, x, w1p, w2 = dev(L.logits), dev(L.x), dev(L.w1p), dev(L.w2)
+    w1q, w1s = ops.quantize_weights(w1p)
+    w2q, w2s = ops.quantize_weights(w2)
+    w1k = ops.pack_weights_mxfp8(w1q, w1s, ops.MOE_EPI_SWIGLU)
+    w2k = ops.pack_weights_mxfp8(w2q, w2s)
+    y, parts = ops.moe_forward_mxfp8(lg, x, w1k, w2k, K)
+    torch.cuda.synchronize()
+    ids, w = orc.route_topk(L.logits, K)
+    sizes, offs, src, dst = orc.permute(ids, E)
+    xq, xs = orc.mxfp8_quantize(orc.gather_rows(L.x, src, K), 0)
+    q1, s1 = orc.mxfp8_quantize(orc.u16(L.w1p).reshape(-1, d), 0)
+    q2, s2 = orc.mxfp8_quantize(orc.u16(L.w2).reshape(-1, f), 0)
+    h = orc.mx_grouped_gemm(xq, xs, q1.reshape(E, 2 * f, d), s1.reshape(E, 2 * f, d // 32), sizes, swiglu=True)
+    hq, hs = orc.mxfp8_quantize(h, 0)
+    yp = orc.mx_grouped_gemm(hq, hs, q2.reshape(E, d, f), s2.reshape(E, d, f // 32), sizes)
+    y_ref = orc.unpermute_combine(yp, w, dst, T, K)
+    np.testing.assert_array_equal(parts["ids"].cpu().numpy(), ids)
+    np.testing.assert_array_equal(parts["xq"].cpu().numpy(), xq)
+    assert rel_l2(y, y_ref) <= MX_TOL
+
+
 def test_permute_maps_only_and_deterministic(ops):
     rng = np.random.default_rng(5)
     T, E, K = 5000, 64, 6
