@@ -4,9 +4,9 @@
 // global memory traffic: one 8-wavefront workgroup per CU (all of LDS), a
 // ping-pong schedule in which each wavefront reads 12 fragments (16 bytes per
 // lane) from LDS, meets a barrier, issues 32 independent
-// v_mfma_f32_16x16x32_bf16 from registers and meets a barrier, with the
-// second wavefront of every SIMD one phase behind the first.  LDS holds either
-// random bf16 values (random mantissas and signs, exponents 2^-4..2^3) or
+// v_mfma_f32_16x16x32_bf16 from registers (in the GEMMs' serpentine order)
+// and meets a barrier, with the second wavefront of every SIMD one phase
+// behind the first.  LDS holds either random bf16 values (random mantissas and signs, exponents 2^-4..2^3) or
 // constant ones.  On MI355X the random case runs well below the nominal MFMA
 // rate (power-limited clocks); its rate is the practical ceiling against
 // which the GEMMs' MFMA utilisation is read.
@@ -64,7 +64,10 @@ __global__ void __launch_bounds__(512, 1) mfma_ceiling_kernel(float* sink, int i
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], x[j], acc[i][j], 0, 0, 0);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = (i & 1) ? 3 - jj : jj;   // serpentine, as the GEMMs issue them
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[i], x[j], acc[i][j], 0, 0, 0);
+      }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);

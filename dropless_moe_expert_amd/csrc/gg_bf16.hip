@@ -106,13 +106,19 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xr
   }
 }
 
-// MFMAs of the wavefront's ACT 16-row subtiles
+// MFMAs of the wavefront's ACT 16-row subtiles, in serpentine order: the row
+// subtile runs forwards for even weight fragments and backwards for odd ones,
+// so consecutive MFMAs share an operand across the turn (measured 2-3 % faster
+// than restarting each row on random operands, where the rate is power-bound)
 template <int ACT>
 __device__ __forceinline__ void mma(const Frags& fr, f32x4_t (&acc)[TN][TM]) {
 #pragma unroll
   for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < ACT; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
+    for (int jj = 0; jj < ACT; ++jj) {
+      const int j = (i & 1) ? ACT - 1 - jj : jj;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0);
+    }
 }
 
 // Stores the wavefront's 128 x (16 * ACT) block (rows xrow0 + ...).  Plain: column n0 + wn*WTN + 16i + 4*g4.

@@ -113,13 +113,16 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xs
   }
 }
 
+// serpentine order, as in the bf16 kernel: consecutive MFMAs share an operand
 __device__ __forceinline__ void mma(const Frags& fr, f32x16_t (&acc)[MTN][MTM]) {
 #pragma unroll
   for (int i = 0; i < MTN; ++i)
 #pragma unroll
-    for (int j = 0; j < MTM; ++j)
+    for (int jj = 0; jj < MTM; ++jj) {
+      const int j = (i & 1) ? MTM - 1 - jj : jj;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr.w[i], fr.x[j], acc[i][j], 0, 0, 0, fr.ws[i], 0,
                                                                    fr.xs[j]);
+    }
 }
 
 // 32x32 accumulator: element v of lane (r32, g) is n = 8*(v/4) + 4*g + v%4,
