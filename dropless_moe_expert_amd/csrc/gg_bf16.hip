@@ -31,9 +31,10 @@
 //    bounds the bytes in flight; each stage waits only for its own loads;
 //  * the group of a tile is found by a wavefront scan over the device
 //    group sizes (no LDS table), which leaves all of LDS to the stages;
-//  * tiles are ordered in blocks of 4 m-tiles x all n-tiles and consecutive
-//    tiles run on one XCD, so the 32 tiles an XCD holds at a time share
-//    4 activation panels and 8 weight panels in its L2.
+//  * tiles go group by group in blocks of about sqrt(32) m-tiles x all
+//    n-tiles, and consecutive tiles run on one XCD, so the 32 tiles an XCD
+//    holds at a time share a few activation and weight panels in its L2
+//    and never mix two experts' weights.
 // Measured on random operands, MI355X sustains about 70 % of its nominal
 // bf16 MFMA rate for this fragment pattern even with no memory traffic
 // (power-limited clocks); every byte moved lowers that further.
@@ -261,9 +262,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
 
   const int wid = worker_id();
   const int f = a.N / 2;
-  int64_t m_tiles = 0;
-  locate(a, -1, &m_tiles);
-  const int64_t total = m_tiles * a.n_tiles;
+  const int64_t total = count_mtiles(a) * a.n_tiles;
   const int64_t lda_b = (int64_t)a.K * 2;
   const int nk = a.K / 32;
   uint32_t koff[TN];   // BL_KN: per-lane LDS offsets of the 8 weight fragments
@@ -275,16 +274,10 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   }
 
   for (int64_t tile = wid; tile < total; tile += gridDim.x) {
-    // tile order: blocks of GM m-tiles; inside a block m varies fastest
-    const int64_t blk = tile / ((int64_t)GM * a.n_tiles);
-    const int rem = (int)(tile - blk * GM * a.n_tiles);
-    const int gm = (int)min<int64_t>(GM, m_tiles - blk * GM);
-    const int64_t mt = blk * GM + rem % gm;
-    const int nt = rem / gm;
-    const TileGroup tg = locate(a, mt, nullptr);
-    const int g = tg.g;
-    const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
-    const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
+    const TileGroup tg = locate(a, tile);
+    const int g = tg.g, nt = tg.nt;
+    const int64_t m0 = tg.m0;
+    const int rows = tg.rows;
     const int n0 = is_swiglu(EPI) ? nt * (BN / 2) : nt * BN;
     const int nrows_b = is_swiglu(EPI) ? 2 * f : a.N;
 

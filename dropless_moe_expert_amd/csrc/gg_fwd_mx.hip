@@ -247,23 +247,16 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
 
   const int wid = worker_id();
   const int f = a.N / 2;
-  int64_t m_tiles = 0;
-  locate(a, -1, &m_tiles);
-  const int64_t total = m_tiles * a.n_tiles;
+  const int64_t total = count_mtiles(a) * a.n_tiles;
   const int64_t lda_b = a.K;            // one byte per code
   const int64_t lds_b = a.K / 32;       // scale bytes per row
   const int nk = a.K / 64;
 
   for (int64_t tile = wid; tile < total; tile += gridDim.x) {
-    const int64_t blk = tile / ((int64_t)GM * a.n_tiles);
-    const int rem = (int)(tile - blk * GM * a.n_tiles);
-    const int gm = (int)min<int64_t>(GM, m_tiles - blk * GM);
-    const int64_t mt = blk * GM + rem % gm;
-    const int nt = rem / gm;
-    const TileGroup tg = locate(a, mt, nullptr);
-    const int g = tg.g;
-    const int64_t m0 = tg.row0 + (mt - tg.tile0) * BM;
-    const int rows = (int)min<int64_t>(BM, tg.row1 - m0);
+    const TileGroup tg = locate(a, tile);
+    const int g = tg.g, nt = tg.nt;
+    const int64_t m0 = tg.m0;
+    const int rows = tg.rows;
     constexpr bool SWI = EPI != MOE_EPI_NONE;   // either SwiGLU epilogue: gate/up tile geometry
     const int n0 = SWI ? nt * (BN / 2) : nt * BN;
     const int nrows_b = SWI ? 2 * f : a.N;

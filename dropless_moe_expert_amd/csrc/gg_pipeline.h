@@ -19,7 +19,6 @@ constexpr int ROWB = 64;            // LDS bytes per row and stage (32 bf16)
 constexpr int WN = 2, WTN = BN / WN;          // two wavefront columns of 128 n each
 constexpr int XOFF = BN * ROWB;               // X (activation) rows follow the W rows in a stage
 constexpr int STAGE = (BM + BN) * ROWB;       // 32 KB
-constexpr int GM = 4;                         // m-tiles per tile-order block
 
 // 16-byte slot swizzles of a 64-byte LDS row: slot = chunk ^ swz_row<SW>(row),
 // chosen by measuring SQ_LDS_BANK_CONFLICT for each fragment read pattern:
@@ -155,13 +154,22 @@ __device__ __forceinline__ bf16x8_t kfrag_read(const uint8_t* buf, uint32_t off)
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Group of m-tile mt from the device group sizes, one wavefront scan over
-// chunks of 64 groups (sizes clamped to >= 0 and the rows to m_cap, as the
-// other kernels do).  Returns g, the group's first row and its first m-tile.
+// Tile order of the ragged-M kernels, from the device group sizes (clamped
+// to >= 0, and the rows to m_cap, as the other kernels do).  Tiles go group
+// by group; a group's m m-tiles are cut into b = round(m / 5.66) blocks of
+// near-equal size (at least one), and inside a block the m-tile varies
+// fastest over all n-tiles.  The 32 consecutive tiles that run together on
+// one XCD then share few operand panels in its L2 (per m-tile, a block of gm
+// m-tiles costs about gm/32 activation panel reads per n-tile plus 1/gm
+// weight panel reads: least at gm = sqrt(32)), and no block mixes the weights
+// of two experts.
+constexpr int kBlockTarget = 566;   // 100 x the m-tiles aimed at per block (sqrt(32))
+
 struct TileGroup {
   int g;
-  int64_t row0, row1;
-  int64_t tile0;
+  int nt;         // n-tile
+  int64_t m0;     // first row of the tile
+  int rows;       // valid rows in the tile (1..BM)
 };
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
@@ -174,45 +182,77 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
   return v;
 }
 
-// total m-tiles (mt < 0) or the group holding m-tile mt
-__device__ __forceinline__ TileGroup locate(const GGArgs& a, int64_t mt, int64_t* total) {
+__device__ __forceinline__ int64_t wave_u64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// total number of m-tiles over all groups
+__device__ __forceinline__ int64_t count_mtiles(const GGArgs& a) {
   const int lane = threadIdx.x & 63;
-  int64_t rbase = 0, tbase = 0;
-  TileGroup r{a.G - 1, 0, 0, 0};
-  bool found = false;
+  int64_t rbase = 0, nt = 0;
   for (int c = 0; c < a.G; c += 64) {
     const int gi = c + lane;
     const int64_t s = gi < a.G ? (int64_t)max(a.sizes[gi], 0) : 0;
     const int64_t rincl = wave_incl_scan(s);
-    const int64_t r1 = min(rbase + rincl, a.m_cap), r0 = min(rbase + rincl - s, a.m_cap);
-    const int64_t nt = (r1 - r0 + BM - 1) / BM;
-    const int64_t tincl = wave_incl_scan(nt);
-    if (!found && mt >= 0) {
-      const uint64_t hit = __ballot(gi < a.G && nt > 0 && tbase + tincl > mt);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        r.g = c + l;
-        r.row0 = __shfl(r0, l, 64);
-        r.row1 = __shfl(r1, l, 64);
-        r.tile0 = tbase + __shfl(tincl - nt, l, 64);
-        found = true;
+    const int64_t n = min(rbase + rincl, a.m_cap) - min(rbase + rincl - s, a.m_cap);
+    nt += (n + BM - 1) / BM;
+    rbase += __shfl(rincl, 63, 64);
+  }
+  return wave_u64(wave_sum(nt));
+}
+
+// tile number `tile` (0 <= tile < m-tiles * n_tiles) of the order above
+__device__ __forceinline__ TileGroup locate(const GGArgs& a, int64_t tile) {
+  const int lane = threadIdx.x & 63;
+  int64_t rbase = 0, tbase = 0;
+  TileGroup r{a.G - 1, 0, 0, 1};
+  for (int c = 0; c < a.G; c += 64) {
+    const int gi = c + lane;
+    const int64_t s = gi < a.G ? (int64_t)max(a.sizes[gi], 0) : 0;
+    const int64_t rincl = wave_incl_scan(s);
+    const int64_t r0 = min(rbase + rincl - s, a.m_cap);
+    const int64_t n = min(rbase + rincl, a.m_cap) - r0;
+    const int64_t cnt = (n + BM - 1) / BM * a.n_tiles;
+    const int64_t tincl = wave_incl_scan(cnt);
+    const uint64_t hit = __ballot(gi < a.G && cnt > 0 && tbase + tincl > tile);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const int64_t u = tile - (tbase + __shfl(tincl - cnt, l, 64));   // tile within the group
+      const int64_t g0 = __shfl(r0, l, 64), gn = __shfl(n, l, 64);
+      const int m = (int)((gn + BM - 1) / BM);
+      const int b = max(1, (100 * m + kBlockTarget / 2) / kBlockTarget);   // round(m / 5.66)
+      const int q = m / b, rr = m % b;                // rr blocks of q + 1 m-tiles, then q-tile blocks
+      const int64_t big = (int64_t)rr * (q + 1) * a.n_tiles;
+      int gm, mstart;
+      int64_t v;
+      if (u < big) {
+        const int k = (int)(u / ((int64_t)(q + 1) * a.n_tiles));
+        gm = q + 1;
+        mstart = k * (q + 1);
+        v = u - (int64_t)k * (q + 1) * a.n_tiles;
+      } else {
+        const int k = (int)((u - big) / ((int64_t)q * a.n_tiles));
+        gm = q;
+        mstart = rr * (q + 1) + k * q;
+        v = u - big - (int64_t)k * q * a.n_tiles;
       }
+      const int mloc = mstart + (int)(v % gm);
+      r.g = c + l;
+      r.nt = (int)(v / gm);
+      r.m0 = g0 + (int64_t)mloc * BM;
+      r.rows = (int)min<int64_t>(BM, gn - (int64_t)mloc * BM);
+      break;
     }
     rbase += __shfl(rincl, 63, 64);
     tbase += __shfl(tincl, 63, 64);
   }
-  if (total) *total = tbase;
   // the results are wavefront-uniform: keep them in scalar registers
-  auto u64 = [](int64_t v) -> int64_t {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-  };
   r.g = __builtin_amdgcn_readfirstlane(r.g);
-  r.row0 = u64(r.row0);
-  r.row1 = u64(r.row1);
-  r.tile0 = u64(r.tile0);
-  if (total) *total = u64(*total);
+  r.nt = __builtin_amdgcn_readfirstlane(r.nt);
+  r.m0 = wave_u64(r.m0);
+  r.rows = __builtin_amdgcn_readfirstlane(r.rows);
   return r;
 }
 
