@@ -6,8 +6,9 @@
 // the expert matmuls, fed by the group-aware quantisation kernels.
 //
 // Same pipeline as the bf16 forward kernel (persistent tiles from the device
-// group prefix, 256 x 256 tiles, 8 wavefronts, direct-to-LDS loads in 64-byte
-// rows, stages loaded three ahead), with K staged 64 codes at a time and
+// group prefix, 256 x 256 tiles, 8 wavefronts in a ping-pong schedule,
+// direct-to-LDS loads in 64-byte rows, stages loaded three ahead), with K
+// staged 64 codes at a time and
 // v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds row l % 32 and, for the
 // lane group g = l / 32, codes k = 16g..16g+15 and 32+16g..32+16g+15 of the
 // stage plus the scale of k-block g (layout verified on the hardware).
@@ -309,34 +310,49 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
         sl.issue(buf, wsb, xsb, kt);
       }
     };
-    // Step kt: stage kt (in cur) has landed once at most the loads of stages
-    // kt + 1 and kt + 2 are outstanding; after the barrier its fragments are
-    // read and multiplied, and stage kt + 3 goes into the buffer of stage
-    // kt - 1.  No register prefetch of fragments here (32 x 32 accumulators
-    // leave no room at two wavefronts per SIMD); the other wavefront on the
-    // SIMD covers the LDS latency.
-    Frags fr;
-    auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
-      MOE_WAIT_VMCNT(2 * LPW_MX);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    // Ping-pong schedule: step kt is a memory phase (issue stage kt + 3 into
+    // the buffer of stage kt - 1, read stage kt's fragments and scales), a
+    // barrier, and a compute phase (its 8 scaled MFMAs from registers).  The
+    // second wavefront of every SIMD runs one barrier behind the first, so
+    // one of the two issues MFMAs while the other reads LDS.  Every barrier
+    // is preceded by this wavefront's wait for the stage the wavefronts
+    // past it will read: stage kt before the memory phase, stage kt + 1
+    // (and this step's LDS reads) before the compute phase.
+    const bool second = wave_id() >= NWAVE / 2;
+    auto barrier = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_barrier" ::: "memory");
-      issue(lbuf, kt + 3);
-      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
-      mma(fr, acc);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
-      const int after = min(2, nk - 1 - kt);
-      if (after >= 2) {
+    // wait until at most n stages' loads of this wavefront are in flight
+    auto wait_stages = [&](int n) {
+      if (n >= 2) {
         MOE_WAIT_VMCNT(2 * LPW_MX);
-      } else if (after == 1) {
+      } else if (n == 1) {
         MOE_WAIT_VMCNT(LPW_MX);
       } else {
         MOE_WAIT_VMCNT(0);
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      asm volatile("s_barrier" ::: "memory");
+    };
+    Frags fr;
+    auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+      MOE_WAIT_VMCNT(2 * LPW_MX);
+      barrier();
+      issue(lbuf, kt + 3);
+      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
+      MOE_WAIT_VMCNT(2 * LPW_MX);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      barrier();
+      mma(fr, acc);
+    };
+    auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+      wait_stages(min(2, nk - 1 - kt));
+      barrier();
       if (kt + 3 < nk) issue(lbuf, kt + 3);
       read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
+      wait_stages(min(2, nk - 2 - kt));
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (!(second && kt == nk - 1)) barrier();   // evens the two halves' barrier counts
       mma(fr, acc);
     };
 
@@ -344,6 +360,10 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     issue(b0, 0);
     if (nk > 1) issue(b1, 1);
     if (nk > 2) issue(b2, 2);
+    if (second) {   // the half-step offset; stage 0 must have landed before it
+      wait_stages(min(2, nk - 1));
+      barrier();
+    }
     int kt = 0;
     for (; kt + 7 <= nk; kt += 4) {   // every step of the group issues a stage (kt + 6 < nk)
       step_fast(b0, b3, kt);
