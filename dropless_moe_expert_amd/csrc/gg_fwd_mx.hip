@@ -12,8 +12,13 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4: lane l holds row l % 32 and, for the
 // lane group g = l / 32, codes k = 16g..16g+15 and 32+16g..32+16g+15 of the
 // stage plus the scale of k-block g (layout verified on the hardware).
-// Each stage also carries its scales: every row's two scale bytes arrive by
-// a 2-byte direct load into one LDS word.  Four stages of 34 KB fit LDS.
+// Each stage also carries its weight rows' scales: a row's two scale bytes
+// arrive by a 2-byte direct load into one LDS word.  The activation rows'
+// scales travel 8 stages at a time (a row's 16 bytes for 512 codes are
+// contiguous in memory), spread over the loads of the previous 8 stages into
+// one of three 8 KB LDS areas: one 2-byte load per row and stage, each from
+// its own row, had cost 13 % of the gate/up GEMM's time.  Four stages of
+// 33 KB and the three scale areas fit LDS (156 KB).
 #include "gg_pipeline.h"
 
 namespace moe {
@@ -25,10 +30,16 @@ constexpr int WTM = BM / WM;                   // 64 x 128 per wavefront
 constexpr int LPW = (BM + BN) / 16 / NWAVE;    // direct row loads per wavefront and stage (4)
 namespace mx {
 
-constexpr int SC_W = 2 * XOFF;                  // W scale words [BN], then X scale words [BM]
-constexpr int SC_X = SC_W + BN * 4;
-constexpr int MSTAGE = SC_X + BM * 4;           // 34 KB
-constexpr int LPW_MX = LPW + 1;                 // per wavefront and stage: 4 row loads + 1 scale load
+constexpr int SC_W = 2 * XOFF;                  // W scale words [BN]
+constexpr int MSTAGE = SC_W + BN * 4;           // 33 KB
+constexpr int LPW_MX = LPW + 1;                 // per wavefront and stage: the row loads + 1 scale load
+// X scale areas: area c % 3 holds chunk c (stages 8c..8c+7); piece p (rows
+// 32p..32p+31) at 1 KB p; in it, the word of lane t = 64 (w % 4) + l holds
+// bytes 2 (t % 8) and 2 (t % 8) + 1 of row 32p + t / 8's 16 bytes, i.e. the
+// two scales of stage 8c + t % 8
+constexpr int XCH = 8;
+constexpr int XCH_BYTES = 8 * 1024;
+constexpr int NXCH = 3;
 constexpr int MTN = WTN / 32, MTM = WTM / 32;   // 4 x 2 subtiles of 32 x 32
 // packed weights: per (expert, n-tile, stage) 16 KB of codes in LDS slot
 // order, then the 256 rows' scale words (bytes 2kt, 2kt + 1 of each row's
@@ -36,24 +47,38 @@ constexpr int MTN = WTN / 32, MTM = WTM / 32;   // 4 x 2 subtiles of 32 x 32
 constexpr int PK_CODES = BN * ROWB;
 constexpr int PK_STAGE = PK_CODES + BN * 4;     // 17 KB
 
-
-
-// one scale word per row: lane l of wavefront w loads row 64 * (w % 4) + l of
-// W (w < 4) or X (w >= 4)
-struct ScaleRow {
-  uint32_t off;
+// One 2-byte direct load per wavefront and stage.  Wavefront w < 4, lane l:
+// the two scale bytes of stage kt of W row 64 w + l into the low half of its
+// LDS word.  Wavefront w >= 4: piece kt % 8 of X scale chunk kt / 8 + 1.
+// Chunk c + 1's first piece goes out with stage 8c, while stage 8c - 4 is
+// read; its area, (c + 1) % 3, last held chunk c - 2 (stages up to 8c - 9).
+// Both kinds are one instruction with operands chosen per wavefront, so the
+// loop has no branch on the wavefront's role.
+struct Scales {
+  uint32_t woff;        // W: the row's scale offset (packed: within the stage block)
+  uint32_t xt2;         // X: this lane's two bytes' offset within a row's 16, 2 (t % 8)
+  int xr;               // X: its row within a piece, t / 8
+  int rows;             // valid rows of the tile
+  int t;                // lane within the four wavefronts of its kind
   bool is_w;
-  template <typename WRow, typename XRow>
-  __device__ __forceinline__ void init(int64_t ld, WRow wrow, XRow xrow) {
+  template <typename WRow>
+  __device__ __forceinline__ void init(int64_t ld, WRow wrow, int rows_) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     is_w = wave < 4;
-    const int r = (wave & 3) * 64 + lane;
-    off = (uint32_t)((is_w ? wrow(r) : xrow(r)) * ld);
+    t = (wave & 3) * 64 + lane;
+    woff = (uint32_t)(wrow(t) * ld);
+    xt2 = 2u * (uint32_t)(t & 7);
+    xr = t >> 3;
+    rows = rows_;
   }
-  __device__ __forceinline__ void issue(uint8_t* buf, const uint8_t* wsb, const uint8_t* xsb, int kt) const {
-    const int wave = wave_id();
-    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + (is_w ? SC_W : SC_X) + (wave & 3) * 256;
-    const uint8_t* base = (is_w ? wsb : xsb) + kt * 2;
+  // this lane's offset for piece p of X chunk c: bytes past a row's end
+  // re-read its first two (never used), so no load leaves the row
+  __device__ __forceinline__ uint32_t xoff(int p, int c, int lds_b) const {
+    const uint32_t rb = (uint32_t)(min(32 * p + xr, rows - 1) * lds_b);
+    const uint32_t cb = 16u * (uint32_t)c;
+    return xt2 + cb < (uint32_t)lds_b ? rb + cb + xt2 : rb;
+  }
+  __device__ __forceinline__ void load(uint32_t l0, uint32_t off, const uint8_t* base) const {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -61,20 +86,34 @@ struct ScaleRow {
         :
         : "s"(l0), "v"(off), "s"(base)
         : "memory", "m0");
-  }  // packed weights: the W rows' scale words lie after the stage's codes; the
-  // X rows' scales are loaded as the aligned word holding the stage's bytes
-  // (row strides K/32 are multiples of 4), so both are plain dword loads
-  __device__ __forceinline__ void issue_packed(uint8_t* buf, const uint8_t* wstage, const uint8_t* xsb, int kt) const {
-    const int wave = wave_id();
-    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + (is_w ? SC_W : SC_X) + (wave & 3) * 256;
-    const uint8_t* base = is_w ? wstage : xsb + (kt >> 1) * 4;
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %1, %2"
-        :
-        : "s"(l0), "v"(off), "s"(base)
-        : "memory", "m0");
+  }
+  // the scale load that goes with stage s; wsrc: stage s's W scale source
+  // (packed: the stage block, else the expert's scales + 2 s)
+  __device__ __forceinline__ void issue(uint8_t* buf, uint8_t* xch, const uint8_t* wsrc, const uint8_t* xsb, int s,
+                                        int lds_b) const {
+    const int c = s / XCH + 1, p = s % XCH;
+    const uint32_t wq = (uint32_t)(wave_id() & 3) * 256;   // wavefront-uniform
+    const uint32_t wl0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + SC_W + wq;
+    const uint32_t xl0 = (uint32_t)(uintptr_t)(lds_ptr_t)xch + (c % NXCH) * XCH_BYTES + p * 1024 + wq;
+    // the role is wavefront-uniform: keep the choice of LDS and global base
+    // in scalar registers (the loads' m0 and base operands must be scalars)
+    const bool w = __builtin_amdgcn_readfirstlane((int)is_w) != 0;
+    const uint64_t base = (uint64_t)(uintptr_t)(w ? wsrc : xsb);
+    const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    // the offset is chosen per lane (threads < 256 are the W wavefronts), a
+    // plain select: as a choice on the uniform role the compiler branched
+    // around the X offset arithmetic and ran out of registers
+    const uint32_t xof = xoff(p, c, lds_b);
+    load(__builtin_amdgcn_readfirstlane(w ? wl0 : xl0), threadIdx.x < 256 ? woff : xof,
+         reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)bhi << 32) | blo)));
+  }
+  // chunk 0, before stage 0: all eight loads by every wavefront (the W
+  // wavefronts write the same words as the X ones)
+  __device__ __forceinline__ void issue_first(uint8_t* xch, const uint8_t* xsb, int lds_b) const {
+    const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)xch + (uint32_t)(wave_id() & 3) * 256;
+#pragma unroll
+    for (int p = 0; p < XCH; ++p) load(l0 + p * 1024, xoff(p, 0, lds_b), xsb);
   }
 };
 
@@ -89,17 +128,15 @@ __device__ __forceinline__ i32x8_t ld32(const uint8_t* rowp, int slot_lo, int sl
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-// xsh: bit offset of the stage's two X scale bytes in their LDS word (16
-// when the packed path loaded the aligned word holding the previous stage's
-// bytes first)
-__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xsh = 0) {
+// xsw: the words of stage kt in its X scale area, (const uint32_t*)area +
+// kt % 8; row r's is at xsw[256 (r / 32) + 8 (r % 32)]
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, const uint32_t* xsw) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r32 = lane & 31, g = lane >> 5;
   const int sw = swz_row<1>(r32);                // rows are 32-aligned bases + r32
   const int s_lo = g ^ sw, s_hi = (2 + g) ^ sw;
   const uint32_t* scw = reinterpret_cast<const uint32_t*>(buf + SC_W);
-  const uint32_t* scx = reinterpret_cast<const uint32_t*>(buf + SC_X);
 #pragma unroll
   for (int i = 0; i < MTN; ++i) {
     const int row = wn * WTN + i * 32 + r32;
@@ -110,7 +147,7 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& fr, int xs
   for (int j = 0; j < MTM; ++j) {
     const int row = wm * WTM + j * 32 + r32;
     fr.x[j] = ld32(buf + XOFF + row * ROWB, s_lo, s_hi);
-    fr.xs[j] = (int)((scx[row] >> (xsh + 8 * g)) & 0xFF);
+    fr.xs[j] = (int)((xsw[(row >> 5) * 256 + r32 * 8] >> (8 * g)) & 0xFF);
   }
 }
 
@@ -231,6 +268,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b1[MSTAGE];
   __shared__ __align__(1024) uint8_t b2[MSTAGE];
   __shared__ __align__(1024) uint8_t b3[MSTAGE];
+  __shared__ __align__(1024) uint8_t xch[NXCH * XCH_BYTES];   // X scales, 8 stages per area
 
   if (blockIdx.x == 0 && threadIdx.x < 64) {
     bool neg = false;
@@ -274,14 +312,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     };
     Rows<BM, NWAVE, 1> xl;
     Rows<BN, NWAVE, 1> wl;
-    ScaleRow sl;
+    Scales sl;
     xl.init(lda_b, xrow);
-    sl.init(lds_b, wrow, xrow);
+    sl.init(lds_b, wrow, rows);
     if constexpr (PACKED) {
       const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
       for (int i = 0; i < Rows<BN, NWAVE, 1>::N; ++i) wl.off[i] = (uint32_t)(((i * NWAVE + wave) * 64 + lane) * 16);
-      if (sl.is_w) sl.off = (uint32_t)(PK_CODES + ((wave & 3) * 64 + lane) * 4);
+      sl.woff = (uint32_t)(PK_CODES + sl.t * 4);
     } else {
       wl.init(lda_b, wrow);
     }
@@ -300,15 +338,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    auto issue = [&](uint8_t* buf, int kt) {
-      const uint8_t* wstage = wbase + (int64_t)kt * wstride;
+    auto issue = [&](uint8_t* buf, int s) {
+      const uint8_t* wstage = wbase + (int64_t)s * wstride;
       wl.issue(buf, wstage);
-      xl.issue(buf + XOFF, xbase + kt * ROWB);
-      if constexpr (PACKED) {
-        sl.issue_packed(buf, wstage, xsb, kt);
-      } else {
-        sl.issue(buf, wsb, xsb, kt);
-      }
+      xl.issue(buf + XOFF, xbase + s * ROWB);
+      sl.issue(buf, xch, PACKED ? wstage : wsb + 2 * s, xsb, s, (int)lds_b);
+    };
+    auto xscales = [&](int kt) {
+      return reinterpret_cast<const uint32_t*>(xch + (kt / XCH % NXCH) * XCH_BYTES) + kt % XCH;
     };
     // Ping-pong schedule: step kt is a memory phase (issue stage kt + 3 into
     // the buffer of stage kt - 1, read stage kt's fragments and scales), a
@@ -336,11 +373,11 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     };
     Frags fr;
     auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
-      MOE_WAIT_VMCNT(2 * LPW_MX);
+      wait_stages(2);
       barrier();
       issue(lbuf, kt + 3);
-      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
-      MOE_WAIT_VMCNT(2 * LPW_MX);
+      read_frags(cur, fr, xscales(kt));
+      wait_stages(2);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       barrier();
       mma(fr, acc);
@@ -349,7 +386,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
       wait_stages(min(2, nk - 1 - kt));
       barrier();
       if (kt + 3 < nk) issue(lbuf, kt + 3);
-      read_frags(cur, fr, PACKED ? 16 * (kt & 1) : 0);
+      read_frags(cur, fr, xscales(kt));
       wait_stages(min(2, nk - 2 - kt));
       __builtin_amdgcn_s_waitcnt(0xC07F);
       if (!(second && kt == nk - 1)) barrier();   // evens the two halves' barrier counts
@@ -357,6 +394,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     };
 
     __syncthreads();
+    sl.issue_first(xch, xsb, (int)lds_b);
     issue(b0, 0);
     if (nk > 1) issue(b1, 1);
     if (nk > 2) issue(b2, 2);
