@@ -437,7 +437,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
   for (int j = 0; j < TM; ++j) kx[j] = XOFF + kfrag_off(wm * WTM + 16 * j);
   const bool second = wave_id() >= NWAVE / 2;
 
-  for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+  // Tiles come largest group first, dealt to the workers in rounds whose
+  // direction alternates (worker w takes tile w of even rounds and tile
+  // grid - 1 - w of odd ones), so the workers that took the longest tiles of
+  // one round take the shortest of the next; consecutive tiles still share
+  // an XCD.
+  for (int64_t r = 0;; ++r) {
+    const int64_t tile = r * gridDim.x + ((r & 1) ? (int64_t)gridDim.x - 1 - wid : wid);
+    if (tile >= total) break;   // every later round starts past it
     const int rank = (int)(tile / per_group), rem = (int)(tile - (int64_t)rank * per_group);
     const int g = gi.tpre[rank];
     const int pt = rem / a.n_tiles, qt = rem - pt * a.n_tiles;
