@@ -38,6 +38,7 @@
 // Measured on random operands, MI355X sustains about 70 % of its nominal
 // bf16 MFMA rate for this fragment pattern even with no memory traffic
 // (power-limited clocks); every byte moved lowers that further.
+#include <atomic>
 #include <type_traits>
 
 #include "gg_pipeline.h"
@@ -413,6 +414,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
 // k-elements of the activation fragments.  Empty groups store zeros.
 constexpr int WG_STAGES = 4;
 
+// Tile queues of the weight-gradient kernel, per launch slot (the host hands
+// out the slots in turn, so launches in flight together use different
+// ones): kQueues tile counters, then the number of workgroups that have
+// finished; the last workgroup to finish zeroes them all for the slot's next
+// launch.  Zero at load time.
+constexpr int kQueues = 8, kSlots = 64;
+__device__ uint32_t g_wgrad_sched[kSlots][kQueues + 1];
+
 template <int OUT>
 __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[STAGE];
@@ -424,9 +433,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
 
   const int P = a.M, Q = a.N;
   const int per_group = a.p_tiles * a.n_tiles;
-  const int64_t total = (int64_t)a.G * per_group;
   const int64_t lda = (int64_t)P * 2, ldb = (int64_t)Q * 2;
-  const int wid = worker_id();
   const int lane = threadIdx.x & 63;
   int wn, wm;
   wave_pos(wn, wm);
@@ -437,15 +444,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
   for (int j = 0; j < TM; ++j) kx[j] = XOFF + kfrag_off(wm * WTM + 16 * j);
   const bool second = wave_id() >= NWAVE / 2;
 
-  // Tiles come largest group first, dealt to the workers in rounds whose
-  // direction alternates (worker w takes tile w of even rounds and tile
-  // grid - 1 - w of odd ones), so the workers that took the longest tiles of
-  // one round take the shortest of the next; consecutive tiles still share
-  // an XCD.
-  for (int64_t r = 0;; ++r) {
-    const int64_t tile = r * gridDim.x + ((r & 1) ? (int64_t)gridDim.x - 1 - wid : wid);
-    if (tile >= total) break;   // every later round starts past it
-    const int rank = (int)(tile / per_group), rem = (int)(tile - (int64_t)rank * per_group);
+  // one tile: rem-th of the group of rank `rank` (groups ranked largest first)
+  auto process = [&](int rank, int rem) {
     const int g = gi.tpre[rank];
     const int pt = rem / a.n_tiles, qt = rem - pt * a.n_tiles;
     const int p0 = pt * BM, q0 = qt * BN;
@@ -557,6 +557,46 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
     } else {
       run(std::integral_constant<int, 0>());
     }
+  };
+
+  // Dynamic tile queues.  Queue q holds the groups of rank k nq + q for even
+  // k and k nq + nq - 1 - q for odd k (k = 0, 1, ...: a snake over the
+  // ranks, so every queue gets a share of large and small groups), each
+  // group's tiles in a row, largest group first.  A workgroup takes tiles
+  // from queue blockIdx % nq - its XCD's, as blocks are dealt round-robin
+  // to the 8 XCDs, so a group's tiles share that XCD's L2 - and, once that
+  // is empty, from the others, so no workgroup idles while tiles remain.
+  // Taking a tile is one atomic increment of the queue's counter.
+  __shared__ int32_t s_tile[2];
+  const int nq = min(kQueues, (int)gridDim.x);
+  const int myq = (int)(blockIdx.x % nq);
+  uint32_t* ctr = g_wgrad_sched[a.sched_slot];
+  int parity = 0;
+  for (int qq = 0; qq < nq; ++qq) {
+    const int q = (myq + qq) % nq;
+    // groups in queue q: one per full round of nq ranks, plus one from the
+    // last, partial round if its direction reaches q
+    const int rounds = a.G / nq, left = a.G % nq;
+    const int ngroups = rounds + (((rounds & 1) ? nq - 1 - q : q) < left ? 1 : 0);
+    const int64_t ntiles = (int64_t)ngroups * per_group;
+    for (;;) {
+      // thread 0 takes the next tile; the two slots alternate, so a slot is
+      // rewritten only after the barrier that follows every thread's read
+      if (threadIdx.x == 0) s_tile[parity] = (int32_t)atomicAdd(&ctr[q], 1u);
+      __syncthreads();
+      const int64_t t = s_tile[parity];
+      parity ^= 1;
+      if (t >= ntiles) break;
+      const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
+      process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
+    }
+  }
+  if (threadIdx.x == 0) {
+    // every tile this workgroup took is done; the last workgroup resets
+    if (atomicAdd(&ctr[kQueues], 1u) == gridDim.x - 1) {
+      for (int q = 0; q < kQueues; ++q) atomicExch(&ctr[q], 0u);
+      atomicExch(&ctr[kQueues], 0u);
+    }
   }
 }
 
@@ -663,7 +703,9 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
 
 // bf16, ragged-K: the weight gradients
 moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s) {
+  static std::atomic<uint32_t> next_slot{0};
   GGArgs b = a;
+  b.sched_slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % fwd::kSlots);
   b.n_tiles = (a.N + fwd::BN - 1) / fwd::BN;
   b.p_tiles = (a.M + fwd::BM - 1) / fwd::BM;
   const int64_t max_tiles = (int64_t)a.G * b.n_tiles * b.p_tiles;

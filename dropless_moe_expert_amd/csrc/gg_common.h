@@ -21,6 +21,7 @@ struct GGArgs {
   int G, M, N, K;
   int n_tiles;             // tiles along n (ragged-M) / q (ragged-K)
   int p_tiles;             // ragged-K: tiles along p (rows of C[g])
+  int sched_slot;          // ragged-K: the launch's slot of tile-queue counters
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

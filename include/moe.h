@@ -138,6 +138,12 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
  * ragged = MOE_RAGGED_K (weight gradient; contraction over a group's rows):
  *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
  *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
+ *   Its workgroups take tiles from counters in the library's own device
+ *   memory (64 slots handed out in turn, each zeroed again by the call that
+ *   used it), so up to 64 such calls may be in flight on one GPU at once;
+ *   a captured call keeps its slot on every replay, so one graph must not
+ *   be replayed on two streams concurrently.  Each tile is computed by one
+ *   workgroup in a fixed order: results are bitwise reproducible.
  * dtype = MOE_DTYPE_MXFP8 (RAGGED_M, B_NK or B_PACKED): A, B are E4M3 codes
  *   with E8M0 scales A_scale [m_cap, K/32], B_scale [G, N, K/32] (value =
  *   code * 2^(scale - 127)); accumulation fp32, output bf16.  With

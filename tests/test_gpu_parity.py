@@ -238,6 +238,36 @@ def test_grouped_gemm_wgrad(ops, P, Q):
         assert torch.all(out[g] == 0)
 
 
+def test_grouped_gemm_wgrad_queues(ops):
+    # The weight-gradient kernel takes tiles from per-launch counters that its
+    # last workgroup resets: consecutive launches of different shapes (a grid
+    # of fewer than 8 workgroups, then many groups of skewed sizes, so
+    # workgroups take tiles from other queues) must each match the oracle, and
+    # a repeated launch must match bit for bit.
+    rng = np.random.default_rng(97)
+    cases = [(8, 8, np.array([3, 0, 40], np.int32)),
+             (136, 264, np.concatenate([[900, 0, 0], rng.integers(0, 120, 37)]).astype(np.int32)),
+             (8, 8, np.array([3, 0, 40], np.int32))]
+    first = None
+    for i, (P, Q, sizes) in enumerate(cases):
+        say("gg wgrad queues", i, P, Q, sizes.size)
+        G, M = sizes.size, int(sizes.sum())
+        r = np.random.default_rng(P + Q + G)
+        X, Y = bf16(r, M + 3, P), bf16(r, M + 3, Q)
+        ref = orc.grouped_wgrad(X[:M], Y[:M], sizes)
+        out = ops.grouped_gemm_wgrad(dev(X), dev(Y), dev(torch.from_numpy(sizes)))
+        again = ops.grouped_gemm_wgrad(dev(X), dev(Y), dev(torch.from_numpy(sizes)))
+        torch.cuda.synchronize()
+        assert max_rel_err(out, ref) <= BF16_TOL
+        assert torch.equal(out, again)
+        for g in np.nonzero(sizes == 0)[0]:
+            assert torch.all(out[g] == 0)
+        if i == 0:
+            first = out
+        if i == 2:
+            assert torch.equal(out, first)
+
+
 # ------------------------------------------------------------------- MXFP8
 
 @pytest.mark.parametrize("R,C", [(300, 256), (1, 32), (1000, 7168 // 4)])
