@@ -127,7 +127,127 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   }
 }
 
+// Transposed axis 1: one thread per (32-row block p, 8-column piece), as
+// above, but each column's 32 codes leave as 32 consecutive bytes of its qT
+// row.  Grouped (group_sizes != NULL): block p lies in the 64-aligned padded
+// layout (kpad = padded group starts); blocks past a group's rows store zero
+// codes and scale 0.  Batched (NULL): G batches of `rows` rows, one group each.
+__global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                                         const int32_t* __restrict__ group_sizes, int G,
+                                                         int64_t k_cap, uint8_t* __restrict__ qT,
+                                                         uint8_t* __restrict__ scaleT, uint32_t* flag) {
+  extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
+  int64_t* roff = sh;
+  int64_t* kpad = sh + G + 1;
+  const bool grouped = group_sizes != nullptr;
+  if (grouped) {
+    if (threadIdx.x == 0) {
+      int64_t o = 0, k = 0;
+      bool neg = false, over = false;
+      for (int g = 0; g < G; ++g) {
+        int64_t sz = group_sizes[g];
+        if (sz < 0) { neg = true; sz = 0; }
+        if (o + sz > rows) { over = true; sz = rows - o; }
+        roff[g] = o;
+        kpad[g] = k;
+        o += sz;
+        k += (sz + 63) / 64 * 64;
+      }
+      roff[G] = o;
+      kpad[G] = k;
+      if (neg) raise_flag(flag, MOE_FLAG_NEGATIVE_SIZE);
+      if (over) raise_flag(flag, MOE_FLAG_ROWS_OVER_CAP);
+    }
+    __syncthreads();
+  }
+  const int64_t bpg = rows / 32;   // batched: blocks per batch
+  const int64_t nblk = grouped ? kpad[G] / 32 : (int64_t)G * bpg;
+  const int npc = cols / 8;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * npc;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = idx / npc;
+    const int c8 = (int)(idx - p * npc) * 8;
+    int64_t r0, ldq;
+    int n;
+    uint8_t* qb;   // the block's first code in column c8's qT row
+    uint8_t* sb;   // its scale in column c8's scaleT row
+    if (grouped) {
+      int lo = 0, hi = G - 1;   // last g with kpad[g] <= 32 p
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (kpad[mid] <= 32 * p) lo = mid; else hi = mid - 1;
+      }
+      const int64_t b = p - kpad[lo] / 32;
+      r0 = roff[lo] + 32 * b;
+      n = (int)max((int64_t)0, min((int64_t)32, roff[lo + 1] - r0));
+      ldq = k_cap;
+      qb = qT + (int64_t)c8 * k_cap + 32 * p;
+      sb = scaleT + (int64_t)c8 * (k_cap / 32) + p;
+    } else {
+      const int64_t g = p / bpg, b = p - g * bpg;
+      r0 = g * rows + 32 * b;
+      n = 32;
+      ldq = rows;
+      qb = qT + g * cols * rows + (int64_t)c8 * rows + 32 * b;
+      sb = scaleT + g * cols * bpg + (int64_t)c8 * bpg + b;
+    }
+    float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < n; ++i) {
+      float f[8];
+      unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], fabsf(f[j]));
+    }
+    int e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = mx_exponent(amax[j]);
+      sb[(int64_t)j * (ldq / 32)] = (uint8_t)(e[j] + 127);
+    }
+    // codes of rows 4w..4w+3 of column j form word w of that column's 32 bytes
+    uint32_t cw[8][8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float f[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * w + i < n) {
+          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + 4 * w + i) * cols + c8), f[i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[i][j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        cw[j][w] = cvt4_e4m3(scale_pow2(f[0][j], e[j]), scale_pow2(f[1][j], e[j]), scale_pow2(f[2][j], e[j]),
+                             scale_pow2(f[3][j], e[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint4* dst = reinterpret_cast<uint4*>(qb + (int64_t)j * ldq);
+      dst[0] = make_uint4(cw[j][0], cw[j][1], cw[j][2], cw[j][3]);
+      dst[1] = make_uint4(cw[j][4], cw[j][5], cw[j][6], cw[j][7]);
+    }
+  }
+}
+
 }  // namespace moe
+
+extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int64_t rows, int32_t cols,
+                                                         const int32_t* group_sizes, int32_t G, int64_t k_cap,
+                                                         uint8_t* qT, uint8_t* scaleT, uint32_t* flag,
+                                                         hipStream_t s) {
+  const int64_t cap = (int64_t)moe_host::device_cu_count() * 16;
+  const int64_t nblk = group_sizes ? k_cap / 32 : (int64_t)G * (rows / 32);   // an upper bound when grouped
+  const int64_t work = nblk * (cols / 8);
+  if (work == 0) return MOE_OK;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
+  const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
+  hipLaunchKernelGGL(moe::mx_quant_t_kernel, dim3((unsigned)blocks), dim3(256), shmem, s, x, rows, cols, group_sizes,
+                     G, k_cap, qT, scaleT, flag);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 extern "C" moe_status_t mxfp8_group_quantize_launch(const uint16_t* x, int64_t rows, int32_t cols, int32_t axis,
                                                     const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,

@@ -33,7 +33,8 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
     "moe_permute_mxfp8", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
     "moe_combine_backward",
-    "moe_swiglu_backward", "mxfp8_group_quantize", "moe_pack_weights_bytes", "moe_pack_weights",
+    "moe_swiglu_backward", "mxfp8_group_quantize", "mxfp8_quantize_transposed", "moe_pack_weights_bytes",
+    "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
     # measurement only (include/moe_bench.h)
     "moe_bench_mfma_flops", "moe_bench_mfma_ceiling",
@@ -79,6 +80,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_combine_backward": (ctypes.c_int, [P, P, P, P, i64, i32, i32, P, P, P]),
             "moe_swiglu_backward": (ctypes.c_int, [P, P, i64, i32, P, i32, P, P]),
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
+            "mxfp8_quantize_transposed": (ctypes.c_int, [P, i64, i32, P, i32, i64, P, P, P, P]),
             "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
@@ -389,6 +391,35 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_sizes: Optional[torch.T
     G = 0 if group_sizes is None else group_sizes.numel()
     _check(lib().mxfp8_group_quantize(_ptr(x), rows, cols, axis, _ptr(group_sizes), G, _ptr(q), _ptr(s), _ptr(flag),
                                       _stream(dev)), "mxfp8_group_quantize")
+    return q, s
+
+
+def k_cap_for(m_cap: int, G: int) -> int:
+    """Positions per row of the grouped transposed layout: room for every
+    group starting 64-aligned."""
+    return (m_cap + 63 * G + 63) // 64 * 64
+
+
+def mxfp8_quantize_transposed(x: torch.Tensor, group_sizes: Optional[torch.Tensor] = None,
+                              flag: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Blocks of 32 down the columns, codes stored column-contiguous.
+    x [rows, cols] with group_sizes -> (qT uint8 [cols, k_cap], scaleT [cols, k_cap/32]);
+    x [G, rows, cols] without -> (qT [G, cols, rows], scaleT [G, cols, rows/32])."""
+    dev = _dev(x, group_sizes)
+    assert x.dtype == torch.bfloat16
+    if group_sizes is not None:
+        rows, cols = x.shape
+        G = group_sizes.numel()
+        k_cap = k_cap_for(rows, G)
+        q = torch.empty((cols, k_cap), dtype=torch.uint8, device=dev)
+        s = torch.empty((cols, k_cap // 32), dtype=torch.uint8, device=dev)
+    else:
+        G, rows, cols = x.shape
+        k_cap = 0
+        q = torch.empty((G, cols, rows), dtype=torch.uint8, device=dev)
+        s = torch.empty((G, cols, rows // 32), dtype=torch.uint8, device=dev)
+    _check(lib().mxfp8_quantize_transposed(_ptr(x), rows, cols, _ptr(group_sizes), G, k_cap, _ptr(q), _ptr(s),
+                                           _ptr(flag), _stream(dev)), "mxfp8_quantize_transposed")
     return q, s
 
 

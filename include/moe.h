@@ -266,6 +266,31 @@ moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols,
                                   const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,
                                   uint32_t* err_flag, void* stream);
 
+/* Transposed group-aware MXFP8 quantisation, for the operands of the MXFP8
+ * backward whose contraction runs down their rows (the weight gradients sum
+ * over a group's tokens; the data gradients contract the weights over their
+ * output axis): blocks of 32 run down each column as in axis 1 above,
+ * restarting at every group's first row, with the same scale rule, and each
+ * column's codes are stored contiguously, so the grouped GEMM reads them as
+ * K-contiguous rows (blog: group-aware MXFP8 quantisation, section "What
+ * specialized optimizations are required for dropless MoE?").
+ * group_sizes != NULL (activations, x bf16 [rows, cols], rows = m_cap):
+ *   group g's rows occupy positions [K_g, K_g + s_g) of every row of
+ *   qT uint8 [cols, k_cap], K_g = sum_{h<g} 64 * ceil(s_h / 64): groups
+ *   start 64-aligned, and positions up to K_g + 64 * ceil(s_g / 64) hold
+ *   zero codes (a block with no rows of the group has scale byte 0).  The
+ *   block at positions [K_g + 32 b, +32) has its scale at scaleT [cols,
+ *   k_cap / 32], column (K_g + 32 b) / 32.  Positions past the last group's
+ *   are not written.  k_cap % 64 == 0, k_cap >= rows + 63 G.
+ * group_sizes == NULL (weights, x bf16 [G, rows, cols], one group per
+ *   batch): qT [G, cols, rows], scaleT [G, cols, rows / 32]; rows % 64 == 0;
+ *   k_cap ignored.
+ * cols % 8 == 0; x, qT 16-byte aligned.  The data errors of the grouped
+ * kernels (negative sizes, sizes past rows) raise err_flag. */
+moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t cols, const int32_t* group_sizes,
+                                       int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint32_t* err_flag,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,7 @@ def lib():
                 "oracle_swiglu_backward": (None, [P, P, i64, i32, P]),
                 "oracle_grouped_dgrad_rows": (None, [P, P, P, i32, i32, i32, P, i64, P]),
                 "oracle_grouped_wgrad": (None, [P, P, P, i32, i32, i32, P, i32, P]),
+                "oracle_mx_grouped_wgrad": (None, [P, P, P, P, P, i32, i32, i32, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -234,6 +235,18 @@ def mx_grouped_gemm(Aq, As, Bq, Bs, group_sizes, swiglu: bool = False, rows=None
     out = np.zeros((r.size, nout), np.uint16)
     lib().oracle_mx_grouped_gemm_rows(_p(aq), _p(as_), _p(bq), _p(bs), _p(s), G, N, Kd, int(swiglu),
                                       _p(r), r.size, _p(out))
+    return out
+
+
+def mx_grouped_wgrad(Aq, As, Bq, Bs, group_sizes) -> np.ndarray:
+    """C[e] = bf16(sum over group e's rows of a[r]^T b[r]) -> [G, P, Q], from
+    operands quantised by mxfp8_quantize(axis=1) (codes [rows, P|Q], scales
+    [sum ceil(s/32), P|Q])."""
+    aq, as_, bq, bs = (_np(t, np.uint8) for t in (Aq, As, Bq, Bs))
+    s = _np(group_sizes, np.int32)
+    P, Q = aq.shape[1], bq.shape[1]
+    out = np.zeros((s.size, P, Q), np.uint16)
+    lib().oracle_mx_grouped_wgrad(_p(aq), _p(as_), _p(bq), _p(bs), _p(s), s.size, P, Q, _p(out))
     return out
 
 

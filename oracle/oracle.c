@@ -396,6 +396,37 @@ void oracle_mx_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const uin
     }
 }
 
+/* MXFP8 weight gradient [BLOG "What specialized optimizations are required  */
+/* for dropless MoE?": group-aware MXFP8 quantisation; "Optimization 1":     */
+/* MXFP8 block scaling].  Both operands quantised along their rows by the     */
+/* group-aware axis-1 rule above (codes [rows, P] and [rows, Q], scales       */
+/* [sum_e ceil(s_e/32), P] and [.., Q]); dequantise exactly, then the plain   */
+/* ragged contraction: C[e][p, q] = bf16(sum_{r in e} a[r, p] * b[r, q]).      */
+void oracle_mx_grouped_wgrad(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq, const uint8_t* Bs,
+                             const int32_t* sizes, int32_t G, int32_t P, int32_t Q, uint16_t* C)
+{
+    int64_t o = 0, pb = 0;
+    for (int e = 0; e < G; ++e) {
+        int64_t s = sizes[e];
+        uint16_t* out = C + (int64_t)e * P * Q;
+        #pragma omp parallel for schedule(static)
+        for (int p = 0; p < P; ++p) {
+            for (int q = 0; q < Q; ++q) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < s; ++i) {
+                    int64_t r = o + i, blk = pb + i / 32;
+                    double a = ldexp(oracle_e4m3_to_f64(Aq[r * P + p]), (int)As[blk * P + p] - 127);
+                    double b = ldexp(oracle_e4m3_to_f64(Bq[r * Q + q]), (int)Bs[blk * Q + q] - 127);
+                    acc += a * b;
+                }
+                out[(int64_t)p * Q + q] = oracle_f64_to_bf16(acc);
+            }
+        }
+        o += s;
+        pb += (s + 31) / 32;
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* S7: backward of the layer (training).  Derivatives of the forward above;   */
 /* each result is accumulated in fp64 and stored as bf16 (dw as fp32).        */

@@ -318,6 +318,48 @@ def test_mxfp8_quantize_axis1_grouped(ops):
     np.testing.assert_array_equal(s[: s_ref.shape[0]].cpu().numpy(), s_ref)
 
 
+def _to_transposed(q, s, sizes, k_cap):
+    """The oracle's axis-1 codes/scales laid out as mxfp8_quantize_transposed
+    stores them (groups 64-aligned along each column's row of positions); the
+    padding positions are zero codes and, for blocks with no rows, scale 0."""
+    C = q.shape[1]
+    qT = np.zeros((C, k_cap), np.uint8)
+    sT = np.zeros((C, k_cap // 32), np.uint8)
+    o = P = K = 0
+    for n in sizes:
+        n = int(n)
+        qT[:, K:K + n] = q[o:o + n].T
+        nb = (n + 31) // 32
+        sT[:, K // 32:K // 32 + nb] = s[P:P + nb].T
+        o, P, K = o + n, P + nb, K + (n + 63) // 64 * 64
+    return qT, sT, K
+
+
+def test_mxfp8_quantize_transposed(ops):
+    rng = np.random.default_rng(12)
+    # grouped: empty groups, short last blocks, a group of exactly 64 rows
+    sizes = np.array([0, 5, 64, 33, 0, 70, 1], np.int32)
+    M, C = int(sizes.sum()), 56
+    say("mx qT grouped", M, C)
+    x = inputs.to_bf16((rng.standard_normal((M + 7, C)) * 3).astype(np.float32))
+    q_ref, s_ref = orc.mxfp8_quantize(x[:M], 1, sizes)
+    qT, sT = ops.mxfp8_quantize_transposed(dev(x), dev(torch.from_numpy(sizes)))
+    torch.cuda.synchronize()
+    want_q, want_s, used = _to_transposed(q_ref, s_ref, sizes, qT.shape[1])
+    np.testing.assert_array_equal(qT[:, :used].cpu().numpy(), want_q[:, :used])
+    np.testing.assert_array_equal(sT[:, :used // 32].cpu().numpy(), want_s[:, :used // 32])
+    # batched (weights): G batches of 128 rows, each one group
+    G, R, C2 = 3, 128, 40
+    say("mx qT batched", G, R, C2)
+    w = inputs.to_bf16((rng.standard_normal((G, R, C2)) * 0.05).astype(np.float32))
+    qT, sT = ops.mxfp8_quantize_transposed(dev(w))
+    torch.cuda.synchronize()
+    for g in range(G):
+        q_ref, s_ref = orc.mxfp8_quantize(w[g], 1, np.array([R], np.int32))
+        np.testing.assert_array_equal(qT[g].cpu().numpy(), q_ref.T)
+        np.testing.assert_array_equal(sT[g].cpu().numpy(), s_ref.T)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_mxfp8(ops, swiglu):
     sizes = np.array([0, 300, 1, 0, 260], np.int32)

@@ -237,6 +237,37 @@ def test_mx_grouped_gemm_vs_torch_dequant(orc):
         o += s
 
 
+def test_mx_grouped_wgrad_vs_torch_dequant(orc):
+    # operands quantised down their rows, blocks restarting at every group
+    # (a 40-row group has a short second block); the contraction runs over
+    # each group's rows of the dequantised values; an empty group gives zeros
+    rng = np.random.default_rng(18)
+    sizes = np.array([40, 0, 7, 33], np.int32)
+    M, P, Q = int(sizes.sum()), 24, 40
+    A, B = _bf16(rng, M, P), _bf16(rng, M, Q, scale=0.2)
+    aq, as_ = orc.mxfp8_quantize(A, 1, sizes)
+    bq, bs = orc.mxfp8_quantize(B, 1, sizes)
+
+    def deq(q, s):
+        v = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        out = np.zeros_like(v)
+        o, pb = 0, 0
+        for n in sizes:
+            for i in range(n):
+                out[o + i] = v[o + i] * 2.0 ** (s[pb + i // 32].astype(np.float64) - 127)
+            o, pb = o + n, pb + (n + 31) // 32
+        return out
+
+    a, b = deq(aq, as_), deq(bq, bs)
+    C = orc.mx_grouped_wgrad(aq, as_, bq, bs, sizes)
+    o = 0
+    for e, n in enumerate(sizes):
+        assert_correctly_rounded(orc, C[e], a[o:o + n].T @ b[o:o + n])
+        if n == 0:
+            assert np.all(C[e] == 0)
+        o += n
+
+
 # --------------------------------------------------------------------------- backward
 
 def test_backward_steps_vs_numpy(orc):
