@@ -172,8 +172,16 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
     }
     if (d->m_cap == 0) return MOE_OK;
   } else if (d->ragged == MOE_RAGGED_K) {
-    if (d->dtype != MOE_DTYPE_BF16 || d->epilogue != MOE_EPI_NONE || C_aux) return MOE_ERR_UNSUPPORTED;
+    if (d->epilogue != MOE_EPI_NONE || C_aux) return MOE_ERR_UNSUPPORTED;
     if (d->M < 8 || d->M % 8) return MOE_ERR_UNSUPPORTED;
+    if (d->dtype == MOE_DTYPE_MXFP8) {
+      // operands laid out by mxfp8_quantize_transposed: K = its k_cap
+      if (d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
+      if (d->K < 64 || d->K % 64 || (int64_t)d->K < d->m_cap + 63 * (int64_t)d->G) return MOE_ERR_INVALID_ARG;
+      if (!A_scale || !B_scale) return MOE_ERR_INVALID_ARG;
+      if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (reinterpret_cast<uintptr_t>(B_scale) & 3u))
+        return MOE_ERR_ALIGNMENT;
+    }
   } else {
     return MOE_ERR_UNSUPPORTED;
   }

@@ -19,6 +19,8 @@
 // one of three 8 KB LDS areas: one 2-byte load per row and stage, each from
 // its own row, had cost 13 % of the gate/up GEMM's time.  Four stages of
 // 33 KB and the three scale areas fit LDS (156 KB).
+#include <atomic>
+
 #include "gg_pipeline.h"
 
 namespace moe {
@@ -71,12 +73,13 @@ struct Scales {
     xr = t >> 3;
     rows = rows_;
   }
-  // this lane's offset for piece p of X chunk c: bytes past a row's end
-  // re-read its first two (never used), so no load leaves the row
-  __device__ __forceinline__ uint32_t xoff(int p, int c, int lds_b) const {
+  // this lane's offset for piece p of X chunk c (rows lds_b bytes apart, xlim
+  // of them from the scales' base to the row's end): bytes past the row's
+  // end re-read its first two (never used), so no load leaves the row
+  __device__ __forceinline__ uint32_t xoff(int p, int c, int lds_b, int xlim) const {
     const uint32_t rb = (uint32_t)(min(32 * p + xr, rows - 1) * lds_b);
     const uint32_t cb = 16u * (uint32_t)c;
-    return xt2 + cb < (uint32_t)lds_b ? rb + cb + xt2 : rb;
+    return xt2 + cb < (uint32_t)xlim ? rb + cb + xt2 : rb;
   }
   __device__ __forceinline__ void load(uint32_t l0, uint32_t off, const uint8_t* base) const {
     asm volatile(
@@ -90,7 +93,7 @@ struct Scales {
   // the scale load that goes with stage s; wsrc: stage s's W scale source
   // (packed: the stage block, else the expert's scales + 2 s)
   __device__ __forceinline__ void issue(uint8_t* buf, uint8_t* xch, const uint8_t* wsrc, const uint8_t* xsb, int s,
-                                        int lds_b) const {
+                                        int lds_b, int xlim) const {
     const int c = s / XCH + 1, p = s % XCH;
     const uint32_t wq = (uint32_t)(wave_id() & 3) * 256;   // wavefront-uniform
     const uint32_t wl0 = (uint32_t)(uintptr_t)(lds_ptr_t)buf + SC_W + wq;
@@ -104,16 +107,16 @@ struct Scales {
     // the offset is chosen per lane (threads < 256 are the W wavefronts), a
     // plain select: as a choice on the uniform role the compiler branched
     // around the X offset arithmetic and ran out of registers
-    const uint32_t xof = xoff(p, c, lds_b);
+    const uint32_t xof = xoff(p, c, lds_b, xlim);
     load(__builtin_amdgcn_readfirstlane(w ? wl0 : xl0), threadIdx.x < 256 ? woff : xof,
          reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)bhi << 32) | blo)));
   }
   // chunk 0, before stage 0: all eight loads by every wavefront (the W
   // wavefronts write the same words as the X ones)
-  __device__ __forceinline__ void issue_first(uint8_t* xch, const uint8_t* xsb, int lds_b) const {
+  __device__ __forceinline__ void issue_first(uint8_t* xch, const uint8_t* xsb, int lds_b, int xlim) const {
     const uint32_t l0 = (uint32_t)(uintptr_t)(lds_ptr_t)xch + (uint32_t)(wave_id() & 3) * 256;
 #pragma unroll
-    for (int p = 0; p < XCH; ++p) load(l0 + p * 1024, xoff(p, 0, lds_b), xsb);
+    for (int p = 0; p < XCH; ++p) load(l0 + p * 1024, xoff(p, 0, lds_b, xlim), xsb);
   }
 };
 
@@ -262,6 +265,106 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
   }
 }
 
+// The loads of one tile's K stages (64 codes each): X rows (the MFMA's m
+// side), W rows or packed W blocks (its n side), their scales.
+template <bool PACKED>
+struct MxLoads {
+  Rows<BM, NWAVE, 1> xl;
+  Rows<BN, NWAVE, 1> wl;
+  Scales sl;
+  const uint8_t* xbase;   // stage 0 of the X rows
+  const uint8_t* wbase;   // stage 0 of the W block (packed) or of the W rows
+  int wstride;            // bytes from one stage's W block to the next
+  const uint8_t* xsb;     // the X rows' scales at stage 0
+  const uint8_t* wsb;     // unpacked: the W rows' scales at stage 0
+  int lds_b;              // scale bytes per row
+  int xlim;               // scale bytes from xsb to the end of an X row
+  __device__ __forceinline__ void issue(uint8_t* buf, uint8_t* xch, int s) const {
+    const uint8_t* wstage = wbase + (int64_t)s * wstride;
+    wl.issue(buf, wstage);
+    xl.issue(buf + XOFF, xbase + s * ROWB);
+    sl.issue(buf, xch, PACKED ? wstage : wsb + 2 * s, xsb, s, lds_b, xlim);
+  }
+};
+
+// One tile's K loop (nk >= 1 stages) into acc.
+template <bool PACKED>
+__device__ __forceinline__ void mx_k_loop(const MxLoads<PACKED>& ld, int nk, f32x16_t (&acc)[MTN][MTM], uint8_t* b0,
+                                          uint8_t* b1, uint8_t* b2, uint8_t* b3, uint8_t* xch) {
+  auto issue = [&](uint8_t* buf, int s) { ld.issue(buf, xch, s); };
+  auto xscales = [&](int kt) {
+    return reinterpret_cast<const uint32_t*>(xch + (kt / XCH % NXCH) * XCH_BYTES) + kt % XCH;
+  };
+  // Ping-pong schedule: step kt is a memory phase (issue stage kt + 3 into
+  // the buffer of stage kt - 1, read stage kt's fragments and scales), a
+  // barrier, and a compute phase (its 8 scaled MFMAs from registers).  The
+  // second wavefront of every SIMD runs one barrier behind the first, so
+  // one of the two issues MFMAs while the other reads LDS.  Every barrier
+  // is preceded by this wavefront's wait for the stage the wavefronts
+  // past it will read: stage kt before the memory phase, stage kt + 1
+  // (and this step's LDS reads) before the compute phase.
+  const bool second = wave_id() >= NWAVE / 2;
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // wait until at most n stages' loads of this wavefront are in flight
+  auto wait_stages = [&](int n) {
+    if (n >= 2) {
+      MOE_WAIT_VMCNT(2 * LPW_MX);
+    } else if (n == 1) {
+      MOE_WAIT_VMCNT(LPW_MX);
+    } else {
+      MOE_WAIT_VMCNT(0);
+    }
+  };
+  Frags fr;
+  auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+    wait_stages(2);
+    barrier();
+    issue(lbuf, kt + 3);
+    read_frags(cur, fr, xscales(kt));
+    wait_stages(2);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    barrier();
+    mma(fr, acc);
+  };
+  auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
+    wait_stages(min(2, nk - 1 - kt));
+    barrier();
+    if (kt + 3 < nk) issue(lbuf, kt + 3);
+    read_frags(cur, fr, xscales(kt));
+    wait_stages(min(2, nk - 2 - kt));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (!(second && kt == nk - 1)) barrier();   // evens the two halves' barrier counts
+    mma(fr, acc);
+  };
+
+  __syncthreads();
+  ld.sl.issue_first(xch, ld.xsb, ld.lds_b, ld.xlim);
+  issue(b0, 0);
+  if (nk > 1) issue(b1, 1);
+  if (nk > 2) issue(b2, 2);
+  if (second) {   // the half-step offset; stage 0 must have landed before it
+    wait_stages(min(2, nk - 1));
+    barrier();
+  }
+  int kt = 0;
+  for (; kt + 7 <= nk; kt += 4) {   // every step of the group issues a stage (kt + 6 < nk)
+    step_fast(b0, b3, kt);
+    step_fast(b1, b0, kt + 1);
+    step_fast(b2, b1, kt + 2);
+    step_fast(b3, b2, kt + 3);
+  }
+  if (kt < nk) step(b0, b3, kt);
+  if (kt + 1 < nk) step(b1, b0, kt + 1);
+  if (kt + 2 < nk) step(b2, b1, kt + 2);
+  if (kt + 3 < nk) step(b3, b2, kt + 3);
+  if (kt + 4 < nk) step(b0, b3, kt + 4);
+  if (kt + 5 < nk) step(b1, b0, kt + 5);
+}
+
 template <int EPI, bool PACKED>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[MSTAGE];
@@ -337,84 +440,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
       for (int j = 0; j < MTM; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    auto issue = [&](uint8_t* buf, int s) {
-      const uint8_t* wstage = wbase + (int64_t)s * wstride;
-      wl.issue(buf, wstage);
-      xl.issue(buf + XOFF, xbase + s * ROWB);
-      sl.issue(buf, xch, PACKED ? wstage : wsb + 2 * s, xsb, s, (int)lds_b);
-    };
-    auto xscales = [&](int kt) {
-      return reinterpret_cast<const uint32_t*>(xch + (kt / XCH % NXCH) * XCH_BYTES) + kt % XCH;
-    };
-    // Ping-pong schedule: step kt is a memory phase (issue stage kt + 3 into
-    // the buffer of stage kt - 1, read stage kt's fragments and scales), a
-    // barrier, and a compute phase (its 8 scaled MFMAs from registers).  The
-    // second wavefront of every SIMD runs one barrier behind the first, so
-    // one of the two issues MFMAs while the other reads LDS.  Every barrier
-    // is preceded by this wavefront's wait for the stage the wavefronts
-    // past it will read: stage kt before the memory phase, stage kt + 1
-    // (and this step's LDS reads) before the compute phase.
-    const bool second = wave_id() >= NWAVE / 2;
-    auto barrier = [&]() {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_barrier" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // wait until at most n stages' loads of this wavefront are in flight
-    auto wait_stages = [&](int n) {
-      if (n >= 2) {
-        MOE_WAIT_VMCNT(2 * LPW_MX);
-      } else if (n == 1) {
-        MOE_WAIT_VMCNT(LPW_MX);
-      } else {
-        MOE_WAIT_VMCNT(0);
-      }
-    };
-    Frags fr;
-    auto step_fast = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
-      wait_stages(2);
-      barrier();
-      issue(lbuf, kt + 3);
-      read_frags(cur, fr, xscales(kt));
-      wait_stages(2);
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      barrier();
-      mma(fr, acc);
-    };
-    auto step = [&](uint8_t* cur, uint8_t* lbuf, int kt) {
-      wait_stages(min(2, nk - 1 - kt));
-      barrier();
-      if (kt + 3 < nk) issue(lbuf, kt + 3);
-      read_frags(cur, fr, xscales(kt));
-      wait_stages(min(2, nk - 2 - kt));
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      if (!(second && kt == nk - 1)) barrier();   // evens the two halves' barrier counts
-      mma(fr, acc);
-    };
-
-    __syncthreads();
-    sl.issue_first(xch, xsb, (int)lds_b);
-    issue(b0, 0);
-    if (nk > 1) issue(b1, 1);
-    if (nk > 2) issue(b2, 2);
-    if (second) {   // the half-step offset; stage 0 must have landed before it
-      wait_stages(min(2, nk - 1));
-      barrier();
-    }
-    int kt = 0;
-    for (; kt + 7 <= nk; kt += 4) {   // every step of the group issues a stage (kt + 6 < nk)
-      step_fast(b0, b3, kt);
-      step_fast(b1, b0, kt + 1);
-      step_fast(b2, b1, kt + 2);
-      step_fast(b3, b2, kt + 3);
-    }
-    if (kt < nk) step(b0, b3, kt);
-    if (kt + 1 < nk) step(b1, b0, kt + 1);
-    if (kt + 2 < nk) step(b2, b1, kt + 2);
-    if (kt + 3 < nk) step(b3, b2, kt + 3);
-    if (kt + 4 < nk) step(b0, b3, kt + 4);
-    if (kt + 5 < nk) step(b1, b0, kt + 5);
+    const MxLoads<PACKED> ld{xl, wl, sl, xbase, wbase, wstride, xsb, wsb, (int)lds_b, (int)lds_b};
+    mx_k_loop<PACKED>(ld, nk, acc, b0, b1, b2, b3, xch);
     store<EPI>(a, acc, m0, rows, n0, SWI ? f : a.N, f, b0, b1);
   }
 }
@@ -474,6 +501,121 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict_
   }
 }
 
+
+// Weight gradient in MXFP8 (the group-aware MXFP8 backward: blog sections
+// "What specialized optimizations are required for dropless MoE?" and
+// "Optimization 1"): C[g] [P, Q] = sum over group g's rows r of
+// A[r, p] * B[r, q], both operands quantised down their rows (blocks of 32
+// restarting at every group) and stored transposed by
+// mxfp8_quantize_transposed: codes [P | Q, k_cap] with group g at positions
+// [K_g, K_g + 64 ceil(s_g / 64)), zero codes past its rows.  A tile
+// (g, p-tile, q-tile) is the forward K loop over those positions with the A
+// rows as X and the B rows as W; the padding multiplies to zero, and an
+// empty group stores zeros.  Tiles come from dynamic queues as in the bf16
+// weight gradient (groups dealt to the queues in a snake over their index).
+constexpr int kWgQueues = 8, kWgSlots = 64;
+__device__ uint32_t g_wgrad_mx_sched[kWgSlots][kWgQueues + 1];
+
+__global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
+  __shared__ __align__(1024) uint8_t b0[MSTAGE];
+  __shared__ __align__(1024) uint8_t b1[MSTAGE];
+  __shared__ __align__(1024) uint8_t b2[MSTAGE];
+  __shared__ __align__(1024) uint8_t b3[MSTAGE];
+  __shared__ __align__(1024) uint8_t xch[NXCH * XCH_BYTES];
+  __shared__ int32_t s_tile[2];
+
+  const int P = a.M, Q = a.N;
+  const int64_t k_cap = a.K, lds_b = a.K / 32;
+  const int per_group = a.p_tiles * a.n_tiles;
+
+  // group g's padded start K_g and padded length, from the device sizes
+  // clamped as the quantiser clamps them (>= 0, rows up to m_cap)
+  auto group_range = [&](int g, int64_t& kg, int64_t& len) {
+    const int lane = threadIdx.x & 63;
+    int64_t rbase = 0, kbase = 0;
+    kg = 0;
+    len = 0;
+    for (int c = 0; c < a.G; c += 64) {
+      const int gi = c + lane;
+      const int64_t sz = gi < a.G ? (int64_t)max(a.sizes[gi], 0) : 0;
+      const int64_t rincl = wave_incl_scan(sz);
+      const int64_t n = min(rbase + rincl, a.m_cap) - min(rbase + rincl - sz, a.m_cap);
+      const int64_t pad = (n + 63) / 64 * 64;
+      const int64_t kincl = wave_incl_scan(pad);
+      if (g >= c && g < c + 64) {
+        kg = kbase + __shfl(kincl - pad, g - c, 64);
+        len = __shfl(pad, g - c, 64);
+      }
+      rbase += __shfl(rincl, 63, 64);
+      kbase += __shfl(kincl, 63, 64);
+    }
+    kg = wave_u64(kg);
+    len = wave_u64(len);
+  };
+
+  auto process = [&](int g, int rem) {
+    const int pt = rem / a.n_tiles, qt = rem - pt * a.n_tiles;
+    const int p0 = pt * BM, q0 = qt * BN;
+    const int rows = min(BM, P - p0), wrows = min(BN, Q - q0);
+    int64_t kg, len;
+    group_range(g, kg, len);
+    const int nk = (int)(len / 64);
+    f32x16_t acc[MTN][MTM];
+#pragma unroll
+    for (int i = 0; i < MTN; ++i)
+#pragma unroll
+      for (int j = 0; j < MTM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    if (nk > 0) {
+      auto xrow = [&](int r) -> int64_t { return p0 + min(r, rows - 1); };
+      auto wrow = [&](int r) -> int64_t { return q0 + min(r, wrows - 1); };
+      MxLoads<false> ld;
+      ld.xl.init(k_cap, xrow);
+      ld.wl.init(k_cap, wrow);
+      ld.sl.init(lds_b, wrow, rows);
+      ld.xbase = a.A + kg;
+      ld.wbase = a.B + kg;
+      ld.wstride = ROWB;
+      ld.xsb = a.As + (int64_t)p0 * lds_b + kg / 32;
+      ld.wsb = a.Bs + kg / 32;
+      ld.lds_b = (int)lds_b;
+      ld.xlim = (int)(lds_b - kg / 32);
+      mx_k_loop<false>(ld, nk, acc, b0, b1, b2, b3, xch);
+    }
+    GGArgs ag = a;
+    ag.C = a.C + (int64_t)g * P * Q * 2;
+    store<MOE_EPI_NONE>(ag, acc, p0, rows, q0, Q, 0, b0, b1);
+  };
+
+  __syncthreads();
+  const int nq = min(kWgQueues, (int)gridDim.x);
+  const int myq = (int)(blockIdx.x % nq);
+  uint32_t* ctr = g_wgrad_mx_sched[a.sched_slot];
+  int parity = 0;
+  for (int qq = 0; qq < nq; ++qq) {
+    const int q = (myq + qq) % nq;
+    const int rounds = a.G / nq, left = a.G % nq;
+    const int ngroups = rounds + (((rounds & 1) ? nq - 1 - q : q) < left ? 1 : 0);
+    const int64_t ntiles = (int64_t)ngroups * per_group;
+    for (;;) {
+      if (threadIdx.x == 0) s_tile[parity] = (int32_t)atomicAdd(&ctr[q], 1u);
+      __syncthreads();
+      const int64_t t = s_tile[parity];
+      parity ^= 1;
+      if (t >= ntiles) break;
+      const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
+      process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (atomicAdd(&ctr[kWgQueues], 1u) == gridDim.x - 1) {
+      for (int q = 0; q < kWgQueues; ++q) atomicExch(&ctr[q], 0u);
+      atomicExch(&ctr[kWgQueues], 0u);
+    }
+  }
+}
+
 }  // namespace mx
 }  // namespace fwd
 
@@ -498,6 +640,20 @@ moe_status_t launch_pack_mx_weights(const uint8_t* q, const uint8_t* sc, int G, 
     hipLaunchKernelGGL((fwd::mx::pack_mx_kernel<MOE_EPI_NONE>), dim3((unsigned)blocks), dim3(256), 0, s, q, sc, G, N, K,
                        n_tiles, reinterpret_cast<uint4*>(out));
   }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s) {
+  static std::atomic<uint32_t> next_slot{0};
+  GGArgs b = a;
+  b.n_tiles = (a.N + fwd::BN - 1) / fwd::BN;
+  b.p_tiles = (a.M + fwd::BM - 1) / fwd::BM;
+  b.sched_slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % fwd::mx::kWgSlots);
+  const int64_t max_tiles = (int64_t)a.G * b.n_tiles * b.p_tiles;
+  int64_t grid = moe_host::device_cu_count();
+  if (max_tiles < grid) grid = max_tiles;
+  if (grid <= 0) grid = 1;
+  hipLaunchKernelGGL(fwd::mx::gg_wgrad_mx_kernel, dim3((unsigned)grid), dim3(fwd::THREADS), 0, s, b);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

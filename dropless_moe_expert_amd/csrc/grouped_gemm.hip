@@ -11,7 +11,9 @@
 //  * ragged M, bf16 (forward with B [G, N, K] rows or packed, data gradient
 //    with B [G, K, N]): gg_bf16.hip, gg_fwd_kernel;
 //  * ragged K, bf16 (weight gradients): gg_bf16.hip, gg_wgrad_kernel;
-//  * ragged M, MXFP8: gg_fwd_mx.hip.
+//  * ragged M, MXFP8: gg_fwd_mx.hip, gg_fwd_mx_kernel;
+//  * ragged K, MXFP8 (operands from mxfp8_quantize_transposed): gg_fwd_mx.hip,
+//    gg_wgrad_mx_kernel.
 // Every grid is a function of host arguments only (CU count, m_cap, G, N, K).
 #include "gg_common.h"
 
@@ -19,6 +21,7 @@ namespace moe {
 moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout, hipStream_t s);  // gg_bf16.hip
 moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s);                             // gg_bf16.hip
 moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s);              // gg_fwd_mx.hip
+moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s);                                       // gg_fwd_mx.hip
 }  // namespace moe
 
 extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A, const uint8_t* As, const void* B,
@@ -45,5 +48,6 @@ extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A,
     if (d->dtype == MOE_DTYPE_MXFP8) return launch_fwd_mx(a, d->epilogue, d->b_layout == MOE_B_PACKED, s);
     return launch_fwd(a, d->epilogue, d->out_dtype == MOE_OUT_F32, d->b_layout, s);
   }
+  if (d->dtype == MOE_DTYPE_MXFP8) return launch_wgrad_mx(a, s);
   return launch_wgrad(a, d->out_dtype == MOE_OUT_F32, s);
 }

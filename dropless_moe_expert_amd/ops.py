@@ -305,6 +305,23 @@ def grouped_gemm_wgrad(X: torch.Tensor, Y: torch.Tensor, group_sizes: torch.Tens
     return out
 
 
+def grouped_gemm_wgrad_mxfp8(AqT: torch.Tensor, AsT: torch.Tensor, BqT: torch.Tensor, BsT: torch.Tensor,
+                             group_sizes: torch.Tensor, m_cap: int, *, out: Optional[torch.Tensor] = None,
+                             flag: Optional[torch.Tensor] = None):
+    """MXFP8 weight gradient: C[g] = sum over group g's rows of a[r]^T b[r] -> bf16 [G, P, Q],
+    from mxfp8_quantize_transposed(a, group_sizes) (codes [P, k_cap]) and the same of b ([Q, k_cap])."""
+    dev = _dev(AqT, AsT, BqT, BsT, group_sizes)
+    P, k_cap = AqT.shape
+    Q = BqT.shape[0]
+    G = group_sizes.numel()
+    if out is None:
+        out = torch.empty((G, P, Q), dtype=torch.bfloat16, device=dev)
+    d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, G, P, Q, k_cap, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(AqT), _ptr(AsT), _ptr(BqT), _ptr(BsT), _ptr(group_sizes),
+                              _ptr(out), None, None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (MXFP8, ragged K)")
+    return out
+
+
 def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torch.Tensor],
                        group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
                        out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,

@@ -144,6 +144,11 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
  *   a captured call keeps its slot on every replay, so one graph must not
  *   be replayed on two streams concurrently.  Each tile is computed by one
  *   workgroup in a fixed order: results are bitwise reproducible.
+ *   dtype = MOE_DTYPE_MXFP8 (the group-aware MXFP8 weight gradient): A and
+ *   B are the outputs of mxfp8_quantize_transposed (grouped) for the same
+ *   group_sizes and m_cap: codes A [M, K], B [N, K] with scales A_scale
+ *   [M, K/32], B_scale [N, K/32], where K is that call's k_cap; output bf16.
+ *   The same 64 queue slots apply (a separate set).
  * dtype = MOE_DTYPE_MXFP8 (RAGGED_M, B_NK or B_PACKED): A, B are E4M3 codes
  *   with E8M0 scales A_scale [m_cap, K/32], B_scale [G, N, K/32] (value =
  *   code * 2^(scale - 127)); accumulation fp32, output bf16.  With
@@ -158,7 +163,8 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
  *   MOE_EPI_SWIGLU.  Rows r >= sum(s_g) are not written.
  * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
  * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
- *   MXFP8: K % 128 == 0.  A, B, C 16-byte aligned.
+ *   MXFP8: K % 128 == 0 (RAGGED_M), K % 64 == 0 and K >= m_cap + 63 G
+ *   (RAGGED_K).  A, B, C 16-byte aligned; scales 4-byte aligned.
  * ------------------------------------------------------------------------ */
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_MXFP8 1

@@ -360,6 +360,36 @@ def test_mxfp8_quantize_transposed(ops):
         np.testing.assert_array_equal(sT[g].cpu().numpy(), s_ref.T)
 
 
+@pytest.mark.parametrize("P,Q", [(136, 264), (256, 64)])
+def test_grouped_gemm_wgrad_mxfp8(ops, P, Q):
+    # group-aware MXFP8 weight gradient: operands quantised down their rows by
+    # the transposed quantiser (bit-exact with the oracle, tested above), the
+    # GEMM against the oracle on the identical codes; groups that are empty,
+    # shorter than a block, and longer than the 8 stages one scale piece covers
+    rng = np.random.default_rng(P + 3 * Q)
+    sizes = np.array([0, 5, 600, 33, 0, 130, 64, 1], np.int32)
+    G, M = sizes.size, int(sizes.sum())
+    say("gg wgrad mxfp8", P, Q, M)
+    A = inputs.to_bf16((rng.standard_normal((M + 5, P)) * 2).astype(np.float32))
+    B = inputs.to_bf16((rng.standard_normal((M + 5, Q)) * 0.5).astype(np.float32))
+    aq, as_ = orc.mxfp8_quantize(A[:M], 1, sizes)
+    bq, bs = orc.mxfp8_quantize(B[:M], 1, sizes)
+    ref = orc.mx_grouped_wgrad(aq, as_, bq, bs, sizes)
+    S = dev(torch.from_numpy(sizes))
+    AqT, AsT = ops.mxfp8_quantize_transposed(dev(A), S)
+    BqT, BsT = ops.mxfp8_quantize_transposed(dev(B), S)
+    out = ops.grouped_gemm_wgrad_mxfp8(AqT, AsT, BqT, BsT, S, M + 5)
+    again = ops.grouped_gemm_wgrad_mxfp8(AqT, AsT, BqT, BsT, S, M + 5)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for g in range(G):
+        if sizes[g] == 0:
+            assert torch.all(got[g] == 0)
+        else:
+            assert rel_l2(got[g], ref[g]) <= MX_TOL, g
+    assert torch.equal(out, again)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_mxfp8(ops, swiglu):
     sizes = np.array([0, 300, 1, 0, 260], np.int32)
