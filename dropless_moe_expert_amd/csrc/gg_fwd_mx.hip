@@ -248,7 +248,16 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
           f32x4_t h;
 #pragma unroll
           for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][j][q * 4 + e]) * acc[i + MTN / 2][j][q * 4 + e];
-          if (mr < rows && jc < f) store_sub<MOE_OUT_BF16>(a.C, f, m0 + mr, jc, h);
+          if (mr < rows && jc < f) {
+            store_sub<MOE_OUT_BF16>(a.C, f, m0 + mr, jc, h);
+            if (a.Caux) {   // the pre-activations [g | u], for the backward
+              const f32x4_t gv = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
+              const f32x4_t uv = {acc[i + MTN / 2][j][q * 4], acc[i + MTN / 2][j][q * 4 + 1],
+                                  acc[i + MTN / 2][j][q * 4 + 2], acc[i + MTN / 2][j][q * 4 + 3]};
+              store_sub<MOE_OUT_BF16>(a.Caux, 2 * f, m0 + mr, jc, gv);
+              store_sub<MOE_OUT_BF16>(a.Caux, 2 * f, m0 + mr, f + jc, uv);
+            }
+          }
         }
       }
     } else {

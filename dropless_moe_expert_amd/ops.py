@@ -325,13 +325,14 @@ def grouped_gemm_wgrad_mxfp8(AqT: torch.Tensor, AsT: torch.Tensor, BqT: torch.Te
 def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torch.Tensor],
                        group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
                        out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
-                       flag: Optional[torch.Tensor] = None):
+                       keep_aux: bool = False, flag: Optional[torch.Tensor] = None):
     """MXFP8 ragged-M grouped GEMM.  Aq uint8 [m_cap, K], As uint8 [m_cap, K/32],
     Bq uint8 [G, N, K] with Bs uint8 [G, N, K/32], or Bq = PackedWeights from
     pack_weights_mxfp8 (Bs None) -> bf16 [m_cap, N] (or N/2 with SwiGLU).
     With MOE_EPI_SWIGLU_MXFP8 (weights packed for MOE_EPI_SWIGLU, or
     unpacked) -> (codes uint8 [m_cap, N/2], scales uint8 [m_cap, N/64]): the
-    SwiGLU output quantised as mxfp8_quantize(h, 0) would."""
+    SwiGLU output quantised as mxfp8_quantize(h, 0) would.  keep_aux (with
+    MOE_EPI_SWIGLU) -> (h, pre-activations bf16 [m_cap, N])."""
     packed = isinstance(Bq, PackedWeights)
     m_cap, Kd = Aq.shape
     fused = epilogue == MOE_EPI_SWIGLU_MXFP8
@@ -353,11 +354,18 @@ def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torc
             out_scale = torch.empty((m_cap, ncols // 32), dtype=torch.uint8, device=dev)
     elif out is None:
         out = torch.empty((m_cap, ncols), dtype=torch.bfloat16, device=dev)
+    aux = None
+    if keep_aux:
+        if epilogue != MOE_EPI_SWIGLU:
+            raise MoeError("keep_aux needs the SwiGLU epilogue")
+        aux = torch.empty((m_cap, N), dtype=torch.bfloat16, device=dev)
     d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, layout, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
     _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bt), None if packed else _ptr(Bs),
-                              _ptr(group_sizes), _ptr(out), _ptr(out_scale) if fused else None, None, 0, _ptr(flag),
-                              _stream(dev)), "grouped_gemm (mxfp8)")
-    return (out, out_scale) if fused else out
+                              _ptr(group_sizes), _ptr(out), _ptr(out_scale) if fused else _ptr(aux), None, 0,
+                              _ptr(flag), _stream(dev)), "grouped_gemm (mxfp8)")
+    if fused:
+        return out, out_scale
+    return (out, aux) if keep_aux else out
 
 
 def unpermute_combine(y_perm: torch.Tensor, topk_w: Optional[torch.Tensor], perm_dst: torch.Tensor, T: int, K: int,
@@ -499,6 +507,63 @@ def moe_backward(dy: torch.Tensor, saved: dict, w1p: torch.Tensor, w2: torch.Ten
     dgu = swiglu_backward(saved["gu"], dh, sizes)
     dxp = grouped_gemm(dgu, w1p, sizes, b_layout=MOE_B_KN, flag=flag)          # dGU [M,2f] x W1p_e [2f,d]
     dw1p = grouped_gemm_wgrad(dgu, saved["x_perm"], sizes, flag=flag)          # [E, 2f, d]
+    dx = unpermute_combine(dxp, None, dst, T, K)
+    return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)
+
+
+def quantize_weights_mxfp8_train(w1p: torch.Tensor, w2: torch.Tensor, flag: Optional[torch.Tensor] = None):
+    """The four MXFP8 weight operands of a training step, packed: W1p [E, 2f, d]
+    and W2 [E, d, f] quantised along their forward contraction (for the
+    forward GEMMs) and along their output axis (for the data gradients, via
+    the transposed quantiser: W2^T [E, f, d] blocks along d, W1p^T [E, d, 2f]
+    blocks along 2f)."""
+    q1, s1 = quantize_weights(w1p)
+    q2, s2 = quantize_weights(w2)
+    q2t, s2t = mxfp8_quantize_transposed(w2, flag=flag)
+    q1t, s1t = mxfp8_quantize_transposed(w1p, flag=flag)
+    return dict(w1k=pack_weights_mxfp8(q1, s1, MOE_EPI_SWIGLU), w2k=pack_weights_mxfp8(q2, s2),
+                w2tk=pack_weights_mxfp8(q2t, s2t), w1tk=pack_weights_mxfp8(q1t, s1t))
+
+
+def moe_forward_mxfp8_train(logits: torch.Tensor, x: torch.Tensor, wk: dict, K: int,
+                            flag: Optional[torch.Tensor] = None):
+    """The routed layer on MXFP8 operands, keeping what the backward needs:
+    route -> permute (bf16 rows) -> quantise -> gate/up GEMM + SwiGLU (bf16 h
+    and pre-activations) -> quantise h -> down GEMM -> combine.  wk from
+    quantize_weights_mxfp8_train."""
+    T = x.shape[0]
+    ids, w = route_topk(logits, K, flag=flag)
+    p = permute(x, ids, wk["w1k"].G, flag=flag)
+    sizes = p["group_sizes"]
+    xq, xs = mxfp8_quantize(p["x_perm"], 0, sizes, flag=flag)
+    h, gu = grouped_gemm_mxfp8(xq, xs, wk["w1k"], None, sizes, epilogue=MOE_EPI_SWIGLU, keep_aux=True, flag=flag)
+    hq, hs = mxfp8_quantize(h, 0, sizes, flag=flag)
+    y_perm = grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag)
+    y = unpermute_combine(y_perm, w, p["perm_dst"], T, K)
+    return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, **p)
+
+
+def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Optional[torch.Tensor] = None):
+    """Backward of moe_forward_mxfp8_train with MXFP8 GEMMs: the data gradients
+    quantise their left operands along the contraction and use the weights
+    quantised along their output axis; the weight gradients quantise both
+    operands down the tokens, blocks restarting at every expert's rows
+    (group-aware MXFP8).  Combine, SwiGLU backward and the dx fold stay bf16."""
+    sizes, dst = saved["group_sizes"], saved["perm_dst"]
+    T = dy.shape[0]
+    m_cap = saved["h"].shape[0]
+    dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
+    q, sc = mxfp8_quantize(dyp, 0, sizes, flag=flag)
+    dh = grouped_gemm_mxfp8(q, sc, wk["w2tk"], None, sizes, flag=flag)                    # [M, f]
+    aT, asT = mxfp8_quantize_transposed(dyp, sizes, flag=flag)
+    bT, bsT = mxfp8_quantize_transposed(saved["h"], sizes, flag=flag)
+    dw2 = grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, m_cap, flag=flag)             # [E, d, f]
+    dgu = swiglu_backward(saved["gu"], dh, sizes)
+    q, sc = mxfp8_quantize(dgu, 0, sizes, flag=flag)
+    dxp = grouped_gemm_mxfp8(q, sc, wk["w1tk"], None, sizes, flag=flag)                   # [M, d]
+    aT, asT = mxfp8_quantize_transposed(dgu, sizes, flag=flag)
+    bT, bsT = mxfp8_quantize_transposed(saved["x_perm"], sizes, flag=flag)
+    dw1p = grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, m_cap, flag=flag)            # [E, 2f, d]
     dx = unpermute_combine(dxp, None, dst, T, K)
     return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)
 

@@ -325,3 +325,72 @@ def layer_backward(dy, saved, w1p, w2, K: int):
     T = saved["ids"].shape[0]
     dx = unpermute_combine(dxp, None, dst, T, K)
     return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)
+
+
+# --------------------------------------------------------------------------
+# the layer in MXFP8 (blog: group-aware MXFP8 quantisation; "Optimization 1":
+# MXFP8 block scaling of the expert matmuls), composed of the functions above
+# --------------------------------------------------------------------------
+
+def _quant_experts(w, axis: int):
+    """[E, R, C] bf16 -> codes and scales per expert: axis 0 -> ([E, R, C],
+    [E, R, C/32]) blocks along C; axis 1 -> ([E, C, R], [E, C, R/32]) blocks
+    down R, each column's codes contiguous (the weight operand of a data
+    gradient, contracted over R)."""
+    wb = u16(w)
+    E, R, C = wb.shape
+    if axis == 0:
+        q, s = mxfp8_quantize(wb.reshape(E * R, C), 0)
+        return q.reshape(E, R, C), s.reshape(E, R, C // 32)
+    qs, ss = [], []
+    for e in range(E):
+        q, s = mxfp8_quantize(wb[e], 1, np.array([R], np.int32))
+        qs.append(q.T.copy())
+        ss.append(s.T.copy())
+    return np.stack(qs), np.stack(ss)
+
+
+def layer_forward_mxfp8(logits, x, w1p, w2, K: int):
+    """layer_forward with MXFP8 GEMMs: the permuted rows and h quantised along
+    their rows (axis 0), the weights along their contraction; h from the
+    gate/up accumulators, the pre-activations kept in bf16."""
+    ids, w = route_topk(logits, K)
+    E = int(w1p.shape[0])
+    sizes, offs, src, dst = permute(ids, E)
+    xp = gather_rows(x, src, K)
+    xq, xs = mxfp8_quantize(xp, 0)
+    w1q, w1s = _quant_experts(w1p, 0)
+    gu = mx_grouped_gemm(xq, xs, w1q, w1s, sizes)
+    h = mx_grouped_gemm(xq, xs, w1q, w1s, sizes, swiglu=True)
+    hq, hs = mxfp8_quantize(h, 0)
+    w2q, w2s = _quant_experts(w2, 0)
+    yp = mx_grouped_gemm(hq, hs, w2q, w2s, sizes)
+    T = ids.shape[0]
+    y = unpermute_combine(yp, w, dst, T, K)
+    return y, dict(ids=ids, w=w, sizes=sizes, offs=offs, perm_src=src, perm_dst=dst, x_perm=xp, h=h, gu=gu,
+                   y_perm=yp)
+
+
+def layer_backward_mxfp8(dy, saved, w1p, w2, K: int):
+    """layer_backward with MXFP8 GEMMs: a data gradient quantises its left
+    operand along the contraction (axis 0) and the weight down its output
+    axis; a weight gradient quantises both operands down the tokens, blocks
+    restarting at every expert's rows (group-aware, axis 1)."""
+    sizes, dst = saved["sizes"], saved["perm_dst"]
+    dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
+    q, s = mxfp8_quantize(dyp, 0)
+    w2tq, w2ts = _quant_experts(w2, 1)
+    dh = mx_grouped_gemm(q, s, w2tq, w2ts, sizes)
+    aq, as_ = mxfp8_quantize(dyp, 1, sizes)
+    bq, bs = mxfp8_quantize(saved["h"], 1, sizes)
+    dw2 = mx_grouped_wgrad(aq, as_, bq, bs, sizes)
+    dgu = swiglu_backward(saved["gu"], dh)
+    q, s = mxfp8_quantize(dgu, 0)
+    w1tq, w1ts = _quant_experts(w1p, 1)
+    dxp = mx_grouped_gemm(q, s, w1tq, w1ts, sizes)
+    aq, as_ = mxfp8_quantize(dgu, 1, sizes)
+    bq, bs = mxfp8_quantize(saved["x_perm"], 1, sizes)
+    dw1p = mx_grouped_wgrad(aq, as_, bq, bs, sizes)
+    T = saved["ids"].shape[0]
+    dx = unpermute_combine(dxp, None, dst, T, K)
+    return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)

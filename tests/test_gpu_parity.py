@@ -531,6 +531,32 @@ def test_tiny_layer_forward_backward(ops):
     assert torch.all(grads["dw2"][7] == 0) and torch.all(grads["dw1p"][7] == 0)
 
 
+def test_tiny_layer_forward_backward_mxfp8(ops):
+    # the training step with every GEMM in MXFP8 (the weight gradients
+    # group-aware along the tokens) against the oracle that quantises the
+    # same way, step by step
+    say("tiny layer mxfp8")
+    L = inputs.workload("tiny")
+    y_ref, saved_ref = orc.layer_forward_mxfp8(L.logits, L.x, L.w1p, L.w2, L.K)
+    g_ref = orc.layer_backward_mxfp8(L.dy, saved_ref, L.w1p, L.w2, L.K)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wk = ops.quantize_weights_mxfp8_train(dev(L.w1p), dev(L.w2), flag=flag)
+    y, saved = ops.moe_forward_mxfp8_train(dev(L.logits), dev(L.x), wk, L.K, flag=flag)
+    grads = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    np.testing.assert_array_equal(saved["group_sizes"].cpu().numpy(), saved_ref["sizes"])
+    M = int(saved_ref["sizes"].sum())
+    for k, got in (("gu", saved["gu"]), ("h", saved["h"]), ("y_perm", saved["y_perm"])):
+        assert rel_l2(got[:M], saved_ref[k]) <= MX_TOL, k
+    assert rel_l2(y, y_ref) <= MX_TOL
+    for k in ("dy_perm", "dh", "dgu", "dx_perm"):
+        assert rel_l2(grads[k][:M], g_ref[k]) <= MX_TOL, k
+    for k in ("dx", "dw2", "dw1p"):
+        assert rel_l2(grads[k], g_ref[k]) <= MX_TOL, k
+    assert torch.all(grads["dw2"][7] == 0) and torch.all(grads["dw1p"][7] == 0)
+
+
 # ------------------------------------------------------------------- data errors: flags, bounds
 
 def test_flags_bad_ids_stay_in_bounds(ops):
