@@ -297,6 +297,67 @@ def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
             "forward_kernel_sum_ms": round(fsum, 4), "backward_kernel_sum_ms": round(bsum, 4), "kernels": kern}
 
 
+def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
+    """The fine-grained forward and backward with every GEMM in MXFP8: the
+    forward as the dsv3 MXFP8 path, the data gradients on the weights
+    quantised along their output axis, the weight gradients on operands
+    quantised down the tokens with blocks restarting at every expert (the
+    pages' group-aware MXFP8).  The four weight quantisations happen once per
+    optimiser step and are timed on their own (weight_quantize_ms)."""
+    T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
+    M = T * K
+    lg, x, w1, w2, dy = (t.to(dev) for t in (L.logits, L.x, L.w1p, L.w2, L.dy))
+    wk = ops.quantize_weights_mxfp8_train(w1, w2, flag=flag)
+    t_wq = timer(lambda: ops.quantize_weights_mxfp8_train(w1, w2, flag=flag))
+    y, s = ops.moe_forward_mxfp8_train(lg, x, wk, K, flag=flag)
+    sizes = s["group_sizes"]
+    xq, xs = ops.mxfp8_quantize(s["x_perm"], 0, sizes, flag=flag)
+    t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(xq, xs, wk["w1k"], None, sizes, epilogue=ops.MOE_EPI_SWIGLU,
+                                                keep_aux=True, flag=flag))
+    hq, hs = ops.mxfp8_quantize(s["h"], 0, sizes, flag=flag)
+    t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag))
+    g = ops.moe_backward_mxfp8(dy, s, wk, K, flag=flag)
+    dyq, dys = ops.mxfp8_quantize(g["dy_perm"], 0, sizes, flag=flag)
+    t_dh = timer(lambda: ops.grouped_gemm_mxfp8(dyq, dys, wk["w2tk"], None, sizes, flag=flag))
+    aT, asT = ops.mxfp8_quantize_transposed(g["dy_perm"], sizes, flag=flag)
+    bT, bsT = ops.mxfp8_quantize_transposed(s["h"], sizes, flag=flag)
+    t_dw2 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, M, flag=flag))
+    gq, gs = ops.mxfp8_quantize(g["dgu"], 0, sizes, flag=flag)
+    t_dx = timer(lambda: ops.grouped_gemm_mxfp8(gq, gs, wk["w1tk"], None, sizes, flag=flag))
+    cT, csT = ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag)
+    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag))
+    xT, xsT = ops.mxfp8_quantize_transposed(s["x_perm"], sizes, flag=flag)
+    t_dw1 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(cT, csT, xT, xsT, sizes, M, flag=flag))
+    del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs
+    for _ in range(2):
+        y, sv = ops.moe_forward_mxfp8_train(lg, x, wk, K, flag=flag)
+        ops.moe_backward_mxfp8(dy, sv, wk, K, flag=flag)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        y, sv = ops.moe_forward_mxfp8_train(lg, x, wk, K, flag=flag)
+        ops.moe_backward_mxfp8(dy, sv, wk, K, flag=flag)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - a) * 1e3 / steps
+    fl = 3 * 2.0 * M * (2 * f * d + d * f)
+    return {"workload": "fine-grained forward+backward T=16384 d=2048 E=128 top-8 ffn=768, every GEMM in MXFP8 "
+                        "(weight gradients group-aware along the tokens), logit bias N(0,1.5) per expert",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "valid_row_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+            "weight_quantize_ms": round(t_wq, 4),
+            "tokens_per_s_with_weight_quantize": round(T / ((ms + t_wq) * 1e-3), 1),
+            "kernels": {
+                "gate_up_swiglu_mxfp8 (keeps pre-activations)": flop_entry(t_g1, 2.0 * M * 2 * f * d,
+                                                                          MXFP8_PEAK_TFLOPS),
+                "down_mxfp8": flop_entry(t_g2, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
+                "dgrad_down_mxfp8": flop_entry(t_dh, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
+                "wgrad_down_mxfp8": flop_entry(t_dw2, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
+                "dgrad_gate_up_mxfp8": flop_entry(t_dx, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
+                "wgrad_gate_up_mxfp8": flop_entry(t_dw1, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
+                "quantize_transposed (dgu)": byte_entry(t_qt, M * 2 * f * 2 + M * 2 * f + M * 2 * f / 32),
+            }}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +477,12 @@ def main() -> int:
         workloads["finegrained"] = bench_finegrained(torch, ops, Lf, dev, timer, flag, max(5, args.steps // 5))
         log(f"fine-grained fwd+bwd: {workloads['finegrained']['ms_per_step']:.3f} ms, "
             f"{workloads['finegrained']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        workloads["finegrained_mxfp8"] = bench_finegrained_mxfp8(torch, ops, Lf, dev, timer, flag,
+                                                                 max(5, args.steps // 5))
+        log(f"fine-grained fwd+bwd mxfp8: {workloads['finegrained_mxfp8']['ms_per_step']:.3f} ms, "
+            f"{workloads['finegrained_mxfp8']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
         del Lf
         torch.cuda.empty_cache()
         torch.cuda.synchronize()

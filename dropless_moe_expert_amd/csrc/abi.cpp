@@ -280,7 +280,8 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
     return MOE_ERR_UNSUPPORTED;
   }
   if (rows > 0 && (!x || !qT || !scaleT)) return MOE_ERR_INVALID_ARG;
-  if (rows > 0 && (!aligned16(x) || !aligned16(qT))) return MOE_ERR_ALIGNMENT;
+  if (rows > 0 && (!aligned16(x) || !aligned16(qT) || (reinterpret_cast<uintptr_t>(scaleT) & 1u)))
+    return MOE_ERR_ALIGNMENT;
   if (rows == 0) return MOE_OK;
   return mxfp8_quantize_transposed_launch(x, rows, cols, group_sizes, G, k_cap, qT, scaleT, err_flag, S(stream));
 }

@@ -127,16 +127,26 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
   }
 }
 
-// Transposed axis 1: one thread per (32-row block p, 8-column piece), as
-// above, but each column's 32 codes leave as 32 consecutive bytes of its qT
-// row.  Grouped (group_sizes != NULL): block p lies in the 64-aligned padded
-// layout (kpad = padded group starts); blocks past a group's rows store zero
-// codes and scale 0.  Batched (NULL): G batches of `rows` rows, one group each.
+// Transposed axis 1, one workgroup per tile of 64 positions (two blocks) x
+// 64 columns: the tile's rows are read as whole 128-byte row pieces into
+// LDS, each (column, block) pair is quantised from there by one thread, the
+// codes are assembled column-major in LDS and leave as 64-byte column rows of
+// qT (four 16-byte pieces per column), the two scales of a column as one
+// 2-byte word.  Grouped (group_sizes != NULL): positions in the 64-aligned
+// padded layout (kpad = padded group starts); positions past a group's rows
+// get zero codes, blocks with no rows scale 0.  Batched (NULL): G batches of
+// `rows` rows, one group each.
+constexpr int QT_R = 64, QT_C = 64;
+constexpr int QT_LD = QT_C + 2;   // bf16 per LDS row: the pad staggers the column reads over the banks
+
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
                                                          const int32_t* __restrict__ group_sizes, int G,
                                                          int64_t k_cap, uint8_t* __restrict__ qT,
                                                          uint8_t* __restrict__ scaleT, uint32_t* flag) {
   extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
+  __shared__ uint16_t xt[QT_R * QT_LD];                 // the tile, bf16, row-major
+  __shared__ __align__(16) uint8_t ct[QT_C * QT_R];     // its codes, column-major
+  __shared__ uint8_t st[QT_C * 2];                      // its scales, two per column
   int64_t* roff = sh;
   int64_t* kpad = sh + G + 1;
   const bool grouped = group_sizes != nullptr;
@@ -160,74 +170,78 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     }
     __syncthreads();
   }
-  const int64_t bpg = rows / 32;   // batched: blocks per batch
-  const int64_t nblk = grouped ? kpad[G] / 32 : (int64_t)G * bpg;
-  const int npc = cols / 8;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < nblk * npc;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = idx / npc;
-    const int c8 = (int)(idx - p * npc) * 8;
+  const int64_t tpb = rows / QT_R;   // batched: position tiles per batch
+  const int64_t ntk = grouped ? kpad[G] / QT_R : (int64_t)G * tpb;
+  const int ntc = (cols + QT_C - 1) / QT_C;
+  const int t = threadIdx.x;
+  for (int64_t tile = blockIdx.x; tile < ntk * ntc; tile += gridDim.x) {
+    const int64_t tk = tile / ntc;
+    const int c0 = (int)(tile - tk * ntc) * QT_C;
     int64_t r0, ldq;
     int n;
-    uint8_t* qb;   // the block's first code in column c8's qT row
-    uint8_t* sb;   // its scale in column c8's scaleT row
+    uint8_t* qb;   // the tile's first code in column c0's qT row
+    uint8_t* sb;   // its first scale in column c0's scaleT row
     if (grouped) {
-      int lo = 0, hi = G - 1;   // last g with kpad[g] <= 32 p
+      int lo = 0, hi = G - 1;   // last g with kpad[g] <= 64 tk
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (kpad[mid] <= 32 * p) lo = mid; else hi = mid - 1;
+        if (kpad[mid] <= QT_R * tk) lo = mid; else hi = mid - 1;
       }
-      const int64_t b = p - kpad[lo] / 32;
-      r0 = roff[lo] + 32 * b;
-      n = (int)max((int64_t)0, min((int64_t)32, roff[lo + 1] - r0));
+      r0 = roff[lo] + (QT_R * tk - kpad[lo]);
+      n = (int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - r0));
       ldq = k_cap;
-      qb = qT + (int64_t)c8 * k_cap + 32 * p;
-      sb = scaleT + (int64_t)c8 * (k_cap / 32) + p;
+      qb = qT + (int64_t)c0 * k_cap + QT_R * tk;
+      sb = scaleT + (int64_t)c0 * (k_cap / 32) + 2 * tk;
     } else {
-      const int64_t g = p / bpg, b = p - g * bpg;
-      r0 = g * rows + 32 * b;
-      n = 32;
+      const int64_t g = tk / tpb, b = tk - g * tpb;
+      r0 = g * rows + QT_R * b;
+      n = QT_R;
       ldq = rows;
-      qb = qT + g * cols * rows + (int64_t)c8 * rows + 32 * b;
-      sb = scaleT + g * cols * bpg + (int64_t)c8 * bpg + b;
+      qb = qT + g * cols * rows + (int64_t)c0 * rows + QT_R * b;
+      sb = scaleT + g * cols * (rows / 32) + (int64_t)c0 * (rows / 32) + 2 * b;
     }
-    float amax[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = 0; i < n; ++i) {
-      float f[8];
-      unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
+    // 1. the tile's rows: 64 rows x 8 pieces of 8 columns, two per thread
+    __syncthreads();   // the previous tile's LDS is read out
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], fabsf(f[j]));
+    for (int k = 0; k < 2; ++k) {
+      const int u = t + 256 * k, r = u >> 3, c = (u & 7) * 8;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < n && c0 + c < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + r) * cols + c0 + c);
+      uint32_t* d = reinterpret_cast<uint32_t*>(xt + r * QT_LD + c);   // 4-byte aligned (QT_LD even)
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
-    int e[8];
+    __syncthreads();
+    // 2. one thread per (column, block): amax, scale, 32 codes into the column
+    if (t < 2 * QT_C) {
+      const int c = t & (QT_C - 1), b = t >> 6;
+      float amax = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)xt[(32 * b + i) * QT_LD + c] << 16)));
+      const int e = mx_exponent(amax);
+      st[2 * c + b] = (uint8_t)(e + 127);
+      uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      e[j] = mx_exponent(amax[j]);
-      sb[(int64_t)j * (ldq / 32)] = (uint8_t)(e[j] + 127);
-    }
-    // codes of rows 4w..4w+3 of column j form word w of that column's 32 bytes
-    uint32_t cw[8][8];
+      for (int q = 0; q < 8; ++q) {
+        float f[4];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      float f[4][8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (4 * w + i < n) {
-          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + 4 * w + i) * cols + c8), f[i]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) f[i][j] = 0.f;
-        }
+        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)xt[(32 * b + 4 * q + i) * QT_LD + c] << 16);
+        w[q] = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        cw[j][w] = cvt4_e4m3(scale_pow2(f[0][j], e[j]), scale_pow2(f[1][j], e[j]), scale_pow2(f[2][j], e[j]),
-                             scale_pow2(f[3][j], e[j]));
+      uint4* d = reinterpret_cast<uint4*>(ct + c * QT_R + 32 * b);
+      d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      d[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint4* dst = reinterpret_cast<uint4*>(qb + (int64_t)j * ldq);
-      dst[0] = make_uint4(cw[j][0], cw[j][1], cw[j][2], cw[j][3]);
-      dst[1] = make_uint4(cw[j][4], cw[j][5], cw[j][6], cw[j][7]);
+    __syncthreads();
+    // 3. column rows out: four 16-byte pieces per column; the scale pair
+    {
+      const int c = t >> 2, piece = t & 3;
+      if (c0 + c < cols) {
+        *reinterpret_cast<uint4*>(qb + (int64_t)c * ldq + 16 * piece) =
+            *reinterpret_cast<const uint4*>(ct + c * QT_R + 16 * piece);
+        if (piece == 0)
+          *reinterpret_cast<uint16_t*>(sb + (int64_t)c * (ldq / 32)) =
+              (uint16_t)(st[2 * c] | ((uint16_t)st[2 * c + 1] << 8));
+      }
     }
   }
 }
@@ -238,11 +252,11 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int6
                                                          const int32_t* group_sizes, int32_t G, int64_t k_cap,
                                                          uint8_t* qT, uint8_t* scaleT, uint32_t* flag,
                                                          hipStream_t s) {
-  const int64_t cap = (int64_t)moe_host::device_cu_count() * 16;
-  const int64_t nblk = group_sizes ? k_cap / 32 : (int64_t)G * (rows / 32);   // an upper bound when grouped
-  const int64_t work = nblk * (cols / 8);
+  const int64_t cap = (int64_t)moe_host::device_cu_count() * 8;
+  const int64_t ntk = group_sizes ? k_cap / 64 : (int64_t)G * (rows / 64);   // an upper bound when grouped
+  const int64_t work = ntk * ((cols + 63) / 64);
   if (work == 0) return MOE_OK;
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((work + 255) / 256, cap));
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
   hipLaunchKernelGGL(moe::mx_quant_t_kernel, dim3((unsigned)blocks), dim3(256), shmem, s, x, rows, cols, group_sizes,
                      G, k_cap, qT, scaleT, flag);

@@ -291,7 +291,7 @@ moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols,
  * group_sizes == NULL (weights, x bf16 [G, rows, cols], one group per
  *   batch): qT [G, cols, rows], scaleT [G, cols, rows / 32]; rows % 64 == 0;
  *   k_cap ignored.
- * cols % 8 == 0; x, qT 16-byte aligned.  The data errors of the grouped
+ * cols % 8 == 0; x, qT 16-byte aligned, scaleT 2-byte aligned.  The data errors of the grouped
  * kernels (negative sizes, sizes past rows) raise err_flag. */
 moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t cols, const int32_t* group_sizes,
                                        int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint32_t* err_flag,
