@@ -521,7 +521,8 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict_
 // (g, p-tile, q-tile) is the forward K loop over those positions with the A
 // rows as X and the B rows as W; the padding multiplies to zero, and an
 // empty group stores zeros.  Tiles come from dynamic queues as in the bf16
-// weight gradient (groups dealt to the queues in a snake over their index).
+// weight gradient: groups ranked largest first (each workgroup ranks them
+// into a 2 KB LDS table), dealt to the queues in a snake over the ranks.
 constexpr int kWgQueues = 8, kWgSlots = 64;
 __device__ uint32_t g_wgrad_mx_sched[kWgSlots][kWgQueues + 1];
 
@@ -532,8 +533,18 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b3[MSTAGE];
   __shared__ __align__(1024) uint8_t xch[NXCH * XCH_BYTES];
   __shared__ int32_t s_tile[2];
+  __shared__ uint16_t by_rank[1024];   // group of each rank, largest first (ties: lower index first)
 
   const int P = a.M, Q = a.N;
+  for (int g = threadIdx.x; g < a.G; g += THREADS) {
+    const int sg = max(a.sizes[g], 0);
+    int r = 0;
+    for (int h = 0; h < a.G; ++h) {
+      const int sh = max(a.sizes[h], 0);
+      r += (sh > sg) || (sh == sg && h < g);
+    }
+    by_rank[r] = (uint16_t)g;
+  }
   const int64_t k_cap = a.K, lds_b = a.K / 32;
   const int per_group = a.p_tiles * a.n_tiles;
 
@@ -614,7 +625,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
       parity ^= 1;
       if (t >= ntiles) break;
       const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
-      process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
+      process(by_rank[k * nq + ((k & 1) ? nq - 1 - q : q)], rem);
     }
   }
   if (threadIdx.x == 0) {
