@@ -325,7 +325,7 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     gq, gs = ops.mxfp8_quantize(g["dgu"], 0, sizes, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm_mxfp8(gq, gs, wk["w1tk"], None, sizes, flag=flag))
     cT, csT = ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag)
-    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag))
+    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag, rows_too=True))
     xT, xsT = ops.mxfp8_quantize_transposed(s["x_perm"], sizes, flag=flag)
     t_dw1 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(cT, csT, xT, xsT, sizes, M, flag=flag))
     del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs
@@ -354,7 +354,7 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
                 "wgrad_down_mxfp8": flop_entry(t_dw2, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
                 "dgrad_gate_up_mxfp8": flop_entry(t_dx, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
                 "wgrad_gate_up_mxfp8": flop_entry(t_dw1, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
-                "quantize_transposed (dgu)": byte_entry(t_qt, M * 2 * f * 2 + M * 2 * f + M * 2 * f / 32),
+                "quantize_both_layouts (dgu)": byte_entry(t_qt, M * 2 * f * 2 + 2 * (M * 2 * f + M * 2 * f / 32)),
             }}
 
 

@@ -24,7 +24,7 @@ moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const
 moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*, int32_t,
                                         uint16_t*, hipStream_t);
 moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, int64_t, int32_t, const int32_t*, int32_t, int64_t,
-                                              uint8_t*, uint8_t*, uint32_t*, hipStream_t);
+                                              uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*, hipStream_t);
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
                                          uint8_t*, uint8_t*, uint32_t*, hipStream_t);
 moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
@@ -270,8 +270,8 @@ moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols,
 }
 
 moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t cols, const int32_t* group_sizes,
-                                       int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint32_t* err_flag,
-                                       void* stream) {
+                                       int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows,
+                                       uint8_t* scale_rows, uint32_t* err_flag, void* stream) {
   if (rows < 0 || cols < 8 || G < 1 || G > 1024) return MOE_ERR_INVALID_ARG;
   if (cols % 8) return MOE_ERR_UNSUPPORTED;
   if (group_sizes) {
@@ -282,8 +282,14 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
   if (rows > 0 && (!x || !qT || !scaleT)) return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!aligned16(x) || !aligned16(qT) || (reinterpret_cast<uintptr_t>(scaleT) & 1u)))
     return MOE_ERR_ALIGNMENT;
+  if (!q_rows != !scale_rows) return MOE_ERR_INVALID_ARG;
+  if (q_rows) {
+    if (cols % 32) return MOE_ERR_UNSUPPORTED;
+    if (rows > 0 && !aligned16(q_rows)) return MOE_ERR_ALIGNMENT;
+  }
   if (rows == 0) return MOE_OK;
-  return mxfp8_quantize_transposed_launch(x, rows, cols, group_sizes, G, k_cap, qT, scaleT, err_flag, S(stream));
+  return mxfp8_quantize_transposed_launch(x, rows, cols, group_sizes, G, k_cap, qT, scaleT, q_rows, scale_rows,
+                                          err_flag, S(stream));
 }
 
 }  // extern "C"

@@ -135,14 +135,17 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
 // 2-byte word.  Grouped (group_sizes != NULL): positions in the 64-aligned
 // padded layout (kpad = padded group starts); positions past a group's rows
 // get zero codes, blocks with no rows scale 0.  Batched (NULL): G batches of
-// `rows` rows, one group each.
+// `rows` rows, one group each.  With q0 != NULL the same tile also yields
+// the row-wise (axis 0) codes and scales of its valid rows, by the threads
+// the column blocks leave idle: one read of x for both layouts.
 constexpr int QT_R = 64, QT_C = 64;
 constexpr int QT_LD = QT_C + 2;   // bf16 per LDS row: the pad staggers the column reads over the banks
 
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
                                                          const int32_t* __restrict__ group_sizes, int G,
                                                          int64_t k_cap, uint8_t* __restrict__ qT,
-                                                         uint8_t* __restrict__ scaleT, uint32_t* flag) {
+                                                         uint8_t* __restrict__ scaleT, uint8_t* __restrict__ q0,
+                                                         uint8_t* __restrict__ s0, uint32_t* flag) {
   extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
   __shared__ uint16_t xt[QT_R * QT_LD];                 // the tile, bf16, row-major
   __shared__ __align__(16) uint8_t ct[QT_C * QT_R];     // its codes, column-major
@@ -151,23 +154,54 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   int64_t* kpad = sh + G + 1;
   const bool grouped = group_sizes != nullptr;
   if (grouped) {
-    if (threadIdx.x == 0) {
-      int64_t o = 0, k = 0;
-      bool neg = false, over = false;
-      for (int g = 0; g < G; ++g) {
-        int64_t sz = group_sizes[g];
-        if (sz < 0) { neg = true; sz = 0; }
-        if (o + sz > rows) { over = true; sz = rows - o; }
-        roff[g] = o;
-        kpad[g] = k;
-        o += sz;
-        k += (sz + 63) / 64 * 64;
-      }
-      roff[G] = o;
-      kpad[G] = k;
-      if (neg) raise_flag(flag, MOE_FLAG_NEGATIVE_SIZE);
-      if (over) raise_flag(flag, MOE_FLAG_ROWS_OVER_CAP);
+    // row offsets and padded starts: each thread sums its run of groups,
+    // a block scan of the sums, then each thread writes its run's prefixes
+    __shared__ int64_t scan_r[256], scan_k[256];
+    const int per = (G + 255) / 256, t0 = threadIdx.x * per;
+    int64_t lr = 0;
+    bool neg = false;
+    for (int g = t0; g < min(G, t0 + per); ++g) {
+      const int32_t v = group_sizes[g];
+      neg |= v < 0;
+      lr += max(v, 0);
     }
+    scan_r[threadIdx.x] = lr;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {   // inclusive scan of the run sums
+      const int64_t v = threadIdx.x >= o ? scan_r[threadIdx.x - o] : 0;
+      __syncthreads();
+      scan_r[threadIdx.x] += v;
+      __syncthreads();
+    }
+    // clamp the rows to `rows` as the groups are walked in order
+    int64_t o = scan_r[threadIdx.x] - lr, lk = 0;
+    for (int g = t0; g < min(G, t0 + per); ++g) {
+      const int64_t sz = min((int64_t)max(group_sizes[g], 0), max((int64_t)0, rows - o));
+      lk += (sz + 63) / 64 * 64;
+      o += max(group_sizes[g], 0);
+    }
+    scan_k[threadIdx.x] = lk;
+    __syncthreads();
+    for (int o2 = 1; o2 < 256; o2 <<= 1) {
+      const int64_t v = threadIdx.x >= o2 ? scan_k[threadIdx.x - o2] : 0;
+      __syncthreads();
+      scan_k[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int64_t ro = scan_r[threadIdx.x] - lr, ko = scan_k[threadIdx.x] - lk;
+    for (int g = t0; g < min(G, t0 + per); ++g) {
+      const int64_t sz = min((int64_t)max(group_sizes[g], 0), max((int64_t)0, rows - ro));
+      roff[g] = min(ro, rows);
+      kpad[g] = ko;
+      ro += max(group_sizes[g], 0);
+      ko += (sz + 63) / 64 * 64;
+    }
+    if (threadIdx.x == 255) {
+      roff[G] = min(scan_r[255], rows);
+      kpad[G] = scan_k[255];
+    }
+    if (blockIdx.x == 0 && __any(neg) && (threadIdx.x & 63) == 0) raise_flag(flag, MOE_FLAG_NEGATIVE_SIZE);
+    if (blockIdx.x == 0 && threadIdx.x == 255 && scan_r[255] > rows) raise_flag(flag, MOE_FLAG_ROWS_OVER_CAP);
     __syncthreads();
   }
   const int64_t tpb = rows / QT_R;   // batched: position tiles per batch
@@ -230,6 +264,28 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       uint4* d = reinterpret_cast<uint4*>(ct + c * QT_R + 32 * b);
       d[0] = make_uint4(w[0], w[1], w[2], w[3]);
       d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else if (q0) {
+      // one thread per (valid row, 32-column block): the axis-0 quantisation
+      const int u = t - 2 * QT_C, r = u >> 1, b = u & 1, cb = c0 + 32 * b;
+      if (r < n && cb < cols) {
+        float f[32];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          f[i] = __uint_as_float((uint32_t)xt[r * QT_LD + 32 * b + i] << 16);
+          amax = fmaxf(amax, fabsf(f[i]));
+        }
+        const int e = mx_exponent(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          w[q] = cvt4_e4m3(scale_pow2(f[4 * q], e), scale_pow2(f[4 * q + 1], e), scale_pow2(f[4 * q + 2], e),
+                           scale_pow2(f[4 * q + 3], e));
+        uint4* d = reinterpret_cast<uint4*>(q0 + (r0 + r) * cols + cb);
+        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        s0[(r0 + r) * (cols / 32) + cb / 32] = (uint8_t)(e + 127);
+      }
     }
     __syncthreads();
     // 3. column rows out: four 16-byte pieces per column; the scale pair
@@ -250,8 +306,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
 
 extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int64_t rows, int32_t cols,
                                                          const int32_t* group_sizes, int32_t G, int64_t k_cap,
-                                                         uint8_t* qT, uint8_t* scaleT, uint32_t* flag,
-                                                         hipStream_t s) {
+                                                         uint8_t* qT, uint8_t* scaleT, uint8_t* q0, uint8_t* s0,
+                                                         uint32_t* flag, hipStream_t s) {
   const int64_t cap = (int64_t)moe_host::device_cu_count() * 8;
   const int64_t ntk = group_sizes ? k_cap / 64 : (int64_t)G * (rows / 64);   // an upper bound when grouped
   const int64_t work = ntk * ((cols + 63) / 64);
@@ -259,7 +315,7 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int6
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
   hipLaunchKernelGGL(moe::mx_quant_t_kernel, dim3((unsigned)blocks), dim3(256), shmem, s, x, rows, cols, group_sizes,
-                     G, k_cap, qT, scaleT, flag);
+                     G, k_cap, qT, scaleT, q0, s0, flag);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -80,7 +80,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_combine_backward": (ctypes.c_int, [P, P, P, P, i64, i32, i32, P, P, P]),
             "moe_swiglu_backward": (ctypes.c_int, [P, P, i64, i32, P, i32, P, P]),
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
-            "mxfp8_quantize_transposed": (ctypes.c_int, [P, i64, i32, P, i32, i64, P, P, P, P]),
+            "mxfp8_quantize_transposed": (ctypes.c_int, [P, i64, i32, P, i32, i64, P, P, P, P, P, P]),
             "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
@@ -426,10 +426,12 @@ def k_cap_for(m_cap: int, G: int) -> int:
 
 
 def mxfp8_quantize_transposed(x: torch.Tensor, group_sizes: Optional[torch.Tensor] = None,
-                              flag: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                              flag: Optional[torch.Tensor] = None, rows_too: bool = False):
     """Blocks of 32 down the columns, codes stored column-contiguous.
     x [rows, cols] with group_sizes -> (qT uint8 [cols, k_cap], scaleT [cols, k_cap/32]);
-    x [G, rows, cols] without -> (qT [G, cols, rows], scaleT [G, cols, rows/32])."""
+    x [G, rows, cols] without -> (qT [G, cols, rows], scaleT [G, cols, rows/32]).
+    rows_too: also the axis-0 codes and scales of the same rows (as
+    mxfp8_quantize(x, 0)), from the same read: returns (qT, scaleT, q, scale)."""
     dev = _dev(x, group_sizes)
     assert x.dtype == torch.bfloat16
     if group_sizes is not None:
@@ -443,9 +445,13 @@ def mxfp8_quantize_transposed(x: torch.Tensor, group_sizes: Optional[torch.Tenso
         k_cap = 0
         q = torch.empty((G, cols, rows), dtype=torch.uint8, device=dev)
         s = torch.empty((G, cols, rows // 32), dtype=torch.uint8, device=dev)
+    q0 = s0 = None
+    if rows_too:
+        q0 = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        s0 = torch.empty(tuple(x.shape[:-1]) + (cols // 32,), dtype=torch.uint8, device=dev)
     _check(lib().mxfp8_quantize_transposed(_ptr(x), rows, cols, _ptr(group_sizes), G, k_cap, _ptr(q), _ptr(s),
-                                           _ptr(flag), _stream(dev)), "mxfp8_quantize_transposed")
-    return q, s
+                                           _ptr(q0), _ptr(s0), _ptr(flag), _stream(dev)), "mxfp8_quantize_transposed")
+    return (q, s, q0, s0) if rows_too else (q, s)
 
 
 # ------------------------------------------------------------------ measurement only
@@ -517,10 +523,8 @@ def quantize_weights_mxfp8_train(w1p: torch.Tensor, w2: torch.Tensor, flag: Opti
     forward GEMMs) and along their output axis (for the data gradients, via
     the transposed quantiser: W2^T [E, f, d] blocks along d, W1p^T [E, d, 2f]
     blocks along 2f)."""
-    q1, s1 = quantize_weights(w1p)
-    q2, s2 = quantize_weights(w2)
-    q2t, s2t = mxfp8_quantize_transposed(w2, flag=flag)
-    q1t, s1t = mxfp8_quantize_transposed(w1p, flag=flag)
+    q1t, s1t, q1, s1 = mxfp8_quantize_transposed(w1p, flag=flag, rows_too=True)
+    q2t, s2t, q2, s2 = mxfp8_quantize_transposed(w2, flag=flag, rows_too=True)
     return dict(w1k=pack_weights_mxfp8(q1, s1, MOE_EPI_SWIGLU), w2k=pack_weights_mxfp8(q2, s2),
                 w2tk=pack_weights_mxfp8(q2t, s2t), w1tk=pack_weights_mxfp8(q1t, s1t))
 
@@ -535,12 +539,14 @@ def moe_forward_mxfp8_train(logits: torch.Tensor, x: torch.Tensor, wk: dict, K: 
     ids, w = route_topk(logits, K, flag=flag)
     p = permute(x, ids, wk["w1k"].G, flag=flag)
     sizes = p["group_sizes"]
-    xq, xs = mxfp8_quantize(p["x_perm"], 0, sizes, flag=flag)
+    # x and h quantised both ways in one read each: along their rows for the
+    # forward GEMMs, down the tokens (kept) for the weight gradients
+    xT, xsT, xq, xs = mxfp8_quantize_transposed(p["x_perm"], sizes, flag=flag, rows_too=True)
     h, gu = grouped_gemm_mxfp8(xq, xs, wk["w1k"], None, sizes, epilogue=MOE_EPI_SWIGLU, keep_aux=True, flag=flag)
-    hq, hs = mxfp8_quantize(h, 0, sizes, flag=flag)
+    hT, hsT, hq, hs = mxfp8_quantize_transposed(h, sizes, flag=flag, rows_too=True)
     y_perm = grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag)
     y = unpermute_combine(y_perm, w, p["perm_dst"], T, K)
-    return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, **p)
+    return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, xT=xT, xsT=xsT, hT=hT, hsT=hsT, **p)
 
 
 def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Optional[torch.Tensor] = None):
@@ -553,17 +559,13 @@ def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Op
     T = dy.shape[0]
     m_cap = saved["h"].shape[0]
     dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
-    q, sc = mxfp8_quantize(dyp, 0, sizes, flag=flag)
+    aT, asT, q, sc = mxfp8_quantize_transposed(dyp, sizes, flag=flag, rows_too=True)
     dh = grouped_gemm_mxfp8(q, sc, wk["w2tk"], None, sizes, flag=flag)                    # [M, f]
-    aT, asT = mxfp8_quantize_transposed(dyp, sizes, flag=flag)
-    bT, bsT = mxfp8_quantize_transposed(saved["h"], sizes, flag=flag)
-    dw2 = grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, m_cap, flag=flag)             # [E, d, f]
+    dw2 = grouped_gemm_wgrad_mxfp8(aT, asT, saved["hT"], saved["hsT"], sizes, m_cap, flag=flag)  # [E, d, f]
     dgu = swiglu_backward(saved["gu"], dh, sizes)
-    q, sc = mxfp8_quantize(dgu, 0, sizes, flag=flag)
+    aT, asT, q, sc = mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True)
     dxp = grouped_gemm_mxfp8(q, sc, wk["w1tk"], None, sizes, flag=flag)                   # [M, d]
-    aT, asT = mxfp8_quantize_transposed(dgu, sizes, flag=flag)
-    bT, bsT = mxfp8_quantize_transposed(saved["x_perm"], sizes, flag=flag)
-    dw1p = grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, m_cap, flag=flag)            # [E, 2f, d]
+    dw1p = grouped_gemm_wgrad_mxfp8(aT, asT, saved["xT"], saved["xsT"], sizes, m_cap, flag=flag)  # [E, 2f, d]
     dx = unpermute_combine(dxp, None, dst, T, K)
     return dict(dy_perm=dyp, dw=dw, dh=dh, dw2=dw2, dgu=dgu, dx_perm=dxp, dw1p=dw1p, dx=dx)
 

@@ -291,11 +291,16 @@ moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols,
  * group_sizes == NULL (weights, x bf16 [G, rows, cols], one group per
  *   batch): qT [G, cols, rows], scaleT [G, cols, rows / 32]; rows % 64 == 0;
  *   k_cap ignored.
+ * q_rows, scale_rows (both or neither; cols % 32 == 0, q_rows 16-byte
+ *   aligned): also the axis-0 quantisation of the same rows, from the same
+ *   read of x, exactly as mxfp8_group_quantize (axis 0) writes it: q_rows
+ *   [rows, cols] (batched: [G, rows, cols]), scale_rows [rows, cols / 32];
+ *   grouped, only rows < sum(group_sizes) are written.
  * cols % 8 == 0; x, qT 16-byte aligned, scaleT 2-byte aligned.  The data errors of the grouped
  * kernels (negative sizes, sizes past rows) raise err_flag. */
 moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t cols, const int32_t* group_sizes,
-                                       int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint32_t* err_flag,
-                                       void* stream);
+                                       int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows,
+                                       uint8_t* scale_rows, uint32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

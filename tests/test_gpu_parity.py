@@ -348,16 +348,30 @@ def test_mxfp8_quantize_transposed(ops):
     want_q, want_s, used = _to_transposed(q_ref, s_ref, sizes, qT.shape[1])
     np.testing.assert_array_equal(qT[:, :used].cpu().numpy(), want_q[:, :used])
     np.testing.assert_array_equal(sT[:, :used // 32].cpu().numpy(), want_s[:, :used // 32])
+    # both layouts from one read (cols % 32 == 0): the axis-0 part as the axis-0 oracle
+    x2 = inputs.to_bf16((rng.standard_normal((M + 7, 96)) * 3).astype(np.float32))
+    q_ref, s_ref = orc.mxfp8_quantize(x2[:M], 1, sizes)
+    q0_ref, s0_ref = orc.mxfp8_quantize(x2[:M], 0)
+    qT, sT, q0, s0 = ops.mxfp8_quantize_transposed(dev(x2), dev(torch.from_numpy(sizes)), rows_too=True)
+    torch.cuda.synchronize()
+    want_q, want_s, used = _to_transposed(q_ref, s_ref, sizes, qT.shape[1])
+    np.testing.assert_array_equal(qT[:, :used].cpu().numpy(), want_q[:, :used])
+    np.testing.assert_array_equal(sT[:, :used // 32].cpu().numpy(), want_s[:, :used // 32])
+    np.testing.assert_array_equal(q0[:M].cpu().numpy(), q0_ref)
+    np.testing.assert_array_equal(s0[:M].cpu().numpy(), s0_ref)
     # batched (weights): G batches of 128 rows, each one group
-    G, R, C2 = 3, 128, 40
+    G, R, C2 = 3, 128, 96
     say("mx qT batched", G, R, C2)
     w = inputs.to_bf16((rng.standard_normal((G, R, C2)) * 0.05).astype(np.float32))
-    qT, sT = ops.mxfp8_quantize_transposed(dev(w))
+    qT, sT, q0, s0 = ops.mxfp8_quantize_transposed(dev(w), rows_too=True)
     torch.cuda.synchronize()
     for g in range(G):
         q_ref, s_ref = orc.mxfp8_quantize(w[g], 1, np.array([R], np.int32))
         np.testing.assert_array_equal(qT[g].cpu().numpy(), q_ref.T)
         np.testing.assert_array_equal(sT[g].cpu().numpy(), s_ref.T)
+        q_ref, s_ref = orc.mxfp8_quantize(w[g], 0)
+        np.testing.assert_array_equal(q0[g].cpu().numpy(), q_ref)
+        np.testing.assert_array_equal(s0[g].cpu().numpy(), s_ref)
 
 
 @pytest.mark.parametrize("P,Q", [(136, 264), (256, 64)])
