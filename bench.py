@@ -317,18 +317,20 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     hq, hs = ops.mxfp8_quantize(s["h"], 0, sizes, flag=flag)
     t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag))
     g = ops.moe_backward_mxfp8(dy, s, wk, K, flag=flag)
+    dgu = ops.swiglu_backward(s["gu"], g["dh"], sizes)
     dyq, dys = ops.mxfp8_quantize(g["dy_perm"], 0, sizes, flag=flag)
     t_dh = timer(lambda: ops.grouped_gemm_mxfp8(dyq, dys, wk["w2tk"], None, sizes, flag=flag))
     aT, asT = ops.mxfp8_quantize_transposed(g["dy_perm"], sizes, flag=flag)
     bT, bsT = ops.mxfp8_quantize_transposed(s["h"], sizes, flag=flag)
     t_dw2 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, M, flag=flag))
-    gq, gs = ops.mxfp8_quantize(g["dgu"], 0, sizes, flag=flag)
+    gq, gs = ops.mxfp8_quantize(dgu, 0, sizes, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm_mxfp8(gq, gs, wk["w1tk"], None, sizes, flag=flag))
-    cT, csT = ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag)
-    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(g["dgu"], sizes, flag=flag, rows_too=True))
+    cT, csT = ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag)
+    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True))
+    t_sbq = timer(lambda: ops.swiglu_backward_mxfp8(s["gu"], g["dh"], sizes, flag=flag))
     xT, xsT = ops.mxfp8_quantize_transposed(s["x_perm"], sizes, flag=flag)
     t_dw1 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(cT, csT, xT, xsT, sizes, M, flag=flag))
-    del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs
+    del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs, dgu
     for _ in range(2):
         y, sv = ops.moe_forward_mxfp8_train(lg, x, wk, K, flag=flag)
         ops.moe_backward_mxfp8(dy, sv, wk, K, flag=flag)
@@ -355,6 +357,8 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
                 "dgrad_gate_up_mxfp8": flop_entry(t_dx, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
                 "wgrad_gate_up_mxfp8": flop_entry(t_dw1, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
                 "quantize_both_layouts (dgu)": byte_entry(t_qt, M * 2 * f * 2 + 2 * (M * 2 * f + M * 2 * f / 32)),
+                "swiglu_backward_quantize_both_layouts": byte_entry(t_sbq, M * 2 * f * 2 + M * f * 2
+                                                                    + 2 * (M * 2 * f + M * 2 * f / 32)),
             }}
 
 

@@ -23,8 +23,9 @@ moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const
                                          int32_t, int32_t, uint16_t*, float*, hipStream_t);
 moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*, int32_t,
                                         uint16_t*, hipStream_t);
-moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, int64_t, int32_t, const int32_t*, int32_t, int64_t,
-                                              uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*, hipStream_t);
+moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*,
+                                              int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*,
+                                              hipStream_t);
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
                                          uint8_t*, uint8_t*, uint32_t*, hipStream_t);
 moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
@@ -288,8 +289,23 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
     if (rows > 0 && !aligned16(q_rows)) return MOE_ERR_ALIGNMENT;
   }
   if (rows == 0) return MOE_OK;
-  return mxfp8_quantize_transposed_launch(x, rows, cols, group_sizes, G, k_cap, qT, scaleT, q_rows, scale_rows,
-                                          err_flag, S(stream));
+  return mxfp8_quantize_transposed_launch(x, nullptr, rows, cols, group_sizes, G, k_cap, qT, scaleT, q_rows,
+                                          scale_rows, err_flag, S(stream));
+}
+
+moe_status_t moe_swiglu_backward_mxfp8(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
+                                       const int32_t* group_sizes, int32_t G, int64_t k_cap, uint8_t* qT,
+                                       uint8_t* scaleT, uint8_t* q_rows, uint8_t* scale_rows, uint32_t* err_flag,
+                                       void* stream) {
+  if (m_cap < 0 || f < 16 || f % 16 || !group_sizes || G < 1 || G > 1024) return MOE_ERR_INVALID_ARG;
+  if (k_cap < 0 || k_cap % 64 || k_cap < m_cap + 63 * (int64_t)G) return MOE_ERR_INVALID_ARG;
+  if (m_cap > 0 && (!gu || !dh || !qT || !scaleT || !q_rows || !scale_rows)) return MOE_ERR_INVALID_ARG;
+  if (m_cap > 0 && (!aligned16(gu) || !aligned16(dh) || !aligned16(qT) || !aligned16(q_rows) ||
+                    (reinterpret_cast<uintptr_t>(scaleT) & 1u)))
+    return MOE_ERR_ALIGNMENT;
+  if (m_cap == 0) return MOE_OK;
+  return mxfp8_quantize_transposed_launch(gu, dh, m_cap, 2 * f, group_sizes, G, k_cap, qT, scaleT, q_rows,
+                                          scale_rows, err_flag, S(stream));
 }
 
 }  // extern "C"

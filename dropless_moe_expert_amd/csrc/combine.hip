@@ -176,11 +176,7 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const uint16_t* __
     unpack8(reinterpret_cast<const uint4*>(gu + r * 2 * f + f)[v], u);
     unpack8(reinterpret_cast<const uint4*>(dh + r * f)[v], d);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float s = 1.0f / (1.0f + __expf(-g[j]));
-      dg[j] = d[j] * u[j] * s * (1.0f + g[j] * (1.0f - s));
-      du[j] = d[j] * g[j] * s;
-    }
+    for (int j = 0; j < 8; ++j) swiglu_grad(g[j], u[j], d[j], dg[j], du[j]);
     reinterpret_cast<uint4*>(dgu + r * 2 * f)[v] = pack8(dg);
     reinterpret_cast<uint4*>(dgu + r * 2 * f + f)[v] = pack8(du);
   }

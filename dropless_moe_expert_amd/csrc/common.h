@@ -65,6 +65,17 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// SwiGLU backward of one element, from the pre-activations g, u and dh:
+// with s = sigmoid(g), dg = dh*u*s*(1 + g*(1-s)), du = dh*g*s.  Shared by
+// the bf16 SwiGLU backward and the one that quantises its output, so both
+// round the same values.
+__device__ __forceinline__ void swiglu_grad(float g, float u, float d, float& dg, float& du) {
+#pragma clang fp contract(off)   // the same roundings wherever it is inlined
+  const float s = 1.0f / (1.0f + __expf(-g));
+  dg = d * u * s * (1.0f + g * (1.0f - s));
+  du = d * g * s;
+}
+
 // ---------------------------------------------------------------- MXFP8 rounding
 // Shared by the quantisation kernels and the GEMM epilogue that quantises its
 // output, so both apply the same rule bit for bit.  Scale rule (OCP MX v1.0):

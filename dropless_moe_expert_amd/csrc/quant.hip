@@ -141,7 +141,13 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
 constexpr int QT_R = 64, QT_C = 64;
 constexpr int QT_LD = QT_C + 2;   // bf16 per LDS row: the pad staggers the column reads over the banks
 
-__global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+// PRODUCER 0: the tile is read from x [rows, cols].  PRODUCER 1: the tile
+// is the SwiGLU backward dgu [rows, cols = 2f] (bf16-rounded, as
+// moe_swiglu_backward stores it), made from x = gu [rows, 2f] and dh
+// [rows, f]: dgu never exists in bf16.
+template <int PRODUCER>
+__global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ dh, int64_t rows, int cols,
                                                          const int32_t* __restrict__ group_sizes, int G,
                                                          int64_t k_cap, uint8_t* __restrict__ qT,
                                                          uint8_t* __restrict__ scaleT, uint8_t* __restrict__ q0,
@@ -240,7 +246,20 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     for (int k = 0; k < 2; ++k) {
       const int u = t + 256 * k, r = u >> 3, c = (u & 7) * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < n && c0 + c < cols) v = *reinterpret_cast<const uint4*>(x + (r0 + r) * cols + c0 + c);
+      if (r < n && c0 + c < cols) {
+        if constexpr (PRODUCER == 0) {
+          v = *reinterpret_cast<const uint4*>(x + (r0 + r) * cols + c0 + c);
+        } else {
+          const int f = cols / 2, j = (c0 + c) % f;   // f % 8 == 0: a piece is all gate or all up
+          float g[8], u[8], d[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + r) * cols + j), g);
+          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + r) * cols + f + j), u);
+          unpack8(*reinterpret_cast<const uint4*>(dh + (r0 + r) * f + j), d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], u[e], d[e], dg[e], du[e]);
+          v = pack8(c0 + c < f ? dg : du);
+        }
+      }
       uint32_t* d = reinterpret_cast<uint32_t*>(xt + r * QT_LD + c);   // 4-byte aligned (QT_LD even)
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
@@ -304,7 +323,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
 
 }  // namespace moe
 
-extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int64_t rows, int32_t cols,
+extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, const uint16_t* dh, int64_t rows,
+                                                         int32_t cols,
                                                          const int32_t* group_sizes, int32_t G, int64_t k_cap,
                                                          uint8_t* qT, uint8_t* scaleT, uint8_t* q0, uint8_t* s0,
                                                          uint32_t* flag, hipStream_t s) {
@@ -314,8 +334,13 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, int6
   if (work == 0) return MOE_OK;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
-  hipLaunchKernelGGL(moe::mx_quant_t_kernel, dim3((unsigned)blocks), dim3(256), shmem, s, x, rows, cols, group_sizes,
-                     G, k_cap, qT, scaleT, q0, s0, flag);
+  if (dh) {
+    hipLaunchKernelGGL(moe::mx_quant_t_kernel<1>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
+                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
+  } else {
+    hipLaunchKernelGGL(moe::mx_quant_t_kernel<0>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
+                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -33,7 +33,8 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
     "moe_permute_mxfp8", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
     "moe_combine_backward",
-    "moe_swiglu_backward", "mxfp8_group_quantize", "mxfp8_quantize_transposed", "moe_pack_weights_bytes",
+    "moe_swiglu_backward", "moe_swiglu_backward_mxfp8", "mxfp8_group_quantize", "mxfp8_quantize_transposed",
+    "moe_pack_weights_bytes",
     "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
     # measurement only (include/moe_bench.h)
@@ -81,6 +82,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_swiglu_backward": (ctypes.c_int, [P, P, i64, i32, P, i32, P, P]),
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
             "mxfp8_quantize_transposed": (ctypes.c_int, [P, i64, i32, P, i32, i64, P, P, P, P, P, P]),
+            "moe_swiglu_backward_mxfp8": (ctypes.c_int, [P, P, i64, i32, P, i32, i64, P, P, P, P, P, P]),
             "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
@@ -454,6 +456,24 @@ def mxfp8_quantize_transposed(x: torch.Tensor, group_sizes: Optional[torch.Tenso
     return (q, s, q0, s0) if rows_too else (q, s)
 
 
+def swiglu_backward_mxfp8(gu: torch.Tensor, dh: torch.Tensor, group_sizes: torch.Tensor,
+                          flag: Optional[torch.Tensor] = None):
+    """SwiGLU backward delivered as MXFP8 only: (qT, scaleT, q, scale) equal to
+    mxfp8_quantize_transposed(swiglu_backward(gu, dh), group_sizes, rows_too=True)."""
+    dev = _dev(gu, dh, group_sizes)
+    m_cap, f = dh.shape
+    G = group_sizes.numel()
+    k_cap = k_cap_for(m_cap, G)
+    qT = torch.empty((2 * f, k_cap), dtype=torch.uint8, device=dev)
+    sT = torch.empty((2 * f, k_cap // 32), dtype=torch.uint8, device=dev)
+    q = torch.empty((m_cap, 2 * f), dtype=torch.uint8, device=dev)
+    sc = torch.empty((m_cap, 2 * f // 32), dtype=torch.uint8, device=dev)
+    _check(lib().moe_swiglu_backward_mxfp8(_ptr(gu), _ptr(dh), m_cap, f, _ptr(group_sizes), G, k_cap, _ptr(qT),
+                                           _ptr(sT), _ptr(q), _ptr(sc), _ptr(flag), _stream(dev)),
+           "moe_swiglu_backward_mxfp8")
+    return qT, sT, q, sc
+
+
 # ------------------------------------------------------------------ measurement only
 
 def bench_mfma_ceiling(random_operands: bool, iters: int, blocks: int, device) -> Tuple[torch.Tensor, int]:
@@ -549,12 +569,14 @@ def moe_forward_mxfp8_train(logits: torch.Tensor, x: torch.Tensor, wk: dict, K: 
     return y, dict(ids=ids, w=w, h=h, gu=gu, y_perm=y_perm, xT=xT, xsT=xsT, hT=hT, hsT=hsT, **p)
 
 
-def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Optional[torch.Tensor] = None):
+def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Optional[torch.Tensor] = None,
+                       fused: bool = True):
     """Backward of moe_forward_mxfp8_train with MXFP8 GEMMs: the data gradients
     quantise their left operands along the contraction and use the weights
     quantised along their output axis; the weight gradients quantise both
     operands down the tokens, blocks restarting at every expert's rows
-    (group-aware MXFP8).  Combine, SwiGLU backward and the dx fold stay bf16."""
+    (group-aware MXFP8).  Combine, SwiGLU backward and the dx fold stay bf16;
+    fused: the SwiGLU backward delivers dgu as MXFP8 only (dgu is then None)."""
     sizes, dst = saved["group_sizes"], saved["perm_dst"]
     T = dy.shape[0]
     m_cap = saved["h"].shape[0]
@@ -562,8 +584,12 @@ def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Op
     aT, asT, q, sc = mxfp8_quantize_transposed(dyp, sizes, flag=flag, rows_too=True)
     dh = grouped_gemm_mxfp8(q, sc, wk["w2tk"], None, sizes, flag=flag)                    # [M, f]
     dw2 = grouped_gemm_wgrad_mxfp8(aT, asT, saved["hT"], saved["hsT"], sizes, m_cap, flag=flag)  # [E, d, f]
-    dgu = swiglu_backward(saved["gu"], dh, sizes)
-    aT, asT, q, sc = mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True)
+    if fused:
+        dgu = None
+        aT, asT, q, sc = swiglu_backward_mxfp8(saved["gu"], dh, sizes, flag=flag)
+    else:
+        dgu = swiglu_backward(saved["gu"], dh, sizes)
+        aT, asT, q, sc = mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True)
     dxp = grouped_gemm_mxfp8(q, sc, wk["w1tk"], None, sizes, flag=flag)                   # [M, d]
     dw1p = grouped_gemm_wgrad_mxfp8(aT, asT, saved["xT"], saved["xsT"], sizes, m_cap, flag=flag)  # [E, 2f, d]
     dx = unpermute_combine(dxp, None, dst, T, K)

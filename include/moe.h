@@ -302,6 +302,18 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
                                        int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows,
                                        uint8_t* scale_rows, uint32_t* err_flag, void* stream);
 
+/* The SwiGLU backward of moe_swiglu_backward with its output dgu [m_cap, 2f]
+ * delivered only as MXFP8, both layouts, as mxfp8_quantize_transposed
+ * (grouped, with q_rows and scale_rows) would quantise the bf16 dgu that
+ * moe_swiglu_backward writes - bit for bit - without dgu ever being stored
+ * in bf16 (the blog's planned quantisation fused with its producer, section
+ * "Optimization 1").  Arguments as those two calls; all outputs required;
+ * f % 16 == 0. */
+moe_status_t moe_swiglu_backward_mxfp8(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
+                                       const int32_t* group_sizes, int32_t G, int64_t k_cap, uint8_t* qT,
+                                       uint8_t* scaleT, uint8_t* q_rows, uint8_t* scale_rows, uint32_t* err_flag,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

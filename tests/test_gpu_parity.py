@@ -374,6 +374,27 @@ def test_mxfp8_quantize_transposed(ops):
         np.testing.assert_array_equal(s0[g].cpu().numpy(), s_ref)
 
 
+def test_swiglu_backward_mxfp8(ops):
+    # dgu delivered only as MXFP8 codes equals quantising the bf16 dgu, bit for bit
+    rng = np.random.default_rng(44)
+    sizes = np.array([3, 0, 70, 130], np.int32)
+    M, f = int(sizes.sum()), 48
+    say("swiglu bwd mxfp8", M, f)
+    gu = dev(inputs.to_bf16((rng.standard_normal((M + 4, 2 * f)) * 2).astype(np.float32)))
+    dh = dev(inputs.to_bf16(rng.standard_normal((M + 4, f)).astype(np.float32)))
+    S = dev(torch.from_numpy(sizes))
+    dgu = ops.swiglu_backward(gu, dh, S)
+    want = ops.mxfp8_quantize_transposed(dgu, S, rows_too=True)
+    got = ops.swiglu_backward_mxfp8(gu, dh, S)
+    torch.cuda.synchronize()
+    used = int(((sizes + 63) // 64 * 64).sum())
+    assert torch.equal(got[0][:, :used], want[0][:, :used])
+    assert torch.equal(got[1][:, :used // 32], want[1][:, :used // 32])
+    assert torch.equal(got[2][:M], want[2][:M]) and torch.equal(got[3][:M], want[3][:M])
+    ref = orc.swiglu_backward(host_u16(gu)[:M], host_u16(dh)[:M])
+    assert max_rel_err(dgu[:M], ref) <= BF16_TOL
+
+
 @pytest.mark.parametrize("P,Q", [(136, 264), (256, 64)])
 def test_grouped_gemm_wgrad_mxfp8(ops, P, Q):
     # group-aware MXFP8 weight gradient: operands quantised down their rows by
@@ -556,9 +577,13 @@ def test_tiny_layer_forward_backward_mxfp8(ops):
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     wk = ops.quantize_weights_mxfp8_train(dev(L.w1p), dev(L.w2), flag=flag)
     y, saved = ops.moe_forward_mxfp8_train(dev(L.logits), dev(L.x), wk, L.K, flag=flag)
-    grads = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag)
+    grads = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag, fused=False)
+    fused = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
+    # the SwiGLU backward that quantises its own output changes no bit downstream
+    for k in ("dx_perm", "dw1p", "dx"):
+        assert torch.equal(fused[k], grads[k]), k
     np.testing.assert_array_equal(saved["group_sizes"].cpu().numpy(), saved_ref["sizes"])
     M = int(saved_ref["sizes"].sum())
     for k, got in (("gu", saved["gu"]), ("h", saved["h"]), ("y_perm", saved["y_perm"])):
