@@ -13,6 +13,11 @@ extern "C" {
 moe_status_t moe_route_topk_launch(const float*, int64_t, int32_t, int32_t, int32_t, int32_t*, float*, uint32_t*,
                                    hipStream_t);
 size_t moe_permute_ws_bytes_impl(int64_t, int32_t, int32_t);
+int moe_route_fused_tokens(int32_t);
+moe_status_t moe_route_fused_launch(const uint16_t*, const uint16_t*, const float*, int64_t, int32_t, int32_t, int32_t,
+                                    int32_t, int32_t*, float*, float*, int32_t*, int32_t*, uint32_t*, hipStream_t);
+moe_status_t moe_permute_routed_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t,
+                                       int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 moe_status_t moe_permute_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
                                 int32_t*, int32_t*, int32_t*, uint16_t*, void*, uint32_t*, hipStream_t);
 moe_status_t moe_permute_mxfp8_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
@@ -126,6 +131,58 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
   return moe_permute_mxfp8_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_q,
                                   x_scale, ws, err_flag, S(stream));
+}
+
+static size_t route_fused_ws_bytes(int64_t T, int32_t E, int32_t K) {
+  const int64_t tw = moe_route_fused_tokens(E);
+  const int64_t nchunk = (T + tw - 1) / tw;
+  const size_t a = ((size_t)(T * K) * 4 + 255) & ~(size_t)255;
+  return a + ((((size_t)nchunk * E * 4) + 255) & ~(size_t)255);
+}
+
+size_t moe_route_fused_workspace_bytes(int64_t T, int32_t E, int32_t K) {
+  if (T < 0 || E < 1 || E > 256 || K < 1) return 0;
+  return route_fused_ws_bytes(T, E, K);
+}
+
+moe_status_t moe_route_fused(const uint16_t* x, const uint16_t* w_router, const float* bias, int64_t T, int32_t d,
+                             int32_t E, int32_t K, int32_t renormalize, int32_t* topk_ids, float* topk_w,
+                             float* logits, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > E || K > 32) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (d < 32 || d % 32 || (int64_t)d * 2 * 255 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!x || !w_router || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x) || !aligned16(w_router) || (logits && !aligned16(logits)))) return MOE_ERR_ALIGNMENT;
+  int32_t* lr = nullptr;
+  int32_t* cc = nullptr;
+  if (ws) {
+    if (ws_bytes < route_fused_ws_bytes(T, E, K)) return MOE_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
+    lr = reinterpret_cast<int32_t*>(ws);
+    cc = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + (((size_t)(T * K) * 4 + 255) & ~(size_t)255));
+  }
+  return moe_route_fused_launch(x, w_router, bias, T, d, E, K, renormalize, topk_ids, topk_w, logits, lr, cc,
+                                err_flag, S(stream));
+}
+
+moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                                int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                                int32_t* perm_dst, uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag,
+                                void* stream) {
+  (void)err_flag;
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    if (d < 8 || d % 8) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGNMENT;
+  }
+  if (!ws || ws_bytes < route_fused_ws_bytes(T, E, K)) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
+  return moe_permute_routed_launch(x, topk_ids, T, d, E, K, moe_route_fused_tokens(E), group_sizes, group_offsets,
+                                   perm_src, perm_dst, x_perm, ws, S(stream));
 }
 
 size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {

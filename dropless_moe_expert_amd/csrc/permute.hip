@@ -137,7 +137,8 @@ template <int KT>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __restrict__ x,
                                                               const int32_t* __restrict__ ids,
                                                               const int32_t* __restrict__ local_rank,
-                                                              const int32_t* __restrict__ chunk_base, int64_t T,
+                                                              const int32_t* __restrict__ chunk_base, int chunk_pairs,
+                                                              int64_t T,
                                                               int d, int E, int K, int32_t* __restrict__ perm_src,
                                                               int32_t* __restrict__ perm_dst,
                                                               uint16_t* __restrict__ x_perm) {
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const uint16_t* __
     const int64_t i = t * K + lane;
     int e = ids[i];
     if (e < 0 || e >= E) e = E - 1;
-    my_row = chunk_base[(i / kChunk) * E + e] + local_rank[i];
+    my_row = chunk_base[(i / chunk_pairs) * E + e] + local_rank[i];
     perm_dst[i] = my_row;
     perm_src[my_row] = (int32_t)i;
   }
@@ -188,7 +189,8 @@ template <int KT>
 __global__ __launch_bounds__(256) void permute_scatter_mx_kernel(const uint16_t* __restrict__ x,
                                                                  const int32_t* __restrict__ ids,
                                                                  const int32_t* __restrict__ local_rank,
-                                                                 const int32_t* __restrict__ chunk_base, int64_t T,
+                                                                 const int32_t* __restrict__ chunk_base, int chunk_pairs,
+                                                                 int64_t T,
                                                                  int d, int E, int K, int32_t* __restrict__ perm_src,
                                                                  int32_t* __restrict__ perm_dst,
                                                                  uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256) void permute_scatter_mx_kernel(const uint16_t*
     const int64_t i = t * K + lane;
     int e = ids[i];
     if (e < 0 || e >= E) e = E - 1;
-    my_row = chunk_base[(i / kChunk) * E + e] + local_rank[i];
+    my_row = chunk_base[(i / chunk_pairs) * E + e] + local_rank[i];
     perm_dst[i] = my_row;
     perm_src[my_row] = (int32_t)i;
   }
@@ -265,16 +267,16 @@ extern "C" moe_status_t moe_permute_launch(const uint16_t* x, const int32_t* ids
   if (T > 0) {
     const dim3 g((unsigned)((T + 3) / 4)), b(256);
     switch (K) {
-      case 1: hipLaunchKernelGGL((moe::permute_scatter_kernel<1>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
-                                 E, K, perm_src, perm_dst, x_perm); break;
-      case 2: hipLaunchKernelGGL((moe::permute_scatter_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
-                                 E, K, perm_src, perm_dst, x_perm); break;
-      case 4: hipLaunchKernelGGL((moe::permute_scatter_kernel<4>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
-                                 E, K, perm_src, perm_dst, x_perm); break;
-      case 8: hipLaunchKernelGGL((moe::permute_scatter_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts, T, d,
-                                 E, K, perm_src, perm_dst, x_perm); break;
-      default: hipLaunchKernelGGL((moe::permute_scatter_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
-                                  d, E, K, perm_src, perm_dst, x_perm);
+      case 1: hipLaunchKernelGGL((moe::permute_scatter_kernel<1>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      case 2: hipLaunchKernelGGL((moe::permute_scatter_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      case 4: hipLaunchKernelGGL((moe::permute_scatter_kernel<4>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      case 8: hipLaunchKernelGGL((moe::permute_scatter_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      default: hipLaunchKernelGGL((moe::permute_scatter_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                  moe::kChunk, T, d, E, K, perm_src, perm_dst, x_perm);
     }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -298,12 +300,41 @@ extern "C" moe_status_t moe_permute_mxfp8_launch(const uint16_t* x, const int32_
   if (T > 0) {
     const dim3 g((unsigned)((T + 3) / 4)), b(256);
     switch (K) {
-      case 2: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
-                                 d, E, K, perm_src, perm_dst, xq, xs); break;
-      case 8: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts, T,
-                                 d, E, K, perm_src, perm_dst, xq, xs); break;
+      case 2: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, xq, xs); break;
+      case 8: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 moe::kChunk, T, d, E, K, perm_src, perm_dst, xq, xs); break;
       default: hipLaunchKernelGGL((moe::permute_scatter_mx_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts,
-                                  T, d, E, K, perm_src, perm_dst, xq, xs);
+                                  moe::kChunk, T, d, E, K, perm_src, perm_dst, xq, xs);
+    }
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// The permute after moe_route_fused: the router already wrote each pair's
+// rank within its token block and the blocks' per-expert counts (chunks of
+// chunk_tokens tokens), so only the scan and the scatter run.
+extern "C" moe_status_t moe_permute_routed_launch(const uint16_t* x, const int32_t* ids, int64_t T, int32_t d,
+                                                  int32_t E, int32_t K, int32_t chunk_tokens, int32_t* group_sizes,
+                                                  int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
+                                                  uint16_t* x_perm, void* ws, hipStream_t s) {
+  const int64_t M = T * K;
+  const int64_t nchunk = (T + chunk_tokens - 1) / chunk_tokens;
+  const int chunk_pairs = chunk_tokens * K;
+  int32_t* local_rank = reinterpret_cast<int32_t*>(ws);
+  size_t a = ((size_t)M * 4 + 255) & ~(size_t)255;
+  int32_t* chunk_counts = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + a);
+  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+                     group_offsets);
+  if (T > 0) {
+    const dim3 g((unsigned)((T + 3) / 4)), b(256);
+    switch (K) {
+      case 2: hipLaunchKernelGGL((moe::permute_scatter_kernel<2>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 chunk_pairs, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      case 8: hipLaunchKernelGGL((moe::permute_scatter_kernel<8>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                 chunk_pairs, T, d, E, K, perm_src, perm_dst, x_perm); break;
+      default: hipLaunchKernelGGL((moe::permute_scatter_kernel<0>), g, b, 0, s, x, ids, local_rank, chunk_counts,
+                                  chunk_pairs, T, d, E, K, perm_src, perm_dst, x_perm);
     }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;

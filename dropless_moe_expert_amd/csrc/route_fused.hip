@@ -1,0 +1,394 @@
+// Fused router: the logits product, top-K with softmax gating and the
+// dispatch histogram in one kernel.
+//
+// Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
+// Engine": intro (a learned router picks each token's Top-K experts) and
+// section "Optimization 2: Expert parallelism to integrate Dispatch and
+// Combine" (the router runs as fused kernels right before the dispatch).
+// "AI Systems Performance Engineering" ch. 1, §4.1: softmax weights are
+// exp(score - max) over their sum.
+//
+// One workgroup (4 wavefronts) per block of TW tokens:
+//  1. logits [TW, E] = x[t0 : t0 + TW] W_r^T on bf16 MFMA (16x16x32, fp32
+//     accumulation).  Rows of x and of W_r stream through an LDS ring of NS
+//     stages of KC = 32 NSUB k-values, filled by direct-to-LDS loads issued
+//     NS - 1 stages ahead; every stage issues the same number of loads (the
+//     sub-steps past d re-read the last one), so one vmcnt count per stage
+//     distance is exact.  A wavefront owns a (16 TM tokens) x (16 TN experts)
+//     block of the logits and, with SK > 1, every SK-th 32-k sub-step.
+//  2. The k-slices' partial logits meet in LDS; one pass sums them in slice
+//     order, adds the bias, turns NaN into -inf (flag) and writes the optional
+//     fp32 logits.
+//  3. Top-K: thread (token t, slice sl) keeps the KL >= K best keys of its
+//     slice of experts; a key is (order-preserving bits of the logit) << 32 |
+//     ~expert, so one unsigned 64-bit compare ranks by logit and, among equal
+//     logits, puts the lower expert first: the rule of moe_route_topk, hence
+//     the same ids for the same logits.  Slices merge pairwise through LDS.
+//  4. Weights: exp(l_k - l_max) over their sum (renormalised) or over the sum
+//     across all E experts.
+//  5. Dispatch histogram: the block's pairs (t, k), in pair order, form one
+//     chunk of moe_permute's counting sort: each pair's rank among the
+//     chunk's earlier pairs with the same expert, and the chunk's per-expert
+//     counts, in the workspace layout moe_permute_routed reads.
+#include "common.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace moe {
+namespace router {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int wave_idx() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// 16-byte slot of chunk c in LDS row r (64-byte rows): c ^ ((r >> 1) & 3),
+// the pattern under which the 16-row fragment reads below hit distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+// sortable key: larger logit first, then lower expert index first
+__device__ __forceinline__ uint64_t make_key(float v, int e) {
+  if (v == 0.f) v = 0.f;   // -0 and +0 compare equal as floats
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(~(uint32_t)k); }
+
+template <int KL>
+__device__ __forceinline__ void insert(uint64_t (&kk)[KL], uint64_t n) {
+#pragma unroll
+  for (int j = KL - 1; j >= 0; --j) {
+    const bool cj = n > kk[j];
+    const bool cp = (j > 0) ? (n > kk[j > 0 ? j - 1 : 0]) : false;
+    kk[j] = cj ? (cp ? kk[j > 0 ? j - 1 : 0] : n) : kk[j];
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void wait_stages(int q) {
+  if (q <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (q == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NB) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NB) : "memory");
+}
+
+template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS>
+struct Cfg {
+  static constexpr int TW = WM * 16 * TM;          // tokens per workgroup
+  static constexpr int EP = WN * 16 * TN;          // experts, padded
+  static constexpr int ROWS = TW + EP;             // 64-byte LDS rows per sub-step
+  static constexpr int SUB_B = ROWS * 64;
+  static constexpr int KC = 32 * NSUB;
+  static constexpr int STAGE_B = NSUB * SUB_B;
+  static constexpr int NJ = ROWS / 16;             // 1-KB load blocks per sub-step
+  static constexpr int NB = NSUB * NJ / 4;         // load blocks per wavefront and stage
+  static constexpr int LS = EP + 4;                // logits row stride (floats)
+  static constexpr int NSL = 256 / TW;             // top-K slices per token
+  static constexpr int SW = EP / NSL;              // experts per slice
+  static_assert(WM * WN * SK == 4, "four wavefronts");
+  static_assert((NSUB * NJ) % 4 == 0 && NSUB % SK == 0 && EP % NSL == 0, "tiling");
+  static_assert(NS >= 2 && NS <= 4, "the stage wait covers up to two stages ahead");
+};
+
+template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS, int KL>
+__global__ __launch_bounds__(256) void route_fused_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias, int64_t T, int d, int E,
+                                                          int K, int renorm, int32_t* __restrict__ ids,
+                                                          float* __restrict__ wout, float* __restrict__ logits,
+                                                          int32_t* __restrict__ local_rank,
+                                                          int32_t* __restrict__ chunk_counts, uint32_t* flag) {
+  using C = Cfg<TM, TN, WM, WN, SK, NSUB, NS>;
+  constexpr int TW = C::TW, EP = C::EP, LS = C::LS, NSL = C::NSL, SW = C::SW, NB = C::NB;
+  constexpr int LG_B = SK * TW * LS * 4;
+  constexpr int MG_B = (NSL / 2) * TW * KL * 8;
+  constexpr int ID_B = TW * 32 * 4;
+  constexpr int EPI_B = LG_B + MG_B + ID_B + 256 * 4 + TW * 4 + NSL * TW * 4;
+  constexpr int LDS_B = (NS * C::STAGE_B > EPI_B) ? NS * C::STAGE_B : EPI_B;
+  __shared__ __align__(1024) uint8_t lds[LDS_B];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_idx();
+  const int64_t t0 = (int64_t)blockIdx.x * TW;
+  const int tvalid = (int)min<int64_t>(TW, T - t0);   // >= 1
+
+  // ---------------------------------------------------------------- 1. logits
+  const int ks = w % SK, wn = (w / SK) % WN, wm = w / (SK * WN);
+  const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + t0 * d));
+  const uint8_t* wb = uniform_ptr(reinterpret_cast<const uint8_t*>(wr));
+  uint32_t voff[NB];
+  int sub_of[NB];
+  uint32_t lds_of[NB];
+  bool is_x[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int b = 4 * i + w, s = b / C::NJ, j = b % C::NJ;
+    const int r = 16 * j + (lane >> 2);
+    const int c = (lane & 3) ^ swz(r);
+    sub_of[i] = s;
+    lds_of[i] = (uint32_t)(s * C::SUB_B + j * 1024);
+    is_x[i] = 16 * j < TW;
+    const int grow = is_x[i] ? min(r, tvalid - 1) : min(r - TW, E - 1);
+    voff[i] = (uint32_t)grow * (uint32_t)d * 2u + (uint32_t)c * 16u;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  const int nst = (d + C::KC - 1) / C::KC;
+  auto issue = [&](int st) {
+    const int buf = st % NS, k0 = st * C::KC;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int kk = min(k0 + 32 * sub_of[i], d - 32);
+      const uint8_t* base = uniform_ptr((is_x[i] ? xb : wb) + (int64_t)kk * 2);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * C::STAGE_B) + lds_of[i]);
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(m0), "v"(voff[i]), "s"(base)
+          : "memory", "m0");
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int st = 0; st < NS - 1 && st < nst; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    wait_stages<NB>(min(nst - 1, st + NS - 2) - st);
+    asm volatile("s_barrier" ::: "memory");
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const uint8_t* sb = lds + (st % NS) * C::STAGE_B;
+    const int k0 = st * C::KC;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s % SK != ks || k0 + 32 * s >= d) continue;
+      const uint8_t* sub = sb + s * C::SUB_B;
+      bf16x8_t xf[TM], wf[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r = wm * 16 * TM + 16 * a + (lane & 15);
+        xf[a] = *reinterpret_cast<const bf16x8_t*>(sub + r * 64 + (((lane >> 4) ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = TW + wn * 16 * TN + 16 * b + (lane & 15);
+        wf[b] = *reinterpret_cast<const bf16x8_t*>(sub + r * 64 + (((lane >> 4) ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], xf[a], acc[a][b], 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ------------------------------------------------- 2. partial logits -> LDS
+  float* LG = reinterpret_cast<float*>(lds);
+  uint64_t* MG = reinterpret_cast<uint64_t*>(lds + LG_B);
+  int32_t* IDL = reinterpret_cast<int32_t*>(lds + LG_B + MG_B);
+  int32_t* running = reinterpret_cast<int32_t*>(lds + LG_B + MG_B + ID_B);
+  float* MX = reinterpret_cast<float*>(lds + LG_B + MG_B + ID_B + 256 * 4);
+  float* PS = MX + TW;
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      // lane: token (lane & 15) of block a, experts 4 (lane >> 4) .. + 3 of block b
+      const int tok = wm * 16 * TM + 16 * a + (lane & 15);
+      const int e = wn * 16 * TN + 16 * b + 4 * (lane >> 4);
+      *reinterpret_cast<f32x4_t*>(LG + (ks * TW + tok) * LS + e) = acc[a][b];
+    }
+  __syncthreads();
+  bool nan_seen = false;
+  for (int u = tid; u < TW * (EP / 4); u += 256) {
+    const int tok = u / (EP / 4), e4 = (u % (EP / 4)) * 4;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(LG + tok * LS + e4);
+#pragma unroll
+    for (int q = 1; q < SK; ++q) {
+      const f32x4_t p = *reinterpret_cast<const f32x4_t*>(LG + (q * TW + tok) * LS + e4);
+      v[0] += p[0]; v[1] += p[1]; v[2] += p[2]; v[3] += p[3];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e4 + j;
+      if (e < E) {
+        float l = v[j] + (bias ? bias[e] : 0.f);
+        if (l != l) { nan_seen = true; l = -INFINITY; }
+        v[j] = l;
+      } else {
+        v[j] = -INFINITY;
+      }
+    }
+    *reinterpret_cast<f32x4_t*>(LG + tok * LS + e4) = v;
+    if (logits && tok < tvalid && e4 < E) {
+      float* dst = logits + (t0 + tok) * E + e4;
+      if ((E & 3) == 0) {
+        *reinterpret_cast<f32x4_t*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e4 + j < E) dst[j] = v[j];
+      }
+    }
+  }
+  if (__any(nan_seen) && lane == 0) raise_flag(flag, MOE_FLAG_NAN_LOGIT);
+  __syncthreads();
+
+  // ------------------------------------------------------------- 3. top-K
+  const int t = tid % TW, sl = tid / TW;
+  uint64_t kk[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) kk[j] = 0;   // below every real key
+  {
+    constexpr int VW = SW >= 4 ? 4 : SW;
+    const float* row = LG + t * LS + sl * SW;
+#pragma unroll 2
+    for (int e0 = 0; e0 < SW; e0 += VW) {
+      float v[VW];
+      if constexpr (VW == 4) {
+        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(row + e0);
+        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+      } else {
+#pragma unroll
+        for (int j = 0; j < VW; ++j) v[j] = row[e0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        const int e = sl * SW + e0 + j;
+        if (e < E) insert<KL>(kk, make_key(v[j], e));
+      }
+    }
+  }
+#pragma unroll
+  for (int step = 1; step < NSL; step <<= 1) {
+    const int q = sl / (2 * step);
+    if (sl % (2 * step) == step) {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) MG[(q * TW + t) * KL + j] = kk[j];
+    }
+    __syncthreads();
+    if (sl % (2 * step) == 0) {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) insert<KL>(kk, MG[(q * TW + t) * KL + j]);
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------- 4. weights
+  const float lmax = key_value(kk[0]);   // meaningful in threads sl == 0
+  float denom = 0.f;
+  if (renorm) {
+#pragma unroll
+    for (int k = 0; k < KL; ++k)
+      if (k < K) denom += expf(key_value(kk[k]) - lmax);
+  } else {
+    if (sl == 0) MX[t] = lmax;
+    __syncthreads();
+    const float m = MX[t];
+    const float* row = LG + t * LS + sl * SW;
+    float s = 0.f;
+    for (int j = 0; j < SW; ++j)
+      if (sl * SW + j < E) s += expf(row[j] - m);
+    PS[sl * TW + t] = s;
+    __syncthreads();
+    for (int q = 0; q < NSL; ++q) denom += PS[q * TW + t];
+  }
+  if (sl == 0 && t < tvalid) {
+    const int64_t o = (t0 + t) * K;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      if (k < K) {
+        const int e = key_expert(kk[k]);
+        ids[o + k] = e;
+        wout[o + k] = expf(key_value(kk[k]) - lmax) / denom;
+        IDL[t * K + k] = e;
+      }
+    }
+  }
+  if (local_rank == nullptr) return;
+  __syncthreads();
+
+  // --------------------------------------------------- 5. dispatch histogram
+  if (w == 0) {
+    for (int e = lane; e < E; e += 64) running[e] = 0;
+    const int npairs = tvalid * K;
+    for (int base = 0; base < npairs; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < npairs;
+      const int e = valid ? IDL[i] : 0;
+      uint64_t same = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? ones : ~ones;
+      }
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const int before = __popcll(same & below);
+      const int total = __popcll(same);
+      const int r = valid ? running[e] + before : 0;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // every lane has read running[] before the updates
+      if (valid) {
+        local_rank[t0 * K + i] = r;
+        if (before == total - 1) running[e] += total;   // the class's highest lane
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)blockIdx.x * E + e] = running[e];
+  }
+}
+
+}  // namespace router
+}  // namespace moe
+
+namespace {
+template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS>
+moe_status_t launch_cfg(const uint16_t* x, const uint16_t* wr, const float* bias, int64_t T, int d, int E, int K,
+                        int renorm, int32_t* ids, float* w, float* logits, int32_t* lr, int32_t* cc, uint32_t* flag,
+                        hipStream_t s) {
+  constexpr int TW = moe::router::Cfg<TM, TN, WM, WN, SK, NSUB, NS>::TW;
+  const dim3 grid((unsigned)((T + TW - 1) / TW)), block(256);
+  if (K <= 2) {
+    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 2>), grid, block, 0, s, x, wr,
+                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+  } else if (K <= 8) {
+    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 8>), grid, block, 0, s, x, wr,
+                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+  } else {
+    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 32>), grid, block, 0, s, x, wr,
+                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+}  // namespace
+
+// tokens per workgroup (= tokens per dispatch-histogram chunk) for E experts
+extern "C" int moe_route_fused_tokens(int32_t E) { return E <= 32 ? 16 : E <= 64 ? 32 : 64; }
+
+extern "C" moe_status_t moe_route_fused_launch(const uint16_t* x, const uint16_t* wr, const float* bias, int64_t T,
+                                               int32_t d, int32_t E, int32_t K, int32_t renorm, int32_t* ids,
+                                               float* w, float* logits, int32_t* local_rank, int32_t* chunk_counts,
+                                               uint32_t* flag, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  if (E <= 32) return launch_cfg<1, 2, 1, 1, 4, 4, 4>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
+                                                       chunk_counts, flag, s);
+  if (E <= 64) return launch_cfg<2, 2, 1, 2, 2, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
+                                                       chunk_counts, flag, s);
+  if (E <= 128) return launch_cfg<2, 4, 2, 2, 1, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
+                                                        chunk_counts, flag, s);
+  return launch_cfg<2, 8, 2, 2, 1, 2, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts,
+                                         flag, s);
+}

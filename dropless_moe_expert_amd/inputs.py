@@ -40,7 +40,7 @@ import numpy as np
 import torch
 
 # stream tags
-_LOGITS, _BIAS, _X, _WGATE, _WUP, _WDOWN, _DY, _SIZES = range(8)
+_LOGITS, _BIAS, _X, _WGATE, _WUP, _WDOWN, _DY, _SIZES, _WROUTER = range(9)
 _ROW_CHUNK = 2048
 
 
@@ -151,6 +151,26 @@ def routed_layer(name: str, T: int, d: int, E: int, K: int, f: int, seed: int,
     if dy:
         L.dy = _normal_rows(seed, _DY, T, d)
     return L
+
+
+def router_weights(seed: int, E: int, d: int) -> torch.Tensor:
+    """Router weight bf16 [E, d], N(0, 1/sqrt(d)): with x ~ N(0,1) each token's
+    score x . w_e is about N(0, 1), the logit distribution of the routed
+    workloads."""
+    return _normal_rows(seed, _WROUTER, E, d, std=float(1.0 / np.sqrt(d)))
+
+
+def expert_bias(name: str) -> Optional[torch.Tensor]:
+    """The per-expert logit bias of a routed workload (fp32 [E]) or None."""
+    c = WORKLOADS[name]
+    if name == "tiny":
+        b = np.zeros(c["E"], dtype=np.float32)
+        b[7] = -1.0e4
+    elif name == "finegrained":
+        b = _rng(c["seed"], _BIAS).standard_normal(c["E"], dtype=np.float32) * np.float32(1.5)
+    else:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32))
 
 
 def zipf_group_sizes(seed: int, E: int, M: int, s: float = 1.2, n_empty: int = 2) -> np.ndarray:

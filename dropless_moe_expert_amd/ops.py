@@ -37,6 +37,7 @@ EXPORTS = (
     "moe_pack_weights_bytes",
     "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
+    "moe_route_fused_workspace_bytes", "moe_route_fused", "moe_permute_routed",
     # measurement only (include/moe_bench.h)
     "moe_bench_mfma_flops", "moe_bench_mfma_ceiling",
 )
@@ -87,6 +88,9 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights_mxfp8": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, sz, P]),
+            "moe_route_fused_workspace_bytes": (sz, [i64, i32, i32]),
+            "moe_route_fused": (ctypes.c_int, [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, sz, P, P]),
+            "moe_permute_routed": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P, P]),
             "moe_bench_mfma_flops": (i64, [i64, i32]),
             "moe_bench_mfma_ceiling": (ctypes.c_int, [i32, i32, P, i64, P]),
         }
@@ -209,6 +213,57 @@ def permute_mxfp8(x: torch.Tensor, topk_ids: torch.Tensor, E: int, flag: Optiona
                                    _ptr(out["xq"]), _ptr(out["xs"]), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(flag), _stream(dev)),
            "moe_permute_mxfp8")
+    return out
+
+
+def route_fused(x: torch.Tensor, w_router: torch.Tensor, K: int, bias: Optional[torch.Tensor] = None,
+                renormalize: bool = True, keep_logits: bool = False, histogram: bool = True,
+                flag: Optional[torch.Tensor] = None):
+    """Fused router: logits = x w_router^T (+ bias), top-K, softmax weights and
+    (histogram=True) the dispatch histogram for permute_routed.
+    -> dict(topk_ids int32 [T,K], topk_w fp32 [T,K], logits fp32 [T,E] or None,
+            ws uint8 workspace or None)."""
+    assert x.dtype == torch.bfloat16 and w_router.dtype == torch.bfloat16
+    assert x.dim() == 2 and w_router.dim() == 2 and x.shape[1] == w_router.shape[1]
+    assert x.is_contiguous() and w_router.is_contiguous()
+    dev = _dev(x, w_router, bias)
+    T, d = x.shape
+    E = w_router.shape[0]
+    if bias is not None:
+        assert bias.dtype == torch.float32 and bias.shape == (E,) and bias.is_contiguous()
+    out = dict(topk_ids=torch.empty((T, K), dtype=torch.int32, device=dev),
+               topk_w=torch.empty((T, K), dtype=torch.float32, device=dev),
+               logits=torch.empty((T, E), dtype=torch.float32, device=dev) if keep_logits else None,
+               ws=None)
+    nbytes = 0
+    if histogram:
+        nbytes = max(int(lib().moe_route_fused_workspace_bytes(T, E, K)), 256)
+        out["ws"] = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_fused(_ptr(x), _ptr(w_router), _ptr(bias), T, d, E, K, int(renormalize),
+                                 _ptr(out["topk_ids"]), _ptr(out["topk_w"]), _ptr(out["logits"]), _ptr(out["ws"]),
+                                 nbytes, _ptr(flag), _stream(dev)), "moe_route_fused")
+    return out
+
+
+def permute_routed(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, ws: torch.Tensor,
+                   flag: Optional[torch.Tensor] = None):
+    """moe_permute's outputs from route_fused's histogram (ws is consumed)."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2 and ws is not None
+    dev = _dev(topk_ids, x, ws)
+    T, K = topk_ids.shape
+    d = 0 if x is None else x.shape[1]
+    M = T * K
+    out = dict(
+        group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
+        group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        perm_src=torch.empty(M, dtype=torch.int32, device=dev),
+        perm_dst=torch.empty(M, dtype=torch.int32, device=dev),
+        x_perm=None if x is None else torch.empty((M, d), dtype=torch.bfloat16, device=dev),
+    )
+    _check(lib().moe_permute_routed(_ptr(x), _ptr(topk_ids), T, d, E, K, _ptr(out["group_sizes"]),
+                                    _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
+                                    _ptr(out["x_perm"]), _ptr(ws), ws.numel() * ws.element_size(), _ptr(flag),
+                                    _stream(dev)), "moe_permute_routed")
     return out
 
 

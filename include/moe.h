@@ -117,6 +117,44 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
                                uint32_t* err_flag, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Fused router (blog section "Optimization 2: Expert parallelism to
+ * integrate Dispatch and Combine": the router runs as fused kernels right
+ * before the dispatch; intro: a learned router picks each token's Top-K
+ * experts).  One kernel computes
+ *   logits[t, e] = sum_k x[t, k] * w_router[e, k]  (+ bias[e])   fp32 accumulation
+ * and from them the same selection and weights as moe_route_topk (equal
+ * logits go to the lower index; renormalize as there), and, when ws is
+ * given, the dispatch histogram that moe_permute_routed consumes.
+ *
+ * x         bf16 [T, d]   tokens, 16-byte aligned
+ * w_router  bf16 [E, d]   router weight, 16-byte aligned
+ * bias      fp32 [E]      added to every token's logits; NULL: none
+ * topk_ids  int32 [T, K], topk_w fp32 [T, K]   out, as moe_route_topk
+ * logits    fp32 [T, E]   out if not NULL (16-byte aligned): the logits the
+ *                         selection was made on (NaN already turned -inf)
+ * ws        NULL, or moe_route_fused_workspace_bytes(T, E, K) bytes,
+ *           256-byte aligned: receives each (token, expert) pair's rank among
+ *           the earlier pairs of its token block with the same expert, and
+ *           every block's per-expert counts.  Pass it unchanged to
+ *           moe_permute_routed (same T, E, K).
+ * Errors: MOE_FLAG_NAN_LOGIT in *err_flag for a NaN logit (taken as -inf).
+ * Limits: 1 <= K <= min(E, 32), E <= 256, d % 32 == 0, d >= 32, T*K < 2^31.
+ * ------------------------------------------------------------------------ */
+size_t moe_route_fused_workspace_bytes(int64_t T, int32_t E, int32_t K);
+moe_status_t moe_route_fused(const uint16_t* x, const uint16_t* w_router, const float* bias, int64_t T, int32_t d,
+                             int32_t E, int32_t K, int32_t renormalize, int32_t* topk_ids, float* topk_w,
+                             float* logits, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream);
+
+/* Permute from the fused router's histogram: the outputs of moe_permute
+ * (same definitions, bit for bit) for the ids moe_route_fused wrote, with
+ * that call's ws (the rank pass is skipped; the ws contents are consumed:
+ * pass a fresh moe_route_fused result each time).  Limits as moe_permute. */
+moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                                int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                                int32_t* perm_dst, uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Grouped GEMM (blog section "Optimization 1: Grouped GEMM": all experts in
  * one call, each with its true token count, only rows with valid tokens
  * computed; counts on the device).  Group g owns rows [o_g, o_g + s_g) of the

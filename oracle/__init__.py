@@ -51,6 +51,7 @@ def lib():
                 "oracle_bf16_round_array": (None, [P, P, i64]),
                 "oracle_e4m3_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
                 "oracle_f64_to_e4m3": (ctypes.c_uint8, [ctypes.c_double]),
+                "oracle_route_logits": (None, [P, P, P, i64, i32, i32, P]),
                 "oracle_route_topk": (None, [P, i64, i32, i32, i32, P, P]),
                 "oracle_permute": (None, [P, i64, i32, i32, P, P, P, P]),
                 "oracle_gather_rows": (None, [P, P, i64, i32, i32, P]),
@@ -135,6 +136,18 @@ def f64_to_e4m3(v) -> np.ndarray:
 # --------------------------------------------------------------------------
 # the layer, step by step
 # --------------------------------------------------------------------------
+
+def route_logits(x, w_router, bias=None) -> np.ndarray:
+    """Router scores in fp64: x [T,d] bf16, w_router [E,d] bf16, bias fp32 [E] or None -> [T,E]."""
+    xs, ws = u16(x), u16(w_router)
+    T, d = xs.shape
+    E = ws.shape[0]
+    assert ws.shape[1] == d
+    b = None if bias is None else _np(bias, np.float32)
+    out = np.empty((T, E), np.float64)
+    lib().oracle_route_logits(_p(xs), _p(ws), _p(b), T, d, E, _p(out))
+    return out
+
 
 def route_topk(logits, K: int, renormalize: bool = True):
     """-> ids int32 [T,K], w fp32 [T,K]."""

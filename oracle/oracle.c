@@ -129,6 +129,27 @@ uint8_t oracle_f64_to_e4m3(double x)
 }
 
 /* ------------------------------------------------------------------------- */
+/* S0: router scores.  [BLOG] intro: a learned router scores every expert for  */
+/* each token; section "Optimization 2": fused router kernels produce them     */
+/* right before the dispatch.  The score is the linear map of the token:       */
+/*   logits[t, e] = sum_k x[t, k] * w[e, k]  (+ bias[e]),  in fp64.            */
+/* ------------------------------------------------------------------------- */
+
+void oracle_route_logits(const uint16_t* x, const uint16_t* w, const float* bias, int64_t T, int32_t d,
+                         int32_t E, double* logits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k)
+                acc += oracle_bf16_to_f64(x[t * d + k]) * oracle_bf16_to_f64(w[(int64_t)e * d + k]);
+            logits[t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* S1: router top-K with softmax gating.                                      */
 /* [BLOG] intro: a learned router activates the Top-K experts of each token.  */
 /* [CH1 §4.1]: softmax = exp of (logit - row max), divided by the row sum.    */

@@ -211,3 +211,16 @@ def test_finegrained_forward_backward_full(ops):
         dw1_ref = orc.grouped_wgrad(DG, xp, sizes, groups=[e])[0]
         assert mre(host_u16(g["dw1p"][e]), dw1_ref) <= BF16_TOL, e
     assert torch.all(g["dw2"][empty] == 0) and torch.all(g["dw1p"][empty] == 0)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "finegrained"])
+def test_route_fused_full(ops, name):
+    """The fused router at the routed workloads' full sizes (every token: the
+    oracle's fp64 scores take a few seconds), with its dispatch maps."""
+    from gpu_util import check_route_fused
+    c = inputs.WORKLOADS[name]
+    say("route fused full", name)
+    x = inputs.workload(name, weights=False).x
+    wr = inputs.router_weights(c["seed"], c["E"], c["d"])
+    n_near, _ = check_route_fused(ops, x, wr, inputs.expert_bias(name), c["K"])
+    assert n_near <= c["T"] // 200, n_near

@@ -12,7 +12,8 @@ import torch
 
 import oracle as orc
 from dropless_moe_expert_amd import inputs
-from gpu_util import (BF16_TOL, MX_TOL, W_RTOL, bf16, dev, host_u16, max_rel_err, rel_l2, say)
+from gpu_util import (BF16_TOL, MX_TOL, W_RTOL, bf16, check_route_fused, dev, host_u16, max_rel_err, rel_l2,
+                      say)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +40,78 @@ def test_route_topk(ops, T, E, K, renorm):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=W_RTOL, atol=1e-30)
+
+
+# -------------------------------------------------------------- fused router
+
+@pytest.mark.parametrize("T,d,E,K,renorm,bias_std", [
+    (256, 128, 8, 2, 1, 0.0),      # 16-token blocks, experts padded to 32
+    (1000, 256, 60, 6, 0, 1.5),    # 32-token blocks, ragged tail, E not a multiple of 16
+    (777, 512, 128, 8, 1, 1.5),    # 64-token blocks, ragged tail
+    (300, 96, 256, 20, 1, 1.0),    # 256 experts, d not a multiple of a stage, 32-slot lists
+    (70, 32, 1, 1, 1, 0.0),        # one expert, the smallest d
+    (64, 64, 16, 16, 0, 0.0),      # K = E
+    (33, 4096, 32, 32, 1, 0.5),    # K = E = 32, long contraction
+    (0, 64, 8, 2, 1, 0.0),
+])
+def test_route_fused(ops, T, d, E, K, renorm, bias_std):
+    say("route fused", T, d, E, K, renorm, bias_std)
+    rng = np.random.default_rng(T * 13 + E * 7 + d)
+    x = bf16(rng, T, d)
+    wr = bf16(rng, E, d, scale=1.0 / np.sqrt(d))
+    bias = torch.from_numpy((rng.standard_normal(E) * bias_std).astype(np.float32)) if bias_std else None
+    n_near, _ = check_route_fused(ops, x, wr, bias, K, bool(renorm))
+    assert n_near <= max(2, T // 50), n_near
+
+
+def test_route_fused_ties_and_tiny_workload(ops):
+    """Exact ties (duplicated router rows score identically on both sides:
+    the lower expert comes first) and the tiny workload's router, whose bias
+    keeps expert 7 empty."""
+    say("route fused ties")
+    rng = np.random.default_rng(5)
+    T, d, E, K = 200, 128, 16, 4
+    w = rng.standard_normal((E, d)).astype(np.float32) / np.sqrt(d)
+    w[1::2] = w[0::2]                 # experts 2j and 2j + 1 identical
+    wr = inputs.to_bf16(w)
+    x = bf16(rng, T, d)
+    _, out = check_route_fused(ops, x, wr, None, K)
+    lg = out["logits"].cpu().numpy()
+    assert np.array_equal(lg[:, 0::2], lg[:, 1::2])
+    ids = out["topk_ids"].cpu().numpy()
+    pos = {(t, int(e)): k for t in range(T) for k, e in enumerate(ids[t])}
+    for t in range(T):
+        for e in ids[t]:
+            if e % 2 == 1:            # the odd twin is picked only after its even twin
+                assert (t, int(e) - 1) in pos and pos[(t, int(e) - 1)] < pos[(t, int(e))]
+    c = inputs.WORKLOADS["tiny"]
+    x = inputs.workload("tiny", weights=False).x
+    wr = inputs.router_weights(c["seed"], c["E"], c["d"])
+    _, out = check_route_fused(ops, x, wr, inputs.expert_bias("tiny"), c["K"])
+    assert not np.any(out["topk_ids"].cpu().numpy() == 7)
+
+
+def test_route_fused_nan_and_unfused_agreement(ops):
+    """A NaN in a token row raises the flag and scores -inf for that token
+    (the lowest experts are then picked, as moe_route_topk does); on the same
+    logits, moe_route_topk returns the fused kernel's ids."""
+    say("route fused nan")
+    rng = np.random.default_rng(9)
+    T, d, E, K = 100, 256, 64, 8
+    x = bf16(rng, T, d)
+    x[17, 5] = float("nan")
+    wr = bf16(rng, E, d, scale=1.0 / 16)
+    flag = ops.new_flag("cuda")
+    out = ops.route_fused(dev(x), dev(wr), K, keep_logits=True, flag=flag)
+    ids2, w2 = ops.route_topk(out["logits"], K)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & ops.FLAG_NAN_LOGIT
+    ids = out["topk_ids"].cpu().numpy()
+    assert ids[17].tolist() == list(range(K))
+    assert np.all(np.isneginf(out["logits"][17].cpu().numpy()))
+    np.testing.assert_array_equal(ids, ids2.cpu().numpy())
+    ok = np.arange(T) != 17
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy()[ok], w2.cpu().numpy()[ok], rtol=W_RTOL)
 
 
 # ------------------------------------------------------------------- permute

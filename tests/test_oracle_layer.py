@@ -80,6 +80,33 @@ def test_route_ties_and_invariants(orc):
 
 # --------------------------------------------------------------------------- permutation
 
+def test_route_logits_closed_forms(orc):
+    """Router scores: a hand-worked 2x2 by 2x3 product, one-hot tokens (which
+    read one column of the router weight each: a transposed operand or a wrong
+    index shows), zero tokens (bias only) and linearity in the bias."""
+    bf = inputs.to_bf16
+    x = bf(np.array([[1.0, 2.0], [3.0, 4.0]], np.float32))
+    w = bf(np.array([[1.0, 0.0], [1.0, 1.0], [0.0, -1.0]], np.float32))
+    # by hand: [1*1+2*0, 1*1+2*1, 1*0+2*(-1)] and [3, 3+4, -4]
+    assert orc.route_logits(x, w).tolist() == [[1.0, 3.0, -2.0], [3.0, 7.0, -4.0]]
+    b = np.array([0.5, -2.0, 8.0], np.float32)
+    assert orc.route_logits(x, w, b).tolist() == [[1.5, 1.0, 6.0], [3.5, 5.0, 4.0]]
+
+    rng = np.random.default_rng(7)
+    T, d, E = 9, 40, 6
+    cols = rng.integers(0, d, T)
+    onehot = np.zeros((T, d), np.float32)
+    onehot[np.arange(T), cols] = 1.0
+    wr = bf(rng.standard_normal((E, d)).astype(np.float32))
+    bias = rng.standard_normal(E).astype(np.float32)
+    got = orc.route_logits(bf(onehot), wr, bias)
+    wf = orc.bf16_to_f64(wr)
+    want = wf[:, cols].T + bias.astype(np.float64)[None, :]
+    assert np.array_equal(got, want)
+    assert np.array_equal(orc.route_logits(bf(np.zeros((3, d), np.float32)), wr, bias),
+                          np.tile(bias.astype(np.float64), (3, 1)))
+
+
 @pytest.mark.parametrize("T,E,K", [(256, 8, 2), (1000, 128, 8), (17, 5, 1), (3, 256, 8), (1, 1, 1)])
 def test_permute_is_stable_counting_sort(orc, T, E, K):
     rng = np.random.default_rng(T * 31 + E)
