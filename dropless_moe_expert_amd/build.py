@@ -39,9 +39,14 @@ def _hipcc() -> str:
     return h
 
 
+# per-source flags: the router keeps MFMA accumulators in arch VGPRs (in
+# AGPRs the register allocator rotated them through copies on every k step)
+SOURCE_FLAGS = {"route_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + CFLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -10,13 +10,18 @@
 //
 // One workgroup (4 wavefronts) per block of TW tokens:
 //  1. logits [TW, E] = x[t0 : t0 + TW] W_r^T on bf16 MFMA (16x16x32, fp32
-//     accumulation).  Rows of x and of W_r stream through an LDS ring of NS
-//     stages of KC = 32 NSUB k-values, filled by direct-to-LDS loads issued
-//     NS - 1 stages ahead; every stage issues the same number of loads (the
-//     sub-steps past d re-read the last one), so one vmcnt count per stage
-//     distance is exact.  A wavefront owns a (16 TM tokens) x (16 TN experts)
-//     block of the logits and, with SK > 1, every SK-th 32-k sub-step.
-//  2. The k-slices' partial logits meet in LDS; one pass sums them in slice
+//     accumulation), in one of two ways:
+//     E > 32: rows of x and of W_r stream through an LDS ring of NS stages of
+//     KC = 32 NSUB k-values, filled by direct-to-LDS loads issued NS - 1
+//     stages ahead.  A stage holds NSUB / 2 pairs of 32-k steps as 128-byte
+//     rows, so each load instruction reads whole cache lines (8 rows x 128
+//     bytes); every stage issues the same number of loads (pairs past d
+//     re-read the last one), so one vmcnt count per stage distance is exact.
+//     A wavefront owns a (16 TM tokens) x (16 TN experts) block of the logits
+//     and, with SK > 1, every SK-th 32-k step.
+//     E <= 32: the wavefronts split the contraction and stream their
+//     fragments straight into registers (route_fused_reg_kernel).
+//  2. The partial logit blocks meet in LDS; one pass sums them in block
 //     order, adds the bias, turns NaN into -inf (flag) and writes the optional
 //     fp32 logits.
 //  3. Top-K: thread (token t, slice sl) keeps the KL >= K best keys of its
@@ -48,9 +53,10 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
-// 16-byte slot of chunk c in LDS row r (64-byte rows): c ^ ((r >> 1) & 3),
-// the pattern under which the 16-row fragment reads below hit distinct banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+// 16-byte slot of chunk c (0..7) in LDS row r (128-byte rows): c ^ ((r >> 1) & 7).
+// A fragment read (16 rows, one chunk) then touches rows of both parities at
+// eight distinct slots each: the 16 lanes of a quarter-wave hit 256 distinct bytes.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // sortable key: larger logit first, then lower expert index first
 __device__ __forceinline__ uint64_t make_key(float v, int e) {
@@ -86,132 +92,49 @@ template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS>
 struct Cfg {
   static constexpr int TW = WM * 16 * TM;          // tokens per workgroup
   static constexpr int EP = WN * 16 * TN;          // experts, padded
-  static constexpr int ROWS = TW + EP;             // 64-byte LDS rows per sub-step
-  static constexpr int SUB_B = ROWS * 64;
+  static constexpr int ROWS = TW + EP;             // LDS rows per pair of steps (x rows, then W_r rows)
+  static constexpr int PAIR_B = ROWS * 128;        // one pair of 32-k steps: 128-byte rows
+  static constexpr int NP = NSUB / 2;              // pairs per stage
   static constexpr int KC = 32 * NSUB;
-  static constexpr int STAGE_B = NSUB * SUB_B;
-  static constexpr int NJ = ROWS / 16;             // 1-KB load blocks per sub-step
-  static constexpr int NB = NSUB * NJ / 4;         // load blocks per wavefront and stage
+  static constexpr int STAGE_B = NP * PAIR_B;
+  static constexpr int NJ = ROWS / 8;              // 1-KB load blocks (8 rows) per pair
+  static constexpr int NB = NP * NJ / 4;           // load blocks per wavefront and stage
   static constexpr int LS = EP + 4;                // logits row stride (floats)
   static constexpr int NSL = 256 / TW;             // top-K slices per token
   static constexpr int SW = EP / NSL;              // experts per slice
   static_assert(WM * WN * SK == 4, "four wavefronts");
-  static_assert((NSUB * NJ) % 4 == 0 && NSUB % SK == 0 && EP % NSL == 0, "tiling");
+  static_assert(NSUB % 2 == 0 && (NP * NJ) % 4 == 0 && NSUB % SK == 0 && EP % NSL == 0, "tiling");
   static_assert(NS >= 2 && NS <= 4, "the stage wait covers up to two stages ahead");
 };
 
-template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS, int KL>
-__global__ __launch_bounds__(256) void route_fused_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ wr,
-                                                          const float* __restrict__ bias, int64_t T, int d, int E,
-                                                          int K, int renorm, int32_t* __restrict__ ids,
-                                                          float* __restrict__ wout, float* __restrict__ logits,
-                                                          int32_t* __restrict__ local_rank,
-                                                          int32_t* __restrict__ chunk_counts, uint32_t* flag) {
-  using C = Cfg<TM, TN, WM, WN, SK, NSUB, NS>;
-  constexpr int TW = C::TW, EP = C::EP, LS = C::LS, NSL = C::NSL, SW = C::SW, NB = C::NB;
-  constexpr int LG_B = SK * TW * LS * 4;
-  constexpr int MG_B = (NSL / 2) * TW * KL * 8;
-  constexpr int ID_B = TW * 32 * 4;
-  constexpr int EPI_B = LG_B + MG_B + ID_B + 256 * 4 + TW * 4 + NSL * TW * 4;
-  constexpr int LDS_B = (NS * C::STAGE_B > EPI_B) ? NS * C::STAGE_B : EPI_B;
-  __shared__ __align__(1024) uint8_t lds[LDS_B];
+// Epilogue shared by both kernels: on entry LG = lds holds SK partial logit
+// blocks [SK][TW][EP + 4] (fp32) written by the caller, and BIAS the bias.
+template <int TW, int EP, int SK, int KL>
+struct Epi {
+  static constexpr int LS = EP + 4;                // logits row stride (floats)
+  static constexpr int NSL = 256 / TW;             // top-K slices per token
+  static constexpr int SW = EP / NSL;              // experts per slice
+  static constexpr int LG_B = SK * TW * LS * 4;
+  static constexpr int MG_B = (NSL / 2) * TW * KL * 8;
+  static constexpr int ID_B = TW * 32 * 4;
+  static constexpr int BYTES = LG_B + MG_B + ID_B + 256 * 4 + TW * 4 + NSL * TW * 4;
+  static_assert(EP % NSL == 0 && SW >= 2, "slices");
+};
 
+template <int TW, int EP, int SK, int KL>
+__device__ __forceinline__ void finish_block(uint8_t* lds, const float* BIAS, int64_t t0, int tvalid, int E, int K,
+                                             int renorm, int32_t* __restrict__ ids, float* __restrict__ wout,
+                                             float* __restrict__ logits, int32_t* __restrict__ local_rank,
+                                             int32_t* __restrict__ chunk_counts, uint32_t* flag) {
+  using P = Epi<TW, EP, SK, KL>;
+  constexpr int LS = P::LS, NSL = P::NSL, SW = P::SW, LG_B = P::LG_B, MG_B = P::MG_B, ID_B = P::ID_B;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_idx();
-  const int64_t t0 = (int64_t)blockIdx.x * TW;
-  const int tvalid = (int)min<int64_t>(TW, T - t0);   // >= 1
-
-  // ---------------------------------------------------------------- 1. logits
-  const int ks = w % SK, wn = (w / SK) % WN, wm = w / (SK * WN);
-  const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + t0 * d));
-  const uint8_t* wb = uniform_ptr(reinterpret_cast<const uint8_t*>(wr));
-  uint32_t voff[NB];
-  int sub_of[NB];
-  uint32_t lds_of[NB];
-  bool is_x[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int b = 4 * i + w, s = b / C::NJ, j = b % C::NJ;
-    const int r = 16 * j + (lane >> 2);
-    const int c = (lane & 3) ^ swz(r);
-    sub_of[i] = s;
-    lds_of[i] = (uint32_t)(s * C::SUB_B + j * 1024);
-    is_x[i] = 16 * j < TW;
-    const int grow = is_x[i] ? min(r, tvalid - 1) : min(r - TW, E - 1);
-    voff[i] = (uint32_t)grow * (uint32_t)d * 2u + (uint32_t)c * 16u;
-  }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
-  const int nst = (d + C::KC - 1) / C::KC;
-  auto issue = [&](int st) {
-    const int buf = st % NS, k0 = st * C::KC;
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int kk = min(k0 + 32 * sub_of[i], d - 32);
-      const uint8_t* base = uniform_ptr((is_x[i] ? xb : wb) + (int64_t)kk * 2);
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * C::STAGE_B) + lds_of[i]);
-      asm volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "s_nop 0\n\t"
-          "global_load_lds_dwordx4 %1, %2"
-          :
-          : "s"(m0), "v"(voff[i]), "s"(base)
-          : "memory", "m0");
-    }
-  };
-
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int st = 0; st < NS - 1 && st < nst; ++st) issue(st);
-  for (int st = 0; st < nst; ++st) {
-    wait_stages<NB>(min(nst - 1, st + NS - 2) - st);
-    asm volatile("s_barrier" ::: "memory");
-    if (st + NS - 1 < nst) issue(st + NS - 1);
-    const uint8_t* sb = lds + (st % NS) * C::STAGE_B;
-    const int k0 = st * C::KC;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-      if (s % SK != ks || k0 + 32 * s >= d) continue;
-      const uint8_t* sub = sb + s * C::SUB_B;
-      bf16x8_t xf[TM], wf[TN];
-#pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        const int r = wm * 16 * TM + 16 * a + (lane & 15);
-        xf[a] = *reinterpret_cast<const bf16x8_t*>(sub + r * 64 + (((lane >> 4) ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int r = TW + wn * 16 * TN + 16 * b + (lane & 15);
-        wf[b] = *reinterpret_cast<const bf16x8_t*>(sub + r * 64 + (((lane >> 4) ^ swz(r)) << 4));
-      }
-#pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], xf[a], acc[a][b], 0, 0, 0);
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // ------------------------------------------------- 2. partial logits -> LDS
   float* LG = reinterpret_cast<float*>(lds);
   uint64_t* MG = reinterpret_cast<uint64_t*>(lds + LG_B);
   int32_t* IDL = reinterpret_cast<int32_t*>(lds + LG_B + MG_B);
   int32_t* running = reinterpret_cast<int32_t*>(lds + LG_B + MG_B + ID_B);
   float* MX = reinterpret_cast<float*>(lds + LG_B + MG_B + ID_B + 256 * 4);
   float* PS = MX + TW;
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      // lane: token (lane & 15) of block a, experts 4 (lane >> 4) .. + 3 of block b
-      const int tok = wm * 16 * TM + 16 * a + (lane & 15);
-      const int e = wn * 16 * TN + 16 * b + 4 * (lane >> 4);
-      *reinterpret_cast<f32x4_t*>(LG + (ks * TW + tok) * LS + e) = acc[a][b];
-    }
   __syncthreads();
   bool nan_seen = false;
   for (int u = tid; u < TW * (EP / 4); u += 256) {
@@ -226,7 +149,7 @@ __global__ __launch_bounds__(256) void route_fused_kernel(const uint16_t* __rest
     for (int j = 0; j < 4; ++j) {
       const int e = e4 + j;
       if (e < E) {
-        float l = v[j] + (bias ? bias[e] : 0.f);
+        float l = v[j] + BIAS[e];
         if (l != l) { nan_seen = true; l = -INFINITY; }
         v[j] = l;
       } else {
@@ -351,25 +274,259 @@ __global__ __launch_bounds__(256) void route_fused_kernel(const uint16_t* __rest
   }
 }
 
+template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS, int KL>
+__global__ __launch_bounds__(256) void route_fused_lds_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          const float* __restrict__ bias, int64_t T, int d, int E,
+                                                          int K, int renorm, int32_t* __restrict__ ids,
+                                                          float* __restrict__ wout, float* __restrict__ logits,
+                                                          int32_t* __restrict__ local_rank,
+                                                          int32_t* __restrict__ chunk_counts, uint32_t* flag) {
+  using C = Cfg<TM, TN, WM, WN, SK, NSUB, NS>;
+  constexpr int TW = C::TW, EP = C::EP, LS = C::LS, NB = C::NB;
+  constexpr int EPI_B = Epi<TW, EP, SK, KL>::BYTES;
+  constexpr int LDS_B = (NS * C::STAGE_B > EPI_B) ? NS * C::STAGE_B : EPI_B;
+  __shared__ __align__(1024) uint8_t lds[LDS_B];
+  __shared__ float BIAS[256];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_idx();
+  const int64_t t0 = (int64_t)blockIdx.x * TW;
+  const int tvalid = (int)min<int64_t>(TW, T - t0);   // >= 1
+  const float bias_r = (bias != nullptr && tid < E) ? bias[tid] : 0.f;   // lands during the k loop
+
+  // ---------------------------------------------------------------- 1. logits
+  const int ks = w % SK, wn = (w / SK) % WN, wm = w / (SK * WN);
+  const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + t0 * d));
+  const uint8_t* wb = uniform_ptr(reinterpret_cast<const uint8_t*>(wr));
+  // load slot i of wavefront w: block b = 4i + w = (pair p, 8-row block j);
+  // lane l fills slot l & 7 of row 8j + l / 8 with chunk (l & 7) ^ swz(row)
+  uint32_t voff[NB], lds_of[NB], hi_adj[NB];
+  int pair_of[NB];
+  bool is_x[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int b = 4 * i + w, p = b / C::NJ, j = b % C::NJ;
+    const int r = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    pair_of[i] = p;
+    lds_of[i] = (uint32_t)(p * C::PAIR_B + j * 1024);
+    is_x[i] = 8 * j < TW;
+    const int grow = is_x[i] ? min(r, tvalid - 1) : min(r - TW, E - 1);
+    voff[i] = (uint32_t)grow * (uint32_t)d * 2u + (uint32_t)c * 16u;
+    hi_adj[i] = c >= 4 ? 64u : 0u;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+  const int nst = (d + C::KC - 1) / C::KC;
+  // the last pair starts at last_pair; when only its first step exists
+  // (d % 64 == 32) its upper 64 bytes re-read the lower ones
+  const int last_pair = ((d - 1) / 64) * 64;
+  const bool half_pair = (d - last_pair) == 32;
+  auto issue = [&](int st) {
+    const int buf = st % NS, k0 = st * C::KC;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int kb = min(k0 + 64 * pair_of[i], last_pair);
+      const uint8_t* base = uniform_ptr((is_x[i] ? xb : wb) + (int64_t)kb * 2);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)(buf * C::STAGE_B) + lds_of[i]);
+      const uint32_t vo = (half_pair && kb == last_pair) ? voff[i] - hi_adj[i] : voff[i];
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(m0), "v"(vo), "s"(base)
+          : "memory", "m0");
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int st = 0; st < NS - 1 && st < nst; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    wait_stages<NB>(min(nst - 1, st + NS - 2) - st);
+    asm volatile("s_barrier" ::: "memory");
+    if (st + NS - 1 < nst) issue(st + NS - 1);
+    const uint8_t* sb = lds + (st % NS) * C::STAGE_B;
+    const int k0 = st * C::KC;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s % SK != ks || k0 + 32 * s >= d) continue;
+      // step s: pair s / 2, chunks 4 (s & 1) .. + 3 of each 128-byte row
+      const uint8_t* pr = sb + (s >> 1) * C::PAIR_B;
+      const int cc = 4 * (s & 1) + (lane >> 4);
+      bf16x8_t xf[TM], wf[TN];
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const int r = wm * 16 * TM + 16 * a + (lane & 15);
+        xf[a] = *reinterpret_cast<const bf16x8_t*>(pr + r * 128 + ((cc ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int r = TW + wn * 16 * TN + 16 * b + (lane & 15);
+        wf[b] = *reinterpret_cast<const bf16x8_t*>(pr + r * 128 + ((cc ^ swz(r)) << 4));
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[b], xf[a], acc[a][b], 0, 0, 0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // ------------------------------------------------- 2. partial logits -> LDS
+  float* LG = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      // lane: token (lane & 15) of block a, experts 4 (lane >> 4) .. + 3 of block b
+      const int tok = wm * 16 * TM + 16 * a + (lane & 15);
+      const int e = wn * 16 * TN + 16 * b + 4 * (lane >> 4);
+      *reinterpret_cast<f32x4_t*>(LG + (ks * TW + tok) * LS + e) = acc[a][b];
+    }
+  BIAS[tid] = bias_r;
+  finish_block<TW, EP, SK, KL>(lds, BIAS, t0, tvalid, E, K, renorm, ids, wout, logits, local_rank, chunk_counts,
+                               flag);
+}
+
+// Small E: the four wavefronts split the contraction instead (wavefront w owns
+// the whole TW x E block for the 64-k pairs of steps q = w, w + 4, ...), so no
+// operand is shared and each wavefront streams its x and W_r fragments from
+// global memory straight into registers, two steps in flight; a pair's two
+// loads cover whole 128-byte lines of every row.  With few experts the W_r
+// share of the traffic is small and this avoids the LDS round trip.
+typedef const __attribute__((address_space(1))) bf16x8_t gbf16x8_t;
+
+template <int TM, int TN>
+struct Frags {
+  bf16x8_t x[TM], w[TN];
+  __device__ __forceinline__ void load(const uint8_t* xb, const uint8_t* wb, const uint32_t (&xo)[TM],
+                                       const uint32_t (&wo)[TN], uint32_t kbytes) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a) x[a] = *(gbf16x8_t*)(xb + xo[a] + kbytes);
+#pragma unroll
+    for (int b = 0; b < TN; ++b) w[b] = *(gbf16x8_t*)(wb + wo[b] + kbytes);
+  }
+  __device__ __forceinline__ void mma(f32x4_t (&acc)[TM][TN]) const {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[b], x[a], acc[a][b], 0, 0, 0);
+  }
+};
+
+template <int TM, int TN, int KL>
+__global__ __launch_bounds__(256) void route_fused_reg_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ wr,
+                                                              const float* __restrict__ bias, int64_t T, int d, int E,
+                                                              int K, int renorm, int32_t* __restrict__ ids,
+                                                              float* __restrict__ wout, float* __restrict__ logits,
+                                                              int32_t* __restrict__ local_rank,
+                                                              int32_t* __restrict__ chunk_counts, uint32_t* flag) {
+  constexpr int TW = 16 * TM, EP = 16 * TN, LS = EP + 4;
+  __shared__ __align__(16) uint8_t lds[Epi<TW, EP, 4, KL>::BYTES];
+  __shared__ float BIAS[256];
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_idx();
+  const int64_t t0 = (int64_t)blockIdx.x * TW;
+  const int tvalid = (int)min<int64_t>(TW, T - t0);   // >= 1
+  const float bias_r = (bias != nullptr && tid < E) ? bias[tid] : 0.f;
+
+  const uint8_t* xb = uniform_ptr(reinterpret_cast<const uint8_t*>(x + t0 * d));
+  const uint8_t* wb = uniform_ptr(reinterpret_cast<const uint8_t*>(wr));
+  uint32_t xo[TM], wo[TN];   // byte offsets of this lane's rows (rows past the end re-read the last one)
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+    xo[a] = (uint32_t)min(16 * a + (lane & 15), tvalid - 1) * (uint32_t)d * 2u + (uint32_t)(lane >> 4) * 16u;
+#pragma unroll
+  for (int b = 0; b < TN; ++b)
+    wo[b] = (uint32_t)min(16 * b + (lane & 15), E - 1) * (uint32_t)d * 2u + (uint32_t)(lane >> 4) * 16u;
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the loop body is branch-free (the last prefetch re-reads the last pair)
+  // so that the compiler's vmcnt waits keep the next pair in flight; the
+  // sched_barrier fences stop the scheduler from sinking loads to their use
+  const int nsteps = d / 32;
+  const int npairs = nsteps / 2;
+  const int cnt = (w < npairs) ? (npairs - w + 3) / 4 : 0;
+  Frags<TM, TN> fa, fb;
+  if (cnt > 0) {
+    fa.load(xb, wb, xo, wo, (uint32_t)w * 128u);
+    fb.load(xb, wb, xo, wo, (uint32_t)w * 128u + 64u);
+    for (int j = 0; j < cnt; ++j) {
+      const uint32_t next = (uint32_t)(w + 4 * min(j + 1, cnt - 1)) * 128u;
+      __builtin_amdgcn_sched_barrier(0);
+      fa.mma(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      fa.load(xb, wb, xo, wo, next);
+      __builtin_amdgcn_sched_barrier(0);
+      fb.mma(acc);
+      __builtin_amdgcn_sched_barrier(0);
+      fb.load(xb, wb, xo, wo, next + 64u);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if ((nsteps & 1) && w == (npairs & 3)) {   // an unpaired last step (d % 64 == 32)
+    fa.load(xb, wb, xo, wo, (uint32_t)(nsteps - 1) * 64u);
+    fa.mma(acc);
+  }
+  float* LG = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int tok = 16 * a + (lane & 15);
+      const int e = 16 * b + 4 * (lane >> 4);
+      *reinterpret_cast<f32x4_t*>(LG + (w * TW + tok) * LS + e) = acc[a][b];
+    }
+  BIAS[tid] = bias_r;
+  finish_block<TW, EP, 4, KL>(lds, BIAS, t0, tvalid, E, K, renorm, ids, wout, logits, local_rank, chunk_counts, flag);
+}
+
 }  // namespace router
 }  // namespace moe
 
 namespace {
 template <int TM, int TN, int WM, int WN, int SK, int NSUB, int NS>
-moe_status_t launch_cfg(const uint16_t* x, const uint16_t* wr, const float* bias, int64_t T, int d, int E, int K,
+moe_status_t launch_lds(const uint16_t* x, const uint16_t* wr, const float* bias, int64_t T, int d, int E, int K,
                         int renorm, int32_t* ids, float* w, float* logits, int32_t* lr, int32_t* cc, uint32_t* flag,
                         hipStream_t s) {
   constexpr int TW = moe::router::Cfg<TM, TN, WM, WN, SK, NSUB, NS>::TW;
   const dim3 grid((unsigned)((T + TW - 1) / TW)), block(256);
   if (K <= 2) {
-    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 2>), grid, block, 0, s, x, wr,
-                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+    hipLaunchKernelGGL((moe::router::route_fused_lds_kernel<TM, TN, WM, WN, SK, NSUB, NS, 2>), grid, block, 0, s, x,
+                       wr, bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
   } else if (K <= 8) {
-    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 8>), grid, block, 0, s, x, wr,
-                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+    hipLaunchKernelGGL((moe::router::route_fused_lds_kernel<TM, TN, WM, WN, SK, NSUB, NS, 8>), grid, block, 0, s, x,
+                       wr, bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
   } else {
-    hipLaunchKernelGGL((moe::router::route_fused_kernel<TM, TN, WM, WN, SK, NSUB, NS, 32>), grid, block, 0, s, x, wr,
-                       bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+    hipLaunchKernelGGL((moe::router::route_fused_lds_kernel<TM, TN, WM, WN, SK, NSUB, NS, 32>), grid, block, 0, s, x,
+                       wr, bias, T, d, E, K, renorm, ids, w, logits, lr, cc, flag);
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+template <int TM, int TN>
+moe_status_t launch_reg(const uint16_t* x, const uint16_t* wr, const float* bias, int64_t T, int d, int E, int K,
+                        int renorm, int32_t* ids, float* w, float* logits, int32_t* lr, int32_t* cc, uint32_t* flag,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)((T + 16 * TM - 1) / (16 * TM))), block(256);
+  if (K <= 2) {
+    hipLaunchKernelGGL((moe::router::route_fused_reg_kernel<TM, TN, 2>), grid, block, 0, s, x, wr, bias, T, d, E, K,
+                       renorm, ids, w, logits, lr, cc, flag);
+  } else if (K <= 8) {
+    hipLaunchKernelGGL((moe::router::route_fused_reg_kernel<TM, TN, 8>), grid, block, 0, s, x, wr, bias, T, d, E, K,
+                       renorm, ids, w, logits, lr, cc, flag);
+  } else {
+    hipLaunchKernelGGL((moe::router::route_fused_reg_kernel<TM, TN, 32>), grid, block, 0, s, x, wr, bias, T, d, E, K,
+                       renorm, ids, w, logits, lr, cc, flag);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -383,12 +540,13 @@ extern "C" moe_status_t moe_route_fused_launch(const uint16_t* x, const uint16_t
                                                float* w, float* logits, int32_t* local_rank, int32_t* chunk_counts,
                                                uint32_t* flag, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  if (E <= 32) return launch_cfg<1, 2, 1, 1, 4, 4, 4>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
-                                                       chunk_counts, flag, s);
-  if (E <= 64) return launch_cfg<2, 2, 1, 2, 2, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
-                                                       chunk_counts, flag, s);
-  if (E <= 128) return launch_cfg<2, 4, 2, 2, 1, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank,
-                                                        chunk_counts, flag, s);
-  return launch_cfg<2, 8, 2, 2, 1, 2, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts,
+  if (E <= 32) return launch_reg<1, 2>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts, flag, s);
+  if (E <= 64)
+    return launch_lds<2, 2, 1, 2, 2, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts,
+                                           flag, s);
+  if (E <= 128)
+    return launch_lds<2, 4, 2, 2, 1, 4, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts,
+                                           flag, s);
+  return launch_lds<2, 8, 2, 2, 1, 2, 3>(x, wr, bias, T, d, E, K, renorm, ids, w, logits, local_rank, chunk_counts,
                                          flag, s);
 }
