@@ -182,6 +182,72 @@ def routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep):
     return kern, t_route + t_perm + t_g1 + t_g2 + t_comb, saved
 
 
+def graph_time(torch, fn, reps: int = 20) -> float:
+    """ms per call of fn from one HIP-graph replay of reps back-to-back calls:
+    the kernels' own time, without the host cost of each Python call (which
+    exceeds a ~10 us kernel)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        best = ms if best is None else min(best, ms)
+    del g
+    return best
+
+
+def router_entries(torch, ops, inputs, L, dev, timer, flag) -> dict:
+    """The fused router (logits product, top-K, weights and the dispatch
+    histogram in one kernel) and the permute that starts from its histogram,
+    beside the unfused chain it replaces: the logits product as a library GEMM
+    (torch.mm, fp32 logits written out), route_topk, permute."""
+    T, d, E, K = L.T, L.d, L.E, L.K
+    M = T * K
+    x = L.x.to(dev)
+    wr = inputs.router_weights(L.seed, E, d).to(dev)
+    b = inputs.expert_bias(L.name)
+    b = None if b is None else b.to(dev)
+    t_rf = graph_time(torch, lambda: ops.route_fused(x, wr, K, bias=b, flag=flag))
+
+    def route_then_permute():
+        r = ops.route_fused(x, wr, K, bias=b, flag=flag)
+        return ops.permute_routed(x, r["topk_ids"], E, r["ws"], flag=flag)
+
+    t_pr = max(graph_time(torch, route_then_permute) - t_rf, 0.0)   # the histogram is consumed: time the pair
+    wt = wr.t().contiguous()
+
+    def logits_gemm():
+        lg = torch.mm(x, wt).float()
+        return lg if b is None else lg + b
+
+    lg = logits_gemm()
+    t_mm = graph_time(torch, logits_gemm)
+    ids, _ = ops.route_topk(lg, K, flag=flag)
+    t_rt = graph_time(torch, lambda: ops.route_topk(lg, K, flag=flag))
+    t_p = graph_time(torch, lambda: ops.permute(x, ids, E, flag=flag))
+    tw = 16 if E <= 32 else 32 if E <= 64 else 64
+    nchunk = (T + tw - 1) // tw
+    return {
+        "route_fused": byte_entry(t_rf, T * d * 2 + E * d * 2 + (E * 4 if b is not None else 0) + M * 8 + M * 4
+                                  + nchunk * E * 4),
+        "permute_routed": byte_entry(t_pr, T * d * 2 + M * 4 + M * d * 2 + M * 8 + 2 * nchunk * E * 4),
+        "unfused_for_comparison_ms": {"logits_gemm_torch_mm_fp32_out": round(t_mm, 4), "route_topk": round(t_rt, 4),
+                                      "permute": round(t_p, 4)},
+        "timing": "HIP-graph replay of 20 back-to-back calls, per call",
+    }
+
+
 def bench_mixtral(torch, ops, L, dev, timer, flag, steps) -> dict:
     lg, x = L.logits.to(dev), L.x.to(dev)
     w1 = ops.pack_weights(L.w1p.to(dev), ops.MOE_EPI_SWIGLU)
@@ -468,6 +534,7 @@ def main() -> int:
         t0 = time.time()
         Lm = inputs.workload("mixtral")
         workloads["mixtral"] = bench_mixtral(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
+        workloads["mixtral"]["router"] = router_entries(torch, ops, inputs, Lm, dev, timer, flag)
         log(f"mixtral layer: {workloads['mixtral']['ms_per_step']:.3f} ms, "
             f"{workloads['mixtral']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
         torch.cuda.empty_cache()
@@ -479,6 +546,7 @@ def main() -> int:
         t0 = time.time()
         Lf = inputs.workload("finegrained")
         workloads["finegrained"] = bench_finegrained(torch, ops, Lf, dev, timer, flag, max(5, args.steps // 5))
+        workloads["finegrained"]["router"] = router_entries(torch, ops, inputs, Lf, dev, timer, flag)
         log(f"fine-grained fwd+bwd: {workloads['finegrained']['ms_per_step']:.3f} ms, "
             f"{workloads['finegrained']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
         torch.cuda.empty_cache()
