@@ -66,6 +66,10 @@ def lib():
                 "oracle_grouped_dgrad_rows": (None, [P, P, P, i32, i32, i32, P, i64, P]),
                 "oracle_grouped_wgrad": (None, [P, P, P, i32, i32, i32, P, i32, P]),
                 "oracle_mx_grouped_wgrad": (None, [P, P, P, P, P, i32, i32, i32, P]),
+                "oracle_e2m1_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
+                "oracle_f64_to_e2m1": (ctypes.c_uint8, [ctypes.c_double]),
+                "oracle_mxfp4_quantize_rows": (None, [P, i64, i32, P, P]),
+                "oracle_mx4_grouped_gemm_rows": (None, [P, P, P, P, P, i32, i32, i32, i32, P, i64, P]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -248,6 +252,43 @@ def mx_grouped_gemm(Aq, As, Bq, Bs, group_sizes, swiglu: bool = False, rows=None
     out = np.zeros((r.size, nout), np.uint16)
     lib().oracle_mx_grouped_gemm_rows(_p(aq), _p(as_), _p(bq), _p(bs), _p(s), G, N, Kd, int(swiglu),
                                       _p(r), r.size, _p(out))
+    return out
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    L = lib()
+    c = _np(codes, np.uint8)
+    table = np.array([L.oracle_e2m1_to_f64(i) for i in range(16)], dtype=np.float64)
+    return table[c & 15]
+
+
+def f64_to_e2m1(v) -> np.ndarray:
+    L = lib()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    return np.array([L.oracle_f64_to_e2m1(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def mxfp4_quantize(x):
+    """32-blocks along columns -> (codes [R,C] uint8, one E2M1 code per byte; scales [R,C/32] uint8)."""
+    xs = u16(x)
+    R, C = xs.shape
+    assert C % 32 == 0
+    q = np.empty((R, C), np.uint8)
+    s = np.empty((R, C // 32), np.uint8)
+    lib().oracle_mxfp4_quantize_rows(_p(xs), R, C, _p(q), _p(s))
+    return q, s
+
+
+def mx4_grouped_gemm(Aq, As, Bq, Bs, group_sizes, swiglu: bool = False, rows=None) -> np.ndarray:
+    """Codes one per byte: Aq [M,K], Bq [G,N,K]; scales [M,K/32], [G,N,K/32]."""
+    aq, as_, bq, bs = (_np(t, np.uint8) for t in (Aq, As, Bq, Bs))
+    s = _np(group_sizes, np.int32)
+    G, N, Kd = bq.shape
+    r = _rows(rows, int(s.sum()))
+    nout = N // 2 if swiglu else N
+    out = np.zeros((r.size, nout), np.uint16)
+    lib().oracle_mx4_grouped_gemm_rows(_p(aq), _p(as_), _p(bq), _p(bs), _p(s), G, N, Kd, int(swiglu),
+                                       _p(r), r.size, _p(out))
     return out
 
 

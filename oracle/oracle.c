@@ -417,6 +417,109 @@ void oracle_mx_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const uin
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* MXFP4: E2M1 elements with an E8M0 scale per 32 (the gfx950 analog of the  */
+/* page's planned NVFP4, [BLOG] "Optimization 1" closing plans; MX element   */
+/* formats per the OCP MX v1.0 specification).                               */
+/* E2M1: sign bit, 2 exponent bits (bias 1), 1 mantissa bit; no Inf/NaN.      */
+/* ------------------------------------------------------------------------- */
+
+double oracle_e2m1_to_f64(uint8_t c)
+{
+    int s = (c >> 3) & 1, ex = (c >> 1) & 3, m = c & 1;
+    double mag = ex == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, ex - 1);
+    return s ? -mag : mag;
+}
+
+/* round to nearest representable magnitude, ties to the even code (mantissa
+   bit 0), saturating at 6; the sign is kept (also for a zero result). */
+uint8_t oracle_f64_to_e2m1(double v)
+{
+    uint8_t sign = signbit(v) ? 8 : 0;
+    double a = fabs(v);
+    if (a >= 6.0) return sign | 7;        /* saturation: 6 is the largest magnitude */
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 8; ++c) {
+        double d = fabs(oracle_e2m1_to_f64((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) { bd = d; best = c; }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* one 32-block: scale 2^e with e = floor(log2 amax) - 2 (2 = largest E2M1
+   exponent), clamped to [-127, 127]; codes one per byte */
+static void mx4_block(const double* v, int n, uint8_t* codes, uint8_t* scale)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    if (amax == 0.0) {
+        *scale = 0;
+        for (int i = 0; i < n; ++i) codes[i] = signbit(v[i]) ? 8 : 0;
+        return;
+    }
+    int ex;
+    frexp(amax, &ex);
+    int e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    *scale = (uint8_t)(e + 127);
+    for (int i = 0; i < n; ++i) codes[i] = oracle_f64_to_e2m1(ldexp(v[i], -e));
+}
+
+/* q[rows, cols]: one code per byte; s[rows, cols/32] */
+void oracle_mxfp4_quantize_rows(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q, uint8_t* s)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double v[32];
+        for (int b = 0; b < cols / 32; ++b) {
+            for (int i = 0; i < 32; ++i) v[i] = oracle_bf16_to_f64(x[r * cols + b * 32 + i]);
+            mx4_block(v, 32, q + r * cols + b * 32, s + r * (cols / 32) + b);
+        }
+    }
+}
+
+/* MXFP4 grouped GEMM on the listed rows of A: dequantise exactly, fp64
+   contraction, bf16 output; swiglu: h = silu(g) * u over B rows [0, N/2) and
+   [N/2, N) of each expert.  Codes one per byte: A [M, K], B [G, N, K];
+   scales [M, K/32], [G, N, K/32]. */
+void oracle_mx4_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq, const uint8_t* Bs,
+                                  const int32_t* sizes, int32_t G, int32_t N, int32_t Kd, int32_t swiglu,
+                                  const int64_t* rows, int64_t nrows, uint16_t* C)
+{
+    int32_t nb = Kd / 32;
+    int32_t nout = swiglu ? N / 2 : N;
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t q = 0; q < nrows; ++q) {
+        int64_t r = rows[q], base;
+        int e = group_of_row(sizes, G, r, &base);
+        if (e < 0) continue;
+        double* av = (double*)malloc(sizeof(double) * (size_t)Kd);
+        for (int i = 0; i < Kd; ++i)
+            av[i] = ldexp(oracle_e2m1_to_f64(Aq[r * Kd + i]), (int)As[r * nb + i / 32] - 127);
+        const uint8_t* bq = Bq + (int64_t)e * N * Kd;
+        const uint8_t* bs = Bs + (int64_t)e * N * nb;
+        double acc2[2];
+        for (int n = 0; n < nout; ++n) {
+            for (int h = 0; h < (swiglu ? 2 : 1); ++h) {
+                int64_t col = n + (int64_t)h * nout;
+                double acc = 0.0;
+                for (int i = 0; i < Kd; ++i)
+                    acc += av[i] * ldexp(oracle_e2m1_to_f64(bq[col * Kd + i]), (int)bs[col * nb + i / 32] - 127);
+                acc2[h] = acc;
+            }
+            if (swiglu) {
+                double g = acc2[0], u = acc2[1];
+                C[q * nout + n] = oracle_f64_to_bf16(g / (1.0 + exp(-g)) * u);
+            } else {
+                C[q * nout + n] = oracle_f64_to_bf16(acc2[0]);
+            }
+        }
+        free(av);
+    }
+}
+
 /* MXFP8 weight gradient [BLOG "What specialized optimizations are required  */
 /* for dropless MoE?": group-aware MXFP8 quantisation; "Optimization 1":     */
 /* MXFP8 block scaling].  Both operands quantised along their rows by the     */

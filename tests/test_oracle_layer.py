@@ -264,6 +264,81 @@ def test_mx_grouped_gemm_vs_torch_dequant(orc):
         o += s
 
 
+# E2M1 by the format's definition (sign, 2 exponent bits with bias 1, one
+# mantissa bit; exponent 0 is subnormal: 0.5 * m), written out by hand
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def test_e2m1_decode_encode(orc):
+    dec = orc.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    assert dec.tolist() == E2M1_VALUES
+    assert np.array_equal(np.signbit(dec), np.array([c >= 8 for c in range(16)]))
+    # every code round-trips
+    assert orc.f64_to_e2m1(dec).tolist() == list(range(16))
+    # ties go to the even mantissa bit; past 6 saturates; the sign of zero is kept
+    cases = {0.25: 0, 0.75: 2, 1.25: 2, 1.75: 4, 2.5: 4, 3.5: 6, 5.0: 6, 6.5: 7, 1e30: 7, 0.2: 0, 0.3: 1,
+             -0.3: 9, -0.0: 8, -0.1: 8, 2.9: 5, 4.9: 6, 5.1: 7}
+    got = orc.f64_to_e2m1(np.array(list(cases.keys())))
+    assert got.tolist() == list(cases.values())
+    # brute force: the code is a nearest representable value of the same sign
+    v = np.linspace(-7.5, 7.5, 6001)
+    c = orc.f64_to_e2m1(v)
+    a, dec = np.abs(v), np.abs(orc.e2m1_to_f64(c))
+    mags = np.array(E2M1_VALUES[:8])
+    dist = np.abs(a[:, None] - mags[None, :]).min(axis=1)
+    inside = a <= 6
+    assert np.array_equal(np.abs(dec - a)[inside], dist[inside])
+    assert np.all(dec[~inside] == 6.0)
+    assert np.all((c >= 8) == np.signbit(v))
+
+
+def test_mx4_block_closed_forms(orc):
+    bf = inputs.to_bf16
+    row = np.zeros((4, 32), np.float32)
+    row[0, :8] = [6.0, -4.0, 3.0, 1.5, 0.5, -0.0, 2.0, 1.0]   # amax 6: scale 2^0, every value on the grid
+    row[1, 0] = 1.0                                            # amax 1: scale 2^-2, 1.0 -> 4.0 (code 6)
+    row[1, 1] = 0.1                                            # 0.4 -> 0.5 (code 1)
+    row[2, 0] = 7.0                                            # amax 7: scale 2^0, 7 saturates to 6
+    q, s = orc.mxfp4_quantize(bf(row))
+    assert s[:, 0].tolist() == [127, 125, 127, 0]
+    assert q[0, :8].tolist() == [7, 14, 5, 3, 1, 8, 4, 2]
+    assert q[1, :2].tolist() == [6, 1]
+    assert q[2, 0] == 7 and q[3].tolist() == [0] * 32
+    # large and tiny blocks: the scale follows floor(log2 amax) - 2 across the exponent range
+    big = np.zeros((3, 32), np.float32)
+    big[0, 0], big[1, 0], big[2, 0] = 2.0 ** 100, 2.0 ** -100, 3.0 * 2.0 ** 20
+    _, s = orc.mxfp4_quantize(bf(big))
+    assert s[:, 0].tolist() == [127 + 98, 127 - 102, 127 + 19]   # 3 * 2^20 = 1.5 * 2^21
+
+
+def test_mx4_grouped_gemm_vs_numpy_dequant(orc):
+    rng = np.random.default_rng(16)
+    sizes = np.array([7, 0, 13, 2], np.int32)
+    M, N, Kd = int(sizes.sum()), 16, 128
+    A, B = _bf16(rng, M, Kd), _bf16(rng, len(sizes), N, Kd, scale=0.1)
+    aq, as_ = orc.mxfp4_quantize(A)
+    bq, bs = orc.mxfp4_quantize(orc.u16(B).reshape(-1, Kd))
+    bq, bs = bq.reshape(len(sizes), N, Kd), bs.reshape(len(sizes), N, Kd // 32)
+    table = np.array(E2M1_VALUES)
+
+    def deq(q, s):
+        return table[q] * np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=-1)
+
+    a, b = deq(aq, as_), deq(bq, bs)
+    C = orc.mx4_grouped_gemm(aq, as_, bq, bs, sizes)
+    o = 0
+    for e, s in enumerate(sizes):
+        assert_correctly_rounded(orc, C[o:o + s], a[o:o + s] @ b[e].T)
+        o += s
+    H = orc.mx4_grouped_gemm(aq, as_, bq, bs, sizes, swiglu=True)
+    o = 0
+    for e, s in enumerate(sizes):
+        gu = a[o:o + s] @ b[e].T
+        g, u = gu[:, :N // 2], gu[:, N // 2:]
+        assert_correctly_rounded(orc, H[o:o + s], torch.nn.functional.silu(torch.from_numpy(g)).numpy() * u, 1e-6)
+        o += s
+
+
 def test_mx_grouped_wgrad_vs_torch_dequant(orc):
     # operands quantised down their rows, blocks restarting at every group
     # (a 40-row group has a short second block); the contraction runs over
