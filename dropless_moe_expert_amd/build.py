@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libmoe.so")
 
-SOURCES = ["abi.cpp", "route.hip", "route_fused.hip", "permute.hip", "combine.hip", "quant.hip", "grouped_gemm.hip", "gg_bf16.hip", "gg_fwd_mx.hip", "bench_ceiling.hip"]
+SOURCES = ["abi.cpp", "route.hip", "route_fused.hip", "permute.hip", "combine.hip", "quant.hip", "grouped_gemm.hip", "gg_bf16.hip", "gg_fwd_mx.hip", "gg_mx4.hip", "bench_ceiling.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

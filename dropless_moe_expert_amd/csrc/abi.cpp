@@ -31,6 +31,7 @@ moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_
 moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*,
                                               int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*,
                                               hipStream_t);
+moe_status_t mxfp4_quantize_launch(const uint16_t*, int64_t, int32_t, uint8_t*, uint8_t*, hipStream_t);
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
                                          uint8_t*, uint8_t*, uint32_t*, hipStream_t);
 moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
@@ -185,6 +186,15 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
                                    perm_src, perm_dst, x_perm, ws, S(stream));
 }
 
+moe_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (rows < 0 || cols < 128 || cols % 128) return rows < 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_ALIGNMENT;
+  return mxfp4_quantize_launch(x, rows, cols, codes, scales, S(stream));
+}
+
 size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
   (void)desc;
   return 0;
@@ -201,7 +211,20 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   if (!A || !B || !C || !group_sizes) return MOE_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MOE_ERR_ALIGNMENT;
   if (C_aux && d->epilogue != MOE_EPI_SWIGLU_MXFP8 && !aligned16(C_aux)) return MOE_ERR_ALIGNMENT;
-  if (d->dtype != MOE_DTYPE_BF16 && d->dtype != MOE_DTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype != MOE_DTYPE_BF16 && d->dtype != MOE_DTYPE_MXFP8 && d->dtype != MOE_DTYPE_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_DTYPE_MXFP4) {
+    if (d->ragged != MOE_RAGGED_M || d->b_layout != MOE_B_NK || d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
+    if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+    if (d->K < 128 || d->K % 128) return MOE_ERR_UNSUPPORTED;
+    if (d->epilogue == MOE_EPI_SWIGLU && (d->N / 2) % 8) return MOE_ERR_UNSUPPORTED;
+    if (C_aux || !A_scale || !B_scale) return MOE_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (reinterpret_cast<uintptr_t>(B_scale) & 3u))
+      return MOE_ERR_ALIGNMENT;
+    if (d->N % 8) return MOE_ERR_UNSUPPORTED;
+    if (d->m_cap == 0) return MOE_OK;
+    return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, err_flag, S(stream));
+  }
   if (d->out_dtype != MOE_OUT_BF16 && d->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
   if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU && d->epilogue != MOE_EPI_SWIGLU_MXFP8)
     return MOE_ERR_UNSUPPORTED;

@@ -22,6 +22,7 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
 moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s);                             // gg_bf16.hip
 moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s);              // gg_fwd_mx.hip
 moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s);                                       // gg_fwd_mx.hip
+moe_status_t launch_fwd_mx4(const GGArgs& a, int epilogue, hipStream_t s);                          // gg_mx4.hip
 }  // namespace moe
 
 extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A, const uint8_t* As, const void* B,
@@ -46,6 +47,7 @@ extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A,
   a.p_tiles = 0;
   if (d->ragged == MOE_RAGGED_M) {
     if (d->dtype == MOE_DTYPE_MXFP8) return launch_fwd_mx(a, d->epilogue, d->b_layout == MOE_B_PACKED, s);
+    if (d->dtype == MOE_DTYPE_MXFP4) return launch_fwd_mx4(a, d->epilogue, s);
     return launch_fwd(a, d->epilogue, d->out_dtype == MOE_OUT_F32, d->b_layout, s);
   }
   if (d->dtype == MOE_DTYPE_MXFP8) return launch_wgrad_mx(a, s);

@@ -321,6 +321,48 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   }
 }
 
+// MXFP4 (E2M1 codes, E8M0 scale per 32 along the columns), one thread per
+// 32-element block.  Scale 2^e with e = floor(log2 amax) - 2 (2 = the largest
+// E2M1 exponent), clamped to [-127, 127]; codes round x / 2^e to the nearest
+// of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even mantissa bit, saturate
+// past 6 and keep the sign (also of a zero).  Output: codes [rows, cols / 2],
+// element 2i in the low nibble of byte i; scales stage-major [cols / 128]
+// [rows][4] (the layout the MXFP4 grouped GEMM loads a stage from).
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float m = fabsf(y);
+  const uint32_t c = m <= 0.25f ? 0u : m < 0.75f ? 1u : m <= 1.25f ? 2u : m < 1.75f ? 3u
+                   : m <= 2.5f ? 4u : m < 3.5f ? 5u : m <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
+  const int nb = cols / 32;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * nb) return;
+  const int64_t r = t / nb;
+  const int b = (int)(t - r * nb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + r * cols + b * 32);
+  float f[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) unpack8(src[v], f + 8 * v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+  const int e = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 2));
+  uint32_t w[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= e2m1_code(scale_pow2(f[8 * v + i], e)) << (4 * i);
+    w[v] = word;
+  }
+  *reinterpret_cast<uint4*>(q + r * (cols / 2) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  sc[((int64_t)(b / 4) * rows + r) * 4 + (b % 4)] = (uint8_t)(e + 127);
+}
+
 }  // namespace moe
 
 extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, const uint16_t* dh, int64_t rows,
@@ -341,6 +383,15 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
     hipLaunchKernelGGL(moe::mx_quant_t_kernel<0>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
                        group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
   }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+extern "C" moe_status_t mxfp4_quantize_launch(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q,
+                                              uint8_t* scale, hipStream_t s) {
+  const int64_t n = rows * (cols / 32);
+  if (n == 0) return MOE_OK;
+  hipLaunchKernelGGL(moe::mx4_quant_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows, cols, q,
+                     scale);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

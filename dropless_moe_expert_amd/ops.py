@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
 
-MOE_DTYPE_BF16, MOE_DTYPE_MXFP8 = 0, 1
+MOE_DTYPE_BF16, MOE_DTYPE_MXFP8, MOE_DTYPE_MXFP4 = 0, 1, 2
 MOE_RAGGED_M, MOE_RAGGED_K = 0, 1
 MOE_B_NK, MOE_B_KN, MOE_B_PACKED = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_MXFP8 = 0, 1, 2
@@ -37,7 +37,7 @@ EXPORTS = (
     "moe_pack_weights_bytes",
     "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
-    "moe_route_fused_workspace_bytes", "moe_route_fused", "moe_permute_routed",
+    "moe_route_fused_workspace_bytes", "moe_route_fused", "moe_permute_routed", "mxfp4_quantize",
     # measurement only (include/moe_bench.h)
     "moe_bench_mfma_flops", "moe_bench_mfma_ceiling",
 )
@@ -91,6 +91,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_route_fused_workspace_bytes": (sz, [i64, i32, i32]),
             "moe_route_fused": (ctypes.c_int, [P, P, P, i64, i32, i32, i32, i32, P, P, P, P, sz, P, P]),
             "moe_permute_routed": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P, P]),
+            "mxfp4_quantize": (ctypes.c_int, [P, i64, i32, P, P, P]),
             "moe_bench_mfma_flops": (i64, [i64, i32]),
             "moe_bench_mfma_ceiling": (ctypes.c_int, [i32, i32, P, i64, P]),
         }
@@ -376,6 +377,38 @@ def grouped_gemm_wgrad_mxfp8(AqT: torch.Tensor, AsT: torch.Tensor, BqT: torch.Te
     d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, G, P, Q, k_cap, m_cap)
     _check(lib().grouped_gemm(ctypes.byref(d), _ptr(AqT), _ptr(AsT), _ptr(BqT), _ptr(BsT), _ptr(group_sizes),
                               _ptr(out), None, None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (MXFP8, ragged K)")
+    return out
+
+
+def mxfp4_quantize(x: torch.Tensor):
+    """bf16 [rows, cols] (or [G, N, K] weights, quantised as G*N rows) ->
+    (codes uint8 [..., cols/2], two E2M1 codes per byte, element 2i in the low
+    nibble; scales uint8 [cols/128, rows, 4], stage-major E8M0 per 32)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    dev = _dev(x)
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    codes = torch.empty(tuple(x.shape[:-1]) + (cols // 2,), dtype=torch.uint8, device=dev)
+    scales = torch.empty((cols // 128, rows, 4), dtype=torch.uint8, device=dev)
+    _check(lib().mxfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(dev)), "mxfp4_quantize")
+    return codes, scales
+
+
+def grouped_gemm_mxfp4(Aq: torch.Tensor, As: torch.Tensor, Bq: torch.Tensor, Bs: torch.Tensor,
+                       group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
+                       out: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None):
+    """MXFP4 ragged-M grouped GEMM from mxfp4_quantize's outputs: Aq [m_cap, K/2],
+    As [K/128, m_cap, 4], Bq [G, N, K/2], Bs [K/128, G*N, 4] -> bf16 [m_cap, N]
+    (N/2 with MOE_EPI_SWIGLU: rows [0, N/2) of each expert are the gate)."""
+    dev = _dev(Aq, As, Bq, Bs, group_sizes)
+    m_cap, Kh = Aq.shape
+    G, N = Bq.shape[0], Bq.shape[1]
+    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
+    if out is None:
+        out = torch.empty((m_cap, ncols), dtype=torch.bfloat16, device=dev)
+    d = GGDesc(MOE_DTYPE_MXFP4, MOE_RAGGED_M, MOE_B_NK, epilogue, MOE_OUT_BF16, G, 0, N, 2 * Kh, m_cap)
+    _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bq), _ptr(Bs), _ptr(group_sizes), _ptr(out),
+                              None, None, 0, _ptr(flag), _stream(dev)), "grouped_gemm (mxfp4)")
     return out
 
 

@@ -203,9 +203,19 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
  *   MXFP8: K % 128 == 0 (RAGGED_M), K % 64 == 0 and K >= m_cap + 63 G
  *   (RAGGED_K).  A, B, C 16-byte aligned; scales 4-byte aligned.
+ * dtype = MOE_DTYPE_MXFP4 (RAGGED_M, B_NK, bf16 out; the gfx950 analog of
+ *   the blog's planned 4-bit format, closing of "Optimization 1"): A and B
+ *   are E2M1 codes, two per byte (element 2i in the low nibble of byte i):
+ *   A [m_cap, K/2], B [G, N, K/2]; A_scale [K/128, m_cap, 4] and
+ *   B_scale [K/128, G*N, 4] are E8M0 scales of the 32-blocks along K,
+ *   stage-major (the word of row r and 128-code stage t holds blocks 4t..4t+3),
+ *   as mxfp4_quantize writes them.  Element value = code value * 2^(scale-127).
+ *   epilogue MOE_EPI_NONE or MOE_EPI_SWIGLU (B rows [0,f) gate, [f,2f) up).
+ *   K % 128 == 0, N % 8 == 0 (N/2 % 8 for SwiGLU); C_aux must be NULL.
  * ------------------------------------------------------------------------ */
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_MXFP8 1
+#define MOE_DTYPE_MXFP4 2
 #define MOE_RAGGED_M 0
 #define MOE_RAGGED_K 1
 #define MOE_B_NK 0
@@ -309,6 +319,18 @@ moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t
 moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols, int32_t axis,
                                   const int32_t* group_sizes, int32_t G, uint8_t* q, uint8_t* scale,
                                   uint32_t* err_flag, void* stream);
+
+/* MXFP4 quantisation for the MXFP4 grouped GEMM (OCP MX E2M1 elements; the
+ * blog's planned 4-bit format, closing of "Optimization 1").  Per row, per 32
+ * consecutive columns: scale 2^e, e = floor(log2 amax) - 2 clamped to
+ * [-127, 127] (byte e + 127); codes = round-to-nearest-even of x / 2^e on
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6}, saturating, sign kept (also of zero).
+ * x bf16 [rows, cols] (16-byte aligned); codes [rows, cols/2] (16-byte
+ * aligned, element 2i in the low nibble of byte i); scales stage-major
+ * [cols/128, rows, 4].  cols % 128 == 0.  Weights [G, N, K] quantise as
+ * rows = G*N. */
+moe_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                            void* stream);
 
 /* Transposed group-aware MXFP8 quantisation, for the operands of the MXFP8
  * backward whose contraction runs down their rows (the weight gradients sum

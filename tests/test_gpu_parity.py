@@ -871,3 +871,66 @@ def test_guard_bands_every_output(ops):
     torch.cuda.synchronize()
     assert _untouched(xbuf, T * K * d, nan16) and _untouched(ybuf, T * d, nan16)
     assert not bool(torch.isnan(xbuf[: T * K * d]).any().item()) and not bool(torch.isnan(ybuf[: T * d]).any().item())
+
+
+# -------------------------------------------------------------------- MXFP4
+
+def _mx4_layout(q, s):
+    """Oracle MXFP4 (one code per byte [R, C], scales [R, C/32]) -> the boundary's
+    layout (two codes per byte, element 2i low; scales [C/128, R, 4]): data movement only."""
+    R, C = q.shape
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    st = np.ascontiguousarray(s.reshape(R, C // 128, 4).transpose(1, 0, 2))
+    return packed, st
+
+
+@pytest.mark.parametrize("R,C,scale", [(300, 384, 1.0), (1, 128, 1e-3), (77, 1024, 300.0)])
+def test_mxfp4_quantize(ops, R, C, scale):
+    """Codes and scales bit for bit the oracle's, with exact E2M1 ties, zeros
+    and signed zeros, saturation and tiny blocks mixed in."""
+    say("mxfp4 quantize", R, C, scale)
+    rng = np.random.default_rng(R + C)
+    x = (rng.standard_normal((R, C)) * scale).astype(np.float32)
+    if R > 2:
+        x[0, :32] = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -0.75, 4, 3, 2, 1.5, 1, 0.5] * 2) * scale
+        x[1, :32] = 0.0
+        x[1, 32:64] = -0.0
+        x[2, 64:96] = 1e-30
+    xb = inputs.to_bf16(x)
+    q_ref, s_ref = _mx4_layout(*orc.mxfp4_quantize(xb))
+    q, s = ops.mxfp4_quantize(dev(xb))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("swiglu,sizes,N,Kd", [
+    (False, [0, 300, 1, 0, 260], 512, 384),      # several m-tiles, empty groups, 3 stages
+    (False, [513, 7], 200, 128),                 # partial n-tile, one stage (fewer than the pipeline depth)
+    (True, [300, 0, 1, 517, 0, 33], 272, 256),   # SwiGLU, f = 136: partial output tile
+])
+def test_grouped_gemm_mxfp4(ops, swiglu, sizes, N, Kd):
+    """The MXFP4 grouped GEMM on the oracle's own codes and scales (moved into
+    the boundary's layout) against the oracle's exact-dequantisation GEMM."""
+    sizes = np.array(sizes, np.int32)
+    say("gg mxfp4", swiglu, sizes.tolist(), N, Kd)
+    rng = np.random.default_rng(31 + N + Kd)
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    aq, as_ = orc.mxfp4_quantize(A)
+    bq, bs = orc.mxfp4_quantize(orc.u16(B).reshape(-1, Kd))
+    ref = orc.mx4_grouped_gemm(aq, as_, bq.reshape(G, N, Kd), bs.reshape(G, N, Kd // 32), sizes, swiglu=swiglu)
+    apk, ast = _mx4_layout(aq, as_)
+    bpk, bst = _mx4_layout(bq, bs)
+    t = lambda a: dev(torch.from_numpy(np.ascontiguousarray(a)))
+    out = ops.grouped_gemm_mxfp4(t(apk), t(ast), t(bpk.reshape(G, N, Kd // 2)), t(bst), t(sizes),
+                                 epilogue=ops.MOE_EPI_SWIGLU if swiglu else ops.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    assert rel_l2(out[:M], ref) <= MX_TOL
+    assert max_rel_err(out[:M], ref) <= 2 * BF16_TOL
+    # the device quantiser feeding the same GEMM gives the same bits
+    q1, s1 = ops.mxfp4_quantize(dev(A))
+    q2, s2 = ops.mxfp4_quantize(dev(B))
+    out2 = ops.grouped_gemm_mxfp4(q1, s1, q2, s2, t(sizes), epilogue=ops.MOE_EPI_SWIGLU if swiglu else ops.MOE_EPI_NONE)
+    torch.cuda.synchronize()
+    assert torch.equal(out2[:M], out[:M])
