@@ -47,6 +47,7 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 MXFP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 / MXFP8 MFMA
+MXFP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 / MXFP4 MFMA
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_swiglu_dsv3_share.json")
 GEMM_SOURCE = os.path.join(ROOT, "dropless_moe_expert_amd", "csrc", "gg_bf16.hip")
@@ -145,6 +146,43 @@ def bench_mxfp8_share(torch, ops, L, dev, timer, flag) -> dict:
             "down_mxfp8": flop_entry(t_g2, f2, MXFP8_PEAK_TFLOPS),
             "gate_up_swiglu_mxfp8 (unfused)": flop_entry(t_g1, f1, MXFP8_PEAK_TFLOPS),
             "quantize_h (unfused)": byte_entry(t_qh, q(M, f)),
+        },
+    }
+
+
+def bench_mxfp4_share(torch, ops, L, dev, timer, flag) -> dict:
+    """The expert share in MXFP4 (E2M1 + E8M0/32): X quantised by
+    mxfp4_quantize, the gate/up GEMM with the SwiGLU epilogue (bf16 h), h
+    quantised, the down GEMM (weights quantised once, outside the timed
+    region)."""
+    M, d, f = L.M, L.d, L.f
+    x = L.x_perm.to(dev)
+    sizes = L.group_sizes.to(dev)
+    w1q, w1s = ops.mxfp4_quantize(L.w1p.to(dev))
+    w2q, w2s = ops.mxfp4_quantize(L.w2.to(dev))
+    xq, xs = ops.mxfp4_quantize(x)
+    h = ops.grouped_gemm_mxfp4(xq, xs, w1q, w1s, sizes, epilogue=ops.MOE_EPI_SWIGLU, flag=flag)
+    hq, hs = ops.mxfp4_quantize(h)
+    y = ops.grouped_gemm_mxfp4(hq, hs, w2q, w2s, sizes, flag=flag)
+    t_qx = timer(lambda: ops.mxfp4_quantize(x))
+    t_g1 = timer(lambda: ops.grouped_gemm_mxfp4(xq, xs, w1q, w1s, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h,
+                                                flag=flag))
+    t_qh = timer(lambda: ops.mxfp4_quantize(h))
+    t_g2 = timer(lambda: ops.grouped_gemm_mxfp4(hq, hs, w2q, w2s, sizes, out=y, flag=flag))
+    f1, f2 = 2.0 * M * 2 * f * d, 2.0 * M * d * f
+    step = t_qx + t_g1 + t_qh + t_g2
+    q = lambda R, C: R * C * 2 + R * C / 2 + R * C / 32   # read bf16, write codes and scales
+    return {
+        "workload": "deepseek-v3-shaped expert share in MXFP4 (same rows, sizes and weights; E2M1 + E8M0/32): "
+                    "quantise X, gate/up + SwiGLU, quantise H, down",
+        "ms_per_step": round(step, 4),
+        "valid_row_tflops": round((f1 + f2) / (step * 1e-3) / 1e12, 2),
+        "frac_of_mxfp4_peak": round((f1 + f2) / (step * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4),
+        "kernels": {
+            "quantize_x": byte_entry(t_qx, q(M, d)),
+            "gate_up_swiglu_mxfp4": flop_entry(t_g1, f1, MXFP4_PEAK_TFLOPS),
+            "quantize_h": byte_entry(t_qh, q(M, f)),
+            "down_mxfp4": flop_entry(t_g2, f2, MXFP4_PEAK_TFLOPS),
         },
     }
 
@@ -530,6 +568,10 @@ def main() -> int:
         workloads["dsv3_mxfp8"] = bench_mxfp8_share(torch, ops, L, dev, timer, flag)
         log(f"mxfp8 share: {workloads['dsv3_mxfp8']['ms_per_step']:.3f} ms/step "
             f"({workloads['dsv3_mxfp8']['valid_row_tflops']} TFLOP/s) [{time.time() - t0:.1f}s]")
+        torch.cuda.empty_cache()
+        workloads["dsv3_mxfp4"] = bench_mxfp4_share(torch, ops, L, dev, timer, flag)
+        log(f"mxfp4 share: {workloads['dsv3_mxfp4']['ms_per_step']:.3f} ms/step "
+            f"({workloads['dsv3_mxfp4']['valid_row_tflops']} TFLOP/s)")
         torch.cuda.empty_cache()
         t0 = time.time()
         Lm = inputs.workload("mixtral")

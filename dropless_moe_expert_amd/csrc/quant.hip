@@ -321,46 +321,57 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   }
 }
 
-// MXFP4 (E2M1 codes, E8M0 scale per 32 along the columns), one thread per
+// MXFP4 (E2M1 codes, E8M0 scale per 32 along the columns), four lanes per
 // 32-element block.  Scale 2^e with e = floor(log2 amax) - 2 (2 = the largest
 // E2M1 exponent), clamped to [-127, 127]; codes round x / 2^e to the nearest
 // of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even mantissa bit, saturate
 // past 6 and keep the sign (also of a zero).  Output: codes [rows, cols / 2],
 // element 2i in the low nibble of byte i; scales stage-major [cols / 128]
 // [rows][4] (the layout the MXFP4 grouped GEMM loads a stage from).
+// E2M1 code of y: below 2 the grid in units of 0.5 is the integers 0..4
+// (codes 0..3, and 4 = 2.0), on [2, 4) it is 2, 3, 4 (codes 4..6), on [4, 8)
+// it is 4, 6 in steps of 2 (codes 6, 7); rintf's ties-to-even on those
+// integers is the format's ties-to-even mantissa bit, and past 6 saturates
 __device__ __forceinline__ uint32_t e2m1_code(float y) {
   const float m = fabsf(y);
-  const uint32_t c = m <= 0.25f ? 0u : m < 0.75f ? 1u : m <= 1.25f ? 2u : m < 1.75f ? 3u
-                   : m <= 2.5f ? 4u : m < 3.5f ? 5u : m <= 5.0f ? 6u : 7u;
-  return c | ((__float_as_uint(y) >> 28) & 8u);
+  const float c = m < 2.f ? rintf(2.f * m) : m < 4.f ? rintf(m) + 2.f : fminf(rintf(0.5f * m) + 4.f, 7.f);
+  return (uint32_t)c | ((__float_as_uint(y) >> 28) & 8u);
 }
 
-__global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+__global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __restrict__ x, uint32_t rows, uint32_t cols,
                                                              uint8_t* __restrict__ q, uint8_t* __restrict__ sc) {
-  const int nb = cols / 32;
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= rows * nb) return;
-  const int64_t r = t / nb;
-  const int b = (int)(t - r * nb);
-  const uint4* src = reinterpret_cast<const uint4*>(x + r * cols + b * 32);
-  float f[32];
+  // lane: 8 consecutive elements (one 16-byte load); four lanes hold a
+  // 32-block and sixteen lanes one 128-code stage of a row, whose four scale
+  // bytes go out as one word.  Indices fit 32 bits (checked by the caller);
+  // the grid-stride step is a multiple of 16, so groups move together.
+  const uint32_t c8 = cols / 8;
+  const uint32_t total = rows * c8;
+  const int lane = threadIdx.x & 63;
+  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v - (uint32_t)(lane & 15) < total; v += gridDim.x * 256u) {
+    const bool live = v < total;
+    const uint32_t r = live ? v / c8 : 0u;
+    const uint32_t k8 = live ? v - r * c8 : 0u;
+    float f[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) unpack8(reinterpret_cast<const uint4*>(x)[v], f);
+    float amax = 0.f;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) unpack8(src[v], f + 8 * v);
-  float amax = 0.f;
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    const int e = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 2));
+    const uint32_t byte = (uint32_t)(e + 127);
+    const int g0 = lane & ~15;
+    const uint32_t word = __shfl(byte, g0, 64) | (__shfl(byte, g0 + 4, 64) << 8) | (__shfl(byte, g0 + 8, 64) << 16) |
+                          (__shfl(byte, g0 + 12, 64) << 24);
+    if (live) {
+      uint32_t codes = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-  const int e = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 2));
-  uint32_t w[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= e2m1_code(scale_pow2(f[8 * v + i], e)) << (4 * i);
-    w[v] = word;
+      for (int i = 0; i < 8; ++i) codes |= e2m1_code(scale_pow2(f[i], e)) << (4 * i);
+      reinterpret_cast<uint32_t*>(q)[v] = codes;
+      if ((k8 & 15u) == 0) reinterpret_cast<uint32_t*>(sc)[(size_t)(k8 >> 4) * rows + r] = word;
+    }
   }
-  *reinterpret_cast<uint4*>(q + r * (cols / 2) + b * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  sc[((int64_t)(b / 4) * rows + r) * 4 + (b % 4)] = (uint8_t)(e + 127);
 }
 
 }  // namespace moe
@@ -388,10 +399,12 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
 
 extern "C" moe_status_t mxfp4_quantize_launch(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q,
                                               uint8_t* scale, hipStream_t s) {
-  const int64_t n = rows * (cols / 32);
+  const int64_t n = rows * (cols / 8);
   if (n == 0) return MOE_OK;
-  hipLaunchKernelGGL(moe::mx4_quant_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, rows, cols, q,
-                     scale);
+  if (n > (int64_t)UINT32_MAX - 65536 * 256) return MOE_ERR_UNSUPPORTED;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)moe_host::device_cu_count() * 32);
+  hipLaunchKernelGGL(moe::mx4_quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, (uint32_t)rows,
+                     (uint32_t)cols, q, scale);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -224,3 +224,49 @@ def test_route_fused_full(ops, name):
     wr = inputs.router_weights(c["seed"], c["E"], c["d"])
     n_near, _ = check_route_fused(ops, x, wr, inputs.expert_bias(name), c["K"])
     assert n_near <= c["T"] // 200, n_near
+
+
+def test_dsv3_share_mxfp4_full(ops):
+    """The expert share in MXFP4 at full size, in the benchmark's launch
+    configuration: the activations' codes and scales bit-exact over the whole
+    tensor, weights of three experts bit-exact, both GEMMs on sampled rows
+    against the oracle fed its own quantisation (H quantised by its own rule)."""
+    say("full: dsv3 share mxfp4")
+    L = inputs.workload("dsv3_share")
+    s = L.group_sizes.numpy()
+    dev = torch.device("cuda")
+    x, w1, w2, sz = L.x_perm.to(dev), L.w1p.to(dev), L.w2.to(dev), L.group_sizes.to(dev)
+
+    def boundary(q, sc):   # oracle layout -> two codes per byte, stage-major scales (data movement only)
+        R, C = q.shape
+        return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8), sc.reshape(R, C // 128, 4).transpose(1, 0, 2)
+
+    xq, xs = ops.mxfp4_quantize(x)
+    xq_ref, xs_ref = orc.mxfp4_quantize(L.x_perm)
+    pq, ps = boundary(xq_ref, xs_ref)
+    np.testing.assert_array_equal(xq.cpu().numpy(), pq)
+    np.testing.assert_array_equal(xs.cpu().numpy(), ps)
+    w1q, w1s = ops.mxfp4_quantize(w1)
+    w2q, w2s = ops.mxfp4_quantize(w2)
+    rows_w1 = 2 * L.f
+    for e in (0, int(np.argmax(s)), L.E - 1):
+        q_ref, s_ref = boundary(*orc.mxfp4_quantize(orc.u16(L.w1p[e])))
+        np.testing.assert_array_equal(w1q[e].cpu().numpy(), q_ref)
+        np.testing.assert_array_equal(w1s[:, e * rows_w1:(e + 1) * rows_w1].cpu().numpy(), s_ref)
+    h = ops.grouped_gemm_mxfp4(xq, xs, w1q, w1s, sz, epilogue=ops.MOE_EPI_SWIGLU)
+    hq, hs = ops.mxfp4_quantize(h)
+    y = ops.grouped_gemm_mxfp4(hq, hs, w2q, w2s, sz)
+    torch.cuda.synchronize()
+    rows = sample_rows(s, 24, 5)
+    w1q_ref, w1s_ref = orc.mxfp4_quantize(orc.u16(L.w1p).reshape(-1, L.d))
+    w1q_ref, w1s_ref = w1q_ref.reshape(L.E, 2 * L.f, L.d), w1s_ref.reshape(L.E, 2 * L.f, L.d // 32)
+    h_ref = orc.mx4_grouped_gemm(xq_ref, xs_ref, w1q_ref, w1s_ref, s, swiglu=True, rows=rows)
+    assert rel_l2(rows_of(h, rows), h_ref) <= MX_TOL
+    hq_ref, hs_ref = orc.mxfp4_quantize(h_ref)
+    HQ = np.zeros((L.M, L.f), np.uint8)
+    HS = np.zeros((L.M, L.f // 32), np.uint8)
+    HQ[rows], HS[rows] = hq_ref, hs_ref
+    w2q_ref, w2s_ref = orc.mxfp4_quantize(orc.u16(L.w2).reshape(-1, L.f))
+    w2q_ref, w2s_ref = w2q_ref.reshape(L.E, L.d, L.f), w2s_ref.reshape(L.E, L.d, L.f // 32)
+    y_ref = orc.mx4_grouped_gemm(HQ, HS, w2q_ref, w2s_ref, s, rows=rows)
+    assert rel_l2(rows_of(y, rows), y_ref) <= MX_TOL
