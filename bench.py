@@ -349,6 +349,39 @@ def bench_mixtral_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
             }}
 
 
+def bench_mixtral_mxfp4(torch, ops, L, dev, timer, flag, steps) -> dict:
+    """The Mixtral-shaped layer on MXFP4 operands: route, permute, quantise
+    the rows, gate/up + SwiGLU, quantise h, down, combine (weights quantised
+    once, outside the timed region)."""
+    T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
+    M = T * K
+    lg, x = L.logits.to(dev), L.x.to(dev)
+    w1 = ops.mxfp4_quantize(L.w1p.to(dev))
+    w2 = ops.mxfp4_quantize(L.w2.to(dev))
+    _, sv = ops.moe_forward_mxfp4(lg, x, w1, w2, K, flag=flag)
+    sizes = sv["group_sizes"]
+    t_g1 = timer(lambda: ops.grouped_gemm_mxfp4(sv["xq"], sv["xs"], w1[0], w1[1], sizes, epilogue=ops.MOE_EPI_SWIGLU,
+                                                out=sv["h"], flag=flag))
+    t_g2 = timer(lambda: ops.grouped_gemm_mxfp4(sv["hq"], sv["hs"], w2[0], w2[1], sizes, out=sv["y_perm"], flag=flag))
+    for _ in range(3):
+        ops.moe_forward_mxfp4(lg, x, w1, w2, K, flag=flag)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(steps):
+        ops.moe_forward_mxfp4(lg, x, w1, w2, K, flag=flag)
+    torch.cuda.synchronize()
+    lms = (time.perf_counter() - a) * 1e3 / steps
+    lflops = 2.0 * M * (2 * f * d + d * f)
+    return {"workload": "mixtral-shaped forward T=4096 d=4096 E=8 top-2 ffn=14336 in MXFP4 (E2M1 + E8M0/32): "
+                        "route, permute, quantise rows, gate/up + SwiGLU, quantise H, down, combine",
+            "tokens_per_s": round(T / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
+            "valid_row_tflops": round(lflops / (lms * 1e-3) / 1e12, 2),
+            "kernels": {
+                "gate_up_swiglu_mxfp4": flop_entry(t_g1, 2.0 * M * 2 * f * d, MXFP4_PEAK_TFLOPS),
+                "down_mxfp4": flop_entry(t_g2, 2.0 * M * d * f, MXFP4_PEAK_TFLOPS),
+            }}
+
+
 def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
     """Forward and backward of the fine-grained layer (weights unpacked: the
     backward reads them as [K, N] too)."""
@@ -581,6 +614,10 @@ def main() -> int:
             f"{workloads['mixtral']['tokens_per_s']:.0f} tokens/s [{time.time() - t0:.1f}s]")
         torch.cuda.empty_cache()
         workloads["mixtral_mxfp8"] = bench_mixtral_mxfp8(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
+        torch.cuda.empty_cache()
+        workloads["mixtral_mxfp4"] = bench_mixtral_mxfp4(torch, ops, Lm, dev, timer, flag, max(5, args.steps // 2))
+        log(f"mixtral layer mxfp4: {workloads['mixtral_mxfp4']['ms_per_step']:.3f} ms, "
+            f"{workloads['mixtral_mxfp4']['tokens_per_s']:.0f} tokens/s")
         log(f"mixtral layer mxfp8: {workloads['mixtral_mxfp8']['ms_per_step']:.3f} ms, "
             f"{workloads['mixtral_mxfp8']['tokens_per_s']:.0f} tokens/s")
         del Lm

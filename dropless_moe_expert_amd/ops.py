@@ -610,6 +610,25 @@ def moe_forward_mxfp8(logits: torch.Tensor, x: torch.Tensor, w1k, w2k, K: int,
     return y, dict(ids=ids, w=w, hq=hq, hs=hs, y_perm=y_perm, **p)
 
 
+def moe_forward_mxfp4(logits: torch.Tensor, x: torch.Tensor, w1: tuple, w2: tuple, K: int,
+                      flag: Optional[torch.Tensor] = None):
+    """The routed layer on MXFP4 operands: router top-K -> permute -> quantise
+    the permuted rows -> gate/up GEMM with SwiGLU -> quantise h -> down GEMM ->
+    combine.  w1 / w2: (codes, scales) from mxfp4_quantize of the [E, 2f, d]
+    gate/up weight and the [E, d, f] down weight.  Returns y [T, d] bf16 and
+    the intermediates."""
+    T = x.shape[0]
+    E = w1[0].shape[0]
+    ids, w = route_topk(logits, K, flag=flag)
+    p = permute(x, ids, E, flag=flag)
+    xq, xs = mxfp4_quantize(p["x_perm"])
+    h = grouped_gemm_mxfp4(xq, xs, w1[0], w1[1], p["group_sizes"], epilogue=MOE_EPI_SWIGLU, flag=flag)
+    hq, hs = mxfp4_quantize(h)
+    y_perm = grouped_gemm_mxfp4(hq, hs, w2[0], w2[1], p["group_sizes"], flag=flag)
+    y = unpermute_combine(y_perm, w, p["perm_dst"], T, K)
+    return y, dict(ids=ids, w=w, xq=xq, xs=xs, h=h, hq=hq, hs=hs, y_perm=y_perm, **p)
+
+
 def moe_backward(dy: torch.Tensor, saved: dict, w1p: torch.Tensor, w2: torch.Tensor, K: int,
                  flag: Optional[torch.Tensor] = None):
     """Backward of moe_forward (routing weights' gradient included, router logits' not)."""

@@ -934,3 +934,28 @@ def test_grouped_gemm_mxfp4(ops, swiglu, sizes, N, Kd):
     out2 = ops.grouped_gemm_mxfp4(q1, s1, q2, s2, t(sizes), epilogue=ops.MOE_EPI_SWIGLU if swiglu else ops.MOE_EPI_NONE)
     torch.cuda.synchronize()
     assert torch.equal(out2[:M], out[:M])
+
+
+def test_routed_layer_mxfp4(ops):
+    """The routed MXFP4 forward (route, permute, quantise, gate/up + SwiGLU,
+    quantise h, down, combine) against the oracle applying the same
+    quantisation at the same points (its own h quantised by its own rule)."""
+    say("routed mxfp4 layer")
+    T, d, E, K, f = 600, 256, 8, 2, 256
+    L = inputs.routed_layer("mx4", T, d, E, K, f, 73, bias_std=1.0)
+    lg, x, w1p, w2 = dev(L.logits), dev(L.x), dev(L.w1p), dev(L.w2)
+    y, parts = ops.moe_forward_mxfp4(lg, x, ops.mxfp4_quantize(w1p), ops.mxfp4_quantize(w2), K)
+    torch.cuda.synchronize()
+    ids, w = orc.route_topk(L.logits, K)
+    sizes, offs, src, dst = orc.permute(ids, E)
+    xq, xs = orc.mxfp4_quantize(orc.gather_rows(L.x, src, K))
+    q1, s1 = orc.mxfp4_quantize(orc.u16(L.w1p).reshape(-1, d))
+    q2, s2 = orc.mxfp4_quantize(orc.u16(L.w2).reshape(-1, f))
+    h = orc.mx4_grouped_gemm(xq, xs, q1.reshape(E, 2 * f, d), s1.reshape(E, 2 * f, d // 32), sizes, swiglu=True)
+    hq, hs = orc.mxfp4_quantize(h)
+    yp = orc.mx4_grouped_gemm(hq, hs, q2.reshape(E, d, f), s2.reshape(E, d, f // 32), sizes)
+    y_ref = orc.unpermute_combine(yp, w, dst, T, K)
+    np.testing.assert_array_equal(parts["ids"].cpu().numpy(), ids)
+    np.testing.assert_array_equal(parts["group_sizes"].cpu().numpy(), sizes)
+    assert rel_l2(parts["h"][:T * K], h) <= MX_TOL
+    assert rel_l2(y, y_ref) <= MX_TOL
