@@ -99,6 +99,28 @@ def test_host_checkable_errors_return_status():
     assert L.mxfp8_group_quantize(fake, 4, 48, 0, None, 0, fake, fake, None, None) == UNSUPPORTED
     assert L.mxfp8_group_quantize(fake, 4, 64, 1, None, 0, fake, fake, None, None) == INVALID
     assert L.mxfp8_group_quantize(fake, 4, 64, 2, None, 0, fake, fake, None, None) == INVALID
+    # fused router: d % 32, K <= E, inputs required, workspace size, alignment
+    assert L.moe_route_fused(fake, fake, None, 4, 48, 8, 2, 1, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    assert L.moe_route_fused(fake, fake, None, 4, 64, 8, 9, 1, fake, fake, None, None, 0, None, None) == INVALID
+    assert L.moe_route_fused(None, fake, None, 4, 64, 8, 2, 1, fake, fake, None, None, 0, None, None) == INVALID
+    assert L.moe_route_fused(fake, fake, None, 4, 64, 8, 2, 1, fake, fake, None, fake, 16, None, None) == WS
+    assert L.moe_route_fused(ctypes.c_void_p((1 << 20) + 4), fake, None, 4, 64, 8, 2, 1, fake, fake, None, None, 0,
+                             None, None) == ALIGN
+    assert L.moe_route_fused_workspace_bytes(16384, 128, 8) >= 16384 * 8 * 4
+    # routed permute: its workspace is required
+    assert L.moe_permute_routed(None, fake, 4, 0, 8, 2, fake, fake, fake, fake, None, None, 0, None, None) == WS
+    # MXFP4: cols % 128 for the quantiser; K % 128, scales and B_NK for the GEMM
+    assert L.mxfp4_quantize(fake, 4, 96, fake, fake, None) == UNSUPPORTED
+    assert L.mxfp4_quantize(None, 4, 128, fake, fake, None) == INVALID
+    d4 = ops.GGDesc(2, 0, 0, 0, 0, 4, 0, 64, 192, 100)
+    b4 = ctypes.byref(d4)
+    assert L.grouped_gemm(b4, fake, fake, fake, fake, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    d4.K = 256
+    assert L.grouped_gemm(b4, fake, None, fake, fake, fake, fake, None, None, 0, None, None) == INVALID
+    d4.b_layout = 1
+    assert L.grouped_gemm(b4, fake, fake, fake, fake, fake, fake, None, None, 0, None, None) == UNSUPPORTED
+    d4.b_layout, d4.ragged = 0, 1
+    assert L.grouped_gemm(b4, fake, fake, fake, fake, fake, fake, None, None, 0, None, None) == UNSUPPORTED
 
 
 def test_product_path_refuses_without_gpu():
