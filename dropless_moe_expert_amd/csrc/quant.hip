@@ -287,19 +287,24 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       // one thread per (valid row, 32-column block): the axis-0 quantisation
       const int u = t - 2 * QT_C, r = u >> 1, b = u & 1, cb = c0 + 32 * b;
       if (r < n && cb < cols) {
-        float f[32];
+        // two passes over the row's 32 values in LDS (pairs per 4-byte read):
+        // amax, then the codes; few live registers keep the occupancy up
+        const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + r * QT_LD + 32 * b);   // QT_LD even
         float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          f[i] = __uint_as_float((uint32_t)xt[r * QT_LD + 32 * b + i] << 16);
-          amax = fmaxf(amax, fabsf(f[i]));
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t p = xr[i];
+          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(p << 16)), fabsf(__uint_as_float(p & 0xFFFF0000u))));
         }
         const int e = mx_exponent(amax);
+        asm volatile("" ::: "memory");   // re-read the row below instead of keeping 16 words live
         uint32_t w[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          w[q] = cvt4_e4m3(scale_pow2(f[4 * q], e), scale_pow2(f[4 * q + 1], e), scale_pow2(f[4 * q + 2], e),
-                           scale_pow2(f[4 * q + 3], e));
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t p0 = xr[2 * q], p1 = xr[2 * q + 1];
+          w[q] = cvt4_e4m3(scale_pow2(__uint_as_float(p0 << 16), e), scale_pow2(__uint_as_float(p0 & 0xFFFF0000u), e),
+                           scale_pow2(__uint_as_float(p1 << 16), e), scale_pow2(__uint_as_float(p1 & 0xFFFF0000u), e));
+        }
         uint4* d = reinterpret_cast<uint4*>(q0 + (r0 + r) * cols + cb);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
