@@ -153,9 +153,9 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ scaleT, uint8_t* __restrict__ q0,
                                                          uint8_t* __restrict__ s0, uint32_t* flag) {
   extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
-  __shared__ uint16_t xt[QT_R * QT_LD];                 // the tile, bf16, row-major
-  __shared__ __align__(16) uint8_t ct[QT_C * QT_R];     // its codes, column-major
-  __shared__ uint8_t st[QT_C * 2];                      // its scales, two per column
+  __shared__ uint16_t xt[2 * QT_R * QT_LD];             // two position units, bf16, row-major
+  __shared__ __align__(16) uint8_t ct[QT_C * 2 * QT_R]; // their codes, column-major (128 per column)
+  __shared__ uint8_t st[QT_C * 4];                      // their scales, four per column
   int64_t* roff = sh;
   int64_t* kpad = sh + G + 1;
   const bool grouped = group_sizes != nullptr;
@@ -210,68 +210,81 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     if (blockIdx.x == 0 && threadIdx.x == 255 && scan_r[255] > rows) raise_flag(flag, MOE_FLAG_ROWS_OVER_CAP);
     __syncthreads();
   }
-  const int64_t tpb = rows / QT_R;   // batched: position tiles per batch
+  const int64_t tpb = rows / QT_R;   // batched: position units per batch
   const int64_t ntk = grouped ? kpad[G] / QT_R : (int64_t)G * tpb;
+  const int64_t ntp = (ntk + 1) / 2;   // pairs of units: a column's 128 codes leave as one line
   const int ntc = (cols + QT_C - 1) / QT_C;
   const int t = threadIdx.x;
-  for (int64_t tile = blockIdx.x; tile < ntk * ntc; tile += gridDim.x) {
-    const int64_t tk = tile / ntc;
-    const int c0 = (int)(tile - tk * ntc) * QT_C;
-    int64_t r0, ldq;
-    int n;
-    uint8_t* qb;   // the tile's first code in column c0's qT row
-    uint8_t* sb;   // its first scale in column c0's scaleT row
-    if (grouped) {
-      int lo = 0, hi = G - 1;   // last g with kpad[g] <= 64 tk
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (kpad[mid] <= QT_R * tk) lo = mid; else hi = mid - 1;
+  for (int64_t tile = blockIdx.x; tile < ntp * ntc; tile += gridDim.x) {
+    const int64_t tp = tile / ntc;
+    const int c0 = (int)(tile - tp * ntc) * QT_C;
+    // each unit (64 positions) of the pair resolves its own rows and outputs
+    int64_t r0[2], ldq = grouped ? k_cap : rows;
+    int n[2];
+    bool val[2];
+    uint8_t* qb[2];   // the unit's first code in column c0's qT row
+    uint8_t* sb[2];   // its first scale in column c0's scaleT row
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t tk = 2 * tp + h;
+      val[h] = tk < ntk;
+      r0[h] = 0;
+      n[h] = 0;
+      qb[h] = qT;
+      sb[h] = scaleT;
+      if (!val[h]) continue;
+      if (grouped) {
+        int lo = 0, hi = G - 1;   // last g with kpad[g] <= 64 tk
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (kpad[mid] <= QT_R * tk) lo = mid; else hi = mid - 1;
+        }
+        r0[h] = roff[lo] + (QT_R * tk - kpad[lo]);
+        n[h] = (int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - r0[h]));
+        qb[h] = qT + (int64_t)c0 * k_cap + QT_R * tk;
+        sb[h] = scaleT + (int64_t)c0 * (k_cap / 32) + 2 * tk;
+      } else {
+        const int64_t g = tk / tpb, b = tk - g * tpb;
+        r0[h] = g * rows + QT_R * b;
+        n[h] = QT_R;
+        qb[h] = qT + g * cols * rows + (int64_t)c0 * rows + QT_R * b;
+        sb[h] = scaleT + g * cols * (rows / 32) + (int64_t)c0 * (rows / 32) + 2 * b;
       }
-      r0 = roff[lo] + (QT_R * tk - kpad[lo]);
-      n = (int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - r0));
-      ldq = k_cap;
-      qb = qT + (int64_t)c0 * k_cap + QT_R * tk;
-      sb = scaleT + (int64_t)c0 * (k_cap / 32) + 2 * tk;
-    } else {
-      const int64_t g = tk / tpb, b = tk - g * tpb;
-      r0 = g * rows + QT_R * b;
-      n = QT_R;
-      ldq = rows;
-      qb = qT + g * cols * rows + (int64_t)c0 * rows + QT_R * b;
-      sb = scaleT + g * cols * (rows / 32) + (int64_t)c0 * (rows / 32) + 2 * b;
     }
-    // 1. the tile's rows: 64 rows x 8 pieces of 8 columns, two per thread
+    // 1. the pair's rows: 128 rows x 8 pieces of 8 columns, four per thread
     __syncthreads();   // the previous tile's LDS is read out
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int u = t + 256 * k, r = u >> 3, c = (u & 7) * 8;
+    for (int k = 0; k < 4; ++k) {
+      const int u = t + 256 * k, rr = u >> 3, c = (u & 7) * 8;
+      const int h = rr >> 6, r = rr & 63;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < n && c0 + c < cols) {
+      if (r < n[h] && c0 + c < cols) {
+        const int64_t row = r0[h] + r;
         if constexpr (PRODUCER == 0) {
-          v = *reinterpret_cast<const uint4*>(x + (r0 + r) * cols + c0 + c);
+          v = *reinterpret_cast<const uint4*>(x + row * cols + c0 + c);
         } else {
           const int f = cols / 2, j = (c0 + c) % f;   // f % 8 == 0: a piece is all gate or all up
-          float g[8], u[8], d[8], dg[8], du[8];
-          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + r) * cols + j), g);
-          unpack8(*reinterpret_cast<const uint4*>(x + (r0 + r) * cols + f + j), u);
-          unpack8(*reinterpret_cast<const uint4*>(dh + (r0 + r) * f + j), d);
+          float g[8], uu[8], dd[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + j), g);
+          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + f + j), uu);
+          unpack8(*reinterpret_cast<const uint4*>(dh + row * f + j), dd);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], u[e], d[e], dg[e], du[e]);
+          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dd[e], dg[e], du[e]);
           v = pack8(c0 + c < f ? dg : du);
         }
       }
-      uint32_t* d = reinterpret_cast<uint32_t*>(xt + r * QT_LD + c);   // 4-byte aligned (QT_LD even)
+      uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + c);   // 4-byte aligned (QT_LD even)
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
     __syncthreads();
-    // 2. one thread per (column, block): amax, scale, 32 codes into the column
-    if (t < 2 * QT_C) {
-      const int c = t & (QT_C - 1), b = t >> 6;
+    // 2a. one thread per (column, 32-position block): amax, scale, 32 codes into the column
+    {
+      const int c = t & (QT_C - 1), b = t >> 6;   // b = 0..3 over the pair's 128 positions
       float amax = 0.f;
 #pragma unroll 8
       for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)xt[(32 * b + i) * QT_LD + c] << 16)));
       const int e = mx_exponent(amax);
-      st[2 * c + b] = (uint8_t)(e + 127);
+      st[4 * c + b] = (uint8_t)(e + 127);
       uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -280,16 +293,18 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
         for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)xt[(32 * b + 4 * q + i) * QT_LD + c] << 16);
         w[q] = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
       }
-      uint4* d = reinterpret_cast<uint4*>(ct + c * QT_R + 32 * b);
+      uint4* d = reinterpret_cast<uint4*>(ct + c * (2 * QT_R) + 32 * b);
       d[0] = make_uint4(w[0], w[1], w[2], w[3]);
       d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    } else if (q0) {
-      // one thread per (valid row, 32-column block): the axis-0 quantisation
-      const int u = t - 2 * QT_C, r = u >> 1, b = u & 1, cb = c0 + 32 * b;
-      if (r < n && cb < cols) {
+    }
+    // 2b. one thread per (row, 32-column block): the axis-0 quantisation of the valid rows
+    if (q0) {
+      const int rr = t >> 1, b = t & 1, cb = c0 + 32 * b;
+      const int h = rr >> 6, r = rr & 63;
+      if (r < n[h] && cb < cols) {
         // two passes over the row's 32 values in LDS (pairs per 4-byte read):
         // amax, then the codes; few live registers keep the occupancy up
-        const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + r * QT_LD + 32 * b);   // QT_LD even
+        const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + rr * QT_LD + 32 * b);   // QT_LD even
         float amax = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -305,22 +320,26 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
           w[q] = cvt4_e4m3(scale_pow2(__uint_as_float(p0 << 16), e), scale_pow2(__uint_as_float(p0 & 0xFFFF0000u), e),
                            scale_pow2(__uint_as_float(p1 << 16), e), scale_pow2(__uint_as_float(p1 & 0xFFFF0000u), e));
         }
-        uint4* d = reinterpret_cast<uint4*>(q0 + (r0 + r) * cols + cb);
+        const int64_t row = r0[h] + r;
+        uint4* d = reinterpret_cast<uint4*>(q0 + row * cols + cb);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        s0[(r0 + r) * (cols / 32) + cb / 32] = (uint8_t)(e + 127);
+        s0[row * (cols / 32) + cb / 32] = (uint8_t)(e + 127);
       }
     }
     __syncthreads();
-    // 3. column rows out: four 16-byte pieces per column; the scale pair
-    {
-      const int c = t >> 2, piece = t & 3;
-      if (c0 + c < cols) {
-        *reinterpret_cast<uint4*>(qb + (int64_t)c * ldq + 16 * piece) =
-            *reinterpret_cast<const uint4*>(ct + c * QT_R + 16 * piece);
-        if (piece == 0)
-          *reinterpret_cast<uint16_t*>(sb + (int64_t)c * (ldq / 32)) =
-              (uint16_t)(st[2 * c] | ((uint16_t)st[2 * c + 1] << 8));
+    // 3. column rows out: lanes (column, 16-byte piece of the pair's 128 codes),
+    //    so one store instruction writes 8 columns x 128 contiguous bytes when the
+    //    two units are adjacent in the column row; the scale pairs
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = t + 256 * k, c = idx >> 3, p8 = idx & 7, h = p8 >> 2;
+      if (val[h] && c0 + c < cols) {
+        *reinterpret_cast<uint4*>(qb[h] + (int64_t)c * ldq + 16 * (p8 & 3)) =
+            *reinterpret_cast<const uint4*>(ct + c * (2 * QT_R) + 16 * p8);
+        if ((p8 & 3) == 0)
+          *reinterpret_cast<uint16_t*>(sb[h] + (int64_t)c * (ldq / 32)) =
+              (uint16_t)(st[4 * c + 2 * h] | ((uint16_t)st[4 * c + 2 * h + 1] << 8));
       }
     }
   }
@@ -388,7 +407,7 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
                                                          uint32_t* flag, hipStream_t s) {
   const int64_t cap = (int64_t)moe_host::device_cu_count() * 8;
   const int64_t ntk = group_sizes ? k_cap / 64 : (int64_t)G * (rows / 64);   // an upper bound when grouped
-  const int64_t work = ntk * ((cols + 63) / 64);
+  const int64_t work = (ntk + 1) / 2 * ((cols + 63) / 64);   // pairs of 64-position units
   if (work == 0) return MOE_OK;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
