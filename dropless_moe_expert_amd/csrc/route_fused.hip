@@ -99,11 +99,9 @@ struct Cfg {
   static constexpr int STAGE_B = NP * PAIR_B;
   static constexpr int NJ = ROWS / 8;              // 1-KB load blocks (8 rows) per pair
   static constexpr int NB = NP * NJ / 4;           // load blocks per wavefront and stage
-  static constexpr int LS = EP + 4;                // logits row stride (floats)
-  static constexpr int NSL = 256 / TW;             // top-K slices per token
-  static constexpr int SW = EP / NSL;              // experts per slice
+  static constexpr int LS = EP + 4;                // logits row stride (floats), as in Epi
   static_assert(WM * WN * SK == 4, "four wavefronts");
-  static_assert(NSUB % 2 == 0 && (NP * NJ) % 4 == 0 && NSUB % SK == 0 && EP % NSL == 0, "tiling");
+  static_assert(NSUB % 2 == 0 && (NP * NJ) % 4 == 0 && NSUB % SK == 0, "tiling");
   static_assert(NS >= 2 && NS <= 4, "the stage wait covers up to two stages ahead");
 };
 
