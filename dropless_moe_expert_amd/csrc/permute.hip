@@ -12,7 +12,7 @@
 //               expert (found with 8 ballots over the id bits).  Writes the
 //               local rank of every pair and the chunk's per-expert counts.
 //   2. scan:    one workgroup: per expert, an exclusive scan over chunks
-//               (each expert's chunks split over 256 / E threads, loads
+//               (each expert's chunks split over 1024 / E threads, loads
 //               batched); the totals are group_sizes; their exclusive scan is
 //               group_offsets; chunk bases become absolute row offsets.
 //   3. scatter: one wavefront per token: row r = base[chunk][e] + local rank
@@ -64,15 +64,16 @@ __global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restr
   for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)blockIdx.x * E + e] = running[e];
 }
 
-__global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
+template <int NT>
+__global__ __launch_bounds__(NT) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
                                                            int32_t* __restrict__ group_sizes,
                                                            int32_t* __restrict__ group_offsets) {
-  __shared__ int32_t part[256];
-  __shared__ int32_t tot[256];
-  // thread (e, p): expert e = tid % E, part p = tid / E of P = 256 / E parts,
+  __shared__ int32_t part[NT];
+  __shared__ int32_t tot[NT];
+  // thread (e, p): expert e = tid % E, part p = tid / E of P = NT / E parts,
   // each a contiguous range of chunks
   const int tid = threadIdx.x;
-  const int P = 256 / E;
+  const int P = NT / E;
   const int e = tid % E, p = tid / E;
   const bool active = p < P;
   const int per = (nchunk + P - 1) / P;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int32_t* __restrict__
   tot[tid] = (active && p == 0) ? total : 0;
   __syncthreads();
   int32_t incl = tot[tid];
-  for (int o = 1; o < 256; o <<= 1) {
+  for (int o = 1; o < NT; o <<= 1) {
     const int32_t add = (tid >= o) ? tot[tid - o] : 0;
     __syncthreads();
     incl += add;
@@ -262,7 +263,7 @@ extern "C" moe_status_t moe_permute_launch(const uint16_t* x, const int32_t* ids
     hipLaunchKernelGGL(moe::permute_rank_kernel, dim3((unsigned)nchunk), dim3(64), 0, s, ids, M, E, local_rank,
                        chunk_counts, flag);
   }
-  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+  hipLaunchKernelGGL(moe::permute_scan_kernel<1024>, dim3(1), dim3(1024), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
                      group_offsets);
   if (T > 0) {
     const dim3 g((unsigned)((T + 3) / 4)), b(256);
@@ -295,7 +296,7 @@ extern "C" moe_status_t moe_permute_mxfp8_launch(const uint16_t* x, const int32_
     hipLaunchKernelGGL(moe::permute_rank_kernel, dim3((unsigned)nchunk), dim3(64), 0, s, ids, M, E, local_rank,
                        chunk_counts, flag);
   }
-  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+  hipLaunchKernelGGL(moe::permute_scan_kernel<1024>, dim3(1), dim3(1024), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
                      group_offsets);
   if (T > 0) {
     const dim3 g((unsigned)((T + 3) / 4)), b(256);
@@ -324,7 +325,7 @@ extern "C" moe_status_t moe_permute_routed_launch(const uint16_t* x, const int32
   int32_t* local_rank = reinterpret_cast<int32_t*>(ws);
   size_t a = ((size_t)M * 4 + 255) & ~(size_t)255;
   int32_t* chunk_counts = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + a);
-  hipLaunchKernelGGL(moe::permute_scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
+  hipLaunchKernelGGL(moe::permute_scan_kernel<1024>, dim3(1), dim3(1024), 0, s, chunk_counts, (int)nchunk, E, group_sizes,
                      group_offsets);
   if (T > 0) {
     const dim3 g((unsigned)((T + 3) / 4)), b(256);
