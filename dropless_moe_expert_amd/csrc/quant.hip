@@ -213,17 +213,23 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   const int64_t tpb = rows / QT_R;   // batched: position units per batch
   const int64_t ntk = grouped ? kpad[G] / QT_R : (int64_t)G * tpb;
   const int64_t ntp = (ntk + 1) / 2;   // pairs of units: a column's 128 codes leave as one line
-  const int ntc = (cols + QT_C - 1) / QT_C;
+  // PRODUCER 2 (SwiGLU backward, f % 32 == 0): a tile's 64 columns are the
+  // gate columns c0 .. c0 + 31 and the up columns f + c0 .. f + c0 + 31, so
+  // one read of g, u and dh gives both halves; otherwise 64 consecutive columns
+  const int fh = cols / 2;
+  const int ntc = PRODUCER == 2 ? (fh + 31) / 32 : (cols + QT_C - 1) / QT_C;
+  auto gcol = [&](int c0, int c) { return PRODUCER == 2 ? (c < 32 ? c0 + c : fh + c0 + (c - 32)) : c0 + c; };
+  auto colvalid = [&](int c0, int c) { return PRODUCER == 2 ? c0 + (c & 31) < fh : c0 + c < cols; };
   const int t = threadIdx.x;
   for (int64_t tile = blockIdx.x; tile < ntp * ntc; tile += gridDim.x) {
     const int64_t tp = tile / ntc;
-    const int c0 = (int)(tile - tp * ntc) * QT_C;
+    const int c0 = (int)(tile - tp * ntc) * (PRODUCER == 2 ? 32 : QT_C);
     // each unit (64 positions) of the pair resolves its own rows and outputs
     int64_t r0[2], ldq = grouped ? k_cap : rows;
     int n[2];
     bool val[2];
-    uint8_t* qb[2];   // the unit's first code in column c0's qT row
-    uint8_t* sb[2];   // its first scale in column c0's scaleT row
+    uint8_t* qb[2];   // the unit's first code in column 0's qT row
+    uint8_t* sb[2];   // its first scale in column 0's scaleT row
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t tk = 2 * tp + h;
@@ -241,18 +247,43 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
         }
         r0[h] = roff[lo] + (QT_R * tk - kpad[lo]);
         n[h] = (int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - r0[h]));
-        qb[h] = qT + (int64_t)c0 * k_cap + QT_R * tk;
-        sb[h] = scaleT + (int64_t)c0 * (k_cap / 32) + 2 * tk;
+        qb[h] = qT + QT_R * tk;
+        sb[h] = scaleT + 2 * tk;
       } else {
         const int64_t g = tk / tpb, b = tk - g * tpb;
         r0[h] = g * rows + QT_R * b;
         n[h] = QT_R;
-        qb[h] = qT + g * cols * rows + (int64_t)c0 * rows + QT_R * b;
-        sb[h] = scaleT + g * cols * (rows / 32) + (int64_t)c0 * (rows / 32) + 2 * b;
+        qb[h] = qT + g * cols * rows + QT_R * b;
+        sb[h] = scaleT + g * cols * (rows / 32) + 2 * b;
       }
     }
     // 1. the pair's rows: 128 rows x 8 pieces of 8 columns, four per thread
     __syncthreads();   // the previous tile's LDS is read out
+    if constexpr (PRODUCER == 2) {
+      // 128 rows x 4 pieces of 8 gate/up pairs, two per thread: dg to columns
+      // 8 jp .., du to 32 + 8 jp ..
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int u = t + 256 * k, rr = u >> 2, jp = u & 3, j = c0 + 8 * jp;
+        const int h = rr >> 6, r = rr & 63;
+        uint4 vg = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
+        if (r < n[h] && j < fh) {
+          const int64_t row = r0[h] + r;
+          float g[8], uu[8], dd[8], dg[8], du[8];
+          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + j), g);
+          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + fh + j), uu);
+          unpack8(*reinterpret_cast<const uint4*>(dh + row * fh + j), dd);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dd[e], dg[e], du[e]);
+          vg = pack8(dg);
+          vu = pack8(du);
+        }
+        uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + 8 * jp);
+        d[0] = vg.x; d[1] = vg.y; d[2] = vg.z; d[3] = vg.w;
+        d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + 32 + 8 * jp);
+        d[0] = vu.x; d[1] = vu.y; d[2] = vu.z; d[3] = vu.w;
+      }
+    } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int u = t + 256 * k, rr = u >> 3, c = (u & 7) * 8;
@@ -275,6 +306,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       }
       uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + c);   // 4-byte aligned (QT_LD even)
       d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
     }
     __syncthreads();
     // 2a. one thread per (column, 32-position block): amax, scale, 32 codes into the column
@@ -299,9 +331,9 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     }
     // 2b. one thread per (row, 32-column block): the axis-0 quantisation of the valid rows
     if (q0) {
-      const int rr = t >> 1, b = t & 1, cb = c0 + 32 * b;
+      const int rr = t >> 1, b = t & 1, cb = gcol(c0, 32 * b);
       const int h = rr >> 6, r = rr & 63;
-      if (r < n[h] && cb < cols) {
+      if (r < n[h] && colvalid(c0, 32 * b)) {
         // two passes over the row's 32 values in LDS (pairs per 4-byte read):
         // amax, then the codes; few live registers keep the occupancy up
         const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + rr * QT_LD + 32 * b);   // QT_LD even
@@ -334,11 +366,12 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int idx = t + 256 * k, c = idx >> 3, p8 = idx & 7, h = p8 >> 2;
-      if (val[h] && c0 + c < cols) {
-        *reinterpret_cast<uint4*>(qb[h] + (int64_t)c * ldq + 16 * (p8 & 3)) =
+      if (val[h] && colvalid(c0, c)) {
+        const int64_t col = gcol(c0, c);
+        *reinterpret_cast<uint4*>(qb[h] + col * ldq + 16 * (p8 & 3)) =
             *reinterpret_cast<const uint4*>(ct + c * (2 * QT_R) + 16 * p8);
         if ((p8 & 3) == 0)
-          *reinterpret_cast<uint16_t*>(sb[h] + (int64_t)c * (ldq / 32)) =
+          *reinterpret_cast<uint16_t*>(sb[h] + col * (ldq / 32)) =
               (uint16_t)(st[4 * c + 2 * h] | ((uint16_t)st[4 * c + 2 * h + 1] << 8));
       }
     }
@@ -411,7 +444,10 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
   if (work == 0) return MOE_OK;
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
-  if (dh) {
+  if (dh && (cols / 2) % 32 == 0) {
+    hipLaunchKernelGGL(moe::mx_quant_t_kernel<2>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
+                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
+  } else if (dh) {
     hipLaunchKernelGGL(moe::mx_quant_t_kernel<1>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
                        group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
   } else {
