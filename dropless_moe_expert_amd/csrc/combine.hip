@@ -154,14 +154,9 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const uint16_t* __
                                                               const int32_t* __restrict__ group_sizes, int G,
                                                               uint16_t* __restrict__ dgu) {
   __shared__ int64_t s_rows;
-  if (threadIdx.x == 0) {
-    int64_t tot = m_cap;
-    if (group_sizes) {
-      tot = 0;
-      for (int g = 0; g < G; ++g) tot += max(group_sizes[g], 0);
-      tot = min(tot, m_cap);
-    }
-    s_rows = tot;
+  if (threadIdx.x < kWave) {
+    const int64_t tot = group_sizes ? rows_in_use(group_sizes, G, m_cap) : m_cap;
+    if (threadIdx.x == 0) s_rows = tot;
   }
   __syncthreads();
   const int64_t rows = s_rows;

@@ -65,6 +65,15 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Rows in use of a ragged operand: the sum of the G device group sizes
+// (negative sizes count as 0), at most cap.  Called by a whole wavefront,
+// which reads the sizes 64 at a time; every lane gets the result.
+__device__ __forceinline__ int64_t rows_in_use(const int32_t* sizes, int G, int64_t cap) {
+  int64_t t = 0;
+  for (int g = (int)(threadIdx.x & 63); g < G; g += kWave) t += max(sizes[g], 0);
+  return min(wave_sum(t), cap);
+}
+
 // SwiGLU backward of one element, from the pre-activations g, u and dh:
 // with s = sigmoid(g), dg = dh*u*s*(1 + g*(1-s)), du = dh*g*s.  Shared by
 // the bf16 SwiGLU backward and the one that quantises its output, so both

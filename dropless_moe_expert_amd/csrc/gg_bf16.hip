@@ -416,11 +416,15 @@ constexpr int WG_STAGES = 4;
 
 // Tile queues of the weight-gradient kernel, per launch slot (the host hands
 // out the slots in turn, so launches in flight together use different
-// ones): kQueues tile counters, then the number of workgroups that have
-// finished; the last workgroup to finish zeroes them all for the slot's next
-// launch.  Zero at load time.
+// ones): kQueues tile counters.  A one-wavefront kernel zeroes the slot on
+// the launch's stream right before every launch, so no count carries over
+// from an earlier launch, not even from one that ended part-way.
 constexpr int kQueues = 8, kSlots = 64;
-__device__ uint32_t g_wgrad_sched[kSlots][kQueues + 1];
+__device__ uint32_t g_wgrad_sched[kSlots][kQueues];
+
+__global__ void __launch_bounds__(64) wgrad_sched_reset_kernel(int slot) {
+  if (threadIdx.x < kQueues) g_wgrad_sched[slot][threadIdx.x] = 0u;
+}
 
 template <int OUT>
 __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
@@ -429,7 +433,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b2[STAGE];
   __shared__ __align__(1024) uint8_t b3[STAGE];
   __shared__ GroupInfo<THREADS> gi;
-  build_groups<THREADS, BM, false>(a, gi);
+  build_groups<THREADS>(a, gi);
 
   const int P = a.M, Q = a.N;
   const int per_group = a.p_tiles * a.n_tiles;
@@ -591,13 +595,6 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
       process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
     }
   }
-  if (threadIdx.x == 0) {
-    // every tile this workgroup took is done; the last workgroup resets
-    if (atomicAdd(&ctr[kQueues], 1u) == gridDim.x - 1) {
-      for (int q = 0; q < kQueues; ++q) atomicExch(&ctr[q], 0u);
-      atomicExch(&ctr[kQueues], 0u);
-    }
-  }
 }
 
 // Packs W [G, rows_b, K] (rows_b = N, or 2f for SwiGLU) into the tile-stage
@@ -713,6 +710,7 @@ moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s) {
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
+  hipLaunchKernelGGL(fwd::wgrad_sched_reset_kernel, dim3(1), dim3(64), 0, s, b.sched_slot);
   if (out_f32) {
     hipLaunchKernelGGL((fwd::gg_wgrad_kernel<MOE_OUT_F32>), g, t, 0, s, b);
   } else {

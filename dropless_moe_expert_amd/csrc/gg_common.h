@@ -26,57 +26,58 @@ struct GGArgs {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // wavefront index as a scalar (uniform) value
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ----------------------------------------------------------------- group prefix
 template <int THREADS>
 struct GroupInfo {
-  int32_t roff[kMaxGroups + 1];   // clamped row offsets
-  int32_t tpre[kMaxGroups + 1];   // m-tile prefix (ragged-M) / rank order (ragged-K)
-  int32_t scan[THREADS];
+  int32_t roff[kMaxGroups + 1];   // row offsets: sizes clamped to >= 0, offsets to m_cap
+  int32_t tpre[kMaxGroups];       // groups ranked by size, largest first
+  int64_t scan[THREADS];
 };
 
-// exclusive scan of v over the workgroup (THREADS values), returns exclusive, total in *tot
+// exclusive scan of v over the workgroup (THREADS values), total in *tot
 template <int THREADS>
-__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t* buf, int32_t* tot) {
+__device__ __forceinline__ int64_t block_scan(int64_t v, int64_t* buf, int64_t* tot) {
   const int t = threadIdx.x;
   buf[t] = v;
   __syncthreads();
   for (int o = 1; o < THREADS; o <<= 1) {
-    int32_t add = (t >= o) ? buf[t - o] : 0;
+    int64_t add = (t >= o) ? buf[t - o] : 0;
     __syncthreads();
     buf[t] += add;
     __syncthreads();
   }
-  int32_t incl = buf[t];
+  int64_t incl = buf[t];
   *tot = buf[THREADS - 1];
   __syncthreads();
   return incl - v;
 }
 
-// Builds roff (row offsets, sizes clamped to >= 0 and to m_cap) and, for
-// ragged-M, tpre = prefix of ceil(size / BM).  Raises flags from block 0.
-template <int THREADS, int BM, bool TILES>
+// Row offsets of the ragged-K groups from the device sizes: each size
+// clamped to >= 0, the running sum taken in 64 bits (1024 sizes of up to
+// 2^31 - 1 each cannot wrap it) and every offset clamped to m_cap, so no
+// group reaches outside the operands; then the groups ranked largest first
+// (ties: lower index first), so the longest contractions start earliest.
+// Raises the data-error flags from block 0.
+template <int THREADS>
 __device__ void build_groups(const GGArgs& a, GroupInfo<THREADS>& gi) {
   const int t = threadIdx.x;
-  constexpr int per = kMaxGroups / THREADS;  // 4 groups per thread
-  int32_t s[per];
-  int32_t local = 0;
+  constexpr int per = kMaxGroups / THREADS;
+  int64_t s[per];
+  int64_t local = 0;
   bool neg = false;
 #pragma unroll
   for (int i = 0; i < per; ++i) {
     int g = t * per + i;
-    int32_t v = (g < a.G) ? a.sizes[g] : 0;
+    int64_t v = (g < a.G) ? (int64_t)a.sizes[g] : 0;
     if (v < 0) { neg = true; v = 0; }
     s[i] = v;
     local += v;
   }
-  int32_t tot;
-  int32_t base = block_scan<THREADS>(local, gi.scan, &tot);
+  int64_t tot;
+  const int64_t base = block_scan<THREADS>(local, gi.scan, &tot);
   const int64_t cap = a.m_cap;
   int64_t o = base;
 #pragma unroll
@@ -86,55 +87,19 @@ __device__ void build_groups(const GGArgs& a, GroupInfo<THREADS>& gi) {
     o += s[i];
   }
   if (t == THREADS - 1 && a.G == kMaxGroups) gi.roff[kMaxGroups] = (int32_t)min<int64_t>(o, cap);
-  if (blockIdx.x == 0 && t == 0) {
-    if ((int64_t)tot > cap) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
-  }
+  if (blockIdx.x == 0 && t == 0 && tot > cap) raise_flag(a.flag, MOE_FLAG_ROWS_OVER_CAP);
   if (blockIdx.x == 0 && __any(neg) && (t & 63) == 0) raise_flag(a.flag, MOE_FLAG_NEGATIVE_SIZE);
   __syncthreads();
-  if (TILES) {
-    int32_t lt = 0;
-    int32_t nt[per];
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      int g = t * per + i;
-      int32_t rows = (g < a.G) ? gi.roff[g + 1] - gi.roff[g] : 0;
-      nt[i] = (rows + BM - 1) / BM;
-      lt += nt[i];
+  for (int g = t; g < a.G; g += THREADS) {
+    const int32_t sg = gi.roff[g + 1] - gi.roff[g];
+    int rank = 0;
+    for (int h = 0; h < a.G; ++h) {
+      const int32_t sh = gi.roff[h + 1] - gi.roff[h];
+      rank += (sh > sg) || (sh == sg && h < g);
     }
-    int32_t tt;
-    int32_t b = block_scan<THREADS>(lt, gi.scan, &tt);
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      int g = t * per + i;
-      if (g <= a.G) gi.tpre[g] = b;
-      b += nt[i];
-    }
-    if (t == THREADS - 1 && a.G == kMaxGroups) gi.tpre[kMaxGroups] = b;
-    __syncthreads();
-  } else {
-    // ragged-K: order groups by size, largest first (ties: lower index first),
-    // so the longest contractions start earliest.  tpre[rank] = group.
-    for (int g = t; g < a.G; g += THREADS) {
-      const int32_t sg = gi.roff[g + 1] - gi.roff[g];
-      int rank = 0;
-      for (int h = 0; h < a.G; ++h) {
-        const int32_t sh = gi.roff[h + 1] - gi.roff[h];
-        rank += (sh > sg) || (sh == sg && h < g);
-      }
-      gi.tpre[rank] = g;
-    }
-    __syncthreads();
+    gi.tpre[rank] = g;
   }
-}
-
-// last g in [0, G) with tpre[g] <= mt
-__device__ __forceinline__ int find_group(const int32_t* tpre, int G, int mt) {
-  int lo = 0, hi = G - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (tpre[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+  __syncthreads();
 }
 
 __device__ __forceinline__ int worker_id() {

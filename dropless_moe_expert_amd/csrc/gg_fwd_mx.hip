@@ -523,8 +523,14 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict_
 // empty group stores zeros.  Tiles come from dynamic queues as in the bf16
 // weight gradient: groups ranked largest first (each workgroup ranks them
 // into a 2 KB LDS table), dealt to the queues in a snake over the ranks.
+// The queue counters of each launch slot are zeroed by a one-wavefront
+// kernel on the launch's stream right before the launch.
 constexpr int kWgQueues = 8, kWgSlots = 64;
-__device__ uint32_t g_wgrad_mx_sched[kWgSlots][kWgQueues + 1];
+__device__ uint32_t g_wgrad_mx_sched[kWgSlots][kWgQueues];
+
+__global__ void __launch_bounds__(64) wgrad_mx_sched_reset_kernel(int slot) {
+  if (threadIdx.x < kWgQueues) g_wgrad_mx_sched[slot][threadIdx.x] = 0u;
+}
 
 __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[MSTAGE];
@@ -628,12 +634,6 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
       process(by_rank[k * nq + ((k & 1) ? nq - 1 - q : q)], rem);
     }
   }
-  if (threadIdx.x == 0) {
-    if (atomicAdd(&ctr[kWgQueues], 1u) == gridDim.x - 1) {
-      for (int q = 0; q < kWgQueues; ++q) atomicExch(&ctr[q], 0u);
-      atomicExch(&ctr[kWgQueues], 0u);
-    }
-  }
 }
 
 }  // namespace mx
@@ -673,6 +673,7 @@ moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s) {
   int64_t grid = moe_host::device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
+  hipLaunchKernelGGL(fwd::mx::wgrad_mx_sched_reset_kernel, dim3(1), dim3(64), 0, s, b.sched_slot);
   hipLaunchKernelGGL(fwd::mx::gg_wgrad_mx_kernel, dim3((unsigned)grid), dim3(fwd::THREADS), 0, s, b);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -23,14 +23,9 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ group_sizes, int G,
                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
   __shared__ int64_t s_rows;
-  if (threadIdx.x == 0) {
-    int64_t tot = rows;
-    if (group_sizes) {
-      tot = 0;
-      for (int g = 0; g < G; ++g) tot += max(group_sizes[g], 0);
-      tot = min(tot, rows);
-    }
-    s_rows = tot;
+  if (threadIdx.x < kWave) {
+    const int64_t tot = group_sizes ? rows_in_use(group_sizes, G, rows) : rows;
+    if (threadIdx.x == 0) s_rows = tot;
   }
   __syncthreads();
   const int64_t nrows = s_rows;

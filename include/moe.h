@@ -177,8 +177,9 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
  *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
  *   Its workgroups take tiles from counters in the library's own device
- *   memory (64 slots handed out in turn, each zeroed again by the call that
- *   used it), so up to 64 such calls may be in flight on one GPU at once;
+ *   memory (64 slots handed out in turn; each call first enqueues a small
+ *   kernel that zeroes its slot, so a call that ended part-way leaves
+ *   nothing behind), so up to 64 such calls may be in flight on one GPU at once;
  *   a captured call keeps its slot on every replay, so one graph must not
  *   be replayed on two streams concurrently.  Each tile is computed by one
  *   workgroup in a fixed order: results are bitwise reproducible.
@@ -284,18 +285,32 @@ moe_status_t moe_pack_weights_mxfp8(const uint8_t* q, const uint8_t* scale, int3
 moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, const int32_t* perm_dst,
                                    int64_t T, int32_t d, int32_t K, uint16_t* y, void* stream);
 
-/* Backward of the combine: dy_perm[perm_dst[t*K+k], :] = bf16(w[t,k] * dy[t, :])
- * and d_topk_w[t,k] = sum_j dy[t,j] * y_perm[perm_dst[t*K+k], j] (fp32).
- * dy bf16 [T,d], y_perm bf16 [T*K,d], dy_perm bf16 [T*K,d], d_topk_w fp32 [T,K]. */
+/* Backward of the combine.  The combine accumulates each token's per-expert
+ * results weighted by its routing weights (blog section "Optimization 2:
+ * Expert parallelism to integrate Dispatch and Combine", the Combine stage);
+ * the pages train this layer (blog title and intro) but give no backward, so
+ * this is the gradient of that weighted sum with the routing held fixed:
+ *   dy_perm[perm_dst[t*K+k], :] = bf16(w[t,k] * dy[t, :])
+ *   d_topk_w[t,k] = sum_j dy[t,j] * y_perm[perm_dst[t*K+k], j] (fp32),
+ * the second being what a router's own backward would take in.
+ * dy bf16 [T,d], y_perm bf16 [T*K,d], dy_perm bf16 [T*K,d], d_topk_w fp32 [T,K];
+ * d % 8 == 0; dy, y_perm, dy_perm 16-byte aligned.  Each row of dy_perm is
+ * written by exactly one pair, so the result is bitwise reproducible. */
 moe_status_t moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
                                   const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint16_t* dy_perm,
                                   float* d_topk_w, void* stream);
 
-/* Backward of SwiGLU from the stored pre-activations gu = [g | u] bf16
- * [m_cap, 2f] and dh bf16 [m_cap, f]: with s = sigmoid(g),
- * dgu[:, j] = bf16(dh*u*s*(1 + g*(1-s))), dgu[:, f+j] = bf16(dh*g*s).
- * Rows >= sum(group_sizes) are skipped (group_sizes may be NULL: all m_cap
- * rows).  f % 8 == 0. */
+/* Backward of SwiGLU.  The expert MLP's two input projections are the
+ * blog's moe_mlpwi_0 / moe_mlpwi_1 (gate and up, fused into one weight by
+ * prefuse_moe_weights), whose activations the DeepSeek-V3 training config
+ * keeps for the backward pass (section "Performance reproduction for
+ * DeepSeek V3", custom_remat_config; section "JAX host offloading": saved
+ * intermediate activations).  From those stored pre-activations
+ * gu = [g | u] bf16 [m_cap, 2f] and dh bf16 [m_cap, f], with s = sigmoid(g):
+ *   dgu[:, j] = bf16(dh*u*s*(1 + g*(1-s))),  dgu[:, f+j] = bf16(dh*g*s)
+ * (the derivative of silu(g)*u), fp32 arithmetic.  Rows >= sum(group_sizes)
+ * are skipped (group_sizes may be NULL: all m_cap rows); negative sizes
+ * count as 0.  f % 8 == 0; gu, dh, dgu 16-byte aligned. */
 moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
                                  const int32_t* group_sizes, int32_t G, uint16_t* dgu, void* stream);
 
