@@ -110,3 +110,35 @@ def check_route_fused(ops, x: torch.Tensor, wr: torch.Tensor, bias, K: int, reno
         np.testing.assert_array_equal(pr["perm_dst"].cpu().numpy(), dst)
         np.testing.assert_array_equal(host_u16(pr["x_perm"]), orc.gather_rows(x, src, K))
     return int((~clear).sum()), out
+
+
+# ---------------------------------------------------------------- full-size sampling helpers
+
+def mre_u16(got_u16, ref_u16) -> float:
+    """max |got - ref| / max |ref| of two bf16 bit arrays."""
+    g, r = orc.bf16_to_f64(got_u16), orc.bf16_to_f64(ref_u16)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def rel_l2_u16(got_u16, ref_u16) -> float:
+    g, r = orc.bf16_to_f64(got_u16), orc.bf16_to_f64(ref_u16)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    return float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300))
+
+
+def sample_rows(sizes, n_extra, seed):
+    """Every non-empty group's first and last row plus n_extra random rows."""
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    rows = []
+    for g in range(len(sizes)):
+        if sizes[g] > 0:
+            rows += [offs[g], offs[g + 1] - 1]
+    rng = np.random.default_rng(seed)
+    rows += list(rng.choice(int(offs[-1]), size=n_extra, replace=False))
+    return np.unique(np.array(rows, np.int64))
+
+
+def rows_of(t: torch.Tensor, rows) -> np.ndarray:
+    """bf16 rows of a device tensor as uint16 bits on the host."""
+    return host_u16(t[torch.from_numpy(np.asarray(rows, np.int64)).to(t.device)])
