@@ -92,10 +92,24 @@ __device__ __forceinline__ void swiglu_grad(float g, float u, float d, float& dg
 // [-127, 127], byte = e + 127; codes are the E4M3FN round-to-nearest-even of
 // v * 2^-e clamped to +-448.  v * 2^-e is exact in fp32 for bf16 inputs;
 // v_cvt_pk_fp8_f32 rounds to nearest even and keeps the sign of zero.
-// floor(log2(amax)) - 8 from the fp32 bits of a bf16 amax; clamped
+// A block holding a NaN or an infinity has no finite shared exponent: its
+// scale is the E8M0 NaN (byte 0xFF = kMxNaN + 127), which makes every element
+// of the block NaN, and each code is the element format's NaN with the
+// value's sign (E2M1, which has none, saturates to its largest code).
+constexpr int kMxNaN = 128;
+
+// running amax of a block: |v| compared as integer bits, so that every
+// finite value < +inf < NaN and a non-finite element is never dropped
+__device__ __forceinline__ float mx_absmax(float m, float v) {
+  return __uint_as_float(max(__float_as_uint(m), __float_as_uint(v) & 0x7FFFFFFFu));
+}
+
+// floor(log2(amax)) - 8 from the fp32 bits of a bf16 amax; clamped;
+// kMxNaN for a NaN or infinite amax
 __device__ __forceinline__ int mx_exponent(float amax) {
   const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
   if (ef == 0) return -127;  // zero or subnormal amax: floor(log2) <= -127
+  if (ef == 255) return kMxNaN;
   return max(-127, min(127, ef - 127 - 8));
 }
 
@@ -119,6 +133,27 @@ __device__ __forceinline__ float scale_pow2(float v, int e) {
   const int ne = -e;  // in [-127, 127]
   if (ne >= -126) return v * pow2i(ne);
   return (v * pow2i(-63)) * pow2i(-64);
+}
+
+// E4M3 codes of four values of one block with shared exponent e (byte 0 =
+// a ... byte 3 = d)
+__device__ __forceinline__ uint32_t mx_codes4(float a, float b, float c, float d, int e) {
+  if (e == kMxNaN)
+    return 0x7F7F7F7Fu | ((__float_as_uint(a) >> 31) << 7) | ((__float_as_uint(b) >> 31) << 15) |
+           ((__float_as_uint(c) >> 31) << 23) | ((__float_as_uint(d) >> 31) << 31);
+  return cvt4_e4m3(scale_pow2(a, e), scale_pow2(b, e), scale_pow2(c, e), scale_pow2(d, e));
+}
+
+// the same with a shared exponent per value (four blocks, one value each)
+__device__ __forceinline__ uint32_t mx_nan_byte(uint32_t q, float v, int e, int sh) {
+  return e == kMxNaN ? ((q & ~(0xFFu << sh)) | ((0x7Fu | ((__float_as_uint(v) >> 31) << 7)) << sh)) : q;
+}
+__device__ __forceinline__ uint32_t mx_codes4(float a, float b, float c, float d, int ea, int eb, int ec, int ed) {
+  uint32_t q = cvt4_e4m3(scale_pow2(a, ea), scale_pow2(b, eb), scale_pow2(c, ec), scale_pow2(d, ed));
+  q = mx_nan_byte(q, a, ea, 0);
+  q = mx_nan_byte(q, b, eb, 8);
+  q = mx_nan_byte(q, c, ec, 16);
+  return mx_nan_byte(q, d, ed, 24);
 }
 
 // silu(g) = g * sigmoid(g); hardware exp and reciprocal (about 1 ulp each)

@@ -202,14 +202,13 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
         }
         float amax = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(h[v]));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        for (int v = 0; v < 16; ++v) amax = mx_absmax(amax, h[v]);
+        amax = mx_absmax(amax, __shfl_xor(amax, 32, 64));
         const int e = mx_exponent(amax);
         const int cb = wn * (WTN / 2) + i * 32;   // the block's first column in the tile
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t codes = cvt4_e4m3(scale_pow2(h[4 * q], e), scale_pow2(h[4 * q + 1], e),
-                                           scale_pow2(h[4 * q + 2], e), scale_pow2(h[4 * q + 3], e));
+          const uint32_t codes = mx_codes4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3], e);
           *reinterpret_cast<uint32_t*>(lds_codes + mr * TC + cb + q * 8 + g * 4) = codes;
         }
         if (g == 0) lds_scales[mr * (TC / 32) + cb / 32] = (uint8_t)(e + 127);

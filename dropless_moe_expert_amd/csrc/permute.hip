@@ -220,14 +220,14 @@ __global__ __launch_bounds__(256) void permute_scatter_mx_kernel(const uint16_t*
     if (live) unpack8(src[v], f);
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    for (int j = 0; j < 8; ++j) amax = mx_absmax(amax, f[j]);
+    amax = mx_absmax(amax, __shfl_xor(amax, 1, 64));
+    amax = mx_absmax(amax, __shfl_xor(amax, 2, 64));
     const int e = mx_exponent(amax);
     if (live) {
       uint2 q;
-      q.x = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
-      q.y = cvt4_e4m3(scale_pow2(f[4], e), scale_pow2(f[5], e), scale_pow2(f[6], e), scale_pow2(f[7], e));
+      q.x = mx_codes4(f[0], f[1], f[2], f[3], e);
+      q.y = mx_codes4(f[4], f[5], f[6], f[7], e);
 #pragma unroll
       for (int k = 0; k < KM; ++k) {
         if (k < K) {

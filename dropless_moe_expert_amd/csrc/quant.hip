@@ -9,7 +9,8 @@
 // scaling figure: each group of (usually) 32 values gets its own scale.
 // Scale rule (OCP MX v1.0): e = floor(log2 amax) - 8 (8 = largest E4M3
 // exponent) clamped to [-127, 127], byte = e + 127; codes are the E4M3FN
-// round-to-nearest-even of v * 2^-e clamped to +-448.
+// round-to-nearest-even of v * 2^-e clamped to +-448.  A block holding a NaN
+// or an infinity gets the E8M0 NaN scale and NaN codes (common.h).
 //
 // v * 2^-e is exact in fp32 (bf16 input times a power of two that keeps the
 // result below 512); v_cvt_pk_fp8_f32 rounds to nearest even and keeps the
@@ -40,14 +41,14 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(const uint16_t* __re
     if (live) unpack8(reinterpret_cast<const uint4*>(x)[idx], f);
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(f[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    for (int j = 0; j < 8; ++j) amax = mx_absmax(amax, f[j]);
+    amax = mx_absmax(amax, __shfl_xor(amax, 1, 64));
+    amax = mx_absmax(amax, __shfl_xor(amax, 2, 64));
     const int e = mx_exponent(amax);
     if (live) {
       uint2 out;
-      out.x = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
-      out.y = cvt4_e4m3(scale_pow2(f[4], e), scale_pow2(f[5], e), scale_pow2(f[6], e), scale_pow2(f[7], e));
+      out.x = mx_codes4(f[0], f[1], f[2], f[3], e);
+      out.y = mx_codes4(f[4], f[5], f[6], f[7], e);
       reinterpret_cast<uint2*>(q)[idx] = out;
       if ((idx & 3) == 0) scale[idx >> 2] = (uint8_t)(e + 127);
     }
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
       float f[8];
       unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) amax[j] = fmaxf(amax[j], fabsf(f[j]));
+      for (int j = 0; j < 8; ++j) amax[j] = mx_absmax(amax[j], f[j]);
     }
     int e[8];
     uint2 sc;
@@ -115,8 +116,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
       float f[8];
       unpack8(*reinterpret_cast<const uint4*>(x + (r0 + i) * cols + c8), f);
       uint2 out;
-      out.x = cvt4_e4m3(scale_pow2(f[0], e[0]), scale_pow2(f[1], e[1]), scale_pow2(f[2], e[2]), scale_pow2(f[3], e[3]));
-      out.y = cvt4_e4m3(scale_pow2(f[4], e[4]), scale_pow2(f[5], e[5]), scale_pow2(f[6], e[6]), scale_pow2(f[7], e[7]));
+      out.x = mx_codes4(f[0], f[1], f[2], f[3], e[0], e[1], e[2], e[3]);
+      out.y = mx_codes4(f[4], f[5], f[6], f[7], e[4], e[5], e[6], e[7]);
       *reinterpret_cast<uint2*>(q + (r0 + i) * cols + c8) = out;
     }
   }
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       const int c = t & (QT_C - 1), b = t >> 6;   // b = 0..3 over the pair's 128 positions
       float amax = 0.f;
 #pragma unroll 8
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)xt[(32 * b + i) * QT_LD + c] << 16)));
+      for (int i = 0; i < 32; ++i) amax = mx_absmax(amax, __uint_as_float((uint32_t)xt[(32 * b + i) * QT_LD + c] << 16));
       const int e = mx_exponent(amax);
       st[4 * c + b] = (uint8_t)(e + 127);
       uint32_t w[8];
@@ -318,7 +319,17 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)xt[(32 * b + 4 * q + i) * QT_LD + c] << 16);
-        w[q] = cvt4_e4m3(scale_pow2(f[0], e), scale_pow2(f[1], e), scale_pow2(f[2], e), scale_pow2(f[3], e));
+        w[q] = mx_codes4(f[0], f[1], f[2], f[3], e);
+      }
+      if (e == kMxNaN) {
+        // a NaN block's codes are NaN only at the group's rows: the padding
+        // positions past them keep zero codes, as in every other block
+        const int nv = min(32, max(0, n[b >> 1] - 32 * (b & 1)));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (4 * q + k >= nv) w[q] &= ~(0xFFu << (8 * k));
       }
       uint4* d = reinterpret_cast<uint4*>(ct + c * (2 * QT_R) + 32 * b);
       d[0] = make_uint4(w[0], w[1], w[2], w[3]);
@@ -336,7 +347,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t p = xr[i];
-          amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(p << 16)), fabsf(__uint_as_float(p & 0xFFFF0000u))));
+          amax = mx_absmax(mx_absmax(amax, __uint_as_float(p << 16)), __uint_as_float(p & 0xFFFF0000u));
         }
         const int e = mx_exponent(amax);
         asm volatile("" ::: "memory");   // re-read the row below instead of keeping 16 words live
@@ -344,8 +355,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const uint32_t p0 = xr[2 * q], p1 = xr[2 * q + 1];
-          w[q] = cvt4_e4m3(scale_pow2(__uint_as_float(p0 << 16), e), scale_pow2(__uint_as_float(p0 & 0xFFFF0000u), e),
-                           scale_pow2(__uint_as_float(p1 << 16), e), scale_pow2(__uint_as_float(p1 & 0xFFFF0000u), e));
+          w[q] = mx_codes4(__uint_as_float(p0 << 16), __uint_as_float(p0 & 0xFFFF0000u), __uint_as_float(p1 << 16),
+                           __uint_as_float(p1 & 0xFFFF0000u), e);
         }
         const int64_t row = r0[h] + r;
         uint4* d = reinterpret_cast<uint4*>(q0 + row * cols + cb);
@@ -407,11 +418,11 @@ __global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __r
     if (live) unpack8(reinterpret_cast<const uint4*>(x)[v], f);
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    for (int i = 0; i < 8; ++i) amax = mx_absmax(amax, f[i]);
+    amax = mx_absmax(amax, __shfl_xor(amax, 1, 64));
+    amax = mx_absmax(amax, __shfl_xor(amax, 2, 64));
     const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
-    const int e = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 2));
+    const int e = ef == 0 ? -127 : ef == 255 ? kMxNaN : max(-127, min(127, ef - 127 - 2));
     const uint32_t byte = (uint32_t)(e + 127);
     const int g0 = lane & ~15;
     const uint32_t word = __shfl(byte, g0, 64) | (__shfl(byte, g0 + 4, 64) << 8) | (__shfl(byte, g0 + 8, 64) << 16) |
@@ -419,7 +430,8 @@ __global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __r
     if (live) {
       uint32_t codes = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) codes |= e2m1_code(scale_pow2(f[i], e)) << (4 * i);
+      for (int i = 0; i < 8; ++i)
+        codes |= (e == kMxNaN ? 7u | ((__float_as_uint(f[i]) >> 28) & 8u) : e2m1_code(scale_pow2(f[i], e))) << (4 * i);
       reinterpret_cast<uint32_t*>(q)[v] = codes;
       if ((k8 & 15u) == 0) reinterpret_cast<uint32_t*>(sc)[(size_t)(k8 >> 4) * rows + r] = word;
     }

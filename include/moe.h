@@ -321,6 +321,10 @@ moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t
  * MX v1.0): per block, e = floor(log2(amax)) - 8 clamped to [-127, 127],
  * scale byte = e + 127 (amax == 0 gives byte 0); codes = E4M3FN
  * round-to-nearest-even of clamp(v * 2^-e, -448, 448), sign kept on zero.
+ * A block holding a NaN or an infinity gets scale byte 0xFF (the E8M0 NaN:
+ * every element of the block decodes to NaN) and codes 0x7F with each
+ * value's sign bit (E4M3FN's NaN; the format has no infinity).  The same
+ * rule holds for every entry point that writes MXFP8 codes.
  *
  * axis 0: blocks of 32 along each row. x bf16 [rows, cols] -> q [rows, cols],
  *   scale [rows, cols/32].  If group_sizes != NULL only rows < sum(sizes)
@@ -339,7 +343,9 @@ moe_status_t mxfp8_group_quantize(const uint16_t* x, int64_t rows, int32_t cols,
  * blog's planned 4-bit format, closing of "Optimization 1").  Per row, per 32
  * consecutive columns: scale 2^e, e = floor(log2 amax) - 2 clamped to
  * [-127, 127] (byte e + 127); codes = round-to-nearest-even of x / 2^e on
- * {0, 0.5, 1, 1.5, 2, 3, 4, 6}, saturating, sign kept (also of zero).
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6}, saturating, sign kept (also of zero).  A
+ * block holding a NaN or an infinity gets scale byte 0xFF (E8M0 NaN) and
+ * codes 7 with each value's sign bit (E2M1 has no NaN: its largest code).
  * x bf16 [rows, cols] (16-byte aligned); codes [rows, cols/2] (16-byte
  * aligned, element 2i in the low nibble of byte i); scales stage-major
  * [cols/128, rows, 4].  cols % 128 == 0.  Weights [G, N, K] quantise as

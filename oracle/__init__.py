@@ -51,6 +51,7 @@ def lib():
                 "oracle_bf16_round_array": (None, [P, P, i64]),
                 "oracle_e4m3_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
                 "oracle_f64_to_e4m3": (ctypes.c_uint8, [ctypes.c_double]),
+                "oracle_e8m0_to_f64": (ctypes.c_double, [ctypes.c_uint8]),
                 "oracle_route_logits": (None, [P, P, P, i64, i32, i32, P]),
                 "oracle_route_topk": (None, [P, i64, i32, i32, i32, P, P]),
                 "oracle_permute": (None, [P, i64, i32, i32, P, P, P, P]),
@@ -129,6 +130,13 @@ def e4m3_to_f64(codes) -> np.ndarray:
     c = _np(codes, np.uint8)
     table = np.array([L.oracle_e4m3_to_f64(i) for i in range(256)], dtype=np.float64)
     return table[c]
+
+
+def e8m0_to_f64(s) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(s-127); 0xFF -> NaN."""
+    L = lib()
+    table = np.array([L.oracle_e8m0_to_f64(i) for i in range(256)], dtype=np.float64)
+    return table[_np(s, np.uint8)]
 
 
 def f64_to_e4m3(v) -> np.ndarray:

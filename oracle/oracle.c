@@ -105,10 +105,13 @@ double oracle_e4m3_to_f64(uint8_t c)
     return s ? -v : v;
 }
 
-/* Saturating round-to-nearest-even encode of an (already scaled) value. */
+/* Saturating round-to-nearest-even encode of an (already scaled) value.
+   NaN and +-infinity become E4M3FN's NaN with the value's sign (the format
+   has no infinity; only finite values saturate at 448). */
 uint8_t oracle_f64_to_e4m3(double x)
 {
     uint8_t sign = signbit(x) ? 0x80 : 0;
+    if (!isfinite(x)) return sign | 0x7F;
     double a = fabs(x);
     if (a >= 448.0) a = 448.0;                       /* clamp before rounding */
     if (a == 0.0) return sign;
@@ -317,8 +320,25 @@ void oracle_unpermute_combine(const uint16_t* y_perm, const float* w, const int3
 /* 1" MXFP8 block scaling].  Rule: OCP MX v1.0 (see header).                   */
 /* ------------------------------------------------------------------------- */
 
+/* E8M0 scale byte -> its value: 2^(s-127); 0xFF is NaN (OCP MX v1.0). */
+double oracle_e8m0_to_f64(uint8_t s)
+{
+    return s == 0xFF ? NAN : ldexp(1.0, (int)s - 127);
+}
+
+/* One block.  A block holding a NaN or an infinity has no finite shared
+   exponent: its scale is the E8M0 NaN (0xFF), which makes every element of
+   the block NaN, and each code is the element format's NaN with the value's
+   sign. */
 static void mx_block(const double* v, int n, uint8_t* codes, uint8_t* scale)
 {
+    for (int i = 0; i < n; ++i) {
+        if (!isfinite(v[i])) {
+            *scale = 0xFF;
+            for (int j = 0; j < n; ++j) codes[j] = oracle_f64_to_e4m3(signbit(v[j]) ? -NAN : NAN);
+            return;
+        }
+    }
     double amax = 0.0;
     for (int i = 0; i < n; ++i) if (fabs(v[i]) > amax) amax = fabs(v[i]);
     if (amax == 0.0) {
@@ -394,7 +414,7 @@ void oracle_mx_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const uin
         if (e < 0) continue;
         double* av = (double*)malloc(sizeof(double) * (size_t)Kd);
         for (int i = 0; i < Kd; ++i)
-            av[i] = ldexp(oracle_e4m3_to_f64(Aq[r * Kd + i]), (int)As[r * nb + i / 32] - 127);
+            av[i] = oracle_e4m3_to_f64(Aq[r * Kd + i]) * oracle_e8m0_to_f64(As[r * nb + i / 32]);
         const uint8_t* bq = Bq + (int64_t)e * N * Kd;
         const uint8_t* bs = Bs + (int64_t)e * N * nb;
         double acc2[2];
@@ -403,7 +423,7 @@ void oracle_mx_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const uin
                 int64_t col = n + (int64_t)h * nout;
                 double acc = 0.0;
                 for (int i = 0; i < Kd; ++i)
-                    acc += av[i] * ldexp(oracle_e4m3_to_f64(bq[col * Kd + i]), (int)bs[col * nb + i / 32] - 127);
+                    acc += av[i] * oracle_e4m3_to_f64(bq[col * Kd + i]) * oracle_e8m0_to_f64(bs[col * nb + i / 32]);
                 acc2[h] = acc;
             }
             if (swiglu) {
@@ -432,12 +452,14 @@ double oracle_e2m1_to_f64(uint8_t c)
 }
 
 /* round to nearest representable magnitude, ties to the even code (mantissa
-   bit 0), saturating at 6; the sign is kept (also for a zero result). */
+   bit 0), saturating at 6; the sign is kept (also for a zero result).  E2M1
+   has no infinity or NaN: infinities saturate like any value past 6, and NaN
+   takes the same largest-magnitude code with its sign. */
 uint8_t oracle_f64_to_e2m1(double v)
 {
     uint8_t sign = signbit(v) ? 8 : 0;
     double a = fabs(v);
-    if (a >= 6.0) return sign | 7;        /* saturation: 6 is the largest magnitude */
+    if (isnan(a) || a >= 6.0) return sign | 7;   /* saturation: 6 is the largest magnitude */
     int best = 0;
     double bd = INFINITY;
     for (int c = 0; c < 8; ++c) {
@@ -451,6 +473,13 @@ uint8_t oracle_f64_to_e2m1(double v)
    exponent), clamped to [-127, 127]; codes one per byte */
 static void mx4_block(const double* v, int n, uint8_t* codes, uint8_t* scale)
 {
+    for (int i = 0; i < n; ++i) {             /* NaN or infinity: NaN scale, as mx_block */
+        if (!isfinite(v[i])) {
+            *scale = 0xFF;
+            for (int j = 0; j < n; ++j) codes[j] = oracle_f64_to_e2m1(signbit(v[j]) ? -NAN : NAN);
+            return;
+        }
+    }
     double amax = 0.0;
     for (int i = 0; i < n; ++i) if (fabs(v[i]) > amax) amax = fabs(v[i]);
     if (amax == 0.0) {
@@ -497,7 +526,7 @@ void oracle_mx4_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const ui
         if (e < 0) continue;
         double* av = (double*)malloc(sizeof(double) * (size_t)Kd);
         for (int i = 0; i < Kd; ++i)
-            av[i] = ldexp(oracle_e2m1_to_f64(Aq[r * Kd + i]), (int)As[r * nb + i / 32] - 127);
+            av[i] = oracle_e2m1_to_f64(Aq[r * Kd + i]) * oracle_e8m0_to_f64(As[r * nb + i / 32]);
         const uint8_t* bq = Bq + (int64_t)e * N * Kd;
         const uint8_t* bs = Bs + (int64_t)e * N * nb;
         double acc2[2];
@@ -506,7 +535,7 @@ void oracle_mx4_grouped_gemm_rows(const uint8_t* Aq, const uint8_t* As, const ui
                 int64_t col = n + (int64_t)h * nout;
                 double acc = 0.0;
                 for (int i = 0; i < Kd; ++i)
-                    acc += av[i] * ldexp(oracle_e2m1_to_f64(bq[col * Kd + i]), (int)bs[col * nb + i / 32] - 127);
+                    acc += av[i] * oracle_e2m1_to_f64(bq[col * Kd + i]) * oracle_e8m0_to_f64(bs[col * nb + i / 32]);
                 acc2[h] = acc;
             }
             if (swiglu) {
@@ -539,8 +568,8 @@ void oracle_mx_grouped_wgrad(const uint8_t* Aq, const uint8_t* As, const uint8_t
                 double acc = 0.0;
                 for (int64_t i = 0; i < s; ++i) {
                     int64_t r = o + i, blk = pb + i / 32;
-                    double a = ldexp(oracle_e4m3_to_f64(Aq[r * P + p]), (int)As[blk * P + p] - 127);
-                    double b = ldexp(oracle_e4m3_to_f64(Bq[r * Q + q]), (int)Bs[blk * Q + q] - 127);
+                    double a = oracle_e4m3_to_f64(Aq[r * P + p]) * oracle_e8m0_to_f64(As[blk * P + p]);
+                    double b = oracle_e4m3_to_f64(Bq[r * Q + q]) * oracle_e8m0_to_f64(Bs[blk * Q + q]);
                     acc += a * b;
                 }
                 out[(int64_t)p * Q + q] = oracle_f64_to_bf16(acc);

@@ -959,3 +959,66 @@ def test_routed_layer_mxfp4(ops):
     np.testing.assert_array_equal(parts["group_sizes"].cpu().numpy(), sizes)
     assert rel_l2(parts["h"][:T * K], h) <= MX_TOL
     assert rel_l2(y, y_ref) <= MX_TOL
+
+
+# ------------------------------------------------------------------- NaN and infinities
+
+def _plant_nonfinite(rng, x: torch.Tensor, n: int) -> torch.Tensor:
+    """x (bf16, CPU) with n entries replaced by +-NaN / +-inf bit patterns."""
+    bits = x.clone().view(torch.int16).numpy().view(np.uint16).copy()
+    flat = bits.reshape(-1)
+    pos = rng.choice(flat.size, size=n, replace=False)
+    flat[pos] = rng.choice(np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80], np.uint16), size=n)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+
+
+def test_quantizers_nonfinite(ops):
+    """A block holding a NaN or an infinity: scale 0xFF and NaN codes with each
+    value's sign (E2M1: code 7 with the sign), other blocks untouched - bit
+    for bit the oracle's, in every quantiser that writes MX codes."""
+    rng = np.random.default_rng(31)
+    R, C = 200, 256
+    x = _plant_nonfinite(rng, bf16(rng, R, C, scale=2.0), 40)
+    say("nonfinite mx q0")
+    q_ref, s_ref = orc.mxfp8_quantize(x, 0)
+    assert (s_ref == 0xFF).sum() >= 30
+    q, s = ops.mxfp8_quantize(dev(x), 0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    # axis 1, grouped, and the transposed layout with the row-wise codes
+    sizes = np.array([37, 0, 100, 63], np.int32)
+    M = int(sizes.sum())
+    say("nonfinite mx q1 / qT", M)
+    q_ref, s_ref = orc.mxfp8_quantize(x[:M], 1, sizes)
+    assert (s_ref == 0xFF).any()
+    S = dev(torch.from_numpy(sizes))
+    q1, s1 = ops.mxfp8_quantize(dev(x), 1, S)
+    qT, sT, q0, s0 = ops.mxfp8_quantize_transposed(dev(x), S, rows_too=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q1[:M].cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s1[:s_ref.shape[0]].cpu().numpy(), s_ref)
+    want_q, want_s, used = _to_transposed(q_ref, s_ref, sizes, qT.shape[1])
+    np.testing.assert_array_equal(qT[:, :used].cpu().numpy(), want_q[:, :used])
+    np.testing.assert_array_equal(sT[:, :used // 32].cpu().numpy(), want_s[:, :used // 32])
+    q0_ref, s0_ref = orc.mxfp8_quantize(x[:M], 0)
+    np.testing.assert_array_equal(q0[:M].cpu().numpy(), q0_ref)
+    np.testing.assert_array_equal(s0[:M].cpu().numpy(), s0_ref)
+    # the dispatch writing MXFP8 rows
+    T, E, K = 64, 8, 2
+    say("nonfinite permute mxfp8", T, E, K)
+    ids = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int32)
+    xt = x[:T]
+    _, _, src, _ = orc.permute(ids, E)
+    xq_ref, xs_ref = orc.mxfp8_quantize(orc.gather_rows(xt, src, K), 0)
+    out = ops.permute_mxfp8(dev(xt), dev(torch.from_numpy(ids)), E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out["xq"].cpu().numpy(), xq_ref.reshape(T * K, C))
+    np.testing.assert_array_equal(out["xs"].cpu().numpy(), xs_ref.reshape(T * K, C // 32))
+    # MXFP4
+    say("nonfinite mxfp4")
+    q_ref, s_ref = _mx4_layout(*orc.mxfp4_quantize(x))
+    q4, s4 = ops.mxfp4_quantize(dev(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q4.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s4.cpu().numpy(), s_ref)

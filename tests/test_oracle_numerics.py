@@ -167,3 +167,80 @@ def test_mx_axis1_group_restart(orc):
                 np.testing.assert_array_equal(q[r0:r1, c][nz], want[nz])
         o += n
         P += (n + 31) // 32
+
+
+# --------------------------------------------------------------------------- NaN and infinities
+# E4M3FN has no infinity and one NaN per sign (0x7F / 0xFF); E8M0 reserves
+# 0xFF for NaN; E2M1 has neither (OCP MX v1.0 element and scale formats).
+# Reading of the MX block rule for a block holding a NaN or an infinity: its
+# amax has no finite exponent, so the block scale is the E8M0 NaN, which makes
+# every element of the block NaN; each code is then the element format's
+# encoding of NaN with the value's sign (E2M1: its largest code, as a
+# saturation).
+
+_NONFINITE_BF16 = {"nan": 0x7FC0, "-nan": 0xFFC0, "inf": 0x7F80, "-inf": 0xFF80}
+
+
+def test_e4m3_encode_nonfinite_matches_torch(orc):
+    vals = np.array([np.nan, -np.nan, np.inf, -np.inf], np.float64)
+    vals[1] = np.copysign(np.nan, -1.0)
+    ref = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.f64_to_e4m3(vals)
+    assert got.tolist() == ref.tolist() == [0x7F, 0xFF, 0x7F, 0xFF]
+
+
+def test_e8m0_decode(orc):
+    s = orc.e8m0_to_f64(np.arange(256, dtype=np.uint8))
+    assert np.isnan(s[255]) and not np.isnan(s[:255]).any()
+    np.testing.assert_array_equal(s[:255], 2.0 ** (np.arange(255) - 127.0))
+
+
+def _row_with(blocks):
+    """bf16 bits [1, 32*len(blocks)]: block b holds normal draws, with the
+    listed non-finite patterns planted at the listed positions."""
+    rng = np.random.default_rng(5)
+    x = orc_bits(rng.standard_normal(32 * len(blocks)).astype(np.float32))
+    for b, plant in enumerate(blocks):
+        for pos, name in plant:
+            x[32 * b + pos] = _NONFINITE_BF16[name]
+    return x[None, :]
+
+
+def orc_bits(a32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(a32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_mx_block_nonfinite(orc):
+    x = _row_with([[(3, "nan")], [(0, "-inf")], [], [(31, "inf"), (7, "-nan")]])
+    q, s = orc.mxfp8_quantize(x, 0)
+    assert s[0, 0] == 0xFF and s[0, 1] == 0xFF and s[0, 3] == 0xFF and s[0, 2] != 0xFF
+    sign = (x[0] >> 15).astype(np.uint8)
+    for b in (0, 1, 3):
+        np.testing.assert_array_equal(q[0, 32 * b:32 * b + 32], 0x7F | (sign[32 * b:32 * b + 32] << 7))
+    # the finite block is quantised as on its own
+    q2, s2 = orc.mxfp8_quantize(np.ascontiguousarray(x[:, 64:96]), 0)
+    assert s2[0, 0] == s[0, 2] and np.array_equal(q2[0], q[0, 64:96])
+    # decoded: every element of a NaN-scale block is NaN, the finite block is finite
+    v = orc.e4m3_to_f64(q[0]) * np.repeat(orc.e8m0_to_f64(s[0]), 32)
+    assert np.isnan(v[:64]).all() and np.isnan(v[96:]).all() and np.isfinite(v[64:96]).all()
+
+
+def test_mx_block_nonfinite_grouped_columns(orc):
+    rng = np.random.default_rng(9)
+    x = orc_bits(rng.standard_normal((70, 16)).astype(np.float32))
+    x[40, 5] = _NONFINITE_BF16["-inf"]       # group 1 (rows 30..69), its block 0 (rows 30..61)
+    q, s = orc.mxfp8_quantize(x, 1, np.array([30, 40], np.int32))
+    # blocks: group 0 -> scale row 0; group 1 -> rows 1 (30..61), 2 (62..69)
+    assert s[1, 5] == 0xFF and (s[[0, 2], 5] != 0xFF).all() and (np.delete(s[1], 5) != 0xFF).all()
+    sign = (x[30:62, 5] >> 15).astype(np.uint8)
+    np.testing.assert_array_equal(q[30:62, 5], 0x7F | (sign << 7))
+
+
+def test_e2m1_nonfinite(orc):
+    v = np.array([np.nan, np.copysign(np.nan, -1.0), np.inf, -np.inf, 1e300, -7.0])
+    assert orc.f64_to_e2m1(v).tolist() == [7, 15, 7, 15, 7, 15]
+    x = np.ascontiguousarray(np.tile(_row_with([[], [(2, "-nan")], [], []]), (2, 1)))
+    q, s = orc.mxfp4_quantize(x)
+    assert (s[:, 1] == 0xFF).all() and (s[:, [0, 2, 3]] != 0xFF).all()
+    sign = (x[:, 32:64] >> 15).astype(np.uint8)
+    np.testing.assert_array_equal(q[:, 32:64], 7 | (sign << 3))
