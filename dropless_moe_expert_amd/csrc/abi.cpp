@@ -20,6 +20,8 @@ moe_status_t moe_permute_routed_launch(const uint16_t*, const int32_t*, int64_t,
                                        int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 moe_status_t moe_permute_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
                                 int32_t*, int32_t*, int32_t*, uint16_t*, void*, uint32_t*, hipStream_t);
+moe_status_t moe_permute_noalloc_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
+                                        int32_t*, int32_t*, int32_t*, uint16_t*, uint32_t*, hipStream_t);
 moe_status_t moe_permute_mxfp8_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t, int32_t*,
                                       int32_t*, int32_t*, int32_t*, uint8_t*, uint8_t*, void*, uint32_t*, hipStream_t);
 moe_status_t moe_unpermute_combine_launch(const uint16_t*, const float*, const int32_t*, int64_t, int32_t, int32_t,
@@ -115,6 +117,23 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
   if (reinterpret_cast<uintptr_t>(ws) & 255u) return MOE_ERR_ALIGNMENT;
   return moe_permute_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_perm, ws,
                             err_flag, S(stream));
+}
+
+moe_status_t moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                                 int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                                 int32_t* perm_dst, uint16_t* x_perm, uint32_t* err_flag, void* stream) {
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (x) {
+    if (d < 8 || d % 8) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGNMENT;
+  }
+  if (moe_permute_ws_bytes_impl(T, E, K) > MOE_PERMUTE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  return moe_permute_noalloc_launch(x, topk_ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_perm,
+                                    err_flag, S(stream));
 }
 
 moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,

@@ -20,6 +20,8 @@
 //               the token's row once from HBM to its K destinations (16-byte
 //               vector loads and stores, all of a lane's loads of the row in
 //               flight before its stores when K is a compile-time value).
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -240,6 +242,51 @@ __global__ __launch_bounds__(256) void permute_scatter_mx_kernel(const uint16_t*
 }
 
 }  // namespace moe
+
+// ------------------------------------------------------------------ no-allocation variant
+// moe_permute_noalloc runs the same three kernels with their workspace (the
+// per-pair ranks and per-chunk counts) in this file-scope device array
+// instead of a caller buffer.  Every GPU the library runs on holds its own
+// copy at its own address until the process ends.  In host code the array's
+// name is not a device address: its address on the current device comes from
+// hipGetSymbolAddress, taken once per device on the first call there and
+// kept.  Nothing in it needs clearing: the rank kernel writes every entry
+// the later kernels read.  Calls that overlap on one GPU share the array and
+// race.
+namespace {
+constexpr size_t kScratchBytes = MOE_PERMUTE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch, or nullptr
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" moe_status_t moe_permute_launch(const uint16_t*, const int32_t*, int64_t, int32_t, int32_t, int32_t,
+                                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, uint32_t*,
+                                           hipStream_t);
+
+extern "C" moe_status_t moe_permute_noalloc_launch(const uint16_t* x, const int32_t* ids, int64_t T, int32_t d,
+                                                   int32_t E, int32_t K, int32_t* group_sizes,
+                                                   int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
+                                                   uint16_t* x_perm, uint32_t* flag, hipStream_t s) {
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_permute_launch(x, ids, T, d, E, K, group_sizes, group_offsets, perm_src, perm_dst, x_perm, ws, flag, s);
+}
 
 extern "C" size_t moe_permute_ws_bytes_impl(int64_t T, int32_t E, int32_t K) {
   const int64_t M = T * K;

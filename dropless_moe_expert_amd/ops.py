@@ -31,7 +31,7 @@ FLAG_NAN_LOGIT = 0x8
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
-    "moe_permute_mxfp8", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
+    "moe_permute_mxfp8", "moe_permute_noalloc", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
     "moe_combine_backward",
     "moe_swiglu_backward", "moe_swiglu_backward_mxfp8", "mxfp8_group_quantize", "mxfp8_quantize_transposed",
     "moe_pack_weights_bytes",
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "moe_permute_workspace_bytes": (sz, [i64, i32, i32]),
             "moe_permute": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, sz, P, P]),
             "moe_permute_mxfp8": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, sz, P, P]),
+            "moe_permute_noalloc": (ctypes.c_int, [P, P, i64, i32, i32, i32, P, P, P, P, P, P, P]),
             "grouped_gemm_workspace_bytes": (sz, [ctypes.POINTER(GGDesc)]),
             "grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GGDesc), P, P, P, P, P, P, P, P, sz, P, P]),
             "moe_unpermute_combine": (ctypes.c_int, [P, P, P, i64, i32, i32, P, P]),
@@ -186,6 +187,33 @@ def permute(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Opt
                              _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
                              _ptr(out["x_perm"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
                              _ptr(flag), _stream(dev)), "moe_permute")
+    return out
+
+
+def permute_noalloc(x: Optional[torch.Tensor], topk_ids: torch.Tensor, E: int, flag: Optional[torch.Tensor] = None,
+                    out: Optional[dict] = None):
+    """moe_permute_noalloc: moe_permute's outputs, workspace in the library's
+    static device memory (no allocation inside the call).  `out` may supply
+    the output tensors (keys as returned), so that nothing at all is
+    allocated."""
+    assert topk_ids.dtype == torch.int32 and topk_ids.dim() == 2
+    dev = _dev(topk_ids, x)
+    T, K = topk_ids.shape
+    d = 0 if x is None else x.shape[1]
+    if x is not None:
+        assert x.dtype == torch.bfloat16 and x.shape[0] == T
+    M = T * K
+    if out is None:
+        out = dict(
+            group_sizes=torch.empty(E, dtype=torch.int32, device=dev),
+            group_offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+            perm_src=torch.empty(M, dtype=torch.int32, device=dev),
+            perm_dst=torch.empty(M, dtype=torch.int32, device=dev),
+            x_perm=None if x is None else torch.empty((M, d), dtype=torch.bfloat16, device=dev),
+        )
+    _check(lib().moe_permute_noalloc(_ptr(x), _ptr(topk_ids), T, d, E, K, _ptr(out["group_sizes"]),
+                                     _ptr(out["group_offsets"]), _ptr(out["perm_src"]), _ptr(out["perm_dst"]),
+                                     _ptr(out["x_perm"]), _ptr(flag), _stream(dev)), "moe_permute_noalloc")
     return out
 
 

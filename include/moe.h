@@ -105,6 +105,25 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
                          int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
                          uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream);
 
+/* For callers that cannot allocate (code under hipGraph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_permute with the
+ * workspace taken from the library's own device memory, a static array of
+ * MOE_PERMUTE_NOALLOC_SCRATCH_BYTES per GPU held until the process ends, so
+ * the call allocates nothing and needs no ws argument.  Arguments, outputs
+ * and limits as moe_permute; additionally moe_permute_workspace_bytes(T, E,
+ * K) must not exceed MOE_PERMUTE_NOALLOC_SCRATCH_BYTES (8 MiB: T*K up to
+ * 2^20 pairs with E = 256, about 2^21 with E = 8), else MOE_ERR_WORKSPACE is
+ * returned and
+ * nothing is enqueued.  The first call on a device looks up the array's
+ * address there (MOE_ERR_HIP if that fails).  All calls on one GPU share the
+ * array: calls that overlap on one GPU (several streams, or several graphs
+ * replayed concurrently) race and give undefined results; calls ordered on
+ * one stream do not. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status_t moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int64_t T, int32_t d, int32_t E,
+                                 int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
+                                 int32_t* perm_dst, uint16_t* x_perm, uint32_t* err_flag, void* stream);
+
 /* Permute with MXFP8 output (the page's planned quantisation fused into the
  * dispatch, section "Optimization 1"): the same maps as moe_permute, and
  * instead of bf16 rows the E4M3 codes x_q uint8 [T*K, d] and E8M0 scales

@@ -62,6 +62,12 @@ def test_host_checkable_errors_return_status():
     assert L.moe_permute(ctypes.c_void_p((1 << 20) + 2), fake, 4, 16, 8, 2, fake, fake, fake, fake, fake, fake,
                          1 << 20, None, None) == ALIGN
     assert L.moe_permute_workspace_bytes(16384, 128, 8) >= 16384 * 8 * 4
+    # permute without allocation: the same checks, and no more workspace than its 8 MiB of static scratch
+    assert L.moe_permute_noalloc(None, fake, 4, 0, 8, 2, None, None, None, None, None, None, None) == INVALID
+    assert L.moe_permute_noalloc(fake, fake, 4, 12, 8, 2, fake, fake, fake, fake, fake, None, None) == UNSUPPORTED
+    big_T = (1 << 17) + 32                     # 2^20 + 256 pairs with E = 256: past 8 MiB
+    assert L.moe_permute_workspace_bytes(big_T, 256, 8) > (8 << 20) >= L.moe_permute_workspace_bytes(1 << 17, 256, 8)
+    assert L.moe_permute_noalloc(None, fake, big_T, 0, 256, 8, fake, fake, fake, fake, None, None, None) == WS
     # permute with MXFP8 output: d % 32 == 0, outputs required
     assert L.moe_permute_mxfp8(fake, fake, 4, 48, 8, 2, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None,
                                None) == UNSUPPORTED
