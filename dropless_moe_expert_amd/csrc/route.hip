@@ -1,80 +1,131 @@
-// Router top-K with softmax gating: one wavefront per token.
+// Router top-K with softmax gating: a group of LPT lanes per token.
 //
 // Page "NVIDIA Accelerates Dropless MoE Training in JAX Using Transformer
 // Engine", intro: a learned router picks each token's Top-K experts.
 // "AI Systems Performance Engineering" ch. 1, §4.1 softmax worked example:
 // exponentials of (score - row max) divided by their sum.
 //
-// A token's E <= 256 logits sit in registers (E/64 per lane).  K rounds of a
-// wavefront argmax pick the experts; the comparison is on raw fp32 logits,
-// larger wins and equal logits go to the lower expert index, so the ids are
-// exact.  Weights: exp(l - l_max) over the sum (the K picks, or all E).
+// A token's E <= 256 logits are spread over LPT = 8 or 16 lanes (one DPP row
+// holds one or two tokens), VPL <= 16 consecutive ones per lane, so one
+// wavefront serves 64 / LPT tokens.  Each of the K rounds takes every lane's
+// best untaken logit and a butterfly of log2(LPT) DPP exchanges within the
+// group.  Measured on 16384 tokens x 128 experts, top 8: 11.6 us, against
+// 21.7 us for one wavefront per token with a 64-lane argmax through the LDS
+// crossbar per round, 13.0 us for the same groups exchanging through the
+// crossbar, and 14.5 us for lanes that sort 64-bit (logit, index) keys once
+// and pass on their head key per round (64-bit compares and key shifts cost
+// more than the scans they save).  The
+// comparison is on raw fp32 logits, larger wins and equal logits go to the
+// lower expert index, so the ids are exact.  Weights: exp(l - l_max) over
+// the sum (the K picks, or all E).
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 
-constexpr int kRouteMaxPerLane = 4;  // E <= 256
+// Lane exchanges inside a row of 16 lanes by DPP (a VALU move, no trip
+// through the LDS crossbar): level 0 swaps neighbours (quad_perm 1,0,3,2),
+// level 1 pairs of neighbours (quad_perm 2,3,0,1), level 2 the two quads of a
+// half row (row_half_mirror), level 3 the two half rows (row_mirror).  After
+// levels 0..log2(n)-1 every lane of an aligned group of n lanes has met all
+// of them, so a max or a sum over the levels reaches every lane of the group
+// (a sum bit-identically: each level adds the same two values in either
+// order).
+template <int LEVEL>
+__device__ __forceinline__ int dpp_xchg(int v) {
+  constexpr int ctrl = LEVEL == 0 ? 0xB1 : LEVEL == 1 ? 0x4E : LEVEL == 2 ? 0x141 : 0x140;
+  return __builtin_amdgcn_mov_dpp(v, ctrl, 0xF, 0xF, false);
+}
+template <int LEVEL>
+__device__ __forceinline__ float dpp_xchg(float v) {
+  return __int_as_float(dpp_xchg<LEVEL>(__float_as_int(v)));
+}
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+template <int LPT, int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int64_t T, int E, int K,
                                                          int renorm, int32_t* __restrict__ ids,
                                                          float* __restrict__ w, uint32_t* flag) {
+  static_assert(LPT == 8 || LPT == 16, "groups of 8 or 16 lanes (DPP rows)");
+  constexpr int TPW = 64 / LPT;                // tokens per wavefront
+  constexpr int SLOTS = (32 + LPT - 1) / LPT;  // picks kept per lane (K <= 32): pick k in lane k % LPT
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + t * E;
-  float v[kRouteMaxPerLane];
+  const int sub = lane % LPT;                  // lane within the token's group
+  const int64_t t = ((int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)) * TPW + lane / LPT;
+  const bool live = t < T;
+  const float* row = logits + (live ? t : 0) * E;
+  float v[VPL];
   bool nan_seen = false;
 #pragma unroll
-  for (int j = 0; j < kRouteMaxPerLane; ++j) {
-    int e = lane + 64 * j;
-    float x = (e < E) ? row[e] : -INFINITY;
+  for (int j = 0; j < VPL; ++j) {
+    const int e = sub * VPL + j;
+    float x = (live && e < E) ? row[e] : -INFINITY;
     if (x != x) { nan_seen = true; x = -INFINITY; }
     v[j] = x;
   }
   if (__any(nan_seen) && lane == 0) raise_flag(flag, MOE_FLAG_NAN_LOGIT);
-  unsigned taken = 0;  // bit j: expert lane + 64j already picked
-  float my_logit = -INFINITY;  // lane k keeps the k-th pick
-  int my_id = 0;
+  unsigned taken = 0;   // bit j: expert sub * VPL + j already picked
+  float pv[SLOTS];
+  int pi[SLOTS];
+#pragma unroll
+  for (int q = 0; q < SLOTS; ++q) { pv[q] = -INFINITY; pi[q] = 0; }
+  float lmax = 0.f;
   for (int k = 0; k < K; ++k) {
-    // lane-local best among untaken (index order within a lane is ascending)
+    // this lane's best untaken logit (ascending index within the lane)
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPerLane; ++j) {
-      int e = lane + 64 * j;
+    for (int j = 0; j < VPL; ++j) {
+      const int e = sub * VPL + j;
       if (e < E && !((taken >> j) & 1u) && better(v[j], e, bv, bi)) { bv = v[j]; bi = e; }
     }
-    // wavefront argmax
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
+    // argmax over the token's group
+    auto level = [&](auto lc) {
+      constexpr int L = decltype(lc)::value;
+      const float ov = dpp_xchg<L>(bv);
+      const int oi = dpp_xchg<L>(bi);
       if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == k) { my_logit = bv; my_id = bi; }
-  }
-  const float lmax = __shfl(my_logit, 0, 64);  // the first pick is the row maximum
-  const float a = (lane < K) ? expf(my_logit - lmax) : 0.f;
-  float denom;
-  if (renorm) {
-    denom = wave_sum(a);
-  } else {
-    float s = 0.f;
+    };
+    level(std::integral_constant<int, 0>());
+    level(std::integral_constant<int, 1>());
+    level(std::integral_constant<int, 2>());
+    if constexpr (LPT == 16) level(std::integral_constant<int, 3>());
+    if (bi / VPL == sub) taken |= 1u << (bi - sub * VPL);
+    if (k == 0) lmax = bv;   // the first pick is the row maximum
 #pragma unroll
-    for (int j = 0; j < kRouteMaxPerLane; ++j) {
-      int e = lane + 64 * j;
-      if (e < E) s += expf(v[j] - lmax);
-    }
-    denom = wave_sum(s);
+    for (int q = 0; q < SLOTS; ++q)
+      if (k == q * LPT + sub) { pv[q] = bv; pi[q] = bi; }
   }
-  if (lane < K) {
-    ids[t * K + lane] = my_id;
-    w[t * K + lane] = a / denom;
+  float a[SLOTS];
+  float part = 0.f;
+#pragma unroll
+  for (int q = 0; q < SLOTS; ++q) {
+    a[q] = (q * LPT + sub < K) ? expf(pv[q] - lmax) : 0.f;
+    part += a[q];
+  }
+  if (!renorm) {
+    part = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+      if (sub * VPL + j < E) part += expf(v[j] - lmax);
+  }
+  part += dpp_xchg<0>(part);
+  part += dpp_xchg<1>(part);
+  part += dpp_xchg<2>(part);
+  if constexpr (LPT == 16) part += dpp_xchg<3>(part);
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+      const int k = q * LPT + sub;
+      if (k < K) {
+        ids[t * K + k] = pi[q];
+        w[t * K + k] = a[q] / part;
+      }
+    }
   }
 }
 
@@ -83,8 +134,24 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 extern "C" moe_status_t moe_route_topk_launch(const float* logits, int64_t T, int32_t E, int32_t K, int32_t renorm,
                                               int32_t* ids, float* w, uint32_t* flag, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const int tokens_per_block = 4;
-  dim3 grid((unsigned)((T + tokens_per_block - 1) / tokens_per_block));
-  hipLaunchKernelGGL(moe::route_topk_kernel, grid, dim3(256), 0, s, logits, T, E, K, renorm, ids, w, flag);
+  // lanes per token and logits per lane: at most 16 logits per lane
+  auto launch = [&](auto kern, int lpt) {
+    const int64_t tokens_per_block = 4 * (64 / lpt);
+    const dim3 grid((unsigned)((T + tokens_per_block - 1) / tokens_per_block));
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, logits, T, E, K, renorm, ids, w, flag);
+  };
+  if (E <= 8) {
+    launch(moe::route_topk_kernel<8, 1>, 8);
+  } else if (E <= 16) {
+    launch(moe::route_topk_kernel<8, 2>, 8);
+  } else if (E <= 32) {
+    launch(moe::route_topk_kernel<8, 4>, 8);
+  } else if (E <= 64) {
+    launch(moe::route_topk_kernel<16, 4>, 16);
+  } else if (E <= 128) {
+    launch(moe::route_topk_kernel<16, 8>, 16);
+  } else {
+    launch(moe::route_topk_kernel<16, 16>, 16);
+  }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
