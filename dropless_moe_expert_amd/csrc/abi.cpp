@@ -68,6 +68,10 @@ int device_cu_count() {
 namespace {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// T * K <= INT32_MAX (T >= 0, K >= 1), without forming a product that could overflow
+inline bool pairs_fit(int64_t T, int32_t K) { return T <= INT32_MAX / K; }
+// k_cap >= rows + 63 G, without forming a sum that could overflow (G <= 1024)
+inline bool kcap_fits(int64_t k_cap, int64_t rows, int32_t G) { return k_cap - 63 * (int64_t)G >= rows; }
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -96,7 +100,7 @@ moe_status_t moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K
 }
 
 size_t moe_permute_workspace_bytes(int64_t T, int32_t E, int32_t K) {
-  if (T < 0 || E < 1 || K < 1) return 0;
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || !pairs_fit(T, K)) return 0;
   return moe_permute_ws_bytes_impl(T, E, K);
 }
 
@@ -104,7 +108,7 @@ moe_status_t moe_permute(const uint16_t* x, const int32_t* topk_ids, int64_t T, 
                          int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src, int32_t* perm_dst,
                          uint16_t* x_perm, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream) {
   if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
-  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
   if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
@@ -123,7 +127,7 @@ moe_status_t moe_permute_noalloc(const uint16_t* x, const int32_t* topk_ids, int
                                  int32_t K, int32_t* group_sizes, int32_t* group_offsets, int32_t* perm_src,
                                  int32_t* perm_dst, uint16_t* x_perm, uint32_t* err_flag, void* stream) {
   if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
-  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
   if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
@@ -141,7 +145,7 @@ moe_status_t moe_permute_mxfp8(const uint16_t* x, const int32_t* topk_ids, int64
                                int32_t* perm_dst, uint8_t* x_q, uint8_t* x_scale, void* ws, size_t ws_bytes,
                                uint32_t* err_flag, void* stream) {
   if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
-  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
   if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !perm_src || !perm_dst || !x || !x_q || !x_scale)) return MOE_ERR_INVALID_ARG;
   if (d < 32 || d % 32) return MOE_ERR_UNSUPPORTED;
@@ -161,7 +165,7 @@ static size_t route_fused_ws_bytes(int64_t T, int32_t E, int32_t K) {
 }
 
 size_t moe_route_fused_workspace_bytes(int64_t T, int32_t E, int32_t K) {
-  if (T < 0 || E < 1 || E > 256 || K < 1) return 0;
+  if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || !pairs_fit(T, K)) return 0;
   return route_fused_ws_bytes(T, E, K);
 }
 
@@ -169,7 +173,7 @@ moe_status_t moe_route_fused(const uint16_t* x, const uint16_t* w_router, const 
                              int32_t E, int32_t K, int32_t renormalize, int32_t* topk_ids, float* topk_w,
                              float* logits, void* ws, size_t ws_bytes, uint32_t* err_flag, void* stream) {
   if (T < 0 || E < 1 || E > 256 || K < 1 || K > E || K > 32) return MOE_ERR_INVALID_ARG;
-  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
   if (d < 32 || d % 32 || (int64_t)d * 2 * 255 > (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (T > 0 && (!x || !w_router || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!aligned16(x) || !aligned16(w_router) || (logits && !aligned16(logits)))) return MOE_ERR_ALIGNMENT;
@@ -191,7 +195,7 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
                                 void* stream) {
   (void)err_flag;
   if (T < 0 || E < 1 || E > 256 || K < 1 || K > 32 || K > E) return MOE_ERR_INVALID_ARG;
-  if (T * (int64_t)K > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!pairs_fit(T, K)) return MOE_ERR_UNSUPPORTED;
   if (!group_sizes || !group_offsets) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !perm_src || !perm_dst)) return MOE_ERR_INVALID_ARG;
   if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARG;
@@ -277,7 +281,7 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
     if (d->dtype == MOE_DTYPE_MXFP8) {
       // operands laid out by mxfp8_quantize_transposed: K = its k_cap
       if (d->out_dtype != MOE_OUT_BF16) return MOE_ERR_UNSUPPORTED;
-      if (d->K < 64 || d->K % 64 || (int64_t)d->K < d->m_cap + 63 * (int64_t)d->G) return MOE_ERR_INVALID_ARG;
+      if (d->K < 64 || d->K % 64 || !kcap_fits(d->K, d->m_cap, d->G)) return MOE_ERR_INVALID_ARG;
       if (!A_scale || !B_scale) return MOE_ERR_INVALID_ARG;
       if ((reinterpret_cast<uintptr_t>(A_scale) & 3u) || (reinterpret_cast<uintptr_t>(B_scale) & 3u))
         return MOE_ERR_ALIGNMENT;
@@ -375,7 +379,7 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
   if (rows < 0 || cols < 8 || G < 1 || G > 1024) return MOE_ERR_INVALID_ARG;
   if (cols % 8) return MOE_ERR_UNSUPPORTED;
   if (group_sizes) {
-    if (k_cap < 0 || k_cap % 64 || k_cap < rows + 63 * (int64_t)G) return MOE_ERR_INVALID_ARG;
+    if (k_cap < 0 || k_cap % 64 || !kcap_fits(k_cap, rows, G)) return MOE_ERR_INVALID_ARG;
   } else if (rows % 64) {
     return MOE_ERR_UNSUPPORTED;
   }
@@ -397,7 +401,7 @@ moe_status_t moe_swiglu_backward_mxfp8(const uint16_t* gu, const uint16_t* dh, i
                                        uint8_t* scaleT, uint8_t* q_rows, uint8_t* scale_rows, uint32_t* err_flag,
                                        void* stream) {
   if (m_cap < 0 || f < 16 || f % 16 || !group_sizes || G < 1 || G > 1024) return MOE_ERR_INVALID_ARG;
-  if (k_cap < 0 || k_cap % 64 || k_cap < m_cap + 63 * (int64_t)G) return MOE_ERR_INVALID_ARG;
+  if (k_cap < 0 || k_cap % 64 || !kcap_fits(k_cap, m_cap, G)) return MOE_ERR_INVALID_ARG;
   if (m_cap > 0 && (!gu || !dh || !qT || !scaleT || !q_rows || !scale_rows)) return MOE_ERR_INVALID_ARG;
   if (m_cap > 0 && (!aligned16(gu) || !aligned16(dh) || !aligned16(qT) || !aligned16(q_rows) ||
                     (reinterpret_cast<uintptr_t>(scaleT) & 1u)))
