@@ -57,6 +57,18 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def source_hash() -> str:
     with open(GEMM_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -74,12 +86,44 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+class Timed(float):
+    """A warm median time in ms that also carries the cold one (or None)."""
+    cold = None
+
+
 class Timer:
     """Median HIP-event time of each named op, recorded on the stream the
     library launches on (torch's current stream)."""
 
+    SCRUB_BYTES = 1 << 30
+
     def __init__(self, torch, stream, reps: int):
         self.torch, self.stream, self.reps = torch, stream, reps
+        self.scrub = None
+
+    def cold(self, fn):
+        """Median time of fn right after a 1 GiB write has evicted the L2 and
+        MALL caches (the write runs before the timed interval, on the same
+        stream)."""
+        torch = self.torch
+        if self.scrub is None:
+            self.scrub = torch.empty(self.SCRUB_BYTES // 4, dtype=torch.int32, device=torch.cuda.current_device())
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.reps)]
+        for i, (a, b) in enumerate(ev):
+            self.scrub.fill_(i)
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    def bw(self, fn):
+        """Warm and cold median times of a bandwidth-bound op."""
+        t = Timed(self(fn))
+        t.cold = self.cold(fn)
+        return t
 
     def __call__(self, fn):
         torch = self.torch
@@ -93,6 +137,23 @@ class Timer:
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
+    def interleaved(self, *fns):
+        """Median times of several ops launched in turn (a, b, c, a, b, c, ...),
+        so that each sees the same clock and power state of the chip."""
+        torch = self.torch
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+              for _ in range(self.reps)]
+        for row in ev:
+            for (a, b), fn in zip(row, fns):
+                a.record(self.stream)
+                fn()
+                b.record(self.stream)
+        torch.cuda.synchronize()
+        return [float(np.median([row[i][0].elapsed_time(row[i][1]) for row in ev])) for i in range(len(fns))]
+
 
 def flop_entry(ms: float, flops: float, peak: float) -> dict:
     t = flops / (ms * 1e-3) / 1e12
@@ -101,8 +162,13 @@ def flop_entry(ms: float, flops: float, peak: float) -> dict:
 
 def byte_entry(ms: float, nbytes: float) -> dict:
     g = nbytes / (ms * 1e-3) / 1e9
-    return {"ms": round(ms, 4), "gbs": round(g, 1), "frac_of_hbm": round(g / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": int(nbytes)}
+    e = {"ms": round(ms, 4), "gbs": round(g, 1), "frac_of_hbm": round(g / HBM_PEAK_GBS, 4),
+         "algorithmic_bytes": int(nbytes)}
+    cold = getattr(ms, "cold", None)
+    if cold:   # after a 1 GiB write that evicted the L2 and MALL caches
+        gc = nbytes / (cold * 1e-3) / 1e9
+        e.update({"cold_ms": round(cold, 4), "cold_gbs": round(gc, 1), "cold_frac_of_hbm": round(gc / HBM_PEAK_GBS, 4)})
+    return e
 
 
 def bench_mxfp8_share(torch, ops, L, dev, timer, flag) -> dict:
@@ -123,23 +189,32 @@ def bench_mxfp8_share(torch, ops, L, dev, timer, flag) -> dict:
     h = ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU, flag=flag)
     hq, hs = ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU_MXFP8, flag=flag)
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
-    t_qx = timer(lambda: ops.mxfp8_quantize(x, 0, sizes, flag=flag))
-    t_g1q = timer(lambda: ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU_MXFP8,
-                                                 out=hq, out_scale=hs, flag=flag))
+    t_qx = timer.bw(lambda: ops.mxfp8_quantize(x, 0, sizes, flag=flag))
     t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, w2k, None, sizes, out=y, flag=flag))
-    t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h,
-                                                flag=flag))
-    t_qh = timer(lambda: ops.mxfp8_quantize(h, 0, sizes, flag=flag))
+    # the fused gate/up (quantising h in its epilogue) and the unfused pair
+    # (bf16 h, then the quantiser), launched in turn so that both run in the
+    # same clock and power state
+    t_g1q, t_g1, t_qh = timer.interleaved(
+        lambda: ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU_MXFP8, out=hq,
+                                       out_scale=hs, flag=flag),
+        lambda: ops.grouped_gemm_mxfp8(xq, xs, w1k, None, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h, flag=flag),
+        lambda: ops.mxfp8_quantize(h, 0, sizes, flag=flag))
+    t_qh = Timed(t_qh)
+    t_qh.cold = timer.cold(lambda: ops.mxfp8_quantize(h, 0, sizes, flag=flag))
     f1, f2 = 2.0 * M * 2 * f * d, 2.0 * M * d * f
-    step = t_qx + t_g1q + t_g2
+    fused_step, unfused_step = t_qx + t_g1q + t_g2, t_qx + t_g1 + t_qh + t_g2
+    step = min(fused_step, unfused_step)
     q = lambda R, C: R * C * 2 + R * C + R * C / 32   # read bf16, write codes and scales
     return {
         "workload": "deepseek-v3-shaped expert share in MXFP8 (same rows, sizes and weights; E4M3 + E8M0/32): "
-                    "quantise X, gate/up + SwiGLU + quantise H in one kernel, down",
+                    "quantise X, gate/up + SwiGLU + quantise H (in the GEMM's epilogue, or bf16 H and the "
+                    "quantiser: the faster path is the step), down",
         "ms_per_step": round(step, 4),
         "valid_row_tflops": round((f1 + f2) / (step * 1e-3) / 1e12, 2),
         "frac_of_mxfp8_peak": round((f1 + f2) / (step * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4),
-        "unfused_ms_per_step": round(t_qx + t_g1 + t_qh + t_g2, 4),
+        "step_path": "fused" if fused_step <= unfused_step else "unfused",
+        "fused_ms_per_step": round(fused_step, 4),
+        "unfused_ms_per_step": round(unfused_step, 4),
         "kernels": {
             "quantize_x": byte_entry(t_qx, q(M, d)),
             "gate_up_swiglu_quantize_mxfp8": flop_entry(t_g1q, f1, MXFP8_PEAK_TFLOPS),
@@ -164,10 +239,10 @@ def bench_mxfp4_share(torch, ops, L, dev, timer, flag) -> dict:
     h = ops.grouped_gemm_mxfp4(xq, xs, w1q, w1s, sizes, epilogue=ops.MOE_EPI_SWIGLU, flag=flag)
     hq, hs = ops.mxfp4_quantize(h)
     y = ops.grouped_gemm_mxfp4(hq, hs, w2q, w2s, sizes, flag=flag)
-    t_qx = timer(lambda: ops.mxfp4_quantize(x))
+    t_qx = timer.bw(lambda: ops.mxfp4_quantize(x))
     t_g1 = timer(lambda: ops.grouped_gemm_mxfp4(xq, xs, w1q, w1s, sizes, epilogue=ops.MOE_EPI_SWIGLU, out=h,
                                                 flag=flag))
-    t_qh = timer(lambda: ops.mxfp4_quantize(h))
+    t_qh = timer.bw(lambda: ops.mxfp4_quantize(h))
     t_g2 = timer(lambda: ops.grouped_gemm_mxfp4(hq, hs, w2q, w2s, sizes, out=y, flag=flag))
     f1, f2 = 2.0 * M * 2 * f * d, 2.0 * M * d * f
     step = t_qx + t_g1 + t_qh + t_g2
@@ -194,8 +269,8 @@ def routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep):
     ids, w = ops.route_topk(lg, K, flag=flag)
     p = ops.permute(x, ids, E, flag=flag)
     ws = None
-    t_route = timer(lambda: ops.route_topk(lg, K, flag=flag))
-    t_perm = timer(lambda: ops.permute(x, ids, E, flag=flag, workspace=ws))
+    t_route = timer.bw(lambda: ops.route_topk(lg, K, flag=flag))
+    t_perm = timer.bw(lambda: ops.permute(x, ids, E, flag=flag, workspace=ws))
     if keep:
         h, gu = ops.grouped_gemm(p["x_perm"], w1, p["group_sizes"], epilogue=ops.MOE_EPI_SWIGLU, keep_aux=True,
                                  flag=flag)
@@ -208,7 +283,7 @@ def routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep):
     y_perm = ops.grouped_gemm(h, w2, p["group_sizes"], flag=flag)
     t_g2 = timer(lambda: ops.grouped_gemm(h, w2, p["group_sizes"], out=y_perm, flag=flag))
     y = ops.unpermute_combine(y_perm, w, p["perm_dst"], T, K)
-    t_comb = timer(lambda: ops.unpermute_combine(y_perm, w, p["perm_dst"], T, K, out=y))
+    t_comb = timer.bw(lambda: ops.unpermute_combine(y_perm, w, p["perm_dst"], T, K, out=y))
     kern = {
         "route": byte_entry(t_route, T * E * 4 + T * K * 8),
         "permute": byte_entry(t_perm, T * d * 2 + T * K * 4 + M * d * 2 + M * 8),
@@ -325,7 +400,7 @@ def bench_mixtral_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     hq, hs = ops.grouped_gemm_mxfp8(p["xq"], p["xs"], w1k, None, p["group_sizes"],
                                     epilogue=ops.MOE_EPI_SWIGLU_MXFP8, flag=flag)
     y_perm = ops.grouped_gemm_mxfp8(hq, hs, w2k, None, p["group_sizes"], flag=flag)
-    t_perm = timer(lambda: ops.permute_mxfp8(x, ids, E, flag=flag))
+    t_perm = timer.bw(lambda: ops.permute_mxfp8(x, ids, E, flag=flag))
     t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(p["xq"], p["xs"], w1k, None, p["group_sizes"],
                                                 epilogue=ops.MOE_EPI_SWIGLU_MXFP8, out=hq, out_scale=hs, flag=flag))
     t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, w2k, None, p["group_sizes"], out=y_perm, flag=flag))
@@ -391,19 +466,19 @@ def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
     kern, fsum, s = routed_forward_kernels(ops, L, dev, timer, flag, lg, x, w1, w2, keep=True)
     sizes, dst = s["group_sizes"], s["perm_dst"]
     dyp, dw = ops.combine_backward(dy, s["y_perm"], s["w"], dst, K)
-    t_cb = timer(lambda: ops.combine_backward(dy, s["y_perm"], s["w"], dst, K))
+    t_cb = timer.bw(lambda: ops.combine_backward(dy, s["y_perm"], s["w"], dst, K))
     dh = ops.grouped_gemm(dyp, w2, sizes, b_layout=ops.MOE_B_KN, flag=flag)
     t_dh = timer(lambda: ops.grouped_gemm(dyp, w2, sizes, b_layout=ops.MOE_B_KN, out=dh, flag=flag))
     dw2 = ops.grouped_gemm_wgrad(dyp, s["h"], sizes, flag=flag)
     t_dw2 = timer(lambda: ops.grouped_gemm_wgrad(dyp, s["h"], sizes, out=dw2, flag=flag))
     dgu = ops.swiglu_backward(s["gu"], dh, sizes)
-    t_sb = timer(lambda: ops.swiglu_backward(s["gu"], dh, sizes, out=dgu))
+    t_sb = timer.bw(lambda: ops.swiglu_backward(s["gu"], dh, sizes, out=dgu))
     dxp = ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, out=dxp, flag=flag))
     dw1 = ops.grouped_gemm_wgrad(dgu, s["x_perm"], sizes, flag=flag)
     t_dw1 = timer(lambda: ops.grouped_gemm_wgrad(dgu, s["x_perm"], sizes, out=dw1, flag=flag))
     dx = ops.unpermute_combine(dxp, None, dst, T, K)
-    t_fold = timer(lambda: ops.unpermute_combine(dxp, None, dst, T, K, out=dx))
+    t_fold = timer.bw(lambda: ops.unpermute_combine(dxp, None, dst, T, K, out=dx))
     kern.update({
         "combine_backward": byte_entry(t_cb, T * d * 2 + M * d * 2 * 2 + M * 8 + M * 4),
         "dgrad_down": flop_entry(t_dh, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
@@ -463,8 +538,8 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     gq, gs = ops.mxfp8_quantize(dgu, 0, sizes, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm_mxfp8(gq, gs, wk["w1tk"], None, sizes, flag=flag))
     cT, csT = ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag)
-    t_qt = timer(lambda: ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True))
-    t_sbq = timer(lambda: ops.swiglu_backward_mxfp8(s["gu"], g["dh"], sizes, flag=flag))
+    t_qt = timer.bw(lambda: ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True))
+    t_sbq = timer.bw(lambda: ops.swiglu_backward_mxfp8(s["gu"], g["dh"], sizes, flag=flag))
     xT, xsT = ops.mxfp8_quantize_transposed(s["x_perm"], sizes, flag=flag)
     t_dw1 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(cT, csT, xT, xsT, sizes, M, flag=flag))
     del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs, dgu
@@ -698,6 +773,7 @@ def main() -> int:
         cpu_s = time.perf_counter() - a
         cpu_flops = 2.0 * len(rows) * (2 * f * d + d * f)
         cpu = {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": f"{len(rows)} of {M} expert-share rows (gate/up+SwiGLU and down GEMM, fp64 accumulation), "
                          f"{cpu_s:.1f}s"}
         # sampled parity of the same rows (the oracle's inputs are the generator's, never the GPU's)
