@@ -156,6 +156,74 @@ __device__ __forceinline__ uint32_t mx_codes4(float a, float b, float c, float d
   return mx_nan_byte(q, d, ed, 24);
 }
 
+// ------------------------------------------- MXFP8 codes of packed bf16 pairs
+// The same rule on bf16 data by gfx950's scaled conversion
+// (v_cvt_scalef32_pk_fp8_bf16: two bf16 times 2^-e, rounded to nearest even
+// into E4M3, sign of zero kept, subnormals kept).  Checked on the hardware
+// against cvt4_e4m3(scale_pow2(v, e)) for every finite bf16 v with
+// |v| < 2^(e+9) and every e in [-127, 127]: identical, except that the
+// conversion does not saturate (a value that rounds past 448 becomes NaN).
+// So each magnitude is first clamped to 448 * 2^e, which is exact: every
+// value in (448, 480) * 2^e rounds to 448 anyway.  Element 0 of a pair is its
+// low half; a code word holds elements 0..3 in bytes 0..3.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// the conversion's scale operand for 2^e: the E8M0 byte in the f32 exponent
+// field (byte 0, e = -127, reads as 2^-127)
+__device__ __forceinline__ float mx_scale_operand(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// bf16 bits of 448 * 2^e in both halves: above e = 119 no finite bf16
+// reaches 464 * 2^e, and the +inf bound leaves every finite value alone
+__device__ __forceinline__ uint32_t mx_clamp_pair(int e) {
+  const uint32_t l = e >= 120 ? 0x7F80u : ((uint32_t)(e + 8 + 127) << 7) | 0x60u;
+  return l | (l << 16);
+}
+
+__device__ __forceinline__ uint32_t min_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t min_i16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(i16x2_t, a),
+                                                                __builtin_bit_cast(i16x2_t, b)));
+}
+
+// |bf16| of both halves as unsigned 16-bit integers (the amax order)
+__device__ __forceinline__ uint32_t mag_pair(uint32_t p) { return p & 0x7FFF7FFFu; }
+// fp32 bits of the larger half of a magnitude pair (an amax for mx_exponent)
+__device__ __forceinline__ float amax_of_pair(uint32_t m) { return __uint_as_float(max(m & 0xFFFFu, m >> 16) << 16); }
+
+// both halves' magnitudes clamped to the bound l (lim2 = l in both halves,
+// l <= 0x7F80), signs kept: as unsigned 16-bit a negative half 0x8000 | m
+// is min'd with 0x8000 | l and a positive one is below that; as signed
+// 16-bit a positive half is min'd with l and a negative one is below it
+__device__ __forceinline__ uint32_t clamp_pair(uint32_t p, uint32_t lim2) {
+  return min_i16x2(min_u16x2(p, lim2 | 0x80008000u), lim2);
+}
+
+// codes of elements 0..3 (p01 = elements 0 and 1, p23 = 2 and 3) of a block
+// with finite exponent e: sc = mx_scale_operand(e), lim2 = mx_clamp_pair(e).
+// Each conversion writes one half of its destination and keeps the other
+// (here the clamped word's, overwritten by the second conversion).
+__device__ __forceinline__ uint32_t mx_codes4_pairs(uint32_t p01, uint32_t p23, float sc, uint32_t lim2) {
+  const uint32_t c01 = clamp_pair(p01, lim2), c23 = clamp_pair(p23, lim2);
+  i16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(__builtin_bit_cast(i16x2_t, c01),
+                                                        __builtin_bit_cast(bf16x2_t, c01), sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2_t, c23), sc, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// the NaN block's codes of the same four elements (0x7F with each sign)
+__device__ __forceinline__ uint32_t mx_nan_codes4_pairs(uint32_t p01, uint32_t p23) {
+  return 0x7F7F7F7Fu | ((p01 >> 8) & 0x80u) | ((p01 >> 16) & 0x8000u) | ((p23 << 8) & 0x800000u) |
+         (p23 & 0x80000000u);
+}
+
 // silu(g) = g * sigmoid(g); hardware exp and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 

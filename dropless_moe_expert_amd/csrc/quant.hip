@@ -135,13 +135,28 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(const uint16_t* __re
 // the row-wise (axis 0) codes and scales of its valid rows, by the threads
 // the column blocks leave idle: one read of x for both layouts.
 constexpr int QT_R = 64, QT_C = 64;
-constexpr int QT_LD = QT_C + 2;   // bf16 per LDS row: the pad staggers the column reads over the banks
+constexpr int QT_LD = QT_C + 2;   // bf16 per LDS row: the pad staggers the row reads over the banks
+// bytes per column of the code tile: 128 codes and 16 of padding, so that
+// 16-byte accesses by consecutive columns start 4 banks apart (at 128 bytes
+// every column would start on the same bank)
+constexpr int QT_CT = 2 * QT_R + 16;
 
 // PRODUCER 0: the tile is read from x [rows, cols].  PRODUCER 1: the tile
 // is the SwiGLU backward dgu [rows, cols = 2f] (bf16-rounded, as
 // moe_swiglu_backward stores it), made from x = gu [rows, 2f] and dh
 // [rows, f]: dgu never exists in bf16.
-template <int PRODUCER>
+// a value equal in every lane, moved to scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// element h (0 or 1, known only at run time) of a two-element array
+template <typename V>
+__device__ __forceinline__ V sel(int h, const V (&a)[2]) { return h ? a[1] : a[0]; }
+
+template <int PRODUCER, bool ROWS>
 __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ dh, int64_t rows, int cols,
                                                          const int32_t* __restrict__ group_sizes, int G,
@@ -149,8 +164,8 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ scaleT, uint8_t* __restrict__ q0,
                                                          uint8_t* __restrict__ s0, uint32_t* flag) {
   extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
-  __shared__ uint16_t xt[2 * QT_R * QT_LD];             // two position units, bf16, row-major
-  __shared__ __align__(16) uint8_t ct[QT_C * 2 * QT_R]; // their codes, column-major (128 per column)
+  __shared__ __align__(16) uint16_t xt[2 * QT_R * QT_LD];  // two position units, bf16, row-major
+  __shared__ __align__(16) uint8_t ct[QT_C * QT_CT];    // their codes, column-major (128 per column)
   __shared__ uint8_t st[QT_C * 4];                      // their scales, four per column
   int64_t* roff = sh;
   int64_t* kpad = sh + G + 1;
@@ -158,7 +173,11 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   if (grouped) {
     // row offsets and padded starts: each thread sums its run of groups,
     // a block scan of the sums, then each thread writes its run's prefixes
-    __shared__ int64_t scan_r[256], scan_k[256];
+    // (the scans live in the tile buffer, unused until the first tile: the
+    //  kernel's LDS then stays small enough for five workgroups per CU)
+    int64_t* scan_r = reinterpret_cast<int64_t*>(xt);
+    int64_t* scan_k = scan_r + 256;
+    static_assert(sizeof(xt) >= 2 * 256 * sizeof(int64_t), "the scans fit the tile buffer");
     const int per = (G + 255) / 256, t0 = threadIdx.x * per;
     int64_t lr = 0;
     bool neg = false;
@@ -217,148 +236,221 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   auto gcol = [&](int c0, int c) { return PRODUCER == 2 ? (c < 32 ? c0 + c : fh + c0 + (c - 32)) : c0 + c; };
   auto colvalid = [&](int c0, int c) { return PRODUCER == 2 ? c0 + (c & 31) < fh : c0 + c < cols; };
   const int t = threadIdx.x;
-  for (int64_t tile = blockIdx.x; tile < ntp * ntc; tile += gridDim.x) {
-    const int64_t tp = tile / ntc;
-    const int c0 = (int)(tile - tp * ntc) * (PRODUCER == 2 ? 32 : QT_C);
-    // each unit (64 positions) of the pair resolves its own rows and outputs
-    int64_t r0[2], ldq = grouped ? k_cap : rows;
+  // A tile's place: for each unit (64 positions) of the pair its first row,
+  // its valid rows and its first code and scale in column 0's qT / scaleT row
+  // (read through sel with constant indices: no array lives in scratch)
+  struct Tile {
+    int64_t r0[2];
     int n[2];
-    bool val[2];
-    uint8_t* qb[2];   // the unit's first code in column 0's qT row
-    uint8_t* sb[2];   // its first scale in column 0's scaleT row
+    int val[2];   // the unit exists (int, not bool: a bool pair was kept in scratch)
+    uint8_t* qb[2];
+    uint8_t* sb[2];
+    int c0;
+  };
+  auto describe = [&](int64_t tile, Tile& D) {
+#ifdef QT_COL_MAJOR
+    const int64_t ct = tile / ntp, tp = tile - ct * ntp;
+    D.c0 = (int)ct * (PRODUCER == 2 ? 32 : QT_C);
+#else
+    const int64_t tp = tile / ntc;
+    D.c0 = (int)(tile - tp * ntc) * (PRODUCER == 2 ? 32 : QT_C);
+#endif
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t tk = 2 * tp + h;
-      val[h] = tk < ntk;
-      r0[h] = 0;
-      n[h] = 0;
-      qb[h] = qT;
-      sb[h] = scaleT;
-      if (!val[h]) continue;
+      D.val[h] = tk < ntk;
+      D.r0[h] = 0;
+      D.n[h] = 0;
+      D.qb[h] = qT;
+      D.sb[h] = scaleT;
+      if (!D.val[h]) continue;
       if (grouped) {
         int lo = 0, hi = G - 1;   // last g with kpad[g] <= 64 tk
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
           if (kpad[mid] <= QT_R * tk) lo = mid; else hi = mid - 1;
         }
-        r0[h] = roff[lo] + (QT_R * tk - kpad[lo]);
-        n[h] = (int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - r0[h]));
-        qb[h] = qT + QT_R * tk;
-        sb[h] = scaleT + 2 * tk;
+        // the same in every lane (read from LDS): kept in scalar registers
+        D.r0[h] = uniform64(roff[lo] + (QT_R * tk - kpad[lo]));
+        D.n[h] = __builtin_amdgcn_readfirstlane((int)max((int64_t)0, min((int64_t)QT_R, roff[lo + 1] - D.r0[h])));
+        D.qb[h] = qT + QT_R * tk;
+        D.sb[h] = scaleT + 2 * tk;
       } else {
         const int64_t g = tk / tpb, b = tk - g * tpb;
-        r0[h] = g * rows + QT_R * b;
-        n[h] = QT_R;
-        qb[h] = qT + g * cols * rows + QT_R * b;
-        sb[h] = scaleT + g * cols * (rows / 32) + 2 * b;
+        D.r0[h] = g * rows + QT_R * b;
+        D.n[h] = QT_R;
+        D.qb[h] = qT + g * cols * rows + QT_R * b;
+        D.sb[h] = scaleT + g * cols * (rows / 32) + 2 * b;
       }
     }
-    // 1. the pair's rows: 128 rows x 8 pieces of 8 columns, four per thread
-    __syncthreads();   // the previous tile's LDS is read out
-    if constexpr (PRODUCER == 2) {
-      // 128 rows x 4 pieces of 8 gate/up pairs, two per thread: dg to columns
-      // 8 jp .., du to 32 + 8 jp ..
+  };
+  const int64_t ldq = grouped ? k_cap : rows;
+  // The pair's rows come in as 16-byte pieces of 8 columns held in registers
+  // until the LDS is free: PRODUCER 0 four pieces of x per thread (128 rows x
+  // 8 pieces); PRODUCER 1 the g, u and dh pieces behind four dgu pieces;
+  // PRODUCER 2 those behind two (gate, up) piece pairs (128 rows x 4 pairs).
+  // The next tile's loads are issued as soon as this tile's rows are in LDS,
+  // so they are in flight while this tile is quantised and written out.
+  constexpr int NP = PRODUCER == 2 ? 2 : 4;   // pieces (pairs) per thread
+  constexpr int NL = PRODUCER == 0 ? 1 : 3;   // loads per piece
+  uint4 raw[NP][NL];
+  auto load = [&](const Tile& D) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int u = t + 256 * k, rr = u >> 2, jp = u & 3, j = c0 + 8 * jp;
-        const int h = rr >> 6, r = rr & 63;
-        uint4 vg = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-        if (r < n[h] && j < fh) {
-          const int64_t row = r0[h] + r;
-          float g[8], uu[8], dd[8], dg[8], du[8];
-          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + j), g);
-          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + fh + j), uu);
-          unpack8(*reinterpret_cast<const uint4*>(dh + row * fh + j), dd);
+    for (int k = 0; k < NP; ++k) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dd[e], dg[e], du[e]);
-          vg = pack8(dg);
-          vu = pack8(du);
+      for (int l = 0; l < NL; ++l) raw[k][l] = make_uint4(0, 0, 0, 0);
+      const int u = t + 256 * k;
+      if constexpr (PRODUCER == 2) {
+        const int rr = u >> 2, j = D.c0 + 8 * (u & 3), h = rr >> 6, r = rr & 63;
+        if (r < sel(h, D.n) && j < fh) {
+          const int64_t row = sel(h, D.r0) + r;
+          raw[k][0] = *reinterpret_cast<const uint4*>(x + row * cols + j);
+          raw[k][1] = *reinterpret_cast<const uint4*>(x + row * cols + fh + j);
+          raw[k][2] = *reinterpret_cast<const uint4*>(dh + row * fh + j);
         }
+      } else {
+        const int rr = u >> 3, c = (u & 7) * 8, h = rr >> 6, r = rr & 63;
+        if (r < sel(h, D.n) && D.c0 + c < cols) {
+          const int64_t row = sel(h, D.r0) + r;
+          if constexpr (PRODUCER == 0) {
+            raw[k][0] = *reinterpret_cast<const uint4*>(x + row * cols + D.c0 + c);
+          } else {
+            const int j = (D.c0 + c) % fh;   // f % 8 == 0: a piece is all gate or all up
+            raw[k][0] = *reinterpret_cast<const uint4*>(x + row * cols + j);
+            raw[k][1] = *reinterpret_cast<const uint4*>(x + row * cols + fh + j);
+            raw[k][2] = *reinterpret_cast<const uint4*>(dh + row * fh + j);
+          }
+        }
+      }
+    }
+  };
+  // the registers to LDS; the SwiGLU producers form dgu here (zero pieces,
+  // those of padding rows and absent columns, give zero)
+  auto stage = [&](const Tile& D) {
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int u = t + 256 * k;
+      if constexpr (PRODUCER == 2) {
+        const int rr = u >> 2, jp = u & 3;
+        float g[8], uu[8], dd[8], dg[8], du[8];
+        unpack8(raw[k][0], g);
+        unpack8(raw[k][1], uu);
+        unpack8(raw[k][2], dd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dd[e], dg[e], du[e]);
+        const uint4 vg = pack8(dg), vu = pack8(du);
         uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + 8 * jp);
         d[0] = vg.x; d[1] = vg.y; d[2] = vg.z; d[3] = vg.w;
         d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + 32 + 8 * jp);
         d[0] = vu.x; d[1] = vu.y; d[2] = vu.z; d[3] = vu.w;
-      }
-    } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = t + 256 * k, rr = u >> 3, c = (u & 7) * 8;
-      const int h = rr >> 6, r = rr & 63;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (r < n[h] && c0 + c < cols) {
-        const int64_t row = r0[h] + r;
-        if constexpr (PRODUCER == 0) {
-          v = *reinterpret_cast<const uint4*>(x + row * cols + c0 + c);
-        } else {
-          const int f = cols / 2, j = (c0 + c) % f;   // f % 8 == 0: a piece is all gate or all up
+      } else {
+        const int rr = u >> 3, c = (u & 7) * 8;
+        uint4 v = raw[k][0];
+        if constexpr (PRODUCER == 1) {
           float g[8], uu[8], dd[8], dg[8], du[8];
-          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + j), g);
-          unpack8(*reinterpret_cast<const uint4*>(x + row * cols + f + j), uu);
-          unpack8(*reinterpret_cast<const uint4*>(dh + row * f + j), dd);
+          unpack8(raw[k][0], g);
+          unpack8(raw[k][1], uu);
+          unpack8(raw[k][2], dd);
 #pragma unroll
           for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dd[e], dg[e], du[e]);
-          v = pack8(c0 + c < f ? dg : du);
+          v = pack8(D.c0 + c < fh ? dg : du);
         }
+        uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + c);   // 4-byte aligned (QT_LD even)
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
       }
-      uint32_t* d = reinterpret_cast<uint32_t*>(xt + rr * QT_LD + c);   // 4-byte aligned (QT_LD even)
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     }
+  };
+  const int64_t ntiles = ntp * ntc;
+  // Round k of the grid takes tiles k * grid .. (k + 1) * grid - 1.  The
+  // hardware deals workgroups to the 8 XCDs in turn (block b to XCD b % 8),
+  // so when the grid is a multiple of 8 each XCD gets a run of consecutive
+  // tiles: the tiles that share output lines then share that XCD's L2.
+  const int64_t per_xcd = gridDim.x % 8 == 0 ? gridDim.x / 8 : 0;
+  const int64_t slot = per_xcd ? (blockIdx.x % 8) * per_xcd + blockIdx.x / 8 : blockIdx.x;
+  auto tile_of = [&](int64_t k) { return k * gridDim.x + slot; };
+  if (tile_of(0) >= ntiles) return;
+  // 1. the first tile's rows into LDS; each later tile's are staged at the
+  //    end of the previous pass, after that pass's stores (the loop is so
+  //    rotated that the wait for those rows counts the stores in between)
+  Tile cur;
+  describe(tile_of(0), cur);
+  load(cur);
+  stage(cur);
+  for (int64_t k = 0;; ++k) {
+    const int c0 = cur.c0;
+    const bool more = tile_of(k + 1) < ntiles;
+    Tile nxt = cur;
+    if (more) {   // the next tile's loads are in flight while this one is quantised and stored
+      describe(tile_of(k + 1), nxt);
+      load(nxt);
     }
     __syncthreads();
-    // 2a. one thread per (column, 32-position block): amax, scale, 32 codes into the column
+    // 2a. one thread per (column, 32-position block): amax, scale, 32 codes
+    //     into the column, on the column's values paired down the rows
     {
       const int c = t & (QT_C - 1), b = t >> 6;   // b = 0..3 over the pair's 128 positions
-      float amax = 0.f;
-#pragma unroll 8
-      for (int i = 0; i < 32; ++i) amax = mx_absmax(amax, __uint_as_float((uint32_t)xt[(32 * b + i) * QT_LD + c] << 16));
-      const int e = mx_exponent(amax);
+      uint32_t pr[16];   // rows 32 b + 2 i (low half) and 32 b + 2 i + 1 (high half)
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pr[i] = (uint32_t)xt[(32 * b + 2 * i) * QT_LD + c] | ((uint32_t)xt[(32 * b + 2 * i + 1) * QT_LD + c] << 16);
+        asm volatile("" : "+v"(pr[i]));   // one register per pair, not its two halves kept apart
+        m = max_u16x2(m, mag_pair(pr[i]));
+      }
+      const int e = mx_exponent(amax_of_pair(m));
       st[4 * c + b] = (uint8_t)(e + 127);
       uint32_t w[8];
+      if (e != kMxNaN) {
+        const float sc = mx_scale_operand(e);
+        const uint32_t lim2 = mx_clamp_pair(e);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float f[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f[i] = __uint_as_float((uint32_t)xt[(32 * b + 4 * q + i) * QT_LD + c] << 16);
-        w[q] = mx_codes4(f[0], f[1], f[2], f[3], e);
-      }
-      if (e == kMxNaN) {
+        for (int q = 0; q < 8; ++q) w[q] = mx_codes4_pairs(pr[2 * q], pr[2 * q + 1], sc, lim2);
+      } else {
         // a NaN block's codes are NaN only at the group's rows: the padding
         // positions past them keep zero codes, as in every other block
-        const int nv = min(32, max(0, n[b >> 1] - 32 * (b & 1)));
+        const int nv = min(32, max(0, sel(b >> 1, cur.n) - 32 * (b & 1)));
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 8; ++q) {
+          w[q] = mx_nan_codes4_pairs(pr[2 * q], pr[2 * q + 1]);
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             if (4 * q + k >= nv) w[q] &= ~(0xFFu << (8 * k));
+        }
       }
-      uint4* d = reinterpret_cast<uint4*>(ct + c * (2 * QT_R) + 32 * b);
+      uint4* d = reinterpret_cast<uint4*>(ct + c * QT_CT + 32 * b);
       d[0] = make_uint4(w[0], w[1], w[2], w[3]);
       d[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
-    // 2b. one thread per (row, 32-column block): the axis-0 quantisation of the valid rows
-    if (q0) {
-      const int rr = t >> 1, b = t & 1, cb = gcol(c0, 32 * b);
-      const int h = rr >> 6, r = rr & 63;
-      if (r < n[h] && colvalid(c0, 32 * b)) {
-        // two passes over the row's 32 values in LDS (pairs per 4-byte read):
-        // amax, then the codes; few live registers keep the occupancy up
+    // 2b. one thread per (row, 32-column block): the axis-0 quantisation of the
+    //     valid rows.  A thread without a valid row or block takes the tile's
+    //     first row and block (always valid) and stores the same bytes to the
+    //     same place as thread 0: every thread issues the same stores, so the
+    //     wait for the next tile's loads need not wait for these stores too.
+    if constexpr (ROWS) {
+      int rr = t >> 1, b = t & 1;
+      if (!((rr & 63) < sel(rr >> 6, cur.n) && colvalid(c0, 32 * b))) rr = b = 0;
+      const int cb = gcol(c0, 32 * b), h = rr >> 6, r = rr & 63;
+      {
         const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + rr * QT_LD + 32 * b);   // QT_LD even
-        float amax = 0.f;
+        uint32_t pr[16];   // columns 2 i and 2 i + 1
+        uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const uint32_t p = xr[i];
-          amax = mx_absmax(mx_absmax(amax, __uint_as_float(p << 16)), __uint_as_float(p & 0xFFFF0000u));
+          pr[i] = xr[i];
+          m = max_u16x2(m, mag_pair(pr[i]));
         }
-        const int e = mx_exponent(amax);
-        asm volatile("" ::: "memory");   // re-read the row below instead of keeping 16 words live
+        const int e = mx_exponent(amax_of_pair(m));
         uint32_t w[8];
+        if (e != kMxNaN) {
+          const float sc = mx_scale_operand(e);
+          const uint32_t lim2 = mx_clamp_pair(e);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t p0 = xr[2 * q], p1 = xr[2 * q + 1];
-          w[q] = mx_codes4(__uint_as_float(p0 << 16), __uint_as_float(p0 & 0xFFFF0000u), __uint_as_float(p1 << 16),
-                           __uint_as_float(p1 & 0xFFFF0000u), e);
+          for (int q = 0; q < 8; ++q) w[q] = mx_codes4_pairs(pr[2 * q], pr[2 * q + 1], sc, lim2);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) w[q] = mx_nan_codes4_pairs(pr[2 * q], pr[2 * q + 1]);
         }
-        const int64_t row = r0[h] + r;
+        const int64_t row = sel(h, cur.r0) + r;
         uint4* d = reinterpret_cast<uint4*>(q0 + row * cols + cb);
         d[0] = make_uint4(w[0], w[1], w[2], w[3]);
         d[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -370,17 +462,24 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
     //    so one store instruction writes 8 columns x 128 contiguous bytes when the
     //    two units are adjacent in the column row; the scale pairs
 #pragma unroll
+    //    (a lane of an absent column or unit repeats the store of column 0,
+    //    unit 0, and each of a column's four lanes stores the scale pair:
+    //    every lane stores, with the same bytes wherever two lanes meet)
     for (int k = 0; k < 2; ++k) {
-      const int idx = t + 256 * k, c = idx >> 3, p8 = idx & 7, h = p8 >> 2;
-      if (val[h] && colvalid(c0, c)) {
-        const int64_t col = gcol(c0, c);
-        *reinterpret_cast<uint4*>(qb[h] + col * ldq + 16 * (p8 & 3)) =
-            *reinterpret_cast<const uint4*>(ct + c * (2 * QT_R) + 16 * p8);
-        if ((p8 & 3) == 0)
-          *reinterpret_cast<uint16_t*>(sb[h] + col * (ldq / 32)) =
-              (uint16_t)(st[4 * c + 2 * h] | ((uint16_t)st[4 * c + 2 * h + 1] << 8));
-      }
+      const int idx = t + 256 * k;
+      int c = idx >> 3, p8 = idx & 7;
+      if (!(sel(p8 >> 2, cur.val) && colvalid(c0, c))) c = 0, p8 &= 3;
+      const int h = p8 >> 2;
+      const int64_t col = gcol(c0, c);
+      *reinterpret_cast<uint4*>(sel(h, cur.qb) + col * ldq + 16 * (p8 & 3)) =
+          *reinterpret_cast<const uint4*>(ct + c * QT_CT + 16 * p8);
+      *reinterpret_cast<uint16_t*>(sel(h, cur.sb) + col * (ldq / 32)) =
+          (uint16_t)(st[4 * c + 2 * h] | ((uint16_t)st[4 * c + 2 * h + 1] << 8));
     }
+    if (!more) break;
+    __syncthreads();   // this tile's LDS is read out
+    stage(nxt);
+    cur = nxt;
   }
 }
 
@@ -445,21 +544,31 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
                                                          const int32_t* group_sizes, int32_t G, int64_t k_cap,
                                                          uint8_t* qT, uint8_t* scaleT, uint8_t* q0, uint8_t* s0,
                                                          uint32_t* flag, hipStream_t s) {
-  const int64_t cap = (int64_t)moe_host::device_cu_count() * 8;
   const int64_t ntk = group_sizes ? k_cap / 64 : (int64_t)G * (rows / 64);   // an upper bound when grouped
   const int64_t work = (ntk + 1) / 2 * ((cols + 63) / 64);   // pairs of 64-position units
   if (work == 0) return MOE_OK;
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(work, cap));
   const size_t shmem = group_sizes ? sizeof(int64_t) * (size_t)(2 * G + 2) : 0;
-  if (dh && (cols / 2) % 32 == 0) {
-    hipLaunchKernelGGL(moe::mx_quant_t_kernel<2>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
-                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
-  } else if (dh) {
-    hipLaunchKernelGGL(moe::mx_quant_t_kernel<1>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
-                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
+  // one resident wave of workgroups, each looping over its tiles (a second
+  // wave would start only as the first drains, and run on a part of the chip)
+  auto launch = [&](auto kern) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, shmem) != hipSuccess) {
+      (void)hipGetLastError();   // the query's failure is not the launch's
+      per_cu = 1;
+    }
+    per_cu = std::max(per_cu, 1);
+    const int64_t blocks = std::min<int64_t>(work, (int64_t)moe_host::device_cu_count() * per_cu);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols, group_sizes, G, k_cap,
+                       qT, scaleT, q0, s0, flag);
+  };
+  if (q0) {
+    if (dh && (cols / 2) % 32 == 0) launch(moe::mx_quant_t_kernel<2, true>);
+    else if (dh) launch(moe::mx_quant_t_kernel<1, true>);
+    else launch(moe::mx_quant_t_kernel<0, true>);
   } else {
-    hipLaunchKernelGGL(moe::mx_quant_t_kernel<0>, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols,
-                       group_sizes, G, k_cap, qT, scaleT, q0, s0, flag);
+    if (dh && (cols / 2) % 32 == 0) launch(moe::mx_quant_t_kernel<2, false>);
+    else if (dh) launch(moe::mx_quant_t_kernel<1, false>);
+    else launch(moe::mx_quant_t_kernel<0, false>);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
