@@ -514,7 +514,9 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     forward as the dsv3 MXFP8 path, the data gradients on the weights
     quantised along their output axis, the weight gradients on operands
     quantised down the tokens with blocks restarting at every expert (the
-    pages' group-aware MXFP8).  The four weight quantisations happen once per
+    pages' group-aware MXFP8).  x and dy are quantised both ways as they are
+    gathered from the tokens (no bf16 x_perm or dy_perm), dgu as the SwiGLU
+    backward forms it.  The four weight quantisations happen once per
     optimiser step and are timed on their own (weight_quantize_ms)."""
     T, d, E, K, f = L.T, L.d, L.E, L.K, L.f
     M = T * K
@@ -522,25 +524,33 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     wk = ops.quantize_weights_mxfp8_train(w1, w2, flag=flag)
     t_wq = timer(lambda: ops.quantize_weights_mxfp8_train(w1, w2, flag=flag))
     y, s = ops.moe_forward_mxfp8_train(lg, x, wk, K, flag=flag)
-    sizes = s["group_sizes"]
-    xq, xs = ops.mxfp8_quantize(s["x_perm"], 0, sizes, flag=flag)
+    sizes, src = s["group_sizes"], s["perm_src"]
+    # x and dy reach the GEMMs only as MXFP8: their row codes as the dispatch
+    # and the combine's backward form them, their transposed codes as they
+    # are gathered from the tokens
+    t_pmx = timer.bw(lambda: ops.permute_mxfp8(x, s["ids"], E, flag=flag))
+    pm = ops.permute_mxfp8(x, s["ids"], E, flag=flag)
+    xq, xs = pm["xq"], pm["xs"]
+    xT, xsT = ops.mxfp8_quantize_gathered(x, src, K, sizes, flag=flag)
+    t_qx = timer.bw(lambda: ops.mxfp8_quantize_gathered(x, src, K, sizes, flag=flag))
     t_g1 = timer(lambda: ops.grouped_gemm_mxfp8(xq, xs, wk["w1k"], None, sizes, epilogue=ops.MOE_EPI_SWIGLU,
                                                 keep_aux=True, flag=flag))
     hq, hs = ops.mxfp8_quantize(s["h"], 0, sizes, flag=flag)
     t_g2 = timer(lambda: ops.grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag))
     g = ops.moe_backward_mxfp8(dy, s, wk, K, flag=flag)
+    t_cbw = timer.bw(lambda: ops.combine_backward_mxfp8(dy, s["y_perm"], s["w"], s["perm_dst"], K))
+    dyq, dys, _ = ops.combine_backward_mxfp8(dy, s["y_perm"], s["w"], s["perm_dst"], K)
     dgu = ops.swiglu_backward(s["gu"], g["dh"], sizes)
-    dyq, dys = ops.mxfp8_quantize(g["dy_perm"], 0, sizes, flag=flag)
+    aT, asT = ops.mxfp8_quantize_gathered(dy, src, K, sizes, topk_w=s["w"], flag=flag)
+    t_qdy = timer.bw(lambda: ops.mxfp8_quantize_gathered(dy, src, K, sizes, topk_w=s["w"], flag=flag))
     t_dh = timer(lambda: ops.grouped_gemm_mxfp8(dyq, dys, wk["w2tk"], None, sizes, flag=flag))
-    aT, asT = ops.mxfp8_quantize_transposed(g["dy_perm"], sizes, flag=flag)
-    bT, bsT = ops.mxfp8_quantize_transposed(s["h"], sizes, flag=flag)
+    bT, bsT = s["hT"], s["hsT"]
     t_dw2 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(aT, asT, bT, bsT, sizes, M, flag=flag))
     gq, gs = ops.mxfp8_quantize(dgu, 0, sizes, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm_mxfp8(gq, gs, wk["w1tk"], None, sizes, flag=flag))
     cT, csT = ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag)
     t_qt = timer.bw(lambda: ops.mxfp8_quantize_transposed(dgu, sizes, flag=flag, rows_too=True))
     t_sbq = timer.bw(lambda: ops.swiglu_backward_mxfp8(s["gu"], g["dh"], sizes, flag=flag))
-    xT, xsT = ops.mxfp8_quantize_transposed(s["x_perm"], sizes, flag=flag)
     t_dw1 = timer(lambda: ops.grouped_gemm_wgrad_mxfp8(cT, csT, xT, xsT, sizes, M, flag=flag))
     del aT, asT, bT, bsT, cT, csT, xT, xsT, xq, xs, hq, hs, dyq, dys, gq, gs, dgu
     for _ in range(2):
@@ -555,7 +565,9 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
     ms = (time.perf_counter() - a) * 1e3 / steps
     fl = 3 * 2.0 * M * (2 * f * d + d * f)
     return {"workload": "fine-grained forward+backward T=16384 d=2048 E=128 top-8 ffn=768, every GEMM in MXFP8 "
-                        "(weight gradients group-aware along the tokens), logit bias N(0,1.5) per expert",
+                        "(weight gradients group-aware along the tokens; x, dy and dgu quantised as they are "
+                        "dispatched, gathered or formed: no bf16 x_perm, dy_perm or dgu), logit bias N(0,1.5) "
+                        "per expert",
             "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "valid_row_tflops": round(fl / (ms * 1e-3) / 1e12, 2),
             "weight_quantize_ms": round(t_wq, 4),
@@ -568,7 +580,15 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
                 "wgrad_down_mxfp8": flop_entry(t_dw2, 2.0 * M * d * f, MXFP8_PEAK_TFLOPS),
                 "dgrad_gate_up_mxfp8": flop_entry(t_dx, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
                 "wgrad_gate_up_mxfp8": flop_entry(t_dw1, 2.0 * M * 2 * f * d, MXFP8_PEAK_TFLOPS),
-                "quantize_both_layouts (dgu)": byte_entry(t_qt, M * 2 * f * 2 + 2 * (M * 2 * f + M * 2 * f / 32)),
+                "permute_mxfp8 (x row codes)": byte_entry(t_pmx, T * d * 2 + M * 4 * 3 + M * d + M * d / 32),
+                "quantize_x_transposed (gathered from the tokens)": byte_entry(t_qx, T * d * 2 + M * 4 + M * d
+                                                                               + M * d / 32),
+                "combine_backward_mxfp8 (dy row codes, routing-weight gradient)": byte_entry(
+                    t_cbw, T * d * 2 + M * d * 2 + M * 8 + M * 4 + M * d + M * d / 32),
+                "quantize_dy_transposed (gathered, weighted)": byte_entry(t_qdy, T * d * 2 + M * 8 + M * d
+                                                                          + M * d / 32),
+                "quantize_both_layouts (dgu, unfused path)": byte_entry(t_qt, M * 2 * f * 2 + 2 * (
+                    M * 2 * f + M * 2 * f / 32)),
                 "swiglu_backward_quantize_both_layouts": byte_entry(t_sbq, M * 2 * f * 2 + M * f * 2
                                                                     + 2 * (M * 2 * f + M * 2 * f / 32)),
             }}

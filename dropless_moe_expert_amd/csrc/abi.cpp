@@ -27,12 +27,15 @@ moe_status_t moe_permute_mxfp8_launch(const uint16_t*, const int32_t*, int64_t, 
 moe_status_t moe_unpermute_combine_launch(const uint16_t*, const float*, const int32_t*, int64_t, int32_t, int32_t,
                                           uint16_t*, hipStream_t);
 moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const float*, const int32_t*, int64_t,
-                                         int32_t, int32_t, uint16_t*, float*, hipStream_t);
+                                         int32_t, int32_t, uint16_t*, float*, uint8_t*, uint8_t*, hipStream_t);
 moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*, int32_t,
                                         uint16_t*, hipStream_t);
 moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*,
                                               int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*,
                                               hipStream_t);
+moe_status_t mxfp8_gather_quantize_launch(const uint16_t*, const int32_t*, const float*, int32_t, int64_t, int32_t,
+                                          const int32_t*, int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
+                                          uint32_t*, hipStream_t);
 moe_status_t mxfp4_quantize_launch(const uint16_t*, int64_t, int32_t, uint8_t*, uint8_t*, hipStream_t);
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
                                          uint8_t*, uint8_t*, uint32_t*, hipStream_t);
@@ -338,9 +341,23 @@ moe_status_t moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, co
                                   const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint16_t* dy_perm,
                                   float* d_topk_w, void* stream) {
   if (T < 0 || K < 1 || K > 32 || d < 8 || d % 8) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!dy || !y_perm || !topk_w || !perm_dst || !dy_perm || !d_topk_w)) return MOE_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned16(dy) || !aligned16(y_perm) || !aligned16(dy_perm))) return MOE_ERR_ALIGNMENT;
-  return moe_combine_backward_launch(dy, y_perm, topk_w, perm_dst, T, d, K, dy_perm, d_topk_w, S(stream));
+  if (T > 0 && (!dy || !y_perm || !topk_w || !perm_dst || !d_topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(dy) || !aligned16(y_perm) || (dy_perm && !aligned16(dy_perm)))) return MOE_ERR_ALIGNMENT;
+  return moe_combine_backward_launch(dy, y_perm, topk_w, perm_dst, T, d, K, dy_perm, d_topk_w, nullptr, nullptr,
+                                     S(stream));
+}
+
+moe_status_t moe_combine_backward_mxfp8(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
+                                        const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint8_t* q_rows,
+                                        uint8_t* scale_rows, float* d_topk_w, void* stream) {
+  if (T < 0 || K < 1 || K > 32 || d < 32) return MOE_ERR_INVALID_ARG;
+  if (d % 32) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (!dy || !y_perm || !topk_w || !perm_dst || !q_rows || !scale_rows || !d_topk_w))
+    return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(dy) || !aligned16(y_perm) || (reinterpret_cast<uintptr_t>(q_rows) & 7u)))
+    return MOE_ERR_ALIGNMENT;
+  return moe_combine_backward_launch(dy, y_perm, topk_w, perm_dst, T, d, K, nullptr, d_topk_w, q_rows, scale_rows,
+                                     S(stream));
 }
 
 moe_status_t moe_swiglu_backward(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,
@@ -394,6 +411,28 @@ moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t 
   if (rows == 0) return MOE_OK;
   return mxfp8_quantize_transposed_launch(x, nullptr, rows, cols, group_sizes, G, k_cap, qT, scaleT, q_rows,
                                           scale_rows, err_flag, S(stream));
+}
+
+moe_status_t mxfp8_quantize_gathered(const uint16_t* x, const int32_t* perm_src, const float* topk_w, int64_t T,
+                                     int32_t K, int32_t cols, const int32_t* group_sizes, int32_t G, int64_t k_cap,
+                                     uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows, uint8_t* scale_rows,
+                                     uint32_t* err_flag, void* stream) {
+  if (T < 0 || K < 1 || K > 32 || !pairs_fit(T, K) || cols < 8 || !group_sizes || G < 1 || G > 1024)
+    return MOE_ERR_INVALID_ARG;
+  if (cols % 8) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = T * K;
+  if (k_cap < 0 || k_cap % 64 || !kcap_fits(k_cap, rows, G)) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x || !perm_src || !qT || !scaleT)) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!aligned16(x) || !aligned16(qT) || (reinterpret_cast<uintptr_t>(scaleT) & 1u)))
+    return MOE_ERR_ALIGNMENT;
+  if (!q_rows != !scale_rows) return MOE_ERR_INVALID_ARG;
+  if (q_rows) {
+    if (cols % 32) return MOE_ERR_UNSUPPORTED;
+    if (rows > 0 && !aligned16(q_rows)) return MOE_ERR_ALIGNMENT;
+  }
+  if (rows == 0) return MOE_OK;
+  return mxfp8_gather_quantize_launch(x, perm_src, topk_w, K, rows, cols, group_sizes, G, k_cap, qT, scaleT, q_rows,
+                                      scale_rows, err_flag, S(stream));
 }
 
 moe_status_t moe_swiglu_backward_mxfp8(const uint16_t* gu, const uint16_t* dh, int64_t m_cap, int32_t f,

@@ -81,13 +81,18 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(const uint16_t* 
 }
 
 // dy_perm[perm_dst[t,k]] = bf16(w[t,k] * dy[t]);  dw[t,k] = <dy[t], y_perm[perm_dst[t,k]]>
-template <int KT>
+// MX: dy_perm leaves as MXFP8 along its rows instead (xq codes, xs scales):
+// each 32-element block, four neighbouring lanes' vectors, gets its amax
+// across those lanes by DPP and the codes of the transposed quantiser's
+// row part, the same rule bit for bit.
+template <int KT, bool MX>
 __global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* __restrict__ dy,
                                                                const uint16_t* __restrict__ y_perm,
                                                                const float* __restrict__ w,
                                                                const int32_t* __restrict__ perm_dst, int64_t T,
                                                                int d, int K, uint16_t* __restrict__ dy_perm,
-                                                               float* __restrict__ dw) {
+                                                               float* __restrict__ dw, uint8_t* __restrict__ xq,
+                                                               uint8_t* __restrict__ xs) {
   constexpr int KM = KT > 0 ? KT : 32;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* _
     for (int k = 0; k < KM; ++k) {
       if (k < K) {
         const int32_t r = rows[k];
-        float yv[8], o[8];
+        float yv[8];
         if constexpr (KT > 0) {
           unpack8(in[k], yv);
         } else {
@@ -130,12 +135,27 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(const uint16_t* _
         }
         float sacc = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          sacc = fmaf(g[j], yv[j], sacc);
-          o[j] = ws[k] * g[j];
-        }
+        for (int j = 0; j < 8; ++j) sacc = fmaf(g[j], yv[j], sacc);
         dot[k] += sacc;
-        reinterpret_cast<uint4*>(dy_perm + (int64_t)r * d)[v] = pack8(o);
+        if constexpr (MX) {
+          const uint4 o = mul8_bf16(ws[k], g);
+          uint32_t m = max_u16x2(max_u16x2(mag_pair(o.x), mag_pair(o.y)), max_u16x2(mag_pair(o.z), mag_pair(o.w)));
+          m = max_u16x2(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+          m = max_u16x2(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+          const int e = mx_exponent(amax_of_pair(m));
+          uint2 q;
+          if (e != kMxNaN) {
+            const float sc = mx_scale_operand(e);
+            const uint32_t lim2 = mx_clamp_pair(e);
+            q = make_uint2(mx_codes4_pairs(o.x, o.y, sc, lim2), mx_codes4_pairs(o.z, o.w, sc, lim2));
+          } else {
+            q = make_uint2(mx_nan_codes4_pairs(o.x, o.y), mx_nan_codes4_pairs(o.z, o.w));
+          }
+          reinterpret_cast<uint2*>(xq + (int64_t)r * d)[v] = q;
+          if ((lane & 3) == 0) xs[(int64_t)r * (d / 32) + (v >> 2)] = (uint8_t)(e + 127);
+        } else {
+          if (dy_perm) reinterpret_cast<uint4*>(dy_perm + (int64_t)r * d)[v] = mul8_bf16(ws[k], g);
+        }
       }
     }
   }
@@ -195,13 +215,25 @@ extern "C" moe_status_t moe_unpermute_combine_launch(const uint16_t* y_perm, con
 
 extern "C" moe_status_t moe_combine_backward_launch(const uint16_t* dy, const uint16_t* y_perm, const float* w,
                                                     const int32_t* perm_dst, int64_t T, int32_t d, int32_t K,
-                                                    uint16_t* dy_perm, float* dw, hipStream_t s) {
+                                                    uint16_t* dy_perm, float* dw, uint8_t* xq, uint8_t* xs,
+                                                    hipStream_t s) {
   if (T == 0) return MOE_OK;
   const dim3 g((unsigned)((T + 3) / 4)), b(256);
-  switch (K) {
-    case 2: hipLaunchKernelGGL((moe::combine_backward_kernel<2>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw); break;
-    case 8: hipLaunchKernelGGL((moe::combine_backward_kernel<8>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw); break;
-    default: hipLaunchKernelGGL((moe::combine_backward_kernel<0>), g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, g, b, 0, s, dy, y_perm, w, perm_dst, T, d, K, dy_perm, dw, xq, xs);
+  };
+  if (xq) {
+    switch (K) {
+      case 2: go(moe::combine_backward_kernel<2, true>); break;
+      case 8: go(moe::combine_backward_kernel<8, true>); break;
+      default: go(moe::combine_backward_kernel<0, true>);
+    }
+  } else {
+    switch (K) {
+      case 2: go(moe::combine_backward_kernel<2, false>); break;
+      case 8: go(moe::combine_backward_kernel<8, false>); break;
+      default: go(moe::combine_backward_kernel<0, false>);
+    }
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -50,6 +50,34 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
+// bf16(w * g[j]) for 8 values, each the exact product rounded to nearest even
+// once.  The fp32 product p can only round differently from the exact one
+// when p lies exactly halfway between two bf16 values (low 16 bits 0x8000):
+// then its exact error e = fma(w, g, -p) says on which side the product
+// lies (e == 0: a true tie, to even).  Exact for products in the normal
+// fp32 range; NaN and infinity as the plain conversion gives them.
+__device__ __forceinline__ uint4 mul8_bf16(float w, const float* g) {
+  float p[8];
+  uint32_t fix[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = w * g[j];
+    const float e = fmaf(w, g[j], -p[j]);
+    const uint32_t b = __float_as_uint(p[j]);
+    const bool mid = (b & 0xFFFFu) == 0x8000u && e != 0.f && (b & 0x7F800000u) != 0x7F800000u;
+    // the bf16 bits toward the exact product: magnitude up when e has p's sign
+    fix[j] = mid ? (b >> 16) + (((__float_as_uint(e) ^ b) >> 31) ^ 1u) : 0xFFFFFFFFu;
+  }
+  const uint4 v = pack8(p);
+  uint32_t h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (fix[2 * q] != 0xFFFFFFFFu) h[q] = (h[q] & 0xFFFF0000u) | fix[2 * q];
+    if (fix[2 * q + 1] != 0xFFFFFFFFu) h[q] = (h[q] & 0xFFFFu) | (fix[2 * q + 1] << 16);
+  }
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+
 // ---------------------------------------------------------------- error flag
 __device__ __forceinline__ void raise_flag(uint32_t* flag, uint32_t bits) {
   if (flag) atomicOr(flag, bits);

@@ -62,7 +62,7 @@ struct Scales {
   int xr;               // X: its row within a piece, t / 8
   int rows;             // valid rows of the tile
   int t;                // lane within the four wavefronts of its kind
-  bool is_w;
+  int is_w;             // a W-scale wavefront
   template <typename WRow>
   __device__ __forceinline__ void init(int64_t ld, WRow wrow, int rows_) {
     const int wave = wave_id(), lane = threadIdx.x & 63;

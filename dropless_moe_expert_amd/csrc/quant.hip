@@ -145,12 +145,29 @@ constexpr int QT_CT = 2 * QT_R + 16;
 // is the SwiGLU backward dgu [rows, cols = 2f] (bf16-rounded, as
 // moe_swiglu_backward stores it), made from x = gu [rows, 2f] and dh
 // [rows, f]: dgu never exists in bf16.
+// the value of the neighbouring lane (t ^ 1), by DPP (quad_perm 1, 0, 3, 2)
+__device__ __forceinline__ int dpp_swap1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
+
 // a value equal in every lane, moved to scalar registers
 __device__ __forceinline__ int64_t uniform64(int64_t v) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
+
+// PRODUCER 3 (gather): row r of the tile source is row perm_src[r] / K of
+// x [T, cols] (the permute's x_perm, never stored), times the routing weight
+// w[perm_src[r]] and rounded to bf16 as moe_combine_backward rounds dy_perm
+// when w != NULL.  The pair / K division is exact as a 64-bit multiply by
+// magic = floor(2^40 / K) + 1 and a shift by 40 for pairs below 2^31 and
+// K <= 32: the product exceeds pair / K by less than 2^-9 < 1 / K.
+struct GatherArgs {
+  const int32_t* src;   // perm_src [rows]
+  const float* w;       // routing weights [rows] or NULL
+  const float* wsrc;    // w, or (unweighted) src read as floats: the weight load is issued either way
+  uint64_t magic;       // floor(2^40 / K) + 1
+  uint32_t last;        // rows - 1: a pair index is clamped to it, so no value read from src leads outside x or w
+};
 
 // element h (0 or 1, known only at run time) of a two-element array
 template <typename V>
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
                                                          const int32_t* __restrict__ group_sizes, int G,
                                                          int64_t k_cap, uint8_t* __restrict__ qT,
                                                          uint8_t* __restrict__ scaleT, uint8_t* __restrict__ q0,
-                                                         uint8_t* __restrict__ s0, uint32_t* flag) {
+                                                         uint8_t* __restrict__ s0, uint32_t* flag, GatherArgs ga) {
   extern __shared__ int64_t sh[];  // grouped: [0,G]: row offsets; [G+1, 2G+2): padded starts
   __shared__ __align__(16) uint16_t xt[2 * QT_R * QT_LD];  // two position units, bf16, row-major
   __shared__ __align__(16) uint8_t ct[QT_C * QT_CT];    // their codes, column-major (128 per column)
@@ -292,8 +309,25 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   // The next tile's loads are issued as soon as this tile's rows are in LDS,
   // so they are in flight while this tile is quantised and written out.
   constexpr int NP = PRODUCER == 2 ? 2 : 4;   // pieces (pairs) per thread
-  constexpr int NL = PRODUCER == 0 ? 1 : 3;   // loads per piece
+  constexpr int NL = PRODUCER == 1 || PRODUCER == 2 ? 3 : 1;   // loads per piece
+  constexpr bool GATHER = PRODUCER == 3;
   uint4 raw[NP][NL];
+  // PRODUCER 3: the pairs of this thread's four rows of the tile to be
+  // loaded next (read a tile ahead, so that the gather waits for no index),
+  // and the routing weights of the rows being loaded
+  int32_t pidx[4];
+  float wv[4];
+  // the index loads: every lane loads (a row past its unit's rows, or of an
+  // absent unit, reads the tile's first row's entry), so the number of
+  // loads issued after a tile's data loads never varies
+  auto load_idx = [&](const Tile& D) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = (t + 256 * k) >> 3, h = rr >> 6, r = rr & 63;
+      const int64_t row = r < sel(h, D.n) ? sel(h, D.r0) + r : D.r0[0];
+      pidx[k] = ga.src[row];
+    }
+  };
   auto load = [&](const Tile& D) {
 #pragma unroll
     for (int k = 0; k < NP; ++k) {
@@ -308,6 +342,16 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
           raw[k][1] = *reinterpret_cast<const uint4*>(x + row * cols + fh + j);
           raw[k][2] = *reinterpret_cast<const uint4*>(dh + row * fh + j);
         }
+      } else if constexpr (GATHER) {
+        const int rr = u >> 3, c = (u & 7) * 8, h = rr >> 6, r = rr & 63;
+        const uint32_t pair = min((uint32_t)pidx[k], ga.last);
+        if (r < sel(h, D.n) && D.c0 + c < cols) {
+          const int64_t tok = (int64_t)(((uint64_t)pair * ga.magic) >> 40);
+          raw[k][0] = *reinterpret_cast<const uint4*>(x + tok * cols + D.c0 + c);
+        }
+        // in every lane and either way (a padding row's weight multiplies
+        // zeros), so the loads after each data load are always the same
+        wv[k] = ga.wsrc[pair];
       } else {
         const int rr = u >> 3, c = (u & 7) * 8, h = rr >> 6, r = rr & 63;
         if (r < sel(h, D.n) && D.c0 + c < cols) {
@@ -346,6 +390,13 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       } else {
         const int rr = u >> 3, c = (u & 7) * 8;
         uint4 v = raw[k][0];
+        if constexpr (GATHER) {
+          if (ga.w) {   // bf16(w * dy) as moe_combine_backward forms dy_perm
+            float g[8];
+            unpack8(raw[k][0], g);
+            v = mul8_bf16(wv[k], g);
+          }
+        }
         if constexpr (PRODUCER == 1) {
           float g[8], uu[8], dd[8], dg[8], du[8];
           unpack8(raw[k][0], g);
@@ -372,17 +423,38 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
   // 1. the first tile's rows into LDS; each later tile's are staged at the
   //    end of the previous pass, after that pass's stores (the loop is so
   //    rotated that the wait for those rows counts the stores in between)
+  //    The gather first needs the pairs of tile 0's rows, then of tile 1's.
   Tile cur;
   describe(tile_of(0), cur);
+  if constexpr (GATHER) load_idx(cur);
   load(cur);
+  if constexpr (GATHER) {
+    Tile t1 = cur;
+    if (tile_of(1) < ntiles) describe(tile_of(1), t1);
+    load_idx(t1);
+  }
   stage(cur);
+  // A pass's gather waits for the pairs loaded in the pass before, with
+  // that pass's stores issued after them (not waited for).  Tile 1's pairs
+  // are waited for here instead, so that entering the first pass adds no
+  // path on which the gather's wait would have to count fewer operations.
+  if constexpr (GATHER) asm volatile("" ::"v"(pidx[0]), "v"(pidx[1]), "v"(pidx[2]), "v"(pidx[3]));
   for (int64_t k = 0;; ++k) {
     const int c0 = cur.c0;
     const bool more = tile_of(k + 1) < ntiles;
+    // the gather's pairs for the next tile, waited for on every path (also
+    // the last pass's, which loads nothing), so that no later write of
+    // their registers waits again
+    if constexpr (GATHER) asm volatile("" ::"v"(pidx[0]), "v"(pidx[1]), "v"(pidx[2]), "v"(pidx[3]));
     Tile nxt = cur;
     if (more) {   // the next tile's loads are in flight while this one is quantised and stored
       describe(tile_of(k + 1), nxt);
       load(nxt);
+    }
+    if constexpr (GATHER) {   // and the pairs of the tile after it (or again those of a tile at hand)
+      Tile n2 = nxt;
+      if (tile_of(k + 2) < ntiles) describe(tile_of(k + 2), n2);
+      load_idx(n2);
     }
     __syncthreads();
     // 2a. one thread per (column, 32-position block): amax, scale, 32 codes
@@ -422,13 +494,21 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
       d[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
     // 2b. one thread per (row, 32-column block): the axis-0 quantisation of the
-    //     valid rows.  A thread without a valid row or block takes the tile's
-    //     first row and block (always valid) and stores the same bytes to the
-    //     same place as thread 0: every thread issues the same stores, so the
-    //     wait for the next tile's loads need not wait for these stores too.
+    //     valid rows, a row's two blocks in neighbouring lanes.  A thread
+    //     without a valid row takes the tile's first row (always valid) and
+    //     stores the same bytes to the same place as that row's threads:
+    //     every thread issues the same stores, so the wait for the next
+    //     tile's loads need not wait for these stores too.  When both blocks
+    //     exist and are adjacent (not the SwiGLU split), the two lanes swap
+    //     halves so that each store writes 32 contiguous bytes of the row,
+    //     and both store the row's two scales as one 2-byte word; otherwise
+    //     (cols % 64 != 0) a lane without its block takes block 0.
     if constexpr (ROWS) {
+      // the same for the whole tile; cols % 64 == 0 keeps the scale word 2-byte aligned
+      const bool pair_ok = PRODUCER != 2 && cols % 64 == 0 && colvalid(c0, 32);
       int rr = t >> 1, b = t & 1;
-      if (!((rr & 63) < sel(rr >> 6, cur.n) && colvalid(c0, 32 * b))) rr = b = 0;
+      if (!((rr & 63) < sel(rr >> 6, cur.n))) rr = 0;
+      if (!pair_ok && !colvalid(c0, 32 * b)) rr = b = 0;
       const int cb = gcol(c0, 32 * b), h = rr >> 6, r = rr & 63;
       {
         const uint32_t* xr = reinterpret_cast<const uint32_t*>(xt + rr * QT_LD + 32 * b);   // QT_LD even
@@ -451,10 +531,28 @@ __global__ __launch_bounds__(256) void mx_quant_t_kernel(const uint16_t* __restr
           for (int q = 0; q < 8; ++q) w[q] = mx_nan_codes4_pairs(pr[2 * q], pr[2 * q + 1]);
         }
         const int64_t row = sel(h, cur.r0) + r;
-        uint4* d = reinterpret_cast<uint4*>(q0 + row * cols + cb);
-        d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        d[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        s0[row * (cols / 32) + cb / 32] = (uint8_t)(e + 127);
+        // the swap: block 0's lane keeps its first 16 codes and receives
+        // block 1's first 16; block 1's lane keeps its last 16 and receives
+        // block 0's last 16 (lanes t and t ^ 1 by DPP)
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (uint32_t)dpp_swap1((int)(b ? w[i] : w[4 + i]));
+        const uint32_t eo = (uint32_t)dpp_swap1(e + 127);
+        uint8_t* rowq = q0 + row * cols;
+        if (pair_ok) {
+          const uint4 lo = b ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(w[0], w[1], w[2], w[3]);
+          const uint4 hi = b ? make_uint4(w[4], w[5], w[6], w[7]) : make_uint4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<uint4*>(rowq + c0 + 16 * b) = lo;
+          *reinterpret_cast<uint4*>(rowq + c0 + 32 + 16 * b) = hi;
+          const uint32_t mine = (uint32_t)(e + 127);
+          *reinterpret_cast<uint16_t*>(s0 + row * (cols / 32) + c0 / 32) =
+              (uint16_t)(b ? (eo | (mine << 8)) : (mine | (eo << 8)));
+        } else {
+          uint4* d = reinterpret_cast<uint4*>(rowq + cb);
+          d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          s0[row * (cols / 32) + cb / 32] = (uint8_t)(e + 127);
+        }
       }
     }
     __syncthreads();
@@ -539,11 +637,11 @@ __global__ __launch_bounds__(256) void mx4_quant_rows_kernel(const uint16_t* __r
 
 }  // namespace moe
 
-extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, const uint16_t* dh, int64_t rows,
-                                                         int32_t cols,
-                                                         const int32_t* group_sizes, int32_t G, int64_t k_cap,
-                                                         uint8_t* qT, uint8_t* scaleT, uint8_t* q0, uint8_t* s0,
-                                                         uint32_t* flag, hipStream_t s) {
+namespace {
+
+moe_status_t quant_t_launch(const uint16_t* x, const uint16_t* dh, int64_t rows, int32_t cols,
+                            const int32_t* group_sizes, int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT,
+                            uint8_t* q0, uint8_t* s0, uint32_t* flag, const moe::GatherArgs* ga, hipStream_t s) {
   const int64_t ntk = group_sizes ? k_cap / 64 : (int64_t)G * (rows / 64);   // an upper bound when grouped
   const int64_t work = (ntk + 1) / 2 * ((cols + 63) / 64);   // pairs of 64-position units
   if (work == 0) return MOE_OK;
@@ -559,9 +657,12 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
     per_cu = std::max(per_cu, 1);
     const int64_t blocks = std::min<int64_t>(work, (int64_t)moe_host::device_cu_count() * per_cu);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), shmem, s, x, dh, rows, cols, group_sizes, G, k_cap,
-                       qT, scaleT, q0, s0, flag);
+                       qT, scaleT, q0, s0, flag, ga ? *ga : moe::GatherArgs{nullptr, nullptr, nullptr, 0, 0});
   };
-  if (q0) {
+  if (ga) {
+    if (q0) launch(moe::mx_quant_t_kernel<3, true>);
+    else launch(moe::mx_quant_t_kernel<3, false>);
+  } else if (q0) {
     if (dh && (cols / 2) % 32 == 0) launch(moe::mx_quant_t_kernel<2, true>);
     else if (dh) launch(moe::mx_quant_t_kernel<1, true>);
     else launch(moe::mx_quant_t_kernel<0, true>);
@@ -571,6 +672,25 @@ extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, cons
     else launch(moe::mx_quant_t_kernel<0, false>);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" moe_status_t mxfp8_quantize_transposed_launch(const uint16_t* x, const uint16_t* dh, int64_t rows,
+                                                         int32_t cols, const int32_t* group_sizes, int32_t G,
+                                                         int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint8_t* q0,
+                                                         uint8_t* s0, uint32_t* flag, hipStream_t s) {
+  return quant_t_launch(x, dh, rows, cols, group_sizes, G, k_cap, qT, scaleT, q0, s0, flag, nullptr, s);
+}
+
+extern "C" moe_status_t mxfp8_gather_quantize_launch(const uint16_t* x, const int32_t* perm_src, const float* w,
+                                                     int32_t K, int64_t rows, int32_t cols,
+                                                     const int32_t* group_sizes, int32_t G, int64_t k_cap,
+                                                     uint8_t* qT, uint8_t* scaleT, uint8_t* q0, uint8_t* s0,
+                                                     uint32_t* flag, hipStream_t s) {
+  const moe::GatherArgs ga{perm_src, w, w ? w : reinterpret_cast<const float*>(perm_src),
+                           ((uint64_t)1 << 40) / (uint64_t)K + 1, (uint32_t)(rows - 1)};
+  return quant_t_launch(x, nullptr, rows, cols, group_sizes, G, k_cap, qT, scaleT, q0, s0, flag, &ga, s);
 }
 
 extern "C" moe_status_t mxfp4_quantize_launch(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* q,

@@ -32,8 +32,9 @@ FLAG_NAN_LOGIT = 0x8
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_route_topk", "moe_permute_workspace_bytes", "moe_permute",
     "moe_permute_mxfp8", "moe_permute_noalloc", "grouped_gemm_workspace_bytes", "grouped_gemm", "moe_unpermute_combine",
-    "moe_combine_backward",
+    "moe_combine_backward", "moe_combine_backward_mxfp8",
     "moe_swiglu_backward", "moe_swiglu_backward_mxfp8", "mxfp8_group_quantize", "mxfp8_quantize_transposed",
+    "mxfp8_quantize_gathered",
     "moe_pack_weights_bytes",
     "moe_pack_weights",
     "moe_pack_weights_mxfp8_bytes", "moe_pack_weights_mxfp8",
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH, require_gpu: bool = True):
             "mxfp8_group_quantize": (ctypes.c_int, [P, i64, i32, i32, P, i32, P, P, P, P]),
             "mxfp8_quantize_transposed": (ctypes.c_int, [P, i64, i32, P, i32, i64, P, P, P, P, P, P]),
             "moe_swiglu_backward_mxfp8": (ctypes.c_int, [P, P, i64, i32, P, i32, i64, P, P, P, P, P, P]),
+            "mxfp8_quantize_gathered": (ctypes.c_int, [P, P, P, i64, i32, i32, P, i32, i64, P, P, P, P, P, P]),
+            "moe_combine_backward_mxfp8": (ctypes.c_int, [P, P, P, P, i64, i32, i32, P, P, P, P]),
             "moe_pack_weights_bytes": (sz, [i32, i32, i32, i32]),
             "moe_pack_weights": (ctypes.c_int, [P, i32, i32, i32, i32, P, sz, P]),
             "moe_pack_weights_mxfp8_bytes": (sz, [i32, i32, i32, i32]),
@@ -497,15 +500,32 @@ def unpermute_combine(y_perm: torch.Tensor, topk_w: Optional[torch.Tensor], perm
     return out
 
 
-def combine_backward(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor, perm_dst: torch.Tensor, K: int):
-    """-> (dy_perm bf16 [T*K, d], d_topk_w fp32 [T, K])."""
+def combine_backward(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor, perm_dst: torch.Tensor, K: int,
+                     weights_only: bool = False):
+    """-> (dy_perm bf16 [T*K, d], d_topk_w fp32 [T, K]); weights_only: dy_perm
+    is not formed (None), as when mxfp8_quantize_gathered delivers it quantised."""
     dev = _dev(dy, y_perm, topk_w, perm_dst)
     T, d = dy.shape
-    dyp = torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
+    dyp = None if weights_only else torch.empty((T * K, d), dtype=torch.bfloat16, device=dev)
     dw = torch.empty((T, K), dtype=torch.float32, device=dev)
     _check(lib().moe_combine_backward(_ptr(dy), _ptr(y_perm), _ptr(topk_w), _ptr(perm_dst), T, d, K, _ptr(dyp),
                                       _ptr(dw), _stream(dev)), "moe_combine_backward")
     return dyp, dw
+
+
+def combine_backward_mxfp8(dy: torch.Tensor, y_perm: torch.Tensor, topk_w: torch.Tensor, perm_dst: torch.Tensor,
+                           K: int):
+    """-> (dy_perm row codes uint8 [T*K, d], their scales [T*K, d/32],
+    d_topk_w fp32 [T, K]): combine_backward with dy_perm quantised along its
+    rows as it is formed (mxfp8_quantize(dy_perm, 0) bit for bit)."""
+    dev = _dev(dy, y_perm, topk_w, perm_dst)
+    T, d = dy.shape
+    q = torch.empty((T * K, d), dtype=torch.uint8, device=dev)
+    sc = torch.empty((T * K, d // 32), dtype=torch.uint8, device=dev)
+    dw = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _check(lib().moe_combine_backward_mxfp8(_ptr(dy), _ptr(y_perm), _ptr(topk_w), _ptr(perm_dst), T, d, K, _ptr(q),
+                                            _ptr(sc), _ptr(dw), _stream(dev)), "moe_combine_backward_mxfp8")
+    return q, sc, dw
 
 
 def swiglu_backward(gu: torch.Tensor, dh: torch.Tensor, group_sizes: Optional[torch.Tensor] = None,
@@ -569,6 +589,31 @@ def mxfp8_quantize_transposed(x: torch.Tensor, group_sizes: Optional[torch.Tenso
         s0 = torch.empty(tuple(x.shape[:-1]) + (cols // 32,), dtype=torch.uint8, device=dev)
     _check(lib().mxfp8_quantize_transposed(_ptr(x), rows, cols, _ptr(group_sizes), G, k_cap, _ptr(q), _ptr(s),
                                            _ptr(q0), _ptr(s0), _ptr(flag), _stream(dev)), "mxfp8_quantize_transposed")
+    return (q, s, q0, s0) if rows_too else (q, s)
+
+
+def mxfp8_quantize_gathered(x: torch.Tensor, perm_src: torch.Tensor, K: int, group_sizes: torch.Tensor,
+                            topk_w: Optional[torch.Tensor] = None, flag: Optional[torch.Tensor] = None,
+                            rows_too: bool = False):
+    """mxfp8_quantize_transposed(x_perm, group_sizes, rows_too=...) without
+    x_perm: row r is x[perm_src[r] // K] (moe_permute's x_perm), or with
+    topk_w that row times topk_w.flatten()[perm_src[r]] rounded to bf16
+    (moe_combine_backward's dy_perm for dy = x).  x bf16 [T, cols]."""
+    dev = _dev(x, perm_src, group_sizes, topk_w)
+    assert x.dtype == torch.bfloat16 and perm_src.dtype == torch.int32
+    T, cols = x.shape
+    M = T * K
+    G = group_sizes.numel()
+    k_cap = k_cap_for(M, G)
+    q = torch.empty((cols, k_cap), dtype=torch.uint8, device=dev)
+    s = torch.empty((cols, k_cap // 32), dtype=torch.uint8, device=dev)
+    q0 = s0 = None
+    if rows_too:
+        q0 = torch.empty((M, cols), dtype=torch.uint8, device=dev)
+        s0 = torch.empty((M, cols // 32), dtype=torch.uint8, device=dev)
+    _check(lib().mxfp8_quantize_gathered(_ptr(x), _ptr(perm_src), _ptr(topk_w), T, K, cols, _ptr(group_sizes), G,
+                                         k_cap, _ptr(q), _ptr(s), _ptr(q0), _ptr(s0), _ptr(flag), _stream(dev)),
+           "mxfp8_quantize_gathered")
     return (q, s, q0, s0) if rows_too else (q, s)
 
 
@@ -685,18 +730,30 @@ def quantize_weights_mxfp8_train(w1p: torch.Tensor, w2: torch.Tensor, flag: Opti
 
 
 def moe_forward_mxfp8_train(logits: torch.Tensor, x: torch.Tensor, wk: dict, K: int,
-                            flag: Optional[torch.Tensor] = None):
+                            flag: Optional[torch.Tensor] = None, fused: bool = True):
     """The routed layer on MXFP8 operands, keeping what the backward needs:
-    route -> permute (bf16 rows) -> quantise -> gate/up GEMM + SwiGLU (bf16 h
-    and pre-activations) -> quantise h -> down GEMM -> combine.  wk from
-    quantize_weights_mxfp8_train."""
+    route -> permute -> quantise -> gate/up GEMM + SwiGLU (bf16 h and
+    pre-activations) -> quantise h -> down GEMM -> combine.  wk from
+    quantize_weights_mxfp8_train.  fused: no bf16 x_perm (None): the row
+    codes come from permute_mxfp8, the transposed ones from
+    mxfp8_quantize_gathered; else permute writes bf16 x_perm and
+    mxfp8_quantize_transposed reads it."""
     T = x.shape[0]
     ids, w = route_topk(logits, K, flag=flag)
-    p = permute(x, ids, wk["w1k"].G, flag=flag)
-    sizes = p["group_sizes"]
-    # x and h quantised both ways in one read each: along their rows for the
-    # forward GEMMs, down the tokens (kept) for the weight gradients
-    xT, xsT, xq, xs = mxfp8_quantize_transposed(p["x_perm"], sizes, flag=flag, rows_too=True)
+    # x and h quantised both ways: along their rows for the forward GEMMs,
+    # down the tokens (kept) for the weight gradients
+    if fused:
+        # the dispatch quantises each token row once for its K rows, the
+        # transposed codes come from the rows gathered from x
+        p = permute_mxfp8(x, ids, wk["w1k"].G, flag=flag)
+        sizes = p["group_sizes"]
+        xq, xs = p.pop("xq"), p.pop("xs")
+        p["x_perm"] = None
+        xT, xsT = mxfp8_quantize_gathered(x, p["perm_src"], K, sizes, flag=flag)
+    else:
+        p = permute(x, ids, wk["w1k"].G, flag=flag)
+        sizes = p["group_sizes"]
+        xT, xsT, xq, xs = mxfp8_quantize_transposed(p["x_perm"], sizes, flag=flag, rows_too=True)
     h, gu = grouped_gemm_mxfp8(xq, xs, wk["w1k"], None, sizes, epilogue=MOE_EPI_SWIGLU, keep_aux=True, flag=flag)
     hT, hsT, hq, hs = mxfp8_quantize_transposed(h, sizes, flag=flag, rows_too=True)
     y_perm = grouped_gemm_mxfp8(hq, hs, wk["w2k"], None, sizes, flag=flag)
@@ -711,12 +768,21 @@ def moe_backward_mxfp8(dy: torch.Tensor, saved: dict, wk: dict, K: int, flag: Op
     quantised along their output axis; the weight gradients quantise both
     operands down the tokens, blocks restarting at every expert's rows
     (group-aware MXFP8).  Combine, SwiGLU backward and the dx fold stay bf16;
-    fused: the SwiGLU backward delivers dgu as MXFP8 only (dgu is then None)."""
+    fused: dy_perm (the combine's backward) and dgu (the SwiGLU backward)
+    are delivered as MXFP8 only, by mxfp8_quantize_gathered and
+    swiglu_backward_mxfp8 (both None in the result)."""
     sizes, dst = saved["group_sizes"], saved["perm_dst"]
     T = dy.shape[0]
     m_cap = saved["h"].shape[0]
-    dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
-    aT, asT, q, sc = mxfp8_quantize_transposed(dyp, sizes, flag=flag, rows_too=True)
+    if fused:
+        # dy_perm's row codes as the combine's backward forms it, its
+        # transposed codes from dy gathered and weighted again
+        dyp = None
+        q, sc, dw = combine_backward_mxfp8(dy, saved["y_perm"], saved["w"], dst, K)
+        aT, asT = mxfp8_quantize_gathered(dy, saved["perm_src"], K, sizes, topk_w=saved["w"], flag=flag)
+    else:
+        dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
+        aT, asT, q, sc = mxfp8_quantize_transposed(dyp, sizes, flag=flag, rows_too=True)
     dh = grouped_gemm_mxfp8(q, sc, wk["w2tk"], None, sizes, flag=flag)                    # [M, f]
     dw2 = grouped_gemm_wgrad_mxfp8(aT, asT, saved["hT"], saved["hsT"], sizes, m_cap, flag=flag)  # [E, d, f]
     if fused:

@@ -314,10 +314,24 @@ moe_status_t moe_unpermute_combine(const uint16_t* y_perm, const float* topk_w, 
  * the second being what a router's own backward would take in.
  * dy bf16 [T,d], y_perm bf16 [T*K,d], dy_perm bf16 [T*K,d], d_topk_w fp32 [T,K];
  * d % 8 == 0; dy, y_perm, dy_perm 16-byte aligned.  Each row of dy_perm is
- * written by exactly one pair, so the result is bitwise reproducible. */
+ * written by exactly one pair, so the result is bitwise reproducible.
+ * dy_perm == NULL computes d_topk_w only (the MXFP8 backward takes dy_perm
+ * from mxfp8_quantize_gathered instead, already quantised). */
 moe_status_t moe_combine_backward(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
                                   const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint16_t* dy_perm,
                                   float* d_topk_w, void* stream);
+
+/* The same backward with dy_perm delivered only as MXFP8 along its rows:
+ * q_rows uint8 [T*K, d] and scale_rows uint8 [T*K, d/32] equal, bit for bit,
+ * mxfp8_group_quantize(axis 0) of the bf16 dy_perm that moe_combine_backward
+ * writes (that quantisation fused with its producer, blog section
+ * "Optimization 1": each dy row is read once for its K weighted copies);
+ * d_topk_w as there.  The transposed codes of dy_perm come from
+ * mxfp8_quantize_gathered with topk_w.  d % 32 == 0; dy, y_perm 16-byte
+ * aligned, q_rows 8-byte aligned. */
+moe_status_t moe_combine_backward_mxfp8(const uint16_t* dy, const uint16_t* y_perm, const float* topk_w,
+                                        const int32_t* perm_dst, int64_t T, int32_t d, int32_t K, uint8_t* q_rows,
+                                        uint8_t* scale_rows, float* d_topk_w, void* stream);
 
 /* Backward of SwiGLU.  The expert MLP's two input projections are the
  * blog's moe_mlpwi_0 / moe_mlpwi_1 (gate and up, fused into one weight by
@@ -401,6 +415,26 @@ moe_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8
 moe_status_t mxfp8_quantize_transposed(const uint16_t* x, int64_t rows, int32_t cols, const int32_t* group_sizes,
                                        int32_t G, int64_t k_cap, uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows,
                                        uint8_t* scale_rows, uint32_t* err_flag, void* stream);
+
+/* Quantisation fused with the dispatch: mxfp8_quantize_transposed (grouped,
+ * rows = T*K) of the permuted rows, read straight from their tokens, so that
+ * the bf16 permuted copy is never written and read back (blog section
+ * "Optimization 2: Expert parallelism to integrate Dispatch and Combine": an
+ * unfused chain reads and writes the data several times; "Optimization 1":
+ * group-aware MXFP8 quantisation).  Row r of the quantised operand is
+ *   topk_w == NULL:  x[perm_src[r] / K, :]                (moe_permute's x_perm)
+ *   topk_w != NULL:  bf16(topk_w[perm_src[r]] * x[perm_src[r] / K, :])
+ *                    (moe_combine_backward's dy_perm for dy = x),
+ * and every output equals, bit for bit, that of mxfp8_quantize_transposed on
+ * that bf16 operand with the same group_sizes, G, k_cap, q_rows, scale_rows.
+ * x bf16 [T, cols]; perm_src int32 [T*K] as moe_permute writes it (a pair
+ * index outside [0, T*K) is clamped into it, never read past x or topk_w);
+ * topk_w fp32 [T*K] or NULL; K in [1, 32]; group_sizes required (sum of the
+ * sizes = T*K); outputs and alignment as mxfp8_quantize_transposed. */
+moe_status_t mxfp8_quantize_gathered(const uint16_t* x, const int32_t* perm_src, const float* topk_w, int64_t T,
+                                     int32_t K, int32_t cols, const int32_t* group_sizes, int32_t G, int64_t k_cap,
+                                     uint8_t* qT, uint8_t* scaleT, uint8_t* q_rows, uint8_t* scale_rows,
+                                     uint32_t* err_flag, void* stream);
 
 /* The SwiGLU backward of moe_swiglu_backward with its output dgu [m_cap, 2f]
  * delivered only as MXFP8, both layouts, as mxfp8_quantize_transposed

@@ -46,12 +46,17 @@ moe_status_t moe_permute_mxfp8_launch(const uint16_t*, const int32_t*, int64_t, 
 moe_status_t moe_unpermute_combine_launch(const uint16_t*, const float*, const int32_t*, int64_t, int32_t, int32_t,
                                           uint16_t*, hipStream_t) { return launched(); }
 moe_status_t moe_combine_backward_launch(const uint16_t*, const uint16_t*, const float*, const int32_t*, int64_t,
-                                         int32_t, int32_t, uint16_t*, float*, hipStream_t) { return launched(); }
+                                         int32_t, int32_t, uint16_t*, float*, uint8_t*, uint8_t*, hipStream_t) {
+  return launched();
+}
 moe_status_t moe_swiglu_backward_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*, int32_t,
                                         uint16_t*, hipStream_t) { return launched(); }
 moe_status_t mxfp8_quantize_transposed_launch(const uint16_t*, const uint16_t*, int64_t, int32_t, const int32_t*,
                                               int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint32_t*,
                                               hipStream_t) { return launched(); }
+moe_status_t mxfp8_gather_quantize_launch(const uint16_t*, const int32_t*, const float*, int32_t, int64_t, int32_t,
+                                          const int32_t*, int32_t, int64_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*,
+                                          uint32_t*, hipStream_t) { return launched(); }
 moe_status_t mxfp4_quantize_launch(const uint16_t*, int64_t, int32_t, uint8_t*, uint8_t*, hipStream_t) {
   return launched();
 }
@@ -155,12 +160,32 @@ int main() {
   EXPECT(moe_unpermute_combine(u16, f, i32, 16, 64, 2, u16, nullptr), MOE_OK);
   EXPECT(moe_unpermute_combine(u16, f, i32, BIG, 64, 2, u16, nullptr), MOE_OK);   // T only counts tokens
   EXPECT(moe_combine_backward(u16, u16, f, i32, 16, 64, 2, u16, f, nullptr), MOE_OK);
+  EXPECT(moe_combine_backward(u16, u16, f, i32, 16, 64, 2, nullptr, f, nullptr), MOE_OK);   // weights only
+  EXPECT(moe_combine_backward(u16, u16, f, i32, 16, 64, 2, u16, nullptr, nullptr), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_combine_backward_mxfp8(u16, u16, f, i32, 16, 64, 2, u8, u8, f, nullptr), MOE_OK);
+  EXPECT(moe_combine_backward_mxfp8(u16, u16, f, i32, 16, 48, 2, u8, u8, f, nullptr), MOE_ERR_UNSUPPORTED);
+  EXPECT(moe_combine_backward_mxfp8(u16, u16, f, i32, 16, 64, 2, nullptr, u8, f, nullptr), MOE_ERR_INVALID_ARG);
+  EXPECT(moe_combine_backward_mxfp8(u16, u16, f, i32, 16, 64, 40, u8, u8, f, nullptr), MOE_ERR_INVALID_ARG);
   EXPECT(moe_swiglu_backward(u16, u16, 16, 64, i32, 4, u16, nullptr), MOE_OK);
   EXPECT(moe_swiglu_backward(u16, u16, 16, 64, i32, 0, u16, nullptr), MOE_ERR_INVALID_ARG);
   EXPECT(mxfp8_group_quantize(u16, 16, 64, 0, nullptr, 0, u8, u8, nullptr, nullptr), MOE_OK);
   EXPECT(mxfp8_group_quantize(u16, 16, 64, 1, i32, 4, u8, u8, nullptr, nullptr), MOE_OK);
   EXPECT(mxfp8_quantize_transposed(u16, 64, 64, i32, 4, 64 * 6, u8, u8, nullptr, nullptr, nullptr, nullptr), MOE_OK);
   EXPECT(mxfp8_quantize_transposed(u16, BIG, 64, i32, 4, 64 * 6, u8, u8, nullptr, nullptr, nullptr, nullptr),
+         MOE_ERR_INVALID_ARG);
+  EXPECT(mxfp8_quantize_gathered(u16, i32, f, 16, 4, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr), MOE_OK);
+  EXPECT(mxfp8_quantize_gathered(u16, i32, nullptr, 16, 4, 64, i32, 4, 64 * 6, u8, u8, nullptr, nullptr, nullptr,
+                                 nullptr),
+         MOE_OK);
+  EXPECT(mxfp8_quantize_gathered(u16, i32, f, 16, 33, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr),
+         MOE_ERR_INVALID_ARG);   // K > 32
+  EXPECT(mxfp8_quantize_gathered(u16, i32, f, BIG, 4, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr),
+         MOE_ERR_INVALID_ARG);   // T * K past int32
+  EXPECT(mxfp8_quantize_gathered(u16, i32, f, 16, 4, 64, i32, 4, 64, u8, u8, u8, u8, nullptr, nullptr),
+         MOE_ERR_INVALID_ARG);   // k_cap below rows + 63 G
+  EXPECT(mxfp8_quantize_gathered(u16, i32, f, 16, 4, 48, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr),
+         MOE_ERR_UNSUPPORTED);   // row codes need cols % 32 == 0
+  EXPECT(mxfp8_quantize_gathered(u16, nullptr, f, 16, 4, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr),
          MOE_ERR_INVALID_ARG);
   EXPECT(moe_swiglu_backward_mxfp8(u16, u16, 64, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr), MOE_OK);
   EXPECT(moe_swiglu_backward_mxfp8(u16, u16, BIG, 64, i32, 4, 64 * 6, u8, u8, u8, u8, nullptr, nullptr),

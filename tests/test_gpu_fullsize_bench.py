@@ -333,10 +333,17 @@ def test_finegrained_mxfp8_step_full(ops):
     y_ref = orc.unpermute_combine(YP, w, dst, L.T, L.K)[tokens]
     assert rel_l2_u16(rows_of(y, tokens), y_ref) <= MX_TOL
     # backward: dh on the weight quantised down d, dgu, dx_perm on W1p quantised down 2f
-    assert mre_u16(rows_of(g["dy_perm"], rows), dyp[rows]) <= BF16_TOL
+    # dy_perm reaches the GEMMs only as MXFP8, quantised as it is gathered:
+    # its row codes are the oracle's codes of the oracle's dy_perm rows
     DYP = np.zeros((M, d), np.uint16)
     DYP[rows] = dyp[rows]
     dq, ds = orc.mxfp8_quantize(DYP, 0)
+    _, _, gq0, gs0 = ops.mxfp8_quantize_gathered(dy, sv["perm_src"], L.K, sv["group_sizes"], topk_w=sv["w"],
+                                                 rows_too=True)
+    sel = torch.from_numpy(rows).to(dev)
+    np.testing.assert_array_equal(gq0[sel].cpu().numpy(), dq[rows])
+    np.testing.assert_array_equal(gs0[sel].cpu().numpy(), ds[rows])
+    del gq0, gs0
     w2tq = np.zeros((L.E, f, d), np.uint8)
     w2ts = np.zeros((L.E, f, d // 32), np.uint8)
     w1tq = np.zeros((L.E, d, 2 * f), np.uint8)

@@ -447,6 +447,42 @@ def test_mxfp8_quantize_transposed(ops):
         np.testing.assert_array_equal(s0[g].cpu().numpy(), s_ref)
 
 
+@pytest.mark.parametrize("T,E,K,C", [(150, 9, 3, 96), (8192, 64, 8, 512)])
+def test_mxfp8_quantize_gathered(ops, T, E, K, C):
+    # the permuted rows quantised both ways straight from their tokens, as
+    # the oracle quantises its own x_perm (no weights) and its own
+    # combine-backward dy_perm (weights), bit for bit; the oracle's perm_src
+    # drives the gather.  The second case gives every workgroup several
+    # tiles (the prefetch of the next tile's pairs and rows); the last
+    # expert receives no token.
+    rng = np.random.default_rng(T + C)
+    ids = np.stack([rng.choice(E - 1, K, replace=False) for _ in range(T)]).astype(np.int32)
+    sizes, _, src, dst = orc.permute(ids, E)
+    assert sizes[-1] == 0
+    M = T * K
+    say("mx gathered", T, E, K, C)
+    x = bf16(rng, T, C, scale=3.0)
+    w = rng.dirichlet(np.ones(K), T).astype(np.float32)
+    refs = {
+        False: orc.gather_rows(x, src, K),
+        True: orc.combine_backward(x, np.zeros((M, C), np.uint16), w, dst, K)[0],
+    }
+    S, SRC = dev(torch.from_numpy(sizes)), dev(torch.from_numpy(src))
+    for weighted, ref in refs.items():
+        q_ref, s_ref = orc.mxfp8_quantize(ref, 1, sizes)
+        q0_ref, s0_ref = orc.mxfp8_quantize(ref, 0)
+        tw = dev(torch.from_numpy(w)) if weighted else None
+        for rows_too in (False, True):
+            got = ops.mxfp8_quantize_gathered(dev(x), SRC, K, S, topk_w=tw, rows_too=rows_too)
+            torch.cuda.synchronize()
+            want_q, want_s, used = _to_transposed(q_ref, s_ref, sizes, got[0].shape[1])
+            np.testing.assert_array_equal(got[0][:, :used].cpu().numpy(), want_q[:, :used])
+            np.testing.assert_array_equal(got[1][:, :used // 32].cpu().numpy(), want_s[:, :used // 32])
+            if rows_too:
+                np.testing.assert_array_equal(got[2].cpu().numpy(), q0_ref)
+                np.testing.assert_array_equal(got[3].cpu().numpy(), s0_ref)
+
+
 def test_swiglu_backward_mxfp8(ops):
     # dgu delivered only as MXFP8 codes equals quantising the bf16 dgu, bit for bit
     rng = np.random.default_rng(44)
@@ -600,8 +636,19 @@ def test_combine_backward_and_swiglu_backward(ops):
     w = rng.dirichlet(np.ones(K), T).astype(np.float32)
     dyp_ref, dw_ref = orc.combine_backward(dy, yp, w, dst, K)
     dyp, dw = ops.combine_backward(dev(dy), dev(yp), dev(torch.from_numpy(w)), dev(torch.from_numpy(dst)), K)
+    _, dw_only = ops.combine_backward(dev(dy), dev(yp), dev(torch.from_numpy(w)), dev(torch.from_numpy(dst)), K,
+                                      weights_only=True)
     torch.cuda.synchronize()
-    assert max_rel_err(dyp, dyp_ref) <= BF16_TOL
+    q_mx, s_mx, dw_mx = ops.combine_backward_mxfp8(dev(dy), dev(yp), dev(torch.from_numpy(w)),
+                                                   dev(torch.from_numpy(dst)), K)
+    torch.cuda.synchronize()
+    # dy_perm: the exact product rounded once to bf16, bit for bit
+    np.testing.assert_array_equal(host_u16(dyp), dyp_ref)
+    assert torch.equal(dw_only, dw) and torch.equal(dw_mx, dw)
+    # and delivered as MXFP8 rows: the oracle's codes of the oracle's dy_perm
+    q_ref, s_ref = orc.mxfp8_quantize(dyp_ref, 0)
+    np.testing.assert_array_equal(q_mx.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s_mx.cpu().numpy(), s_ref)
     np.testing.assert_allclose(dw.cpu().numpy(), dw_ref, rtol=1e-3, atol=1e-3 * np.abs(dw_ref).max())
     M = T * K
     gu, dh = bf16(rng, M, 2 * f, scale=2.0), bf16(rng, M, f)
@@ -649,13 +696,25 @@ def test_tiny_layer_forward_backward_mxfp8(ops):
     g_ref = orc.layer_backward_mxfp8(L.dy, saved_ref, L.w1p, L.w2, L.K)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     wk = ops.quantize_weights_mxfp8_train(dev(L.w1p), dev(L.w2), flag=flag)
-    y, saved = ops.moe_forward_mxfp8_train(dev(L.logits), dev(L.x), wk, L.K, flag=flag)
+    y, saved = ops.moe_forward_mxfp8_train(dev(L.logits), dev(L.x), wk, L.K, flag=flag, fused=False)
+    y_f, saved_f = ops.moe_forward_mxfp8_train(dev(L.logits), dev(L.x), wk, L.K, flag=flag)
     grads = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag, fused=False)
-    fused = ops.moe_backward_mxfp8(dev(L.dy), saved, wk, L.K, flag=flag)
+    fused = ops.moe_backward_mxfp8(dev(L.dy), saved_f, wk, L.K, flag=flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
-    # the SwiGLU backward that quantises its own output changes no bit downstream
-    for k in ("dx_perm", "dw1p", "dx"):
+    # the quantisers that gather their rows (x, dy) or form them (dgu)
+    # themselves change no bit downstream
+    assert saved_f["x_perm"] is None and fused["dy_perm"] is None and fused["dgu"] is None
+    assert torch.equal(y_f, y)
+    used = int(((saved_ref["sizes"] + 63) // 64 * 64).sum())   # written positions of the transposed codes
+    for k in ("xT", "hT"):
+        assert torch.equal(saved_f[k][:, :used], saved[k][:, :used]), k
+    for k in ("xsT", "hsT"):
+        assert torch.equal(saved_f[k][:, :used // 32], saved[k][:, :used // 32]), k
+    M_all = int(saved_ref["sizes"].sum())
+    for k in ("h", "gu", "y_perm"):
+        assert torch.equal(saved_f[k][:M_all], saved[k][:M_all]), k
+    for k in ("dw", "dh", "dw2", "dx_perm", "dw1p", "dx"):
         assert torch.equal(fused[k], grads[k]), k
     np.testing.assert_array_equal(saved["group_sizes"].cpu().numpy(), saved_ref["sizes"])
     M = int(saved_ref["sizes"].sum())
