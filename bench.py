@@ -74,16 +74,17 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+def measured_counters():
+    """The gate/up GEMM's figures from the committed rocprofv3 counter
+    summary (HBM bytes per launch, MFMA busy fraction, clock), if they were
+    taken on the current kernel source; else an empty dict."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("source_sha256_16") != source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+        return {}
+    return t
 
 
 class Timed(float):
@@ -594,6 +595,40 @@ def bench_finegrained_mxfp8(torch, ops, L, dev, timer, flag, steps) -> dict:
             }}
 
 
+# --only: the workloads and how each is set up and run (as in the full run)
+ONLY_WORKLOADS = {
+    "dsv3_mxfp8": ("dsv3_share", lambda torch, ops, L, dev, timer, flag, steps: bench_mxfp8_share(
+        torch, ops, L, dev, timer, flag)),
+    "dsv3_mxfp4": ("dsv3_share", lambda torch, ops, L, dev, timer, flag, steps: bench_mxfp4_share(
+        torch, ops, L, dev, timer, flag)),
+    "mixtral": ("mixtral", bench_mixtral),
+    "mixtral_mxfp8": ("mixtral", bench_mixtral_mxfp8),
+    "mixtral_mxfp4": ("mixtral", bench_mixtral_mxfp4),
+    "finegrained": ("finegrained", bench_finegrained),
+    "finegrained_mxfp8": ("finegrained", bench_finegrained_mxfp8),
+}
+
+
+def run_only(args, torch, ops, inputs, dev) -> int:
+    """One workload's kernels alone (so that a profiler run attributes every
+    dispatch of a kernel to that workload); prints its bench entry."""
+    inp, fn = ONLY_WORKLOADS[args.only]
+    L = inputs.workload(inp)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    timer = Timer(torch, torch.cuda.current_stream(dev), max(5, args.steps // 2))
+    entry = fn(torch, ops, L, dev, timer, flag, max(5, args.steps // 5))
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0, "device error flag raised"
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"only": args.only, "entry": entry}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -604,6 +639,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=2304, help="expert-share rows the oracle computes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling the HBM byte counters)")
+    ap.add_argument("--only", choices=["dsv3_share"] + list(ONLY_WORKLOADS),
+                    help="profiling: run one workload's kernels alone and print its entry (no headline line "
+                         "unless it is dsv3_share)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -618,6 +656,10 @@ def main() -> int:
     ops.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "dsv3_share":
+        args.no_layer = args.no_cpu_baseline = True
+    elif args.only:
+        return run_only(args, torch, ops, inputs, dev)
 
     # ------------------------------------------------------------ expert share (headline)
     t0 = time.time()
@@ -681,7 +723,9 @@ def main() -> int:
         "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(gg1_tflops / BF16_PEAK_TFLOPS, 4),
-        "traffic": measured_traffic(),
+        "traffic": measured_counters().get("hbm_bytes_per_launch"),
+        "mfma_busy_counter": measured_counters().get("mfma_busy"),
+        "clock_ghz_counter": measured_counters().get("clock_ghz"),
         "algorithmic_flop_per_launch": flops_gg1,
         "avg_launch_ms": round(gg1_ms, 4),
     }
