@@ -28,7 +28,11 @@ def ops():
 # ------------------------------------------------------------------- routing
 
 @pytest.mark.parametrize("T,E,K,renorm", [(300, 8, 2, 1), (1000, 128, 8, 1), (77, 256, 8, 1), (64, 4, 1, 1),
-                                          (50, 32, 32, 1), (129, 60, 5, 0), (0, 8, 2, 1)])
+                                          (50, 32, 32, 1), (129, 60, 5, 0), (0, 8, 2, 1),
+                                          # E not a multiple of the lane's chunk: one load per logit
+                                          (513, 130, 9, 0), (300, 7, 7, 1),
+                                          # more picks than lanes per token: several slots per lane
+                                          (1000, 64, 16, 1), (16384, 128, 8, 1)])
 def test_route_topk(ops, T, E, K, renorm):
     say("route", T, E, K, renorm)
     rng = np.random.default_rng(T * 7 + E)
@@ -39,6 +43,29 @@ def test_route_topk(ops, T, E, K, renorm):
     ids, w = ops.route_topk(dev(torch.from_numpy(l)), K, renormalize=bool(renorm))
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=W_RTOL, atol=1e-30)
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (128, 8), (200, 20)])
+def test_route_topk_signed_zeros_and_infinities(ops, E, K):
+    """-0 and +0 are equal logits (the lower expert first), -inf logits are
+    picked after every finite one and among themselves by index, and a row
+    of only -inf picks the K lowest experts with NaN weights, as the oracle
+    does."""
+    say("route special", E, K)
+    rng = np.random.default_rng(E)
+    T = 96
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    l[0::4, ::2] = 0.0
+    l[0::4, 1::2] = -0.0
+    l[1::4, : E - K // 2] = -np.inf             # fewer finite logits than picks
+    l[2::4] = -np.inf
+    l[3::4, ::3] = np.float32(3.0)
+    ids_ref, w_ref = orc.route_topk(l, K)
+    ids, w = ops.route_topk(dev(torch.from_numpy(l)), K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_array_equal(ids_ref[2], np.arange(K))
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=W_RTOL, atol=1e-30)
 
 
