@@ -414,17 +414,10 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
 // k-elements of the activation fragments.  Empty groups store zeros.
 constexpr int WG_STAGES = 4;
 
-// Tile queues of the weight-gradient kernel, per launch slot (the host hands
-// out the slots in turn, so launches in flight together use different
-// ones): kQueues tile counters.  A one-wavefront kernel zeroes the slot on
-// the launch's stream right before every launch, so no count carries over
-// from an earlier launch, not even from one that ended part-way.
-constexpr int kQueues = 8, kSlots = 64;
-__device__ uint32_t g_wgrad_sched[kSlots][kQueues];
-
-__global__ void __launch_bounds__(64) wgrad_sched_reset_kernel(int slot) {
-  if (threadIdx.x < kQueues) g_wgrad_sched[slot][threadIdx.x] = 0u;
-}
+// Tile queues of the weight-gradient kernel: one slot of tile_queue.h's
+// words per launch (the host hands out epochs and slots in turn, so launches
+// in flight together use different slots).
+__device__ tq::Slots g_wgrad_sched = tq::initial_slots();
 
 template <int OUT>
 __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
@@ -563,38 +556,9 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
     }
   };
 
-  // Dynamic tile queues.  Queue q holds the groups of rank k nq + q for even
-  // k and k nq + nq - 1 - q for odd k (k = 0, 1, ...: a snake over the
-  // ranks, so every queue gets a share of large and small groups), each
-  // group's tiles in a row, largest group first.  A workgroup takes tiles
-  // from queue blockIdx % nq - its XCD's, as blocks are dealt round-robin
-  // to the 8 XCDs, so a group's tiles share that XCD's L2 - and, once that
-  // is empty, from the others, so no workgroup idles while tiles remain.
-  // Taking a tile is one atomic increment of the queue's counter.
-  __shared__ int32_t s_tile[2];
-  const int nq = min(kQueues, (int)gridDim.x);
-  const int myq = (int)(blockIdx.x % nq);
-  uint32_t* ctr = g_wgrad_sched[a.sched_slot];
-  int parity = 0;
-  for (int qq = 0; qq < nq; ++qq) {
-    const int q = (myq + qq) % nq;
-    // groups in queue q: one per full round of nq ranks, plus one from the
-    // last, partial round if its direction reaches q
-    const int rounds = a.G / nq, left = a.G % nq;
-    const int ngroups = rounds + (((rounds & 1) ? nq - 1 - q : q) < left ? 1 : 0);
-    const int64_t ntiles = (int64_t)ngroups * per_group;
-    for (;;) {
-      // thread 0 takes the next tile; the two slots alternate, so a slot is
-      // rewritten only after the barrier that follows every thread's read
-      if (threadIdx.x == 0) s_tile[parity] = (int32_t)atomicAdd(&ctr[q], 1u);
-      __syncthreads();
-      const int64_t t = s_tile[parity];
-      parity ^= 1;
-      if (t >= ntiles) break;
-      const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
-      process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
-    }
-  }
+  // Dynamic tile queues (tq_walk): groups by size rank, largest first, each
+  // group's tiles in a row; taking a tile is one atomic add.
+  tq_walk(g_wgrad_sched.w[a.sched_slot], a.sched_epoch, a.sched_next, a.G, per_group, process);
 }
 
 // Packs W [G, rows_b, K] (rows_b = N, or 2f for SwiGLU) into the tile-stage
@@ -700,17 +664,20 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
 
 // bf16, ragged-K: the weight gradients
 moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s) {
-  static std::atomic<uint32_t> next_slot{0};
+  static std::atomic<uint64_t> launches{0};
   GGArgs b = a;
-  b.sched_slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % fwd::kSlots);
   b.n_tiles = (a.N + fwd::BN - 1) / fwd::BN;
   b.p_tiles = (a.M + fwd::BM - 1) / fwd::BM;
   const int64_t max_tiles = (int64_t)a.G * b.n_tiles * b.p_tiles;
+  if (max_tiles > tq::kMaxTiles) return MOE_ERR_INVALID_ARG;   // the queue counts' range
+  const uint64_t n = launches.fetch_add(1u, std::memory_order_relaxed);
+  b.sched_slot = tq::launch_slot(n);
+  b.sched_epoch = tq::launch_epoch(n);
+  b.sched_next = tq::slot_next_epoch(n);
   int64_t grid = moe_host::device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
-  hipLaunchKernelGGL(fwd::wgrad_sched_reset_kernel, dim3(1), dim3(64), 0, s, b.sched_slot);
   if (out_f32) {
     hipLaunchKernelGGL((fwd::gg_wgrad_kernel<MOE_OUT_F32>), g, t, 0, s, b);
   } else {

@@ -2,6 +2,7 @@
 // group prefix (the tile scheduler's input), tile-order helpers, stores.
 #pragma once
 #include "common.h"
+#include "tile_queue.h"
 
 namespace moe {
 
@@ -21,13 +22,68 @@ struct GGArgs {
   int G, M, N, K;
   int n_tiles;             // tiles along n (ragged-M) / q (ragged-K)
   int p_tiles;             // ragged-K: tiles along p (rows of C[g])
-  int sched_slot;          // ragged-K: the launch's slot of tile-queue counters
+  int sched_slot;          // ragged-K: the launch's slot of tile-queue words
+  uint32_t sched_epoch;    // ragged-K: the launch's epoch (tile_queue.h)
+  uint32_t sched_next;     // ragged-K: the epoch of the slot's next launch
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // wavefront index as a scalar (uniform) value
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ----------------------------------------------------------------- tile queues
+// One tile-queue word in device memory, for tq::take / tq::finish.
+struct DeviceWord {
+  uint32_t* p;
+  __device__ uint32_t add1() { return atomicAdd(p, 1u); }
+  __device__ uint32_t cas(uint32_t expected, uint32_t desired) { return atomicCAS(p, expected, desired); }
+};
+
+// One workgroup's walk over a launch's tile queues (per_group tiles per
+// group, G groups dealt to the queues in a snake over the size ranks: queue
+// q holds ranks k nq + q for even k and k nq + nq - 1 - q for odd k, so
+// every queue gets a share of large and small groups).  Its own queue
+// blockIdx % nq first - blocks are dealt round-robin to the 8 XCDs, so a
+// queue's tiles share one XCD's L2 - and then the others, so no workgroup
+// idles while tiles remain.  process(rank, tile) runs with the whole
+// workgroup.  Thread 0 takes; the two s_tile entries alternate, so one is
+// rewritten only after the barrier that follows every thread's read of it.
+// Thread 0 of the last workgroup to finish presets the slot for its next
+// launch (tile_queue.h).
+template <class F>
+__device__ __forceinline__ void tq_walk(uint32_t* slot, uint32_t epoch, uint32_t next_epoch, int G,
+                                        int per_group, F&& process) {
+  __shared__ int32_t s_tile[2];
+  const int nq = min(tq::kQueues, (int)gridDim.x);
+  const int myq = (int)(blockIdx.x % nq);
+  int parity = 0;
+  for (int qq = 0; qq < nq; ++qq) {
+    const int q = (myq + qq) % nq;
+    const int rounds = G / nq, left = G % nq;
+    const int ngroups = rounds + (((rounds & 1) ? nq - 1 - q : q) < left ? 1 : 0);
+    const int64_t ntiles = (int64_t)ngroups * per_group;
+    for (;;) {
+      if (threadIdx.x == 0) {
+        DeviceWord w{slot + q};
+        s_tile[parity] = (int32_t)tq::take(w, epoch);
+      }
+      __syncthreads();
+      const int64_t t = s_tile[parity];
+      parity ^= 1;
+      if (t >= ntiles) break;
+      const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
+      process(k * nq + ((k & 1) ? nq - 1 - q : q), rem);
+    }
+  }
+  if (threadIdx.x == 0) {
+    DeviceWord done{slot + tq::kQueues};
+    if (tq::finish(done, epoch, gridDim.x)) {
+#pragma unroll
+      for (int i = 0; i < tq::kWords; ++i) atomicExch(slot + i, tq::word(next_epoch, 0u));
+    }
+  }
+}
 
 // ----------------------------------------------------------------- group prefix
 template <int THREADS>

@@ -522,14 +522,8 @@ __global__ __launch_bounds__(256) void pack_mx_kernel(const uint8_t* __restrict_
 // empty group stores zeros.  Tiles come from dynamic queues as in the bf16
 // weight gradient: groups ranked largest first (each workgroup ranks them
 // into a 2 KB LDS table), dealt to the queues in a snake over the ranks.
-// The queue counters of each launch slot are zeroed by a one-wavefront
-// kernel on the launch's stream right before the launch.
-constexpr int kWgQueues = 8, kWgSlots = 64;
-__device__ uint32_t g_wgrad_mx_sched[kWgSlots][kWgQueues];
-
-__global__ void __launch_bounds__(64) wgrad_mx_sched_reset_kernel(int slot) {
-  if (threadIdx.x < kWgQueues) g_wgrad_mx_sched[slot][threadIdx.x] = 0u;
-}
+// The queues are tile_queue.h's epoch-tagged words, one slot per launch.
+__device__ tq::Slots g_wgrad_mx_sched = tq::initial_slots();
 
 __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[MSTAGE];
@@ -537,7 +531,6 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b2[MSTAGE];
   __shared__ __align__(1024) uint8_t b3[MSTAGE];
   __shared__ __align__(1024) uint8_t xch[NXCH * XCH_BYTES];
-  __shared__ int32_t s_tile[2];
   __shared__ uint16_t by_rank[1024];   // group of each rank, largest first (ties: lower index first)
 
   const int P = a.M, Q = a.N;
@@ -614,25 +607,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
   };
 
   __syncthreads();
-  const int nq = min(kWgQueues, (int)gridDim.x);
-  const int myq = (int)(blockIdx.x % nq);
-  uint32_t* ctr = g_wgrad_mx_sched[a.sched_slot];
-  int parity = 0;
-  for (int qq = 0; qq < nq; ++qq) {
-    const int q = (myq + qq) % nq;
-    const int rounds = a.G / nq, left = a.G % nq;
-    const int ngroups = rounds + (((rounds & 1) ? nq - 1 - q : q) < left ? 1 : 0);
-    const int64_t ntiles = (int64_t)ngroups * per_group;
-    for (;;) {
-      if (threadIdx.x == 0) s_tile[parity] = (int32_t)atomicAdd(&ctr[q], 1u);
-      __syncthreads();
-      const int64_t t = s_tile[parity];
-      parity ^= 1;
-      if (t >= ntiles) break;
-      const int k = (int)(t / per_group), rem = (int)(t - (int64_t)k * per_group);
-      process(by_rank[k * nq + ((k & 1) ? nq - 1 - q : q)], rem);
-    }
-  }
+  tq_walk(g_wgrad_mx_sched.w[a.sched_slot], a.sched_epoch, a.sched_next, a.G, per_group,
+          [&](int rank, int rem) { process(by_rank[rank], rem); });
 }
 
 }  // namespace mx
@@ -663,16 +639,19 @@ moe_status_t launch_pack_mx_weights(const uint8_t* q, const uint8_t* sc, int G, 
 }
 
 moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s) {
-  static std::atomic<uint32_t> next_slot{0};
+  static std::atomic<uint64_t> launches{0};
   GGArgs b = a;
   b.n_tiles = (a.N + fwd::BN - 1) / fwd::BN;
   b.p_tiles = (a.M + fwd::BM - 1) / fwd::BM;
-  b.sched_slot = (int)(next_slot.fetch_add(1u, std::memory_order_relaxed) % fwd::mx::kWgSlots);
   const int64_t max_tiles = (int64_t)a.G * b.n_tiles * b.p_tiles;
+  if (max_tiles > tq::kMaxTiles) return MOE_ERR_INVALID_ARG;   // the queue counts' range
+  const uint64_t n = launches.fetch_add(1u, std::memory_order_relaxed);
+  b.sched_slot = tq::launch_slot(n);
+  b.sched_epoch = tq::launch_epoch(n);
+  b.sched_next = tq::slot_next_epoch(n);
   int64_t grid = moe_host::device_cu_count();
   if (max_tiles < grid) grid = max_tiles;
   if (grid <= 0) grid = 1;
-  hipLaunchKernelGGL(fwd::mx::wgrad_mx_sched_reset_kernel, dim3(1), dim3(64), 0, s, b.sched_slot);
   hipLaunchKernelGGL(fwd::mx::gg_wgrad_mx_kernel, dim3((unsigned)grid), dim3(fwd::THREADS), 0, s, b);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -196,11 +196,15 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
  *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
  *   Its workgroups take tiles from counters in the library's own device
- *   memory (64 slots handed out in turn; each call first enqueues a small
- *   kernel that zeroes its slot, so a call that ended part-way leaves
- *   nothing behind), so up to 64 such calls may be in flight on one GPU at once;
- *   a captured call keeps its slot on every replay, so one graph must not
- *   be replayed on two streams concurrently.  Each tile is computed by one
+ *   memory (64 slots handed out in turn, each call tagged with its own
+ *   epoch: counts left in a slot by another call, one that ended part-way
+ *   included, count as zero, and the call's last workgroup presets the slot
+ *   for the slot's next call when it finishes), so up to 64 such calls may
+ *   be in flight on one GPU at once; a captured call keeps its slot and
+ *   epoch on every replay, so one graph must not be replayed on two streams
+ *   concurrently.  A call of more than 2^22 output tiles (G ceil(M/256)
+ *   ceil(N/256); an output that fits in memory has fewer) returns
+ *   MOE_ERR_INVALID_ARG.  Each tile is computed by one
  *   workgroup in a fixed order: results are bitwise reproducible.
  *   dtype = MOE_DTYPE_MXFP8 (the group-aware MXFP8 weight gradient): A and
  *   B are the outputs of mxfp8_quantize_transposed (grouped) for the same

@@ -368,6 +368,56 @@ def test_grouped_gemm_wgrad_queues(ops):
             assert torch.equal(out, first)
 
 
+def test_grouped_gemm_wgrad_graph_replay_and_slot_wrap(ops):
+    """The weight gradients' tile queues carry each call's epoch and are
+    zeroed by the call's last workgroup: a captured call (whose epoch repeats
+    on every replay) replayed with eager calls in between, and 140 eager
+    calls in a row (every one of the 64 slots reused twice), all equal the
+    first eager result bit for bit, in bf16 and in MXFP8."""
+    rng = np.random.default_rng(131)
+    sizes = np.concatenate([[700, 0], rng.integers(0, 90, 21)]).astype(np.int32)
+    G, M = sizes.size, int(sizes.sum())
+    say("gg wgrad graph + slots", G, M)
+    P, Q = 136, 264
+    Xh, Yh = bf16(rng, M + 3, P), bf16(rng, M + 3, Q)
+    X, Y = dev(Xh), dev(Yh)
+    S = dev(torch.from_numpy(sizes))
+    ref = orc.grouped_wgrad(Xh[:M], Yh[:M], sizes)
+    XqT, XsT = ops.mxfp8_quantize_transposed(X, S)
+    YqT, YsT = ops.mxfp8_quantize_transposed(Y, S)
+    calls = {"bf16": lambda: ops.grouped_gemm_wgrad(X, Y, S),
+             "mxfp8": lambda: ops.grouped_gemm_wgrad_mxfp8(XqT, XsT, YqT, YsT, S, M + 3)}
+    for name, call in calls.items():
+        eager = call()
+        torch.cuda.synchronize()
+        if name == "bf16":
+            assert max_rel_err(eager, ref) <= BF16_TOL
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            call()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            out = call()
+        for rep in range(4):
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), (name, rep)
+            between = call()
+            torch.cuda.synchronize()
+            assert torch.equal(between, eager), (name, rep)
+        for i in range(140):
+            got = call()
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), name
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), name
+
+
 # ------------------------------------------------------------------- MXFP8
 
 @pytest.mark.parametrize("R,C", [(300, 256), (1, 32), (1000, 7168 // 4)])

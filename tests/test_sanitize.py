@@ -1,7 +1,9 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only):
 the oracle (oracle/oracle.c) on a tiny layer with edge cases, and the C ABI's
 argument checks (csrc/abi.cpp linked against stub launchers, so no kernel
-runs), including sizes at the ends of their types.  Built with the host
+runs), including sizes at the ends of their types, and the ragged-K
+tile-queue protocol (csrc/tile_queue.h) on host threads, under ASan/UBSan
+and under ThreadSanitizer.  Built with the host
 compilers (gcc / g++); no GPU code is compiled or run."""
 import os
 import shutil
@@ -45,3 +47,15 @@ def test_abi_host_checks_under_asan_ubsan(tmp_path):
                            os.path.join(HERE, "abi_host_checks.cpp"), "-L" + os.path.join(ROCM, "lib"),
                            "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe])
     assert "ok: 0 checks failed" in _run(exe, tmp_path)
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+@pytest.mark.parametrize("san", [SAN, ["-g", "-O1", "-fsanitize=thread"]], ids=["asan_ubsan", "tsan"])
+def test_tile_queue_epochs(tmp_path, san):
+    exe = str(tmp_path / "tq_san")
+    subprocess.check_call(["g++", "-std=c++17", *san, "-pthread", "-D__HIP_PLATFORM_AMD__",
+                           "-I" + os.path.join(ROCM, "include"),
+                           "-I" + os.path.join(ROOT, "dropless_moe_expert_amd", "csrc"),
+                           os.path.join(HERE, "tile_queue_check.cpp"), "-o", exe])
+    out = _run(exe, tmp_path)
+    assert "ok: 0 checks failed" in out and "ThreadSanitizer" not in out, out
