@@ -338,6 +338,39 @@ def test_grouped_gemm_wgrad(ops, P, Q):
         assert torch.all(out[g] == 0)
 
 
+@pytest.mark.parametrize("P,Q,out_dtype", [(256, 256, "bf16"), (512, 768, "bf16"), (512, 264, "f32")])
+def test_grouped_gemm_wgrad_many_groups(ops, P, Q, out_dtype):
+    """300 groups, most of one or two stages, runs of empty groups between
+    and at the ends, and one long group: every group against the oracle on
+    its own scale (so a short group's error shows), empty ones exactly
+    zero, and a repeat bit for bit.  Full 256 x 256 tiles and a partial
+    column tile; bf16 and fp32 outputs."""
+    rng = np.random.default_rng(P * 7 + Q)
+    sizes = rng.integers(0, 41, 300).astype(np.int32)
+    sizes[rng.random(300) < 0.25] = 0
+    sizes[:3] = 0
+    sizes[-4:] = 0
+    sizes[150] = 2000
+    sizes[151:160] = 0
+    G, M = sizes.size, int(sizes.sum())
+    say("gg wgrad many groups", P, Q, out_dtype, G, M)
+    X, Y = bf16(rng, M + 5, P), bf16(rng, M + 5, Q)
+    ref = orc.grouped_wgrad(X[:M], Y[:M], sizes)
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    S = dev(torch.from_numpy(sizes))
+    out = ops.grouped_gemm_wgrad(dev(X), dev(Y), S, out_dtype=dt)
+    again = ops.grouped_gemm_wgrad(dev(X), dev(Y), S, out_dtype=dt)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    got = out.float().cpu().numpy().astype(np.float64)
+    want = orc.bf16_to_f64(ref)
+    for g in range(G):
+        if sizes[g] == 0:
+            assert not np.any(got[g]), g
+        else:   # each group against its own scale, so a short group's error shows
+            assert np.abs(got[g] - want[g]).max() <= BF16_TOL * np.abs(want[g]).max(), g
+
+
 def test_grouped_gemm_wgrad_queues(ops):
     # The weight-gradient kernel takes tiles from per-launch counters that its
     # last workgroup resets: consecutive launches of different shapes (a grid
