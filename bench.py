@@ -797,7 +797,20 @@ def main() -> int:
     dst = torch.empty_like(src)
     ms = ctimer(lambda: dst.copy_(src))
     ceil["hbm_copy_gbs"] = round(2 * src.numel() * 2 / (ms * 1e-3) / 1e9, 1)
-    del src, dst
+    # the cold rates the bandwidth kernels are read against: plain device
+    # copies (bytes read + written) and a write-only fill, each timed right
+    # after the same 1 GiB scrub as the kernels' cold timings
+    for mib in (64, 256, 1024):
+        n = (mib << 20) // 4   # int16 elements per side: half the bytes moved are reads
+        a_, b_ = src[:n], dst[:n]
+        ms = ctimer.cold(lambda: b_.copy_(a_))
+        ceil[f"hbm_copy_cold_gbs_{mib}MiB_moved"] = round(2 * n * 2 / (ms * 1e-3) / 1e9, 1)
+    fill = dst[: (512 << 20) // 2]
+    ms = ctimer(lambda: fill.fill_(7))
+    ceil["hbm_fill_gbs_512MiB"] = round(fill.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    ms = ctimer.cold(lambda: fill.fill_(7))
+    ceil["hbm_fill_cold_gbs_512MiB"] = round(fill.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del src, dst, fill
     roofline["measured_mfma_ceiling"] = ceil["mfma_bf16_random_operands_tflops"]
     roofline["frac_of_measured_ceiling"] = round(gg1_tflops / ceil["mfma_bf16_random_operands_tflops"], 4)
     log(f"ceilings: {ceil}")

@@ -60,14 +60,49 @@ def _mean(xs):
 
 
 def _copy_scale(disp, counter):
-    vals = [d[counter] for d in disp.values() if "copyBuffer" in d["name"] and d.get(counter)
-            and d[counter] > COPY_KIB / 4]
-    return COPY_KIB / _mean(vals) if vals else None
+    """COPY_KIB over what the counter reads for the run's 1 GiB copies: the
+    largest device copies of the run (within 5 % of the largest reading),
+    so that smaller copies in the same run do not enter the mean."""
+    vals = [d[counter] for d in disp.values() if "copyBuffer" in d["name"] and d.get(counter)]
+    if not vals:
+        return None
+    top = max(vals)
+    return COPY_KIB / _mean(v for v in vals if v >= 0.95 * top)
 
 
 def short(name: str) -> str:
     name = name.replace("|", "/")
     return name if len(name) <= 90 else name[:87] + "..."
+
+
+def calibration(args) -> str:
+    """Per-dispatch table of the counter passes of counter_calibration.py:
+    each kernel's reading against the bytes it reads and writes."""
+    lines = [f"# {args.title}", "", "Commands (from the repository root), one counter pass each:", ""]
+    lines += ["    " + c for c in args.command] + [""]
+    rows = collections.OrderedDict()
+    for path in (args.fetch, args.write, args.mfma):
+        if not path:
+            continue
+        for i, d in enumerate(_dispatches(path).values()):
+            r = rows.setdefault(i, {"name": d["name"]})
+            r.update({k: v for k, v in d.items() if k.isupper()})
+    sizes = [int(x) for x in args.sizes.split(",")]
+    lines.append("| dispatch | kernel | MiB read and written | FETCH_SIZE MiB | read / FETCH_SIZE | WRITE_SIZE MiB | "
+                 "written / WRITE_SIZE |")
+    lines.append("|---|---|---|---|---|---|---|")
+    si = -1
+    for i, r in rows.items():
+        if "Fill" in r["name"]:   # each size starts with the fill of its source
+            si += 1
+            continue
+        if si < 0 or ("copyBuffer" not in r["name"] and "elementwise" not in r["name"]):
+            continue
+        mib = sizes[min(si, len(sizes) - 1)]
+        f, w = r.get("FETCH_SIZE", 0) / 1024, r.get("WRITE_SIZE", 0) / 1024
+        lines.append(f"| {i} | `{short(r['name'])}` | {mib} | {f:.1f} | {mib / f if f else float('nan'):.3f} | "
+                     f"{w:.1f} | {mib / w if w else float('nan'):.3f} |")
+    return "\n".join(lines) + "\n"
 
 
 def summarise(args) -> str:
@@ -148,8 +183,11 @@ def main(argv=None) -> int:
     ap.add_argument("--write", help="CSV of WRITE_SIZE")
     ap.add_argument("--json", help="write the named kernel's figures here")
     ap.add_argument("--json-kernel")
+    ap.add_argument("--calibration", action="store_true",
+                    help="per-dispatch table of counter_calibration.py's copies (--sizes: MiB per side, in order)")
+    ap.add_argument("--sizes", default="256,1024,2048")
     args = ap.parse_args(argv)
-    sys.stdout.write(summarise(args))
+    sys.stdout.write(calibration(args) if args.calibration else summarise(args))
     return 0
 
 
