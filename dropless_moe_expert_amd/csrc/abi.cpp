@@ -234,6 +234,8 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   if (!d) return MOE_ERR_INVALID_ARG;
   if (d->G < 1 || d->G > 1024 || d->N < 1 || d->m_cap < 0) return MOE_ERR_INVALID_ARG;
   if (d->m_cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // a 256-row output tile is addressed by 32-bit offsets from its first row
+  if (d->N > (1 << 22)) return MOE_ERR_UNSUPPORTED;
   if (!A || !B || !C || !group_sizes) return MOE_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MOE_ERR_ALIGNMENT;
   if (C_aux && d->epilogue != MOE_EPI_SWIGLU_MXFP8 && !aligned16(C_aux)) return MOE_ERR_ALIGNMENT;

@@ -218,13 +218,31 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < BM * UR; c += THREADS) {
-    const int row = c / UR, u = c - row * UR;
-    const int col = n0 + 8 * u;
-    if (row < rows && col < ncols) {
+  // the thread's LDS reads four at a time ahead of their stores, so the
+  // reads overlap instead of each store waiting for its own read
+  constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
+  constexpr int NB = 4;
+  // the tile's rows start at a uniform base; a piece is a 32-bit offset
+  // from it (256 rows of at most 2^22 bf16 columns)
+  uint8_t* const cbase = a.C + m0 * (int64_t)ncols * 2;
+  static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
+#pragma unroll 1
+  for (int k0 = 0; k0 < NPT; k0 += NB) {   // rolled: per-piece addresses stay local to the epilogue
+    uint4 v[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int c = threadIdx.x + (k0 + k) * THREADS;
+      const int row = c / UR, u = c - row * UR;
       const int rl = row % WTM;
-      const uint4 v = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
-      *reinterpret_cast<uint4*>(a.C + ((m0 + row) * (int64_t)ncols + col) * 2) = v;
+      v[k] = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int c = threadIdx.x + (k0 + k) * THREADS;
+      const int row = c / UR, u = c - row * UR;
+      const int col = n0 + 8 * u;
+      if (row < rows && col < ncols)
+        *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ncols + col) * 2u) = v[k];
     }
   }
 }

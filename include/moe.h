@@ -224,7 +224,8 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   [m_cap, f/32]; f % 32 == 0; packed weights are those packed for
  *   MOE_EPI_SWIGLU.  Rows r >= sum(s_g) are not written.
  * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
- * Limits: G <= 1024; bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
+ * Limits: G <= 1024; N <= 2^22 (else MOE_ERR_UNSUPPORTED);
+ *   bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
  *   MXFP8: K % 128 == 0 (RAGGED_M), K % 64 == 0 and K >= m_cap + 63 G
  *   (RAGGED_K).  A, B, C 16-byte aligned; scales 4-byte aligned.
  * dtype = MOE_DTYPE_MXFP4 (RAGGED_M, B_NK, bf16 out; the gfx950 analog of

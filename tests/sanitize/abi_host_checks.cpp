@@ -147,6 +147,11 @@ int main() {
   EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_OK);
   d.m_cap = BIG;
   EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
+  d.m_cap = 100;
+  d.N = 1 << 22;   // the widest output the 32-bit tile offsets address
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_OK);
+  d.N = (1 << 22) + 8;
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
   d = {MOE_DTYPE_MXFP8, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, 1024, 64, 64, INT32_MAX - 63, INT32_MAX};
   EXPECT(grouped_gemm(&d, p, u8, p, u8, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_INVALID_ARG);
   d = {MOE_DTYPE_BF16, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, 4, 64, 64, 0, 100};
