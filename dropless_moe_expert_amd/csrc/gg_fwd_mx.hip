@@ -177,12 +177,66 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x16_t (&acc)[MTN][MTM]) 
 // (256 rows x 128 codes, 256 x 4 scales) is assembled in LDS (the stage
 // buffers, free once every wavefront has left the K loop) and written out by
 // the whole workgroup as 16-byte row pieces and 4-byte scale words.
+//
+// The plain bf16 output (down GEMM, data and weight gradients) also leaves
+// through LDS: each wavefront writes its 64 rows into the stage buffer of its
+// row slot (16-byte units XOR-swizzled by row), then the workgroup copies
+// whole 512-byte tile rows out as 16-byte pieces, each thread's LDS reads
+// four at a time ahead of their stores.
 template <int EPI>
 __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM], int64_t m0, int rows, int n0,
-                                      int ncols, int f, uint8_t* lds_codes, uint8_t* lds_scales) {
+                                      int ncols, int f, uint8_t* lds_codes, uint8_t* lds_scales, uint8_t* s2,
+                                      uint8_t* s3) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wn = wave / WM, wm = wave % WM;
   const int r32 = lane & 31, g = lane >> 5;
+  if constexpr (EPI == MOE_EPI_NONE) {
+    constexpr int RB = 512, UR = RB / 16;   // bytes and 16-byte units per staged row
+    auto buf = [&](int i) { return i == 0 ? lds_codes : i == 1 ? lds_scales : i == 2 ? s2 : s3; };
+    __syncthreads();   // every wavefront has read its last stage
+    uint8_t* sb = buf(wm);
+#pragma unroll
+    for (int j = 0; j < MTM; ++j) {
+      const int rl = j * 32 + r32;   // row within the slot
+#pragma unroll
+      for (int i = 0; i < MTN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * WTN + i * 32 + q * 8 + g * 4;
+          const uint2 w = make_uint2(pack_bf16x2(acc[i][j][q * 4], acc[i][j][q * 4 + 1]),
+                                     pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]));
+          *reinterpret_cast<uint2*>(sb + rl * RB + (((col >> 3) ^ (rl % UR)) << 4) + ((col >> 2) & 1) * 8) = w;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
+    constexpr int NB = 4;
+    static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
+    // the tile's rows start at a uniform base; a piece is a 32-bit offset
+    // from it (256 rows of at most 2^22 columns)
+    uint8_t* const cbase = a.C + m0 * (int64_t)ncols * 2;
+#pragma unroll 1
+    for (int k0 = 0; k0 < NPT; k0 += NB) {
+      uint4 v[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int c = threadIdx.x + (k0 + k) * THREADS;
+        const int row = c / UR, u = c - row * UR;
+        const int rl = row % WTM;
+        v[k] = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int c = threadIdx.x + (k0 + k) * THREADS;
+        const int row = c / UR, u = c - row * UR;
+        const int col = n0 + 8 * u;
+        if (row < rows && col < ncols)
+          *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ncols + col) * 2u) = v[k];
+      }
+    }
+    return;
+  }
   if constexpr (EPI == MOE_EPI_SWIGLU_MXFP8) {
     constexpr int TC = BN / 2;   // codes per tile row
     __syncthreads();             // every wavefront has read its last stage
@@ -450,7 +504,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     const MxLoads<PACKED> ld{xl, wl, sl, xbase, wbase, wstride, xsb, wsb, (int)lds_b, (int)lds_b};
     mx_k_loop<PACKED>(ld, nk, acc, b0, b1, b2, b3, xch);
-    store<EPI>(a, acc, m0, rows, n0, SWI ? f : a.N, f, b0, b1);
+    store<EPI>(a, acc, m0, rows, n0, SWI ? f : a.N, f, b0, b1, b2, b3);
   }
 }
 
@@ -603,7 +657,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_mx_kernel(GGArgs a) {
     }
     GGArgs ag = a;
     ag.C = a.C + (int64_t)g * P * Q * 2;
-    store<MOE_EPI_NONE>(ag, acc, p0, rows, q0, Q, 0, b0, b1);
+    store<MOE_EPI_NONE>(ag, acc, p0, rows, q0, Q, 0, b0, b1, b2, b3);
   };
 
   __syncthreads();
