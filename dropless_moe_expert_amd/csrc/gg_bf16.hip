@@ -181,51 +181,66 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
 // row so that the 16 rows one store instruction touches fall on distinct
 // banks; after a barrier the workgroup copies whole tile rows out with
 // 16-byte stores (the direct epilogue writes 32-byte pieces of 16 rows per
-// instruction).  Plain: 256 columns per row (512 bytes); SwiGLU: h, 128
-// columns (256 bytes).
-template <int EPI, int ACT>
+// instruction), each thread's LDS reads four at a time ahead of their
+// stores.  ST_PLAIN: C [., ncols], the tile's 256 columns from n0 (512-byte
+// rows); ST_H: SwiGLU's h, C [., f], 128 columns from n0 (256 bytes);
+// ST_AUX: the pre-activations C_aux [., 2f], the tile's 128 gate columns
+// from n0 then its 128 up columns from f + n0 (512 bytes).
+enum { ST_PLAIN = 0, ST_H = 1, ST_AUX = 2 };
+
+// hp: ST_H takes h already rounded and packed (hp[i][j] for acc[i][j] and
+// acc[i + TN/2][j]) instead of forming it from acc
+template <int MODE, int ACT>
 __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN][TM], int64_t m0, int rows, int n0,
-                                             int ncols, int xrow0, uint8_t* s0, uint8_t* s1, uint8_t* s2,
-                                             uint8_t* s3) {
+                                             int ncols, int f, int xrow0, uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                             uint8_t* s3, const uint2 (*hp)[TM] = nullptr) {
   auto buf = [&](int i) { return i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3; };
-  constexpr bool SWI = EPI == MOE_EPI_SWIGLU;
-  constexpr int RB = SWI ? 256 : 512;   // bytes per staged row
-  constexpr int UR = RB / 16;           // 16-byte units per row
+  constexpr int RB = MODE == ST_H ? 256 : 512;   // bytes per staged row
+  constexpr int UR = RB / 16;                    // 16-byte units per row
   const int lane = threadIdx.x & 63;
   int wn, wm;
   wave_pos(wn, wm);
   const int r16 = lane & 15, g4 = lane >> 4;
   uint8_t* sb = buf(xrow0 / WTM);
+  auto put = [&](int rl, int col, uint2 w) {
+    const int u = col >> 3, half = (col >> 2) & 1;
+    *reinterpret_cast<uint2*>(sb + rl * RB + ((u ^ (rl % UR)) << 4) + half * 8) = w;
+  };
+  auto pack4 = [](const f32x4_t& v) { return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])); };
 #pragma unroll
   for (int j = 0; j < ACT; ++j) {
     const int rl = j * 16 + r16;   // row within the slot
+    if constexpr (MODE == ST_PLAIN) {
 #pragma unroll
-    for (int i = 0; i < (SWI ? TN / 2 : TN); ++i) {
-      uint2 w;
-      int col;
-      if constexpr (SWI) {
-        f32x4_t h;
+      for (int i = 0; i < TN; ++i) put(rl, wn * WTN + i * 16 + g4 * 4, pack4(acc[i][j]));
+    } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = silu_f32(acc[i][j][q]) * acc[i + TN / 2][j][q];
-        w = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-        col = wn * (WTN / 2) + i * 16 + g4 * 4;
-      } else {
-        w = make_uint2(pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3]));
-        col = wn * WTN + i * 16 + g4 * 4;
+      for (int i = 0; i < TN / 2; ++i) {
+        const int col = wn * (WTN / 2) + i * 16 + g4 * 4;
+        if constexpr (MODE == ST_H) {
+          if (hp) {
+            put(rl, col, hp[i][j]);
+          } else {
+            f32x4_t h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = silu_f32(acc[i][j][q]) * acc[i + TN / 2][j][q];
+            put(rl, col, pack4(h));
+          }
+        } else {
+          put(rl, col, pack4(acc[i][j]));                  // gate
+          put(rl, BN / 2 + col, pack4(acc[i + TN / 2][j]));  // up
+        }
       }
-      const int u = col >> 3, half = (col >> 2) & 1;
-      *reinterpret_cast<uint2*>(sb + rl * RB + ((u ^ (rl % UR)) << 4) + half * 8) = w;
     }
   }
   __syncthreads();
-  // the thread's LDS reads four at a time ahead of their stores, so the
-  // reads overlap instead of each store waiting for its own read
   constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
   constexpr int NB = 4;
+  static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
   // the tile's rows start at a uniform base; a piece is a 32-bit offset
   // from it (256 rows of at most 2^22 bf16 columns)
-  uint8_t* const cbase = a.C + m0 * (int64_t)ncols * 2;
-  static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
+  const int ld = MODE == ST_PLAIN ? ncols : MODE == ST_H ? f : 2 * f;
+  uint8_t* const cbase = (MODE == ST_AUX ? a.Caux : a.C) + m0 * (int64_t)ld * 2;
 #pragma unroll 1
   for (int k0 = 0; k0 < NPT; k0 += NB) {   // rolled: per-piece addresses stay local to the epilogue
     uint4 v[NB];
@@ -240,9 +255,16 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
     for (int k = 0; k < NB; ++k) {
       const int c = threadIdx.x + (k0 + k) * THREADS;
       const int row = c / UR, u = c - row * UR;
-      const int col = n0 + 8 * u;
-      if (row < rows && col < ncols)
-        *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ncols + col) * 2u) = v[k];
+      int col, lim;
+      if constexpr (MODE == ST_AUX) {
+        const int uh = u % (UR / 2);
+        col = (u < UR / 2 ? 0 : f) + n0 + 8 * uh;
+        lim = (u < UR / 2 ? 0 : f) + f;
+      } else {
+        col = n0 + 8 * u;
+        lim = MODE == ST_PLAIN ? ncols : f;
+      }
+      if (row < rows && col < lim) *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ld + col) * 2u) = v[k];
     }
   }
 }
@@ -399,8 +421,26 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       if (s + 1 < nk) iter(b1, b0, s + 1);
       if (s + 2 < nk) iter(b2, b1, s + 2);
       if (s + 3 < nk) iter(b3, b2, s + 3);
-      if constexpr (OUT == MOE_OUT_BF16 && EPI != EPI_SWIGLU_AUX) {
-        store_staged<EPI, ACT>(a, acc, m0, rows, n0, EPI == MOE_EPI_SWIGLU ? f : a.N, xrow0, b0, b1, b2, b3);
+      if constexpr (OUT == MOE_OUT_BF16 && EPI == EPI_SWIGLU_AUX) {
+        // h formed and packed first, so the accumulators are free once the
+        // pre-activations are in LDS; then (once every thread has read
+        // those out) h
+        uint2 hp[TN / 2][TM];
+#pragma unroll
+        for (int j = 0; j < ACT; ++j)
+#pragma unroll
+          for (int i = 0; i < TN / 2; ++i) {
+            f32x4_t h;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) h[q] = silu_f32(acc[i][j][q]) * acc[i + TN / 2][j][q];
+            hp[i][j] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          }
+        store_staged<ST_AUX, ACT>(a, acc, m0, rows, n0, 0, f, xrow0, b0, b1, b2, b3);
+        __syncthreads();
+        store_staged<ST_H, ACT>(a, acc, m0, rows, n0, 0, f, xrow0, b0, b1, b2, b3, hp);
+      } else if constexpr (OUT == MOE_OUT_BF16) {
+        store_staged<EPI == MOE_EPI_SWIGLU ? ST_H : ST_PLAIN, ACT>(a, acc, m0, rows, n0, a.N, f, xrow0, b0, b1, b2,
+                                                                  b3);
       } else {
         store<EPI, OUT, ACT>(a, acc, m0, rows, n0, is_swiglu(EPI) ? f : a.N, f, xrow0);
       }
@@ -556,7 +596,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_wgrad_kernel(GGArgs a) {
       GGArgs ag = a;
       ag.C = a.C + (int64_t)g * P * Q * (OUT == MOE_OUT_F32 ? 4 : 2);
       if constexpr (OUT == MOE_OUT_BF16) {
-        store_staged<MOE_EPI_NONE, ACT>(ag, acc, p0, rows, q0, Q, xrow0, b0, b1, b2, b3);
+        store_staged<ST_PLAIN, ACT>(ag, acc, p0, rows, q0, Q, 0, xrow0, b0, b1, b2, b3);
       } else {
         store<MOE_EPI_NONE, OUT, ACT>(ag, acc, p0, rows, q0, Q, 0, xrow0);
       }
