@@ -177,6 +177,44 @@ __device__ __forceinline__ void mma(const Frags& fr, f32x16_t (&acc)[MTN][MTM]) 
 // (256 rows x 128 codes, 256 x 4 scales) is assembled in LDS (the stage
 // buffers, free once every wavefront has left the K loop) and written out by
 // the whole workgroup as 16-byte row pieces and 4-byte scale words.
+// Copies a tile staged in LDS out to global memory: row r (r < rows) of the
+// tile lies in buffer r / WTM at (r % WTM) * RB, its 16-byte units u XOR-
+// swizzled by (r % WTM) % UR; the first half of a row's units goes to
+// columns col_a + 8u (those < lim_a), the second half to col_b + 8(u - UR/2)
+// (those < lim_b), of rows ld bf16 elements apart from cbase.  Each
+// thread's LDS reads go four at a time ahead of their stores, in a rolled
+// loop; a piece is a 32-bit offset from cbase (256 rows of at most 2^22
+// columns).
+template <int RB>
+__device__ __forceinline__ void copy_staged(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3, uint8_t* cbase,
+                                            int ld, int rows, int col_a, int lim_a, int col_b, int lim_b) {
+  constexpr int UR = RB / 16;
+  constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
+  constexpr int NB = 4;
+  static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
+  auto buf = [&](int i) { return i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3; };
+#pragma unroll 1
+  for (int k0 = 0; k0 < NPT; k0 += NB) {
+    uint4 v[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int c = threadIdx.x + (k0 + k) * THREADS;
+      const int row = c / UR, u = c - row * UR;
+      const int rl = row % WTM;
+      v[k] = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int c = threadIdx.x + (k0 + k) * THREADS;
+      const int row = c / UR, u = c - row * UR;
+      const bool first = u < UR / 2;
+      const int col = first ? col_a + 8 * u : col_b + 8 * (u - UR / 2);
+      if (row < rows && col < (first ? lim_a : lim_b))
+        *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ld + col) * 2u) = v[k];
+    }
+  }
+}
+
 //
 // The plain bf16 output (down GEMM, data and weight gradients) also leaves
 // through LDS: each wavefront writes its 64 rows into the stage buffer of its
@@ -210,31 +248,8 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
       }
     }
     __syncthreads();
-    constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
-    constexpr int NB = 4;
-    static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
-    // the tile's rows start at a uniform base; a piece is a 32-bit offset
-    // from it (256 rows of at most 2^22 columns)
-    uint8_t* const cbase = a.C + m0 * (int64_t)ncols * 2;
-#pragma unroll 1
-    for (int k0 = 0; k0 < NPT; k0 += NB) {
-      uint4 v[NB];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const int c = threadIdx.x + (k0 + k) * THREADS;
-        const int row = c / UR, u = c - row * UR;
-        const int rl = row % WTM;
-        v[k] = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
-      }
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        const int c = threadIdx.x + (k0 + k) * THREADS;
-        const int row = c / UR, u = c - row * UR;
-        const int col = n0 + 8 * u;
-        if (row < rows && col < ncols)
-          *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ncols + col) * 2u) = v[k];
-      }
-    }
+    copy_staged<RB>(lds_codes, lds_scales, s2, s3, a.C + m0 * (int64_t)ncols * 2, ncols, rows, n0, ncols,
+                    n0 + BN / 2, ncols);
     return;
   }
   if constexpr (EPI == MOE_EPI_SWIGLU_MXFP8) {
@@ -289,41 +304,61 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x16_t (&acc)[MTN][MTM]
     }
     return;
   }
+  // SwiGLU without quantisation: h (and, with C_aux, the pre-activations
+  // [gate | up] for the backward) staged through LDS as the plain output
+  // is.  h is formed and packed first, so the accumulators are free once
+  // the pre-activations are in LDS.
+  if constexpr (EPI == MOE_EPI_SWIGLU) {
+  auto buf = [&](int i) { return i == 0 ? lds_codes : i == 1 ? lds_scales : i == 2 ? s2 : s3; };
+  uint8_t* sb = buf(wm);
+  auto put = [&](int rb, int rl, int col, uint2 w) {
+    const int ur = rb / 16;
+    *reinterpret_cast<uint2*>(sb + rl * rb + (((col >> 3) ^ (rl % ur)) << 4) + ((col >> 2) & 1) * 8) = w;
+  };
+  uint2 hp[MTN / 2][MTM][4];
+#pragma unroll
+  for (int j = 0; j < MTM; ++j)
+#pragma unroll
+    for (int i = 0; i < MTN / 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][j][q * 4 + e]) * acc[i + MTN / 2][j][q * 4 + e];
+        hp[i][j][q] = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+      }
+  __syncthreads();   // every wavefront has read its last stage
+  if (a.Caux) {
+#pragma unroll
+    for (int j = 0; j < MTM; ++j) {
+      const int rl = j * 32 + r32;
+#pragma unroll
+      for (int i = 0; i < MTN / 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wn * (WTN / 2) + i * 32 + q * 8 + g * 4;
+          put(512, rl, col, make_uint2(pack_bf16x2(acc[i][j][q * 4], acc[i][j][q * 4 + 1]),
+                                       pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3])));
+          put(512, rl, BN / 2 + col,
+              make_uint2(pack_bf16x2(acc[i + MTN / 2][j][q * 4], acc[i + MTN / 2][j][q * 4 + 1]),
+                         pack_bf16x2(acc[i + MTN / 2][j][q * 4 + 2], acc[i + MTN / 2][j][q * 4 + 3])));
+        }
+    }
+    __syncthreads();
+    copy_staged<512>(lds_codes, lds_scales, s2, s3, a.Caux + m0 * (int64_t)(2 * f) * 2, 2 * f, rows, n0, f,
+                     f + n0, 2 * f);
+    __syncthreads();   // every thread has read the pre-activations out
+  }
 #pragma unroll
   for (int j = 0; j < MTM; ++j) {
-    const int mr = wm * WTM + j * 32 + r32;
-    if constexpr (EPI == MOE_EPI_SWIGLU) {
+    const int rl = j * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < MTN / 2; ++i) {
+    for (int i = 0; i < MTN / 2; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int jc = n0 + wn * (WTN / 2) + i * 32 + q * 8 + g * 4;
-          f32x4_t h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[i][j][q * 4 + e]) * acc[i + MTN / 2][j][q * 4 + e];
-          if (mr < rows && jc < f) {
-            store_sub<MOE_OUT_BF16>(a.C, f, m0 + mr, jc, h);
-            if (a.Caux) {   // the pre-activations [g | u], for the backward
-              const f32x4_t gv = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-              const f32x4_t uv = {acc[i + MTN / 2][j][q * 4], acc[i + MTN / 2][j][q * 4 + 1],
-                                  acc[i + MTN / 2][j][q * 4 + 2], acc[i + MTN / 2][j][q * 4 + 3]};
-              store_sub<MOE_OUT_BF16>(a.Caux, 2 * f, m0 + mr, jc, gv);
-              store_sub<MOE_OUT_BF16>(a.Caux, 2 * f, m0 + mr, f + jc, uv);
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < MTN; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = n0 + wn * WTN + i * 32 + q * 8 + g * 4;
-          const f32x4_t v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-          if (mr < rows && n < ncols) store_sub<MOE_OUT_BF16>(a.C, ncols, m0 + mr, n, v);
-        }
-      }
-    }
+      for (int q = 0; q < 4; ++q) put(256, rl, wn * (WTN / 2) + i * 32 + q * 8 + g * 4, hp[i][j][q]);
+  }
+  __syncthreads();
+  copy_staged<256>(lds_codes, lds_scales, s2, s3, a.C + m0 * (int64_t)f * 2, f, rows, n0, f, n0 + BN / 4, f);
   }
 }
 
