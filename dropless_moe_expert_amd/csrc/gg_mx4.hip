@@ -178,28 +178,62 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx4_kernel(GGArgs a) {
     }
 
     // 32x32 accumulator: element v of lane (r32, g) is weight row 8 (v / 4) + 4 g + v % 4
-    // of subtile i and token row r32 of subtile j
+    // of subtile i and token row r32 of subtile j.  The bf16 tile leaves
+    // through LDS: every wavefront writes its rows (16-byte units XOR-
+    // swizzled by row), then the workgroup copies whole rows out as 16-byte
+    // pieces, each thread's LDS reads four at a time ahead of their stores.
+    constexpr int RB = SWI ? 256 : 512, UR = RB / 16;   // bytes and 16-byte units per tile row
+    static_assert(BM * RB <= NS * STAGE_B, "the tile fits in the stage buffers");
+    auto put = [&](int row, int col, uint2 w) {
+      *reinterpret_cast<uint2*>(lds + row * RB + (((col >> 3) ^ (row % UR)) << 4) + ((col >> 2) & 1) * 8) = w;
+    };
+    __syncthreads();   // every wavefront has read its last stage
 #pragma unroll
     for (int j = 0; j < MTM; ++j) {
       const int mr = wm * WTM + 32 * j + r32;
       if constexpr (SWI) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int jc = n0 + wn * (WTN / 2) + q * 8 + g * 4;
-          f32x4_t h;
+          float h[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) h[e] = silu_f32(acc[0][j][q * 4 + e]) * acc[1][j][q * 4 + e];
-          if (mr < rows && jc < f) store_sub<MOE_OUT_BF16>(a.C, f, m0 + mr, jc, h);
+          put(mr, wn * (WTN / 2) + q * 8 + g * 4, make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])));
         }
       } else {
 #pragma unroll
         for (int i = 0; i < MTN; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = n0 + wn * WTN + 32 * i + q * 8 + g * 4;
-            const f32x4_t v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-            if (mr < rows && n < a.N) store_sub<MOE_OUT_BF16>(a.C, a.N, m0 + mr, n, v);
-          }
+          for (int q = 0; q < 4; ++q)
+            put(mr, wn * WTN + 32 * i + q * 8 + g * 4,
+                make_uint2(pack_bf16x2(acc[i][j][q * 4], acc[i][j][q * 4 + 1]),
+                           pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3])));
+      }
+    }
+    __syncthreads();
+    {
+      constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
+      constexpr int NBT = 4;
+      static_assert(BM * UR % THREADS == 0 && NPT % NBT == 0, "whole batches");
+      const int ld = SWI ? f : a.N;
+      // a piece is a 32-bit offset from the tile's first row (256 rows of at
+      // most 2^22 columns)
+      uint8_t* const cbase = a.C + m0 * (int64_t)ld * 2;
+#pragma unroll 1
+      for (int k0 = 0; k0 < NPT; k0 += NBT) {
+        uint4 v[NBT];
+#pragma unroll
+        for (int k = 0; k < NBT; ++k) {
+          const int c = threadIdx.x + (k0 + k) * THREADS;
+          const int row = c / UR, u = c - row * UR;
+          v[k] = *reinterpret_cast<const uint4*>(lds + row * RB + ((u ^ (row % UR)) << 4));
+        }
+#pragma unroll
+        for (int k = 0; k < NBT; ++k) {
+          const int c = threadIdx.x + (k0 + k) * THREADS;
+          const int row = c / UR, u = c - row * UR;
+          const int col = n0 + 8 * u;
+          if (row < rows && col < ld) *reinterpret_cast<uint4*>(cbase + (uint32_t)(row * ld + col) * 2u) = v[k];
+        }
       }
     }
   }
