@@ -24,18 +24,17 @@
 //  2. The partial logit blocks meet in LDS; one pass sums them in block
 //     order, adds the bias, turns NaN into -inf (flag) and writes the optional
 //     fp32 logits.
-//  3. Top-K: thread (token t, slice sl) keeps the KL >= K best keys of its
-//     slice of experts; a key is (order-preserving bits of the logit) << 32 |
-//     ~expert, so one unsigned 64-bit compare ranks by logit and, among equal
-//     logits, puts the lower expert first: the rule of moe_route_topk, hence
-//     the same ids for the same logits.  Slices merge pairwise through LDS.
+//  3. Top-K: a group of 4-16 lanes per token reads the token's logits from
+//     LDS and selects as moe_route_topk does (route_select.h), hence the same
+//     ids for the same logits.
 //  4. Weights: exp(l_k - l_max) over their sum (renormalised) or over the sum
-//     across all E experts.
+//     across all E experts, as moe_route_topk computes them.
 //  5. Dispatch histogram: the block's pairs (t, k), in pair order, form one
 //     chunk of moe_permute's counting sort: each pair's rank among the
 //     chunk's earlier pairs with the same expert, and the chunk's per-expert
 //     counts, in the workspace layout moe_permute_routed reads.
 #include "common.h"
+#include "route_select.h"
 
 #pragma clang diagnostic ignored "-Winline-asm"
 
@@ -57,29 +56,6 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
 // A fragment read (16 rows, one chunk) then touches rows of both parities at
 // eight distinct slots each: the 16 lanes of a quarter-wave hit 256 distinct bytes.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-
-// sortable key: larger logit first, then lower expert index first
-__device__ __forceinline__ uint64_t make_key(float v, int e) {
-  if (v == 0.f) v = 0.f;   // -0 and +0 compare equal as floats
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(~e);
-}
-__device__ __forceinline__ float key_value(uint64_t k) {
-  const uint32_t u = (uint32_t)(k >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-__device__ __forceinline__ int key_expert(uint64_t k) { return (int)(~(uint32_t)k); }
-
-template <int KL>
-__device__ __forceinline__ void insert(uint64_t (&kk)[KL], uint64_t n) {
-#pragma unroll
-  for (int j = KL - 1; j >= 0; --j) {
-    const bool cj = n > kk[j];
-    const bool cp = (j > 0) ? (n > kk[j > 0 ? j - 1 : 0]) : false;
-    kk[j] = cj ? (cp ? kk[j > 0 ? j - 1 : 0] : n) : kk[j];
-  }
-}
 
 template <int NB>
 __device__ __forceinline__ void wait_stages(int q) {
@@ -110,13 +86,14 @@ struct Cfg {
 template <int TW, int EP, int SK, int KL>
 struct Epi {
   static constexpr int LS = EP + 4;                // logits row stride (floats)
-  static constexpr int NSL = 256 / TW;             // top-K slices per token
-  static constexpr int SW = EP / NSL;              // experts per slice
   static constexpr int LG_B = SK * TW * LS * 4;
-  static constexpr int MG_B = (NSL / 2) * TW * KL * 8;
   static constexpr int ID_B = TW * 32 * 4;
-  static constexpr int BYTES = LG_B + MG_B + ID_B + 256 * 4 + TW * 4 + NSL * TW * 4;
-  static_assert(EP % NSL == 0 && SW >= 2, "slices");
+  static constexpr int BYTES = LG_B + ID_B + 256 * 4;
+  // top-K: a group of LPT lanes per token, VPL logits per lane (route_select.h)
+  static constexpr int LPT = EP <= 32 ? 4 : EP <= 128 ? 8 : 16;
+  static constexpr int VPL = EP / LPT;
+  static constexpr int SLOTS = (KL + LPT - 1) / LPT;
+  static_assert(VPL <= 16 && VPL % 4 == 0, "whole 16-byte chunks of logits per lane");
 };
 
 template <int TW, int EP, int SK, int KL>
@@ -125,14 +102,11 @@ __device__ __forceinline__ void finish_block(uint8_t* lds, const float* BIAS, in
                                              float* __restrict__ logits, int32_t* __restrict__ local_rank,
                                              int32_t* __restrict__ chunk_counts, uint32_t* flag) {
   using P = Epi<TW, EP, SK, KL>;
-  constexpr int LS = P::LS, NSL = P::NSL, SW = P::SW, LG_B = P::LG_B, MG_B = P::MG_B, ID_B = P::ID_B;
+  constexpr int LS = P::LS, LG_B = P::LG_B, ID_B = P::ID_B;
   const int tid = threadIdx.x, lane = tid & 63, w = wave_idx();
   float* LG = reinterpret_cast<float*>(lds);
-  uint64_t* MG = reinterpret_cast<uint64_t*>(lds + LG_B);
-  int32_t* IDL = reinterpret_cast<int32_t*>(lds + LG_B + MG_B);
-  int32_t* running = reinterpret_cast<int32_t*>(lds + LG_B + MG_B + ID_B);
-  float* MX = reinterpret_cast<float*>(lds + LG_B + MG_B + ID_B + 256 * 4);
-  float* PS = MX + TW;
+  int32_t* IDL = reinterpret_cast<int32_t*>(lds + LG_B);
+  int32_t* running = reinterpret_cast<int32_t*>(lds + LG_B + ID_B);
   __syncthreads();
   bool nan_seen = false;
   for (int u = tid; u < TW * (EP / 4); u += 256) {
@@ -169,74 +143,41 @@ __device__ __forceinline__ void finish_block(uint8_t* lds, const float* BIAS, in
   if (__any(nan_seen) && lane == 0) raise_flag(flag, MOE_FLAG_NAN_LOGIT);
   __syncthreads();
 
-  // ------------------------------------------------------------- 3. top-K
-  const int t = tid % TW, sl = tid / TW;
-  uint64_t kk[KL];
-#pragma unroll
-  for (int j = 0; j < KL; ++j) kk[j] = 0;   // below every real key
+  // ------------------------------------------------- 3-4. top-K and weights
+  // A group of LPT lanes per token, as moe_route_topk (route_select.h): the
+  // same ids and weights for the same logits.  Lane sub of the group reads
+  // its chunks of 4 logits from the token's LDS row (padded experts hold
+  // -inf and are absent to the selection).
   {
-    constexpr int VW = SW >= 4 ? 4 : SW;
-    const float* row = LG + t * LS + sl * SW;
-#pragma unroll 2
-    for (int e0 = 0; e0 < SW; e0 += VW) {
-      float v[VW];
-      if constexpr (VW == 4) {
-        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(row + e0);
-        v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
-      } else {
+    using G = topk::Group<P::LPT, P::VPL>;
+    constexpr int TPW = 64 / P::LPT;   // tokens per wavefront and pass
+    const int sub = lane % P::LPT;
+#pragma unroll 1
+    for (int base = 0; base < TW; base += 4 * TPW) {
+      const int t = base + w * TPW + lane / P::LPT;
+      if (t >= TW) break;   // whole groups of lanes leave together
+      float v[P::VPL];
+      const float* row = LG + t * LS;
 #pragma unroll
-        for (int j = 0; j < VW; ++j) v[j] = row[e0 + j];
+      for (int c = 0; c < P::VPL / 4; ++c) {
+        const f32x4_t q = *reinterpret_cast<const f32x4_t*>(row + G::expert(sub, 4 * c));
+        v[4 * c] = q[0]; v[4 * c + 1] = q[1]; v[4 * c + 2] = q[2]; v[4 * c + 3] = q[3];
       }
+      int pk[P::SLOTS], pi[P::SLOTS], kmax;
+      G::template select<P::SLOTS>(v, E, K, sub, pk, pi, kmax);
+      float a[P::SLOTS];
+      const float part = G::template weights<P::SLOTS>(v, E, K, renorm, sub, pk, kmax, a);
+      if (t < tvalid) {
+        const int64_t o = (t0 + t) * K;
 #pragma unroll
-      for (int j = 0; j < VW; ++j) {
-        const int e = sl * SW + e0 + j;
-        if (e < E) insert<KL>(kk, make_key(v[j], e));
-      }
-    }
-  }
-#pragma unroll
-  for (int step = 1; step < NSL; step <<= 1) {
-    const int q = sl / (2 * step);
-    if (sl % (2 * step) == step) {
-#pragma unroll
-      for (int j = 0; j < KL; ++j) MG[(q * TW + t) * KL + j] = kk[j];
-    }
-    __syncthreads();
-    if (sl % (2 * step) == 0) {
-#pragma unroll
-      for (int j = 0; j < KL; ++j) insert<KL>(kk, MG[(q * TW + t) * KL + j]);
-    }
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------- 4. weights
-  const float lmax = key_value(kk[0]);   // meaningful in threads sl == 0
-  float denom = 0.f;
-  if (renorm) {
-#pragma unroll
-    for (int k = 0; k < KL; ++k)
-      if (k < K) denom += expf(key_value(kk[k]) - lmax);
-  } else {
-    if (sl == 0) MX[t] = lmax;
-    __syncthreads();
-    const float m = MX[t];
-    const float* row = LG + t * LS + sl * SW;
-    float s = 0.f;
-    for (int j = 0; j < SW; ++j)
-      if (sl * SW + j < E) s += expf(row[j] - m);
-    PS[sl * TW + t] = s;
-    __syncthreads();
-    for (int q = 0; q < NSL; ++q) denom += PS[q * TW + t];
-  }
-  if (sl == 0 && t < tvalid) {
-    const int64_t o = (t0 + t) * K;
-#pragma unroll
-    for (int k = 0; k < KL; ++k) {
-      if (k < K) {
-        const int e = key_expert(kk[k]);
-        ids[o + k] = e;
-        wout[o + k] = expf(key_value(kk[k]) - lmax) / denom;
-        IDL[t * K + k] = e;
+        for (int q = 0; q < P::SLOTS; ++q) {
+          const int k = q * P::LPT + sub;
+          if (k < K) {
+            ids[o + k] = pi[q];
+            wout[o + k] = a[q] / part;
+            IDL[t * K + k] = pi[q];
+          }
+        }
       }
     }
   }
