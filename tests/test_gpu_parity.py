@@ -874,6 +874,28 @@ def test_flags_bad_sizes(ops):
     assert max_rel_err(buf[:m_cap], ref) <= BF16_TOL
 
 
+def test_flags_wgrad_sizes_past_int32(ops):
+    """Weight-gradient sizes whose sum passes 2^31 (and a negative one): the
+    offsets are summed in 64 bits and clamped to the rows given, so the
+    flags rise and the first group contracts every given row while the rest
+    are empty (zeros), the clamped reading of the oracle; no row outside the
+    operands is read."""
+    say("flags wgrad sizes")
+    rng = np.random.default_rng(33)
+    m_cap, P, Q = 300, 64, 64
+    X, Y = bf16(rng, m_cap, P), bf16(rng, m_cap, Q)
+    sizes = np.array([2 ** 30, 2 ** 30, 100, -7], np.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = ops.grouped_gemm_wgrad(dev(X), dev(Y), dev(torch.from_numpy(sizes)), flag=flag)
+    torch.cuda.synchronize()
+    f = int(flag.item())
+    assert f & ops.FLAG_NEGATIVE_SIZE and f & ops.FLAG_ROWS_OVER_CAP
+    ref = orc.grouped_wgrad(X, Y, np.array([m_cap, 0, 0, 0], np.int32))
+    assert max_rel_err(out, ref) <= BF16_TOL
+    for g in (1, 2, 3):
+        assert torch.all(out[g] == 0)
+
+
 def test_flag_nan_logit(ops):
     l = torch.randn(4, 8)
     l[2, 3] = float("nan")
