@@ -105,6 +105,37 @@ def calibration(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def counters_table(args) -> str:
+    """Per-kernel averages of every counter in one --pmc CSV (--counters),
+    with the LDS figures derived from them when present: utilisation
+    (SQ_LDS_IDX_ACTIVE over GRBM_GUI_ACTIVE / 8 XCCs x 256 CUs, the tool's
+    own LDS-utilisation formula), bank-conflict cycles per active cycle, and
+    the share of wave cycles spent waiting to issue an LDS instruction
+    (SQ_WAIT_INST_LDS counts units of 4 cycles)."""
+    lines = [f"# {args.title}", ""]
+    for src in args.source or []:
+        lines.append(f"{src.split('/')[-1]} sha256[:16] = {hashlib.sha256(open(src, 'rb').read()).hexdigest()[:16]}  ")
+    lines += ["", "Command (from the repository root):", ""] + ["    " + c for c in args.command] + [""]
+    kern = _by_kernel(_dispatches(args.counters))
+    names = sorted({c for ds in kern.values() for c in ds[0] if c.isupper()})
+    lines.append("| kernel | calls | avg us | LDS util | bank conflict / active | LDS issue wait / wave cycles | "
+                 + " | ".join(names) + " |")
+    lines.append("|---" * (6 + len(names)) + "|")
+    for name, ds in kern.items():
+        if args.kernel_filter and not any(f in name for f in args.kernel_filter):
+            continue
+        m = {c: _mean(d.get(c, 0.0) for d in ds) for c in names}
+        cyc = m.get("GRBM_GUI_ACTIVE", 0.0) / XCC
+        util = 100 * m["SQ_LDS_IDX_ACTIVE"] / (cyc * 256) if cyc and "SQ_LDS_IDX_ACTIVE" in m else None
+        conf = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_LDS_IDX_ACTIVE"] if m.get("SQ_LDS_IDX_ACTIVE") else None
+        wait = 4 * m["SQ_WAIT_INST_LDS"] / m["SQ_WAVE_CYCLES"] if m.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_LDS" in m else None
+        f = lambda v, fmt: "" if v is None else fmt.format(v)   # noqa: E731
+        lines.append(f"| `{short(name)}` | {len(ds)} | {_mean(d['dur_ns'] for d in ds) / 1e3:.1f} | "
+                     f"{f(util, '{:.1f} %')} | {f(conf, '{:.3f}')} | {f(wait, '{:.2f}')} | "
+                     + " | ".join(f"{m[c]:.4g}" for c in names) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def summarise(args) -> str:
     lines = [f"# {args.title}", ""]
     for s in args.source or []:
@@ -186,8 +217,13 @@ def main(argv=None) -> int:
     ap.add_argument("--calibration", action="store_true",
                     help="per-dispatch table of counter_calibration.py's copies (--sizes: MiB per side, in order)")
     ap.add_argument("--sizes", default="256,1024,2048")
+    ap.add_argument("--counters", help="one --pmc CSV: a per-kernel table of all its counters")
+    ap.add_argument("--kernel-filter", action="append", help="with --counters: kernels whose name holds this")
     args = ap.parse_args(argv)
-    sys.stdout.write(calibration(args) if args.calibration else summarise(args))
+    if args.counters:
+        sys.stdout.write(counters_table(args))
+    else:
+        sys.stdout.write(calibration(args) if args.calibration else summarise(args))
     return 0
 
 
