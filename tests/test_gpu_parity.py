@@ -1099,6 +1099,7 @@ def test_mxfp4_quantize(ops, R, C, scale):
     (False, [0, 300, 1, 0, 260], 512, 384),      # several m-tiles, empty groups, 3 stages
     (False, [513, 7], 200, 128),                 # partial n-tile, one stage (fewer than the pipeline depth)
     (True, [300, 0, 1, 517, 0, 33], 272, 256),   # SwiGLU, f = 136: partial output tile
+    (False, [260, 3], 256, 640),                 # five stages: the stage buffers wrap around
 ])
 def test_grouped_gemm_mxfp4(ops, swiglu, sizes, N, Kd):
     """The MXFP4 grouped GEMM on the oracle's own codes and scales (moved into
