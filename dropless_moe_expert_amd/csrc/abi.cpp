@@ -40,7 +40,8 @@ moe_status_t mxfp4_quantize_launch(const uint16_t*, int64_t, int32_t, uint8_t*, 
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t,
                                          uint8_t*, uint8_t*, uint32_t*, hipStream_t);
 moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
-                                 const int32_t*, void*, void*, uint32_t*, hipStream_t);
+                                 const int32_t*, void*, void*, void*, size_t, uint32_t*, hipStream_t);
+size_t grouped_gemm_ws_bytes_impl(const moe_gg_desc*);
 }
 
 namespace moe {  // gg_fwd.hip
@@ -222,15 +223,13 @@ moe_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8
 }
 
 size_t grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
-  (void)desc;
-  return 0;
+  if (!desc) return 0;
+  return grouped_gemm_ws_bytes_impl(desc);
 }
 
 moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_scale, const void* B,
                           const uint8_t* B_scale, const int32_t* group_sizes, void* C, void* C_aux, void* ws,
                           size_t ws_bytes, uint32_t* err_flag, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!d) return MOE_ERR_INVALID_ARG;
   if (d->G < 1 || d->G > 1024 || d->N < 1 || d->m_cap < 0) return MOE_ERR_INVALID_ARG;
   if (d->m_cap > INT32_MAX) return MOE_ERR_UNSUPPORTED;
@@ -251,7 +250,7 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
       return MOE_ERR_ALIGNMENT;
     if (d->N % 8) return MOE_ERR_UNSUPPORTED;
     if (d->m_cap == 0) return MOE_OK;
-    return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, err_flag, S(stream));
+    return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, ws, ws_bytes, err_flag, S(stream));
   }
   if (d->out_dtype != MOE_OUT_BF16 && d->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
   if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU && d->epilogue != MOE_EPI_SWIGLU_MXFP8)
@@ -294,7 +293,7 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
-  return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, err_flag, S(stream));
+  return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, ws, ws_bytes, err_flag, S(stream));
 }
 
 size_t moe_pack_weights_bytes(int32_t G, int32_t N, int32_t K, int32_t epilogue) {

@@ -269,6 +269,109 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
   }
 }
 
+// ------------------------------------------------------------------ split tail
+// The ragged-M kernel deals tiles to its workers in turn, so a last round of
+// t tiles keeps only t of the grid's workers busy for a whole tile.  In the
+// kernel's SPLIT instantiation (which the host picks for calls of at most
+// three rounds of long-K tiles, where a short last round is likely and
+// costly), when t is at most half the grid each of those tiles is instead
+// cut along K into S = min(4, grid / t, stages / 16) equal stage ranges
+// ("units"), the units of one tile on consecutive workers.  Every unit
+// writes its fp32 partial sums to its own slot of the caller's workspace
+// (each thread its accumulators, in register order) and counts itself in at
+// the tile's counter; the unit that brings the count to S reads the S
+// partials back and adds them in split order (so the result does not depend
+// on which unit finishes last), then runs the tile's epilogue.  The
+// partition depends only on the group sizes, the grid and K: results are
+// bitwise reproducible.  Counters: one slot of kSplitWords words per call
+// (64 slots handed out in turn), epoch-tagged as the tile queues
+// (tile_queue.h), reset for the slot's next call by the call's last
+// workgroup.
+constexpr int kMaxSplit = 4, kMinSplitStages = 16;
+constexpr int kSplitWords = 512 + 1;   // tail tiles (at most half a grid of <= 1024) + done count
+
+struct SplitSlots {
+  uint32_t w[tq::kSlots][kSplitWords];
+};
+constexpr SplitSlots initial_split_slots() {
+  SplitSlots t{};
+  for (int s = 0; s < tq::kSlots; ++s)
+    for (int i = 0; i < kSplitWords; ++i) t.w[s][i] = tq::word(tq::launch_epoch((uint64_t)s), 0u);
+  return t;
+}
+__device__ SplitSlots g_split_sched = initial_split_slots();
+
+struct SplitTail {
+  int64_t full;    // tiles of the whole rounds (units [0, full) are whole tiles)
+  int64_t units;   // full + tail tiles x S
+  int S;           // splits of each tail tile (1: none)
+};
+
+__device__ __forceinline__ SplitTail split_tail(int64_t total, int grid, int nk) {
+  SplitTail r{total, total, 1};
+  const int64_t tail = total % grid;
+  if (tail == 0 || 2 * tail > grid || tail > kSplitWords - 1) return r;
+  const int S = min(kMaxSplit, min(grid / (int)tail, nk / kMinSplitStages));
+  if (S < 2) return r;
+  r.full = total - tail;
+  r.units = r.full + tail * S;
+  r.S = S;
+  return r;
+}
+
+// Unit tail_unit (tile tail_unit / S, split tail_unit % S) has its partial
+// sums in acc.  Returns true, with acc holding the tile's full sums, to the
+// unit that completes the tile; false to the others.  box: one int of LDS
+// that no wavefront reads or writes once it has left its K loop.
+template <int ACT>
+__device__ __forceinline__ bool split_reduce(const GGArgs& a, const SplitTail& sp, int64_t tail_unit,
+                                             f32x4_t (&acc)[TN][TM], int32_t* box) {
+  constexpr int SLOT = BM * BN;   // floats per unit
+  const int t = threadIdx.x;
+  const int64_t tile_tail = tail_unit / sp.S;
+  float* const mine = a.part + tail_unit * SLOT;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < ACT; ++j)
+      *reinterpret_cast<f32x4_t*>(mine + ((i * TM + j) * THREADS + t) * 4) = acc[i][j];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's partials are visible to the device
+  __syncthreads();                                      // every thread's, and every wavefront has left its K loop
+  if (t == 0) {
+    DeviceWord w{g_split_sched.w[a.sched_slot] + tile_tail};
+    box[0] = (int32_t)tq::take(w, a.sched_epoch) == sp.S - 1;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(box[0])) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other units' partials
+  const float* const first = a.part + tile_tail * sp.S * SLOT;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < ACT; ++j) {
+      const int64_t off = ((i * TM + j) * THREADS + t) * 4;
+      f32x4_t v = *reinterpret_cast<const f32x4_t*>(first + off);
+      for (int q = 1; q < sp.S; ++q) v += *reinterpret_cast<const f32x4_t*>(first + q * SLOT + off);
+      acc[i][j] = v;
+    }
+  return true;
+}
+
+// Once per workgroup of a call that split its tail, after its last unit:
+// the last workgroup to arrive presets the slot's words for the slot's next
+// call.  box: one int of LDS no wavefront uses any more.
+__device__ __forceinline__ void split_finish(const GGArgs& a, int32_t* box) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    DeviceWord done{g_split_sched.w[a.sched_slot] + (kSplitWords - 1)};
+    box[0] = tq::finish(done, a.sched_epoch, gridDim.x);
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(box[0]))
+    for (int i = threadIdx.x; i < kSplitWords; i += blockDim.x)
+      atomicExch(g_split_sched.w[a.sched_slot] + i, tq::word(a.sched_next, 0u));
+}
+
 // Weight layouts (BL): BL_NK reads B [G, N, K] rows (K contiguous); BL_PACKED
 // reads the tile-stage blocks of moe_pack_weights: for expert g, n-tile nt
 // and K-stage kt the 256 weight rows of the tile (in the order the tile uses
@@ -276,7 +379,7 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
 // 16 KB, already in the LDS slot order, so each direct load reads 1 KB of
 // consecutive bytes; BL_KN reads B [G, K, N] (the data gradient's weight)
 // as K-outer stages, 32 rows of 256 columns, through LDS transpose reads.
-template <int EPI, int OUT, int BL>
+template <int EPI, int OUT, int BL, bool SPLIT = false>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   // five named 32 KB stage buffers (the whole 160 KB LDS): stage kt lives in
   // buffer kt % 5; loads run four stages ahead of the stage being read
@@ -305,7 +408,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
   const int f = a.N / 2;
   const int64_t total = count_mtiles(a) * a.n_tiles;
   const int64_t lda_b = (int64_t)a.K * 2;
-  const int nk = a.K / 32;
+  const int nk_all = a.K / 32;
   uint32_t koff[TN];   // BL_KN: per-lane LDS offsets of the 8 weight fragments
   {
     int wn, wm;
@@ -314,7 +417,20 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     for (int i = 0; i < TN; ++i) koff[i] = BL == BL_KN ? kfrag_off(wn * WTN + 16 * i) : 0u;
   }
 
-  for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+  // units: whole tiles, then (SPLIT) the split tail's stage ranges
+  const SplitTail sp = SPLIT ? split_tail(total, (int)gridDim.x, nk_all) : SplitTail{total, total, 1};
+  for (int64_t unit = wid; unit < sp.units; unit += gridDim.x) {
+    int64_t tile = unit, tail_unit = -1;
+    int kt0 = 0, nk = nk_all;   // the unit's first stage and stage count
+    if constexpr (SPLIT) {
+      if (unit >= sp.full) {
+        tail_unit = unit - sp.full;
+        tile = sp.full + tail_unit / sp.S;
+        const int part = (int)(tail_unit % sp.S);
+        kt0 = (int)((int64_t)part * nk_all / sp.S);
+        nk = (int)((int64_t)(part + 1) * nk_all / sp.S) - kt0;
+      }
+    }
     const TileGroup tg = locate(a, tile);
     const int g = tg.g, nt = tg.nt;
     const int64_t m0 = tg.m0;
@@ -336,12 +452,14 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
         return min(n0 + r, a.N - 1);
       }
     });
-    const uint8_t* xbase = a.A + m0 * lda_b;
-    const uint8_t* wbase = BL == BL_PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * (BN * ROWB)
-                           : BL == BL_KN   ? a.B + (int64_t)g * a.K * a.N * 2
-                                           : a.B + (int64_t)g * nrows_b * lda_b;
     // bytes from one stage's weight block to the next
     const int wstride = BL == BL_PACKED ? BN * ROWB : BL == BL_KN ? 32 * a.N * 2 : ROWB;
+    // operands from the unit's first stage kt0 on
+    const uint8_t* xbase = a.A + m0 * lda_b + (int64_t)kt0 * ROWB;
+    const uint8_t* wbase = (BL == BL_PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk_all * (BN * ROWB)
+                            : BL == BL_KN   ? a.B + (int64_t)g * a.K * a.N * 2
+                                            : a.B + (int64_t)g * nrows_b * lda_b) +
+                           (int64_t)kt0 * wstride;
     if constexpr (BL == BL_PACKED) {
       const int wave = wave_id(), lane = threadIdx.x & 63;
 #pragma unroll
@@ -421,6 +539,11 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
       if (s + 1 < nk) iter(b1, b0, s + 1);
       if (s + 2 < nk) iter(b2, b1, s + 2);
       if (s + 3 < nk) iter(b3, b2, s + 3);
+      if constexpr (SPLIT) {
+        // a split unit: partial sums to the workspace; the unit that
+        // completes the tile adds them, in split order, and runs the epilogue
+        if (tail_unit >= 0 && !split_reduce<ACT>(a, sp, tail_unit, acc, reinterpret_cast<int32_t*>(b4))) return;
+      }
       if constexpr (OUT == MOE_OUT_BF16 && EPI == EPI_SWIGLU_AUX) {
         // h formed and packed first, so the accumulators are free once the
         // pre-activations are in LDS; then (once every thread has read
@@ -456,6 +579,9 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     } else {
       run(std::integral_constant<int, 0>());
     }
+  }
+  if constexpr (SPLIT) {
+    if (sp.S > 1) split_finish(a, reinterpret_cast<int32_t*>(b4));
   }
 }
 
@@ -678,9 +804,15 @@ moe_status_t launch_pack_weights(const uint16_t* w, int G, int N, int K, int epi
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// workspace of the bf16 ragged-M kernel's split tail: one fp32 tile per worker
+size_t fwd_split_workspace_bytes() {
+  return (size_t)moe_host::device_cu_count() * fwd::BM * fwd::BN * sizeof(float);
+}
+
 // bf16, ragged-M: the forward kernels (B [G, N, K] rows or packed) and the
 // data gradient (B [G, K, N])
 moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout, hipStream_t s) {
+  static std::atomic<uint64_t> launches{0};
   GGArgs b = a;
   const int ncols = epilogue == MOE_EPI_SWIGLU ? a.N / 2 : a.N;
   const int bn = epilogue == MOE_EPI_SWIGLU ? fwd::BN / 2 : fwd::BN;
@@ -691,6 +823,47 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
   using namespace fwd;
+  // The split-tail instantiation: given the workspace, for calls of at most
+  // three rounds (even with every group's last tile partial) of tiles at
+  // least 64 stages long, where a short last round is likely and costs a
+  // large share of the call.  Other calls keep the plain kernel.
+  if (b.part && max_tiles <= 3 * grid && a.K / 32 >= 64) {
+    const uint64_t n = launches.fetch_add(1u, std::memory_order_relaxed);
+    b.sched_slot = tq::launch_slot(n);
+    b.sched_epoch = tq::launch_epoch(n);
+    b.sched_next = tq::slot_next_epoch(n);
+    if (b_layout == MOE_B_KN) {
+      if (epilogue == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
+      if (out_f32) {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_KN, true>), g, t, 0, s, b);
+      } else {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_KN, true>), g, t, 0, s, b);
+      }
+    } else if (epilogue == MOE_EPI_SWIGLU && a.Caux) {
+      if (b_layout == MOE_B_PACKED) {
+        hipLaunchKernelGGL((gg_fwd_kernel<EPI_SWIGLU_AUX, MOE_OUT_BF16, BL_PACKED, true>), g, t, 0, s, b);
+      } else {
+        hipLaunchKernelGGL((gg_fwd_kernel<EPI_SWIGLU_AUX, MOE_OUT_BF16, BL_NK, true>), g, t, 0, s, b);
+      }
+    } else if (epilogue == MOE_EPI_SWIGLU) {
+      if (b_layout == MOE_B_PACKED) {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_PACKED, true>), g, t, 0, s, b);
+      } else {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU, MOE_OUT_BF16, BL_NK, true>), g, t, 0, s, b);
+      }
+    } else if (b_layout == MOE_B_PACKED) {
+      if (out_f32) {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_PACKED, true>), g, t, 0, s, b);
+      } else {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_PACKED, true>), g, t, 0, s, b);
+      }
+    } else if (out_f32) {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_NK, true>), g, t, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_NK, true>), g, t, 0, s, b);
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   if (b_layout == MOE_B_KN) {
     if (epilogue == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
     if (out_f32) {

@@ -22,9 +22,10 @@ struct GGArgs {
   int G, M, N, K;
   int n_tiles;             // tiles along n (ragged-M) / q (ragged-K)
   int p_tiles;             // ragged-K: tiles along p (rows of C[g])
-  int sched_slot;          // ragged-K: the launch's slot of tile-queue words
-  uint32_t sched_epoch;    // ragged-K: the launch's epoch (tile_queue.h)
-  uint32_t sched_next;     // ragged-K: the epoch of the slot's next launch
+  int sched_slot;          // the launch's slot of tile-queue (ragged-K) or split (ragged-M) words
+  uint32_t sched_epoch;    // the launch's epoch (tile_queue.h)
+  uint32_t sched_next;     // the epoch of the slot's next launch
+  float* part;             // ragged-M bf16: workspace of the split tail's partial sums, or NULL
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;

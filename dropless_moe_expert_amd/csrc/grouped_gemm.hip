@@ -9,7 +9,8 @@
 // dropless MoE?": the counts may be invisible to the CPU.
 //
 //  * ragged M, bf16 (forward with B [G, N, K] rows or packed, data gradient
-//    with B [G, K, N]): gg_bf16.hip, gg_fwd_kernel;
+//    with B [G, K, N]): gg_bf16.hip, gg_fwd_kernel (with the caller's
+//    workspace, the tiles of a short last round split along K);
 //  * ragged K, bf16 (weight gradients): gg_bf16.hip, gg_wgrad_kernel;
 //  * ragged M, MXFP8: gg_fwd_mx.hip, gg_fwd_mx_kernel;
 //  * ragged K, MXFP8 (operands from mxfp8_quantize_transposed): gg_fwd_mx.hip,
@@ -23,11 +24,18 @@ moe_status_t launch_wgrad(const GGArgs& a, int out_f32, hipStream_t s);         
 moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_t s);              // gg_fwd_mx.hip
 moe_status_t launch_wgrad_mx(const GGArgs& a, hipStream_t s);                                       // gg_fwd_mx.hip
 moe_status_t launch_fwd_mx4(const GGArgs& a, int epilogue, hipStream_t s);                          // gg_mx4.hip
+size_t fwd_split_workspace_bytes();                                                                  // gg_bf16.hip
 }  // namespace moe
+
+// The workspace a call can use: the bf16 ragged-M kernel's split tail
+extern "C" size_t grouped_gemm_ws_bytes_impl(const moe_gg_desc* d) {
+  if (d->ragged == MOE_RAGGED_M && d->dtype == MOE_DTYPE_BF16) return moe::fwd_split_workspace_bytes();
+  return 0;
+}
 
 extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A, const uint8_t* As, const void* B,
                                             const uint8_t* Bs, const int32_t* sizes, void* C, void* Caux,
-                                            uint32_t* flag, hipStream_t s) {
+                                            void* ws, size_t ws_bytes, uint32_t* flag, hipStream_t s) {
   using namespace moe;
   GGArgs a;
   a.A = reinterpret_cast<const uint8_t*>(A);
@@ -45,6 +53,12 @@ extern "C" moe_status_t grouped_gemm_launch(const moe_gg_desc* d, const void* A,
   a.K = d->K;
   a.n_tiles = 0;
   a.p_tiles = 0;
+  a.sched_slot = 0;
+  a.sched_epoch = a.sched_next = 0;
+  // the split tail runs only with the whole workspace, 256-byte aligned
+  const size_t need = grouped_gemm_ws_bytes_impl(d);
+  a.part = (need && ws && ws_bytes >= need && !(reinterpret_cast<uintptr_t>(ws) & 255u)) ? reinterpret_cast<float*>(ws)
+                                                                                         : nullptr;
   if (d->ragged == MOE_RAGGED_M) {
     if (d->dtype == MOE_DTYPE_MXFP8) return launch_fwd_mx(a, d->epilogue, d->b_layout == MOE_B_PACKED, s);
     if (d->dtype == MOE_DTYPE_MXFP4) return launch_fwd_mx4(a, d->epilogue, s);

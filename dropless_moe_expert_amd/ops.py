@@ -344,14 +344,32 @@ def pack_weights_mxfp8(Bq: torch.Tensor, Bs: torch.Tensor, epilogue: int = MOE_E
     return PackedWeights(data, G, N, Kd, epilogue, mxfp8=True)
 
 
+_gemm_ws = {}   # device index -> the bf16 ragged-M calls' workspace (one per device)
+
+
+def _gemm_workspace(d: "GGDesc", dev: torch.device) -> Optional[torch.Tensor]:
+    """The library's workspace for this call (grouped_gemm_workspace_bytes),
+    allocated once per device and shared by this module's calls, which run
+    on the device's current stream one after another."""
+    need = lib().grouped_gemm_workspace_bytes(ctypes.byref(d))
+    if need == 0:
+        return None
+    ws = _gemm_ws.get(dev.index)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _gemm_ws[dev.index] = ws
+    return ws
+
+
 def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int = MOE_B_NK,
                  epilogue: int = MOE_EPI_NONE, out_dtype: torch.dtype = torch.bfloat16, keep_aux: bool = False,
                  out: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
-                 flag: Optional[torch.Tensor] = None):
+                 flag: Optional[torch.Tensor] = None, split: bool = True):
     """Ragged-M grouped GEMM, bf16.  A [m_cap, K]; B [G, N, K] (NK), [G, K, N]
     (KN) or PackedWeights.  Returns C [m_cap, N] (or [m_cap, N/2] with SwiGLU)
     and, with keep_aux, the pre-activations [m_cap, N].  Rows past
-    sum(group_sizes) are left untouched."""
+    sum(group_sizes) are left untouched.  split: pass the library its
+    workspace, so that a short last round of tiles is split along K."""
     packed = isinstance(B, PackedWeights)
     Bt = B.data if packed else B
     dev = _dev(A, Bt, group_sizes)
@@ -372,8 +390,10 @@ def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int
         aux = torch.empty((m_cap, N), dtype=torch.bfloat16, device=dev)
     d = GGDesc(MOE_DTYPE_BF16, MOE_RAGGED_M, b_layout, epilogue,
                MOE_OUT_F32 if out_dtype == torch.float32 else MOE_OUT_BF16, G, 0, N, Kd, m_cap)
+    ws = _gemm_workspace(d, dev) if split else None
     _check(lib().grouped_gemm(ctypes.byref(d), _ptr(A), None, _ptr(Bt), None, _ptr(group_sizes), _ptr(out),
-                              _ptr(aux), None, 0, _ptr(flag), _stream(dev)), "grouped_gemm")
+                              _ptr(aux), _ptr(ws), ws.numel() if ws is not None else 0, _ptr(flag), _stream(dev)),
+           "grouped_gemm")
     return (out, aux) if keep_aux else out
 
 

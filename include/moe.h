@@ -223,7 +223,23 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   codes uint8 [m_cap, f], C_aux (required) the E8M0 scales uint8
  *   [m_cap, f/32]; f % 32 == 0; packed weights are those packed for
  *   MOE_EPI_SWIGLU.  Rows r >= sum(s_g) are not written.
- * ws: grouped_gemm_workspace_bytes(desc) bytes (0 today).
+ * ws: optional.  grouped_gemm_workspace_bytes(desc) is 0 except for bf16
+ *   RAGGED_M calls, where it is one fp32 256 x 256 tile per compute unit
+ *   (64 MiB on MI355X).  Given that many bytes (256-byte aligned), a call
+ *   with K >= 2048 whose tiles fill at most three rounds of the grid even
+ *   if every group ends in a partial tile (G + ceil(m_cap / 256) row tiles
+ *   times the column tiles <= 3 x the workgroups) splits the tiles of its
+ *   last round along K when that round holds at most half as many tiles as
+ *   the grid has workgroups: each tile's K stages are cut into 2-4 equal
+ *   ranges on different workgroups, whose fp32 partial sums meet in ws and
+ *   are added in range order by the one that arrives last (the work of a
+ *   short last round is shared instead of leaving most of the GPU idle;
+ *   blog section "Optimization 1", full utilisation with irregular expert
+ *   shapes).  The partition depends only on the group sizes, the grid and
+ *   K, so results stay bitwise reproducible (and within a rounding of the
+ *   unsplit sums); with ws NULL or smaller, nothing is split.  A call's
+ *   arrival counters are library words handed out in 64 slots as for the
+ *   weight gradients; calls in flight together must not share ws.
  * Limits: G <= 1024; N <= 2^22 (else MOE_ERR_UNSUPPORTED);
  *   bf16: K % 64 == 0 (RAGGED_M), N % 8 == 0, M % 8 == 0;
  *   MXFP8: K % 128 == 0 (RAGGED_M), K % 64 == 0 and K >= m_cap + 63 G

@@ -63,7 +63,13 @@ moe_status_t mxfp4_quantize_launch(const uint16_t*, int64_t, int32_t, uint8_t*, 
 moe_status_t mxfp8_group_quantize_launch(const uint16_t*, int64_t, int32_t, int32_t, const int32_t*, int32_t, uint8_t*,
                                          uint8_t*, uint32_t*, hipStream_t) { return launched(); }
 moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*, const void*, const uint8_t*,
-                                 const int32_t*, void*, void*, uint32_t*, hipStream_t) { return launched(); }
+                                 const int32_t*, void*, void*, void*, size_t, uint32_t*, hipStream_t) {
+  return launched();
+}
+// the library's rule: bf16 ragged-M calls can use one fp32 256 x 256 tile per CU (256 CUs here)
+size_t grouped_gemm_ws_bytes_impl(const moe_gg_desc* d) {
+  return d->ragged == MOE_RAGGED_M && d->dtype == MOE_DTYPE_BF16 ? (size_t)256 * 256 * 256 * 4 : 0;
+}
 }
 
 namespace moe {
@@ -157,6 +163,11 @@ int main() {
   d = {MOE_DTYPE_BF16, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, 4, 64, 64, 0, 100};
   EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_OK);
   if (grouped_gemm_workspace_bytes(&d) != 0) { std::printf("FAIL: gemm workspace\n"); ++g_fail; }
+  d.ragged = MOE_RAGGED_M;
+  d.K = 64;
+  if (grouped_gemm_workspace_bytes(&d) == 0) { std::printf("FAIL: ragged-M gemm workspace\n"); ++g_fail; }
+  if (grouped_gemm_workspace_bytes(nullptr) != 0) { std::printf("FAIL: null desc workspace\n"); ++g_fail; }
+  d.ragged = MOE_RAGGED_K;
   EXPECT(moe_pack_weights(u16, 4, 64, 64, MOE_EPI_NONE, p, 4 * 64 * 64 * 2, nullptr), MOE_OK);
   EXPECT(moe_pack_weights(u16, 4, 64, 64, MOE_EPI_NONE, p, 16, nullptr), MOE_ERR_WORKSPACE);
   EXPECT(moe_pack_weights(u16, INT32_MAX, 64, 64, MOE_EPI_NONE, p, 1 << 12, nullptr), MOE_ERR_UNSUPPORTED);

@@ -948,6 +948,110 @@ def test_grouped_gemm_bitwise_deterministic(ops):
     assert torch.equal(c1, c2)
 
 
+# ------------------------------------------------------------------- split tail
+
+# three m-tiles over eight groups: the grid (sized by the groups' upper bound)
+# is more than twice the two n-tiles' six tiles, so with K = 2048 (64 stages)
+# every tile of the one round is split along K in three
+SPLIT_SIZES = np.array([300, 0, 0, 0, 0, 0, 0, 40], np.int32)
+
+
+@pytest.mark.parametrize("mode", ["nk", "packed_swiglu", "kn", "f32"])
+def test_grouped_gemm_split_tail(ops, mode):
+    """Tiles of a short last round split along K, their fp32 partials added in
+    split order by the last to arrive: the oracle's result, the same bits on
+    every call, and the unsplit kernel's result within rounding."""
+    sizes, N, Kd = SPLIT_SIZES, 512, 2048
+    say("gg split tail", mode)
+    rng = np.random.default_rng(71 + len(mode))
+    G, M = sizes.size, int(sizes.sum())
+    sz = dev(torch.from_numpy(sizes))
+    A = bf16(rng, M, Kd)
+    if mode == "kn":
+        B = bf16(rng, G, Kd, N, scale=Kd ** -0.5)
+        ref = orc.grouped_dgrad(A, B, sizes)
+        run = lambda split: ops.grouped_gemm(dev(A), dev(B), sz, b_layout=ops.MOE_B_KN, split=split)
+    elif mode == "packed_swiglu":
+        B = bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+        ref, _ = orc.gemm_swiglu(A, B, sizes, keep_gu=True)
+        P = ops.pack_weights(dev(B), ops.MOE_EPI_SWIGLU)
+        run = lambda split: ops.grouped_gemm(dev(A), P, sz, epilogue=ops.MOE_EPI_SWIGLU, split=split)
+    else:
+        B = bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+        ref = orc.grouped_gemm(A, B, sizes)
+        odt = torch.float32 if mode == "f32" else torch.bfloat16
+        run = lambda split: ops.grouped_gemm(dev(A), dev(B), sz, out_dtype=odt, split=split)
+    c1, c2, c0 = run(True), run(True), run(False)
+    torch.cuda.synchronize()
+    if mode == "f32":
+        r = orc.bf16_to_f64(ref)
+        assert np.abs(c1.cpu().double().numpy() - r).max() <= 1e-2 * np.abs(r).max()
+        assert torch.allclose(c1, c0, rtol=1e-5, atol=1e-5 * float(c0.abs().max()))
+    else:
+        assert max_rel_err(c1, ref) <= BF16_TOL
+        # one bf16 rounding apart at most: the two sum the same products in another order
+        d = (c1.float() - c0.float()).abs()
+        assert float(d.max()) <= 2 ** -7 * float(c0.float().abs().max())
+    assert torch.equal(c1, c2)
+
+
+def test_grouped_gemm_split_tail_after_whole_rounds(ops):
+    """592 tiles on a 256-workgroup grid (eight groups of about 1,024 rows,
+    N = 4096): two whole rounds, then 80 tiles split in three.  The whole
+    output against the unsplit kernel, sampled rows of every group (those
+    of the split tiles included) against the oracle."""
+    sizes = np.array([1010, 1050, 980, 1030, 1000, 1044, 1040, 1038], np.int32)
+    N, Kd = 4096, 2048
+    say("gg split tail after whole rounds")
+    rng = np.random.default_rng(77)
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    Ad, Bd, sz = dev(A), dev(B), dev(torch.from_numpy(sizes))
+    c1 = ops.grouped_gemm(Ad, Bd, sz)
+    c0 = ops.grouped_gemm(Ad, Bd, sz, split=False)
+    torch.cuda.synchronize()
+    d = (c1.float() - c0.float()).abs()
+    assert float(d.max()) <= 2 ** -7 * float(c0.float().abs().max())
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    rows = np.unique(np.concatenate([np.linspace(off[g], off[g + 1] - 1, 6).astype(np.int64) for g in range(G)]))
+    ref = orc.grouped_gemm(A, B, sizes, rows=rows)
+    assert max_rel_err(c1[torch.from_numpy(rows).cuda()], ref) <= BF16_TOL
+
+
+def test_grouped_gemm_split_tail_graph_replay(ops):
+    """A captured call replayed with group sizes that do and do not split its
+    last round (the split decision is taken on the device) matches an eager
+    call bit for bit on every replay."""
+    N, Kd, G = 512, 2048, 8
+    rng = np.random.default_rng(75)
+    m_cap = 1024
+    A, B = dev(bf16(rng, m_cap, Kd)), dev(bf16(rng, G, N, Kd, scale=Kd ** -0.5))
+    sz = dev(torch.from_numpy(SPLIT_SIZES.copy()))
+    out = torch.empty((m_cap, N), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            ops.grouped_gemm(A, B, sz, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.grouped_gemm(A, B, sz, out=out)
+    for sizes in ([300, 0, 0, 0, 0, 0, 0, 40], [1000, 0, 0, 0, 0, 0, 0, 24], [128] * 8, [0, 0, 0, 1, 0, 0, 0, 0]):
+        say("split replay", sizes)
+        sizes = np.array(sizes, np.int32)
+        M = int(sizes.sum())
+        sz.copy_(torch.from_numpy(sizes))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = ops.grouped_gemm(A, B, sz)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:M], eager[:M])
+        ref = orc.grouped_gemm(A[:M], B, sizes)
+        assert max_rel_err(out[:M], ref) <= BF16_TOL
+
+
 # ------------------------------------------------------------------- guard bands
 
 def _guarded(shape, dtype, fill):
