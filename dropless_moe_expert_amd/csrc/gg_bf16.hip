@@ -270,54 +270,8 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
 }
 
 // ------------------------------------------------------------------ split tail
-// The ragged-M kernel deals tiles to its workers in turn, so a last round of
-// t tiles keeps only t of the grid's workers busy for a whole tile.  In the
-// kernel's SPLIT instantiation (which the host picks for calls of at most
-// three rounds of long-K tiles, where a short last round is likely and
-// costly), when t is at most half the grid each of those tiles is instead
-// cut along K into S = min(4, grid / t, stages / 16) equal stage ranges
-// ("units"), the units of one tile on consecutive workers.  Every unit
-// writes its fp32 partial sums to its own slot of the caller's workspace
-// (each thread its accumulators, in register order) and counts itself in at
-// the tile's counter; the unit that brings the count to S reads the S
-// partials back and adds them in split order (so the result does not depend
-// on which unit finishes last), then runs the tile's epilogue.  The
-// partition depends only on the group sizes, the grid and K: results are
-// bitwise reproducible.  Counters: one slot of kSplitWords words per call
-// (64 slots handed out in turn), epoch-tagged as the tile queues
-// (tile_queue.h), reset for the slot's next call by the call's last
-// workgroup.
-constexpr int kMaxSplit = 4, kMinSplitStages = 16;
-constexpr int kSplitWords = 512 + 1;   // tail tiles (at most half a grid of <= 1024) + done count
-
-struct SplitSlots {
-  uint32_t w[tq::kSlots][kSplitWords];
-};
-constexpr SplitSlots initial_split_slots() {
-  SplitSlots t{};
-  for (int s = 0; s < tq::kSlots; ++s)
-    for (int i = 0; i < kSplitWords; ++i) t.w[s][i] = tq::word(tq::launch_epoch((uint64_t)s), 0u);
-  return t;
-}
+// (split_tail and its counters: gg_pipeline.h)
 __device__ SplitSlots g_split_sched = initial_split_slots();
-
-struct SplitTail {
-  int64_t full;    // tiles of the whole rounds (units [0, full) are whole tiles)
-  int64_t units;   // full + tail tiles x S
-  int S;           // splits of each tail tile (1: none)
-};
-
-__device__ __forceinline__ SplitTail split_tail(int64_t total, int grid, int nk) {
-  SplitTail r{total, total, 1};
-  const int64_t tail = total % grid;
-  if (tail == 0 || 2 * tail > grid || tail > kSplitWords - 1) return r;
-  const int S = min(kMaxSplit, min(grid / (int)tail, nk / kMinSplitStages));
-  if (S < 2) return r;
-  r.full = total - tail;
-  r.units = r.full + tail * S;
-  r.S = S;
-  return r;
-}
 
 // Unit tail_unit (tile tail_unit / S, split tail_unit % S) has its partial
 // sums in acc.  Returns true, with acc holding the tile's full sums, to the
@@ -355,21 +309,6 @@ __device__ __forceinline__ bool split_reduce(const GGArgs& a, const SplitTail& s
       acc[i][j] = v;
     }
   return true;
-}
-
-// Once per workgroup of a call that split its tail, after its last unit:
-// the last workgroup to arrive presets the slot's words for the slot's next
-// call.  box: one int of LDS no wavefront uses any more.
-__device__ __forceinline__ void split_finish(const GGArgs& a, int32_t* box) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    DeviceWord done{g_split_sched.w[a.sched_slot] + (kSplitWords - 1)};
-    box[0] = tq::finish(done, a.sched_epoch, gridDim.x);
-  }
-  __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(box[0]))
-    for (int i = threadIdx.x; i < kSplitWords; i += blockDim.x)
-      atomicExch(g_split_sched.w[a.sched_slot] + i, tq::word(a.sched_next, 0u));
 }
 
 // Weight layouts (BL): BL_NK reads B [G, N, K] rows (K contiguous); BL_PACKED
@@ -581,7 +520,7 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
     }
   }
   if constexpr (SPLIT) {
-    if (sp.S > 1) split_finish(a, reinterpret_cast<int32_t*>(b4));
+    if (sp.S > 1) split_finish(a, g_split_sched.w[a.sched_slot], reinterpret_cast<int32_t*>(b4));
   }
 }
 
@@ -823,11 +762,9 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
   using namespace fwd;
-  // The split-tail instantiation: given the workspace, for calls of at most
-  // three rounds (even with every group's last tile partial) of tiles at
-  // least 64 stages long, where a short last round is likely and costs a
-  // large share of the call.  Other calls keep the plain kernel.
-  if (b.part && max_tiles <= 3 * grid && a.K / 32 >= 64) {
+  // The split-tail instantiation (where a short last round is likely and
+  // costs a large share of the call); other calls keep the plain kernel.
+  if (use_split_tail(b.part != nullptr, max_tiles, grid, a.K / 32)) {
     const uint64_t n = launches.fetch_add(1u, std::memory_order_relaxed);
     b.sched_slot = tq::launch_slot(n);
     b.sched_epoch = tq::launch_epoch(n);

@@ -462,13 +462,61 @@ __device__ __forceinline__ void mx_k_loop(const MxLoads<PACKED>& ld, int nk, f32
   if (kt + 5 < nk) step(b1, b0, kt + 5);
 }
 
-template <int EPI, bool PACKED>
+// Split tail (gg_pipeline.h): the counters of this kernel's calls.
+__device__ SplitSlots g_split_sched_mx = initial_split_slots();
+
+// Unit tail_unit of a split tail: its partial sums (acc) go to its slot of
+// the workspace, each thread's accumulators in register order; it counts
+// itself in at its tile; true, with acc holding the tile's sums (its units'
+// partials added in split order), to the unit that completes the tile.
+__device__ __forceinline__ bool split_reduce_mx(const GGArgs& a, const SplitTail& sp, int64_t tail_unit,
+                                                f32x16_t (&acc)[MTN][MTM], int32_t* box) {
+  constexpr int SLOT = BM * BN;
+  static_assert(MTN * MTM * 16 * THREADS == SLOT, "a unit's partials fill its slot");
+  const int t = threadIdx.x;
+  const int64_t tile_tail = tail_unit / sp.S;
+  float* const mine = a.part + tail_unit * SLOT;
+#pragma unroll
+  for (int i = 0; i < MTN; ++i)
+#pragma unroll
+    for (int j = 0; j < MTM; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(mine + (((i * MTM + j) * 4 + q) * THREADS + t) * 4) =
+            f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // this thread's partials are visible to the device
+  __syncthreads();                                      // every thread's, and every wavefront has left its K loop
+  if (t == 0) {
+    DeviceWord w{g_split_sched_mx.w[a.sched_slot] + tile_tail};
+    box[0] = (int32_t)tq::take(w, a.sched_epoch) == sp.S - 1;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(box[0])) return false;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other units' partials
+  const float* const first = a.part + tile_tail * sp.S * SLOT;
+#pragma unroll
+  for (int i = 0; i < MTN; ++i)
+#pragma unroll
+    for (int j = 0; j < MTM; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t off = (((i * MTM + j) * 4 + q) * THREADS + t) * 4;
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(first + off);
+        for (int u = 1; u < sp.S; ++u) v += *reinterpret_cast<const f32x4_t*>(first + u * SLOT + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = v[e];
+      }
+  return true;
+}
+
+template <int EPI, bool PACKED, bool SPLIT = false>
 __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   __shared__ __align__(1024) uint8_t b0[MSTAGE];
   __shared__ __align__(1024) uint8_t b1[MSTAGE];
   __shared__ __align__(1024) uint8_t b2[MSTAGE];
   __shared__ __align__(1024) uint8_t b3[MSTAGE];
   __shared__ __align__(1024) uint8_t xch[NXCH * XCH_BYTES];   // X scales, 8 stages per area
+  __shared__ int32_t split_box[1];                             // SPLIT: a unit's arrival result
 
   if (blockIdx.x == 0 && threadIdx.x < 64) {
     bool neg = false;
@@ -489,9 +537,22 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
   const int64_t total = count_mtiles(a) * a.n_tiles;
   const int64_t lda_b = a.K;            // one byte per code
   const int64_t lds_b = a.K / 32;       // scale bytes per row
-  const int nk = a.K / 64;
+  const int nk_all = a.K / 64;
 
-  for (int64_t tile = wid; tile < total; tile += gridDim.x) {
+  // units: whole tiles, then (SPLIT) the split tail's stage ranges
+  const SplitTail sp = SPLIT ? split_tail(total, (int)gridDim.x, nk_all) : SplitTail{total, total, 1};
+  for (int64_t unit = wid; unit < sp.units; unit += gridDim.x) {
+    int64_t tile = unit, tail_unit = -1;
+    int kt0 = 0, nk = nk_all;   // the unit's first stage and stage count
+    if constexpr (SPLIT) {
+      if (unit >= sp.full) {
+        tail_unit = unit - sp.full;
+        tile = sp.full + tail_unit / sp.S;
+        const int part = (int)(tail_unit % sp.S);
+        kt0 = (int)((int64_t)part * nk_all / sp.S);
+        nk = (int)((int64_t)(part + 1) * nk_all / sp.S) - kt0;
+      }
+    }
     const TileGroup tg = locate(a, tile);
     const int g = tg.g, nt = tg.nt;
     const int64_t m0 = tg.m0;
@@ -523,12 +584,15 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
     } else {
       wl.init(lda_b, wrow);
     }
-    const uint8_t* xbase = a.A + m0 * lda_b;
-    const uint8_t* wbase = PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk * PK_STAGE
-                                  : a.B + (int64_t)g * nrows_b * lda_b;
     const int wstride = PACKED ? PK_STAGE : ROWB;
-    const uint8_t* xsb = a.As + m0 * lds_b;
-    const uint8_t* wsb = PACKED ? nullptr : a.Bs + (int64_t)g * nrows_b * lds_b;
+    // operands and scales from the unit's first stage kt0 on (2 scale bytes per row and stage)
+    const uint8_t* xbase = a.A + m0 * lda_b + (int64_t)kt0 * ROWB;
+    const uint8_t* wbase = (PACKED ? a.B + ((int64_t)g * a.n_tiles + nt) * nk_all * PK_STAGE
+                                   : a.B + (int64_t)g * nrows_b * lda_b) +
+                           (int64_t)kt0 * wstride;
+    const uint8_t* xsb = a.As + m0 * lds_b + 2 * kt0;
+    const uint8_t* wsb = PACKED ? nullptr : a.Bs + (int64_t)g * nrows_b * lds_b + 2 * kt0;
+    const int xlim = (int)lds_b - 2 * kt0;   // scale bytes from xsb to the end of an X row
 
     f32x16_t acc[MTN][MTM];
 #pragma unroll
@@ -537,9 +601,17 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_mx_kernel(GGArgs a) {
       for (int j = 0; j < MTM; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    const MxLoads<PACKED> ld{xl, wl, sl, xbase, wbase, wstride, xsb, wsb, (int)lds_b, (int)lds_b};
+    const MxLoads<PACKED> ld{xl, wl, sl, xbase, wbase, wstride, xsb, wsb, (int)lds_b, xlim};
     mx_k_loop<PACKED>(ld, nk, acc, b0, b1, b2, b3, xch);
+    if constexpr (SPLIT) {
+      // a split unit: partial sums to the workspace; the unit that completes
+      // the tile adds them, in split order, and runs the epilogue
+      if (tail_unit >= 0 && !split_reduce_mx(a, sp, tail_unit, acc, split_box)) continue;
+    }
     store<EPI>(a, acc, m0, rows, n0, SWI ? f : a.N, f, b0, b1, b2, b3);
+  }
+  if constexpr (SPLIT) {
+    if (sp.S > 1) split_finish(a, g_split_sched_mx.w[a.sched_slot], split_box);
   }
 }
 
@@ -757,6 +829,30 @@ moe_status_t launch_fwd_mx(const GGArgs& a, int epilogue, int packed, hipStream_
   if (grid <= 0) grid = 1;
   const dim3 g((unsigned)grid), t(fwd::THREADS);
   using namespace fwd::mx;
+  if (fwd::use_split_tail(b.part != nullptr, max_tiles, grid, a.K / 64)) {
+    // the split-tail instantiation (gg_pipeline.h); its counters' slot and epoch
+    static std::atomic<uint64_t> launches{0};
+    const uint64_t n = launches.fetch_add(1u, std::memory_order_relaxed);
+    b.sched_slot = tq::launch_slot(n);
+    b.sched_epoch = tq::launch_epoch(n);
+    b.sched_next = tq::slot_next_epoch(n);
+    if (packed) {
+      if (epilogue == MOE_EPI_SWIGLU_MXFP8) {
+        hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU_MXFP8, true, true>), g, t, 0, s, b);
+      } else if (epilogue == MOE_EPI_SWIGLU) {
+        hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU, true, true>), g, t, 0, s, b);
+      } else {
+        hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_NONE, true, true>), g, t, 0, s, b);
+      }
+    } else if (epilogue == MOE_EPI_SWIGLU_MXFP8) {
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU_MXFP8, false, true>), g, t, 0, s, b);
+    } else if (epilogue == MOE_EPI_SWIGLU) {
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU, false, true>), g, t, 0, s, b);
+    } else {
+      hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_NONE, false, true>), g, t, 0, s, b);
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
   if (packed) {
     if (epilogue == MOE_EPI_SWIGLU_MXFP8) {
       hipLaunchKernelGGL((gg_fwd_mx_kernel<MOE_EPI_SWIGLU_MXFP8, true>), g, t, 0, s, b);

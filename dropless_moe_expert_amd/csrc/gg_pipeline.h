@@ -256,5 +256,75 @@ __device__ __forceinline__ TileGroup locate(const GGArgs& a, int64_t tile) {
   return r;
 }
 
+// ------------------------------------------------------------------ split tail
+// The ragged-M kernels (bf16 and MXFP8) deal tiles to their workers in turn,
+// so a last round of t tiles keeps only t of the grid's workers busy for a
+// whole tile.  In a kernel's SPLIT instantiation (which the host picks for
+// calls of at most three rounds of long-K tiles, where a short last round is
+// likely and costly), when t is at most half the grid each of those tiles is
+// instead
+// cut along K into S = min(4, grid / t, stages / 16) equal stage ranges
+// ("units"), the units of one tile on consecutive workers.  Every unit
+// writes its fp32 partial sums to its own slot of the caller's workspace
+// (each thread its accumulators, in register order) and counts itself in at
+// the tile's counter; the unit that brings the count to S reads the S
+// partials back and adds them in split order (so the result does not depend
+// on which unit finishes last), then runs the tile's epilogue.  The
+// partition depends only on the group sizes, the grid and K: results are
+// bitwise reproducible.  Counters: one slot of kSplitWords words per call
+// (64 slots handed out in turn; each kernel file holds its own array),
+// epoch-tagged as the tile queues (tile_queue.h), reset for the slot's next
+// call by the call's last workgroup (split_finish).
+constexpr int kMaxSplit = 4, kMinSplitStages = 16;
+constexpr int kSplitWords = 512 + 1;   // tail tiles (at most half a grid of <= 1024) + done count
+
+struct SplitSlots {
+  uint32_t w[tq::kSlots][kSplitWords];
+};
+constexpr SplitSlots initial_split_slots() {
+  SplitSlots t{};
+  for (int s = 0; s < tq::kSlots; ++s)
+    for (int i = 0; i < kSplitWords; ++i) t.w[s][i] = tq::word(tq::launch_epoch((uint64_t)s), 0u);
+  return t;
+}
+struct SplitTail {
+  int64_t full;    // tiles of the whole rounds (units [0, full) are whole tiles)
+  int64_t units;   // full + tail tiles x S
+  int S;           // splits of each tail tile (1: none)
+};
+
+__device__ __forceinline__ SplitTail split_tail(int64_t total, int grid, int nk) {
+  SplitTail r{total, total, 1};
+  const int64_t tail = total % grid;
+  if (tail == 0 || 2 * tail > grid || tail > kSplitWords - 1) return r;
+  const int S = min(kMaxSplit, min(grid / (int)tail, nk / kMinSplitStages));
+  if (S < 2) return r;
+  r.full = total - tail;
+  r.units = r.full + tail * S;
+  r.S = S;
+  return r;
+}
+
+// Once per workgroup of a call that split its tail, after its last unit:
+// the last workgroup to arrive presets the slot's words (w) for the slot's
+// next call.  box: one int of LDS no wavefront uses any more.
+__device__ __forceinline__ void split_finish(const GGArgs& a, uint32_t* w, int32_t* box) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    DeviceWord done{w + (kSplitWords - 1)};
+    box[0] = tq::finish(done, a.sched_epoch, gridDim.x);
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(box[0]))
+    for (int i = threadIdx.x; i < kSplitWords; i += blockDim.x) atomicExch(w + i, tq::word(a.sched_next, 0u));
+}
+
+// The host's choice of a SPLIT instantiation: given the workspace, for calls
+// whose tiles fill at most three rounds even with every group's last tile
+// partial, of at least 64 stages each.
+inline bool use_split_tail(bool have_ws, int64_t max_tiles, int64_t grid, int stages) {
+  return have_ws && max_tiles <= 3 * grid && stages >= 64;
+}
+
 }  // namespace fwd
 }  // namespace moe

@@ -12,7 +12,7 @@
 //    with B [G, K, N]): gg_bf16.hip, gg_fwd_kernel (with the caller's
 //    workspace, the tiles of a short last round split along K);
 //  * ragged K, bf16 (weight gradients): gg_bf16.hip, gg_wgrad_kernel;
-//  * ragged M, MXFP8: gg_fwd_mx.hip, gg_fwd_mx_kernel;
+//  * ragged M, MXFP8: gg_fwd_mx.hip, gg_fwd_mx_kernel (split tail as bf16);
 //  * ragged K, MXFP8 (operands from mxfp8_quantize_transposed): gg_fwd_mx.hip,
 //    gg_wgrad_mx_kernel.
 // Every grid is a function of host arguments only (CU count, m_cap, G, N, K).
@@ -27,9 +27,10 @@ moe_status_t launch_fwd_mx4(const GGArgs& a, int epilogue, hipStream_t s);      
 size_t fwd_split_workspace_bytes();                                                                  // gg_bf16.hip
 }  // namespace moe
 
-// The workspace a call can use: the bf16 ragged-M kernel's split tail
+// The workspace a call can use: the bf16 and MXFP8 ragged-M kernels' split tail
 extern "C" size_t grouped_gemm_ws_bytes_impl(const moe_gg_desc* d) {
-  if (d->ragged == MOE_RAGGED_M && d->dtype == MOE_DTYPE_BF16) return moe::fwd_split_workspace_bytes();
+  if (d->ragged == MOE_RAGGED_M && (d->dtype == MOE_DTYPE_BF16 || d->dtype == MOE_DTYPE_MXFP8))
+    return moe::fwd_split_workspace_bytes();
   return 0;
 }
 

@@ -344,7 +344,7 @@ def pack_weights_mxfp8(Bq: torch.Tensor, Bs: torch.Tensor, epilogue: int = MOE_E
     return PackedWeights(data, G, N, Kd, epilogue, mxfp8=True)
 
 
-_gemm_ws = {}   # device index -> the bf16 ragged-M calls' workspace (one per device)
+_gemm_ws = {}   # device index -> the ragged-M calls' workspace (one per device)
 
 
 def _gemm_workspace(d: "GGDesc", dev: torch.device) -> Optional[torch.Tensor]:
@@ -466,14 +466,15 @@ def grouped_gemm_mxfp4(Aq: torch.Tensor, As: torch.Tensor, Bq: torch.Tensor, Bs:
 def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torch.Tensor],
                        group_sizes: torch.Tensor, *, epilogue: int = MOE_EPI_NONE,
                        out: Optional[torch.Tensor] = None, out_scale: Optional[torch.Tensor] = None,
-                       keep_aux: bool = False, flag: Optional[torch.Tensor] = None):
+                       keep_aux: bool = False, flag: Optional[torch.Tensor] = None, split: bool = True):
     """MXFP8 ragged-M grouped GEMM.  Aq uint8 [m_cap, K], As uint8 [m_cap, K/32],
     Bq uint8 [G, N, K] with Bs uint8 [G, N, K/32], or Bq = PackedWeights from
     pack_weights_mxfp8 (Bs None) -> bf16 [m_cap, N] (or N/2 with SwiGLU).
     With MOE_EPI_SWIGLU_MXFP8 (weights packed for MOE_EPI_SWIGLU, or
     unpacked) -> (codes uint8 [m_cap, N/2], scales uint8 [m_cap, N/64]): the
     SwiGLU output quantised as mxfp8_quantize(h, 0) would.  keep_aux (with
-    MOE_EPI_SWIGLU) -> (h, pre-activations bf16 [m_cap, N])."""
+    MOE_EPI_SWIGLU) -> (h, pre-activations bf16 [m_cap, N]).  split: pass
+    the library its workspace (a short last round of tiles split along K)."""
     packed = isinstance(Bq, PackedWeights)
     m_cap, Kd = Aq.shape
     fused = epilogue == MOE_EPI_SWIGLU_MXFP8
@@ -501,9 +502,10 @@ def grouped_gemm_mxfp8(Aq: torch.Tensor, As: torch.Tensor, Bq, Bs: Optional[torc
             raise MoeError("keep_aux needs the SwiGLU epilogue")
         aux = torch.empty((m_cap, N), dtype=torch.bfloat16, device=dev)
     d = GGDesc(MOE_DTYPE_MXFP8, MOE_RAGGED_M, layout, epilogue, MOE_OUT_BF16, G, 0, N, Kd, m_cap)
+    ws = _gemm_workspace(d, dev) if split else None
     _check(lib().grouped_gemm(ctypes.byref(d), _ptr(Aq), _ptr(As), _ptr(Bt), None if packed else _ptr(Bs),
-                              _ptr(group_sizes), _ptr(out), _ptr(out_scale) if fused else _ptr(aux), None, 0,
-                              _ptr(flag), _stream(dev)), "grouped_gemm (mxfp8)")
+                              _ptr(group_sizes), _ptr(out), _ptr(out_scale) if fused else _ptr(aux), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _ptr(flag), _stream(dev)), "grouped_gemm (mxfp8)")
     if fused:
         return out, out_scale
     return (out, aux) if keep_aux else out

@@ -224,9 +224,10 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   [m_cap, f/32]; f % 32 == 0; packed weights are those packed for
  *   MOE_EPI_SWIGLU.  Rows r >= sum(s_g) are not written.
  * ws: optional.  grouped_gemm_workspace_bytes(desc) is 0 except for bf16
- *   RAGGED_M calls, where it is one fp32 256 x 256 tile per compute unit
- *   (64 MiB on MI355X).  Given that many bytes (256-byte aligned), a call
- *   with K >= 2048 whose tiles fill at most three rounds of the grid even
+ *   and MXFP8 RAGGED_M calls, where it is one fp32 256 x 256 tile per
+ *   compute unit (64 MiB on MI355X).  Given that many bytes (256-byte
+ *   aligned), a call of at least 64 K stages (K >= 2048 in bf16, K >= 4096
+ *   in MXFP8) whose tiles fill at most three rounds of the grid even
  *   if every group ends in a partial tile (G + ceil(m_cap / 256) row tiles
  *   times the column tiles <= 3 x the workgroups) splits the tiles of its
  *   last round along K when that round holds at most half as many tiles as

@@ -66,9 +66,11 @@ moe_status_t grouped_gemm_launch(const moe_gg_desc*, const void*, const uint8_t*
                                  const int32_t*, void*, void*, void*, size_t, uint32_t*, hipStream_t) {
   return launched();
 }
-// the library's rule: bf16 ragged-M calls can use one fp32 256 x 256 tile per CU (256 CUs here)
+// the library's rule: bf16 and MXFP8 ragged-M calls can use one fp32 256 x 256 tile per CU (256 CUs here)
 size_t grouped_gemm_ws_bytes_impl(const moe_gg_desc* d) {
-  return d->ragged == MOE_RAGGED_M && d->dtype == MOE_DTYPE_BF16 ? (size_t)256 * 256 * 256 * 4 : 0;
+  return d->ragged == MOE_RAGGED_M && (d->dtype == MOE_DTYPE_BF16 || d->dtype == MOE_DTYPE_MXFP8)
+             ? (size_t)256 * 256 * 256 * 4
+             : 0;
 }
 }
 

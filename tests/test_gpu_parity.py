@@ -1018,6 +1018,74 @@ def test_grouped_gemm_split_tail_after_whole_rounds(ops):
     assert max_rel_err(c1[torch.from_numpy(rows).cuda()], ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("mode", ["nk", "packed", "packed_swiglu", "fused_quant"])
+def test_grouped_gemm_mxfp8_split_tail(ops, mode):
+    """The MXFP8 kernel's split tail (K = 4096: 64 stages, three ranges per
+    tile): the oracle's result on the same codes, the same bits on every
+    call, the unsplit kernel's result within rounding; with the quantising
+    epilogue, codes and scales of the split run's h equal quantising its own
+    bf16 h."""
+    sizes, N, Kd = SPLIT_SIZES, 512, 4096
+    say("gg mxfp8 split tail", mode)
+    rng = np.random.default_rng(81 + len(mode))
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    aq, as_ = orc.mxfp8_quantize(A, 0)
+    bq, bs = orc.mxfp8_quantize(orc.u16(B).reshape(-1, Kd), 0)
+    bq, bs = bq.reshape(G, N, Kd), bs.reshape(G, N, Kd // 32)
+    t = lambda a: dev(torch.from_numpy(np.ascontiguousarray(a)))
+    sz = t(sizes)
+    swi = mode != "nk" and mode != "packed"
+    ref = orc.mx_grouped_gemm(aq, as_, bq, bs, sizes, swiglu=swi)
+    epi = ops.MOE_EPI_SWIGLU if swi else ops.MOE_EPI_NONE
+    Bw, Bsc = (ops.pack_weights_mxfp8(t(bq), t(bs), epi), None) if mode.startswith("packed") else (t(bq), t(bs))
+    if mode == "fused_quant":
+        run = lambda split: ops.grouped_gemm_mxfp8(t(aq), t(as_), Bw, Bsc, sz, epilogue=ops.MOE_EPI_SWIGLU_MXFP8,
+                                                   split=split)
+        (q1, s1), (q2, s2) = run(True), run(True)
+        h = ops.grouped_gemm_mxfp8(t(aq), t(as_), Bw, Bsc, sz, epilogue=ops.MOE_EPI_SWIGLU)
+        qh, sh = ops.mxfp8_quantize(h, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(q1, q2) and torch.equal(s1, s2)
+        assert torch.equal(q1[:M], qh[:M]) and torch.equal(s1[:M], sh[:M])
+        assert rel_l2(h[:M], ref) <= MX_TOL
+        return
+    run = lambda split: ops.grouped_gemm_mxfp8(t(aq), t(as_), Bw, Bsc, sz, epilogue=epi, split=split)
+    c1, c2, c0 = run(True), run(True), run(False)
+    torch.cuda.synchronize()
+    assert rel_l2(c1[:M], ref) <= MX_TOL and max_rel_err(c1[:M], ref) <= 2 * BF16_TOL
+    assert torch.equal(c1, c2)
+    d = (c1[:M].float() - c0[:M].float()).abs()
+    assert float(d.max()) <= 2 ** -7 * float(c0[:M].float().abs().max())
+
+
+def test_grouped_gemm_mxfp8_split_tail_after_whole_rounds(ops):
+    """592 MXFP8 tiles on a 256-workgroup grid (eight groups of about 1,024
+    rows, N = 4096, K = 4096): two whole rounds, then 80 tiles split in
+    three; the whole output against the unsplit kernel, sampled rows of every
+    group against the oracle."""
+    sizes = np.array([1010, 1050, 980, 1030, 1000, 1044, 1040, 1038], np.int32)
+    N, Kd = 4096, 4096
+    say("gg mxfp8 split tail after whole rounds")
+    rng = np.random.default_rng(83)
+    G, M = sizes.size, int(sizes.sum())
+    A, B = bf16(rng, M, Kd), bf16(rng, G, N, Kd, scale=Kd ** -0.5)
+    aq, as_ = ops.mxfp8_quantize(dev(A), 0)
+    bq, bs = ops.mxfp8_quantize(dev(B).reshape(-1, Kd), 0)
+    bq, bs = bq.reshape(G, N, Kd), bs.reshape(G, N, Kd // 32)
+    sz = dev(torch.from_numpy(sizes))
+    c1 = ops.grouped_gemm_mxfp8(aq, as_, bq, bs, sz)
+    c0 = ops.grouped_gemm_mxfp8(aq, as_, bq, bs, sz, split=False)
+    torch.cuda.synchronize()
+    d = (c1.float() - c0.float()).abs()
+    assert float(d.max()) <= 2 ** -7 * float(c0.float().abs().max())
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    rows = np.unique(np.concatenate([np.linspace(off[g], off[g + 1] - 1, 6).astype(np.int64) for g in range(G)]))
+    h = lambda x: x.cpu().numpy()
+    ref = orc.mx_grouped_gemm(h(aq), h(as_), h(bq), h(bs), sizes, rows=rows)
+    assert rel_l2(c1[torch.from_numpy(rows).cuda()], ref) <= MX_TOL
+
+
 def test_grouped_gemm_split_tail_graph_replay(ops):
     """A captured call replayed with group sizes that do and do not split its
     last round (the split decision is taken on the device) matches an eager
