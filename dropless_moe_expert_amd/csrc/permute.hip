@@ -11,10 +11,11 @@
 //               the chunk = running count + lanes below it with the same
 //               expert (found with 8 ballots over the id bits).  Writes the
 //               local rank of every pair and the chunk's per-expert counts.
-//   2. scan:    one workgroup: per expert, an exclusive scan over chunks
-//               (each expert's chunks split over 1024 / E threads, loads
-//               batched); the totals are group_sizes; their exclusive scan is
-//               group_offsets; chunk bases become absolute row offsets.
+//   2. scan:    one workgroup: each expert's chunks split over 1024 / E
+//               threads (a thread's loads all in flight, kept in registers);
+//               one workgroup-wide scan of the parts' sums in expert-major
+//               order gives every part's absolute first row, hence
+//               group_offsets, group_sizes and the chunk bases.
 //   3. scatter: one wavefront per token: row r = base[chunk][e] + local rank
 //               for each of its K pairs; writes perm_dst / perm_src and copies
 //               the token's row once from HBM to its K destinations (16-byte
@@ -66,71 +67,100 @@ __global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restr
   for (int e = lane; e < E; e += 64) chunk_counts[(int64_t)blockIdx.x * E + e] = running[e];
 }
 
+// Scan: thread t owns part p = t / E of expert e = t % E (its loads of a
+// chunk row are then consecutive), P = NT / E parts per expert, each a
+// contiguous range of chunks.  The parts' sums, laid out expert-major
+// (e P + p), go through one workgroup-wide exclusive scan: in that order
+// expert e's rows follow every smaller expert's, so the scan at (e, p) is
+// directly the absolute row of the part's first pair (group_offsets[e] +
+// the rows of the expert's earlier parts), and at (e, 0) the expert's
+// offset.  A thread's chunk counts (at most kScanRegs of them) stay in
+// registers between the sum and the write-back of the chunk bases, all of
+// its loads in flight at once.
+constexpr int kScanRegs = 64;
+
+template <int NT>
+__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t* wsum, int32_t* total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int NW = NT / 64;
+  int32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int32_t x = lane < NW ? wsum[lane] : 0, xi = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t u = __shfl_up(xi, o, 64);
+      if (lane >= o) xi += u;
+    }
+    if (lane < NW) wsum[lane] = xi - x;   // exclusive prefix of the wavefront totals
+    if (lane == NW - 1) wsum[NW] = xi;    // the grand total
+  }
+  __syncthreads();
+  *total = wsum[NW];
+  return wsum[w] + incl - v;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void permute_scan_kernel(int32_t* __restrict__ chunk_counts, int nchunk, int E,
                                                            int32_t* __restrict__ group_sizes,
                                                            int32_t* __restrict__ group_offsets) {
   __shared__ int32_t part[NT];
-  __shared__ int32_t tot[NT];
-  // thread (e, p): expert e = tid % E, part p = tid / E of P = NT / E parts,
-  // each a contiguous range of chunks
+  __shared__ int32_t wsum[NT / 64 + 1];
   const int tid = threadIdx.x;
   const int P = NT / E;
   const int e = tid % E, p = tid / E;
   const bool active = p < P;
   const int per = (nchunk + P - 1) / P;
   const int c0 = min(nchunk, p * per), c1 = min(nchunk, c0 + per);
-  constexpr int B = 8;   // loads in flight per thread
+  const int n = active ? c1 - c0 : 0;
+  int32_t* const col = chunk_counts + (int64_t)c0 * E + e;   // this thread's chunk counts, E apart
+  const bool in_regs = per <= kScanRegs;                      // uniform
+  int32_t v[kScanRegs];
   int32_t sum = 0;
-  if (active) {
-    for (int c = c0; c < c1; c += B) {
-      int32_t v[B];
+  if (in_regs) {
 #pragma unroll
-      for (int b = 0; b < B; ++b) v[b] = (c + b < c1) ? chunk_counts[(int64_t)(c + b) * E + e] : 0;
+    for (int b = 0; b < kScanRegs; ++b) v[b] = b < n ? col[(int64_t)b * E] : 0;
 #pragma unroll
-      for (int b = 0; b < B; ++b) sum += v[b];
-    }
+    for (int b = 0; b < kScanRegs; ++b) sum += v[b];
+  } else {
+    for (int b = 0; b < n; ++b) sum += col[(int64_t)b * E];
   }
-  part[tid] = active ? sum : 0;
+  // expert-major slot of this part; the threads past E P hold zeros at the end
+  const int slot = active ? e * P + p : tid;
+  part[slot] = sum;
   __syncthreads();
-  // exclusive prefix of this thread's part within its expert, and the expert total
-  int32_t before = 0, total = 0;
-  if (active) {
-    for (int q = 0; q < P; ++q) {
-      const int32_t v = part[q * E + e];
-      before += (q < p) ? v : 0;
-      total += v;
-    }
-  }
-  // exclusive scan over experts (E <= 256), Hillis-Steele in LDS
-  tot[tid] = (active && p == 0) ? total : 0;
+  const int32_t mine = part[tid];
+  int32_t total;
+  const int32_t excl = block_excl_scan<NT>(mine, wsum, &total);
   __syncthreads();
-  int32_t incl = tot[tid];
-  for (int o = 1; o < NT; o <<= 1) {
-    const int32_t add = (tid >= o) ? tot[tid - o] : 0;
-    __syncthreads();
-    incl += add;
-    tot[tid] = incl;
-    __syncthreads();
+  part[tid] = excl;   // exclusive scan at each expert-major slot
+  __syncthreads();
+  if (!active) return;
+  const int32_t base = part[slot];   // the row of this part's first pair
+  if (p == 0) {
+    const int32_t next = e + 1 < E ? part[(e + 1) * P] : total;
+    group_offsets[e] = base;
+    group_sizes[e] = next - base;
+    if (e == E - 1) group_offsets[E] = total;
   }
-  // tot[e] is now the inclusive prefix of the totals (threads e < E hold p == 0)
-  if (active) {
-    const int32_t goff = tot[e] - total;
-    if (p == 0) {
-      group_sizes[e] = total;
-      group_offsets[e] = goff;
-      if (e == E - 1) group_offsets[E] = tot[e];
+  int32_t run = base;
+  if (in_regs) {
+#pragma unroll
+    for (int b = 0; b < kScanRegs; ++b) {
+      if (b < n) col[(int64_t)b * E] = run;   // absolute base of the chunk
+      run += v[b];
     }
-    int32_t run = goff + before;
-    for (int c = c0; c < c1; c += B) {
-      int32_t v[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) v[b] = (c + b < c1) ? chunk_counts[(int64_t)(c + b) * E + e] : 0;
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        if (c + b < c1) chunk_counts[(int64_t)(c + b) * E + e] = run;   // absolute base of the chunk
-        run += v[b];
-      }
+  } else {
+    for (int b = 0; b < n; ++b) {
+      const int32_t c = col[(int64_t)b * E];
+      col[(int64_t)b * E] = run;
+      run += c;
     }
   }
 }
