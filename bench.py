@@ -474,6 +474,9 @@ def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
     t_dw2 = timer(lambda: ops.grouped_gemm_wgrad(dyp, s["h"], sizes, out=dw2, flag=flag))
     dgu = ops.swiglu_backward(s["gu"], dh, sizes)
     t_sb = timer.bw(lambda: ops.swiglu_backward(s["gu"], dh, sizes, out=dgu))
+    # the path moe_backward takes: SwiGLU's backward in the data gradient's epilogue (dh never stored)
+    t_dhf = timer(lambda: ops.grouped_gemm(dyp, w2, sizes, b_layout=ops.MOE_B_KN,
+                                           epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=s["gu"], out=dgu, flag=flag))
     dxp = ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, flag=flag)
     t_dx = timer(lambda: ops.grouped_gemm(dgu, w1, sizes, b_layout=ops.MOE_B_KN, out=dxp, flag=flag))
     dw1 = ops.grouped_gemm_wgrad(dgu, s["x_perm"], sizes, flag=flag)
@@ -485,11 +488,12 @@ def bench_finegrained(torch, ops, L, dev, timer, flag, steps) -> dict:
         "dgrad_down": flop_entry(t_dh, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
         "wgrad_down": flop_entry(t_dw2, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
         "swiglu_backward": byte_entry(t_sb, M * 2 * f * 2 + M * f * 2 + M * 2 * f * 2),
+        "dgrad_down_swiglu_bwd": flop_entry(t_dhf, 2.0 * M * d * f, BF16_PEAK_TFLOPS),
         "dgrad_gate_up": flop_entry(t_dx, 2.0 * M * 2 * f * d, BF16_PEAK_TFLOPS),
         "wgrad_gate_up": flop_entry(t_dw1, 2.0 * M * 2 * f * d, BF16_PEAK_TFLOPS),
         "fold_dx": byte_entry(t_fold, M * d * 2 + M * 4 + T * d * 2),
     })
-    bsum = t_cb + t_dh + t_dw2 + t_sb + t_dx + t_dw1 + t_fold
+    bsum = t_cb + t_dhf + t_dw2 + t_dx + t_dw1 + t_fold
     # the whole forward + backward back to back
     for _ in range(2):
         y, sv = ops.moe_forward(lg, x, w1, w2, K, keep=True, flag=flag)

@@ -253,7 +253,8 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
     return grouped_gemm_launch(d, A, A_scale, B, B_scale, group_sizes, C, C_aux, ws, ws_bytes, err_flag, S(stream));
   }
   if (d->out_dtype != MOE_OUT_BF16 && d->out_dtype != MOE_OUT_F32) return MOE_ERR_UNSUPPORTED;
-  if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU && d->epilogue != MOE_EPI_SWIGLU_MXFP8)
+  if (d->epilogue != MOE_EPI_NONE && d->epilogue != MOE_EPI_SWIGLU && d->epilogue != MOE_EPI_SWIGLU_MXFP8 &&
+      d->epilogue != MOE_EPI_SWIGLU_BWD)
     return MOE_ERR_UNSUPPORTED;
   if (d->N % 8) return MOE_ERR_UNSUPPORTED;
   if (d->ragged == MOE_RAGGED_M) {
@@ -264,6 +265,13 @@ moe_status_t grouped_gemm(const moe_gg_desc* d, const void* A, const uint8_t* A_
     } else if (d->epilogue == MOE_EPI_SWIGLU_MXFP8) {
       // codes to C, scales to C_aux (1-byte elements: 4-byte aligned rows of codes)
       if (d->dtype != MOE_DTYPE_MXFP8 || d->out_dtype != MOE_OUT_BF16 || (d->N / 2) % 32) return MOE_ERR_UNSUPPORTED;
+      if (!C_aux) return MOE_ERR_INVALID_ARG;
+    } else if (d->epilogue == MOE_EPI_SWIGLU_BWD) {
+      // dgu to C [m_cap, 2N] from the pre-activations in C_aux [m_cap, 2N]
+      // (its row pitch is 2N: 256 rows of it stay within 32-bit byte offsets)
+      if (d->dtype != MOE_DTYPE_BF16 || d->b_layout != MOE_B_KN || d->out_dtype != MOE_OUT_BF16 ||
+          d->N > (1 << 21))
+        return MOE_ERR_UNSUPPORTED;
       if (!C_aux) return MOE_ERR_INVALID_ARG;
     } else if (C_aux) {
       return MOE_ERR_INVALID_ARG;

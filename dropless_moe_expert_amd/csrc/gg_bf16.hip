@@ -57,7 +57,10 @@ static_assert(KRows<NWAVE>::N == Rows<BN, NWAVE>::N, "a K-outer weight stage tak
 enum { BL_NK = 0, BL_PACKED = 1, BL_KN = 2 };
 // kernel-internal epilogue: SwiGLU that also stores the pre-activations
 // (C_aux != NULL); its own instantiation keeps the h-only SwiGLU kernel lean
-constexpr int EPI_SWIGLU_AUX = 3;
+constexpr int EPI_SWIGLU_AUX = 7;
+static_assert(EPI_SWIGLU_AUX != MOE_EPI_NONE && EPI_SWIGLU_AUX != MOE_EPI_SWIGLU &&
+                  EPI_SWIGLU_AUX != MOE_EPI_SWIGLU_MXFP8 && EPI_SWIGLU_AUX != MOE_EPI_SWIGLU_BWD,
+              "a kernel-internal epilogue value");
 constexpr bool is_swiglu(int epi) { return epi == MOE_EPI_SWIGLU || epi == EPI_SWIGLU_AUX; }
 
 // MFMA fragments of one stage: 8 W (n) and up to 4 X (m) 16x32 slices per lane
@@ -186,7 +189,10 @@ __device__ __forceinline__ void store(const GGArgs& a, f32x4_t (&acc)[TN][TM], i
 // rows); ST_H: SwiGLU's h, C [., f], 128 columns from n0 (256 bytes);
 // ST_AUX: the pre-activations C_aux [., 2f], the tile's 128 gate columns
 // from n0 then its 128 up columns from f + n0 (512 bytes).
-enum { ST_PLAIN = 0, ST_H = 1, ST_AUX = 2 };
+// ST_BWD: the data gradient dh (staged as ST_PLAIN) leaves as SwiGLU's
+// backward, C [., 2f] = [dg | du] from the forward's pre-activations in
+// C_aux [., 2f] (read).
+enum { ST_PLAIN = 0, ST_H = 1, ST_AUX = 2, ST_BWD = 3 };
 
 // hp: ST_H takes h already rounded and packed (hp[i][j] for acc[i][j] and
 // acc[i + TN/2][j]) instead of forming it from acc
@@ -210,7 +216,7 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
 #pragma unroll
   for (int j = 0; j < ACT; ++j) {
     const int rl = j * 16 + r16;   // row within the slot
-    if constexpr (MODE == ST_PLAIN) {
+    if constexpr (MODE == ST_PLAIN || MODE == ST_BWD) {
 #pragma unroll
       for (int i = 0; i < TN; ++i) put(rl, wn * WTN + i * 16 + g4 * 4, pack4(acc[i][j]));
     } else {
@@ -237,6 +243,70 @@ __device__ __forceinline__ void store_staged(const GGArgs& a, f32x4_t (&acc)[TN]
   constexpr int NPT = BM * UR / THREADS;   // 16-byte pieces per thread
   constexpr int NB = 4;
   static_assert(BM * UR % THREADS == 0 && NPT % NB == 0, "whole batches");
+  if constexpr (MODE == ST_BWD) {
+    // SwiGLU backward of each 8-column piece of dh: its gate and up pieces
+    // (C_aux, row pitch 2f) come in one batch ahead, so a batch's loads are
+    // in flight while the batch before it is formed and stored; dg and du
+    // go to C (row pitch 2f) at the piece's column and f + that column
+    const int64_t ld2 = 2 * (int64_t)ncols;   // ncols = f
+    const uint8_t* const gbase = a.Caux + m0 * ld2 * 2;
+    uint8_t* const cbase = a.C + m0 * ld2 * 2;
+    auto piece = [&](int k, int& row, int& col) {
+      const int c = threadIdx.x + k * THREADS;
+      row = c / UR;
+      col = n0 + 8 * (c - row * UR);
+    };
+    uint4 gv0[NB], uv0[NB], gv1[NB], uv1[NB];
+    auto load = [&](int k0, uint4 (&gv)[NB], uint4 (&uv)[NB]) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        int row, col;
+        piece(k0 + k, row, col);
+        if (row < rows && col < ncols) {
+          const uint32_t o = (uint32_t)(row * ld2 + col) * 2u;
+          gv[k] = *reinterpret_cast<const uint4*>(gbase + o);
+          uv[k] = *reinterpret_cast<const uint4*>(gbase + o + (uint32_t)ncols * 2u);
+        }
+      }
+    };
+    // batch k0 (its gate and up pieces in gv, uv): issue the next batch's
+    // loads into (gn, un), then form and store this one
+    auto batch = [&](int k0, const uint4 (&gv)[NB], const uint4 (&uv)[NB], uint4 (&gn)[NB], uint4 (&un)[NB]) {
+      uint4 v[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int c = threadIdx.x + (k0 + k) * THREADS;
+        const int row = c / UR, u = c - row * UR;
+        const int rl = row % WTM;
+        v[k] = *reinterpret_cast<const uint4*>(buf(row / WTM) + rl * RB + ((u ^ (rl % UR)) << 4));
+      }
+      if (k0 + NB < NPT) load(k0 + NB, gn, un);
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        int row, col;
+        piece(k0 + k, row, col);
+        if (row < rows && col < ncols) {
+          float g[8], uu[8], dh[8], dg[8], du[8];
+          unpack8(gv[k], g);
+          unpack8(uv[k], uu);
+          unpack8(v[k], dh);   // dh as stored: rounded to bf16
+#pragma unroll
+          for (int e = 0; e < 8; ++e) swiglu_grad(g[e], uu[e], dh[e], dg[e], du[e]);
+          const uint32_t o = (uint32_t)(row * ld2 + col) * 2u;
+          *reinterpret_cast<uint4*>(cbase + o) = pack8(dg);
+          *reinterpret_cast<uint4*>(cbase + o + (uint32_t)ncols * 2u) = pack8(du);
+        }
+      }
+    };
+    static_assert(NPT % (2 * NB) == 0, "whole pairs of batches");
+    load(0, gv0, uv0);
+#pragma unroll 1
+    for (int k0 = 0; k0 < NPT; k0 += 2 * NB) {
+      batch(k0, gv0, uv0, gv1, uv1);
+      batch(k0 + NB, gv1, uv1, gv0, uv0);
+    }
+    return;
+  }
   // the tile's rows start at a uniform base; a piece is a 32-bit offset
   // from it (256 rows of at most 2^22 bf16 columns)
   const int ld = MODE == ST_PLAIN ? ncols : MODE == ST_H ? f : 2 * f;
@@ -500,6 +570,8 @@ __global__ void __launch_bounds__(THREADS, 1) gg_fwd_kernel(GGArgs a) {
         store_staged<ST_AUX, ACT>(a, acc, m0, rows, n0, 0, f, xrow0, b0, b1, b2, b3);
         __syncthreads();
         store_staged<ST_H, ACT>(a, acc, m0, rows, n0, 0, f, xrow0, b0, b1, b2, b3, hp);
+      } else if constexpr (OUT == MOE_OUT_BF16 && EPI == MOE_EPI_SWIGLU_BWD) {
+        store_staged<ST_BWD, ACT>(a, acc, m0, rows, n0, a.N, f, xrow0, b0, b1, b2, b3);
       } else if constexpr (OUT == MOE_OUT_BF16) {
         store_staged<EPI == MOE_EPI_SWIGLU ? ST_H : ST_PLAIN, ACT>(a, acc, m0, rows, n0, a.N, f, xrow0, b0, b1, b2,
                                                                   b3);
@@ -771,7 +843,9 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
     b.sched_next = tq::slot_next_epoch(n);
     if (b_layout == MOE_B_KN) {
       if (epilogue == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
-      if (out_f32) {
+      if (epilogue == MOE_EPI_SWIGLU_BWD) {
+        hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU_BWD, MOE_OUT_BF16, BL_KN, true>), g, t, 0, s, b);
+      } else if (out_f32) {
         hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_KN, true>), g, t, 0, s, b);
       } else {
         hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_KN, true>), g, t, 0, s, b);
@@ -803,7 +877,9 @@ moe_status_t launch_fwd(const GGArgs& a, int epilogue, int out_f32, int b_layout
   }
   if (b_layout == MOE_B_KN) {
     if (epilogue == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
-    if (out_f32) {
+    if (epilogue == MOE_EPI_SWIGLU_BWD) {
+      hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_SWIGLU_BWD, MOE_OUT_BF16, BL_KN>), g, t, 0, s, b);
+    } else if (out_f32) {
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_F32, BL_KN>), g, t, 0, s, b);
     } else {
       hipLaunchKernelGGL((gg_fwd_kernel<MOE_EPI_NONE, MOE_OUT_BF16, BL_KN>), g, t, 0, s, b);

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoe.so")
 MOE_DTYPE_BF16, MOE_DTYPE_MXFP8, MOE_DTYPE_MXFP4 = 0, 1, 2
 MOE_RAGGED_M, MOE_RAGGED_K = 0, 1
 MOE_B_NK, MOE_B_KN, MOE_B_PACKED = 0, 1, 2
-MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_MXFP8 = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_SWIGLU_MXFP8, MOE_EPI_SWIGLU_BWD = 0, 1, 2, 3
 MOE_OUT_BF16, MOE_OUT_F32 = 0, 1
 
 FLAG_BAD_EXPERT_ID = 0x1
@@ -367,7 +367,9 @@ def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int
                  flag: Optional[torch.Tensor] = None, split: bool = True):
     """Ragged-M grouped GEMM, bf16.  A [m_cap, K]; B [G, N, K] (NK), [G, K, N]
     (KN) or PackedWeights.  Returns C [m_cap, N] (or [m_cap, N/2] with SwiGLU)
-    and, with keep_aux, the pre-activations [m_cap, N].  Rows past
+    and, with keep_aux, the pre-activations [m_cap, N].  With
+    MOE_EPI_SWIGLU_BWD (KN): aux = the forward's pre-activations [m_cap, 2N]
+    (read), returns [dg | du] [m_cap, 2N] from dh = bf16(A Bop).  Rows past
     sum(group_sizes) are left untouched.  split: pass the library its
     workspace, so that a short last round of tiles is split along K."""
     packed = isinstance(B, PackedWeights)
@@ -383,7 +385,9 @@ def grouped_gemm(A: torch.Tensor, B, group_sizes: torch.Tensor, *, b_layout: int
         assert B.dtype == torch.bfloat16
     G = B.shape[0]
     N = B.shape[2] if b_layout == MOE_B_KN else B.shape[1]
-    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else N
+    ncols = N // 2 if epilogue == MOE_EPI_SWIGLU else 2 * N if epilogue == MOE_EPI_SWIGLU_BWD else N
+    if epilogue == MOE_EPI_SWIGLU_BWD and (aux is None or aux.shape != (m_cap, 2 * N)):
+        raise MoeError("MOE_EPI_SWIGLU_BWD reads the forward's pre-activations: aux [m_cap, 2N]")
     if out is None:
         out = torch.empty((m_cap, ncols), dtype=out_dtype, device=dev)
     if keep_aux and aux is None:
@@ -725,14 +729,22 @@ def moe_forward_mxfp4(logits: torch.Tensor, x: torch.Tensor, w1: tuple, w2: tupl
 
 
 def moe_backward(dy: torch.Tensor, saved: dict, w1p: torch.Tensor, w2: torch.Tensor, K: int,
-                 flag: Optional[torch.Tensor] = None):
-    """Backward of moe_forward (routing weights' gradient included, router logits' not)."""
+                 flag: Optional[torch.Tensor] = None, fused: bool = True):
+    """Backward of moe_forward (routing weights' gradient included, router
+    logits' not).  fused: the down projection's data gradient forms SwiGLU's
+    backward in its epilogue (dh is not written; None in the result); else
+    dh is written and moe_swiglu_backward reads it (the same bits)."""
     sizes, dst = saved["group_sizes"], saved["perm_dst"]
     T = dy.shape[0]
     dyp, dw = combine_backward(dy, saved["y_perm"], saved["w"], dst, K)
-    dh = grouped_gemm(dyp, w2, sizes, b_layout=MOE_B_KN, flag=flag)           # dY_perm [M,d] x W2_e [d,f]
+    if fused:
+        dh = None
+        dgu = grouped_gemm(dyp, w2, sizes, b_layout=MOE_B_KN, epilogue=MOE_EPI_SWIGLU_BWD, aux=saved["gu"],
+                           flag=flag)
+    else:
+        dh = grouped_gemm(dyp, w2, sizes, b_layout=MOE_B_KN, flag=flag)       # dY_perm [M,d] x W2_e [d,f]
+        dgu = swiglu_backward(saved["gu"], dh, sizes)
     dw2 = grouped_gemm_wgrad(dyp, saved["h"], sizes, flag=flag)                # [E, d, f]
-    dgu = swiglu_backward(saved["gu"], dh, sizes)
     dxp = grouped_gemm(dgu, w1p, sizes, b_layout=MOE_B_KN, flag=flag)          # dGU [M,2f] x W1p_e [2f,d]
     dw1p = grouped_gemm_wgrad(dgu, saved["x_perm"], sizes, flag=flag)          # [E, 2f, d]
     dx = unpermute_combine(dxp, None, dst, T, K)

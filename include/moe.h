@@ -192,6 +192,15 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
  *   weight of the blog's MaxText config) and, if C_aux is not NULL,
  *   C_aux [m_cap, 2f] = bf16(acc) (the pre-activations, for the backward).
  *   Rows r >= sum(s_g) are not written.
+ *   epilogue MOE_EPI_SWIGLU_BWD (B_KN, bf16 only: the data gradient of the
+ *   down projection fused with SwiGLU's backward, so that dh is never
+ *   written and read back; blog section "Optimization 2", data read and
+ *   written to memory multiple times): N = f; with dh = bf16(A*Bop) and the
+ *   forward's pre-activations C_aux [m_cap, 2f] = [g | u] (required, read
+ *   only), C [m_cap, 2f] = [dg | du], dg = bf16(dh u s (1 + g (1 - s))),
+ *   du = bf16(dh g s), s = 1 / (1 + e^-g), as moe_swiglu_backward computes
+ *   them from the stored dh.  N <= 2^21.  Rows r >= sum(s_g) are not
+ *   written.
  * ragged = MOE_RAGGED_K (weight gradient; contraction over a group's rows):
  *   C[g] [M, N] = sum over rows r of group g of A[r, m] * B[r, n];
  *   A [m_cap, M], B [m_cap, N] (both row-major).  Empty groups get zeros.
@@ -266,6 +275,7 @@ moe_status_t moe_permute_routed(const uint16_t* x, const int32_t* topk_ids, int6
 #define MOE_EPI_NONE 0
 #define MOE_EPI_SWIGLU 1
 #define MOE_EPI_SWIGLU_MXFP8 2
+#define MOE_EPI_SWIGLU_BWD 3
 #define MOE_OUT_BF16 0
 #define MOE_OUT_F32 1
 

@@ -160,6 +160,21 @@ int main() {
   EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_OK);
   d.N = (1 << 22) + 8;
   EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
+  // SwiGLU backward in the data gradient's epilogue: bf16, B_KN, bf16 out, the pre-activations required
+  d = {MOE_DTYPE_BF16, MOE_RAGGED_M, MOE_B_KN, MOE_EPI_SWIGLU_BWD, MOE_OUT_BF16, 4, 0, 1 << 21, 64, 100};
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, p, nullptr, 0, nullptr, nullptr), MOE_OK);
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_INVALID_ARG);
+  d.N = (1 << 21) + 8;   // a 2N row pitch past the 32-bit tile offsets
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, p, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
+  d.N = 64;
+  d.b_layout = MOE_B_NK;
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, p, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
+  d.b_layout = MOE_B_KN;
+  d.out_dtype = MOE_OUT_F32;
+  EXPECT(grouped_gemm(&d, p, nullptr, p, nullptr, i32, p, p, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
+  d.out_dtype = MOE_OUT_BF16;
+  d.dtype = MOE_DTYPE_MXFP8;
+  EXPECT(grouped_gemm(&d, p, u8, p, u8, i32, p, p, nullptr, 0, nullptr, nullptr), MOE_ERR_UNSUPPORTED);
   d = {MOE_DTYPE_MXFP8, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, 1024, 64, 64, INT32_MAX - 63, INT32_MAX};
   EXPECT(grouped_gemm(&d, p, u8, p, u8, i32, p, nullptr, nullptr, 0, nullptr, nullptr), MOE_ERR_INVALID_ARG);
   d = {MOE_DTYPE_BF16, MOE_RAGGED_K, MOE_B_NK, MOE_EPI_NONE, MOE_OUT_BF16, 4, 64, 64, 0, 100};

@@ -163,9 +163,13 @@ def test_finegrained_forward_backward_full(ops):
     lg, x, w1, w2, dy = (t.to(dev) for t in (L.logits, L.x, L.w1p, L.w2, L.dy))
     flag = torch.zeros(1, dtype=torch.int32, device=dev)
     y, saved = ops.moe_forward(lg, x, w1, w2, L.K, keep=True, flag=flag)
-    g = ops.moe_backward(dy, saved, w1, w2, L.K, flag=flag)
+    g = ops.moe_backward(dy, saved, w1, w2, L.K, flag=flag, fused=False)
+    dgu_fused = ops.moe_backward(dy, saved, w1, w2, L.K, flag=flag)["dgu"]
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
+    rows_all = int(saved["group_sizes"].sum())
+    assert torch.equal(dgu_fused[:rows_all], g["dgu"][:rows_all])
+    del dgu_fused
     ids_ref, w_ref, sizes, src, dst = check_routing(ops, L, saved["ids"], saved["w"], saved)
     assert (sizes == 0).sum() >= 1
     tokens = np.unique(np.concatenate([[0, L.T - 1], np.random.default_rng(5).choice(L.T, 10, replace=False)]))

@@ -777,9 +777,15 @@ def test_tiny_layer_forward_backward(ops):
     g_ref = orc.layer_backward(L.dy, saved_ref, L.w1p, L.w2, L.K)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     y, saved = ops.moe_forward(dev(L.logits), dev(L.x), dev(L.w1p), dev(L.w2), L.K, keep=True, flag=flag)
-    grads = ops.moe_backward(dev(L.dy), saved, dev(L.w1p), dev(L.w2), L.K, flag=flag)
+    grads = ops.moe_backward(dev(L.dy), saved, dev(L.w1p), dev(L.w2), L.K, flag=flag, fused=False)
+    fused = ops.moe_backward(dev(L.dy), saved, dev(L.w1p), dev(L.w2), L.K, flag=flag)
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
+    # SwiGLU's backward formed in the data-gradient GEMM's epilogue gives the
+    # same bits as the GEMM's stored dh followed by the elementwise kernel
+    assert fused["dh"] is None
+    for k in ("dy_perm", "dgu", "dx_perm", "dx", "dw2", "dw1p"):
+        assert torch.equal(fused[k], grads[k]), k
     np.testing.assert_array_equal(saved["ids"].cpu().numpy(), saved_ref["ids"])
     np.testing.assert_array_equal(saved["group_sizes"].cpu().numpy(), saved_ref["sizes"])
     assert saved_ref["sizes"][7] == 0
@@ -1016,6 +1022,39 @@ def test_grouped_gemm_split_tail_after_whole_rounds(ops):
     rows = np.unique(np.concatenate([np.linspace(off[g], off[g + 1] - 1, 6).astype(np.int64) for g in range(G)]))
     ref = orc.grouped_gemm(A, B, sizes, rows=rows)
     assert max_rel_err(c1[torch.from_numpy(rows).cuda()], ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("case", ["ragged", "split_tail"])
+def test_grouped_gemm_swiglu_bwd_epilogue(ops, case):
+    """SwiGLU's backward formed in the data-gradient GEMM's epilogue: the
+    oracle's dgu from the oracle's dh, the same bits as the stored dh
+    followed by moe_swiglu_backward, rows past the groups not written.
+    ragged: empty groups, one-row and partial tiles, a partial column tile
+    (f = 200); split_tail: one round of tiles split along K in three."""
+    if case == "ragged":
+        sizes, f, Kd = np.array([0, 37, 256, 1, 0, 300, 129, 0], np.int32), 200, 192
+    else:
+        sizes, f, Kd = SPLIT_SIZES, 512, 2048
+    say("gg swiglu bwd epilogue", case)
+    rng = np.random.default_rng(83 + len(case))
+    G, M = sizes.size, int(sizes.sum())
+    m_cap = M + 40
+    A, B = bf16(rng, m_cap, Kd), bf16(rng, G, Kd, f, scale=Kd ** -0.5)
+    gu = bf16(rng, m_cap, 2 * f, scale=2.0)
+    dh_ref = orc.grouped_dgrad(A[:M], B, sizes)
+    dgu_ref = orc.swiglu_backward(gu[:M], dh_ref)
+    Ad, Bd, gud, sz = dev(A), dev(B), dev(gu), dev(torch.from_numpy(sizes))
+    out = torch.full((m_cap, 2 * f), 3.0, dtype=torch.bfloat16, device="cuda")
+    r = ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN, epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=gud, out=out)
+    again = ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN, epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=gud)
+    dh = ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN)
+    dgu = ops.swiglu_backward(gud, dh, sz)
+    torch.cuda.synchronize()
+    assert r is out
+    assert max_rel_err(out[:M], dgu_ref) <= BF16_TOL
+    assert torch.equal(out[:M], dgu[:M]) and torch.equal(again[:M], out[:M])
+    assert torch.all(out[M:] == 3.0)
+    assert torch.equal(gud, dev(gu))   # the pre-activations are only read
 
 
 @pytest.mark.parametrize("mode", ["nk", "packed", "packed_swiglu", "fused_quant"])
