@@ -1024,15 +1024,18 @@ def test_grouped_gemm_split_tail_after_whole_rounds(ops):
     assert max_rel_err(c1[torch.from_numpy(rows).cuda()], ref) <= BF16_TOL
 
 
-@pytest.mark.parametrize("case", ["ragged", "split_tail"])
+@pytest.mark.parametrize("case", ["ragged", "split_tail", "empty"])
 def test_grouped_gemm_swiglu_bwd_epilogue(ops, case):
     """SwiGLU's backward formed in the data-gradient GEMM's epilogue: the
     oracle's dgu from the oracle's dh, the same bits as the stored dh
     followed by moe_swiglu_backward, rows past the groups not written.
     ragged: empty groups, one-row and partial tiles, a partial column tile
-    (f = 200); split_tail: one round of tiles split along K in three."""
+    (f = 200); split_tail: one round of tiles split along K in three;
+    empty: every group empty, nothing written."""
     if case == "ragged":
         sizes, f, Kd = np.array([0, 37, 256, 1, 0, 300, 129, 0], np.int32), 200, 192
+    elif case == "empty":
+        sizes, f, Kd = np.zeros(4, np.int32), 64, 64
     else:
         sizes, f, Kd = SPLIT_SIZES, 512, 2048
     say("gg swiglu bwd epilogue", case)
@@ -1041,9 +1044,15 @@ def test_grouped_gemm_swiglu_bwd_epilogue(ops, case):
     m_cap = M + 40
     A, B = bf16(rng, m_cap, Kd), bf16(rng, G, Kd, f, scale=Kd ** -0.5)
     gu = bf16(rng, m_cap, 2 * f, scale=2.0)
+    Ad, Bd, gud, sz = dev(A), dev(B), dev(gu), dev(torch.from_numpy(sizes))
+    if M == 0:
+        out = torch.full((m_cap, 2 * f), 3.0, dtype=torch.bfloat16, device="cuda")
+        ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN, epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=gud, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 3.0)
+        return
     dh_ref = orc.grouped_dgrad(A[:M], B, sizes)
     dgu_ref = orc.swiglu_backward(gu[:M], dh_ref)
-    Ad, Bd, gud, sz = dev(A), dev(B), dev(gu), dev(torch.from_numpy(sizes))
     out = torch.full((m_cap, 2 * f), 3.0, dtype=torch.bfloat16, device="cuda")
     r = ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN, epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=gud, out=out)
     again = ops.grouped_gemm(Ad, Bd, sz, b_layout=ops.MOE_B_KN, epilogue=ops.MOE_EPI_SWIGLU_BWD, aux=gud)
