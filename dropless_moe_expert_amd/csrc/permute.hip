@@ -6,7 +6,8 @@
 // expert before the exchange; Figure 3: combine restores the original order.
 //
 // Three launches, no atomics deciding any order:
-//   1. rank:    one wavefront per chunk of kChunk pairs.  Pairs are taken 64 at
+//   1. rank:    one wavefront per chunk of kChunk pairs, its ids loaded at
+//               once.  Pairs are taken 64 at
 //               a time in pair order; a lane's rank among equal experts in
 //               the chunk = running count + lanes below it with the same
 //               expert (found with 8 ballots over the id bits).  Writes the
@@ -38,11 +39,23 @@ __global__ __launch_bounds__(64) void permute_rank_kernel(const int32_t* __restr
   __syncthreads();
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   const int64_t c1 = min(M, c0 + kChunk);
+  // the chunk's ids, all loads in flight at once (the ranking below is a
+  // serial walk over the chunk's 64-pair steps)
+  constexpr int kSteps = kChunk / 64;
+  int ev[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t i = c0 + 64 * s + lane;
+    ev[s] = i < c1 ? ids[i] : 0;
+  }
   bool bad = false;
-  for (int64_t base = c0; base < c1; base += 64) {
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t base = c0 + 64 * s;
+    if (base >= c1) break;   // uniform
     const int64_t i = base + lane;
     const bool valid = i < c1;
-    int e = valid ? ids[i] : 0;
+    int e = valid ? ev[s] : 0;
     if (valid && (e < 0 || e >= E)) { bad = true; e = E - 1; }
     // lanes with the same expert: AND over the 8 id bits of (ballot or its complement)
     uint64_t same = __ballot(valid);
